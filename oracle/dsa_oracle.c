@@ -1,0 +1,387 @@
+/*
+ * dsa_oracle.c -- plain, slow, fp64 CPU oracle for the DeepSeek Sparse Attention
+ * (DSA) hot path: lightning indexer -> per-query top-k -> sparse MLA (MQA mode).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library shares
+ * no code, header, table or helper with it.
+ *
+ * What is computed, and where it is stated:
+ *  - The indexer gives every query token an "index score" against each
+ *    preceding token, with few heads, a ReLU activation and FP8 operands
+ *    (mizuki-eaf.pages.dev, "DeepSeek Sparse Attention" / "How it works";
+ *    m.digipub.cc, section 2).  The score formula
+ *        I[t,s] = sum_j w[t,j] * ReLU( q_I[t,j] . k_I[s] )
+ *    and the per-token fp32 scales of the FP8 operands are the workload's
+ *    definition; the pages name only "few heads, ReLU, FP8".
+ *  - Each query keeps the key/value entries with the top-k index scores,
+ *    k = 2048 (mizuki-eaf.pages.dev, same section, and its "DSA key
+ *    parameters" table; m.36881.com.cn, "Fine-grained Token Selection").
+ *  - Main attention is MLA in MQA mode: one latent vector per token is shared
+ *    by all query heads of a query token (mizuki-eaf.pages.dev, "built on
+ *    MLA"); the latent is 576-dim (512 + 64 rope) and its first 512 dims are
+ *    the value.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *  - "preceding tokens" includes the query's own position: candidates of the
+ *    query at position p are s in [0, p], so a query selects min(k, p+1).
+ *  - ties in the index score are broken toward the larger (more recent)
+ *    position; the order is (score descending, position descending).
+ *  - -0 scores are canonicalised to +0.
+ *  - FP8 is OCP E4M3FN (bias 7, max 448, no infinities, S.1111.111 = NaN).
+ *  - per-token quantisation: scale = amax(|x_row|)/448 in fp32 (1 when the
+ *    row is all zero); payload = RNE-to-E4M3, saturating at +-448, of the fp32
+ *    quotient x/scale.
+ *  - an empty selected set gives o = 0 and lse = -inf.
+ *
+ * Every floating-point accumulation here is fp64, in the plain loop order of
+ * the definition; nothing is blocked, fused or reordered.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ codecs */
+
+/* OCP 8-bit floating point spec v1.0, E4M3: bias 7; e=0 is subnormal with
+ * value m/8 * 2^-6; e=15,m=7 is NaN; no infinities. */
+double ora_e4m3_decode(uint8_t c)
+{
+    int s = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* bf16 is the top half of an IEEE binary32. */
+double ora_bf16_decode(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* fp32 -> E4M3 with round-to-nearest-even and saturation at +-448. */
+uint8_t ora_e4m3_encode(float x)
+{
+    uint8_t sign;
+    double a, step, q, v;
+    int E;
+    if (isnan(x))
+        return 0x7F;
+    sign = signbit(x) ? 0x80 : 0x00;
+    a = fabs((double)x);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a == 0.0)
+        return sign;
+    /* exponent of a; below the smallest normal (2^-6) the grid step is 2^-9 */
+    E = ilogb(a);
+    if (E < -6)
+        E = -6;
+    step = ldexp(1.0, E - 3);       /* 3 mantissa bits */
+    q = rint(a / step);             /* exact quotient, RNE (default rounding mode) */
+    v = q * step;                   /* rounded magnitude, on the E4M3 grid */
+    if (v >= 448.0)
+        return sign | 0x7E;
+    if (v == 0.0)
+        return sign;
+    if (v < ldexp(1.0, -6))         /* subnormal: m * 2^-9 */
+        return sign | (uint8_t)(v / ldexp(1.0, -9));
+    E = ilogb(v);
+    return sign | (uint8_t)(((E + 7) << 3) | ((int)(v / ldexp(1.0, E - 3)) - 8));
+}
+
+/* Per-row quantisation of an fp32 matrix [rows, cols] to E4M3 + fp32 scale. */
+void ora_quantize_rows(const float *x, int64_t rows, int32_t cols, uint8_t *x8, float *scale)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        const float *xr = x + r * (int64_t)cols;
+        float amax = 0.0f, s;
+        int32_t c;
+        for (c = 0; c < cols; ++c) {
+            float a = fabsf(xr[c]);
+            if (a > amax)
+                amax = a;
+        }
+        s = amax / 448.0f;          /* fp32 division, correctly rounded */
+        if (!(s > 0.0f))
+            s = 1.0f;
+        scale[r] = s;
+        for (c = 0; c < cols; ++c) {
+            float qf = xr[c] / s;   /* fp32 quotient, then one rounding to E4M3 */
+            x8[r * (int64_t)cols + c] = ora_e4m3_encode(qf);
+        }
+    }
+}
+
+/* ----------------------------------------------------------------- indexer */
+
+enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_E4M3 = 2 };
+
+static double elem(int dtype, const void *p, int64_t i)
+{
+    if (dtype == ORA_E4M3)
+        return ora_e4m3_decode(((const uint8_t *)p)[i]);
+    if (dtype == ORA_BF16)
+        return ora_bf16_decode(((const uint16_t *)p)[i]);
+    return (double)((const float *)p)[i];
+}
+
+/*
+ * Index scores of selected query rows.
+ *   q  [T, H_I, D_I]  (E4M3 payload with q_scale[T], or F32 with no scale)
+ *   k  [S, D_I]       (same dtype; k_scale[S] for E4M3)
+ *   w  [T, H_I] fp32, q_pos[T]
+ * For each i < nrows, t = rows[i]:
+ *   out[i, s] = sum_j w[t,j] * max(0, sum_d (qs[t] q[t,j,d]) * (ks[s] k[s,d]))
+ *               for s <= q_pos[t]   (and s < S),
+ *   out[i, s] = -inf otherwise.
+ */
+void ora_indexer_rows(int dtype, const void *q, const float *q_scale, const void *k,
+                      const float *k_scale, const float *w, const int32_t *q_pos, int64_t T,
+                      int64_t S, int32_t H_I, int32_t D_I, const int64_t *rows, int64_t nrows,
+                      double *out)
+{
+    int64_t i;
+    (void)T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        int64_t t = rows[i], s;
+        int64_t p = q_pos[t];
+        double *o = out + i * S;
+        double *qv = (double *)malloc(sizeof(double) * (size_t)H_I * (size_t)D_I);
+        double *kv = (double *)malloc(sizeof(double) * (size_t)D_I);
+        double qs = (dtype == ORA_E4M3) ? (double)q_scale[t] : 1.0;
+        int32_t j, d;
+        for (j = 0; j < H_I; ++j)
+            for (d = 0; d < D_I; ++d)
+                qv[j * D_I + d] = qs * elem(dtype, q, (t * H_I + j) * (int64_t)D_I + d);
+        for (s = 0; s < S; ++s) {
+            double ks, acc = 0.0;
+            if (s > p) {
+                o[s] = -INFINITY;
+                continue;
+            }
+            ks = (dtype == ORA_E4M3) ? (double)k_scale[s] : 1.0;
+            for (d = 0; d < D_I; ++d)
+                kv[d] = ks * elem(dtype, k, s * (int64_t)D_I + d);
+            for (j = 0; j < H_I; ++j) {
+                double dot = 0.0;
+                for (d = 0; d < D_I; ++d)
+                    dot += qv[j * D_I + d] * kv[d];
+                acc += (double)w[t * H_I + j] * (dot > 0.0 ? dot : 0.0);
+            }
+            o[s] = (acc == 0.0) ? 0.0 : acc;   /* -0 -> +0 */
+        }
+        free(qv);
+        free(kv);
+    }
+}
+
+/* ------------------------------------------------------------------- top-k */
+
+typedef struct {
+    double v;
+    int64_t pos;
+} cand_t;
+
+/* (score descending, position descending) */
+static int cand_cmp(const void *a, const void *b)
+{
+    const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+    if (x->v > y->v)
+        return -1;
+    if (x->v < y->v)
+        return 1;
+    if (x->pos > y->pos)
+        return -1;
+    if (x->pos < y->pos)
+        return 1;
+    return 0;
+}
+
+static int i32_cmp(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * Top-k of one row of n candidate scores (positions 0..n-1).  Writes the
+ * K = min(k, n) kept positions to idx[0..K) in ascending position order,
+ * -1 to idx[K..k), and returns K.  *tau = score of the K-th kept candidate
+ * (-inf if K = 0).
+ */
+int64_t ora_topk_row(const double *scores, int64_t n, int32_t k, int32_t *idx, double *tau)
+{
+    int64_t K = n < k ? n : k, i;
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+    for (i = 0; i < n; ++i) {
+        c[i].v = scores[i];
+        c[i].pos = i;
+    }
+    qsort(c, (size_t)n, sizeof(cand_t), cand_cmp);
+    for (i = 0; i < K; ++i)
+        idx[i] = (int32_t)c[i].pos;
+    qsort(idx, (size_t)K, sizeof(int32_t), i32_cmp);
+    for (i = K; i < k; ++i)
+        idx[i] = -1;
+    *tau = K > 0 ? c[K - 1].v : -INFINITY;
+    free(c);
+    return K;
+}
+
+/* Row-wise top-k over a [nrows, ld] score matrix with per-row candidate counts. */
+void ora_topk_rows(const double *scores, int64_t ld, const int64_t *n_valid, int64_t nrows,
+                   int32_t k, int32_t *idx, double *tau)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i)
+        ora_topk_row(scores + i * ld, n_valid[i], k, idx + i * (int64_t)k, tau + i);
+}
+
+/* ------------------------------------------------------------- sparse MLA */
+
+/*
+ * Sparse MLA in MQA mode for selected query rows.
+ *   q   [T, H, Dqk]  (F32 or BF16)
+ *   kv  [N, Dqk]     (same dtype); the value of row r is kv[r, 0..Dv)
+ *   idx [T, k]       row indices into kv; -1 entries are skipped
+ * For t = rows[i] and every head h, over the valid entries r_1..r_m of idx[t]:
+ *   z_a = sm_scale * sum_d q[t,h,d] kv[r_a,d]
+ *   o[i,h,:] = sum_a softmax(z)_a kv[r_a, 0..Dv)
+ *   lse[i,h] = log sum_a exp(z_a)       (natural log)
+ * with m = 0 giving o = 0, lse = -inf.
+ */
+void ora_sparse_mla_rows(int dtype, const void *q, const void *kv, const int32_t *idx, int64_t T,
+                         int32_t H, int64_t N, int32_t k, int32_t Dqk, int32_t Dv, double sm_scale,
+                         const int64_t *rows, int64_t nrows, double *o, double *lse)
+{
+    int64_t i;
+    (void)T;
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        int64_t t = rows[i];
+        const int32_t *sel = idx + t * (int64_t)k;
+        double *z = (double *)malloc(sizeof(double) * (size_t)k);
+        double *qh = (double *)malloc(sizeof(double) * (size_t)Dqk);
+        int32_t h;
+        for (h = 0; h < H; ++h) {
+            double *oh = o + (i * H + h) * (int64_t)Dv;
+            double mx = -INFINITY, sum = 0.0;
+            int32_t a, d, m = 0;
+            for (d = 0; d < Dqk; ++d)
+                qh[d] = elem(dtype, q, (t * H + h) * (int64_t)Dqk + d);
+            for (d = 0; d < Dv; ++d)
+                oh[d] = 0.0;
+            for (a = 0; a < k; ++a) {
+                double dot = 0.0;
+                int64_t r = sel[a];
+                if (r < 0) {
+                    z[a] = -INFINITY;
+                    continue;
+                }
+                for (d = 0; d < Dqk; ++d)
+                    dot += qh[d] * elem(dtype, kv, r * Dqk + d);
+                z[a] = sm_scale * dot;
+                if (z[a] > mx)
+                    mx = z[a];
+                ++m;
+            }
+            if (m == 0) {
+                lse[i * H + h] = -INFINITY;
+                continue;
+            }
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    sum += exp(z[a] - mx);
+            for (a = 0; a < k; ++a) {
+                double p;
+                int64_t r = sel[a];
+                if (r < 0)
+                    continue;
+                p = exp(z[a] - mx) / sum;
+                for (d = 0; d < Dv; ++d)
+                    oh[d] += p * elem(dtype, kv, r * Dqk + d);
+            }
+            lse[i * H + h] = mx + log(sum);
+        }
+        free(z);
+        free(qh);
+    }
+}
+
+/* ------------------------------------------------------------ paged decode */
+
+/*
+ * One decode query per sequence over a paged cache of 64-token pages.
+ * Sequence b has ctx[b] cached tokens; its query sits at position ctx[b]-1
+ * (its own key and latent are already in the cache), so candidates are
+ * positions 0..ctx[b]-1.  Logical position p of sequence b lives in physical
+ * row  block_table[b*max_blocks + p/64]*64 + p%64  of the pools:
+ *   k8 pool [nrows_phys, D_I] E4M3 + ks pool [nrows_phys] fp32 (indexer keys)
+ *   kv pool [nrows_phys, Dqk] BF16 (latent; value = first Dv dims)
+ * Query side per sequence: q8 [B, H_I, D_I] E4M3 + qs [B], w [B, H_I],
+ * q [B, H, Dqk] BF16.
+ * Outputs for sequences seqs[0..nseq): idx [nseq, k] logical positions
+ * (ascending, -1 padded), tau [nseq], o [nseq, H, Dv], lse [nseq, H].
+ */
+void ora_decode(const uint8_t *q8, const float *qs, const float *w, const uint16_t *q,
+                const uint8_t *k8_pool, const float *ks_pool, const uint16_t *kv_pool,
+                const int32_t *block_table, int32_t max_blocks, const int32_t *ctx, int32_t B,
+                int32_t H_I, int32_t D_I, int32_t H, int32_t k, int32_t Dqk, int32_t Dv,
+                double sm_scale, const int64_t *seqs, int64_t nseq, int32_t *idx, double *tau,
+                double *o, double *lse)
+{
+    int64_t i;
+    (void)B;
+    for (i = 0; i < nseq; ++i) {
+        int64_t b = seqs[i], n = ctx[b], p;
+        double *sc = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        int32_t *phys = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+        int32_t *lidx = idx + i * (int64_t)k;
+        int32_t a;
+        double qsv = (double)qs[b];
+#pragma omp parallel for schedule(static)
+        for (p = 0; p < n; ++p) {
+            int64_t row = (int64_t)block_table[b * max_blocks + p / 64] * 64 + p % 64;
+            double ksv = (double)ks_pool[row], acc = 0.0;
+            int32_t j, d;
+            for (j = 0; j < H_I; ++j) {
+                double dot = 0.0;
+                for (d = 0; d < D_I; ++d)
+                    dot += (qsv * ora_e4m3_decode(q8[(b * H_I + j) * (int64_t)D_I + d])) *
+                           (ksv * ora_e4m3_decode(k8_pool[row * D_I + d]));
+                acc += (double)w[b * H_I + j] * (dot > 0.0 ? dot : 0.0);
+            }
+            sc[p] = (acc == 0.0) ? 0.0 : acc;
+        }
+        ora_topk_row(sc, n, k, lidx, tau + i);
+        /* selected logical positions -> physical latent rows */
+        for (a = 0; a < k; ++a) {
+            int32_t lp = lidx[a];
+            phys[a] = lp < 0 ? -1 : block_table[b * max_blocks + lp / 64] * 64 + lp % 64;
+        }
+        {
+            int64_t one = 0;
+            /* q row b viewed as a single-row problem whose idx row is phys */
+            ora_sparse_mla_rows(ORA_BF16, q + b * (int64_t)H * Dqk, kv_pool, phys, 1, H, 0, k, Dqk,
+                                Dv, sm_scale, &one, 1, o + i * (int64_t)H * Dv, lse + i * H);
+        }
+        free(sc);
+        free(phys);
+    }
+}
