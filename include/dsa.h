@@ -1,0 +1,220 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) implementation of the
+ * DeepSeek Sparse Attention (DSA) hot path:
+ *
+ *   lightning indexer  ->  per-query top-k selection  ->  sparse MLA (MQA mode)
+ *
+ * The method (DeepSeek-V3.2; mizuki-eaf.pages.dev, section "DeepSeek Sparse
+ * Attention", "How it works" and "built on MLA"; m.digipub.cc, section 2):
+ * a light indexer with few heads, ReLU and FP8 operands scores every query
+ * token against each preceding token; each query keeps the key/value entries
+ * with the top-k scores (k = 2048); main attention runs over only those
+ * entries, as MLA in MQA mode, where one latent vector per token is shared by
+ * all query heads of a query token.
+ *
+ * Conventions (all entry points)
+ *  - Tensor pointers are DEVICE pointers owned by the caller; tensors are
+ *    dense, row-major, with the shapes given below.  The library never
+ *    allocates device memory: scratch space comes from a caller-provided
+ *    workspace sized by the matching *_workspace_bytes() query.
+ *  - Calls only validate and enqueue work on `stream`; they return before the
+ *    GPU finishes.  Results are deterministic run to run.
+ *  - Every call returns a dsa_status.  Host-side validation runs before any
+ *    HIP call; on failure nothing is enqueued and dsa_last_error() returns a
+ *    message (thread-local, valid until the next call on the same thread).
+ *  - Offsets are 64-bit; the 128K-token shapes are supported.
+ *  - Positions: the query at position p may select keys at positions
+ *    0..p inclusive, so it selects min(k, p+1) of them.  Equal index scores
+ *    are ordered by position, the larger (more recent) position first.
+ *  - FP8 is OCP E4M3FN (bias 7, max 448, no infinities).  bf16 is the top 16
+ *    bits of an IEEE binary32.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent size   */
+    DSA_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement  */
+    DSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required     */
+    DSA_ERR_HIP = 4           /* a HIP call (launch, query) failed              */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_E4M3 = 2 } dsa_dtype;
+
+enum {
+    DSA_D_QK = 576,    /* latent width: 512 no-rope + 64 rope               */
+    DSA_D_V = 512,     /* value width: the first 512 dims of the latent     */
+    DSA_MAX_K = 2048,  /* largest supported top-k                           */
+    DSA_PAGE = 64      /* tokens per page of the paged decode cache         */
+};
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *dsa_last_error(void);
+
+/* Library version string. */
+const char *dsa_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Per-token E4M3 quantisation of indexer operands (the indexer "can run in
+ * FP8": mizuki-eaf.pages.dev, "How it works"; m.digipub.cc, section 2).
+ *   x      [rows, cols] fp32
+ *   x8     [rows, cols] E4M3 out;  scale [rows] fp32 out
+ * scale[r] = amax_c |x[r,c]| / 448 (fp32 division; 1 if the row is all zero);
+ * x8[r,c] = E4M3 of the fp32 quotient x[r,c]/scale[r], round-to-nearest-even,
+ * saturating at +-448.  cols must be a multiple of 4 and at most 16384.
+ */
+dsa_status dsa_quantize_e4m3_per_token(const float *x, int64_t rows, int32_t cols, uint8_t *x8,
+                                       float *scale, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Lightning indexer scores (mizuki-eaf.pages.dev, "How it works":
+ * "index score" of a query token against every preceding token).
+ *   I[t,s] = sum_{j<H_I} w[t,j] * ReLU( (qs[t] q[t,j,:]) . (ks[s] k[s,:]) )
+ *   q       [T, H_I, D_I]  E4M3 (with q_scale [T]) or F32 (q_scale NULL)
+ *   k       [S, D_I]       same dtype (with k_scale [S] for E4M3)
+ *   w       [T, H_I] fp32 head weights
+ *   q_pos   [T] int32: query t may see keys s in [0, q_pos[t]]
+ *   scores  [T, ld_scores] fp32 out; s > q_pos[t] (s < S) is written -inf.
+ * E4M3: products are exact, sums are fp32 (FP8 MFMA); scales must be > 0.
+ * Limits: E4M3 needs D_I = 128 and H_I a multiple of 32 (<= 64);
+ *         F32 needs D_I <= 128 and H_I <= 64.
+ */
+dsa_status dsa_indexer_scores(const void *q, const float *q_scale, const void *k,
+                              const float *k_scale, const float *w, const int32_t *q_pos,
+                              int32_t T, int32_t S, int32_t H_I, int32_t D_I, dsa_dtype dt,
+                              float *scores, int64_t ld_scores, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Fine-grained token selection (mizuki-eaf.pages.dev, "How it works";
+ * m.digipub.cc, section 2): per row keep the k largest scores.
+ *   scores  [T, ld_scores] fp32; row t has candidates s in [0, n_valid[t])
+ *   n_valid [T] int32 (device)
+ *   idx     [T, k] int32 out: the min(k, n_valid[t]) selected positions in
+ *           ascending order, then -1.
+ * Order: score descending, then position descending.  k <= 2048; rows of any
+ * length up to 2^31-1.  No workspace is needed (pass NULL, 0).
+ */
+dsa_status dsa_topk_select(const float *scores, int64_t ld_scores, const int32_t *n_valid,
+                           int32_t T, int32_t k, int32_t *idx, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse MLA forward in MQA mode (mizuki-eaf.pages.dev, "built on MLA";
+ * jienda.com, section 2.1): one latent row per token, shared by all heads.
+ *   q    [T, H, 576]   BF16 or F32
+ *   kv   [N, 576]      same dtype; the value of row r is kv[r, 0:512]
+ *   idx  [T, k] int32  rows of kv attended by query t; -1 entries are skipped
+ *   out  [T, H, 512]   same dtype as q;  lse [T, H] fp32 (natural log), may be NULL
+ *   o[t,h] = sum_i softmax_i(sm_scale * q[t,h].kv[idx[t,i]]) kv[idx[t,i], :512]
+ * A query with no valid entry gets o = 0 and lse = -inf.
+ * BF16: bf16 MFMA, fp32 softmax and accumulation, output rounded (RNE) to bf16.
+ * Limits: BF16 needs H a multiple of 16; F32 needs H <= 128; k <= 2048.
+ * workspace (optional) lets the kernel split long selections across more
+ * workgroups when T is small; size it with dsa_sparse_mla_workspace_bytes().
+ */
+size_t dsa_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t k);
+dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const int32_t *idx,
+                              int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale,
+                              void *out, float *lse, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused prefill of one causal sequence (query t sits at position t):
+ * indexer scores are computed tile by tile and fed straight into a per-query
+ * streaming top-k held on chip, so the L x L score matrix is never written;
+ * then sparse MLA over the selected rows.
+ *   idx_dt E4M3: q_idx [L,H_I,D_I] + q_scale [L], k_idx [L,D_I] + k_scale [L]
+ *          (D_I = 128, H_I = 64);
+ *   idx_dt F32 : same shapes in fp32, scales NULL; runs the three unfused
+ *          calls with the L x L scores in the workspace (small L only).
+ *   w [L,H_I] fp32;  q [L,H,576], kv [L,576] in attn_dt (BF16 or F32);
+ *   idx [L,k] int32 out (selected positions, ascending, -1 padded);
+ *   out [L,H,512] in attn_dt;  lse [L,H] fp32 (may be NULL).
+ */
+typedef struct {
+    int32_t L, H_I, D_I, H, k;
+    dsa_dtype idx_dt;
+    const void *q_idx;
+    const float *q_scale;
+    const void *k_idx;
+    const float *k_scale;
+    const float *w;
+    dsa_dtype attn_dt;
+    const void *q;
+    const void *kv;
+    float sm_scale;
+    int32_t *idx;
+    void *out;
+    float *lse;
+} dsa_prefill_args;
+
+size_t dsa_prefill_workspace_bytes(const dsa_prefill_args *a);
+dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged decode: one query per sequence at position ctx_len[b]-1, whose own
+ * key and latent are already in the cache.  The cache is paged in 64-token
+ * pages; logical position p of sequence b lives in physical row
+ *     block_table[b*max_blocks + p/64]*64 + p%64
+ * of every pool.  Steps: indexer over the sequence's FP8 keys -> top-k ->
+ * sparse MLA gathering the selected latent rows through the block table.
+ *   q8 [B,H_I,D_I] E4M3, q_scale [B], w [B,H_I] fp32, q [B,H,576] BF16
+ *   k8_pool [n_pool_rows, D_I] E4M3, ks_pool [n_pool_rows] fp32,
+ *   kv_pool [n_pool_rows, 576] BF16, with n_pool_rows a multiple of 64
+ *   block_table [B, max_blocks] int32, ctx_len [B] int32 (device)
+ *   max_ctx: host-side upper bound of ctx_len (sizes grids and workspace)
+ *   idx_out [B,k] int32 (optional, logical positions ascending, -1 padded)
+ *   out [B,H,512] BF16, lse [B,H] fp32 (may be NULL)
+ * Limits: D_I = 128, H_I = 64, H a multiple of 16, 1 <= ctx_len <= max_ctx.
+ */
+typedef struct {
+    int32_t B, H_I, D_I, H, k;
+    const uint8_t *q8;
+    const float *q_scale;
+    const float *w;
+    const void *q;
+    const uint8_t *k8_pool;
+    const float *ks_pool;
+    const void *kv_pool;
+    int64_t n_pool_rows;
+    const int32_t *block_table;
+    int32_t max_blocks;
+    const int32_t *ctx_len;
+    int32_t max_ctx;
+    float sm_scale;
+    int32_t *idx_out;
+    void *out;
+    float *lse;
+} dsa_decode_args;
+
+size_t dsa_decode_workspace_bytes(const dsa_decode_args *a);
+dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged cache append (MLA's latent cache: jienda.com, section 2.1): write one
+ * token per sequence into the pools at logical position pos[b].
+ *   latent [B,576] BF16, k8 [B,D_I] E4M3, ks [B] fp32, pos [B] int32 (device)
+ *   pools and block_table as for dsa_decode.  Positions must be mapped by the
+ *   block table (the page must exist); rows of different b must differ.
+ */
+dsa_status dsa_paged_cache_append(const void *latent, const uint8_t *k8, const float *ks,
+                                  const int32_t *pos, int32_t B, int32_t D_I,
+                                  const int32_t *block_table, int32_t max_blocks, void *kv_pool,
+                                  uint8_t *k8_pool, float *ks_pool, int64_t n_pool_rows,
+                                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,304 @@
+// capi.cpp -- the C ABI of libdsa: argument validation, workspace layout and
+// dispatch to the gfx950 kernels.  Validation happens before any HIP call;
+// nothing is enqueued on failure.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dsa_common.h"
+
+namespace dsa {
+static thread_local char g_err[512];
+
+dsa_status fail(dsa_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dsa_status hip_check(hipError_t e, const char *what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStream_t s);
+
+// Workgroups of the bf16 sparse-MLA kernel without splitting, and the split
+// count that brings a small batch up to about one workgroup per CU.
+static int mla_waves(int H) { return H % 128 == 0 ? 8 : H % 64 == 0 ? 4 : H % 32 == 0 ? 2 : 1; }
+static int mla_splits(int64_t T, int H, int k) {
+  const int64_t base = T * (H / (16 * mla_waves(H)));
+  const int ntiles = (k + 31) / 32;
+  if (base <= 0 || base >= 256) return 1;
+  int s = (int)((256 + base - 1) / base);
+  if (s > ntiles) s = ntiles;
+  if (s > 32) s = 32;
+  return s < 1 ? 1 : s;
+}
+static size_t mla_ws_bytes(int64_t T, int H, int k) {
+  const int s = mla_splits(T, H, k);
+  if (s <= 1) return 0;
+  return align_up((size_t)T * s * H * 512 * 4, 256) + align_up((size_t)T * s * H * 2 * 4, 256);
+}
+static void mla_ws_split(void *ws, int64_t T, int H, int k, float **po, float **pml) {
+  const int s = mla_splits(T, H, k);
+  *po = (float *)ws;
+  *pml = (float *)((char *)ws + align_up((size_t)T * s * H * 512 * 4, 256));
+}
+}  // namespace dsa
+
+using namespace dsa;
+
+#define CLEAR_ERR() (g_err[0] = '\0')
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+extern "C" {
+
+const char *dsa_last_error(void) { return g_err; }
+const char *dsa_version(void) { return "libdsa 0.1 gfx950"; }
+
+dsa_status dsa_quantize_e4m3_per_token(const float *x, int64_t rows, int32_t cols, uint8_t *x8,
+                                       float *scale, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(rows >= 0, DSA_ERR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
+  REQUIRE(cols > 0, DSA_ERR_INVALID_ARG, "cols must be > 0 (got %d)", cols);
+  REQUIRE(rows == 0 || (x && x8 && scale), DSA_ERR_INVALID_ARG, "null pointer");
+  REQUIRE(cols % 4 == 0 && cols <= 16384, DSA_ERR_UNSUPPORTED, "cols must be a multiple of 4, <= 16384");
+  return hip_check(launch_quantize(x, rows, cols, x8, scale, stream), "quantize launch");
+}
+
+dsa_status dsa_indexer_scores(const void *q, const float *q_scale, const void *k, const float *k_scale,
+                              const float *w, const int32_t *q_pos, int32_t T, int32_t S, int32_t H_I,
+                              int32_t D_I, dsa_dtype dt, float *scores, int64_t ld_scores,
+                              hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0 && S >= 0, DSA_ERR_INVALID_ARG, "T and S must be >= 0");
+  REQUIRE(H_I > 0 && D_I > 0, DSA_ERR_INVALID_ARG, "H_I and D_I must be > 0");
+  REQUIRE(ld_scores >= S, DSA_ERR_INVALID_ARG, "ld_scores (%lld) < S (%d)", (long long)ld_scores, S);
+  if (T == 0 || S == 0) return DSA_OK;
+  REQUIRE(q && k && w && q_pos && scores, DSA_ERR_INVALID_ARG, "null pointer");
+  if (dt == DSA_E4M3) {
+    REQUIRE(q_scale && k_scale, DSA_ERR_INVALID_ARG, "E4M3 needs q_scale and k_scale");
+    REQUIRE(D_I == 128 && (H_I == 32 || H_I == 64), DSA_ERR_UNSUPPORTED,
+            "E4M3 indexer needs D_I = 128 and H_I in {32, 64} (got %d, %d)", D_I, H_I);
+    return hip_check(launch_indexer_scores_fp8((const uint8_t *)q, q_scale, (const uint8_t *)k, k_scale, w,
+                                               q_pos, T, S, H_I, scores, ld_scores, stream),
+                     "indexer launch");
+  }
+  if (dt == DSA_F32) {
+    REQUIRE(D_I <= 128 && H_I <= 64, DSA_ERR_UNSUPPORTED, "F32 indexer needs D_I <= 128, H_I <= 64");
+    return hip_check(launch_indexer_scores_f32((const float *)q, (const float *)k, w, q_pos, T, S, H_I, D_I,
+                                               scores, ld_scores, stream),
+                     "indexer launch");
+  }
+  return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be E4M3 or F32");
+}
+
+dsa_status dsa_topk_select(const float *scores, int64_t ld_scores, const int32_t *n_valid, int32_t T,
+                           int32_t k, int32_t *idx, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  CLEAR_ERR();
+  (void)workspace;
+  (void)workspace_bytes;
+  REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "T must be >= 0");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d (got %d)", DSA_MAX_K, k);
+  REQUIRE(ld_scores >= 0, DSA_ERR_INVALID_ARG, "ld_scores must be >= 0");
+  if (T == 0) return DSA_OK;
+  REQUIRE(scores && n_valid && idx, DSA_ERR_INVALID_ARG, "null pointer");
+  return hip_check(launch_topk(scores, ld_scores, n_valid, 0x7FFFFFFF, T, k, idx, stream), "topk launch");
+}
+
+size_t dsa_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t k) {
+  if (T <= 0 || H <= 0 || k <= 0 || H % 16) return 0;
+  return mla_ws_bytes(T, H, k);
+}
+
+dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const int32_t *idx, int32_t T,
+                              int32_t H, int64_t N, int32_t k, float sm_scale, void *out, float *lse,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0 && N >= 0, DSA_ERR_INVALID_ARG, "T and N must be >= 0");
+  REQUIRE(H > 0, DSA_ERR_INVALID_ARG, "H must be > 0");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (T == 0) return DSA_OK;
+  REQUIRE(q && kv && idx && out, DSA_ERR_INVALID_ARG, "null pointer");
+  if (dt == DSA_BF16) {
+    REQUIRE(H % 16 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 16 (got %d)", H);
+    const size_t need = mla_ws_bytes(T, H, k);
+    int splits = 1;
+    float *po = nullptr, *pml = nullptr;
+    if (workspace && need > 0) {
+      REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu", workspace_bytes,
+              need);
+      splits = mla_splits(T, H, k);
+      mla_ws_split(workspace, T, H, k, &po, &pml);
+    }
+    return hip_check(launch_sparse_mla_bf16(q, kv, idx, nullptr, 0, N, T, H, k, sm_scale, out, lse, splits,
+                                            po, pml, stream),
+                     "sparse mla launch");
+  }
+  if (dt == DSA_F32) {
+    return hip_check(launch_sparse_mla_f32((const float *)q, (const float *)kv, idx, N, T, H, k, sm_scale,
+                                           (float *)out, lse, stream),
+                     "sparse mla launch");
+  }
+  return fail(DSA_ERR_UNSUPPORTED, "sparse MLA dtype must be BF16 or F32");
+}
+
+static dsa_status check_prefill(const dsa_prefill_args *a) {
+  REQUIRE(a, DSA_ERR_INVALID_ARG, "null args");
+  REQUIRE(a->L >= 1, DSA_ERR_INVALID_ARG, "L must be >= 1");
+  REQUIRE(a->H > 0 && a->H_I > 0 && a->D_I > 0, DSA_ERR_INVALID_ARG, "head counts and D_I must be > 0");
+  REQUIRE(a->k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(a->k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(a->q_idx && a->k_idx && a->w && a->q && a->kv && a->idx && a->out, DSA_ERR_INVALID_ARG,
+          "null pointer");
+  REQUIRE(a->sm_scale == a->sm_scale && a->sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (a->idx_dt == DSA_E4M3) {
+    REQUIRE(a->q_scale && a->k_scale, DSA_ERR_INVALID_ARG, "E4M3 needs q_scale and k_scale");
+    REQUIRE(a->H_I == 64 && a->D_I == 128, DSA_ERR_UNSUPPORTED, "fused E4M3 prefill needs H_I = 64, D_I = 128");
+  } else if (a->idx_dt == DSA_F32) {
+    REQUIRE(a->D_I <= 128 && a->H_I <= 64, DSA_ERR_UNSUPPORTED, "F32 indexer needs D_I <= 128, H_I <= 64");
+    REQUIRE((int64_t)a->L * a->L <= (int64_t)1 << 28, DSA_ERR_UNSUPPORTED,
+            "the F32 prefill keeps the L x L scores in the workspace; L must be <= 16384");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be E4M3 or F32");
+  }
+  if (a->attn_dt == DSA_BF16)
+    REQUIRE(a->H % 16 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 16");
+  else
+    REQUIRE(a->attn_dt == DSA_F32, DSA_ERR_UNSUPPORTED, "attention dtype must be BF16 or F32");
+  return DSA_OK;
+}
+
+size_t dsa_prefill_workspace_bytes(const dsa_prefill_args *a) {
+  if (!a || a->L < 1) return 0;
+  if (a->idx_dt == DSA_F32) {
+    const size_t L = (size_t)a->L;
+    return align_up(L * L * 4, 256) + 2 * align_up(L * 4, 256);
+  }
+  return 0;
+}
+
+dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  CLEAR_ERR();
+  dsa_status st = check_prefill(a);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa_prefill_workspace_bytes(a);
+  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), DSA_ERR_WORKSPACE,
+          "workspace %zu < required %zu", workspace ? workspace_bytes : (size_t)0, need);
+  const int L = a->L;
+  if (a->idx_dt == DSA_E4M3) {
+    st = hip_check(launch_prefill_indexer_topk((const uint8_t *)a->q_idx, a->q_scale, (const uint8_t *)a->k_idx,
+                                               a->k_scale, a->w, L, a->k, a->idx, stream),
+                   "prefill indexer/top-k launch");
+  } else {
+    float *sc = (float *)workspace;
+    int32_t *qpos = (int32_t *)((char *)workspace + align_up((size_t)L * L * 4, 256));
+    int32_t *nval = (int32_t *)((char *)qpos + align_up((size_t)L * 4, 256));
+    st = hip_check(launch_positions(qpos, nval, L, stream), "positions launch");
+    if (st == DSA_OK)
+      st = hip_check(launch_indexer_scores_f32((const float *)a->q_idx, (const float *)a->k_idx, a->w, qpos, L, L,
+                                               a->H_I, a->D_I, sc, L, stream),
+                     "indexer launch");
+    if (st == DSA_OK) st = hip_check(launch_topk(sc, L, nval, L, L, a->k, a->idx, stream), "topk launch");
+  }
+  if (st != DSA_OK) return st;
+  if (a->attn_dt == DSA_BF16)
+    return hip_check(launch_sparse_mla_bf16(a->q, a->kv, a->idx, nullptr, 0, L, L, a->H, a->k, a->sm_scale,
+                                            a->out, a->lse, 1, nullptr, nullptr, stream),
+                     "sparse mla launch");
+  return hip_check(launch_sparse_mla_f32((const float *)a->q, (const float *)a->kv, a->idx, L, L, a->H, a->k,
+                                         a->sm_scale, (float *)a->out, a->lse, stream),
+                   "sparse mla launch");
+}
+
+static dsa_status check_decode(const dsa_decode_args *a) {
+  REQUIRE(a, DSA_ERR_INVALID_ARG, "null args");
+  REQUIRE(a->B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
+  REQUIRE(a->k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(a->k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(a->max_ctx >= 1, DSA_ERR_INVALID_ARG, "max_ctx must be >= 1");
+  REQUIRE(a->max_blocks >= (a->max_ctx + DSA_PAGE - 1) / DSA_PAGE, DSA_ERR_INVALID_ARG,
+          "max_blocks (%d) too small for max_ctx (%d)", a->max_blocks, a->max_ctx);
+  REQUIRE(a->n_pool_rows > 0 && a->n_pool_rows % DSA_PAGE == 0, DSA_ERR_INVALID_ARG,
+          "n_pool_rows must be a positive multiple of 64");
+  REQUIRE(a->H_I == 64 && a->D_I == 128, DSA_ERR_UNSUPPORTED, "decode indexer needs H_I = 64, D_I = 128");
+  REQUIRE(a->H > 0 && a->H % 16 == 0, DSA_ERR_UNSUPPORTED, "decode attention needs H a multiple of 16");
+  REQUIRE(a->sm_scale == a->sm_scale && a->sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (a->B == 0) return DSA_OK;
+  REQUIRE(a->q8 && a->q_scale && a->w && a->q && a->k8_pool && a->ks_pool && a->kv_pool && a->block_table &&
+              a->ctx_len && a->out,
+          DSA_ERR_INVALID_ARG, "null pointer");
+  return DSA_OK;
+}
+
+static int64_t decode_ld(const dsa_decode_args *a) { return (int64_t)align_up((size_t)a->max_ctx, 64); }
+
+size_t dsa_decode_workspace_bytes(const dsa_decode_args *a) {
+  if (!a || a->B <= 0 || a->max_ctx <= 0 || a->k <= 0) return 0;
+  size_t n = align_up((size_t)a->B * decode_ld(a) * 4, 256);
+  if (!a->idx_out) n += align_up((size_t)a->B * a->k * 4, 256);
+  if (a->H > 0 && a->H % 16 == 0) n += mla_ws_bytes(a->B, a->H, a->k);
+  return n;
+}
+
+dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  dsa_status st = check_decode(a);
+  if (st != DSA_OK) return st;
+  if (a->B == 0) return DSA_OK;
+  const size_t need = dsa_decode_workspace_bytes(a);
+  REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
+          workspace ? workspace_bytes : (size_t)0, need);
+  const int64_t ld = decode_ld(a);
+  char *p = (char *)workspace;
+  float *scores = (float *)p;
+  p += align_up((size_t)a->B * ld * 4, 256);
+  int32_t *idx = a->idx_out;
+  if (!idx) {
+    idx = (int32_t *)p;
+    p += align_up((size_t)a->B * a->k * 4, 256);
+  }
+  float *po = nullptr, *pml = nullptr;
+  const int splits = mla_splits(a->B, a->H, a->k);
+  if (splits > 1) mla_ws_split(p, a->B, a->H, a->k, &po, &pml);
+  st = hip_check(launch_decode_indexer(a->q8, a->q_scale, a->w, a->k8_pool, a->ks_pool, a->block_table,
+                                       a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores, ld, stream),
+                 "decode indexer launch");
+  if (st != DSA_OK) return st;
+  st = hip_check(launch_topk(scores, ld, a->ctx_len, a->max_ctx, a->B, a->k, idx, stream), "topk launch");
+  if (st != DSA_OK) return st;
+  return hip_check(launch_sparse_mla_bf16(a->q, a->kv_pool, idx, a->block_table, a->max_blocks, a->n_pool_rows,
+                                          a->B, a->H, a->k, a->sm_scale, a->out, a->lse, splits, po, pml, stream),
+                   "sparse mla launch");
+}
+
+dsa_status dsa_paged_cache_append(const void *latent, const uint8_t *k8, const float *ks, const int32_t *pos,
+                                  int32_t B, int32_t D_I, const int32_t *block_table, int32_t max_blocks,
+                                  void *kv_pool, uint8_t *k8_pool, float *ks_pool, int64_t n_pool_rows,
+                                  hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
+  REQUIRE(max_blocks >= 1, DSA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  REQUIRE(n_pool_rows > 0 && n_pool_rows % DSA_PAGE == 0, DSA_ERR_INVALID_ARG,
+          "n_pool_rows must be a positive multiple of 64");
+  REQUIRE(D_I > 0 && D_I % 16 == 0 && D_I <= 128, DSA_ERR_UNSUPPORTED, "D_I must be a multiple of 16, <= 128");
+  if (B == 0) return DSA_OK;
+  REQUIRE(latent && k8 && ks && pos && block_table && kv_pool && k8_pool && ks_pool, DSA_ERR_INVALID_ARG,
+          "null pointer");
+  return hip_check(launch_cache_append(latent, k8, ks, pos, B, D_I, block_table, max_blocks, n_pool_rows, kv_pool,
+                                       k8_pool, ks_pool, stream),
+                   "cache append launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Paged decode pieces: the indexer over each sequence's FP8 key pages, and the
+// cache append of one new token per sequence.
+//
+// The latent KV cache of MLA (jienda.com, section 2.1: keys and values
+// compressed into a latent space) is paged in 64-token pages; logical
+// position p of sequence b lives in physical row
+// block_table[b][p/64]*64 + p%64 of each pool.
+//
+// Decode indexer: one query (64 heads x 128 E4M3) per sequence against all of
+// its ctx keys.  This streams 132 B per key from HBM (the key payload and its
+// scale) and is bandwidth bound; each wavefront scores one page (64 keys,
+// 8 KB contiguous in the pool), so every page is read exactly once.
+#include "indexer_core.h"
+
+namespace {
+
+constexpr int kPagesPerBlock = 4;  // 4 waves, one page each
+
+// grid: (ceil(max_ctx / 256), B)
+__global__ __launch_bounds__(256) void decode_indexer_kernel(
+    const uint8_t *__restrict__ q8, const float *__restrict__ qs, const float *__restrict__ w,
+    const uint8_t *__restrict__ k8_pool, const float *__restrict__ ks_pool, const int32_t *__restrict__ bt,
+    int max_blocks, const int32_t *__restrict__ ctx_len, int64_t n_pool_rows, float *__restrict__ scores,
+    int64_t ld, int max_ctx) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b = blockIdx.y;
+  const int ctx = min(ctx_len[b], max_ctx);
+  const int page = blockIdx.x * kPagesPerBlock + wave;
+  const int s0 = page * 64;
+  if (s0 >= ctx || page >= max_blocks) return;
+  const int32_t blk = bt[b * max_blocks + page];
+  const int64_t prow = (int64_t)blk * 64;  // first physical row of the page
+  if (blk < 0 || prow + 64 > n_pool_rows) {  // unmapped page: nothing to score
+    if (s0 + lane < ctx) scores[b * ld + s0 + lane] = -INFINITY;
+    return;
+  }
+  IdxQuery<2> Q;
+  idx_load_query<2>(Q, q8 + b * 64 * 128, w + b * 64, qs[b], lane);
+  const uint8_t *pk = k8_pool + prow * 128;
+  i32x8 bb[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      bb[u][kk] = *reinterpret_cast<const i32x8 *>(pk + (u * 32 + (lane & 31)) * 128 + kk * 64 + (lane >> 5) * 32);
+  const float tot = idx_score64<2>(Q, bb);
+  const int s = s0 + lane;
+  if (s < ctx) scores[b * ld + s] = canon_zero(tot * ks_pool[prow + lane]);
+}
+
+// One workgroup per appended token: 72 chunks of latent, 8 of key, 1 scale.
+__global__ __launch_bounds__(128) void cache_append_kernel(const __bf16 *__restrict__ latent,
+                                                           const uint8_t *__restrict__ k8,
+                                                           const float *__restrict__ ks,
+                                                           const int32_t *__restrict__ pos, int D_I,
+                                                           const int32_t *__restrict__ bt, int max_blocks,
+                                                           int64_t n_pool_rows, __bf16 *__restrict__ kv_pool,
+                                                           uint8_t *__restrict__ k8_pool,
+                                                           float *__restrict__ ks_pool) {
+  const int64_t b = blockIdx.x;
+  const int p = pos[b];
+  if (p < 0 || (p >> 6) >= max_blocks) return;  // position outside the table
+  const int32_t blk = bt[b * max_blocks + (p >> 6)];
+  const int64_t row = (int64_t)blk * 64 + (p & 63);
+  if (blk < 0 || row >= n_pool_rows) return;    // unmapped page
+  const int tid = threadIdx.x;
+  if (tid < 72) {
+    *reinterpret_cast<i32x4 *>(kv_pool + row * 576 + tid * 8) =
+        *reinterpret_cast<const i32x4 *>(latent + b * 576 + tid * 8);
+  } else if (tid < 72 + D_I / 16) {
+    const int c = tid - 72;
+    *reinterpret_cast<i32x4 *>(k8_pool + row * D_I + c * 16) =
+        *reinterpret_cast<const i32x4 *>(k8 + b * D_I + c * 16);
+  } else if (tid == 127) {
+    ks_pool[row] = ks[b];
+  }
+}
+
+}  // namespace
+
+namespace dsa {
+hipError_t launch_decode_indexer(const uint8_t *q8, const float *qs, const float *w,
+                                 const uint8_t *k8_pool, const float *ks_pool,
+                                 const int32_t *block_table, int32_t max_blocks,
+                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, int64_t n_pool_rows,
+                                 float *scores, int64_t ld, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  dim3 grid((max_ctx + 64 * kPagesPerBlock - 1) / (64 * kPagesPerBlock), B);
+  hipLaunchKernelGGL(decode_indexer_kernel, grid, dim3(256), 0, s, q8, qs, w, k8_pool, ks_pool, block_table,
+                     max_blocks, ctx_len, n_pool_rows, scores, ld, max_ctx);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_append(const void *latent, const uint8_t *k8, const float *ks,
+                               const int32_t *pos, int32_t B, int32_t D_I,
+                               const int32_t *block_table, int32_t max_blocks, int64_t n_pool_rows,
+                               void *kv_pool, uint8_t *k8_pool, float *ks_pool, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(cache_append_kernel, dim3(B), dim3(128), 0, s, (const __bf16 *)latent, k8, ks, pos, D_I,
+                     block_table, max_blocks, n_pool_rows, (__bf16 *)kv_pool, k8_pool, ks_pool);
+  return hipGetLastError();
+}
+}  // namespace dsa

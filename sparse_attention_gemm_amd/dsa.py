@@ -1,0 +1,197 @@
+"""Thin ctypes binding of libdsa (include/dsa.h), one function per C entry point.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch device tensors (their data pointers are passed through);
+work is enqueued on torch's current HIP stream unless ``stream`` is given.
+A non-OK status raises DSAError carrying dsa_last_error().  There is no CPU
+fallback: without a built libdsa.so, importing the library fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_F32, DSA_BF16, DSA_E4M3 = 0, 1, 2
+STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
+                4: "DSA_ERR_HIP"}
+EXPORTS = (
+    "dsa_last_error", "dsa_version", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select",
+    "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_fwd", "dsa_prefill_workspace_bytes", "dsa_prefill",
+    "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append",
+)
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [("L", _I32), ("H_I", _I32), ("D_I", _I32), ("H", _I32), ("k", _I32),
+                ("idx_dt", ctypes.c_int), ("q_idx", _P), ("q_scale", _P), ("k_idx", _P), ("k_scale", _P),
+                ("w", _P), ("attn_dt", ctypes.c_int), ("q", _P), ("kv", _P), ("sm_scale", _F32),
+                ("idx", _P), ("out", _P), ("lse", _P)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("B", _I32), ("H_I", _I32), ("D_I", _I32), ("H", _I32), ("k", _I32),
+                ("q8", _P), ("q_scale", _P), ("w", _P), ("q", _P),
+                ("k8_pool", _P), ("ks_pool", _P), ("kv_pool", _P), ("n_pool_rows", _I64),
+                ("block_table", _P), ("max_blocks", _I32), ("ctx_len", _P), ("max_ctx", _I32),
+                ("sm_scale", _F32), ("idx_out", _P), ("out", _P), ("lse", _P)]
+
+
+_lib = None
+
+
+def load():
+    """Load libdsa.so (built in-tree by sparse_attention_gemm_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libdsa.so not built ({LIB_PATH}); run python -m sparse_attention_gemm_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    L.dsa_last_error.restype = ctypes.c_char_p
+    L.dsa_version.restype = ctypes.c_char_p
+    L.dsa_quantize_e4m3_per_token.argtypes = [_P, _I64, _I32, _P, _P, _P]
+    L.dsa_indexer_scores.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I64, _P]
+    L.dsa_topk_select.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
+    L.dsa_sparse_mla_workspace_bytes.argtypes = [_I32, _I32, _I32]
+    L.dsa_sparse_mla_workspace_bytes.restype = _SZ
+    L.dsa_sparse_mla_fwd.argtypes = [_P, _P, ctypes.c_int, _P, _I32, _I32, _I64, _I32, _F32, _P, _P, _P, _SZ, _P]
+    L.dsa_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
+    L.dsa_prefill_workspace_bytes.restype = _SZ
+    L.dsa_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _P, _SZ, _P]
+    L.dsa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
+    L.dsa_decode_workspace_bytes.restype = _SZ
+    L.dsa_decode.argtypes = [ctypes.POINTER(DecodeArgs), _P, _SZ, _P]
+    L.dsa_paged_cache_append.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _P, _I64, _P]
+    for name in ("dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
+                 "dsa_prefill", "dsa_decode", "dsa_paged_cache_append"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        raise DSAError(status, load().dsa_last_error().decode())
+
+
+def dsa_version() -> str:
+    return load().dsa_version().decode()
+
+
+def dsa_last_error() -> str:
+    return load().dsa_last_error().decode()
+
+
+def dsa_quantize_e4m3_per_token(x, x8, scale, rows=None, cols=None, stream=None):
+    """x [rows, cols] fp32 -> x8 [rows, cols] uint8 (E4M3), scale [rows] fp32."""
+    rows = x.numel() // x.shape[-1] if rows is None else rows
+    cols = x.shape[-1] if cols is None else cols
+    _check(load().dsa_quantize_e4m3_per_token(_ptr(x), rows, cols, _ptr(x8), _ptr(scale), _stream(stream)))
+
+
+def dsa_indexer_scores(q, q_scale, k, k_scale, w, q_pos, scores, dt, T=None, S=None, H_I=None, D_I=None,
+                       ld_scores=None, stream=None):
+    T = q.shape[0] if T is None else T
+    S = k.shape[0] if S is None else S
+    H_I = q.shape[1] if H_I is None else H_I
+    D_I = q.shape[2] if D_I is None else D_I
+    ld = scores.stride(0) if ld_scores is None else ld_scores
+    _check(load().dsa_indexer_scores(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(q_pos),
+                                     T, S, H_I, D_I, dt, _ptr(scores), ld, _stream(stream)))
+
+
+def dsa_topk_select(scores, n_valid, k, idx, T=None, ld_scores=None, workspace=None, stream=None):
+    T = scores.shape[0] if T is None else T
+    ld = scores.stride(0) if ld_scores is None else ld_scores
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_topk_select(_ptr(scores), ld, _ptr(n_valid), T, k, _ptr(idx), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))
+
+
+def dsa_sparse_mla_workspace_bytes(T: int, H: int, k: int) -> int:
+    return int(load().dsa_sparse_mla_workspace_bytes(T, H, k))
+
+
+def dsa_sparse_mla_fwd(q, kv, idx, sm_scale, out, lse=None, dt=None, workspace=None, N=None, stream=None):
+    T, H = q.shape[0], q.shape[1]
+    k = idx.shape[1]
+    N = kv.shape[0] if N is None else N
+    if dt is None:
+        dt = DSA_BF16 if q.dtype == torch.bfloat16 else DSA_F32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_sparse_mla_fwd(_ptr(q), _ptr(kv), dt, _ptr(idx), T, H, N, k, float(sm_scale), _ptr(out),
+                                     _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def make_prefill_args(L, H_I, D_I, H, k, idx_dt, q_idx, q_scale, k_idx, k_scale, w, attn_dt, q, kv, sm_scale,
+                      idx, out, lse=None) -> PrefillArgs:
+    return PrefillArgs(L, H_I, D_I, H, k, idx_dt, _ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w),
+                       attn_dt, _ptr(q), _ptr(kv), float(sm_scale), _ptr(idx), _ptr(out), _ptr(lse))
+
+
+def dsa_prefill_workspace_bytes(args: PrefillArgs) -> int:
+    return int(load().dsa_prefill_workspace_bytes(ctypes.byref(args)))
+
+
+def dsa_prefill(args: PrefillArgs, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_prefill(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def make_decode_args(B, H_I, D_I, H, k, q8, q_scale, w, q, k8_pool, ks_pool, kv_pool, n_pool_rows, block_table,
+                     max_blocks, ctx_len, max_ctx, sm_scale, out, lse=None, idx_out=None) -> DecodeArgs:
+    return DecodeArgs(B, H_I, D_I, H, k, _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(q), _ptr(k8_pool), _ptr(ks_pool),
+                      _ptr(kv_pool), n_pool_rows, _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx,
+                      float(sm_scale), _ptr(idx_out), _ptr(out), _ptr(lse))
+
+
+def dsa_decode_workspace_bytes(args: DecodeArgs) -> int:
+    return int(load().dsa_decode_workspace_bytes(ctypes.byref(args)))
+
+
+def dsa_decode(args: DecodeArgs, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_decode(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_paged_cache_append(latent, k8, ks, pos, block_table, kv_pool, k8_pool, ks_pool, B=None, D_I=None,
+                           max_blocks=None, n_pool_rows=None, stream=None):
+    B = latent.shape[0] if B is None else B
+    D_I = k8.shape[-1] if D_I is None else D_I
+    max_blocks = block_table.shape[1] if max_blocks is None else max_blocks
+    n_pool_rows = kv_pool.numel() // 576 if n_pool_rows is None else n_pool_rows
+    _check(load().dsa_paged_cache_append(_ptr(latent), _ptr(k8), _ptr(ks), _ptr(pos), B, D_I, _ptr(block_table),
+                                         max_blocks, _ptr(kv_pool), _ptr(k8_pool), _ptr(ks_pool), n_pool_rows,
+                                         _stream(stream)))

@@ -1,0 +1,98 @@
+"""Comparison rules between the GPU path and the fp64 oracle.
+
+Tolerances (stated once, used by every parity test):
+  * index scores: |gpu - ora| <= 1e-3 * max(|ora|, A) + (D_I + H_I + 2) u C,
+    where A is the same score with every head weight replaced by its
+    absolute value (the sum of the absolute terms; without cancellation this
+    is plain 1e-3 relative), u = 2^-24, and C = sum_j |w_j| sum_d |q_jd k_d|
+    (scales included).  The second term is the worst-case rounding of fp32
+    dot products of D_I terms and a sum over H_I heads: it only matters where
+    a head's dot product is so close to zero that fp32 rounding moves it
+    across the ReLU kink.
+  * top-k sets: identical, except that a position may differ between the two
+    sets only if its oracle score is within 1e-4 * max(1, |tau|) of the
+    oracle's k-th score tau.  Counts, range, uniqueness and ascending order
+    are checked exactly.
+  * attention: bf16 max|do| <= 2e-2 and <= 1e-2 * max|o_ora|, |dlse| <= 1e-3;
+    fp32 max|do| <= 1e-4 and <= 1e-5 * max|o_ora|, |dlse| <= 1e-5.
+    Attention is always checked with the GPU's own selection fed to the
+    oracle, since a legal tie swap changes the output.
+"""
+import numpy as np
+
+SCORE_RTOL = 1e-3
+TIE_RTOL = 1e-4
+
+
+def abs_payload(x):
+    """|x| for fp32 arrays, or the E4M3 payload with its sign bit cleared."""
+    x = np.asarray(x)
+    return (x & 0x7F).astype(np.uint8) if x.dtype == np.uint8 else np.abs(x)
+
+
+def oracle_score_bounds(ora, q, k, w, pos, rows=None, q_scale=None, k_scale=None):
+    """(scores, scores with |w|, scores with |w|,|q|,|k|) from the oracle."""
+    w = np.asarray(w)
+    o = ora.indexer_rows(q, k, w, pos, rows=rows, q_scale=q_scale, k_scale=k_scale)
+    a = ora.indexer_rows(q, k, np.abs(w), pos, rows=rows, q_scale=q_scale, k_scale=k_scale)
+    m = ora.indexer_rows(abs_payload(q), abs_payload(k), np.abs(w), pos, rows=rows, q_scale=q_scale,
+                         k_scale=k_scale)
+    return o, a, m
+
+
+def check_scores(gpu, ora, ora_abs, ora_mag, n_terms, label=""):
+    """ora_abs: oracle score with |w|; ora_mag: with |w|, |q|, |k|;
+    n_terms = D_I + H_I."""
+    gpu = np.asarray(gpu, np.float64)
+    fin = np.isfinite(ora)
+    assert np.array_equal(np.isfinite(gpu), fin), f"{label}: -inf pattern differs"
+    assert np.all(gpu[~fin] == -np.inf)
+    err = np.abs(gpu[fin] - ora[fin])
+    bound = SCORE_RTOL * np.maximum(np.abs(ora[fin]), ora_abs[fin]) + (n_terms + 2) * 2.0 ** -24 * ora_mag[fin]
+    bad = err > bound
+    assert not bad.any(), (f"{label}: {bad.sum()} scores out of tolerance; worst err {err.max():.3e}, "
+                           f"bound there {bound[np.argmax(err)]:.3e}")
+    return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+
+
+def check_topk_row(gpu_idx, ora_scores_row, n, k, label=""):
+    """gpu_idx: int array [k]; ora_scores_row: fp64 scores of positions 0..n-1."""
+    K = min(k, n)
+    g = np.asarray(gpu_idx)
+    assert np.all(g[K:] == -1), f"{label}: padding"
+    sel = g[:K]
+    assert np.all(sel >= 0) and np.all(sel < n), f"{label}: out of range"
+    assert np.all(np.diff(sel) > 0), f"{label}: not strictly ascending"
+    if K == n:
+        assert np.array_equal(sel, np.arange(n))
+        return 0
+    s = ora_scores_row[:n]
+    order = np.lexsort((-np.arange(n), -s))  # score desc, then position desc
+    ref = np.sort(order[:K])
+    tau = s[order[K - 1]]
+    diff = np.setxor1d(sel, ref)
+    if diff.size:
+        tol = TIE_RTOL * max(1.0, abs(tau))
+        far = np.abs(s[diff] - tau) > tol
+        assert not far.any(), (f"{label}: {far.sum()} selection differences beyond the tie band "
+                               f"(tau={tau}, worst |s-tau|={np.abs(s[diff] - tau).max():.3e})")
+    return int(diff.size)
+
+
+def check_attention(o_gpu, lse_gpu, o_ora, lse_ora, dtype, label=""):
+    o_gpu = np.asarray(o_gpu, np.float64)
+    lse_gpu = np.asarray(lse_gpu, np.float64)
+    d = np.abs(o_gpu - o_ora).max() if o_ora.size else 0.0
+    omax = np.abs(o_ora).max() if o_ora.size else 0.0
+    if dtype == "bf16":
+        abs_tol, rel_tol, lse_tol = 2e-2, 1e-2, 1e-3
+    else:
+        abs_tol, rel_tol, lse_tol = 1e-4, 1e-5, 1e-5
+    assert d <= abs_tol, f"{label}: max|do| {d:.3e} > {abs_tol}"
+    assert d <= rel_tol * omax + 1e-30, f"{label}: max|do| {d:.3e} > {rel_tol} * max|o| ({omax:.3e})"
+    fin = np.isfinite(lse_ora)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), f"{label}: lse -inf pattern"
+    if fin.any():
+        dl = np.abs(lse_gpu[fin] - lse_ora[fin]).max()
+        assert dl <= lse_tol, f"{label}: max|dlse| {dl:.3e} > {lse_tol}"
+    return d, omax

@@ -1,0 +1,192 @@
+"""The C ABI on the host, no GPU needed: the library loads, exports every
+function include/dsa.h declares, and rejects bad arguments with the right
+status before making any HIP call (nothing here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+FAKE = 0x1000  # a non-null pointer value; never dereferenced by failing validation
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_gemm_amd import build, dsa as d
+    if not os.path.exists(d.LIB_PATH):
+        build.build()
+    d.load()
+    return d
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd", "dsa_prefill", "dsa_decode",
+              "dsa_quantize_e4m3_per_token", "dsa_paged_cache_append", "dsa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(dsa):
+    lib = ctypes.CDLL(dsa.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(_declared()) == set(dsa.EXPORTS)
+    assert dsa.dsa_version().startswith("libdsa")
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_quantize_validation(dsa):
+    L = dsa.load()
+    assert L.dsa_quantize_e4m3_per_token(FAKE, -1, 128, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_quantize_e4m3_per_token(FAKE, 4, 0, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_quantize_e4m3_per_token(None, 4, 128, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_quantize_e4m3_per_token(FAKE, 4, 130, FAKE, FAKE, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert "multiple of 4" in dsa.dsa_last_error()
+    # nothing to do is not an error (and launches nothing)
+    assert L.dsa_quantize_e4m3_per_token(None, 0, 128, None, None, None) == dsa.DSA_OK
+
+
+def test_indexer_validation(dsa):
+    L = dsa.load()
+    f = L.dsa_indexer_scores
+    ok_args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 100, 64, 128, dsa.DSA_E4M3, FAKE, 100, None]
+    bad = list(ok_args)
+    bad[6] = -1
+    assert f(*bad) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(ok_args)
+    bad[12] = 50  # ld < S
+    assert f(*bad) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(ok_args)
+    bad[1] = None  # E4M3 without q scale
+    assert f(*bad) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(ok_args)
+    bad[9] = 64  # D_I 64 with E4M3
+    assert f(*bad) == dsa.DSA_ERR_UNSUPPORTED
+    bad = list(ok_args)
+    bad[8] = 48
+    assert f(*bad) == dsa.DSA_ERR_UNSUPPORTED
+    bad = list(ok_args)
+    bad[10] = dsa.DSA_BF16
+    assert f(*bad) == dsa.DSA_ERR_UNSUPPORTED
+    bad = list(ok_args)
+    bad[10], bad[8] = dsa.DSA_F32, 65
+    assert f(*bad) == dsa.DSA_ERR_UNSUPPORTED
+    bad = list(ok_args)
+    bad[11] = None
+    assert f(*bad) == dsa.DSA_ERR_INVALID_ARG
+    empty = list(ok_args)
+    empty[6] = 0
+    assert f(*empty) == dsa.DSA_OK
+
+
+def test_topk_validation(dsa):
+    f = dsa.load().dsa_topk_select
+    assert f(FAKE, 100, FAKE, 4, 0, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert f(FAKE, 100, FAKE, 4, 2049, FAKE, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(FAKE, 100, None, 4, 16, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert f(FAKE, -1, FAKE, 4, 16, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert f(None, 100, None, 0, 16, None, None, 0, None) == dsa.DSA_OK
+
+
+def test_sparse_mla_validation(dsa):
+    L = dsa.load()
+    f = L.dsa_sparse_mla_fwd
+    base = [FAKE, FAKE, dsa.DSA_BF16, FAKE, 64, 128, 1000, 2048, 0.07, FAKE, FAKE, None, 0, None]
+    b = list(base)
+    b[5] = 24  # H not a multiple of 16 for bf16
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[7] = 4096
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[8] = -1.0
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[8] = float("nan")
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[2] = dsa.DSA_E4M3
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[11], b[12] = FAKE, 16  # a workspace smaller than required
+    need = L.dsa_sparse_mla_workspace_bytes(64, 128, 2048)
+    assert need > 16
+    assert f(*b) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_sparse_mla_workspace_bytes(100000, 128, 2048) == 0  # enough queries: no split
+
+
+def test_prefill_validation(dsa):
+    L = dsa.load()
+    a = dsa.make_prefill_args(1000, 64, 128, 128, 2048, dsa.DSA_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE, dsa.DSA_BF16,
+                              FAKE, FAKE, 0.07, FAKE, FAKE, FAKE)
+    assert L.dsa_prefill(None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    a.H_I = 32
+    assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    a.H_I = 64
+    a.k = 0
+    assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    a.k = 2048
+    a.q_scale = None
+    assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    a.q_scale = FAKE
+    a.H = 8
+    assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    a.H = 128
+    a.idx_dt = dsa.DSA_F32
+    a.q_scale = a.k_scale = None
+    need = dsa.dsa_prefill_workspace_bytes(a)
+    assert need >= 1000 * 1000 * 4
+    assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_prefill(ctypes.byref(a), FAKE, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    a.L = 20000
+    assert L.dsa_prefill(ctypes.byref(a), FAKE, 1 << 40, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_decode_validation(dsa):
+    L = dsa.load()
+    a = dsa.make_decode_args(4, 64, 128, 128, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64 * 100, FAKE, 100,
+                             FAKE, 6400, 0.07, FAKE, FAKE, None)
+    need = dsa.dsa_decode_workspace_bytes(a)
+    assert need >= 4 * 6400 * 4 + 4 * 2048 * 4
+    assert L.dsa_decode(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_WORKSPACE
+    a.max_blocks = 50
+    assert L.dsa_decode(ctypes.byref(a), FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG
+    a.max_blocks = 100
+    a.n_pool_rows = 6401
+    assert L.dsa_decode(ctypes.byref(a), FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG
+    a.n_pool_rows = 6400
+    a.H = 120
+    assert L.dsa_decode(ctypes.byref(a), FAKE, need, None) == dsa.DSA_ERR_UNSUPPORTED
+    a.H = 128
+    a.ctx_len = None
+    assert L.dsa_decode(ctypes.byref(a), FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_cache_append_validation(dsa):
+    f = dsa.load().dsa_paged_cache_append
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, FAKE, 10, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 120, FAKE, 10, FAKE, FAKE, FAKE, 640, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(FAKE, None, FAKE, FAKE, 4, 128, FAKE, 10, FAKE, FAKE, FAKE, 640, None) == dsa.DSA_ERR_INVALID_ARG
+    assert f(None, None, None, None, 0, 128, None, 10, None, None, None, 640, None) == dsa.DSA_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    from sparse_attention_gemm_amd import dsa as d
+    monkeypatch.setattr(d, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(d, "_lib", None)
+    with pytest.raises(ImportError):
+        d.load()
+    importlib.reload(d)

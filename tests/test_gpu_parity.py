@@ -1,0 +1,395 @@
+"""GPU parity of every hot-path step against the fp64 oracle, through the C ABI.
+
+Sizes here finish in seconds on the oracle yet span several tiles and ragged
+tails; the full-size workloads are in test_gpu_fullsize.py.  Each test prints
+its case before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.parity import check_attention, check_scores, check_topk_row, oracle_score_bounds
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_gemm_amd import dsa as d
+    d.load()
+    return d
+
+
+def _quant_gpu(dsa, x):
+    rows, cols = x.numel() // x.shape[-1], x.shape[-1]
+    x8 = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(x.shape[:-1], dtype=torch.float32, device=DEV)
+    xd = x.to(DEV).contiguous()
+    dsa.dsa_quantize_e4m3_per_token(xd, x8, sc, rows=rows, cols=cols)
+    torch.cuda.synchronize()
+    return x8.cpu(), sc.cpu()
+
+
+# ------------------------------------------------------------------ A0
+def test_quantize_bit_exact(dsa, ora):
+    _say("quantize 300x8192 + 1000x128 + sweep")
+    for shape in ((300, 64 * 128), (1000, 128), (7, 4)):
+        x = synth.normal(21, 1, shape) * 3.0
+        x[3 % shape[0]] = 0.0
+        g8, gs = _quant_gpu(dsa, x)
+        o8, os_ = ora.quantize_rows(x.numpy())
+        assert np.array_equal(gs.numpy(), os_), f"scales differ for {shape}"
+        assert np.array_equal(g8.numpy(), o8), f"payload differs for {shape}: {(g8.numpy() != o8).sum()}"
+    # sweep the encoder: rows whose amax is 448 (scale 1) carry arbitrary values
+    grid = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float()
+    grid = grid[torch.isfinite(grid) & (grid >= 0)].unique().double()
+    mids = (grid[1:] + grid[:-1]) / 2
+    vals = torch.cat([grid, mids, -mids, synth.normal(5, 9, (20000,)).double() * 30]).float()
+    vals = vals[vals.abs() < 448]
+    n = (vals.numel() + 126) // 127
+    rows = torch.zeros(n * 127, dtype=torch.float32)
+    rows[:vals.numel()] = vals
+    rows = torch.cat([rows.view(n, 127), torch.full((n, 1), 448.0)], dim=1)
+    g8, gs = _quant_gpu(dsa, rows)
+    o8, os_ = ora.quantize_rows(rows.numpy())
+    assert np.all(os_ == 1.0) and np.array_equal(gs.numpy(), os_)
+    assert np.array_equal(g8.numpy(), o8)
+
+
+# ------------------------------------------------------------------ A1
+def _indexer_case(seed, T, S, H_I, fp8=True, pos_offset=0):
+    q = synth.normal(seed, synth.T_QI, (T, H_I, 128))
+    k = synth.normal(seed, synth.T_KI, (S, 128))
+    w = synth.normal(seed, synth.T_W, (T, H_I), std=0.5)
+    pos = (torch.arange(T, dtype=torch.int32) * max(1, S // max(T, 1)) + pos_offset).clamp(max=S - 1)
+    return q, k, w, pos
+
+
+def _gpu_scores(dsa, q8, qs, k8, ks, w, pos, S, dt):
+    T = q8.shape[0]
+    sc = torch.full((T, S + 5), 7.0, dtype=torch.float32, device=DEV)  # ld > S, tail untouched
+    args = [t.to(DEV).contiguous() if t is not None else None for t in (q8, qs, k8, ks, w, pos)]
+    dsa.dsa_indexer_scores(args[0], args[1], args[2], args[3], args[4], args[5], sc, dt, S=S)
+    torch.cuda.synchronize()
+    out = sc.cpu()
+    assert torch.all(out[:, S:] == 7.0), "wrote past S"
+    return out[:, :S].double().numpy()
+
+
+@pytest.mark.parametrize("H_I", [64, 32])
+def test_indexer_fp8_scores(dsa, ora, H_I):
+    T, S = 37, 1000  # ragged: S not a multiple of 64 or 512
+    _say(f"indexer fp8 T={T} S={S} H_I={H_I}")
+    q, k, w, pos = _indexer_case(3, T, S, H_I)
+    q8, qs = ora.quantize_rows(q.view(T, -1).numpy())
+    k8, ks = ora.quantize_rows(k.numpy())
+    q8 = torch.from_numpy(q8).view(T, H_I, 128)
+    g = _gpu_scores(dsa, q8, torch.from_numpy(qs), torch.from_numpy(k8), torch.from_numpy(ks), w, pos, S,
+                    dsa.DSA_E4M3)
+    o, a, m = oracle_score_bounds(ora, q8.numpy(), k8, w.numpy(), pos, q_scale=qs, k_scale=ks)
+    check_scores(g, o, a, m, 128 + H_I, "fp8 scores")
+
+
+def test_indexer_fp8_exact_arithmetic(dsa, ora):
+    """E4M3 payloads in {0,+-1,+-2}, scales 1, w in {+-1,+-0.5}: every partial
+    sum is exact in fp32, so scores must be bit-identical and the top-k
+    (full of exact ties) identical under the position tie rule."""
+    T, S, H_I = 70, 700, 64
+    _say("indexer exact arithmetic")
+    lut = torch.tensor([0xC0, 0xB8, 0x00, 0x38, 0x40], dtype=torch.uint8)  # -2,-1,0,1,2
+    qi = synth.randint(4, 1, (T, H_I, 128), 0, 4)
+    ki = synth.randint(4, 2, (S, 128), 0, 4)
+    q8, k8 = lut[qi], lut[ki]
+    w = torch.tensor([-1.0, -0.5, 0.5, 1.0])[synth.randint(4, 3, (T, H_I), 0, 3)]
+    ones_t, ones_s = torch.ones(T), torch.ones(S)
+    pos = torch.arange(T, dtype=torch.int32) * 10
+    g = _gpu_scores(dsa, q8, ones_t, k8, ones_s, w, pos, S, dsa.DSA_E4M3)
+    o = ora.indexer_rows(q8.numpy(), k8.numpy(), w, pos, q_scale=ones_t, k_scale=ones_s)
+    assert np.array_equal(g, o)
+    # top-k over these exactly tied scores: identical sets
+    sc = torch.from_numpy(g).float().to(DEV)
+    nval = (pos + 1).to(DEV)
+    for kk in (5, 64, 256):
+        idx = torch.empty((T, kk), dtype=torch.int32, device=DEV)
+        dsa.dsa_topk_select(sc, nval, kk, idx)
+        torch.cuda.synchronize()
+        ref, _ = ora.topk_rows(np.where(np.isinf(o), 0, o), (pos + 1).numpy(), kk)
+        assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_indexer_f32_tiny_config(dsa, ora):
+    cfg = synth.CONFIGS["tiny"]
+    _say("indexer f32 tiny config L=2048")
+    q, k, w = synth.prefill_indexer_inputs(cfg)
+    pos = torch.arange(cfg.L, dtype=torch.int32)
+    g = _gpu_scores(dsa, q, None, k, None, w, pos, cfg.L, dsa.DSA_F32)
+    rows = np.arange(0, cfg.L, 7)
+    o, a, m = oracle_score_bounds(ora, q.numpy(), k.numpy(), w.numpy(), pos, rows=rows)
+    check_scores(g[rows], o, a, m, cfg.D_I + cfg.H_I, "f32 scores")
+
+
+# ------------------------------------------------------------------ A2
+@pytest.mark.parametrize("n,k", [(5000, 2048), (40000, 2048), (3000, 256), (2047, 2048), (131072, 2048),
+                                 (700, 1)])
+def test_topk_matches_oracle_on_same_scores(dsa, ora, n, k):
+    """Same fp32 scores on both sides: the selection must be identical."""
+    _say(f"topk n={n} k={k}")
+    T = 3
+    sc = synth.normal(7, 1, (T, n))
+    sc[1] = torch.round(sc[1] * 4) / 4  # heavy ties
+    sc[2, : n // 2] = 0.0                # a block of exact zeros
+    nv = torch.tensor([n, n - 17, max(1, n // 3)], dtype=torch.int32)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    scd, nvd = sc.to(DEV), nv.to(DEV)
+    dsa.dsa_topk_select(scd, nvd, k, idx)
+    torch.cuda.synchronize()
+    ref, _ = ora.topk_rows(sc.double().numpy(), nv.numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_topk_negative_zero_and_all_equal(dsa, ora):
+    _say("topk -0 / all equal")
+    n, k = 5000, 300
+    sc = torch.zeros((2, n))
+    sc[0, ::2] = -0.0
+    sc[1] = -3.5
+    idx = torch.empty((2, k), dtype=torch.int32, device=DEV)
+    scd, nvd = sc.to(DEV), torch.tensor([n, n], dtype=torch.int32, device=DEV)
+    dsa.dsa_topk_select(scd, nvd, k, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert np.array_equal(got[0], np.arange(n - k, n))
+    assert np.array_equal(got[1], np.arange(n - k, n))
+
+
+# ------------------------------------------------------------------ A3
+def _mla_gpu(dsa, q, kv, idx, scale, dtype, use_ws=False):
+    T, H = q.shape[0], q.shape[1]
+    qd, kvd, idd = q.to(DEV), kv.to(DEV), idx.to(DEV)
+    out = torch.empty((T, H, 512), dtype=q.dtype, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    ws = None
+    if use_ws:
+        nb = dsa.dsa_sparse_mla_workspace_bytes(T, H, idx.shape[1])
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV)
+    dsa.dsa_sparse_mla_fwd(qd, kvd, idd, scale, out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    return out.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("H,k,use_ws,qstd", [(128, 2048, False, 1.0), (128, 2048, True, 40.0), (16, 256, False, 1.0),
+                                             (64, 100, True, 40.0), (32, 48, False, 1.0)])
+def test_sparse_mla_bf16(dsa, ora, H, k, use_ws, qstd):
+    N, T = 5000, 6
+    _say(f"sparse mla bf16 H={H} k={k} ws={use_ws} qstd={qstd}")
+    q = synth.normal(11, 1, (T, H, 576), std=qstd).to(torch.bfloat16)
+    kv = synth.normal(11, 2, (N, 576), std=1 / 24).to(torch.bfloat16)
+    idx = torch.stack([synth.permutation(11, 10 + t, N)[:k] for t in range(T)]).to(torch.int32)
+    idx[1, k // 2:] = -1          # ragged selection
+    idx[2, :] = -1                # empty selection
+    idx[3, 5] = N + 3             # out of range: skipped
+    idx[4] = torch.sort(idx[4]).values
+    g, gl = _mla_gpu(dsa, q, kv, idx, 1 / math.sqrt(192), "bf16", use_ws)
+    ref_idx = idx.clone()
+    ref_idx[3, 5] = -1
+    o, l = ora.sparse_mla_rows(q, kv, ref_idx.numpy(), 1 / math.sqrt(192))
+    assert np.all(g[2] == 0) and np.all(np.isneginf(gl[2]))
+    check_attention(g, gl, o, l, "bf16", "mla bf16")
+
+
+def test_sparse_mla_f32_tiny_config(dsa, ora):
+    cfg = synth.CONFIGS["tiny"]
+    _say("sparse mla f32 tiny config")
+    q = synth.prefill_attn_q(cfg)
+    kv = synth.prefill_latent(cfg)
+    # selections: causal windows of varied length
+    L, k = cfg.L, cfg.k
+    idx = torch.full((L, k), -1, dtype=torch.int32)
+    for t in range(L):
+        n = min(k, t + 1)
+        idx[t, :n] = torch.arange(t + 1 - n, t + 1)
+    g, gl = _mla_gpu(dsa, q, kv, idx, cfg.sm_scale, "f32")
+    rows = np.arange(0, L, 13)
+    o, l = ora.sparse_mla_rows(q, kv, idx.numpy(), cfg.sm_scale, rows=rows)
+    check_attention(g[rows], gl[rows], o, l, "f32", "mla f32")
+
+
+# ------------------------------------------------------------------ prefill
+def _prefill_inputs(cfg, dev=DEV):
+    q_i, k_i, w = synth.prefill_indexer_inputs(cfg)
+    q = synth.prefill_attn_q(cfg)
+    kv = synth.prefill_latent(cfg)
+    return q_i, k_i, w, q, kv
+
+
+def _run_prefill(dsa, cfg, q_i, k_i, w, q, kv):
+    L = cfg.L
+    t = {}
+    t["w"] = w.to(DEV)
+    t["q"], t["kv"] = q.to(DEV), kv.to(DEV)
+    if cfg.fp8_indexer:
+        t["q8"] = torch.empty((L, cfg.H_I, cfg.D_I), dtype=torch.uint8, device=DEV)
+        t["qs"] = torch.empty(L, dtype=torch.float32, device=DEV)
+        t["k8"] = torch.empty((L, cfg.D_I), dtype=torch.uint8, device=DEV)
+        t["ks"] = torch.empty(L, dtype=torch.float32, device=DEV)
+        qi_d, ki_d = q_i.to(DEV), k_i.to(DEV)
+        dsa.dsa_quantize_e4m3_per_token(qi_d, t["q8"], t["qs"], rows=L, cols=cfg.H_I * cfg.D_I)
+        dsa.dsa_quantize_e4m3_per_token(ki_d, t["k8"], t["ks"], rows=L, cols=cfg.D_I)
+        qa, qsa, ka, ksa, idt = t["q8"], t["qs"], t["k8"], t["ks"], dsa.DSA_E4M3
+    else:
+        t["qi"], t["ki"] = q_i.to(DEV), k_i.to(DEV)
+        qa, qsa, ka, ksa, idt = t["qi"], None, t["ki"], None, dsa.DSA_F32
+    adt = dsa.DSA_BF16 if cfg.attn_dtype == "bf16" else dsa.DSA_F32
+    t["idx"] = torch.empty((L, cfg.k), dtype=torch.int32, device=DEV)
+    t["out"] = torch.empty((L, cfg.H, 512), dtype=q.dtype, device=DEV)
+    t["lse"] = torch.empty((L, cfg.H), dtype=torch.float32, device=DEV)
+    args = dsa.make_prefill_args(L, cfg.H_I, cfg.D_I, cfg.H, cfg.k, idt, qa, qsa, ka, ksa, t["w"], adt, t["q"],
+                                 t["kv"], cfg.sm_scale, t["idx"], t["out"], t["lse"])
+    nb = dsa.dsa_prefill_workspace_bytes(args)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV) if nb else None
+    dsa.dsa_prefill(args, ws)
+    torch.cuda.synchronize()
+    return t
+
+
+def _check_prefill_rows(ora, cfg, q_i, k_i, w, q, kv, t, rows, label):
+    L = cfg.L
+    pos = np.arange(L, dtype=np.int32)
+    if cfg.fp8_indexer:
+        q8, qs = ora.quantize_rows(q_i.view(L, -1).numpy())
+        k8, ks = ora.quantize_rows(k_i.numpy())
+        assert np.array_equal(t["q8"].cpu().view(L, -1).numpy(), q8)
+        assert np.array_equal(t["k8"].cpu().numpy(), k8)
+        sc = ora.indexer_rows(q8.reshape(L, cfg.H_I, cfg.D_I), k8, w, pos, rows=rows, q_scale=qs, k_scale=ks)
+    else:
+        sc = ora.indexer_rows(q_i.numpy(), k_i.numpy(), w, pos, rows=rows)
+    gidx = t["idx"].cpu().numpy()
+    diffs = 0
+    for i, r in enumerate(rows):
+        diffs += check_topk_row(gidx[r], sc[i], r + 1, cfg.k, f"{label} row {r}")
+    o, l = ora.sparse_mla_rows(q, kv, gidx, cfg.sm_scale, rows=rows)
+    g = t["out"].float().cpu().double().numpy()[rows]
+    gl = t["lse"].cpu().double().numpy()[rows]
+    check_attention(g, gl, o, l, cfg.attn_dtype, label)
+    return diffs
+
+
+def test_prefill_tiny_fp32_config(dsa, ora):
+    cfg = synth.CONFIGS["tiny"]
+    _say("prefill tiny fp32 L=2048 (unfused path)")
+    ins = _prefill_inputs(cfg)
+    t = _run_prefill(dsa, cfg, *ins)
+    rows = np.unique(np.concatenate([np.arange(0, cfg.L, 37), [0, 1, 255, 256, 257, 2047]]))
+    _check_prefill_rows(ora, cfg, *ins, t, rows, "tiny fp32")
+
+
+@pytest.mark.parametrize("L,k,H", [(1000, 256, 16), (777, 64, 32), (4500, 2048, 128), (130, 2048, 16)])
+def test_prefill_fused_fp8(dsa, ora, L, k, H):
+    cfg = synth.scaled_down(synth.CONFIGS["prefill16k"], L=L, k=k, H=H, seed=5)
+    _say(f"prefill fused fp8 L={L} k={k} H={H}")
+    ins = _prefill_inputs(cfg)
+    t = _run_prefill(dsa, cfg, *ins)
+    rows = np.unique(np.concatenate([np.arange(0, L, max(1, L // 40)), [0, 1, k - 1, k, k + 1, L - 1]]))
+    rows = rows[rows < L]
+    _check_prefill_rows(ora, cfg, *ins, t, rows, f"prefill L={L}")
+    # the fused selection equals top-k of the unfused score matrix
+    sc = torch.empty((L, L), dtype=torch.float32, device=DEV)
+    pos = torch.arange(L, dtype=torch.int32, device=DEV)
+    dsa.dsa_indexer_scores(t["q8"], t["qs"], t["k8"], t["ks"], t["w"], pos, sc, dsa.DSA_E4M3)
+    idx2 = torch.empty((L, k), dtype=torch.int32, device=DEV)
+    nval = pos + 1
+    dsa.dsa_topk_select(sc, nval, k, idx2)
+    torch.cuda.synchronize()
+    bad = (idx2 != t["idx"]).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"fused and unfused selections differ in {len(bad)} rows, first {bad[:5]}"
+
+
+
+# ------------------------------------------------------------------ decode
+def _decode_case(cfg, seqs=None):
+    ctx = synth.decode_ctx(cfg)
+    bt, nb = synth.decode_block_table(cfg, ctx)
+    k8p, ksp, kvp = synth.build_decode_pools(cfg, ctx, bt, nb, seqs=seqs)
+    q8, qs, w, q = synth.decode_queries(cfg)
+    return ctx, bt, nb, (k8p, ksp, kvp), (q8, qs, w, q)
+
+
+def _run_decode(dsa, cfg, ctx, bt, nb, pools, qside, with_idx=True):
+    k8p, ksp, kvp = [p.to(DEV) for p in pools]
+    q8, qs, w, q = [x.to(DEV) for x in qside]
+    ctxd, btd = ctx.to(torch.int32).to(DEV), bt.to(DEV)
+    out = torch.empty((cfg.B, cfg.H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=DEV)
+    idx = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=DEV) if with_idx else None
+    args = dsa.make_decode_args(cfg.B, cfg.H_I, cfg.D_I, cfg.H, cfg.k, q8, qs, w, q, k8p, ksp, kvp, nb * 64, btd,
+                                bt.shape[1], ctxd, int(ctx.max()), cfg.sm_scale, out, lse, idx)
+    ws = torch.empty(dsa.dsa_decode_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    dsa.dsa_decode(args, ws)
+    torch.cuda.synchronize()
+    keep = (k8p, ksp, kvp, q8, qs, w, q, ctxd, btd, ws)
+    del keep
+    return out, lse, idx
+
+
+@pytest.mark.parametrize("B,lo,hi,k,shuffled", [(5, 100, 3000, 256, True), (4, 2000, 2100, 2048, False),
+                                                (3, 1, 70, 64, True), (6, 4096, 9000, 2048, True)])
+def test_decode_paged(dsa, ora, B, lo, hi, k, shuffled):
+    cfg = synth.DecodeConfig("t", B, lo, hi, 64, 128, 128, k, 9, shuffled)
+    _say(f"decode B={B} ctx=[{lo},{hi}] k={k} shuffled={shuffled}")
+    ctx, bt, nb, pools, qside = _decode_case(cfg)
+    out, lse, idx = _run_decode(dsa, cfg, ctx, bt, nb, pools, qside)
+    gidx = idx.cpu().numpy()
+    q8, qs, w, q = qside
+    for b in range(B):
+        c = int(ctx[b])
+        kb, sb = synth.decode_seq_keys(cfg, b, c)
+        sc = ora.indexer_rows(q8[b:b + 1], kb, w[b:b + 1], np.array([c - 1], np.int32), q_scale=qs[b:b + 1],
+                              k_scale=sb)
+        check_topk_row(gidx[b], sc[0], c, k, f"decode b={b}")
+        lat = synth.decode_seq_latent(cfg, b, c)
+        o, l = ora.sparse_mla_rows(q[b:b + 1], lat, gidx[b:b + 1], cfg.sm_scale)
+        check_attention(out[b:b + 1].float().cpu().double().numpy(), lse[b:b + 1].cpu().double().numpy(), o, l,
+                        "bf16", f"decode b={b}")
+
+
+def test_decode_block_shuffle_invariance(dsa):
+    _say("decode shuffle invariance")
+    res = []
+    for sh in (False, True):
+        cfg = synth.DecodeConfig("t", 4, 500, 5000, 64, 128, 128, 512, 3, sh)
+        ctx, bt, nb, pools, qside = _decode_case(cfg)
+        out, lse, idx = _run_decode(dsa, cfg, ctx, bt, nb, pools, qside)
+        res.append((out.cpu(), lse.cpu(), idx.cpu()))
+    assert torch.equal(res[0][2], res[1][2])
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_paged_cache_append(dsa):
+    _say("paged cache append")
+    cfg = synth.DecodeConfig("t", 6, 100, 1000, 64, 128, 128, 64, 12, True)
+    ctx = synth.decode_ctx(cfg)
+    bt, nb = synth.decode_block_table(cfg, ctx)
+    k8p, ksp, kvp = synth.build_decode_pools(cfg, ctx, bt, nb)
+    lat, k8, ks = synth.new_token_rows(cfg, 0)
+    pos = (ctx - 1).to(torch.int32)
+    dk8, dks, dkv = k8p.to(DEV), ksp.to(DEV), kvp.to(DEV)
+    dl, d8, ds, dp, dbt = lat.to(DEV), k8.to(DEV), ks.to(DEV), pos.to(DEV), bt.to(DEV)
+    dsa.dsa_paged_cache_append(dl, d8, ds, dp, dbt, dkv, dk8, dks, n_pool_rows=nb * 64)
+    torch.cuda.synchronize()
+    ek8, eks, ekv = k8p.clone(), ksp.clone(), kvp.clone()
+    for b in range(cfg.B):
+        p = int(pos[b])
+        blk = int(bt[b, p // 64])
+        ek8[blk, p % 64] = k8[b]
+        eks[blk, p % 64] = ks[b]
+        ekv[blk, p % 64] = lat[b]
+    assert torch.equal(dk8.cpu(), ek8) and torch.equal(dks.cpu(), eks)
+    assert torch.equal(dkv.cpu().view(torch.int16), ekv.view(torch.int16))
