@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: prefill of one causal sequence of L = 131072 tokens with
+the full-size shapes (indexer 64 heads x 128 FP8, top-k 2048, 128 bf16 query
+heads over a 576-d latent).  One step is the whole hot path on that input:
+per-token E4M3 quantisation of the indexer q/k, the fused indexer + top-k
+(no L x L score matrix) and sparse MLA over the selected rows.  ``value`` is
+prefill tokens/s = L * K / wall time of K steps (inputs resident in HBM).
+
+Also reported (one JSON line): per-kernel HIP-event times and their roofline
+fractions, decode tokens/s for B = 64 sequences at context 32768 and for the
+ragged paged batch (B = 128, context 4096..131072, shuffled 64-token pages),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Inputs are synthetic (synth), drawn on the GPU with the same counter-based
+generator the oracle side uses.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "DSA prefill tokens/s at L=128K + decode tokens/s; % FP8 MFMA / HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--decode-steps", type=int, default=30)
+    ap.add_argument("--no-decode", action="store_true", help="prefill only")
+    ap.add_argument("--no-paged", action="store_true", help="skip the ragged paged decode batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows in the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain 1 GiB device copies (to scale HBM counters)")
+    ap.add_argument("--L", type=int, default=None, help="override the prefill length (testing only)")
+    return ap.parse_args()
+
+
+class Stages:
+    """HIP events between the launches of one step, on the launching stream."""
+
+    def __init__(self, torch, names):
+        self.torch = torch
+        self.names = names
+        self.acc = {n: 0.0 for n in names}
+        self.count = 0
+
+    def new(self):
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+
+    def add(self, evs):
+        for i, n in enumerate(self.names):
+            self.acc[n] += evs[i].elapsed_time(evs[i + 1])
+        self.count += 1
+
+    def avg_ms(self):
+        return {n: self.acc[n] / max(self.count, 1) for n in self.names}
+
+
+# --------------------------------------------------------------------------- prefill
+def setup_prefill(torch, dsa, synth, cfg, dev):
+    L = cfg.L
+    t = {}
+    t["qi"], t["ki"], t["w"] = synth.prefill_indexer_inputs(cfg, device=dev)
+    t["q"] = synth.prefill_attn_q(cfg, device=dev)
+    t["kv"] = synth.prefill_latent(cfg, device=dev)
+    t["q8"] = torch.empty((L, cfg.H_I, cfg.D_I), dtype=torch.uint8, device=dev)
+    t["qs"] = torch.empty(L, dtype=torch.float32, device=dev)
+    t["k8"] = torch.empty((L, cfg.D_I), dtype=torch.uint8, device=dev)
+    t["ks"] = torch.empty(L, dtype=torch.float32, device=dev)
+    t["idx"] = torch.empty((L, cfg.k), dtype=torch.int32, device=dev)
+    t["out"] = torch.empty((L, cfg.H, 512), dtype=torch.bfloat16, device=dev)
+    t["lse"] = torch.empty((L, cfg.H), dtype=torch.float32, device=dev)
+    t["args"] = dsa.make_prefill_args(L, cfg.H_I, cfg.D_I, cfg.H, cfg.k, dsa.DSA_E4M3, t["q8"], t["qs"], t["k8"],
+                                      t["ks"], t["w"], dsa.DSA_BF16, t["q"], t["kv"], cfg.sm_scale, t["idx"],
+                                      t["out"], t["lse"])
+    return t
+
+
+def prefill_step(dsa, cfg, t, evs, stream):
+    L = cfg.L
+    evs[0].record(stream)
+    dsa.dsa_quantize_e4m3_per_token(t["qi"], t["q8"], t["qs"], rows=L, cols=cfg.H_I * cfg.D_I, stream=stream)
+    dsa.dsa_quantize_e4m3_per_token(t["ki"], t["k8"], t["ks"], rows=L, cols=cfg.D_I, stream=stream)
+    evs[1].record(stream)
+    dsa.dsa_prefill_select(t["args"], stream=stream)
+    evs[2].record(stream)
+    dsa.dsa_sparse_mla_fwd(t["q"], t["kv"], t["idx"], cfg.sm_scale, t["out"], t["lse"], stream=stream)
+    evs[3].record(stream)
+
+
+def prefill_work(cfg):
+    L, k = cfg.L, cfg.k
+    pairs = L * (L + 1) // 2
+    selected = sum(min(k, t + 1) for t in range(min(L, k))) + max(0, L - k) * k
+    return {
+        "quantize_bytes": L * cfg.H_I * cfg.D_I * 5 + L * cfg.D_I * 5 + 2 * L * 4,
+        "indexer_flop": 2 * cfg.H_I * cfg.D_I * pairs,
+        "causal_pairs": pairs,
+        "mla_flop": 2 * cfg.H * (576 + 512) * selected,
+        "selected_pairs": selected,
+    }
+
+
+# --------------------------------------------------------------------------- decode
+def setup_decode(torch, dsa, synth, cfg, dev):
+    ctx = synth.decode_ctx(cfg)
+    bt, nb = synth.decode_block_table(cfg, ctx)
+    t = {"ctx_cpu": ctx, "nb": nb}
+    t["k8p"], t["ksp"], t["kvp"] = synth.build_decode_pools(cfg, ctx, bt, nb, device=dev)
+    t["q8"], t["qs"], t["w"], t["q"] = [x.to(dev) for x in synth.decode_queries(cfg, device=dev)]
+    t["ctx"] = ctx.to(torch.int32).to(dev)
+    t["bt"] = bt.to(dev)
+    max_ctx = int(ctx.max())
+    t["max_ctx"] = max_ctx
+    t["ld"] = (max_ctx + 63) // 64 * 64
+    t["scores"] = torch.empty((cfg.B, t["ld"]), dtype=torch.float32, device=dev)
+    t["idx"] = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=dev)
+    t["out"] = torch.empty((cfg.B, cfg.H, 512), dtype=torch.bfloat16, device=dev)
+    t["lse"] = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=dev)
+    nws = dsa.dsa_sparse_mla_workspace_bytes(cfg.B, cfg.H, cfg.k)
+    t["ws"] = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    t["args"] = dsa.make_decode_args(cfg.B, cfg.H_I, cfg.D_I, cfg.H, cfg.k, t["q8"], t["qs"], t["w"], t["q"],
+                                     t["k8p"], t["ksp"], t["kvp"], nb * 64, t["bt"], bt.shape[1], t["ctx"],
+                                     max_ctx, cfg.sm_scale, t["out"], t["lse"], t["idx"])
+    # the token appended each step: the cached token at position ctx-1 (same bytes)
+    pos = (ctx - 1).to(torch.int32)
+    rows = torch.stack([bt[b, int(pos[b]) // 64].long() * 64 + int(pos[b]) % 64 for b in range(cfg.B)])
+    rows = rows.to(dev)
+    t["app_pos"] = pos.to(dev)
+    t["app_lat"] = t["kvp"].view(-1, 576)[rows].clone()
+    t["app_k8"] = t["k8p"].view(-1, cfg.D_I)[rows].clone()
+    t["app_ks"] = t["ksp"].view(-1)[rows].clone()
+    return t
+
+
+def decode_step(dsa, cfg, t, evs, stream):
+    evs[0].record(stream)
+    dsa.dsa_paged_cache_append(t["app_lat"], t["app_k8"], t["app_ks"], t["app_pos"], t["bt"], t["kvp"], t["k8p"],
+                               t["ksp"], n_pool_rows=t["nb"] * 64, stream=stream)
+    evs[1].record(stream)
+    dsa.dsa_decode_indexer_scores(t["args"], t["scores"], stream=stream)
+    evs[2].record(stream)
+    dsa.dsa_topk_select(t["scores"], t["ctx"], cfg.k, t["idx"], stream=stream)
+    evs[3].record(stream)
+    dsa.dsa_sparse_mla_paged_fwd(t["q"], t["kvp"], t["bt"], t["idx"], cfg.sm_scale, t["out"], t["lse"],
+                                 workspace=t["ws"], n_pool_rows=t["nb"] * 64, stream=stream)
+    evs[4].record(stream)
+
+
+def decode_work(cfg, ctx):
+    ctx = [int(c) for c in ctx]
+    sel = sum(min(cfg.k, c) for c in ctx)
+    B = cfg.B
+    return {
+        "append_bytes": B * (576 * 2 + cfg.D_I + 4) * 2,
+        "indexer_bytes": sum(ctx) * (cfg.D_I + 4) + B * (cfg.H_I * cfg.D_I + cfg.H_I * 4 + 4) + sum(ctx) * 4,
+        "topk_bytes": sum(ctx) * 4 + B * cfg.k * 4,
+        "mla_bytes": sel * 1152 + B * (cfg.H * 576 * 2 + cfg.H * 512 * 2 + cfg.k * 4 + cfg.H * 4),
+        "mla_flop": 2 * cfg.H * (576 + 512) * sel,
+        "context_tokens": sum(ctx),
+        "selected_pairs": sel,
+    }
+
+
+def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
+    t = setup_decode(torch, dsa, synth, cfg, dev)
+    stream = torch.cuda.current_stream()
+    names = ["cache_append", "decode_indexer", "topk", "sparse_mla"]
+    st = Stages(torch, names)
+    for i in range(warmup + steps):
+        flush.zero_()  # evict the 256 MB MALL and L2: each step reads its inputs from HBM
+        evs = st.new()
+        decode_step(dsa, cfg, t, evs, stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            st.add(evs)
+    ms = st.avg_ms()
+    work = decode_work(cfg, t["ctx_cpu"])
+    step_ms = sum(ms.values())
+    res = {
+        "workload": cfg.name, "B": cfg.B, "ctx_min": int(t["ctx_cpu"].min()), "ctx_max": int(t["ctx_cpu"].max()),
+        "ctx_mean": float(t["ctx_cpu"].float().mean()), "k": cfg.k, "H": cfg.H,
+        "paged_shuffled": cfg.shuffled, "steps": steps,
+        "ms_per_step": step_ms,
+        "tokens_per_s": cfg.B / (step_ms / 1e3),
+        "unit": "tokens/s",
+        "cold_cache": True,
+        "stages_ms": ms,
+        "roofline": {
+            "decode_indexer": _rl("hbm", work["indexer_bytes"] / (ms["decode_indexer"] / 1e3) / 1e9, PEAK_HBM_GBS,
+                                  "GB/s"),
+            "topk": _rl("hbm", work["topk_bytes"] / (ms["topk"] / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s"),
+            "sparse_mla": _rl("hbm", work["mla_bytes"] / (ms["sparse_mla"] / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s"),
+            "sparse_mla_mfma": _rl("mfma", work["mla_flop"] / (ms["sparse_mla"] / 1e3) / 1e12, PEAK_BF16_TFLOPS,
+                                   "TFLOP/s"),
+        },
+        "work": work,
+    }
+    del t
+    torch.cuda.empty_cache()
+    return res
+
+
+def _rl(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(torch, synth, cfg, nrows):
+    """The fp64 oracle on `nrows` query rows evenly spaced over the sequence
+    (an unbiased sample of the per-row cost), with the same inputs."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    L = cfg.L
+    rows = np.unique(((np.arange(nrows) + 0.5) * L / nrows).astype(np.int64))
+    k_i = synth.prefill_indexer_keys(cfg)
+    kv = synth.prefill_latent(cfg)
+    q_rows, w_rows, qa_rows = [], [], []
+    for r in rows:
+        qi, w = synth.prefill_indexer_query(cfg, rows=(int(r), int(r) + 1))
+        q_rows.append(qi)
+        w_rows.append(w)
+        qa_rows.append(synth.prefill_attn_q(cfg, rows=(int(r), int(r) + 1)))
+    qi = torch.cat(q_rows)
+    w = torch.cat(w_rows)
+    qa = torch.cat(qa_rows)
+    n = len(rows)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    q8, qsc = oracle.quantize_rows(qi.view(n, -1).numpy())
+    k8, ksc = oracle.quantize_rows(k_i.numpy())
+    pos = rows.astype(np.int32)
+    sc = oracle.indexer_rows(q8.reshape(n, cfg.H_I, cfg.D_I), k8, w.numpy(), pos, q_scale=qsc, k_scale=ksc)
+    idx, _ = oracle.topk_rows(sc, pos.astype(np.int64) + 1, cfg.k)
+    oracle.sparse_mla_rows(qa, kv, idx, cfg.sm_scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows evenly spaced over L={L} (quantise, fp64 indexer over all s<=t, "
+                      f"top-{cfg.k}, fp64 sparse MLA over 128 heads); {dt:.1f} s wall"}
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
+              f"(the multi-GPU sharding of the path is described in the design notes, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from sparse_attention_gemm_amd import dsa
+    dsa.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS["prefill128k"]
+    if args.L:
+        cfg = synth.scaled_down(cfg, L=args.L)
+    print(f"[bench] drawing prefill inputs L={cfg.L}", file=sys.stderr, flush=True)
+    t = setup_prefill(torch, dsa, synth, cfg, dev)
+    stream = torch.cuda.current_stream()
+    names = ["quantize", "indexer_topk", "sparse_mla"]
+    st = Stages(torch, names)
+    for i in range(args.warmup):
+        evs = st.new()
+        prefill_step(dsa, cfg, t, evs, stream)
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
+    all_evs = [st.new() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        prefill_step(dsa, cfg, t, all_evs[i], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e in all_evs:
+        st.add(e)
+    print(f"[bench] {args.steps} prefill steps in {wall:.3f} s", file=sys.stderr, flush=True)
+    ms = st.avg_ms()
+    work = prefill_work(cfg)
+    idx_tflops = work["indexer_flop"] / (ms["indexer_topk"] / 1e3) / 1e12
+    mla_tflops = work["mla_flop"] / (ms["sparse_mla"] / 1e3) / 1e12
+    q_gbs = work["quantize_bytes"] / (ms["quantize"] / 1e3) / 1e9
+    value = cfg.L * args.steps / wall
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "L": cfg.L, "H_I": cfg.H_I, "D_I": cfg.D_I, "H": cfg.H, "k": cfg.k,
+                   "seed": cfg.seed, "parallelism": "single GPU"},
+        "roofline": dict(_rl("mfma", idx_tflops, PEAK_FP8_TFLOPS, "TFLOP/s"), kernel="prefill_indexer_topk"),
+        "stages": {
+            "quantize": dict(ms=round(ms["quantize"], 3), **_rl("hbm", q_gbs, PEAK_HBM_GBS, "GB/s")),
+            "indexer_topk": dict(ms=round(ms["indexer_topk"], 3),
+                                 **_rl("mfma", idx_tflops, PEAK_FP8_TFLOPS, "TFLOP/s")),
+            "sparse_mla": dict(ms=round(ms["sparse_mla"], 3), **_rl("mfma", mla_tflops, PEAK_BF16_TFLOPS, "TFLOP/s")),
+        },
+        "work": work,
+    }
+    if args.calibrate_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_calibration"] = {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4, "launches": 3}
+        del a, b
+    del t
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dcfg = synth.CONFIGS["decode"]
+        print("[bench] decode B=64 ctx=32768", file=sys.stderr, flush=True)
+        line["decode"] = run_decode(torch, dsa, synth, dcfg, dev, args.decode_steps, 3, flush)
+        if not args.no_paged:
+            print("[bench] paged decode B=128", file=sys.stderr, flush=True)
+            line["paged_decode"] = run_decode(torch, dsa, synth, synth.CONFIGS["paged"], dev, args.decode_steps, 3,
+                                              flush)
+        del flush
+    if not args.no_cpu_baseline:
+        print(f"[bench] oracle on {args.cpu_rows} sampled rows", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(torch, synth, cfg, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,6 +161,12 @@ size_t dsa_prefill_workspace_bytes(const dsa_prefill_args *a);
 dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* The selection stage of dsa_prefill alone (indexer + top-k into a->idx;
+ * q, kv, out, lse are not touched and may be NULL).  dsa_prefill is exactly
+ * this call followed by dsa_sparse_mla_fwd on a->idx with no workspace. */
+dsa_status dsa_prefill_select(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Paged decode: one query per sequence at position ctx_len[b]-1, whose own
  * key and latent are already in the cache.  The cache is paged in 64-token
@@ -200,6 +206,29 @@ typedef struct {
 size_t dsa_decode_workspace_bytes(const dsa_decode_args *a);
 dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/* The stages of dsa_decode, callable one by one.  dsa_decode is exactly
+ *   dsa_decode_indexer_scores -> dsa_topk_select (n_valid = ctx_len) ->
+ *   dsa_sparse_mla_paged_fwd
+ * on buffers carved from its workspace.
+ *
+ * Indexer scores of each sequence's query against its cached keys:
+ *   scores [B, ld_scores] fp32 out, ld_scores >= max_ctx; positions
+ *   p < ctx_len[b] are written, the rest of the row is left untouched.
+ *   (q, kv_pool, out, lse, idx_out of a are not used.) */
+dsa_status dsa_decode_indexer_scores(const dsa_decode_args *a, float *scores, int64_t ld_scores,
+                                     hipStream_t stream);
+
+/* Sparse MLA over a paged latent pool: idx [T, k] holds LOGICAL positions of
+ * sequence t (-1 = skip); row = block_table[t*max_blocks + p/64]*64 + p%64
+ * of kv_pool [n_pool_rows, 576] BF16.  q [T,H,576] BF16, out [T,H,512] BF16,
+ * lse [T,H] fp32 or NULL.  Entries whose page is unmapped (or outside the
+ * pool) are skipped.  workspace as for dsa_sparse_mla_fwd (optional). */
+dsa_status dsa_sparse_mla_paged_fwd(const void *q, const void *kv_pool, int64_t n_pool_rows,
+                                    const int32_t *block_table, int32_t max_blocks,
+                                    const int32_t *idx, int32_t T, int32_t H, int32_t k,
+                                    float sm_scale, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Paged cache append (MLA's latent cache: jienda.com, section 2.1): write one

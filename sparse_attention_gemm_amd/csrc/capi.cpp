@@ -153,15 +153,17 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
   return fail(DSA_ERR_UNSUPPORTED, "sparse MLA dtype must be BF16 or F32");
 }
 
-static dsa_status check_prefill(const dsa_prefill_args *a) {
+static dsa_status check_prefill(const dsa_prefill_args *a, bool attention) {
   REQUIRE(a, DSA_ERR_INVALID_ARG, "null args");
   REQUIRE(a->L >= 1, DSA_ERR_INVALID_ARG, "L must be >= 1");
   REQUIRE(a->H > 0 && a->H_I > 0 && a->D_I > 0, DSA_ERR_INVALID_ARG, "head counts and D_I must be > 0");
   REQUIRE(a->k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
   REQUIRE(a->k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
-  REQUIRE(a->q_idx && a->k_idx && a->w && a->q && a->kv && a->idx && a->out, DSA_ERR_INVALID_ARG,
-          "null pointer");
-  REQUIRE(a->sm_scale == a->sm_scale && a->sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  REQUIRE(a->q_idx && a->k_idx && a->w && a->idx, DSA_ERR_INVALID_ARG, "null pointer");
+  if (attention) {
+    REQUIRE(a->q && a->kv && a->out, DSA_ERR_INVALID_ARG, "null pointer");
+    REQUIRE(a->sm_scale == a->sm_scale && a->sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  }
   if (a->idx_dt == DSA_E4M3) {
     REQUIRE(a->q_scale && a->k_scale, DSA_ERR_INVALID_ARG, "E4M3 needs q_scale and k_scale");
     REQUIRE(a->H_I == 64 && a->D_I == 128, DSA_ERR_UNSUPPORTED, "fused E4M3 prefill needs H_I = 64, D_I = 128");
@@ -172,6 +174,7 @@ static dsa_status check_prefill(const dsa_prefill_args *a) {
   } else {
     return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be E4M3 or F32");
   }
+  if (!attention) return DSA_OK;
   if (a->attn_dt == DSA_BF16)
     REQUIRE(a->H % 16 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 16");
   else
@@ -188,30 +191,46 @@ size_t dsa_prefill_workspace_bytes(const dsa_prefill_args *a) {
   return 0;
 }
 
+// indexer + top-k of one prefill sequence into a->idx
+static dsa_status prefill_select(const dsa_prefill_args *a, void *workspace, hipStream_t stream) {
+  const int L = a->L;
+  if (a->idx_dt == DSA_E4M3)
+    return hip_check(launch_prefill_indexer_topk((const uint8_t *)a->q_idx, a->q_scale, (const uint8_t *)a->k_idx,
+                                                 a->k_scale, a->w, L, a->k, a->idx, stream),
+                     "prefill indexer/top-k launch");
+  float *sc = (float *)workspace;
+  int32_t *qpos = (int32_t *)((char *)workspace + align_up((size_t)L * L * 4, 256));
+  int32_t *nval = (int32_t *)((char *)qpos + align_up((size_t)L * 4, 256));
+  dsa_status st = hip_check(launch_positions(qpos, nval, L, stream), "positions launch");
+  if (st == DSA_OK)
+    st = hip_check(launch_indexer_scores_f32((const float *)a->q_idx, (const float *)a->k_idx, a->w, qpos, L, L,
+                                             a->H_I, a->D_I, sc, L, stream),
+                   "indexer launch");
+  if (st == DSA_OK) st = hip_check(launch_topk(sc, L, nval, L, L, a->k, a->idx, stream), "topk launch");
+  return st;
+}
+
+dsa_status dsa_prefill_select(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  CLEAR_ERR();
+  dsa_status st = check_prefill(a, false);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa_prefill_workspace_bytes(a);
+  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), DSA_ERR_WORKSPACE,
+          "workspace %zu < required %zu", workspace ? workspace_bytes : (size_t)0, need);
+  return prefill_select(a, workspace, stream);
+}
+
 dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
                        hipStream_t stream) {
   CLEAR_ERR();
-  dsa_status st = check_prefill(a);
+  dsa_status st = check_prefill(a, true);
   if (st != DSA_OK) return st;
   const size_t need = dsa_prefill_workspace_bytes(a);
   REQUIRE(need == 0 || (workspace && workspace_bytes >= need), DSA_ERR_WORKSPACE,
           "workspace %zu < required %zu", workspace ? workspace_bytes : (size_t)0, need);
   const int L = a->L;
-  if (a->idx_dt == DSA_E4M3) {
-    st = hip_check(launch_prefill_indexer_topk((const uint8_t *)a->q_idx, a->q_scale, (const uint8_t *)a->k_idx,
-                                               a->k_scale, a->w, L, a->k, a->idx, stream),
-                   "prefill indexer/top-k launch");
-  } else {
-    float *sc = (float *)workspace;
-    int32_t *qpos = (int32_t *)((char *)workspace + align_up((size_t)L * L * 4, 256));
-    int32_t *nval = (int32_t *)((char *)qpos + align_up((size_t)L * 4, 256));
-    st = hip_check(launch_positions(qpos, nval, L, stream), "positions launch");
-    if (st == DSA_OK)
-      st = hip_check(launch_indexer_scores_f32((const float *)a->q_idx, (const float *)a->k_idx, a->w, qpos, L, L,
-                                               a->H_I, a->D_I, sc, L, stream),
-                     "indexer launch");
-    if (st == DSA_OK) st = hip_check(launch_topk(sc, L, nval, L, L, a->k, a->idx, stream), "topk launch");
-  }
+  st = prefill_select(a, workspace, stream);
   if (st != DSA_OK) return st;
   if (a->attn_dt == DSA_BF16)
     return hip_check(launch_sparse_mla_bf16(a->q, a->kv, a->idx, nullptr, 0, L, L, a->H, a->k, a->sm_scale,
@@ -222,7 +241,7 @@ dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t worksp
                    "sparse mla launch");
 }
 
-static dsa_status check_decode(const dsa_decode_args *a) {
+static dsa_status check_decode(const dsa_decode_args *a, bool attention) {
   REQUIRE(a, DSA_ERR_INVALID_ARG, "null args");
   REQUIRE(a->B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
   REQUIRE(a->k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
@@ -233,12 +252,14 @@ static dsa_status check_decode(const dsa_decode_args *a) {
   REQUIRE(a->n_pool_rows > 0 && a->n_pool_rows % DSA_PAGE == 0, DSA_ERR_INVALID_ARG,
           "n_pool_rows must be a positive multiple of 64");
   REQUIRE(a->H_I == 64 && a->D_I == 128, DSA_ERR_UNSUPPORTED, "decode indexer needs H_I = 64, D_I = 128");
-  REQUIRE(a->H > 0 && a->H % 16 == 0, DSA_ERR_UNSUPPORTED, "decode attention needs H a multiple of 16");
-  REQUIRE(a->sm_scale == a->sm_scale && a->sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (attention) {
+    REQUIRE(a->H > 0 && a->H % 16 == 0, DSA_ERR_UNSUPPORTED, "decode attention needs H a multiple of 16");
+    REQUIRE(a->sm_scale == a->sm_scale && a->sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  }
   if (a->B == 0) return DSA_OK;
-  REQUIRE(a->q8 && a->q_scale && a->w && a->q && a->k8_pool && a->ks_pool && a->kv_pool && a->block_table &&
-              a->ctx_len && a->out,
+  REQUIRE(a->q8 && a->q_scale && a->w && a->k8_pool && a->ks_pool && a->block_table && a->ctx_len,
           DSA_ERR_INVALID_ARG, "null pointer");
+  if (attention) REQUIRE(a->q && a->kv_pool && a->out, DSA_ERR_INVALID_ARG, "null pointer");
   return DSA_OK;
 }
 
@@ -252,9 +273,51 @@ size_t dsa_decode_workspace_bytes(const dsa_decode_args *a) {
   return n;
 }
 
+dsa_status dsa_decode_indexer_scores(const dsa_decode_args *a, float *scores, int64_t ld_scores,
+                                     hipStream_t stream) {
+  CLEAR_ERR();
+  dsa_status st = check_decode(a, false);
+  if (st != DSA_OK) return st;
+  REQUIRE(ld_scores >= a->max_ctx, DSA_ERR_INVALID_ARG, "ld_scores < max_ctx");
+  if (a->B == 0) return DSA_OK;
+  REQUIRE(scores, DSA_ERR_INVALID_ARG, "null pointer");
+  return hip_check(launch_decode_indexer(a->q8, a->q_scale, a->w, a->k8_pool, a->ks_pool, a->block_table,
+                                         a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores,
+                                         ld_scores, stream),
+                   "decode indexer launch");
+}
+
+dsa_status dsa_sparse_mla_paged_fwd(const void *q, const void *kv_pool, int64_t n_pool_rows,
+                                    const int32_t *block_table, int32_t max_blocks, const int32_t *idx,
+                                    int32_t T, int32_t H, int32_t k, float sm_scale, void *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "T must be >= 0");
+  REQUIRE(n_pool_rows > 0 && n_pool_rows % DSA_PAGE == 0, DSA_ERR_INVALID_ARG,
+          "n_pool_rows must be a positive multiple of 64");
+  REQUIRE(max_blocks >= 1, DSA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(H > 0 && H % 16 == 0, DSA_ERR_UNSUPPORTED, "paged sparse MLA needs H a multiple of 16");
+  REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (T == 0) return DSA_OK;
+  REQUIRE(q && kv_pool && block_table && idx && out, DSA_ERR_INVALID_ARG, "null pointer");
+  const size_t need = mla_ws_bytes(T, H, k);
+  int splits = 1;
+  float *po = nullptr, *pml = nullptr;
+  if (workspace && need > 0) {
+    REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu", workspace_bytes, need);
+    splits = mla_splits(T, H, k);
+    mla_ws_split(workspace, T, H, k, &po, &pml);
+  }
+  return hip_check(launch_sparse_mla_bf16(q, kv_pool, idx, block_table, max_blocks, n_pool_rows, T, H, k,
+                                          sm_scale, out, lse, splits, po, pml, stream),
+                   "sparse mla launch");
+}
+
 dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   CLEAR_ERR();
-  dsa_status st = check_decode(a);
+  dsa_status st = check_decode(a, true);
   if (st != DSA_OK) return st;
   if (a->B == 0) return DSA_OK;
   const size_t need = dsa_decode_workspace_bytes(a);
@@ -273,7 +336,8 @@ dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspac
   const int splits = mla_splits(a->B, a->H, a->k);
   if (splits > 1) mla_ws_split(p, a->B, a->H, a->k, &po, &pml);
   st = hip_check(launch_decode_indexer(a->q8, a->q_scale, a->w, a->k8_pool, a->ks_pool, a->block_table,
-                                       a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores, ld, stream),
+                                       a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores, ld,
+                                       stream),
                  "decode indexer launch");
   if (st != DSA_OK) return st;
   st = hip_check(launch_topk(scores, ld, a->ctx_len, a->max_ctx, a->B, a->k, idx, stream), "topk launch");

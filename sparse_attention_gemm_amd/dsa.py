@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
 EXPORTS = (
     "dsa_last_error", "dsa_version", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select",
     "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_fwd", "dsa_prefill_workspace_bytes", "dsa_prefill",
-    "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append",
+    "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
+    "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd",
 )
 
 
@@ -78,8 +79,12 @@ def load():
     L.dsa_decode_workspace_bytes.restype = _SZ
     L.dsa_decode.argtypes = [ctypes.POINTER(DecodeArgs), _P, _SZ, _P]
     L.dsa_paged_cache_append.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _P, _I64, _P]
+    L.dsa_prefill_select.argtypes = [ctypes.POINTER(PrefillArgs), _P, _SZ, _P]
+    L.dsa_decode_indexer_scores.argtypes = [ctypes.POINTER(DecodeArgs), _P, _I64, _P]
+    L.dsa_sparse_mla_paged_fwd.argtypes = [_P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]
     for name in ("dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
-                 "dsa_prefill", "dsa_decode", "dsa_paged_cache_append"):
+                 "dsa_prefill", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
+                 "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -170,6 +175,11 @@ def dsa_prefill(args: PrefillArgs, workspace=None, stream=None):
     _check(load().dsa_prefill(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def dsa_prefill_select(args: PrefillArgs, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_prefill_select(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def make_decode_args(B, H_I, D_I, H, k, q8, q_scale, w, q, k8_pool, ks_pool, kv_pool, n_pool_rows, block_table,
                      max_blocks, ctx_len, max_ctx, sm_scale, out, lse=None, idx_out=None) -> DecodeArgs:
     return DecodeArgs(B, H_I, D_I, H, k, _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(q), _ptr(k8_pool), _ptr(ks_pool),
@@ -184,6 +194,22 @@ def dsa_decode_workspace_bytes(args: DecodeArgs) -> int:
 def dsa_decode(args: DecodeArgs, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().dsa_decode(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_decode_indexer_scores(args: DecodeArgs, scores, ld_scores=None, stream=None):
+    ld = scores.stride(0) if ld_scores is None else ld_scores
+    _check(load().dsa_decode_indexer_scores(ctypes.byref(args), _ptr(scores), ld, _stream(stream)))
+
+
+def dsa_sparse_mla_paged_fwd(q, kv_pool, block_table, idx, sm_scale, out, lse=None, workspace=None,
+                             n_pool_rows=None, stream=None):
+    T, H = q.shape[0], q.shape[1]
+    k = idx.shape[1]
+    n_pool_rows = kv_pool.numel() // 576 if n_pool_rows is None else n_pool_rows
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_sparse_mla_paged_fwd(_ptr(q), _ptr(kv_pool), n_pool_rows, _ptr(block_table),
+                                           block_table.shape[1], _ptr(idx), T, H, k, float(sm_scale), _ptr(out),
+                                           _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dsa_paged_cache_append(latent, k8, ks, pos, block_table, kv_pool, k8_pool, ks_pool, B=None, D_I=None,

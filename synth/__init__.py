@@ -190,7 +190,6 @@ class DecodeConfig:
 CONFIGS = {
     # tiny fp32 prefill: parity only
     "tiny": PrefillConfig("tiny_fp32_L2048", 2048, 4, 64, 8, 256, 0, "f32", False),
-    "tiny_fp8": PrefillConfig("tiny_fp8_L2048", 2048, 4, 64, 16, 256, 0, "bf16", True),
     "decode": DecodeConfig("decode_B64_ctx32768", 64, 32768, 32768, 64, 128, 128, 2048, 0, False),
     "prefill16k": PrefillConfig("prefill_L16384", 16384, 64, 128, 128, 2048, 1, "bf16", True),
     "prefill128k": PrefillConfig("prefill_L131072", 131072, 64, 128, 128, 2048, 1, "bf16", True),
@@ -207,16 +206,26 @@ def scaled_down(cfg, **kw):
 
 
 # ----------------------------------------------------------------- prefill draws
-def prefill_indexer_inputs(cfg: PrefillConfig, rows=None, device="cpu"):
-    """q_I [T, H_I, D_I] fp32 for the given rows (default all), k_I [L, D_I] fp32,
-    w [T, H_I] fp32."""
+def prefill_indexer_query(cfg: PrefillConfig, rows=None, device="cpu"):
+    """q_I [T, H_I, D_I] fp32 and w [T, H_I] fp32 for rows [r0, r1) (default all)."""
     r0, r1 = (0, cfg.L) if rows is None else rows
     n = r1 - r0
     hd = cfg.H_I * cfg.D_I
     q = normal(cfg.seed, T_QI, (n, cfg.H_I, cfg.D_I), start=r0 * hd, device=device)
-    k = normal(cfg.seed, T_KI, (cfg.L, cfg.D_I), device=device)
     w = normal(cfg.seed, T_W, (n, cfg.H_I), start=r0 * cfg.H_I, device=device, std=cfg.w_std)
-    return q, k, w
+    return q, w
+
+
+def prefill_indexer_keys(cfg: PrefillConfig, device="cpu"):
+    """k_I [L, D_I] fp32."""
+    return normal(cfg.seed, T_KI, (cfg.L, cfg.D_I), device=device)
+
+
+def prefill_indexer_inputs(cfg: PrefillConfig, rows=None, device="cpu"):
+    """q_I [T, H_I, D_I] fp32 for the given rows (default all), k_I [L, D_I] fp32,
+    w [T, H_I] fp32."""
+    q, w = prefill_indexer_query(cfg, rows, device)
+    return q, prefill_indexer_keys(cfg, device), w
 
 
 def prefill_attn_q(cfg: PrefillConfig, rows=None, device="cpu"):

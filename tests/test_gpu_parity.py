@@ -393,3 +393,46 @@ def test_paged_cache_append(dsa):
         ekv[blk, p % 64] = lat[b]
     assert torch.equal(dk8.cpu(), ek8) and torch.equal(dks.cpu(), eks)
     assert torch.equal(dkv.cpu().view(torch.int16), ekv.view(torch.int16))
+
+
+def test_decode_equals_its_stages(dsa):
+    """dsa_decode == indexer scores -> top-k -> paged sparse MLA, bit for bit."""
+    _say("decode stages compose")
+    cfg = synth.DecodeConfig("t", 5, 300, 6000, 64, 128, 128, 1024, 8, True)
+    ctx, bt, nb, pools, qside = _decode_case(cfg)
+    out, lse, idx = _run_decode(dsa, cfg, ctx, bt, nb, pools, qside)
+    k8p, ksp, kvp = [p.to(DEV) for p in pools]
+    q8, qs, w, q = [x.to(DEV) for x in qside]
+    ctxd, btd = ctx.to(torch.int32).to(DEV), bt.to(DEV)
+    max_ctx = int(ctx.max())
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    args = dsa.make_decode_args(cfg.B, 64, 128, cfg.H, cfg.k, q8, qs, w, q, k8p, ksp, kvp, nb * 64, btd,
+                                bt.shape[1], ctxd, max_ctx, cfg.sm_scale, out2, lse2, None)
+    sc = torch.full((cfg.B, max_ctx + 3), -7.0, dtype=torch.float32, device=DEV)
+    dsa.dsa_decode_indexer_scores(args, sc)
+    idx2 = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk_select(sc, ctxd, cfg.k, idx2)
+    ws = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_bytes(cfg.B, cfg.H, cfg.k)), dtype=torch.uint8,
+                     device=DEV)
+    dsa.dsa_sparse_mla_paged_fwd(q, kvp, btd, idx2, cfg.sm_scale, out2, lse2, workspace=ws, n_pool_rows=nb * 64)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16)) and torch.equal(lse2, lse)
+    # positions past each context are left untouched
+    scc = sc.cpu()
+    for b in range(cfg.B):
+        assert torch.all(scc[b, int(ctx[b]):] == -7.0)
+
+
+def test_prefill_select_equals_prefill_selection(dsa):
+    _say("prefill select stage")
+    cfg = synth.scaled_down(synth.CONFIGS["prefill16k"], L=600, k=128, H=16, seed=6)
+    ins = _prefill_inputs(cfg)
+    t = _run_prefill(dsa, cfg, *ins)
+    idx2 = torch.full_like(t["idx"], 12345)
+    args = dsa.make_prefill_args(cfg.L, 64, 128, cfg.H, cfg.k, dsa.DSA_E4M3, t["q8"], t["qs"], t["k8"], t["ks"],
+                                 t["w"], dsa.DSA_BF16, None, None, cfg.sm_scale, idx2, None, None)
+    dsa.dsa_prefill_select(args)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, t["idx"])
