@@ -8,14 +8,20 @@
 // rope); the value is the first 512 dims.
 //
 // bf16 kernel (one workgroup per query token and group of 16*NW heads):
-//  * the selected rows are gathered 32 at a time into LDS, once per workgroup
-//    for all its heads: row-major for the logits and transposed (value dims
-//    x keys) for the PV product;
+//  * the physical rows of the workgroup's selection are resolved once (index,
+//    then block table when paged) into LDS;
+//  * the selected latent rows are gathered 32 at a time straight from global
+//    memory into LDS (direct-to-LDS loads, no register staging), row-major,
+//    double buffered so the gather of tile i+1 overlaps the MFMAs of tile i;
+//    each row is fetched once for all heads of the workgroup;
 //  * logits are computed transposed, S^T = C Q^T (keys x heads), with bf16
 //    MFMA 16x16x32 and Q^T resident in registers; in that layout each lane
 //    holds 8 keys of one head, which is exactly the B operand layout the PV
-//    MFMA needs (up to a fixed permutation of the keys, applied to the value
-//    rows as well), so P never moves between lanes;
+//    MFMA needs (up to a fixed permutation of the keys), so P never moves
+//    between lanes;
+//  * the value operand of PV (value dims x keys) is read from the same
+//    row-major tile with the transposing LDS load, which hands each lane four
+//    keys of one value column;
 //  * online softmax in fp32 (base-2 exponent with the scale folded in),
 //    output O^T (value dims x heads) accumulated in fp32 registers;
 //  * optional split of the selection across workgroups with an LSE-weighted
@@ -25,9 +31,16 @@
 namespace {
 
 constexpr int kBN = 32;                  // selected rows per tile
-constexpr int kCRow = 576 * 2 + 16;      // LDS bytes per gathered row (padded)
-constexpr int kVRow = kBN * 2 + 16;      // LDS bytes per transposed value row (padded)
-constexpr int kSmemMla = kBN * kCRow + 512 * kVRow + kBN * 4;
+constexpr int kRowSlots = 73;            // 16-byte slots per LDS row: 72 of data + 1 pad (bank spread)
+constexpr int kCRow = kRowSlots * 16;    // LDS bytes per gathered row
+constexpr int kTileBytes = kBN * kCRow;  // 37376
+constexpr int kTileSlots = kBN * kRowSlots;
+constexpr int kGatherInsts = (kTileSlots + 63) / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
+constexpr int kSmemMla = 2 * kTileBytes + 2048 * 4;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Row of kv for entry e of query t, or -1 (padding, or not a row of [0, N)).
 __device__ __forceinline__ int64_t phys_row(const int32_t *__restrict__ irow, const int32_t *__restrict__ bt,
@@ -42,46 +55,23 @@ __device__ __forceinline__ int64_t phys_row(const int32_t *__restrict__ irow, co
   return (blk >= 0 && row < N) ? row : -1;
 }
 
-// Gather tile rows [e0, e0+32) of query t into LDS.
-//  task < 512: rows 4*kg..4*kg+3 (kg = task/64), value chunk dc = task%64
-//              (8 dims): row-major copy + 4-key transposed copy;
-//  task >= 512: rope chunk (dims 512..575) of one row.
-__device__ __forceinline__ void gather_tile(uint8_t *__restrict__ ctile, uint8_t *__restrict__ vt,
-                                            int *__restrict__ rowv, const __bf16 *__restrict__ kv,
-                                            const int32_t *__restrict__ irow, const int32_t *__restrict__ bt,
-                                            int max_blocks, int64_t N, int64_t t, int e0, int k, int nthreads) {
-  const int tid = threadIdx.x;
-  if (tid < kBN) rowv[tid] = phys_row(irow, bt, max_blocks, N, t, e0 + tid, k) >= 0 ? 1 : 0;
-  for (int task = tid; task < 512 + kBN * 8; task += nthreads) {
-    if (task < 512) {
-      const int kg = task >> 6, dc = task & 63;
-      uint32_t v[4][4];
+// Issue the direct-to-LDS loads of tile rows [r0, r0+32) of this workgroup's
+// selection (rows[] holds physical rows, -1 for skipped entries, which load
+// row 0 instead and are masked later).  Instruction i of the tile writes LDS
+// slots [64i, 64i+64); slot s holds row s/73, 16-byte chunk s%73 (chunk 72 is
+// padding and reloads chunk 71).
+template <int NW>
+__device__ __forceinline__ void gather_tile_async(uint8_t *__restrict__ dst, const int *__restrict__ rows,
+                                                  int r0, const __bf16 *__restrict__ kv, int wave, int lane) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t pr = phys_row(irow, bt, max_blocks, N, t, e0 + kg * 4 + r, k);
-        i32x4 x = {0, 0, 0, 0};
-        if (pr >= 0) x = *reinterpret_cast<const i32x4 *>(kv + pr * 576 + dc * 8);
-        *reinterpret_cast<i32x4 *>(ctile + (kg * 4 + r) * kCRow + dc * 16) = x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[r][j] = (uint32_t)x[j];
-      }
-      // transpose: value dim dc*8 + j  <- 4 keys (rows kg*4 .. +3)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sh = (j & 1) * 16;
-        const uint32_t a0 = (v[0][j >> 1] >> sh) & 0xFFFFu, a1 = (v[1][j >> 1] >> sh) & 0xFFFFu;
-        const uint32_t a2 = (v[2][j >> 1] >> sh) & 0xFFFFu, a3 = (v[3][j >> 1] >> sh) & 0xFFFFu;
-        i32x2 pk;
-        pk[0] = (int)(a0 | (a1 << 16));
-        pk[1] = (int)(a2 | (a3 << 16));
-        *reinterpret_cast<i32x2 *>(vt + (dc * 8 + j) * kVRow + kg * 8) = pk;
-      }
-    } else {
-      const int q = task - 512, r = q >> 3, ch = 64 + (q & 7);
-      const int64_t pr = phys_row(irow, bt, max_blocks, N, t, e0 + r, k);
-      i32x4 x = {0, 0, 0, 0};
-      if (pr >= 0) x = *reinterpret_cast<const i32x4 *>(kv + pr * 576 + ch * 8);
-      *reinterpret_cast<i32x4 *>(ctile + r * kCRow + ch * 16) = x;
+  for (int i = wave; i < kGatherInsts; i += NW) {
+    const int slot = i * 64 + lane;
+    if (slot < kTileSlots) {
+      const int r = slot / kRowSlots;
+      const int j = min(slot - r * kRowSlots, 71);
+      const int pr = rows[r0 + r];
+      const __bf16 *src = kv + (int64_t)(pr >= 0 ? pr : 0) * 576 + j * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + i * 1024), 16, 0, 0);
     }
   }
 }
@@ -93,9 +83,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
     __bf16 *__restrict__ out, float *__restrict__ lse, int splits, float *__restrict__ part_o,
     float *__restrict__ part_ml) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  uint8_t *ctile = smem_raw;
-  uint8_t *vt = smem_raw + kBN * kCRow;
-  int *rowv = reinterpret_cast<int *>(vt + 512 * kVRow);
+  uint8_t *tiles = smem_raw;                                        // 2 x kTileBytes
+  int *rows = reinterpret_cast<int *>(smem_raw + 2 * kTileBytes);   // <= 2048 physical rows
 
   const int n_hg = H / (16 * NW);
   const int bid = blockIdx.x;
@@ -108,6 +97,13 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
   const int ntiles = (k + kBN - 1) / kBN;
   const int per = (ntiles + splits - 1) / splits;
   const int tb = sp * per, te = min(ntiles, tb + per);
+  const int32_t *irow = idx + t * k;
+
+  // physical rows of this workgroup's entries [tb*32, te*32)
+  for (int e = tid; e < (te - tb) * kBN; e += NW * 64)
+    rows[e] = (int)phys_row(irow, bt, max_blocks, N, t, tb * kBN + e, k);
+  __syncthreads();
+  if (tb < te) gather_tile_async<NW>(tiles, rows, 0, kv, wave, lane);
 
   // Q^T in registers: lane (g, c) holds head h0+c, dims 32*s + 8*g .. +8 for step s.
   bf16x8 qr[18];
@@ -119,27 +115,38 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
   for (int m = 0; m < 32; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
-  const int32_t *irow = idx + t * k;
+  // transposing-load lane roles: row 4g + (c>>2) of each 4-row group, value chunk (c&3)
+  const int tr_row = 4 * g + (c >> 2), tr_col = (c & 3) * 4;
 
   for (int tile = tb; tile < te; ++tile) {
-    __syncthreads();
-    gather_tile(ctile, vt, rowv, kv, irow, bt, max_blocks, N, t, tile * kBN, k, NW * 64);
-    __syncthreads();
+    const int cur = (tile - tb) & 1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of `tile` have landed in LDS
+    __syncthreads();                // ... and every wave's; tile-1 is no longer read
+    if (tile + 1 < te)
+      gather_tile_async<NW>(tiles + (cur ^ 1) * kTileBytes, rows, (tile + 1 - tb) * kBN, kv, wave, lane);
+    const uint8_t *ct = tiles + cur * kTileBytes;
+    const int *rv = rows + (tile - tb) * kBN;
     // S^T for keys [0,16) and [16,32) of the tile
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(ctile + c * kCRow + (s * 32 + g * 8) * 2);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(ctile + (16 + c) * kCRow + (s * 32 + g * 8) * 2);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(ct + c * kCRow + (s * 32 + g * 8) * 2);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(ct + (16 + c) * kCRow + (s * 32 + g * 8) * 2);
       s0 = mfma_bf16_16x16x32(a0, qr[s], s0);
       s1 = mfma_bf16_16x16x32(a1, qr[s], s1);
+    }
+    // keep LDS reads close to their MFMAs (bounds live registers)
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // lane (g,c): x[r] = key 4g+r, x[4+r] = key 16+4g+r, head c
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r] = rowv[4 * g + r] ? s0[r] * scale_log2 : -INFINITY;
-      x[4 + r] = rowv[16 + 4 * g + r] ? s1[r] * scale_log2 : -INFINITY;
+      x[r] = rv[4 * g + r] >= 0 ? s0[r] * scale_log2 : -INFINITY;
+      x[4 + r] = rv[16 + 4 * g + r] >= 0 ? s1[r] * scale_log2 : -INFINITY;
     }
     float mx = x[0];
 #pragma unroll
@@ -165,13 +172,20 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
     // O^T[dv, head] += V^T[dv, keys] P^T[keys, head]; key slot order matches pb
+    const uint8_t *tr0 = ct + tr_row * kCRow + tr_col * 2;
+    const uint8_t *tr1 = tr0 + 16 * kCRow;
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const uint8_t *vr = vt + (16 * m + c) * kVRow;
-      const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vr + (4 * g) * 2);
-      const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vr + (16 + 4 * g) * 2);
-      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tr0 + m * 32));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tr1 + m * 32));
+      const i16x4 lohi[2] = {lo, hi};
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lohi);
       o[m] = mfma_bf16_16x16x32(a, pb, o[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
     }
   }
 
