@@ -27,9 +27,10 @@ hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStre
 
 // Workgroups of the bf16 sparse-MLA kernel without splitting, and the split
 // count that brings a small batch up to about one workgroup per CU.
-static int mla_waves(int H) { return H % 128 == 0 ? 8 : H % 64 == 0 ? 4 : H % 32 == 0 ? 2 : 1; }
+// heads per workgroup of the bf16 kernel (16 per wave)
+static int mla_heads_per_wg(int H) { return H % 128 == 0 ? 128 : H % 64 == 0 ? 64 : H % 32 == 0 ? 32 : 16; }
 static int mla_splits(int64_t T, int H, int k) {
-  const int64_t base = T * (H / (16 * mla_waves(H)));
+  const int64_t base = T * (H / mla_heads_per_wg(H));
   const int ntiles = (k + 31) / 32;
   if (base <= 0 || base >= 256) return 1;
   int s = (int)((256 + base - 1) / base);

@@ -31,12 +31,14 @@
 namespace {
 
 constexpr int kBN = 32;                  // selected rows per tile
-constexpr int kRowSlots = 73;            // 16-byte slots per LDS row: 72 of data + 1 pad (bank spread)
+constexpr int kRowSlots = 74;            // 16-byte slots per LDS row: 72 of data + 2 pad; a row stride
+                                         // of 40 dwords mod 64 keeps both tile read patterns conflict-free
 constexpr int kCRow = kRowSlots * 16;    // LDS bytes per gathered row
 constexpr int kTileBytes = kBN * kCRow;  // 37376
 constexpr int kTileSlots = kBN * kRowSlots;
 constexpr int kGatherInsts = (kTileSlots + 63) / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
-constexpr int kSmemMla = 2 * kTileBytes + 2048 * 4;
+constexpr int kPBytes = 8 * 64 * 16;    // P^T of up to 8 head tiles, in B-operand lane order
+constexpr int kSmemMla = 2 * kTileBytes + kPBytes + 128 * 4 + 2048 * 4 + 16;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -58,8 +60,8 @@ __device__ __forceinline__ int64_t phys_row(const int32_t *__restrict__ irow, co
 // Issue the direct-to-LDS loads of tile rows [r0, r0+32) of this workgroup's
 // selection (rows[] holds physical rows, -1 for skipped entries, which load
 // row 0 instead and are masked later).  Instruction i of the tile writes LDS
-// slots [64i, 64i+64); slot s holds row s/73, 16-byte chunk s%73 (chunk 72 is
-// padding and reloads chunk 71).
+// slots [64i, 64i+64); slot s holds row s/74, 16-byte chunk s%74 (chunks 72
+// and 73 are padding and reload chunk 71).
 template <int NW>
 __device__ __forceinline__ void gather_tile_async(uint8_t *__restrict__ dst, const int *__restrict__ rows,
                                                   int r0, const __bf16 *__restrict__ kv, int wave, int lane) {
@@ -76,6 +78,195 @@ __device__ __forceinline__ void gather_tile_async(uint8_t *__restrict__ dst, con
   }
 }
 
+// Shared state of one sparse-MLA workgroup.
+struct MlaCtx {
+  const __bf16 *kv;
+  uint8_t *tiles;       // 2 x kTileBytes of LDS
+  uint8_t *pbuf;        // P^T exchange: [head tile][lane] x 16 bytes
+  float *lbuf;          // softmax sums of the workgroup's heads
+  const int *rows;      // physical rows of the workgroup's entries (LDS)
+  int *flag;            // LDS: set when a tile overshoots the softmax reference
+  int tb, te;           // tile range of this workgroup
+  int wave, lane, g, c;
+};
+
+// Logits of one tile for the wave's 16 heads: S^T[keys, heads] for key
+// blocks [0,16) and [16,32), scaled to base 2 and masked; lane (g,c) gets
+// x[r] = key 4g+r and x[4+r] = key 16+4g+r of head c.  The LDS operands of
+// step s+1 are requested before the MFMAs of step s; the scheduling fences
+// keep at most two steps of operands live.
+__device__ __forceinline__ void tile_logits(const uint8_t *__restrict__ ct, const int *__restrict__ rv,
+                                            const bf16x8 (&qr)[18], float scale_log2, int g, int c,
+                                            float (&x)[8]) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t *arow0 = ct + c * kCRow + g * 16;
+  const uint8_t *arow1 = arow0 + 16 * kCRow;
+  bf16x8 op[2][2];
+  op[0][0] = *reinterpret_cast<const bf16x8 *>(arow0);
+  op[0][1] = *reinterpret_cast<const bf16x8 *>(arow1);
+#pragma unroll
+  for (int s = 0; s < 18; ++s) {
+    const int cs = s & 1;
+    if (s + 1 < 18) {
+      op[cs ^ 1][0] = *reinterpret_cast<const bf16x8 *>(arow0 + (s + 1) * 64);
+      op[cs ^ 1][1] = *reinterpret_cast<const bf16x8 *>(arow1 + (s + 1) * 64);
+    }
+    s0 = mfma_bf16_16x16x32(op[cs][0], qr[s], s0);
+    s1 = mfma_bf16_16x16x32(op[cs][1], qr[s], s1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = rv[4 * g + r] >= 0 ? s0[r] * scale_log2 : -INFINITY;
+    x[4 + r] = rv[16 + 4 * g + r] >= 0 ? s1[r] * scale_log2 : -INFINITY;
+  }
+}
+
+// Max over the tile's keys for the lane's head (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float tile_max(const float (&x)[8]) {
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// Walk the workgroup's tiles: wait for tile i, barrier, prefetch tile i+1,
+// then body(ct, rv) on tile i.  The gather of tile i+1 overlaps the body.
+template <int NW, typename Body>
+__device__ __forceinline__ void for_each_tile(const MlaCtx &cx, Body &&body) {
+  if (cx.tb < cx.te) gather_tile_async<NW>(cx.tiles, cx.rows, 0, cx.kv, cx.wave, cx.lane);
+  int cur = 0;
+  for (int tile = cx.tb; tile < cx.te; ++tile, cur ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of `tile` have landed in LDS
+    __syncthreads();                // ... and every wave's; the other buffer is no longer read
+    if (tile + 1 < cx.te)
+      gather_tile_async<NW>(cx.tiles + (cur ^ 1) * kTileBytes, cx.rows, (tile + 1 - cx.tb) * kBN, cx.kv, cx.wave,
+                            cx.lane);
+    body(cx.tiles + cur * kTileBytes, cx.rows + (tile - cx.tb) * kBN);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// One accumulation pass over the workgroup's tiles.
+//  * Logits/softmax: wave w owns head tile w (heads 16w..16w+15 of the
+//    workgroup).  It turns its logits into bf16 probabilities and publishes
+//    them, already in the PV B-operand lane order, in LDS.
+//  * PV: wave w owns value dims [w*512/NW, (w+1)*512/NW) for ALL NW head
+//    tiles: O^T[dv, head] += V^T[dv, keys] P^T[keys, head].  V^T comes from
+//    the row-major tile through the transposing LDS load, P^T from LDS.
+//    Splitting PV by value dims reads each tile's values once per workgroup
+//    instead of once per wave.
+// fixed = false: each head's exponent reference is the max of its first tile
+// with a valid entry; a later tile more than 64 above it sets cx.flag and the
+// pass is discarded (returns false, nothing written).  fixed = true: the
+// references are given (exact maxima).
+template <int NW, bool fixed>
+__device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18], float &m_ref, float scale_log2,
+                                         int64_t t, int H, int hw0, __bf16 *__restrict__ out,
+                                         float *__restrict__ lse, int splits, int sp, float *__restrict__ part_o,
+                                         float *__restrict__ part_ml) {
+  constexpr int MT = 32 / NW;  // value-dim tiles of 16 per wave
+  const int g = cx.g, c = cx.c, wave = cx.wave;
+  f32x4 o[MT][NW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int n = 0; n < NW; ++n) o[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float l_run = 0.0f;
+  // transposing-load lane roles: row 4g + (c>>2) of each 4-row group, value chunk (c&3),
+  // starting at this wave's first value tile
+  const int tr_off = (4 * g + (c >> 2)) * kCRow + (c & 3) * 8 + wave * MT * 32;
+  for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
+    float x[8];
+    tile_logits(ct, rv, qr, scale_log2, g, c, x);
+    bool over = false;
+    if (!fixed) {
+      const float mx = tile_max(x);
+      if (m_ref == -INFINITY) m_ref = mx;  // O and l are still zero for this head
+      over = mx > m_ref + 64.0f;
+    }
+    const float msub = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    bf16x8 pb;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = exp2f(fminf(x[i] - msub, 64.0f));
+      psum += p;
+      pb[i] = (__bf16)p;
+    }
+    l_run += psum;
+    if (!fixed && __ballot(over) && cx.lane == 0) *cx.flag = 1;
+    *reinterpret_cast<bf16x8 *>(cx.pbuf + (wave * 64 + cx.lane) * 16) = pb;
+    __syncthreads();  // every head tile's P is in LDS
+    // value operands of this wave's MT tiles (keys 4g..4g+3 | 16+4g..16+4g+3)
+    bf16x8 va[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(ct + tr_off + i * 32));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(ct + tr_off + i * 32 + 16 * kCRow));
+      const i16x4 lohi[2] = {lo, hi};
+      va[i] = *reinterpret_cast<const bf16x8 *>(lohi);
+    }
+    bf16x8 pn[2];
+    pn[0] = *reinterpret_cast<const bf16x8 *>(cx.pbuf + cx.lane * 16);
+#pragma unroll
+    for (int n = 0; n < NW; ++n) {
+      if (n + 1 < NW) pn[(n + 1) & 1] = *reinterpret_cast<const bf16x8 *>(cx.pbuf + ((n + 1) * 64 + cx.lane) * 16);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) o[i][n] = mfma_bf16_16x16x32(va[i], pn[n & 1], o[i][n]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  });
+  if (!fixed && *cx.flag) return false;  // uniform: read after the final barrier
+  // softmax sums of the wave's head tile -> LDS, for the waves that own other value dims
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (g == 0) cx.lbuf[wave * 16 + c] = l_tot;
+  const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
+  const int head_own = hw0 + wave * 16 + c;
+  if (g == 0) {
+    if (splits == 1) {
+      if (lse) lse[t * H + head_own] = l_tot > 0.0f ? (mr + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    } else {
+      float *pm = part_ml + ((t * splits + sp) * H + head_own) * 2;
+      pm[0] = l_tot > 0.0f ? mr : -INFINITY;
+      pm[1] = l_tot;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < NW; ++n) {
+    const int head = hw0 + n * 16 + c;
+    const float lh = cx.lbuf[n * 16 + c];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int dv = (wave * MT + i) * 16 + 4 * g;
+      if (splits == 1) {
+        const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[i][n][r] * inv);
+        *reinterpret_cast<bf16x4 *>(out + (t * H + head) * 512 + dv) = v;
+      } else {
+        *reinterpret_cast<f32x4 *>(part_o + ((t * splits + sp) * H + head) * 512 + dv) = o[i][n];
+      }
+    }
+  }
+  return true;
+}
+
+// NW waves: 16*NW heads per workgroup; for the logits wave w owns 16 heads,
+// for PV it owns 512/NW value dims of all 16*NW heads.
+//
+// Softmax reference: each head's exponent reference m_ref (base 2, scale
+// folded in) is the max of the first tile in which the head has a valid
+// entry, and then stays fixed, so the accumulators are only ever written by
+// MFMAs.  Probabilities are exp2(x - m_ref); while x <= m_ref + 64 they stay
+// below 2^64, far inside the fp32/bf16 range, and the result is the same
+// softmax.  If any tile overshoots that, the workgroup instead takes the
+// exact per-head maxima in an extra logits-only pass and accumulates again.
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
@@ -83,8 +274,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
     __bf16 *__restrict__ out, float *__restrict__ lse, int splits, float *__restrict__ part_o,
     float *__restrict__ part_ml) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  uint8_t *tiles = smem_raw;                                        // 2 x kTileBytes
-  int *rows = reinterpret_cast<int *>(smem_raw + 2 * kTileBytes);   // <= 2048 physical rows
+  MlaCtx cx;
+  cx.kv = kv;
+  cx.tiles = smem_raw;
+  cx.pbuf = smem_raw + 2 * kTileBytes;
+  cx.lbuf = reinterpret_cast<float *>(cx.pbuf + kPBytes);
+  int *rows = reinterpret_cast<int *>(cx.lbuf + 128);   // <= 2048 physical rows
+  cx.rows = rows;
+  cx.flag = rows + 2048;
 
   const int n_hg = H / (16 * NW);
   const int bid = blockIdx.x;
@@ -92,128 +289,40 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
   const int rest = bid / splits;
   const int hg = rest % n_hg;
   const int64_t t = rest / n_hg;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int h0 = (hg * NW + wave) * 16;
+  const int tid = threadIdx.x;
+  cx.wave = tid >> 6;
+  cx.lane = tid & 63;
+  cx.g = cx.lane >> 4;
+  cx.c = cx.lane & 15;
+  const int hw0 = hg * NW * 16;  // first head of the workgroup
   const int ntiles = (k + kBN - 1) / kBN;
   const int per = (ntiles + splits - 1) / splits;
-  const int tb = sp * per, te = min(ntiles, tb + per);
+  cx.tb = sp * per;
+  cx.te = min(ntiles, cx.tb + per);
   const int32_t *irow = idx + t * k;
 
   // physical rows of this workgroup's entries [tb*32, te*32)
-  for (int e = tid; e < (te - tb) * kBN; e += NW * 64)
-    rows[e] = (int)phys_row(irow, bt, max_blocks, N, t, tb * kBN + e, k);
+  for (int e = tid; e < (cx.te - cx.tb) * kBN; e += NW * 64)
+    rows[e] = (int)phys_row(irow, bt, max_blocks, N, t, cx.tb * kBN + e, k);
+  if (tid == 0) *cx.flag = 0;
   __syncthreads();
-  if (tb < te) gather_tile_async<NW>(tiles, rows, 0, kv, wave, lane);
 
-  // Q^T in registers: lane (g, c) holds head h0+c, dims 32*s + 8*g .. +8 for step s.
+  // Q^T of the wave's head tile in registers: lane (g, c) holds head
+  // hw0 + 16*wave + c, dims 32*s + 8*g .. +8 for step s.
   bf16x8 qr[18];
-  const __bf16 *qrow = q + (t * H + h0 + c) * 576 + g * 8;
+  const __bf16 *qrow = q + (t * H + hw0 + 16 * cx.wave + cx.c) * 576 + cx.g * 8;
 #pragma unroll
   for (int s = 0; s < 18; ++s) qr[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
-
-  f32x4 o[32];
-#pragma unroll
-  for (int m = 0; m < 32; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  // transposing-load lane roles: row 4g + (c>>2) of each 4-row group, value chunk (c&3)
-  const int tr_row = 4 * g + (c >> 2), tr_col = (c & 3) * 4;
-
-  for (int tile = tb; tile < te; ++tile) {
-    const int cur = (tile - tb) & 1;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of `tile` have landed in LDS
-    __syncthreads();                // ... and every wave's; tile-1 is no longer read
-    if (tile + 1 < te)
-      gather_tile_async<NW>(tiles + (cur ^ 1) * kTileBytes, rows, (tile + 1 - tb) * kBN, kv, wave, lane);
-    const uint8_t *ct = tiles + cur * kTileBytes;
-    const int *rv = rows + (tile - tb) * kBN;
-    // S^T for keys [0,16) and [16,32) of the tile
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 18; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(ct + c * kCRow + (s * 32 + g * 8) * 2);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(ct + (16 + c) * kCRow + (s * 32 + g * 8) * 2);
-      s0 = mfma_bf16_16x16x32(a0, qr[s], s0);
-      s1 = mfma_bf16_16x16x32(a1, qr[s], s1);
-    }
-    // keep LDS reads close to their MFMAs (bounds live registers)
-#pragma unroll
-    for (int s = 0; s < 18; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    // lane (g,c): x[r] = key 4g+r, x[4+r] = key 16+4g+r, head c
+  float m_ref = -INFINITY;
+  if (mla_pass<NW, false>(cx, qr, m_ref, scale_log2, t, H, hw0, out, lse, splits, sp, part_o, part_ml)) return;
+  // rare: exact per-head maxima, then accumulate with them
+  m_ref = -INFINITY;
+  for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
     float x[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = rv[4 * g + r] >= 0 ? s0[r] * scale_log2 : -INFINITY;
-      x[4 + r] = rv[16 + 4 * g + r] >= 0 ? s1[r] * scale_log2 : -INFINITY;
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
-    float p[8], psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = exp2f(x[i] - msub);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int m = 0; m < 32; ++m) o[m] *= alpha;
-    }
-    m_run = m_new;
-    bf16x8 pb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
-    // O^T[dv, head] += V^T[dv, keys] P^T[keys, head]; key slot order matches pb
-    const uint8_t *tr0 = ct + tr_row * kCRow + tr_col * 2;
-    const uint8_t *tr1 = tr0 + 16 * kCRow;
-#pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tr0 + m * 32));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tr1 + m * 32));
-      const i16x4 lohi[2] = {lo, hi};
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lohi);
-      o[m] = mfma_bf16_16x16x32(a, pb, o[m]);
-    }
-#pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    }
-  }
-
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const int head = h0 + c;
-  if (splits == 1) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    __bf16 *orow = out + (t * H + head) * 512;
-#pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      bf16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[m][r] * inv);
-      *reinterpret_cast<bf16x4 *>(orow + 16 * m + 4 * g) = v;
-    }
-    if (lse && g == 0)
-      lse[t * H + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-  } else {
-    float *po = part_o + ((t * splits + sp) * H + head) * 512;
-#pragma unroll
-    for (int m = 0; m < 32; ++m) *reinterpret_cast<f32x4 *>(po + 16 * m + 4 * g) = o[m];
-    if (g == 0) {
-      float *pm = part_ml + ((t * splits + sp) * H + head) * 2;
-      pm[0] = m_run;
-      pm[1] = l_tot;
-    }
-  }
+    tile_logits(ct, rv, qr, scale_log2, cx.g, cx.c, x);
+    m_ref = fmaxf(m_ref, tile_max(x));
+  });
+  mla_pass<NW, true>(cx, qr, m_ref, scale_log2, t, H, hw0, out, lse, splits, sp, part_o, part_ml);
 }
 
 // LSE-weighted combine of split partials.  grid (T*H/4), block 256: 4 heads,
@@ -328,7 +437,7 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
     attr_done = true;
   }
   const int64_t blocks = (int64_t)T * (H / (16 * NW)) * splits;
-  hipLaunchKernelGGL(sparse_mla_bf16_kernel<NW>, dim3((uint32_t)blocks), dim3(NW * 64), kSmemMla, s,
+  hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW>), dim3((uint32_t)blocks), dim3(NW * 64), kSmemMla, s,
                      (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
                      (__bf16 *)out, lse, splits, part_o, part_ml);
   return hipGetLastError();

@@ -436,3 +436,24 @@ def test_prefill_select_equals_prefill_selection(dsa):
     dsa.dsa_prefill_select(args)
     torch.cuda.synchronize()
     assert torch.equal(idx2, t["idx"])
+
+
+@pytest.mark.parametrize("H", [128, 16])
+def test_sparse_mla_bf16_late_large_logits(dsa, ora, H):
+    """Logits in a late tile far above the first tile's (over 2^64 in base 2)
+    for some heads: the result must still be the exact softmax."""
+    _say(f"sparse mla bf16 late large logits H={H}")
+    N, T, k = 3000, 3, 2048
+    q = synth.normal(13, 1, (T, H, 576)) * 0.5
+    kv = synth.normal(13, 2, (N, 576), std=1 / 24)
+    q[:, ::3, 0] = 30.0            # every third head looks along dim 0
+    kv[:, 0] = 0.01
+    late = torch.arange(2500, 2520)
+    kv[late, 0] = 100.0            # logit 3000 * sm_scale for those heads, only in late rows
+    q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
+    idx = torch.stack([torch.arange(k) + t * 100 for t in range(T)]).to(torch.int32)
+    idx[idx >= N] = -1
+    g, gl = _mla_gpu(dsa, q, kv, idx, 1 / math.sqrt(192), "bf16", use_ws=True)
+    o, l = ora.sparse_mla_rows(q, kv, idx.numpy(), 1 / math.sqrt(192))
+    assert np.isfinite(g).all() and np.isfinite(gl).all()
+    check_attention(g, gl, o, l, "bf16", "mla late large logits")
