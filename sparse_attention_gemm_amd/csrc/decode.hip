@@ -34,16 +34,12 @@ __global__ __launch_bounds__(256) void decode_indexer_kernel(
     if (s0 + lane < ctx) scores[b * ld + s0 + lane] = -INFINITY;
     return;
   }
-  IdxQuery<2> Q;
-  idx_load_query<2>(Q, q8 + b * 64 * 128, w + b * 64, qs[b], lane);
-  const uint8_t *pk = k8_pool + prow * 128;
-  i32x8 bb[2][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      bb[u][kk] = *reinterpret_cast<const i32x8 *>(pk + (u * 32 + (lane & 31)) * 128 + kk * 64 + (lane >> 5) * 32);
-  const float tot = idx_score64<2>(Q, bb);
+  IdxHalf Q0, Q1;
+  idx_load_half(Q0, q8 + b * 64 * 128, w + b * 64, qs[b], 0, lane);
+  idx_load_half(Q1, q8 + b * 64 * 128, w + b * 64, qs[b], 32, lane);
+  i32x8 kb[4];
+  idx_load_keys(kb, k8_pool + prow * 128, 128, lane);  // the page's 64 keys are contiguous
+  const float tot = idx_half_score64(Q0, kb) + idx_half_score64(Q1, kb);
   const int s = s0 + lane;
   if (s < ctx) scores[b * ld + s] = canon_zero(tot * ks_pool[prow + lane]);
 }

@@ -10,12 +10,13 @@ namespace {
 constexpr int kTilesPerWave = 8;  // 512 keys per wave: amortises the query load
 
 // grid: (ceil(S / (64*kTilesPerWave)), ceil(T/4)); 4 waves, one token each.
-template <int NHT>
+// NHALF head halves of 32 (H_I = 32 * NHALF).
+template <int NHALF>
 __global__ __launch_bounds__(256) void indexer_scores_fp8_kernel(
     const uint8_t *__restrict__ q8, const float *__restrict__ qs, const uint8_t *__restrict__ k8,
     const float *__restrict__ ks, const float *__restrict__ w, const int32_t *__restrict__ q_pos,
     int32_t T, int32_t S, float *__restrict__ scores, int64_t ld) {
-  constexpr int H_I = 32 * NHT;
+  constexpr int H_I = 32 * NHALF;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.y * 4 + wave;
   if (t >= T) return;
@@ -27,23 +28,25 @@ __global__ __launch_bounds__(256) void indexer_scores_fp8_kernel(
     for (int s = sbeg + lane; s < send; s += 64) orow[s] = -INFINITY;
     return;
   }
-  IdxQuery<NHT> Q;
-  idx_load_query<NHT>(Q, q8 + (int64_t)t * H_I * 128, w + (int64_t)t * H_I, qs[t], lane);
+  IdxHalf Q[NHALF];
+#pragma unroll
+  for (int h = 0; h < NHALF; ++h)
+    idx_load_half(Q[h], q8 + (int64_t)t * H_I * 128, w + (int64_t)t * H_I, qs[t], 32 * h, lane);
+  const int g = lane >> 4, c = lane & 15;
   for (int s0 = sbeg; s0 < send; s0 += 64) {
     const int s = s0 + lane;
     if (s0 > p) {
       if (s < send) orow[s] = -INFINITY;
       continue;
     }
-    i32x8 b[2][2];
+    i32x8 b[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = min(s0 + u * 32 + (lane & 31), S - 1);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        b[u][kk] = *reinterpret_cast<const i32x8 *>(k8 + (int64_t)key * 128 + kk * 64 + (lane >> 5) * 32);
+    for (int u = 0; u < 4; ++u) {
+      const int key = min(s0 + 16 * u + c, S - 1);
+      b[u] = *reinterpret_cast<const i32x8 *>(k8 + (int64_t)key * 128 + 32 * g);
     }
-    const float tot = idx_score64<NHT>(Q, b);
+    float tot = idx_half_score64(Q[0], b);
+    if (NHALF == 2) tot = tot + idx_half_score64(Q[NHALF - 1], b);
     if (s < send) orow[s] = (s <= p) ? canon_zero(tot * ks[s]) : -INFINITY;
   }
 }

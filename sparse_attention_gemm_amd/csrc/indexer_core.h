@@ -5,67 +5,86 @@
 // there, the head-weighted form is the workload's definition):
 //     I[t,s] = sum_j w[t,j] * ReLU(qs[t] ks[s] <q8[t,j], k8[s]>)
 //            = ks[s] * sum_j (w[t,j] qs[t]) * ReLU(<q8[t,j], k8[s]>)    (qs, ks > 0)
-// The dot products are E4M3 x E4M3 MFMAs (32x32x64, exact products, fp32
-// sums); D_I = 128 is two K steps.  Heads run along the MFMA rows (32 per
-// tile), keys along the columns.  Each lane then holds 16 heads of one key
-// per head tile and applies ReLU and its head weights in registers; the two
-// lane halves hold complementary heads and are combined with one
-// permlane32 swap, which also scatters the 64 keys of the tile one per lane.
+// The dot products are E4M3 x E4M3 MFMAs (16x16x128: the whole D_I = 128 in
+// one instruction; products exact, fp32 sums).  Heads run along the MFMA
+// rows, keys along the columns: lane (g = l/16, c = l%16) receives 4 heads
+// (4g..4g+3 of a 16-head tile) of key c and applies ReLU and its head
+// weights in registers.  A 64-key tile is 4 key blocks of 16; the four lane
+// groups' partial sums are then reduce-scattered with two permlane swaps so
+// that lane l ends up with key l of the tile.
 //
-// Every kernel that produces index scores goes through idx_score64(), so the
-// unfused score matrix and the fused streaming top-k see identical values.
+// Heads are processed in halves of 32 (two 16-head tiles).  The score of a
+// key is   half(heads 0..31) + half(heads 32..63),   each half with a fixed
+// accumulation order, so a kernel that splits the halves across two
+// wavefronts produces exactly the same fp32 value as one that computes both.
 #pragma once
 #include "dsa_common.h"
 
-template <int NHT>  // head tiles of 32: H_I = 32 * NHT
-struct IdxQuery {
-  i32x8 a[NHT][2];     // A operand: q8 rows (heads) x 64-byte K steps
-  float w[NHT][16];    // head weight (times q scale) of this lane's 16 rows per tile
-};
-
-// q8_t: the token's [H_I][128] payload; w_t: its [H_I] weights.
-template <int NHT>
-__device__ __forceinline__ void idx_load_query(IdxQuery<NHT> &Q, const uint8_t *__restrict__ q8_t,
-                                               const float *__restrict__ w_t, float qs, int lane) {
-  const int row = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      Q.a[ht][ks] = *reinterpret_cast<const i32x8 *>(q8_t + (ht * 32 + row) * 128 + ks * 64 + half * 32);
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int head = ht * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-      Q.w[ht][r] = w_t[head] * qs;
-    }
+// FP8 MFMA 16x16x128 (E4M3 x E4M3): lane l holds A[row l%16][k 32(l/16) .. +32]
+// and B[k ..][col l%16]; register r of the result is D[4(l/16) + r][l%16].
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8 &a, const i32x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// b[u][ks]: B operand of sub-tile u (keys u*32 + lane%32), bytes ks*64 + (lane/32)*32.
-// Returns, in lane l, sum_j w'_j ReLU(<q8_j, k8[key l of the tile]>) (without ks).
-template <int NHT>
-__device__ __forceinline__ float idx_score64(const IdxQuery<NHT> &Q, const i32x8 (&b)[2][2]) {
-  float part[2];
-  f32x16 c[2][NHT];
+// x + (the same register of lane l^32), for two registers at once: returns
+// lanes 0-31: x[l] + x[l+32];  lanes 32-63: y[l-32] + y[l].
+__device__ __forceinline__ float swap32_sum(float x, float y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Same across 16-lane rows: rows 0,2 get x summed with the next row, rows 1,3
+// get y summed with the previous row.
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One half (32 heads) of a query's indexer heads.
+struct IdxHalf {
+  i32x8 a[2];      // A operand: 16-head tiles x 128 bytes
+  float w[2][4];   // head weight (times q scale) of this lane's 4 rows per tile
+};
+
+// q8_t: the token's [H_I][128] payload; w_t its [H_I] weights; head0: first head of the half.
+__device__ __forceinline__ void idx_load_half(IdxHalf &Q, const uint8_t *__restrict__ q8_t,
+                                              const float *__restrict__ w_t, float qs, int head0, int lane) {
+  const int g = lane >> 4, c = lane & 15;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int i = 0; i < 2; ++i) {
+    Q.a[i] = *reinterpret_cast<const i32x8 *>(q8_t + (head0 + 16 * i + c) * 128 + 32 * g);
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      f32x16 z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      z = mfma_fp8_32x32x64(Q.a[ht][0], b[u][0], z);
-      c[u][ht] = mfma_fp8_32x32x64(Q.a[ht][1], b[u][1], z);
-    }
+    for (int r = 0; r < 4; ++r) Q.w[i][r] = w_t[head0 + 16 * i + 4 * g + r] * qs;
+  }
+}
+
+// b[u]: B operand of key block u (keys 16u + lane%16), bytes 32*(lane/16) .. +32.
+// Returns, in lane l, sum over the half's heads of w' ReLU(<q8_j, k8[key l]>) (without ks).
+__device__ __forceinline__ float idx_half_score64(const IdxHalf &Q, const i32x8 (&b)[4]) {
+  f32x4 d[4][2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) d[u][i] = mfma_fp8_16x16x128(Q.a[i], b[u], f32x4{0.f, 0.f, 0.f, 0.f});
+  float v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
     float p = 0.0f;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p = fmaf(Q.w[ht][r], fmaxf(c[u][ht][r], 0.0f), p);
-    part[u] = p;
+      for (int r = 0; r < 4; ++r) p = fmaf(Q.w[i][r], fmaxf(d[u][i][r], 0.0f), p);
+    v[u] = p;
   }
-  // lanes 0-31: sub-tile 0 summed over both halves; lanes 32-63: sub-tile 1.
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
-  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  // lane groups g = 0..3 hold 4 heads each of the same keys: sum them, and
+  // scatter the four key blocks so that lane l holds key l
+  const float s02 = swap32_sum(v[0], v[2]);  // rows 0,1: block 0 (g, g+2); rows 2,3: block 2
+  const float s13 = swap32_sum(v[1], v[3]);  // rows 0,1: block 1;          rows 2,3: block 3
+  return swap16_sum(s02, s13);               // row 0: block 0, row 1: block 1, row 2: block 2, row 3: block 3
+}
+
+// B operands of a 64-key tile whose rows are `stride` bytes apart.
+__device__ __forceinline__ void idx_load_keys(i32x8 (&b)[4], const uint8_t *__restrict__ rows, int stride, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) b[u] = *reinterpret_cast<const i32x8 *>(rows + (16 * u + c) * stride + 32 * g);
 }

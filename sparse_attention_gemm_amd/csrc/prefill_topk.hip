@@ -6,11 +6,18 @@
 // "How it works" (index score of each query against its preceding tokens,
 // then the top-k KV entries per query, k = 2048); m.digipub.cc, section 2.
 //
-// Workgroup = 4 wavefronts = 4 consecutive query tokens, one per wave.  Key
-// tiles (64 keys x 128 B of E4M3 + 64 fp32 scales) are staged in LDS once
-// and shared by the four waves (double buffered, one barrier per tile).
-// Each wave owns a 4096-entry candidate buffer in LDS holding (order key,
-// position) pairs in ascending position order, plus a threshold tau:
+// Workgroup = 8 wavefronts = 4 consecutive query tokens; each token's 64
+// indexer heads are split over a pair of waves (heads 0..31 and 32..63), so
+// one wave's ReLU/weight epilogue (VALU) overlaps the other's MFMAs on the
+// same SIMD.  Key tiles (64 keys x 128 B of E4M3 + 64 fp32 scales) are
+// loaded straight into LDS (direct-to-LDS loads, double buffered, one
+// barrier per tile) and shared by all eight waves.  The first wave of a pair
+// publishes its half-score of each key in LDS; one tile later the second
+// wave adds it to its own half and runs the selection.
+//
+// The second wave of each pair owns the token's 4096-entry candidate buffer
+// in LDS holding (order key, position) pairs in ascending position order,
+// plus a threshold tau:
 //   * a key enters the buffer if its order key >= tau (keys arrive in
 //     increasing position, so a new key that ties tau outranks it);
 //   * when the buffer would overflow, it is compacted in place to exactly
@@ -25,18 +32,24 @@
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kTok = 4;         // query tokens per workgroup
+constexpr int kWaves = 8;       // two per token
 constexpr int kCap = 4096;      // candidate buffer entries per query
 constexpr int kTile = 64;       // keys per tile
-constexpr int kRowB = 144;      // LDS bytes per key row (128 + 16 pad: spreads banks)
+constexpr int kKRow = 160;      // LDS bytes per key row: 128 + 32 pad (40 dwords mod 64: conflict-free reads)
+constexpr int kKSlots = kKRow / 16;
+constexpr int kKeyInsts = kTile * kKSlots / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
 constexpr int kBins = 256;      // compaction histogram
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 struct PrefillShared {
-  uint8_t keys[2][kTile * kRowB];
+  uint8_t keys[2][kTile * kKRow];
   float ksc[2][kTile];
-  uint32_t bkey[kWaves][kCap];
-  uint32_t bpos[kWaves][kCap];
-  uint32_t hist[kWaves][kBins];
+  float part[2][kTok][kTile];   // half-scores (heads 0..31) of the current and previous tile
+  uint32_t bkey[kTok][kCap];
+  uint32_t bpos[kTok][kCap];
+  uint32_t hist[kTok][kBins];
 };
 
 // Compact buf[0..n) to its `keep` best entries (order key desc, position desc),
@@ -131,70 +144,62 @@ __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict
   return tau;
 }
 
-__device__ __forceinline__ void load_tile_regs(const uint8_t *__restrict__ k8, const float *__restrict__ ks,
-                                               int L, int tile, int tid, i32x4 &r0, i32x4 &r1, float &sv) {
-  // thread tid: key tid/4 of the tile, bytes (tid%4)*32 .. +32
-  const int key = min(tile * kTile + (tid >> 2), L - 1);
-  const uint8_t *src = k8 + (int64_t)key * 128 + (tid & 3) * 32;
-  r0 = *reinterpret_cast<const i32x4 *>(src);
-  r1 = *reinterpret_cast<const i32x4 *>(src + 16);
-  sv = (tid < kTile) ? ks[min(tile * kTile + tid, L - 1)] : 0.0f;
+// Issue the direct-to-LDS loads of key tile `tile` into buffer `buf`.
+// Instruction i writes slots [64i, 64i+64); slot s holds row s/10, 16-byte
+// chunk s%10 (chunks 8, 9 are padding and reload chunk 7).  Keys past L-1
+// read key L-1 (never selected: they are beyond every query of the sequence).
+__device__ __forceinline__ void load_tile_async(PrefillShared &sm, int buf, const uint8_t *__restrict__ k8,
+                                                const float *__restrict__ ks, int L, int tile, int wave, int lane) {
+#pragma unroll
+  for (int i = wave; i < kKeyInsts; i += kWaves) {
+    const int slot = i * 64 + lane;
+    const int r = slot / kKSlots;
+    const int j = min(slot - r * kKSlots, 7);
+    const int key = min(tile * kTile + r, L - 1);
+    __builtin_amdgcn_global_load_lds(k8 + (int64_t)key * 128 + j * 16, (lds_void *)(sm.keys[buf] + i * 1024), 16, 0,
+                                     0);
+  }
+  if (wave == kWaves - 1) {
+    const int key = min(tile * kTile + lane, L - 1);
+    __builtin_amdgcn_global_load_lds(ks + key, (lds_void *)sm.ksc[buf], 4, 0, 0);
+  }
 }
 
-__device__ __forceinline__ void store_tile_lds(PrefillShared &sm, int buf, int tid, const i32x4 &r0,
-                                               const i32x4 &r1, float sv) {
-  uint8_t *dst = sm.keys[buf] + (tid >> 2) * kRowB + (tid & 3) * 32;
-  *reinterpret_cast<i32x4 *>(dst) = r0;
-  *reinterpret_cast<i32x4 *>(dst + 16) = r1;
-  if (tid < kTile) sm.ksc[buf][tid] = sv;
-}
-
-__global__ __launch_bounds__(256, 1) void prefill_indexer_topk_kernel(
+__global__ __launch_bounds__(kWaves * 64, 1) void prefill_indexer_topk_kernel(
     const uint8_t *__restrict__ q8, const float *__restrict__ qs, const uint8_t *__restrict__ k8,
     const float *__restrict__ ks, const float *__restrict__ w, int32_t L, int32_t k,
     int32_t *__restrict__ idx) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   PrefillShared &sm = *reinterpret_cast<PrefillShared *>(smem_raw);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = gridDim.x - 1 - blockIdx.x;  // longest rows first
-  const int t0 = g * kWaves;
-  const int t = t0 + wave;
+  const int tok = wave >> 1, half = wave & 1;
+  const int grp = gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int t0 = grp * kTok;
+  const int t = t0 + tok;
   const bool active = t < L;
   const int tq = min(t, L - 1);
-  const int last = min(t0 + kWaves - 1, L - 1);
+  const int last = min(t0 + kTok - 1, L - 1);
   const int ntiles = last / kTile + 1;
 
-  IdxQuery<2> Q;
-  idx_load_query<2>(Q, q8 + (int64_t)tq * 64 * 128, w + (int64_t)tq * 64, qs[tq], lane);
+  IdxHalf Q;
+  idx_load_half(Q, q8 + (int64_t)tq * 64 * 128, w + (int64_t)tq * 64, qs[tq], 32 * half, lane);
 
-  uint32_t *bk = sm.bkey[wave];
-  uint32_t *bp = sm.bpos[wave];
-  uint32_t *hist = sm.hist[wave];
+  uint32_t *bk = sm.bkey[tok];
+  uint32_t *bp = sm.bpos[tok];
+  uint32_t *hist = sm.hist[tok];
   int nbuf = 0;
   uint32_t thr = 0u;
+  float prev = 0.0f, prev_ks = 0.0f;  // second wave: its half-score and the key scale of the last tile
 
-  i32x4 r0, r1;
-  float sv;
-  load_tile_regs(k8, ks, L, 0, tid, r0, r1, sv);
-  store_tile_lds(sm, 0, tid, r0, r1, sv);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
+  load_tile_async(sm, 0, k8, ks, L, 0, wave, lane);
+  for (int it = 0; it <= ntiles; ++it) {
     const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile_regs(k8, ks, L, it + 1, tid, r0, r1, sv);
-    const int s0 = it * kTile;
-    if (active && s0 <= t) {
-      i32x8 b[2][2];
-      const uint8_t *kt = sm.keys[buf];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          b[u][kk] = *reinterpret_cast<const i32x8 *>(kt + (u * 32 + (lane & 31)) * kRowB + kk * 64 +
-                                                       (lane >> 5) * 32);
-      const float tot = idx_score64<2>(Q, b);
-      const int s = s0 + lane;
-      const float v = canon_zero(tot * sm.ksc[buf][lane]);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed in LDS
+    __syncthreads();                // ... and every wave's; tile it-1's buffer is free
+    if (half == 1 && active && it > 0) {
+      // score of key (it-1)*64 + lane = half(0..31) + half(32..63), times its scale
+      const int s = (it - 1) * kTile + lane;
+      const float v = canon_zero((sm.part[buf ^ 1][tok][lane] + prev) * prev_ks);
       const uint32_t key = score_key(v);
       const bool valid = s <= t;
       bool pass = valid && key >= thr;
@@ -213,11 +218,22 @@ __global__ __launch_bounds__(256, 1) void prefill_indexer_topk_kernel(
       }
       nbuf += cnt;
     }
-    if (it + 1 < ntiles) store_tile_lds(sm, buf ^ 1, tid, r0, r1, sv);
-    __syncthreads();
+    if (it == ntiles) break;
+    if (it + 1 < ntiles) load_tile_async(sm, buf ^ 1, k8, ks, L, it + 1, wave, lane);
+    if (active) {
+      i32x8 b[4];
+      idx_load_keys(b, sm.keys[buf], kKRow, lane);
+      const float part = idx_half_score64(Q, b);
+      if (half == 0) {
+        sm.part[buf][tok][lane] = part;
+      } else {
+        prev = part;
+        prev_ks = sm.ksc[buf][lane];
+      }
+    }
   }
 
-  if (!active) return;
+  if (!active || half == 0) return;
   __builtin_amdgcn_wave_barrier();
   if (nbuf > k) compact_wave(bk, bp, hist, nbuf, k, lane);
   int32_t *orow = idx + (int64_t)t * k;
@@ -239,9 +255,9 @@ hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  const int groups = (L + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(prefill_indexer_topk_kernel, dim3(groups), dim3(256), smem, s, q8, qs, k8, ks, w, L,
-                     k, idx);
+  const int groups = (L + kTok - 1) / kTok;
+  hipLaunchKernelGGL(prefill_indexer_topk_kernel, dim3(groups), dim3(kWaves * 64), smem, s, q8, qs, k8, ks, w,
+                     L, k, idx);
   return hipGetLastError();
 }
 }  // namespace dsa
