@@ -90,6 +90,7 @@ def setup_prefill(torch, dsa, synth, cfg, dev):
     t["args"] = dsa.make_prefill_args(L, cfg.H_I, cfg.D_I, cfg.H, cfg.k, dsa.DSA_E4M3, t["q8"], t["qs"], t["k8"],
                                       t["ks"], t["w"], dsa.DSA_BF16, t["q"], t["kv"], cfg.sm_scale, t["idx"],
                                       t["out"], t["lse"])
+    t["ws"] = torch.empty(max(1, dsa.dsa_prefill_workspace_bytes(t["args"])), dtype=torch.uint8, device=dev)
     return t
 
 
@@ -99,7 +100,7 @@ def prefill_step(dsa, cfg, t, evs, stream):
     dsa.dsa_quantize_e4m3_per_token(t["qi"], t["q8"], t["qs"], rows=L, cols=cfg.H_I * cfg.D_I, stream=stream)
     dsa.dsa_quantize_e4m3_per_token(t["ki"], t["k8"], t["ks"], rows=L, cols=cfg.D_I, stream=stream)
     evs[1].record(stream)
-    dsa.dsa_prefill_select(t["args"], stream=stream)
+    dsa.dsa_prefill_select(t["args"], workspace=t["ws"], stream=stream)
     evs[2].record(stream)
     dsa.dsa_sparse_mla_fwd(t["q"], t["kv"], t["idx"], cfg.sm_scale, t["out"], t["lse"], stream=stream)
     evs[3].record(stream)

@@ -163,7 +163,10 @@ dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t worksp
 
 /* The selection stage of dsa_prefill alone (indexer + top-k into a->idx;
  * q, kv, out, lse are not touched and may be NULL).  dsa_prefill is exactly
- * this call followed by dsa_sparse_mla_fwd on a->idx with no workspace. */
+ * this call followed by dsa_sparse_mla_fwd on a->idx with no workspace.
+ * Both need dsa_prefill_workspace_bytes(a) of workspace: for E4M3 the
+ * streaming top-k keeps a 4096-entry candidate buffer per query there
+ * (32 KiB per query: 4 GiB at L = 131072); for F32, the L x L scores. */
 dsa_status dsa_prefill_select(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
 

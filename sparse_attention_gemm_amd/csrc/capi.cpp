@@ -189,7 +189,7 @@ size_t dsa_prefill_workspace_bytes(const dsa_prefill_args *a) {
     const size_t L = (size_t)a->L;
     return align_up(L * L * 4, 256) + 2 * align_up(L * 4, 256);
   }
-  return 0;
+  return align_up(prefill_candidate_bytes(a->L), 256);  // per-query candidate buffers of the streaming top-k
 }
 
 // indexer + top-k of one prefill sequence into a->idx
@@ -197,7 +197,7 @@ static dsa_status prefill_select(const dsa_prefill_args *a, void *workspace, hip
   const int L = a->L;
   if (a->idx_dt == DSA_E4M3)
     return hip_check(launch_prefill_indexer_topk((const uint8_t *)a->q_idx, a->q_scale, (const uint8_t *)a->k_idx,
-                                                 a->k_scale, a->w, L, a->k, a->idx, stream),
+                                                 a->k_scale, a->w, L, a->k, a->idx, (uint32_t *)workspace, stream),
                      "prefill indexer/top-k launch");
   float *sc = (float *)workspace;
   int32_t *qpos = (int32_t *)((char *)workspace + align_up((size_t)L * L * 4, 256));
@@ -217,8 +217,8 @@ dsa_status dsa_prefill_select(const dsa_prefill_args *a, void *workspace, size_t
   dsa_status st = check_prefill(a, false);
   if (st != DSA_OK) return st;
   const size_t need = dsa_prefill_workspace_bytes(a);
-  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), DSA_ERR_WORKSPACE,
-          "workspace %zu < required %zu", workspace ? workspace_bytes : (size_t)0, need);
+  REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
+          workspace ? workspace_bytes : (size_t)0, need);
   return prefill_select(a, workspace, stream);
 }
 
@@ -228,8 +228,8 @@ dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t worksp
   dsa_status st = check_prefill(a, true);
   if (st != DSA_OK) return st;
   const size_t need = dsa_prefill_workspace_bytes(a);
-  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), DSA_ERR_WORKSPACE,
-          "workspace %zu < required %zu", workspace ? workspace_bytes : (size_t)0, need);
+  REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
+          workspace ? workspace_bytes : (size_t)0, need);
   const int L = a->L;
   st = prefill_select(a, workspace, stream);
   if (st != DSA_OK) return st;

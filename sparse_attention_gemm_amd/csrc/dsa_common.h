@@ -95,9 +95,11 @@ hipError_t launch_indexer_scores_f32(const float *q, const float *k, const float
 // Rows take min(n_valid[t], n_cap) candidates (n_cap guards the row length).
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
                        int32_t k, int32_t *idx, hipStream_t s);
+// Fused prefill selection; cand: prefill_candidate_bytes(L) of scratch.
+size_t prefill_candidate_bytes(int32_t L);
 hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const uint8_t *k8,
                                        const float *ks, const float *w, int32_t L, int32_t k,
-                                       int32_t *idx, hipStream_t s);
+                                       int32_t *idx, uint32_t *cand, hipStream_t s);
 // Sparse MLA.  block_table != NULL: idx holds logical positions of sequence
 // t (page size 64); otherwise idx holds rows of kv.  Entries that do not map
 // to a row in [0, N) are skipped like -1.  splits > 1 needs the

@@ -16,8 +16,10 @@
 // wave adds it to its own half and runs the selection.
 //
 // The second wave of each pair owns the token's 4096-entry candidate buffer
-// in LDS holding (order key, position) pairs in ascending position order,
-// plus a threshold tau:
+// (in the workspace: it stays in L2/MALL, and after the first few thousand
+// keys a key enters it only rarely; keeping it out of LDS lets two
+// workgroups share a CU) holding (order key, position) pairs in ascending
+// position order, plus a threshold tau:
 //   * a key enters the buffer if its order key >= tau (keys arrive in
 //     increasing position, so a new key that ties tau outranks it);
 //   * when the buffer would overflow, it is compacted in place to exactly
@@ -47,16 +49,16 @@ struct PrefillShared {
   uint8_t keys[2][kTile * kKRow];
   float ksc[2][kTile];
   float part[2][kTok][kTile];   // half-scores (heads 0..31) of the current and previous tile
-  uint32_t bkey[kTok][kCap];
-  uint32_t bpos[kTok][kCap];
   uint32_t hist[kTok][kBins];
 };
 
 // Compact buf[0..n) to its `keep` best entries (order key desc, position desc),
 // preserving ascending position order.  Returns the new threshold (k-th key).
-// All 64 lanes of the owning wave call this together.
+// All 64 lanes of the owning wave call this together; bk/bp are the wave's
+// own candidate buffer (global memory), hist its LDS histogram.
 __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict__ bp,
                                  uint32_t *__restrict__ hist, int &n, int keep, int lane) {
+  __threadfence_block();  // the wave's earlier appends (other lanes) are visible
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int i = lane; i < n; i += 64) {
     const uint32_t key = bk[i];
@@ -140,6 +142,7 @@ __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict
     tie_seen += (uint32_t)__popcll(tmask);
     __builtin_amdgcn_wave_barrier();
   }
+  __threadfence_block();  // the moved entries are visible to every lane
   n = (int)out;
   return tau;
 }
@@ -165,10 +168,10 @@ __device__ __forceinline__ void load_tile_async(PrefillShared &sm, int buf, cons
   }
 }
 
-__global__ __launch_bounds__(kWaves * 64, 1) void prefill_indexer_topk_kernel(
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_indexer_topk_kernel(
     const uint8_t *__restrict__ q8, const float *__restrict__ qs, const uint8_t *__restrict__ k8,
     const float *__restrict__ ks, const float *__restrict__ w, int32_t L, int32_t k,
-    int32_t *__restrict__ idx) {
+    int32_t *__restrict__ idx, uint32_t *__restrict__ cand) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   PrefillShared &sm = *reinterpret_cast<PrefillShared *>(smem_raw);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -184,8 +187,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_indexer_topk_kernel(
   IdxHalf Q;
   idx_load_half(Q, q8 + (int64_t)tq * 64 * 128, w + (int64_t)tq * 64, qs[tq], 32 * half, lane);
 
-  uint32_t *bk = sm.bkey[tok];
-  uint32_t *bp = sm.bpos[tok];
+  uint32_t *bk = cand + (int64_t)tq * 2 * kCap;  // order keys
+  uint32_t *bp = bk + kCap;                        // positions
   uint32_t *hist = sm.hist[tok];
   int nbuf = 0;
   uint32_t thr = 0u;
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_indexer_topk_kernel(
   }
 
   if (!active || half == 0) return;
-  __builtin_amdgcn_wave_barrier();
+  __threadfence_block();
   if (nbuf > k) compact_wave(bk, bp, hist, nbuf, k, lane);
   int32_t *orow = idx + (int64_t)t * k;
   for (int i = lane; i < k; i += 64) orow[i] = i < nbuf ? (int32_t)bp[i] : -1;
@@ -243,9 +246,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_indexer_topk_kernel(
 }  // namespace
 
 namespace dsa {
+size_t prefill_candidate_bytes(int32_t L) { return (size_t)L * 2 * kCap * sizeof(uint32_t); }
+
 hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const uint8_t *k8,
                                        const float *ks, const float *w, int32_t L, int32_t k,
-                                       int32_t *idx, hipStream_t s) {
+                                       int32_t *idx, uint32_t *cand, hipStream_t s) {
   if (L == 0) return hipSuccess;
   static bool attr_done = false;
   const size_t smem = sizeof(PrefillShared);
@@ -257,7 +262,7 @@ hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const
   }
   const int groups = (L + kTok - 1) / kTok;
   hipLaunchKernelGGL(prefill_indexer_topk_kernel, dim3(groups), dim3(kWaves * 64), smem, s, q8, qs, k8, ks, w,
-                     L, k, idx);
+                     L, k, idx, cand);
   return hipGetLastError();
 }
 }  // namespace dsa

@@ -433,7 +433,8 @@ def test_prefill_select_equals_prefill_selection(dsa):
     idx2 = torch.full_like(t["idx"], 12345)
     args = dsa.make_prefill_args(cfg.L, 64, 128, cfg.H, cfg.k, dsa.DSA_E4M3, t["q8"], t["qs"], t["k8"], t["ks"],
                                  t["w"], dsa.DSA_BF16, None, None, cfg.sm_scale, idx2, None, None)
-    dsa.dsa_prefill_select(args)
+    ws = torch.empty(dsa.dsa_prefill_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    dsa.dsa_prefill_select(args, ws)
     torch.cuda.synchronize()
     assert torch.equal(idx2, t["idx"])
 
