@@ -22,11 +22,15 @@
 // position order, plus a threshold tau:
 //   * a key enters the buffer if its order key >= tau (keys arrive in
 //     increasing position, so a new key that ties tau outranks it);
-//   * when the buffer would overflow, it is compacted in place to exactly
-//     the k best entries under (score desc, position desc) by histogram
-//     narrowing, and tau becomes the k-th key.
-// At the end the buffer is compacted to min(k, t+1) entries and written out
-// in ascending position order (deterministic).
+//   * when the buffer would overflow, it is compacted in place by histogram
+//     narrowing over the order keys.  The narrowing stops at the first level
+//     whose bin holding the k-th key is small enough: every entry at or above
+//     that bin's lower edge is kept and tau becomes the edge.  (Ties make the
+//     narrowing run down to single keys, where the cut is exact.)  The key
+//     range is tracked while appending, so a compaction is one histogram pass
+//     per level plus one compaction pass.
+// At the end the buffer is compacted exactly to min(k, t+1) entries (score
+// desc, position desc) and written out in ascending position order.
 //
 // Workgroups are issued longest-first (the last query block first) so that
 // the causal triangle drains evenly.
@@ -42,6 +46,9 @@ constexpr int kKRow = 160;      // LDS bytes per key row: 128 + 32 pad (40 dword
 constexpr int kKSlots = kKRow / 16;
 constexpr int kKeyInsts = kTile * kKSlots / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
 constexpr int kBins = 256;      // compaction histogram
+// An early cut may leave at most this many entries (k <= 2048), so that it
+// frees at least a quarter of the buffer; otherwise the narrowing continues.
+constexpr int kCutLimit = kCap - kCap / 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -52,36 +59,45 @@ struct PrefillShared {
   uint32_t hist[kTok][kBins];
 };
 
-// Compact buf[0..n) to its `keep` best entries (order key desc, position desc),
-// preserving ascending position order.  Returns the new threshold (k-th key).
-// All 64 lanes of the owning wave call this together; bk/bp are the wave's
-// own candidate buffer (global memory), hist its LDS histogram.
+constexpr int kUnroll = 8;     // buffer chunks of 64 entries loaded together in a compaction pass
+
+// Compact the candidate buffer bk/bp[0..n) (order keys, positions; ascending
+// position order, which is preserved), all of whose keys lie in [lo, hi].
+// All 64 lanes of the owning wave call this together; hist is its LDS
+// histogram.  Returns the new threshold tau.
+//   limit == 0 (exact): keep exactly the `keep` best entries under (key desc,
+//     position desc); tau is the keep-th key.
+//   limit > 0 (early cut): stop narrowing as soon as cutting at the lower edge
+//     of the bin that holds the keep-th key leaves at most `limit` entries, and
+//     keep every entry >= that edge (tau).  At least `keep` entries survive, all
+//     >= tau, so everything dropped (< tau) is outranked by `keep` survivors.
 __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict__ bp,
-                                 uint32_t *__restrict__ hist, int &n, int keep, int lane) {
+                                 uint32_t *__restrict__ hist, int &n, int keep, int limit, uint32_t lo,
+                                 uint32_t hi, int lane) {
   __threadfence_block();  // the wave's earlier appends (other lanes) are visible
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = lane; i < n; i += 64) {
-    const uint32_t key = bk[i];
-    mn = key < mn ? key : mn;
-    mx = key > mx ? key : mx;
-  }
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  uint32_t base = mn;
-  const uint32_t span = mx - mn;
+  uint32_t base = lo;
+  const uint32_t span = hi - lo;
   int shift = span == 0 ? 0 : max(0, 32 - __clz(span) - 8);
   uint32_t remaining = (uint32_t)keep;
-  uint32_t tau, ties;
+  uint32_t tau, ties = 0;
+  bool exact_cut = false;
   uint32_t nbins = kBins;  // later levels: only as many bins as the window is wide
   while (true) {
 #pragma unroll
     for (int b = lane; b < kBins; b += 64) hist[b] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int i = lane; i < n; i += 64) {
-      const uint32_t key = bk[i];
-      if (key >= base) {
-        const uint32_t d = (key - base) >> shift;
-        if (d < nbins) atomicAdd(&hist[d], 1u);
+    for (int b0 = 0; b0 < n; b0 += 64 * kUnroll) {
+      uint32_t kk[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = b0 + 64 * u + lane;
+        kk[u] = i < n ? bk[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = b0 + 64 * u + lane;
+        const uint32_t d = (kk[u] - base) >> shift;
+        if (i < n && kk[u] >= base && d < nbins) atomicAdd(&hist[d], 1u);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -109,38 +125,53 @@ __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict
     const uint32_t above = __shfl(babove, src);
     const uint32_t cnt = __shfl(bcnt, src);
     __builtin_amdgcn_wave_barrier();
+    const uint32_t edge = base + (bstar << shift);
+    if (limit > 0 && (uint32_t)keep - remaining + above + cnt <= (uint32_t)limit) {
+      tau = edge;  // early cut at the bin's lower edge
+      break;
+    }
     remaining -= above;
-    base += bstar << shift;
+    base = edge;
     if (shift == 0) {
       tau = base;
       ties = cnt;
+      exact_cut = true;
       break;
     }
     const int nshift = max(0, shift - 8);
     nbins = 1u << (shift - nshift);
     shift = nshift;
   }
-  // ordered in-place compaction: keep key > tau and the last `remaining` ties
-  const uint32_t tie_cut = ties - remaining;
+  // ordered in-place compaction: keep key > tau, and of the keys equal to tau
+  // all (early cut) or the last `remaining` (exact cut).  Entry i moves to
+  // dst <= i, below every entry not yet read.
+  const uint32_t tie_cut = exact_cut ? ties - remaining : 0u;
   uint32_t out = 0, tie_seen = 0;
-  for (int b0 = 0; b0 < n; b0 += 64) {
-    const int i = b0 + lane;
-    const bool in = i < n;
-    const uint32_t key = in ? bk[i] : 0u;
-    const uint32_t pos = in ? bp[i] : 0u;
-    const bool tie = in && key == tau;
-    const uint64_t tmask = __ballot(tie);
-    const uint32_t my_tie = tie_seen + (uint32_t)lanes_below(tmask);
-    const bool kp = in && (key > tau || (tie && my_tie >= tie_cut));
-    const uint64_t kmask = __ballot(kp);
-    if (kp) {
-      const uint32_t dst = out + (uint32_t)lanes_below(kmask);
-      bk[dst] = key;
-      bp[dst] = pos;
+  for (int b0 = 0; b0 < n; b0 += 64 * kUnroll) {
+    uint32_t kk[kUnroll], pp[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = b0 + 64 * u + lane;
+      kk[u] = i < n ? bk[i] : 0u;
+      pp[u] = i < n ? bp[i] : 0u;
     }
-    out += (uint32_t)__popcll(kmask);
-    tie_seen += (uint32_t)__popcll(tmask);
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = b0 + 64 * u + lane;
+      const bool in = i < n;
+      const bool tie = in && kk[u] == tau;
+      const uint64_t tmask = __ballot(tie);
+      const uint32_t my_tie = tie_seen + (uint32_t)lanes_below(tmask);
+      const bool kp = in && (kk[u] > tau || (tie && my_tie >= tie_cut));
+      const uint64_t kmask = __ballot(kp);
+      if (kp) {
+        const uint32_t dst = out + (uint32_t)lanes_below(kmask);
+        bk[dst] = kk[u];
+        bp[dst] = pp[u];
+      }
+      out += (uint32_t)__popcll(kmask);
+      tie_seen += (uint32_t)__popcll(tmask);
+    }
   }
   __threadfence_block();  // the moved entries are visible to every lane
   n = (int)out;
@@ -192,6 +223,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_indexer_topk_kernel(
   uint32_t *hist = sm.hist[tok];
   int nbuf = 0;
   uint32_t thr = 0u;
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u;  // bounds of the keys this lane appended since the last cut
   float prev = 0.0f, prev_ks = 0.0f;  // second wave: its half-score and the key scale of the last tile
 
   load_tile_async(sm, 0, k8, ks, L, 0, wave, lane);
@@ -209,12 +241,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_indexer_topk_kernel(
       uint64_t mask = __ballot(pass);
       int cnt = __popcll(mask);
       if (nbuf + cnt > kCap) {
-        thr = compact_wave(bk, bp, hist, nbuf, k, lane);
+        thr = compact_wave(bk, bp, hist, nbuf, k, kCutLimit, wave_min_u32(klo), wave_max_u32(khi), lane);
+        klo = thr;  // every survivor is >= tau
         pass = valid && key >= thr;
         mask = __ballot(pass);
         cnt = __popcll(mask);
       }
       if (pass) {
+        klo = min(klo, key);
+        khi = max(khi, key);
         const int dst = nbuf + lanes_below(mask);
         bk[dst] = key;
         bp[dst] = (uint32_t)s;
@@ -238,7 +273,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_indexer_topk_kernel(
 
   if (!active || half == 0) return;
   __threadfence_block();
-  if (nbuf > k) compact_wave(bk, bp, hist, nbuf, k, lane);
+  if (nbuf > k) compact_wave(bk, bp, hist, nbuf, k, 0, wave_min_u32(klo), wave_max_u32(khi), lane);
   int32_t *orow = idx + (int64_t)t * k;
   for (int i = lane; i < k; i += 64) orow[i] = i < nbuf ? (int32_t)bp[i] : -1;
 }

@@ -313,6 +313,68 @@ def test_prefill_fused_fp8(dsa, ora, L, k, H):
 
 
 
+def _fused_vs_unfused(dsa, q8, qs, k8, ks, w, k):
+    """Run the fused selection and top-k of the unfused score matrix on device
+    inputs of one causal sequence; returns both index matrices (CPU)."""
+    L, H_I = q8.shape[0], q8.shape[1]
+    idx = torch.empty((L, k), dtype=torch.int32, device=DEV)
+    args = dsa.make_prefill_args(L, H_I, 128, 16, k, dsa.DSA_E4M3, q8, qs, k8, ks, w, dsa.DSA_BF16, None, None,
+                                 0.1, idx, None, None)
+    ws = torch.empty(dsa.dsa_prefill_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    dsa.dsa_prefill_select(args, ws)
+    sc = torch.empty((L, L), dtype=torch.float32, device=DEV)
+    pos = torch.arange(L, dtype=torch.int32, device=DEV)
+    dsa.dsa_indexer_scores(q8, qs, k8, ks, w, pos, sc, dsa.DSA_E4M3)
+    idx2 = torch.empty((L, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk_select(sc, pos + 1, k, idx2)
+    torch.cuda.synchronize()
+    return idx.cpu(), idx2.cpu(), sc
+
+
+def test_prefill_select_fused_long(dsa, ora):
+    """Rows long enough for many buffer compactions (early and exact cuts)."""
+    L, k = 20000, 2048
+    _say(f"fused select long L={L}")
+    cfg = synth.scaled_down(synth.CONFIGS["prefill16k"], L=L, k=k, H=16, seed=11)
+    q_i, k_i, w = synth.prefill_indexer_inputs(cfg)
+    q8 = torch.empty((L, 64, 128), dtype=torch.uint8, device=DEV)
+    qs = torch.empty(L, dtype=torch.float32, device=DEV)
+    k8 = torch.empty((L, 128), dtype=torch.uint8, device=DEV)
+    ks = torch.empty(L, dtype=torch.float32, device=DEV)
+    dsa.dsa_quantize_e4m3_per_token(q_i.to(DEV), q8, qs, rows=L, cols=8192)
+    dsa.dsa_quantize_e4m3_per_token(k_i.to(DEV), k8, ks, rows=L, cols=128)
+    a, b, sc = _fused_vs_unfused(dsa, q8, qs, k8, ks, w.to(DEV), k)
+    bad = (a != b).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"fused and unfused selections differ in {len(bad)} rows, first {bad[:5]}"
+    # sampled rows against the oracle's scores and selection
+    rows = np.array([0, k - 1, k, 4095, 4096, 4097, 9000, L - 2, L - 1])
+    o, _, _ = oracle_score_bounds(ora, q8.cpu().numpy(), k8.cpu().numpy(), w.numpy(),
+                                  torch.arange(L, dtype=torch.int32), q_scale=qs.cpu().numpy(),
+                                  k_scale=ks.cpu().numpy(), rows=rows)
+    for j, r in enumerate(rows):
+        check_topk_row(a[r].numpy(), o[j], r + 1, k, f"fused long row {r}")
+
+
+def test_prefill_select_fused_ties(dsa, ora):
+    """E4M3 payloads in {0,+-1,+-2} and unit scales: exact scores with huge
+    tie classes, so compactions must fall through to the exact tie cut."""
+    L, H_I, k = 9000, 64, 2048
+    _say(f"fused select ties L={L}")
+    lut = torch.tensor([0xC0, 0xB8, 0x00, 0x38, 0x40], dtype=torch.uint8)
+    q8 = lut[synth.randint(6, 1, (L, H_I, 128), 0, 4)]
+    k8 = lut[synth.randint(6, 2, (L, 128), 0, 4)]
+    w = torch.tensor([-1.0, -0.5, 0.5, 1.0])[synth.randint(6, 3, (L, H_I), 0, 3)]
+    ones = torch.ones(L)
+    a, b, sc = _fused_vs_unfused(dsa, q8.to(DEV), ones.to(DEV), k8.to(DEV), ones.to(DEV), w.to(DEV), k)
+    bad = (a != b).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"fused and unfused selections differ in {len(bad)} rows, first {bad[:5]}"
+    rows = np.array([100, 2047, 2048, 5000, 8191, L - 1])
+    pos = torch.arange(L, dtype=torch.int32)
+    o = ora.indexer_rows(q8[rows].numpy(), k8.numpy(), w[rows], pos[rows], q_scale=ones[rows], k_scale=ones)
+    ref, _ = ora.topk_rows(np.where(np.isinf(o), 0, o), (pos[rows] + 1).numpy(), k)
+    assert np.array_equal(a[rows].numpy(), ref)
+
+
 # ------------------------------------------------------------------ decode
 def _decode_case(cfg, seqs=None):
     ctx = synth.decode_ctx(cfg)
