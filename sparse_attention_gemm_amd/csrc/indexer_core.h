@@ -39,6 +39,12 @@ __device__ __forceinline__ float swap16_sum(float x, float y) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ReLU of an MFMA dot product.  fmaxf would first quiet a possible signalling
+// NaN (one extra v_max per element); the products of finite E4M3 payloads are
+// finite and far below FLT_MAX, so a clamp to [0, FLT_MAX] is the same
+// function in a single v_med3.
+__device__ __forceinline__ float relu_dot(float d) { return __builtin_amdgcn_fmed3f(d, 0.0f, 3.402823466e38f); }
+
 // One half (32 heads) of a query's indexer heads.
 struct IdxHalf {
   i32x8 a[2];      // A operand: 16-head tiles x 128 bytes
@@ -72,7 +78,7 @@ __device__ __forceinline__ float idx_half_score64(const IdxHalf &Q, const i32x8 
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p = fmaf(Q.w[i][r], fmaxf(d[u][i][r], 0.0f), p);
+      for (int r = 0; r < 4; ++r) p = fmaf(Q.w[i][r], relu_dot(d[u][i][r]), p);
     v[u] = p;
   }
   // lane groups g = 0..3 hold 4 heads each of the same keys: sum them, and

@@ -224,17 +224,23 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_indexer_topk_kernel(
   int nbuf = 0;
   uint32_t thr = 0u;
   uint32_t klo = 0xFFFFFFFFu, khi = 0u;  // bounds of the keys this lane appended since the last cut
-  float prev = 0.0f, prev_ks = 0.0f;  // second wave: its half-score and the key scale of the last tile
+  float part = 0.0f;     // this wave's half-score of the last computed tile
+  float prev_ks = 0.0f;  // second wave: key scales of that tile
 
+  // LDS reads of a tile are issued before the next tile's direct-to-LDS
+  // loads, and LDS writes only once this wave has none in flight: the
+  // compiler cannot tell the two apart and would otherwise wait for the
+  // prefetch before touching LDS.
   load_tile_async(sm, 0, k8, ks, L, 0, wave, lane);
   for (int it = 0; it <= ntiles; ++it) {
     const int buf = it & 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed in LDS
-    __syncthreads();                // ... and every wave's; tile it-1's buffer is free
+    if (half == 0 && it > 0) sm.part[buf ^ 1][tok][lane] = part;  // publish tile it-1
+    __syncthreads();                // every wave's loads and parts; tile it-1's buffer is free
     if (half == 1 && active && it > 0) {
       // score of key (it-1)*64 + lane = half(0..31) + half(32..63), times its scale
       const int s = (it - 1) * kTile + lane;
-      const float v = canon_zero((sm.part[buf ^ 1][tok][lane] + prev) * prev_ks);
+      const float v = canon_zero((sm.part[buf ^ 1][tok][lane] + part) * prev_ks);
       const uint32_t key = score_key(v);
       const bool valid = s <= t;
       bool pass = valid && key >= thr;
@@ -257,18 +263,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_indexer_topk_kernel(
       nbuf += cnt;
     }
     if (it == ntiles) break;
-    if (it + 1 < ntiles) load_tile_async(sm, buf ^ 1, k8, ks, L, it + 1, wave, lane);
+    i32x8 b[4];
     if (active) {
-      i32x8 b[4];
       idx_load_keys(b, sm.keys[buf], kKRow, lane);
-      const float part = idx_half_score64(Q, b);
-      if (half == 0) {
-        sm.part[buf][tok][lane] = part;
-      } else {
-        prev = part;
-        prev_ks = sm.ksc[buf][lane];
-      }
+      if (half == 1) prev_ks = sm.ksc[buf][lane];
     }
+    if (it + 1 < ntiles) load_tile_async(sm, buf ^ 1, k8, ks, L, it + 1, wave, lane);
+    if (active) part = idx_half_score64(Q, b);
   }
 
   if (!active || half == 0) return;
