@@ -6,16 +6,13 @@
 // "How it works" (index score of each query against its preceding tokens,
 // then the top-k KV entries per query, k = 2048); m.digipub.cc, section 2.
 //
-// Workgroup = 8 wavefronts = 4 consecutive query tokens; each token's 64
-// indexer heads are split over a pair of waves (heads 0..31 and 32..63), so
-// one wave's ReLU/weight epilogue (VALU) overlaps the other's MFMAs on the
-// same SIMD.  Key tiles (64 keys x 128 B of E4M3 + 64 fp32 scales) are
-// loaded straight into LDS (direct-to-LDS loads, double buffered, one
-// barrier per tile) and shared by all eight waves.  The first wave of a pair
-// publishes its half-score of each key in LDS; one tile later the second
-// wave adds it to its own half and runs the selection.
+// Workgroup = 8 wavefronts = 8 consecutive query tokens, one wave per token
+// with all 64 indexer heads in registers (4 MFMA A tiles), so every key
+// block read from LDS feeds four MFMAs.  Key tiles (64 keys x 128 B of E4M3 +
+// 64 fp32 scales) are loaded straight into LDS (direct-to-LDS loads, double
+// buffered, one barrier per tile) and shared by the eight waves.
 //
-// The second wave of each pair owns the token's 4096-entry candidate buffer
+// Each wave owns its token's 4096-entry candidate buffer
 // (in the workspace: it stays in L2/MALL, and after the first few thousand
 // keys a key enters it only rarely; keeping it out of LDS lets two
 // workgroups share a CU) holding (order key, position) pairs in ascending
@@ -39,7 +36,7 @@
 namespace {
 
 constexpr int kTok = 4;         // query tokens per workgroup
-constexpr int kWaves = 8;       // two per token
+constexpr int kWaves = kTok;    // one per token
 constexpr int kCap = 4096;      // candidate buffer entries per query
 constexpr int kTile = 64;       // keys per tile
 constexpr int kKRow = 160;      // LDS bytes per key row: 128 + 32 pad (40 dwords mod 64: conflict-free reads)
@@ -55,7 +52,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 struct PrefillShared {
   uint8_t keys[2][kTile * kKRow];
   float ksc[2][kTile];
-  float part[2][kTok][kTile];   // half-scores (heads 0..31) of the current and previous tile
   uint32_t hist[kTok][kBins];
 };
 
@@ -178,101 +174,116 @@ __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict
   return tau;
 }
 
-// Issue the direct-to-LDS loads of key tile `tile` into buffer `buf`.
+// Issue the direct-to-LDS loads of key tile `tile` into dkeys/dks.
 // Instruction i writes slots [64i, 64i+64); slot s holds row s/10, 16-byte
-// chunk s%10 (chunks 8, 9 are padding and reload chunk 7).  Keys past L-1
-// read key L-1 (never selected: they are beyond every query of the sequence).
-__device__ __forceinline__ void load_tile_async(PrefillShared &sm, int buf, const uint8_t *__restrict__ k8,
+// chunk s%10 (chunks 8, 9 are padding and reload chunk 7).  Addresses are a
+// uniform tile base plus a 32-bit lane offset.  In the sequence's last tile,
+// keys past L-1 read key L-1 (never selected: they are beyond every query).
+__device__ __forceinline__ void load_tile_async(uint8_t *dkeys, float *dks, const uint8_t *__restrict__ k8,
                                                 const float *__restrict__ ks, int L, int tile, int wave, int lane) {
+  const uint8_t *kbase = k8 + (int64_t)tile * kTile * 128;
+  const int nrow = L - tile * kTile;  // rows of this tile inside the sequence
 #pragma unroll
   for (int i = wave; i < kKeyInsts; i += kWaves) {
     const int slot = i * 64 + lane;
     const int r = slot / kKSlots;
     const int j = min(slot - r * kKSlots, 7);
-    const int key = min(tile * kTile + r, L - 1);
-    __builtin_amdgcn_global_load_lds(k8 + (int64_t)key * 128 + j * 16, (lds_void *)(sm.keys[buf] + i * 1024), 16, 0,
-                                     0);
+    const uint32_t off = (uint32_t)(min(r, nrow - 1) * 128 + j * 16);
+    __builtin_amdgcn_global_load_lds(kbase + off, (lds_void *)(dkeys + i * 1024), 16, 0, 0);
   }
   if (wave == kWaves - 1) {
-    const int key = min(tile * kTile + lane, L - 1);
-    __builtin_amdgcn_global_load_lds(ks + key, (lds_void *)sm.ksc[buf], 4, 0, 0);
+    const float *sbase = ks + (int64_t)tile * kTile;
+    __builtin_amdgcn_global_load_lds(sbase + min(lane, nrow - 1), (lds_void *)dks, 4, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_indexer_topk_kernel(
+// Score tile `it` from (ckeys, cks) for one token and prefetch tile it+1
+// into (nkeys, nks).  The current tile's LDS reads are issued before the
+// prefetch: the compiler cannot tell the direct-to-LDS writes from them and
+// would otherwise wait for the prefetch before reading LDS.
+__device__ __forceinline__ float score_and_prefetch(uint8_t *nkeys, float *nks, const uint8_t *ckeys, const float *cks,
+                                                    bool prefetch, bool need, const IdxHalf &Q0, const IdxHalf &Q1,
+                                                    const uint8_t *__restrict__ k8, const float *__restrict__ ks,
+                                                    int L, int next, int wave, int lane) {
+  i32x8 b[4];
+  float ksv = 0.0f;
+  if (need) {
+    idx_load_keys(b, ckeys, kKRow, lane);
+    ksv = cks[lane];
+  }
+  if (prefetch) load_tile_async(nkeys, nks, k8, ks, L, next, wave, lane);
+  if (!need) return 0.0f;
+  const float h0 = idx_half_score64(Q0, b);
+  const float h1 = idx_half_score64(Q1, b);
+  return canon_zero((h0 + h1) * ksv);
+}
+
+__global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
     const uint8_t *__restrict__ q8, const float *__restrict__ qs, const uint8_t *__restrict__ k8,
     const float *__restrict__ ks, const float *__restrict__ w, int32_t L, int32_t k,
     int32_t *__restrict__ idx, uint32_t *__restrict__ cand) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   PrefillShared &sm = *reinterpret_cast<PrefillShared *>(smem_raw);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tok = wave >> 1, half = wave & 1;
   const int grp = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int t0 = grp * kTok;
-  const int t = t0 + tok;
+  const int t = t0 + wave;
   const bool active = t < L;
   const int tq = min(t, L - 1);
   const int last = min(t0 + kTok - 1, L - 1);
   const int ntiles = last / kTile + 1;
 
-  IdxHalf Q;
-  idx_load_half(Q, q8 + (int64_t)tq * 64 * 128, w + (int64_t)tq * 64, qs[tq], 32 * half, lane);
+  // heads 0..31 and 32..63; the score is half(0..31) + half(32..63)
+  IdxHalf Q0, Q1;
+  {
+    const uint8_t *qt = q8 + (int64_t)tq * 64 * 128;
+    const float *wt = w + (int64_t)tq * 64;
+    const float qsv = qs[tq];
+    idx_load_half(Q0, qt, wt, qsv, 0, lane);
+    idx_load_half(Q1, qt, wt, qsv, 32, lane);
+  }
 
   uint32_t *bk = cand + (int64_t)tq * 2 * kCap;  // order keys
   uint32_t *bp = bk + kCap;                        // positions
-  uint32_t *hist = sm.hist[tok];
+  uint32_t *hist = sm.hist[wave];
   int nbuf = 0;
   uint32_t thr = 0u;
   uint32_t klo = 0xFFFFFFFFu, khi = 0u;  // bounds of the keys this lane appended since the last cut
-  float part = 0.0f;     // this wave's half-score of the last computed tile
-  float prev_ks = 0.0f;  // second wave: key scales of that tile
 
-  // LDS reads of a tile are issued before the next tile's direct-to-LDS
-  // loads, and LDS writes only once this wave has none in flight: the
-  // compiler cannot tell the two apart and would otherwise wait for the
-  // prefetch before touching LDS.
-  load_tile_async(sm, 0, k8, ks, L, 0, wave, lane);
-  for (int it = 0; it <= ntiles; ++it) {
+  load_tile_async(sm.keys[0], sm.ksc[0], k8, ks, L, 0, wave, lane);
+  for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed in LDS
-    if (half == 0 && it > 0) sm.part[buf ^ 1][tok][lane] = part;  // publish tile it-1
-    __syncthreads();                // every wave's loads and parts; tile it-1's buffer is free
-    if (half == 1 && active && it > 0) {
-      // score of key (it-1)*64 + lane = half(0..31) + half(32..63), times its scale
-      const int s = (it - 1) * kTile + lane;
-      const float v = canon_zero((sm.part[buf ^ 1][tok][lane] + part) * prev_ks);
-      const uint32_t key = score_key(v);
-      const bool valid = s <= t;
-      bool pass = valid && key >= thr;
-      uint64_t mask = __ballot(pass);
-      int cnt = __popcll(mask);
-      if (nbuf + cnt > kCap) {
-        thr = compact_wave(bk, bp, hist, nbuf, k, kCutLimit, wave_min_u32(klo), wave_max_u32(khi), lane);
-        klo = thr;  // every survivor is >= tau
-        pass = valid && key >= thr;
-        mask = __ballot(pass);
-        cnt = __popcll(mask);
-      }
-      if (pass) {
-        klo = min(klo, key);
-        khi = max(khi, key);
-        const int dst = nbuf + lanes_below(mask);
-        bk[dst] = key;
-        bp[dst] = (uint32_t)s;
-      }
-      nbuf += cnt;
+    __syncthreads();                // ... and every wave's; tile it-1's buffer is free
+    const bool need = active && it * kTile <= t;
+    const float v = score_and_prefetch(sm.keys[buf ^ 1], sm.ksc[buf ^ 1], sm.keys[buf], sm.ksc[buf], it + 1 < ntiles,
+                                       need, Q0, Q1, k8, ks, L, it + 1, wave, lane);
+    if (!need) continue;
+    // score of key it*64 + lane
+    const int s = it * kTile + lane;
+    const uint32_t key = score_key(v);
+    const bool valid = s <= t;
+    bool pass = valid && key >= thr;
+    uint64_t mask = __ballot(pass);
+    int cnt = __popcll(mask);
+    if (nbuf + cnt > kCap) {
+      thr = compact_wave(bk, bp, hist, nbuf, k, kCutLimit, wave_min_u32(klo), wave_max_u32(khi), lane);
+      klo = thr;  // every survivor is >= tau
+      pass = valid && key >= thr;
+      mask = __ballot(pass);
+      cnt = __popcll(mask);
     }
-    if (it == ntiles) break;
-    i32x8 b[4];
-    if (active) {
-      idx_load_keys(b, sm.keys[buf], kKRow, lane);
-      if (half == 1) prev_ks = sm.ksc[buf][lane];
+    if (pass) {
+      klo = min(klo, key);
+      khi = max(khi, key);
+      const int dst = nbuf + lanes_below(mask);
+      bk[dst] = key;
+      bp[dst] = (uint32_t)s;
     }
-    if (it + 1 < ntiles) load_tile_async(sm, buf ^ 1, k8, ks, L, it + 1, wave, lane);
-    if (active) part = idx_half_score64(Q, b);
+    nbuf += cnt;
   }
 
-  if (!active || half == 0) return;
+  if (!active) return;
   __threadfence_block();
   if (nbuf > k) compact_wave(bk, bp, hist, nbuf, k, 0, wave_min_u32(klo), wave_max_u32(khi), lane);
   int32_t *orow = idx + (int64_t)t * k;
