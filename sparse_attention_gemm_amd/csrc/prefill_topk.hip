@@ -224,7 +224,8 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
     int32_t *__restrict__ idx, uint32_t *__restrict__ cand) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   PrefillShared &sm = *reinterpret_cast<PrefillShared *>(smem_raw);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
   const int grp = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int t0 = grp * kTok;
   const int t = t0 + wave;
