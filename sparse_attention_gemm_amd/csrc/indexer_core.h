@@ -88,6 +88,47 @@ __device__ __forceinline__ float idx_half_score64(const IdxHalf &Q, const i32x8 
   return swap16_sum(s02, s13);               // row 0: block 0, row 1: block 1, row 2: block 2, row 3: block 3
 }
 
+// Both halves of a 64-head query against a 64-key tile: returns, in lane l,
+// half(0..31) + half(32..63) of key l (without ks) -- the same operations in
+// the same order as two idx_half_score64 calls.  The issue order is fixed
+// (scheduling fences, and an empty asm that pins each partial sum): each MFMA
+// of key block u is followed by the ReLU/weight epilogue of one MFMA result of block u-1, so the matrix core
+// and the VALU overlap within the wave and no result is waited for.
+__device__ __forceinline__ float idx_full_score64(const IdxHalf &Q0, const IdxHalf &Q1, const i32x8 (&b)[4]) {
+  const IdxHalf *Q[2] = {&Q0, &Q1};
+  f32x4 d[2][2][2];  // [block parity][half][head tile]
+  float p[2] = {0.0f, 0.0f};
+  float v[2][4];
+#pragma unroll
+  for (int u = 0; u <= 4; ++u) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int h = m >> 1, i = m & 1;
+      if (u < 4) d[u & 1][h][i] = mfma_fp8_16x16x128(Q[h]->a[i], b[u], f32x4{0.f, 0.f, 0.f, 0.f});
+      __builtin_amdgcn_sched_barrier(0);
+      if (u > 0) {
+        const f32x4 &dd = d[(u - 1) & 1][h][i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[h] = fmaf(Q[h]->w[i][r], relu_dot(dd[r]), p[h]);
+        asm volatile("" : "+v"(p[h]));  // computed here, not sunk below later MFMAs
+        if (i == 1) {
+          v[h][u - 1] = p[h];
+          p[h] = 0.0f;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float hs[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float s02 = swap32_sum(v[h][0], v[h][2]);
+    const float s13 = swap32_sum(v[h][1], v[h][3]);
+    hs[h] = swap16_sum(s02, s13);
+  }
+  return hs[0] + hs[1];
+}
+
 // B operands of a 64-key tile whose rows are `stride` bytes apart.
 __device__ __forceinline__ void idx_load_keys(i32x8 (&b)[4], const uint8_t *__restrict__ rows, int stride, int lane) {
   const int g = lane >> 4, c = lane & 15;

@@ -205,17 +205,14 @@ __device__ __forceinline__ float score_and_prefetch(uint8_t *nkeys, float *nks, 
                                                     bool prefetch, bool need, const IdxHalf &Q0, const IdxHalf &Q1,
                                                     const uint8_t *__restrict__ k8, const float *__restrict__ ks,
                                                     int L, int next, int wave, int lane) {
+  // read unconditionally (the buffer is always valid LDS): a conditional
+  // read would make the compiler initialise the 32 operand registers
   i32x8 b[4];
-  float ksv = 0.0f;
-  if (need) {
-    idx_load_keys(b, ckeys, kKRow, lane);
-    ksv = cks[lane];
-  }
+  idx_load_keys(b, ckeys, kKRow, lane);
+  const float ksv = cks[lane];
   if (prefetch) load_tile_async(nkeys, nks, k8, ks, L, next, wave, lane);
   if (!need) return 0.0f;
-  const float h0 = idx_half_score64(Q0, b);
-  const float h1 = idx_half_score64(Q1, b);
-  return canon_zero((h0 + h1) * ksv);
+  return canon_zero(idx_full_score64(Q0, Q1, b) * ksv);
 }
 
 __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
