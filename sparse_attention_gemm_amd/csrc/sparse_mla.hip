@@ -65,16 +65,21 @@ __device__ __forceinline__ int64_t phys_row(const int32_t *__restrict__ irow, co
 template <int NW>
 __device__ __forceinline__ void gather_tile_async(uint8_t *__restrict__ dst, const int *__restrict__ rows,
                                                   int r0, const __bf16 *__restrict__ kv, int wave, int lane) {
+  static_assert(kTileSlots == kGatherInsts * 64, "every gather instruction is full");
+  // Lane roles are recomputed per tile from a laundered lane id: hoisting
+  // them would hold a 64-bit address per instruction for the whole kernel.
+  int l = lane;
+  asm volatile("" : "+v"(l));
 #pragma unroll
-  for (int i = wave; i < kGatherInsts; i += NW) {
-    const int slot = i * 64 + lane;
-    if (slot < kTileSlots) {
-      const int r = slot / kRowSlots;
-      const int j = min(slot - r * kRowSlots, 71);
-      const int pr = rows[r0 + r];
-      const __bf16 *src = kv + (int64_t)(pr >= 0 ? pr : 0) * 576 + j * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + i * 1024), 16, 0, 0);
-    }
+  for (int n = 0; n < (kGatherInsts + NW - 1) / NW; ++n) {
+    const int i = wave + n * NW;  // uniform
+    if (i >= kGatherInsts) break;
+    const int slot = i * 64 + l;
+    const int r = slot / kRowSlots;
+    const int j = min(slot - r * kRowSlots, 71);
+    const int pr = rows[r0 + r];
+    const __bf16 *src = kv + ((int64_t)(pr >= 0 ? pr : 0) * 576 + j * 8);
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + i * 1024), 16, 0, 0);
   }
 }
 
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
   const int hg = rest % n_hg;
   const int64_t t = rest / n_hg;
   const int tid = threadIdx.x;
-  cx.wave = tid >> 6;
+  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave values stay in SGPRs
   cx.lane = tid & 63;
   cx.g = cx.lane >> 4;
   cx.c = cx.lane & 15;
