@@ -96,7 +96,7 @@ struct MlaCtx {
 };
 
 // Logits of one tile for the wave's 16 heads: S^T[keys, heads] for key
-// blocks [0,16) and [16,32), scaled to base 2 and masked; lane (g,c) gets
+// blocks [0,16) and [16,32), unscaled, -inf where masked; lane (g,c) gets
 // x[r] = key 4g+r and x[4+r] = key 16+4g+r of head c.  The LDS operands of
 // step s+1 are requested before the MFMAs of step s; the scheduling fences
 // keep at most two steps of operands live.
@@ -122,18 +122,23 @@ __device__ __forceinline__ void tile_logits(const uint8_t *__restrict__ ct, cons
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    x[r] = rv[4 * g + r] >= 0 ? s0[r] * scale_log2 : -INFINITY;
-    x[4 + r] = rv[16 + 4 * g + r] >= 0 ? s1[r] * scale_log2 : -INFINITY;
+    x[r] = rv[4 * g + r] >= 0 ? s0[r] : -INFINITY;
+    x[4 + r] = rv[16 + 4 * g + r] >= 0 ? s1[r] : -INFINITY;
   }
 }
 
-// Max over the tile's keys for the lane's head (lanes c, c+16, c+32, c+48).
-__device__ __forceinline__ float tile_max(const float (&x)[8]) {
+// Max over the tile's keys for the lane's head (lanes c, c+16, c+32, c+48),
+// in base-2 units (scale > 0).  The cross-row steps are permlane swaps: with
+// both operands equal, the two results hold the row pair's two halves.
+__device__ __forceinline__ float tile_max(const float (&x)[8], float scale_log2) {
   float mx = x[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  return fmaxf(mx, __shfl_xor(mx, 32));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  return mx * scale_log2;
 }
 
 // Walk the workgroup's tiles: wait for tile i, barrier, prefetch tile i+1,
@@ -188,7 +193,7 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
     tile_logits(ct, rv, qr, scale_log2, g, c, x);
     bool over = false;
     if (!fixed) {
-      const float mx = tile_max(x);
+      const float mx = tile_max(x, scale_log2);
       if (m_ref == -INFINITY) m_ref = mx;  // O and l are still zero for this head
       over = mx > m_ref + 64.0f;
     }
@@ -197,7 +202,9 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = exp2f(fminf(x[i] - msub, 64.0f));
+      // exponent <= 64 unless the pass is discarded; results below 2^-126 of
+      // the reference flush to zero (v_exp_f32), which no sum can notice
+      const float p = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -msub));
       psum += p;
       pb[i] = (__bf16)p;
     }
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
   for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
     float x[8];
     tile_logits(ct, rv, qr, scale_log2, cx.g, cx.c, x);
-    m_ref = fmaxf(m_ref, tile_max(x));
+    m_ref = fmaxf(m_ref, tile_max(x, scale_log2));
   });
   mla_pass<NW, true>(cx, qr, m_ref, scale_log2, t, H, hw0, out, lse, splits, sp, part_o, part_ml);
 }
