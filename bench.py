@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="prefill only")
     ap.add_argument("--no-paged", action="store_true", help="skip the ragged paged decode batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="query rows in the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain 1 GiB device copies (to scale HBM counters)")
     ap.add_argument("--L", type=int, default=None, help="override the prefill length (testing only)")
@@ -219,6 +219,32 @@ def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
     return res
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "prefill_indexer_topk_L131072_traffic.json")
+
+
+def kernel_source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(L):
+    """HBM bytes per launch of the fused indexer from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE record, if it was taken on these kernel sources at
+    this L; otherwise None."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("L") != L or rec.get("source_sha256") != kernel_source_hash(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def _rl(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -317,7 +343,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "L": cfg.L, "H_I": cfg.H_I, "D_I": cfg.D_I, "H": cfg.H, "k": cfg.k,
                    "seed": cfg.seed, "parallelism": "single GPU"},
-        "roofline": dict(_rl("mfma", idx_tflops, PEAK_FP8_TFLOPS, "TFLOP/s"), kernel="prefill_indexer_topk"),
+        "roofline": dict(_rl("mfma", idx_tflops, PEAK_FP8_TFLOPS, "TFLOP/s", recorded_traffic(cfg.L)),
+                         kernel="prefill_indexer_topk"),
         "stages": {
             "quantize": dict(ms=round(ms["quantize"], 3), **_rl("hbm", q_gbs, PEAK_HBM_GBS, "GB/s")),
             "indexer_topk": dict(ms=round(ms["indexer_topk"], 3),
@@ -327,12 +354,18 @@ def main():
         "work": work,
     }
     if args.calibrate_copy:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        # plain copies of known size for scaling HBM counters: the runtime's
+        # device copy, then an elementwise kernel (vector loads and stores)
+        a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
-        line["copy_calibration"] = {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4, "launches": 3}
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        line["copy_calibration"] = {"bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4,
+                                    "launches": "3 runtime copies, then 3 elementwise copies"}
         del a, b
     del t
     torch.cuda.empty_cache()
