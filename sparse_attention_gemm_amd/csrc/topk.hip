@@ -2,16 +2,22 @@
 // mizuki-eaf.pages.dev, "How it works"; m.digipub.cc, section 2).
 //
 // One 1024-thread workgroup per row.  Scores are mapped to order-preserving
-// u32 keys.  The k-th largest key tau is found exactly by histogram
-// narrowing: a 2048-bin histogram over the row's [min, max] key range, then
-// repeatedly over the bin that holds the k-th element, 11 bits at a time,
-// until a bin is one key wide.  Spreading the first histogram over the
-// observed range keeps LDS atomic conflicts low even when all scores share
-// sign and exponent.  The output pass keeps key > tau, plus the most recent
-// (largest-position) ties at tau, and writes positions in ascending order
-// through an ordered block scan, so results are deterministic.
-//
-// The row is re-read from L2 on every pass; HBM sees it once.
+// u32 keys.  The row is read from global memory in coalesced passes (each
+// thread takes 4 consecutive scores, as one 16-byte load when the row is
+// aligned, with several such groups in flight):
+//   1. 2048-bin histograms over the window that holds the k-th largest key,
+//      starting from the top 11 key bits (sign, exponent and two mantissa
+//      bits of the score) and narrowing 11 bits at a time, until the entries
+//      at or above the lower edge of that bin fit in LDS (18432 candidates;
+//      usually after the first histogram);
+//   2. one ordered pass that copies those candidates (key, position) into
+//      LDS in position order.
+// The exact k-th key tau is then found by narrowing over the candidates in
+// LDS, and the output pass keeps key > tau plus the most recent
+// (largest-position) ties at tau, writing positions in ascending order
+// through ordered block scans, so results are deterministic.  If a single
+// key value is too frequent to fit (massive ties), the output pass runs over
+// the row in global memory instead.
 #include "dsa_common.h"
 
 namespace {
@@ -19,12 +25,17 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
+constexpr int kCand = 18432;  // candidates held in LDS
+constexpr int kU = 4;         // groups of 4 row elements per thread in flight
 
 struct TopkShared {
   uint32_t hist[kBins];
+  uint32_t ckey[kCand];
+  int32_t cpos[kCand];
   uint32_t wred[2][kWaves];
-  uint32_t bstar, above, tie_cnt;
+  uint32_t bstar, above, bcnt;
 };
+constexpr size_t kTopkSmem = sizeof(TopkShared);
 
 __device__ __forceinline__ uint32_t row_key(const float *__restrict__ sc, int i) {
   return score_key(canon_zero(sc[i]));
@@ -58,11 +69,143 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wred, 
   return off + inc - v;
 }
 
+// Keys of the 4 consecutive row elements starting at i0 (those >= n are 0).
+__device__ __forceinline__ void load4(const float *__restrict__ sc, bool aligned, int i0, int n, uint32_t (&k4)[4]) {
+  if (aligned && i0 + 3 < n) {
+    const float4 v = *reinterpret_cast<const float4 *>(sc + i0);
+    k4[0] = score_key(canon_zero(v.x));
+    k4[1] = score_key(canon_zero(v.y));
+    k4[2] = score_key(canon_zero(v.z));
+    k4[3] = score_key(canon_zero(v.w));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k4[j] = i0 + j < n ? row_key(sc, i0 + j) : 0u;
+  }
+}
+
+// Visit the row in blocks of 4096 elements (thread t takes elements
+// 4t..4t+3 of a block; kU blocks in flight): f(i0, k4) with i0 the first
+// element of the thread's group.  Every thread runs every block (the loop
+// bounds are uniform), so f may synchronise the workgroup.
+template <typename F>
+__device__ __forceinline__ void for_row4(const float *__restrict__ sc, bool aligned, int n, F &&f) {
+  const int tid = threadIdx.x;
+  for (int b0 = 0; b0 < n; b0 += 4 * kThreads * kU) {
+    uint32_t kk[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) load4(sc, aligned, b0 + 4 * (u * kThreads + tid), n, kk[u]);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (b0 + 4 * u * kThreads >= n) break;  // uniform
+      f(b0 + 4 * (u * kThreads + tid), kk[u]);
+    }
+  }
+}
+
+// Given the histogram in sm.hist, find the bin that holds the remaining-th
+// largest element of the window: its index, the count strictly above it and
+// its own count (all threads get them).
+__device__ __forceinline__ void select_bin(TopkShared &sm, uint32_t remaining, uint32_t &bstar,
+                                           uint32_t &above, uint32_t &bcnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Suffix sums from the top bin.  Thread tid owns bins 2*tid and 2*tid+1;
+  // s_hi = number of window elements in bins above 2*tid+1.
+  const uint32_t h1 = sm.hist[2 * tid + 1], h0 = sm.hist[2 * tid];
+  const uint32_t mine = h0 + h1;
+  // inclusive scan over reversed lanes gives, read back reversed, the
+  // in-wave suffix sum including the own lane
+  const uint32_t inc = wave_incl_scan(__shfl(mine, 63 - lane), lane);
+  const uint32_t suffix_in_wave = __shfl(inc, 63 - lane);
+  if (lane == 0) sm.wred[0][wave] = suffix_in_wave;  // wave total
+  __syncthreads();
+  uint32_t above_waves = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) above_waves += (w > wave) ? sm.wred[0][w] : 0;
+  const uint32_t s_hi = above_waves + suffix_in_wave - mine;  // count in bins > 2*tid+1
+  const uint32_t s1 = s_hi + h1;                               // count in bins >= 2*tid+1
+  const uint32_t s0 = s1 + h0;                                 // count in bins >= 2*tid
+  if (s1 >= remaining && s_hi < remaining) {
+    sm.bstar = 2 * tid + 1;
+    sm.above = s_hi;
+    sm.bcnt = h1;
+  } else if (s0 >= remaining && s1 < remaining) {
+    sm.bstar = 2 * tid;
+    sm.above = s1;
+    sm.bcnt = h0;
+  }
+  __syncthreads();
+  bstar = sm.bstar;
+  above = sm.above;
+  bcnt = sm.bcnt;
+  __syncthreads();
+}
+
+// Histogram narrowing state over a window [base, base + (nbins << shift)).
+struct Narrow {
+  uint32_t base;
+  int shift;
+  uint32_t nbins;
+  uint32_t remaining;  // rank of the target inside the window
+  // the whole key space, binned on the top 11 bits
+  __device__ __forceinline__ void init_full(uint32_t k) {
+    base = 0;
+    shift = 21;
+    nbins = kBins;
+    remaining = k;
+  }
+  __device__ __forceinline__ void init(uint32_t lo, uint32_t hi, uint32_t k) {
+    base = lo;
+    const uint32_t span = hi - lo;
+    shift = span == 0 ? 0 : max(0, 32 - __clz(span) - 11);
+    nbins = kBins;
+    remaining = k;
+  }
+  __device__ __forceinline__ void add(TopkShared &sm, uint32_t key) const {
+    if (key >= base) {
+      const uint32_t d = (key - base) >> shift;
+      if (d < nbins) atomicAdd(&sm.hist[d], 1u);
+    }
+  }
+  // narrow to bin bstar (call after select_bin); returns false at a single key
+  __device__ __forceinline__ bool descend(uint32_t bstar, uint32_t above) {
+    remaining -= above;
+    base += bstar << shift;
+    if (shift == 0) return false;
+    const int nshift = max(0, shift - 11);
+    nbins = 1u << (shift - nshift);
+    shift = nshift;
+    return true;
+  }
+};
+
+__device__ __forceinline__ void clear_hist(TopkShared &sm) {
+  for (int b = threadIdx.x; b < kBins; b += kThreads) sm.hist[b] = 0;
+  __syncthreads();
+}
+
+// Ordered output of one block of up to 1024 entries (one per thread, thread
+// order = position order): keep key > tau, and the ties at tau whose rank
+// among all ties (in position order) is >= tie_cut.  dst and tie_seen carry
+// across blocks.
+__device__ __forceinline__ void emit_block(TopkShared &sm, bool in, uint32_t key, int32_t pos, uint32_t tau,
+                                           uint32_t tie_cut, uint32_t &dst, uint32_t &tie_seen,
+                                           int32_t *__restrict__ out) {
+  const bool tie = in && key == tau;
+  uint32_t n_tie, n_gt;
+  const uint32_t tie_rank = tie_seen + block_excl_scan(tie ? 1u : 0u, sm.wred[0], n_tie);
+  const bool keep = in && (key > tau || (tie && tie_rank >= tie_cut));
+  const uint32_t off = block_excl_scan(keep ? 1u : 0u, sm.wred[1], n_gt);
+  if (keep) out[dst + off] = pos;
+  dst += n_gt;
+  tie_seen += n_tie;
+}
+
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ n_valid, int32_t n_cap,
                                                              int32_t k, int32_t *__restrict__ idx) {
-  __shared__ TopkShared sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  TopkShared &sm = *reinterpret_cast<TopkShared *>(smem_raw);
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int n = max(0, min(n_valid[row], n_cap));
   const float *sc = scores + row * ld;
@@ -71,115 +214,77 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
     for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
     return;
   }
-  // ---- pass 0: key range
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int i = tid; i < n; i += kThreads) {
-    const uint32_t key = row_key(sc, i);
-    kmin = key < kmin ? key : kmin;
-    kmax = key > kmax ? key : kmax;
-  }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if (lane == 0) {
-    sm.wred[0][wave] = kmin;
-    sm.wred[1][wave] = kmax;
-  }
-  __syncthreads();
-  kmin = 0xFFFFFFFFu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    kmin = sm.wred[0][w] < kmin ? sm.wred[0][w] : kmin;
-    kmax = sm.wred[1][w] > kmax ? sm.wred[1][w] : kmax;
-  }
-  __syncthreads();
-  // ---- narrowing passes
-  uint32_t base = kmin;
-  const uint32_t span = kmax - kmin;
-  int shift = span == 0 ? 0 : max(0, 32 - __clz(span) - 11);
-  uint32_t remaining = (uint32_t)k;
-  uint32_t tau = 0, ties = 0;
-  // bins in use at this level: the whole digit at level 0 (the window is the
-  // key range), afterwards only as many as the previous bin was wide
-  uint32_t nbins = kBins;
+  const bool aligned = (reinterpret_cast<uintptr_t>(sc) & 15) == 0;
+  // ---- pass 1: narrow over the row until the candidates fit in LDS
+  Narrow nw;
+  nw.init_full((uint32_t)k);
+  uint32_t above_total = 0, edge = 0;
   while (true) {
-    for (int b = tid; b < kBins; b += kThreads) sm.hist[b] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t key = row_key(sc, i);
-      if (key >= base) {
-        const uint32_t d = (key - base) >> shift;
-        if (d < nbins) atomicAdd(&sm.hist[d], 1u);
-      }
-    }
-    __syncthreads();
-    // Suffix sums from the top bin.  Thread tid owns bins 2*tid and 2*tid+1;
-    // s_hi = number of window elements in bins above 2*tid+1.
-    const uint32_t h1 = sm.hist[2 * tid + 1], h0 = sm.hist[2 * tid];
-    const uint32_t mine = h0 + h1;
-    // inclusive scan over reversed lanes gives, read back reversed, the
-    // in-wave suffix sum including the own lane
-    const uint32_t inc = wave_incl_scan(__shfl(mine, 63 - lane), lane);
-    const uint32_t suffix_in_wave = __shfl(inc, 63 - lane);
-    if (lane == 0) sm.wred[0][wave] = suffix_in_wave;  // wave total
-    __syncthreads();
-    uint32_t above_waves = 0;
+    clear_hist(sm);
+    for_row4(sc, aligned, n, [&](int i0, const uint32_t (&k4)[4]) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) above_waves += (w > wave) ? sm.wred[0][w] : 0;
-    const uint32_t s_hi = above_waves + suffix_in_wave - mine;  // count in bins > 2*tid+1
-    const uint32_t s1 = s_hi + h1;                               // count in bins >= 2*tid+1
-    const uint32_t s0 = s1 + h0;                                 // count in bins >= 2*tid
-    if (s1 >= remaining && s_hi < remaining) {
-      sm.bstar = 2 * tid + 1;
-      sm.above = s_hi;
-      sm.tie_cnt = h1;
-    } else if (s0 >= remaining && s1 < remaining) {
-      sm.bstar = 2 * tid;
-      sm.above = s1;
-      sm.tie_cnt = h0;
+      for (int j = 0; j < 4; ++j)
+        if (i0 + j < n) nw.add(sm, k4[j]);
+    });
+    __syncthreads();
+    uint32_t bstar, above, bcnt;
+    select_bin(sm, nw.remaining, bstar, above, bcnt);
+    edge = nw.base + (bstar << nw.shift);
+    if (above_total + above + bcnt <= (uint32_t)kCand) break;
+    above_total += above;
+    if (!nw.descend(bstar, above)) {
+      // one key value too frequent for LDS: output straight from the row
+      const uint32_t tie_cut = bcnt - nw.remaining;
+      uint32_t dst = 0, tie_seen = 0;
+      for (int b0 = 0; b0 < n; b0 += kThreads) {
+        const int i = b0 + tid;
+        emit_block(sm, i < n, i < n ? row_key(sc, i) : 0u, i, nw.base, tie_cut, dst, tie_seen, out);
+      }
+      return;
     }
+  }
+  // ---- pass 2: candidates (key >= edge) into LDS, in position order
+  uint32_t m = 0;
+  for_row4(sc, aligned, n, [&](int i0, const uint32_t (&k4)[4]) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cnt += (i0 + j < n && k4[j] >= edge) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t off = m + block_excl_scan(cnt, sm.wred[0], tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i0 + j < n && k4[j] >= edge) {
+        sm.ckey[off] = k4[j];
+        sm.cpos[off] = i0 + j;
+        ++off;
+      }
+    m += tot;
+  });
+  __syncthreads();
+  // ---- exact k-th key among the m candidates (all >= edge)
+  Narrow nc;
+  nc.init(edge, 0xFFFFFFFFu, (uint32_t)k);
+  uint32_t tau, ties;
+  while (true) {
+    clear_hist(sm);
+    for (int i = tid; i < (int)m; i += kThreads) nc.add(sm, sm.ckey[i]);
     __syncthreads();
-    const uint32_t bstar = sm.bstar, above = sm.above, bcnt = sm.tie_cnt;
-    __syncthreads();
-    remaining -= above;
-    base += bstar << shift;
-    if (shift == 0) {
-      tau = base;
+    uint32_t bstar, above, bcnt;
+    select_bin(sm, nc.remaining, bstar, above, bcnt);
+    if (!nc.descend(bstar, above)) {
+      tau = nc.base;
       ties = bcnt;
       break;
     }
-    const int nshift = max(0, shift - 11);
-    nbins = 1u << (shift - nshift);
-    shift = nshift;
   }
-  // ---- output pass: contiguous position chunks per thread, ordered scan
-  const int chunk = (n + kThreads - 1) / kThreads;
-  const int pbeg = min(n, tid * chunk), pend = min(n, pbeg + chunk);
-  uint32_t cnt_gt = 0, cnt_eq = 0;
-  for (int i = pbeg; i < pend; ++i) {
-    const uint32_t key = row_key(sc, i);
-    cnt_gt += key > tau;
-    cnt_eq += key == tau;
+  // ---- ordered output from LDS
+  const uint32_t tie_cut = ties - nc.remaining;
+  uint32_t dst = 0, tie_seen = 0;
+  for (int b0 = 0; b0 < (int)m; b0 += kThreads) {
+    const int i = b0 + tid;
+    const bool in = i < (int)m;
+    emit_block(sm, in, in ? sm.ckey[i] : 0u, in ? sm.cpos[i] : 0, tau, tie_cut, dst, tie_seen, out);
   }
-  uint32_t tot_gt, tot_eq;
-  const uint32_t off_gt = block_excl_scan(cnt_gt, sm.wred[0], tot_gt);
-  const uint32_t off_eq = block_excl_scan(cnt_eq, sm.wred[1], tot_eq);
-  (void)ties;
-  const uint32_t need = remaining;            // ties to keep, the most recent ones
-  const uint32_t tie_cut = tot_eq - need;     // tie rank (ascending position) >= tie_cut is kept
-  // kept before my chunk: all gt before + ties before that are kept
-  uint32_t tie_rank = off_eq;
-  uint32_t dst = off_gt + (off_eq > tie_cut ? off_eq - tie_cut : 0);
-  for (int i = pbeg; i < pend; ++i) {
-    const uint32_t key = row_key(sc, i);
-    bool keep = key > tau;
-    if (key == tau) {
-      keep = tie_rank >= tie_cut;
-      ++tie_rank;
-    }
-    if (keep) out[dst++] = i;
-  }
-  // k entries are always written (n > k here)
 }
 
 __global__ void positions_kernel(int32_t *__restrict__ q_pos, int32_t *__restrict__ n_valid, int32_t L) {
@@ -203,7 +308,15 @@ hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStre
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
                        int32_t k, int32_t *idx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(T), dim3(kThreads), 0, s, scores, ld, n_valid, n_cap, k, idx);
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void *)topk_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kTopkSmem);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
+                     idx);
   return hipGetLastError();
 }
 }  // namespace dsa

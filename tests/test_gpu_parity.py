@@ -170,6 +170,27 @@ def test_topk_negative_zero_and_all_equal(dsa, ora):
     assert np.array_equal(got[1], np.arange(n - k, n))
 
 
+def test_topk_tie_class_larger_than_lds(dsa, ora):
+    """A tie class at the k-th score bigger than the LDS candidate buffer:
+    the output pass runs over the row itself and must keep the most recent
+    ties."""
+    _say("topk massive ties")
+    n, k = 40000, 2048
+    base = torch.cat([10.0 + torch.arange(1000, dtype=torch.float32) / 1000.0,
+                      torch.full((30000,), 0.5),
+                      -1.0 - torch.arange(9000, dtype=torch.float32) / 1000.0])
+    perm = synth.permutation(8, 1, n)
+    sc = torch.stack([base[perm], torch.full((n,), 0.25), base.flip(0)])
+    nv = torch.tensor([n, 20000, n], dtype=torch.int32)
+    idx = torch.empty((3, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk_select(sc.to(DEV), nv.to(DEV), k, idx)
+    torch.cuda.synchronize()
+    ref, _ = ora.topk_rows(sc.double().numpy(), nv.numpy(), k)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[1], np.arange(20000 - k, 20000))
+
+
 # ------------------------------------------------------------------ A3
 def _mla_gpu(dsa, q, kv, idx, scale, dtype, use_ws=False):
     T, H = q.shape[0], q.shape[1]
