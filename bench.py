@@ -186,7 +186,9 @@ def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
     names = ["cache_append", "decode_indexer", "topk", "sparse_mla"]
     st = Stages(torch, names)
     for i in range(warmup + steps):
-        flush.zero_()  # evict the 256 MB MALL and L2: each step reads its inputs from HBM
+        # evict the 256 MB MALL and the L2s by reading 512 MB (a read leaves no dirty
+        # lines behind to be written back during the step): each step reads its inputs from HBM
+        flush.view(torch.int64).sum()
         evs = st.new()
         decode_step(dsa, cfg, t, evs, stream)
         torch.cuda.synchronize()
@@ -370,7 +372,7 @@ def main():
     del t
     torch.cuda.empty_cache()
     if not args.no_decode:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
         dcfg = synth.CONFIGS["decode"]
         print("[bench] decode B=64 ctx=32768", file=sys.stderr, flush=True)
         line["decode"] = run_decode(torch, dsa, synth, dcfg, dev, args.decode_steps, 3, flush)

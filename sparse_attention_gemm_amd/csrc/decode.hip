@@ -8,40 +8,70 @@
 //
 // Decode indexer: one query (64 heads x 128 E4M3) per sequence against all of
 // its ctx keys.  This streams 132 B per key from HBM (the key payload and its
-// scale) and is bandwidth bound; each wavefront scores one page (64 keys,
-// 8 KB contiguous in the pool), so every page is read exactly once.
+// scale) and is bandwidth bound.  A wavefront keeps the query's 64 heads in
+// registers and scores kPagesPerWave pages (64 keys, 8 KB contiguous in the
+// pool, each read exactly once), loading the next page's keys while it
+// computes the current one.
 #include "indexer_core.h"
 
 namespace {
 
-constexpr int kPagesPerBlock = 4;  // 4 waves, one page each
+constexpr int kWavesD = 4;
+constexpr int kPagesPerWave = 8;
+constexpr int kPagesPerBlock = kWavesD * kPagesPerWave;
 
-// grid: (ceil(max_ctx / 256), B)
-__global__ __launch_bounds__(256) void decode_indexer_kernel(
+// grid: (ceil(max_ctx / (64 * kPagesPerBlock)), B)
+__global__ __launch_bounds__(kWavesD * 64) void decode_indexer_kernel(
     const uint8_t *__restrict__ q8, const float *__restrict__ qs, const float *__restrict__ w,
     const uint8_t *__restrict__ k8_pool, const float *__restrict__ ks_pool, const int32_t *__restrict__ bt,
     int max_blocks, const int32_t *__restrict__ ctx_len, int64_t n_pool_rows, float *__restrict__ scores,
     int64_t ld, int max_ctx) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t b = blockIdx.y;
   const int ctx = min(ctx_len[b], max_ctx);
-  const int page = blockIdx.x * kPagesPerBlock + wave;
-  const int s0 = page * 64;
-  if (s0 >= ctx || page >= max_blocks) return;
-  const int32_t blk = bt[b * max_blocks + page];
-  const int64_t prow = (int64_t)blk * 64;  // first physical row of the page
-  if (blk < 0 || prow + 64 > n_pool_rows) {  // unmapped page: nothing to score
-    if (s0 + lane < ctx) scores[b * ld + s0 + lane] = -INFINITY;
-    return;
-  }
+  const int npages = min((ctx + 63) >> 6, max_blocks);
+  const int p0 = blockIdx.x * kPagesPerBlock + wave * kPagesPerWave;
+  const int np = min(kPagesPerWave, npages - p0);  // pages of this wave
+  if (np <= 0) return;
+  float *srow = scores + b * ld;
+  // physical first row of page p0 + j, or -1 when unmapped
+  auto page_row = [&](int j) -> int64_t {
+    const int32_t blk = bt[b * max_blocks + p0 + j];
+    const int64_t prow = (int64_t)blk * 64;
+    return (blk < 0 || prow + 64 > n_pool_rows) ? -1 : prow;
+  };
   IdxHalf Q0, Q1;
   idx_load_half(Q0, q8 + b * 64 * 128, w + b * 64, qs[b], 0, lane);
   idx_load_half(Q1, q8 + b * 64 * 128, w + b * 64, qs[b], 32, lane);
-  i32x8 kb[4];
-  idx_load_keys(kb, k8_pool + prow * 128, 128, lane);  // the page's 64 keys are contiguous
-  const float tot = idx_half_score64(Q0, kb) + idx_half_score64(Q1, kb);
-  const int s = s0 + lane;
-  if (s < ctx) scores[b * ld + s] = canon_zero(tot * ks_pool[prow + lane]);
+  i32x8 kb[2][4];
+  float kscale[2];
+  int64_t prow = page_row(0);
+  if (prow >= 0) {
+    idx_load_keys(kb[0], k8_pool + prow * 128, 128, lane);
+    kscale[0] = ks_pool[prow + lane];
+  }
+#pragma unroll
+  for (int j = 0; j < kPagesPerWave; ++j) {
+    if (j >= np) break;  // uniform
+    const int cur = j & 1;
+    int64_t next = -1;
+    if (j + 1 < np) {
+      next = page_row(j + 1);
+      if (next >= 0) {
+        idx_load_keys(kb[cur ^ 1], k8_pool + next * 128, 128, lane);
+        kscale[cur ^ 1] = ks_pool[next + lane];
+      }
+    }
+    const int s = (p0 + j) * 64 + lane;
+    if (prow >= 0) {
+      const float tot = idx_half_score64(Q0, kb[cur]) + idx_half_score64(Q1, kb[cur]);
+      if (s < ctx) srow[s] = canon_zero(tot * kscale[cur]);
+    } else if (s < ctx) {
+      srow[s] = -INFINITY;  // unmapped page: nothing to score
+    }
+    prow = next;
+  }
 }
 
 // One workgroup per appended token: 72 chunks of latent, 8 of key, 1 scale.
@@ -82,7 +112,7 @@ hipError_t launch_decode_indexer(const uint8_t *q8, const float *qs, const float
                                  float *scores, int64_t ld, hipStream_t s) {
   if (B == 0) return hipSuccess;
   dim3 grid((max_ctx + 64 * kPagesPerBlock - 1) / (64 * kPagesPerBlock), B);
-  hipLaunchKernelGGL(decode_indexer_kernel, grid, dim3(256), 0, s, q8, qs, w, k8_pool, ks_pool, block_table,
+  hipLaunchKernelGGL(decode_indexer_kernel, grid, dim3(kWavesD * 64), 0, s, q8, qs, w, k8_pool, ks_pool, block_table,
                      max_blocks, ctx_len, n_pool_rows, scores, ld, max_ctx);
   return hipGetLastError();
 }
