@@ -541,3 +541,87 @@ def test_sparse_mla_bf16_late_large_logits(dsa, ora, H):
     o, l = ora.sparse_mla_rows(q, kv, idx.numpy(), 1 / math.sqrt(192))
     assert np.isfinite(g).all() and np.isfinite(gl).all()
     check_attention(g, gl, o, l, "bf16", "mla late large logits")
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _sample_rows(L, extra, seed):
+    fixed = [0, 1, 2046, 2047, 2048, 2049, 4095, L // 2 - 1, L - 1]
+    drawn = synth.randint(seed, 1, (extra,), 0, L).tolist()
+    return np.array(sorted(set(r for r in fixed + drawn if 0 <= r < L)), dtype=np.int64)
+
+
+@pytest.mark.slow
+def test_prefill_full_size_sampled_rows(dsa, ora):
+    """The benchmarked L = 131072 pipeline (quantise -> fused indexer + top-k ->
+    sparse MLA), checked against the oracle on sampled query rows."""
+    cfg = synth.CONFIGS["prefill128k"]
+    L, k = cfg.L, cfg.k
+    _say(f"prefill full size L={L}")
+    q_i, k_i, w = synth.prefill_indexer_inputs(cfg, device=DEV)
+    q = synth.prefill_attn_q(cfg, device=DEV)
+    kv = synth.prefill_latent(cfg, device=DEV)
+    q8 = torch.empty((L, cfg.H_I, cfg.D_I), dtype=torch.uint8, device=DEV)
+    qs = torch.empty(L, dtype=torch.float32, device=DEV)
+    k8 = torch.empty((L, cfg.D_I), dtype=torch.uint8, device=DEV)
+    ks = torch.empty(L, dtype=torch.float32, device=DEV)
+    dsa.dsa_quantize_e4m3_per_token(q_i, q8, qs, rows=L, cols=cfg.H_I * cfg.D_I)
+    dsa.dsa_quantize_e4m3_per_token(k_i, k8, ks, rows=L, cols=cfg.D_I)
+    idx = torch.empty((L, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((L, cfg.H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((L, cfg.H), dtype=torch.float32, device=DEV)
+    args = dsa.make_prefill_args(L, cfg.H_I, cfg.D_I, cfg.H, k, dsa.DSA_E4M3, q8, qs, k8, ks, w, dsa.DSA_BF16, q, kv,
+                                 cfg.sm_scale, idx, out, lse)
+    ws = torch.empty(dsa.dsa_prefill_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    dsa.dsa_prefill_select(args, ws)
+    dsa.dsa_sparse_mla_fwd(q, kv, idx, cfg.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    del ws
+    rows = _sample_rows(L, 3, 21)
+    rt = torch.from_numpy(rows).to(DEV)
+    # quantiser: bit-exact on the sampled query rows and on every key
+    o8, os_ = ora.quantize_rows(q_i[rt].view(len(rows), -1).cpu().numpy())
+    assert np.array_equal(q8[rt].view(len(rows), -1).cpu().numpy(), o8)
+    assert np.array_equal(qs[rt].cpu().numpy(), os_)
+    ok8, oks = ora.quantize_rows(k_i.cpu().numpy())
+    k8c, ksc = k8.cpu().numpy(), ks.cpu().numpy()
+    assert np.array_equal(k8c, ok8) and np.array_equal(ksc, oks)
+    del q_i, k_i
+    # selection: oracle scores of the sampled rows
+    sc = ora.indexer_rows(q8[rt].cpu().numpy(), k8c, w[rt].cpu().numpy(), rows.astype(np.int32),
+                          q_scale=qs[rt].cpu().numpy(), k_scale=ksc)
+    gidx = idx[rt].cpu().numpy()
+    for j, r in enumerate(rows):
+        check_topk_row(gidx[j], sc[j], int(r) + 1, k, f"L={L} row {r}")
+    # attention over the GPU's own selection
+    o, l = ora.sparse_mla_rows(q[rt].cpu(), kv.cpu(), gidx, cfg.sm_scale)
+    check_attention(out[rt].float().cpu().double().numpy(), lse[rt].cpu().double().numpy(), o, l, "bf16",
+                    f"L={L}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["decode", "paged"])
+def test_decode_full_size_sampled_sequences(dsa, ora, name):
+    """The benchmarked decode batches (B = 64 at context 32768; B = 128 ragged
+    with shuffled pages), checked against the oracle on sampled sequences."""
+    cfg = synth.CONFIGS[name]
+    _say(f"decode full size {cfg.name}")
+    ctx = synth.decode_ctx(cfg)
+    bt, nb = synth.decode_block_table(cfg, ctx)
+    pools = synth.build_decode_pools(cfg, ctx, bt, nb, device=DEV)
+    qside = synth.decode_queries(cfg)
+    out, lse, idx = _run_decode(dsa, cfg, ctx, bt, nb, pools, qside)
+    del pools
+    gidx = idx.cpu().numpy()
+    q8, qs, w, q = qside
+    seqs = sorted({0, cfg.B - 1, int(torch.argmax(ctx)), int(torch.argmin(ctx)),
+                   int(synth.randint(22, 1, (1,), 0, cfg.B)[0])})
+    for b in seqs:
+        c = int(ctx[b])
+        kb, sb = synth.decode_seq_keys(cfg, b, c)
+        sc = ora.indexer_rows(q8[b:b + 1], kb, w[b:b + 1], np.array([c - 1], np.int32), q_scale=qs[b:b + 1],
+                              k_scale=sb)
+        check_topk_row(gidx[b], sc[0], c, cfg.k, f"{cfg.name} b={b}")
+        lat = synth.decode_seq_latent(cfg, b, c)
+        o, l = ora.sparse_mla_rows(q[b:b + 1], lat, gidx[b:b + 1], cfg.sm_scale)
+        check_attention(out[b:b + 1].float().cpu().double().numpy(), lse[b:b + 1].cpu().double().numpy(), o, l,
+                        "bf16", f"{cfg.name} b={b}")
