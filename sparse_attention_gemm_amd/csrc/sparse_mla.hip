@@ -12,8 +12,7 @@
 //    then block table when paged) into LDS;
 //  * the selected latent rows are gathered 32 at a time straight from global
 //    memory into LDS (direct-to-LDS loads, no register staging), row-major,
-//    double buffered so the gather of tile i+1 overlaps the MFMAs of tile i;
-//    each row is fetched once for all heads of the workgroup;
+//    into three buffers; each row is fetched once for all heads;
 //  * logits are computed transposed, S^T = C Q^T (keys x heads), with bf16
 //    MFMA 16x16x32 and Q^T resident in registers; in that layout each lane
 //    holds 8 keys of one head, which is exactly the B operand layout the PV
@@ -22,10 +21,15 @@
 //  * the value operand of PV (value dims x keys) is read from the same
 //    row-major tile with the transposing LDS load, which hands each lane four
 //    keys of one value column;
+//  * probabilities and PV are pipelined across tiles with one barrier per
+//    tile: while tile j+2 is gathered, the probabilities of tile j+1 are
+//    formed and published and PV runs on tile j;
 //  * online softmax in fp32 (base-2 exponent with the scale folded in),
 //    output O^T (value dims x heads) accumulated in fp32 registers;
 //  * optional split of the selection across workgroups with an LSE-weighted
 //    combine (used when there are too few queries to fill the GPU).
+#include <algorithm>
+
 #include "dsa_common.h"
 
 namespace {
@@ -38,7 +42,8 @@ constexpr int kTileBytes = kBN * kCRow;  // 37376
 constexpr int kTileSlots = kBN * kRowSlots;
 constexpr int kGatherInsts = (kTileSlots + 63) / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
 constexpr int kPBytes = 8 * 64 * 16;    // P^T of up to 8 head tiles, in B-operand lane order
-constexpr int kSmemMla = 2 * kTileBytes + kPBytes + 128 * 4 + 2048 * 4 + 16;
+constexpr int kNBuf = 3;                 // gathered tiles: PV of tile j, logits of tile j+1, gather of j+2
+constexpr int kSmemMla = kNBuf * kTileBytes + 2 * kPBytes + 128 * 4 + 2048 * 4 + 16;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -86,8 +91,8 @@ __device__ __forceinline__ void gather_tile_async(uint8_t *__restrict__ dst, con
 // Shared state of one sparse-MLA workgroup.
 struct MlaCtx {
   const __bf16 *kv;
-  uint8_t *tiles;       // 2 x kTileBytes of LDS
-  uint8_t *pbuf;        // P^T exchange: [head tile][lane] x 16 bytes
+  uint8_t *tiles;       // kNBuf x kTileBytes of LDS
+  uint8_t *pbuf;        // P^T exchange, two buffers of [head tile][lane] x 16 bytes
   float *lbuf;          // softmax sums of the workgroup's heads
   const int *rows;      // physical rows of the workgroup's entries (LDS)
   int *flag;            // LDS: set when a tile overshoots the softmax reference
@@ -159,6 +164,21 @@ __device__ __forceinline__ void for_each_tile(const MlaCtx &cx, Body &&body) {
   __syncthreads();
 }
 
+// s_waitcnt immediate: at most n vector-memory operations outstanding
+// (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Wait until only the newest tile's gathers may still be in flight (every
+// tile costs a wave the same number of gather instructions).
+template <int NW>
+__device__ __forceinline__ void wait_all_but_newest_tile(int wave) {
+  constexpr int base = kGatherInsts / NW, rem = kGatherInsts % NW;
+  if (rem != 0 && wave < rem)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(base + 1));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(base));
+}
+
 // One accumulation pass over the workgroup's tiles.
 //  * Logits/softmax: wave w owns head tile w (heads 16w..16w+15 of the
 //    workgroup).  It turns its logits into bf16 probabilities and publishes
@@ -168,6 +188,10 @@ __device__ __forceinline__ void for_each_tile(const MlaCtx &cx, Body &&body) {
 //    the row-major tile through the transposing LDS load, P^T from LDS.
 //    Splitting PV by value dims reads each tile's values once per workgroup
 //    instead of once per wave.
+//  * The two are pipelined across tiles with one barrier per tile: iteration
+//    j computes the probabilities of tile j+1 and then PV of tile j with the
+//    probabilities every wave published before the barrier.  Three tile
+//    buffers (j, j+1, and j+2 being gathered) and two P buffers.
 // fixed = false: each head's exponent reference is the max of its first tile
 // with a valid entry; a later tile more than 64 above it sets cx.flag and the
 // pass is discarded (returns false, nothing written).  fixed = true: the
@@ -188,9 +212,13 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
   // transposing-load lane roles: row 4g + (c>>2) of each 4-row group, value chunk (c&3),
   // starting at this wave's first value tile
   const int tr_off = (4 * g + (c >> 2)) * kCRow + (c & 3) * 8 + wave * MT * 32;
-  for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
+  const int n = cx.te - cx.tb;
+  auto tile_of = [&](int j) { return cx.tiles + (j % kNBuf) * kTileBytes; };
+  auto gather = [&](int j) { gather_tile_async<NW>(tile_of(j), cx.rows, j * kBN, cx.kv, cx.wave, cx.lane); };
+  // logits and probabilities of tile j, published in P buffer j&1
+  auto score_tile = [&](int j) {
     float x[8];
-    tile_logits(ct, rv, qr, scale_log2, g, c, x);
+    tile_logits(tile_of(j), cx.rows + j * kBN, qr, scale_log2, g, c, x);
     bool over = false;
     if (!fixed) {
       const float mx = tile_max(x, scale_log2);
@@ -210,8 +238,12 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
     }
     l_run += psum;
     if (!fixed && __ballot(over) && cx.lane == 0) *cx.flag = 1;
-    *reinterpret_cast<bf16x8 *>(cx.pbuf + (wave * 64 + cx.lane) * 16) = pb;
-    __syncthreads();  // every head tile's P is in LDS
+    *reinterpret_cast<bf16x8 *>(cx.pbuf + (j & 1) * kPBytes + (wave * 64 + cx.lane) * 16) = pb;
+  };
+  // PV of tile j with the probabilities in P buffer j&1
+  auto pv_tile = [&](int j) {
+    const uint8_t *ct = tile_of(j);
+    const uint8_t *pj = cx.pbuf + (j & 1) * kPBytes;
     // value operands of this wave's MT tiles (keys 4g..4g+3 | 16+4g..16+4g+3)
     bf16x8 va[MT];
 #pragma unroll
@@ -222,15 +254,35 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
       va[i] = *reinterpret_cast<const bf16x8 *>(lohi);
     }
     bf16x8 pn[2];
-    pn[0] = *reinterpret_cast<const bf16x8 *>(cx.pbuf + cx.lane * 16);
+    pn[0] = *reinterpret_cast<const bf16x8 *>(pj + cx.lane * 16);
 #pragma unroll
-    for (int n = 0; n < NW; ++n) {
-      if (n + 1 < NW) pn[(n + 1) & 1] = *reinterpret_cast<const bf16x8 *>(cx.pbuf + ((n + 1) * 64 + cx.lane) * 16);
+    for (int nn = 0; nn < NW; ++nn) {
+      if (nn + 1 < NW) pn[(nn + 1) & 1] = *reinterpret_cast<const bf16x8 *>(pj + ((nn + 1) * 64 + cx.lane) * 16);
 #pragma unroll
-      for (int i = 0; i < MT; ++i) o[i][n] = mfma_bf16_16x16x32(va[i], pn[n & 1], o[i][n]);
+      for (int i = 0; i < MT; ++i) o[i][nn] = mfma_bf16_16x16x32(va[i], pn[nn & 1], o[i][nn]);
       __builtin_amdgcn_sched_barrier(0);
     }
-  });
+  };
+  if (n > 0) {
+    gather(0);
+    if (n > 1) {
+      gather(1);
+      wait_all_but_newest_tile<NW>(wave);  // tile 0 landed (tile 1 may be in flight)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    score_tile(0);
+    for (int j = 0; j < n; ++j) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's gathers of tile j+1 have landed
+      __syncthreads();  // P(j) from every wave; tile j+1 from every wave; nobody reads tile j-1 any more
+      if (j + 2 < n) gather(j + 2);
+      if (j + 1 < n) score_tile(j + 1);
+      pv_tile(j);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   if (!fixed && *cx.flag) return false;  // uniform: read after the final barrier
   // softmax sums of the wave's head tile -> LDS, for the waves that own other value dims
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -269,6 +321,67 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
   return true;
 }
 
+// Work item of one workgroup: query token t, head group hg, selection split
+// sp.  Resolves the item's physical rows into LDS, loads Q^T of the wave's
+// head tile (lane (g, c) holds head hw0 + 16*wave + c, dims 32*s + 8*g .. +8
+// for step s) and clears the overshoot flag.
+struct MlaItem {
+  int64_t t;
+  int hg, sp, hw0;
+};
+
+template <int NW>
+__device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, uint8_t *smem_raw, int64_t wid, const int32_t *__restrict__ idx,
+                                             const int32_t *__restrict__ bt, int max_blocks, int64_t N, int H, int k,
+                                             int splits) {
+  cx.tiles = smem_raw;
+  cx.pbuf = smem_raw + kNBuf * kTileBytes;
+  cx.lbuf = reinterpret_cast<float *>(cx.pbuf + 2 * kPBytes);
+  int *rows = reinterpret_cast<int *>(cx.lbuf + 128);   // <= 2048 physical rows
+  cx.rows = rows;
+  cx.flag = rows + 2048;
+  const int n_hg = H / (16 * NW);
+  MlaItem it;
+  it.sp = (int)(wid % splits);
+  const int64_t rest = wid / splits;
+  it.hg = (int)(rest % n_hg);
+  it.t = rest / n_hg;
+  const int tid = threadIdx.x;
+  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave values stay in SGPRs
+  cx.lane = tid & 63;
+  cx.g = cx.lane >> 4;
+  cx.c = cx.lane & 15;
+  it.hw0 = it.hg * NW * 16;  // first head of the workgroup
+  const int ntiles = (k + kBN - 1) / kBN;
+  const int per = (ntiles + splits - 1) / splits;
+  cx.tb = it.sp * per;
+  cx.te = min(ntiles, cx.tb + per);
+  const int32_t *irow = idx + it.t * k;
+  // physical rows of this workgroup's entries [tb*32, te*32)
+  for (int e = tid; e < (cx.te - cx.tb) * kBN; e += NW * 64)
+    rows[e] = (int)phys_row(irow, bt, max_blocks, N, it.t, cx.tb * kBN + e, k);
+  if (tid == 0) *cx.flag = 0;
+  __syncthreads();
+  return it;
+}
+
+__device__ __forceinline__ void load_qt(bf16x8 (&qr)[18], const __bf16 *__restrict__ q, int64_t t, int H, int hw0,
+                                        const MlaCtx &cx) {
+  const __bf16 *qrow = q + (t * H + hw0 + 16 * cx.wave + cx.c) * 576 + cx.g * 8;
+#pragma unroll
+  for (int s = 0; s < 18; ++s) qr[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
+}
+
+// The first output element of a work item doubles as its "redo" mark: an
+// all-ones (NaN) pattern written when the item's first pass was discarded.
+// Every completed item overwrites it with its result.
+__device__ __forceinline__ uint32_t *redo_mark_f32(float *part_o, int64_t t, int splits, int sp, int H, int hw0) {
+  return reinterpret_cast<uint32_t *>(part_o + ((t * splits + sp) * H + hw0) * 512);
+}
+__device__ __forceinline__ uint16_t *redo_mark_bf16(__bf16 *out, int64_t t, int H, int hw0) {
+  return reinterpret_cast<uint16_t *>(out + (t * H + hw0) * 512);
+}
+
 // NW waves: 16*NW heads per workgroup; for the logits wave w owns 16 heads,
 // for PV it owns 512/NW value dims of all 16*NW heads.
 //
@@ -277,8 +390,8 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
 // entry, and then stays fixed, so the accumulators are only ever written by
 // MFMAs.  Probabilities are exp2(x - m_ref); while x <= m_ref + 64 they stay
 // below 2^64, far inside the fp32/bf16 range, and the result is the same
-// softmax.  If any tile overshoots that, the workgroup instead takes the
-// exact per-head maxima in an extra logits-only pass and accumulates again.
+// softmax.  If any tile overshoots that, the workgroup writes its redo mark
+// instead and sparse_mla_bf16_redo_kernel recomputes it with exact maxima.
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
@@ -288,53 +401,66 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
   extern __shared__ __align__(16) uint8_t smem_raw[];
   MlaCtx cx;
   cx.kv = kv;
-  cx.tiles = smem_raw;
-  cx.pbuf = smem_raw + 2 * kTileBytes;
-  cx.lbuf = reinterpret_cast<float *>(cx.pbuf + kPBytes);
-  int *rows = reinterpret_cast<int *>(cx.lbuf + 128);   // <= 2048 physical rows
-  cx.rows = rows;
-  cx.flag = rows + 2048;
-
-  const int n_hg = H / (16 * NW);
-  const int bid = blockIdx.x;
-  const int sp = bid % splits;
-  const int rest = bid / splits;
-  const int hg = rest % n_hg;
-  const int64_t t = rest / n_hg;
-  const int tid = threadIdx.x;
-  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave values stay in SGPRs
-  cx.lane = tid & 63;
-  cx.g = cx.lane >> 4;
-  cx.c = cx.lane & 15;
-  const int hw0 = hg * NW * 16;  // first head of the workgroup
-  const int ntiles = (k + kBN - 1) / kBN;
-  const int per = (ntiles + splits - 1) / splits;
-  cx.tb = sp * per;
-  cx.te = min(ntiles, cx.tb + per);
-  const int32_t *irow = idx + t * k;
-
-  // physical rows of this workgroup's entries [tb*32, te*32)
-  for (int e = tid; e < (cx.te - cx.tb) * kBN; e += NW * 64)
-    rows[e] = (int)phys_row(irow, bt, max_blocks, N, t, cx.tb * kBN + e, k);
-  if (tid == 0) *cx.flag = 0;
-  __syncthreads();
-
-  // Q^T of the wave's head tile in registers: lane (g, c) holds head
-  // hw0 + 16*wave + c, dims 32*s + 8*g .. +8 for step s.
+  const MlaItem it = mla_setup<NW>(cx, smem_raw, blockIdx.x, idx, bt, max_blocks, N, H, k, splits);
   bf16x8 qr[18];
-  const __bf16 *qrow = q + (t * H + hw0 + 16 * cx.wave + cx.c) * 576 + cx.g * 8;
-#pragma unroll
-  for (int s = 0; s < 18; ++s) qr[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
+  load_qt(qr, q, it.t, H, it.hw0, cx);
   float m_ref = -INFINITY;
-  if (mla_pass<NW, false>(cx, qr, m_ref, scale_log2, t, H, hw0, out, lse, splits, sp, part_o, part_ml)) return;
-  // rare: exact per-head maxima, then accumulate with them
-  m_ref = -INFINITY;
-  for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
-    float x[8];
-    tile_logits(ct, rv, qr, scale_log2, cx.g, cx.c, x);
-    m_ref = fmaxf(m_ref, tile_max(x, scale_log2));
-  });
-  mla_pass<NW, true>(cx, qr, m_ref, scale_log2, t, H, hw0, out, lse, splits, sp, part_o, part_ml);
+  if (mla_pass<NW, false>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o, part_ml))
+    return;
+  if (threadIdx.x == 0) {
+    if (splits == 1)
+      *redo_mark_bf16(out, it.t, H, it.hw0) = 0xFFFFu;
+    else
+      *redo_mark_f32(part_o, it.t, splits, it.sp, H, it.hw0) = 0xFFFFFFFFu;
+  }
+}
+
+// Recomputes, with exact per-head maxima, the work items whose redo mark is
+// set.  One workgroup per CU walks the items in strides; it reads one mark
+// per item and exits when none is set (the overshoot is rare).
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_redo_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ bt, int max_blocks, int64_t N, int T, int H, int k, float scale_log2,
+    __bf16 *__restrict__ out, float *__restrict__ lse, int splits, float *__restrict__ part_o,
+    float *__restrict__ part_ml, int64_t nitems) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  __shared__ int64_t todo[NW * 64];
+  __shared__ int ntodo;
+  const int tid = threadIdx.x;
+  const int n_hg = H / (16 * NW);
+  for (int64_t base = (int64_t)blockIdx.x * (NW * 64); base < nitems; base += (int64_t)gridDim.x * (NW * 64)) {
+    if (tid == 0) ntodo = 0;
+    __syncthreads();
+    const int64_t wid = base + tid;
+    if (wid < nitems) {
+      const int sp = (int)(wid % splits);
+      const int64_t rest = wid / splits;
+      const int hw0 = (int)(rest % n_hg) * NW * 16;
+      const int64_t t = rest / n_hg;
+      const bool marked = splits == 1 ? *redo_mark_bf16(out, t, H, hw0) == 0xFFFFu
+                                      : *redo_mark_f32(part_o, t, splits, sp, H, hw0) == 0xFFFFFFFFu;
+      if (marked) todo[atomicAdd(&ntodo, 1)] = wid;
+    }
+    __syncthreads();
+    const int n = ntodo;
+    for (int i = 0; i < n; ++i) {
+      const int64_t w = todo[i];
+      MlaCtx cx;
+      cx.kv = kv;
+      const MlaItem it = mla_setup<NW>(cx, smem_raw, w, idx, bt, max_blocks, N, H, k, splits);
+      bf16x8 qr[18];
+      load_qt(qr, q, it.t, H, it.hw0, cx);
+      float m_ref = -INFINITY;
+      for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
+        float x[8];
+        tile_logits(ct, rv, qr, scale_log2, cx.g, cx.c, x);
+        m_ref = fmaxf(m_ref, tile_max(x, scale_log2));
+      });
+      mla_pass<NW, true>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o, part_ml);
+    }
+    __syncthreads();
+  }
 }
 
 // LSE-weighted combine of split partials.  grid (T*H/4), block 256: 4 heads,
@@ -446,12 +572,23 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
     hipError_t e = hipFuncSetAttribute((const void *)sparse_mla_bf16_kernel<NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemMla);
     if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void *)sparse_mla_bf16_redo_kernel<NW>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kSmemMla);
+    if (e != hipSuccess) return e;
     attr_done = true;
   }
-  const int64_t blocks = (int64_t)T * (H / (16 * NW)) * splits;
-  hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW>), dim3((uint32_t)blocks), dim3(NW * 64), kSmemMla, s,
+  const int64_t items = (int64_t)T * (H / (16 * NW)) * splits;
+  hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW>), dim3((uint32_t)items), dim3(NW * 64), kSmemMla, s,
                      (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
                      (__bf16 *)out, lse, splits, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t grid = std::min<int64_t>(cus, (items + NW * 64 - 1) / (NW * 64));
+  hipLaunchKernelGGL((sparse_mla_bf16_redo_kernel<NW>), dim3((uint32_t)grid), dim3(NW * 64), kSmemMla, s,
+                     (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
+                     (__bf16 *)out, lse, splits, part_o, part_ml, items);
   return hipGetLastError();
 }
 
