@@ -26,6 +26,7 @@ __global__ __launch_bounds__(kWavesD * 64) void decode_indexer_kernel(
     const uint8_t *__restrict__ k8_pool, const float *__restrict__ ks_pool, const int32_t *__restrict__ bt,
     int max_blocks, const int32_t *__restrict__ ctx_len, int64_t n_pool_rows, float *__restrict__ scores,
     int64_t ld, int max_ctx) {
+  __shared__ uint8_t qscratch[kWavesD][kQueryScratch];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t b = blockIdx.y;
@@ -41,9 +42,8 @@ __global__ __launch_bounds__(kWavesD * 64) void decode_indexer_kernel(
     const int64_t prow = (int64_t)blk * 64;
     return (blk < 0 || prow + 64 > n_pool_rows) ? -1 : prow;
   };
-  IdxHalf Q0, Q1;
-  idx_load_half(Q0, q8 + b * 64 * 128, w + b * 64, qs[b], 0, lane);
-  idx_load_half(Q1, q8 + b * 64 * 128, w + b * 64, qs[b], 32, lane);
+  IdxQuery<4> Q;
+  idx_load_query<4>(Q, q8 + b * 64 * 128, w + b * 64, qs[b], lane, qscratch[wave]);
   i32x8 kb[2][4];
   float kscale[2];
   int64_t prow = page_row(0);
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kWavesD * 64) void decode_indexer_kernel(
     }
     const int s = (p0 + j) * 64 + lane;
     if (prow >= 0) {
-      const float tot = idx_half_score64(Q0, kb[cur]) + idx_half_score64(Q1, kb[cur]);
+      const float tot = idx_score64<4>(Q, kb[cur]);
       if (s < ctx) srow[s] = canon_zero(tot * kscale[cur]);
     } else if (s < ctx) {
       srow[s] = -INFINITY;  // unmapped page: nothing to score

@@ -17,7 +17,9 @@ __global__ __launch_bounds__(256) void indexer_scores_fp8_kernel(
     const float *__restrict__ ks, const float *__restrict__ w, const int32_t *__restrict__ q_pos,
     int32_t T, int32_t S, float *__restrict__ scores, int64_t ld) {
   constexpr int H_I = 32 * NHALF;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ uint8_t qscratch[4][kQueryScratch];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.y * 4 + wave;
   if (t >= T) return;
   const int p = q_pos[t];
@@ -28,10 +30,8 @@ __global__ __launch_bounds__(256) void indexer_scores_fp8_kernel(
     for (int s = sbeg + lane; s < send; s += 64) orow[s] = -INFINITY;
     return;
   }
-  IdxHalf Q[NHALF];
-#pragma unroll
-  for (int h = 0; h < NHALF; ++h)
-    idx_load_half(Q[h], q8 + (int64_t)t * H_I * 128, w + (int64_t)t * H_I, qs[t], 32 * h, lane);
+  IdxQuery<2 * NHALF> Q;
+  idx_load_query<2 * NHALF>(Q, q8 + (int64_t)t * H_I * 128, w + (int64_t)t * H_I, qs[t], lane, qscratch[wave]);
   const int g = lane >> 4, c = lane & 15;
   for (int s0 = sbeg; s0 < send; s0 += 64) {
     const int s = s0 + lane;
@@ -45,8 +45,7 @@ __global__ __launch_bounds__(256) void indexer_scores_fp8_kernel(
       const int key = min(s0 + 16 * u + c, S - 1);
       b[u] = *reinterpret_cast<const i32x8 *>(k8 + (int64_t)key * 128 + 32 * g);
     }
-    float tot = idx_half_score64(Q[0], b);
-    if (NHALF == 2) tot = tot + idx_half_score64(Q[NHALF - 1], b);
+    const float tot = idx_score64<2 * NHALF>(Q, b);
     if (s < send) orow[s] = (s <= p) ? canon_zero(tot * ks[s]) : -INFINITY;
   }
 }

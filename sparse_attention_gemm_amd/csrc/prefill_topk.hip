@@ -43,6 +43,7 @@ constexpr int kKRow = 160;      // LDS bytes per key row: 128 + 32 pad (40 dword
 constexpr int kKSlots = kKRow / 16;
 constexpr int kKeyInsts = kTile * kKSlots / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
 constexpr int kBins = 256;      // compaction histogram
+static_assert(kBins * 4 >= kQueryScratch, "the histogram doubles as query scratch");
 // An early cut may leave at most this many entries (k <= 2048), so that it
 // frees at least a quarter of the buffer; otherwise the narrowing continues.
 constexpr int kCutLimit = kCap - kCap / 4;
@@ -187,8 +188,14 @@ __device__ __forceinline__ void load_tile_async(uint8_t *dkeys, float *dks, cons
   for (int i = wave; i < kKeyInsts; i += kWaves) {
     const int slot = i * 64 + lane;
     const int r = slot / kKSlots;
-    const int j = min(slot - r * kKSlots, 7);
-    const uint32_t off = (uint32_t)(min(r, nrow - 1) * 128 + j * 16);
+    const uint32_t off_full = (uint32_t)(r * 128 + min(slot - r * kKSlots, 7) * 16);
+    uint32_t off = off_full;
+    if (nrow < kTile) {  // uniform: the sequence's last tile; recompute from a fresh lane id
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      const int s2 = i * 64 + l, r2 = s2 / kKSlots;
+      off = (uint32_t)(min(r2, nrow - 1) * 128 + min(s2 - r2 * kKSlots, 7) * 16);
+    }
     __builtin_amdgcn_global_load_lds(kbase + off, (lds_void *)(dkeys + i * 1024), 16, 0, 0);
   }
   if (wave == kWaves - 1) {
@@ -201,18 +208,26 @@ __device__ __forceinline__ void load_tile_async(uint8_t *dkeys, float *dks, cons
 // into (nkeys, nks).  The current tile's LDS reads are issued before the
 // prefetch: the compiler cannot tell the direct-to-LDS writes from them and
 // would otherwise wait for the prefetch before reading LDS.
+// Score tile `it` from (ckeys, cks) for one token and prefetch tile it+1
+// into (nkeys, nks).  Every LDS read of the tile is issued before the
+// prefetch (the last key block's operand right before it): the compiler
+// cannot tell the direct-to-LDS writes from them and would otherwise wait for
+// the prefetch before reading LDS.
 __device__ __forceinline__ float score_and_prefetch(uint8_t *nkeys, float *nks, const uint8_t *ckeys, const float *cks,
-                                                    bool prefetch, bool need, const IdxHalf &Q0, const IdxHalf &Q1,
+                                                    bool prefetch, bool need, const IdxQuery<4> &Q,
                                                     const uint8_t *__restrict__ k8, const float *__restrict__ ks,
                                                     int L, int next, int wave, int lane) {
-  // read unconditionally (the buffer is always valid LDS): a conditional
-  // read would make the compiler initialise the 32 operand registers
-  i32x8 b[4];
-  idx_load_keys(b, ckeys, kKRow, lane);
+  const int g = lane >> 4, c = lane & 15;
   const float ksv = cks[lane];
-  if (prefetch) load_tile_async(nkeys, nks, k8, ks, L, next, wave, lane);
-  if (!need) return 0.0f;
-  return canon_zero(idx_full_score64(Q0, Q1, b) * ksv);
+  auto issue_prefetch = [&] {
+    if (prefetch) load_tile_async(nkeys, nks, k8, ks, L, next, wave, lane);
+  };
+  if (!need) {
+    issue_prefetch();
+    return 0.0f;
+  }
+  auto get_b = [&](int u) { return *reinterpret_cast<const i32x8 *>(ckeys + (16 * u + c) * kKRow + 32 * g); };
+  return canon_zero(idx_score64<4>(Q, get_b, issue_prefetch) * ksv);
 }
 
 __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
@@ -231,15 +246,11 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
   const int last = min(t0 + kTok - 1, L - 1);
   const int ntiles = last / kTile + 1;
 
-  // heads 0..31 and 32..63; the score is half(0..31) + half(32..63)
-  IdxHalf Q0, Q1;
-  {
-    const uint8_t *qt = q8 + (int64_t)tq * 64 * 128;
-    const float *wt = w + (int64_t)tq * 64;
-    const float qsv = qs[tq];
-    idx_load_half(Q0, qt, wt, qsv, 0, lane);
-    idx_load_half(Q1, qt, wt, qsv, 32, lane);
-  }
+  // the query's 64 heads (and the pieces of its weighted sum); the LDS of its
+  // compaction histogram serves as scratch until the first compaction
+  IdxQuery<4> Q;
+  idx_load_query<4>(Q, q8 + (int64_t)tq * 64 * 128, w + (int64_t)tq * 64, qs[tq], lane,
+                    reinterpret_cast<uint8_t *>(sm.hist[wave]));
 
   uint32_t *bk = cand + (int64_t)tq * 2 * kCap;  // order keys
   uint32_t *bp = bk + kCap;                        // positions
@@ -255,7 +266,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
     __syncthreads();                // ... and every wave's; tile it-1's buffer is free
     const bool need = active && it * kTile <= t;
     const float v = score_and_prefetch(sm.keys[buf ^ 1], sm.ksc[buf ^ 1], sm.keys[buf], sm.ksc[buf], it + 1 < ntiles,
-                                       need, Q0, Q1, k8, ks, L, it + 1, wave, lane);
+                                       need, Q, k8, ks, L, it + 1, wave, lane);
     if (!need) continue;
     // score of key it*64 + lane
     const int s = it * kTile + lane;
