@@ -6,26 +6,31 @@
 // "How it works" (index score of each query against its preceding tokens,
 // then the top-k KV entries per query, k = 2048); m.digipub.cc, section 2.
 //
-// Workgroup = 8 wavefronts = 8 consecutive query tokens, one wave per token
-// with all 64 indexer heads in registers (4 MFMA A tiles), so every key
-// block read from LDS feeds four MFMAs.  Key tiles (64 keys x 128 B of E4M3 +
-// 64 fp32 scales) are loaded straight into LDS (direct-to-LDS loads, double
-// buffered, one barrier per tile) and shared by the eight waves.
+// Workgroup = 4 wavefronts = 4 consecutive query tokens, one wave per token
+// with all 64 indexer heads in registers (4 MFMA A tiles plus the tile of the
+// weighted query sum), so every key block read from LDS feeds five MFMAs.
+// Key tiles (64 keys x 128 B of E4M3 + 64 fp32 scales) are loaded straight
+// into LDS (direct-to-LDS loads, double buffered, one barrier per tile) and
+// shared by the four waves.
 //
-// Each wave owns its token's 4096-entry candidate buffer
-// (in the workspace: it stays in L2/MALL, and after the first few thousand
-// keys a key enters it only rarely; keeping it out of LDS lets two
-// workgroups share a CU) holding (order key, position) pairs in ascending
-// position order, plus a threshold tau:
+// Each wave owns its token's 4096-entry candidate buffer in the workspace
+// (in L2/MALL; after the first few thousand keys a key enters it only
+// rarely), holding (order key, position) pairs in ascending position order,
+// plus a threshold tau:
 //   * a key enters the buffer if its order key >= tau (keys arrive in
 //     increasing position, so a new key that ties tau outranks it);
-//   * when the buffer would overflow, it is compacted in place by histogram
-//     narrowing over the order keys.  The narrowing stops at the first level
-//     whose bin holding the k-th key is small enough: every entry at or above
-//     that bin's lower edge is kept and tau becomes the edge.  (Ties make the
-//     narrowing run down to single keys, where the cut is exact.)  The key
-//     range is tracked while appending, so a compaction is one histogram pass
-//     per level plus one compaction pass.
+//   * when a buffer could overflow on the next tile, it is compacted in place
+//     by histogram narrowing over the order keys.  The narrowing stops at the
+//     first level whose bin holding the k-th key is small enough: every entry
+//     at or above that bin's lower edge is kept and tau becomes the edge.
+//     (Ties make the narrowing run down to single keys, where the cut is
+//     exact.)  The key range is tracked while appending, so a compaction is
+//     one histogram pass per level plus one compaction pass, each reading the
+//     buffer 16 bytes per lane.
+//   * the four tokens see the same keys, so their buffers fill at nearly the
+//     same rate: when one wave must compact, every wave whose buffer is past
+//     a watermark compacts at the same tile, and the workgroup stalls once
+//     instead of once per wave.
 // At the end the buffer is compacted exactly to min(k, t+1) entries (score
 // desc, position desc) and written out in ascending position order.
 //
@@ -44,6 +49,7 @@ constexpr int kKSlots = kKRow / 16;
 constexpr int kKeyInsts = kTile * kKSlots / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
 constexpr int kBins = 256;      // compaction histogram
 static_assert(kBins * 4 >= kQueryScratch, "the histogram doubles as query scratch");
+static_assert(kWaves == 4, "the overflow flags of the four waves are read together");
 // An early cut may leave at most this many entries (k <= 2048), so that it
 // frees at least a quarter of the buffer; otherwise the narrowing continues.
 constexpr int kCutLimit = kCap - kCap / 4;
@@ -54,9 +60,17 @@ struct PrefillShared {
   uint8_t keys[2][kTile * kKRow];
   float ksc[2][kTile];
   uint32_t hist[kTok][kBins];
+  uint32_t full[2][kWaves];  // per tile parity: the wave's buffer could overflow on the next tile
 };
+// When any wave of the workgroup must compact, every wave whose buffer holds
+// more than this compacts at the same tile: the four tokens see the same keys,
+// so their buffers fill at nearly the same rate, and compactions that overlap
+// cost the workgroup one stall instead of four.
+constexpr int kSyncMark = kCap / 2 + kCap / 8;
 
-constexpr int kUnroll = 8;     // buffer chunks of 64 entries loaded together in a compaction pass
+constexpr int kVec = 4;    // consecutive buffer entries per lane and load (16 bytes)
+constexpr int kBatch = 4;  // key loads in flight per lane in a histogram pass (1024 entries)
+constexpr int kBatchC = 2; // key + position loads in flight per lane in the compaction pass
 
 // Compact the candidate buffer bk/bp[0..n) (order keys, positions; ascending
 // position order, which is preserved), all of whose keys lie in [lo, hi].
@@ -68,10 +82,16 @@ constexpr int kUnroll = 8;     // buffer chunks of 64 entries loaded together in
 //     of the bin that holds the keep-th key leaves at most `limit` entries, and
 //     keep every entry >= that edge (tau).  At least `keep` entries survive, all
 //     >= tau, so everything dropped (< tau) is outranked by `keep` survivors.
+// The buffer is read 16 bytes per lane (4 consecutive entries), 1024 entries
+// per batch of loads; it holds kCap entries, so the last group of 4 never
+// leaves it (entries past n are masked).
 __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict__ bp,
                                  uint32_t *__restrict__ hist, int &n, int keep, int limit, uint32_t lo,
                                  uint32_t hi, int lane) {
+  static_assert(kCap % (64 * kVec) == 0, "whole groups of 4 entries");
   __threadfence_block();  // the wave's earlier appends (other lanes) are visible
+  // lane-derived addresses are computed here, not kept live across the caller's loop
+  asm volatile("" : "+v"(lane));
   uint32_t base = lo;
   const uint32_t span = hi - lo;
   int shift = span == 0 ? 0 : max(0, 32 - __clz(span) - 8);
@@ -83,18 +103,22 @@ __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict
 #pragma unroll
     for (int b = lane; b < kBins; b += 64) hist[b] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int b0 = 0; b0 < n; b0 += 64 * kUnroll) {
-      uint32_t kk[kUnroll];
+    for (int b0 = 0; b0 < n; b0 += 64 * kVec * kBatch) {
+      uint4 kk[kBatch];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = b0 + 64 * u + lane;
-        kk[u] = i < n ? bk[i] : 0u;
+      for (int u = 0; u < kBatch; ++u) {
+        const int i0 = b0 + (u * 64 + lane) * kVec;
+        kk[u] = i0 < n ? *reinterpret_cast<const uint4 *>(bk + i0) : uint4{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = b0 + 64 * u + lane;
-        const uint32_t d = (kk[u] - base) >> shift;
-        if (i < n && kk[u] >= base && d < nbins) atomicAdd(&hist[d], 1u);
+      for (int u = 0; u < kBatch; ++u) {
+        const int i0 = b0 + (u * 64 + lane) * kVec;
+        const uint32_t k4[4] = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+          const uint32_t d = (k4[j] - base) >> shift;
+          if (i0 + j < n && k4[j] >= base && d < nbins) atomicAdd(&hist[d], 1u);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -140,34 +164,61 @@ __device__ uint32_t compact_wave(uint32_t *__restrict__ bk, uint32_t *__restrict
     shift = nshift;
   }
   // ordered in-place compaction: keep key > tau, and of the keys equal to tau
-  // all (early cut) or the last `remaining` (exact cut).  Entry i moves to
-  // dst <= i, below every entry not yet read.
+  // all (early cut) or the last `remaining` (exact cut).  A batch is loaded
+  // whole before any of it is written, and entry i moves to dst <= i, below
+  // every entry not yet read.
   const uint32_t tie_cut = exact_cut ? ties - remaining : 0u;
   uint32_t out = 0, tie_seen = 0;
-  for (int b0 = 0; b0 < n; b0 += 64 * kUnroll) {
-    uint32_t kk[kUnroll], pp[kUnroll];
+  for (int b0 = 0; b0 < n; b0 += 64 * kVec * kBatchC) {
+    uint4 kk[kBatchC], pp[kBatchC];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = b0 + 64 * u + lane;
-      kk[u] = i < n ? bk[i] : 0u;
-      pp[u] = i < n ? bp[i] : 0u;
+    for (int u = 0; u < kBatchC; ++u) {
+      const int i0 = b0 + (u * 64 + lane) * kVec;
+      kk[u] = i0 < n ? *reinterpret_cast<const uint4 *>(bk + i0) : uint4{0, 0, 0, 0};
+      pp[u] = i0 < n ? *reinterpret_cast<const uint4 *>(bp + i0) : uint4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = b0 + 64 * u + lane;
-      const bool in = i < n;
-      const bool tie = in && kk[u] == tau;
-      const uint64_t tmask = __ballot(tie);
-      const uint32_t my_tie = tie_seen + (uint32_t)lanes_below(tmask);
-      const bool kp = in && (kk[u] > tau || (tie && my_tie >= tie_cut));
-      const uint64_t kmask = __ballot(kp);
-      if (kp) {
-        const uint32_t dst = out + (uint32_t)lanes_below(kmask);
-        bk[dst] = kk[u];
-        bp[dst] = pp[u];
+    for (int u = 0; u < kBatchC; ++u) {
+      if (b0 + u * 64 * kVec >= n) break;  // uniform
+      const int i0 = b0 + (u * 64 + lane) * kVec;
+      const uint32_t k4[4] = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
+      const uint32_t p4[4] = {pp[u].x, pp[u].y, pp[u].z, pp[u].w};
+      // entry (lane l, j) is entry 4l + j of the group: the entries of lower
+      // lanes come first, then the lane's own lower j
+      bool kp[4];
+      if (exact_cut) {
+        uint64_t tm[4];
+        uint32_t rank = tie_seen;
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+          tm[j] = __ballot(i0 + j < n && k4[j] == tau);
+          rank += (uint32_t)lanes_below(tm[j]);
+          tie_seen += (uint32_t)__popcll(tm[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+          const bool tie = (tm[j] >> lane) & 1u;
+          kp[j] = i0 + j < n && (k4[j] > tau || (tie && rank >= tie_cut));
+          rank += tie ? 1u : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) kp[j] = i0 + j < n && k4[j] >= tau;
       }
-      out += (uint32_t)__popcll(kmask);
-      tie_seen += (uint32_t)__popcll(tmask);
+      uint32_t dst = out;
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const uint64_t km = __ballot(kp[j]);
+        dst += (uint32_t)lanes_below(km);
+        out += (uint32_t)__popcll(km);
+      }
+#pragma unroll
+      for (int j = 0; j < kVec; ++j)
+        if (kp[j]) {
+          bk[dst] = k4[j];
+          bp[dst] = p4[j];
+          ++dst;
+        }
     }
   }
   __threadfence_block();  // the moved entries are visible to every lane
@@ -264,32 +315,34 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
     const int buf = it & 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed in LDS
     __syncthreads();                // ... and every wave's; tile it-1's buffer is free
+    if (it > 0) {
+      const int par = (it - 1) & 1;
+      const uint32_t any = __builtin_amdgcn_readfirstlane(sm.full[par][0] | sm.full[par][1] | sm.full[par][2] |
+                                                          sm.full[par][3]);
+      if (any != 0u && nbuf > kSyncMark) {
+        thr = compact_wave(bk, bp, hist, nbuf, k, kCutLimit, wave_min_u32(klo), wave_max_u32(khi), lane);
+        klo = thr;  // every survivor is >= tau
+      }
+    }
     const bool need = active && it * kTile <= t;
     const float v = score_and_prefetch(sm.keys[buf ^ 1], sm.ksc[buf ^ 1], sm.keys[buf], sm.ksc[buf], it + 1 < ntiles,
                                        need, Q, k8, ks, L, it + 1, wave, lane);
-    if (!need) continue;
-    // score of key it*64 + lane
-    const int s = it * kTile + lane;
-    const uint32_t key = score_key(v);
-    const bool valid = s <= t;
-    bool pass = valid && key >= thr;
-    uint64_t mask = __ballot(pass);
-    int cnt = __popcll(mask);
-    if (nbuf + cnt > kCap) {
-      thr = compact_wave(bk, bp, hist, nbuf, k, kCutLimit, wave_min_u32(klo), wave_max_u32(khi), lane);
-      klo = thr;  // every survivor is >= tau
-      pass = valid && key >= thr;
-      mask = __ballot(pass);
-      cnt = __popcll(mask);
+    if (need) {
+      // score of key it*64 + lane; the buffer has room for the whole tile
+      const int s = it * kTile + lane;
+      const uint32_t key = score_key(v);
+      const bool pass = s <= t && key >= thr;
+      const uint64_t mask = __ballot(pass);
+      if (pass) {
+        klo = min(klo, key);
+        khi = max(khi, key);
+        const int dst = nbuf + lanes_below(mask);
+        bk[dst] = key;
+        bp[dst] = (uint32_t)s;
+      }
+      nbuf += __popcll(mask);
     }
-    if (pass) {
-      klo = min(klo, key);
-      khi = max(khi, key);
-      const int dst = nbuf + lanes_below(mask);
-      bk[dst] = key;
-      bp[dst] = (uint32_t)s;
-    }
-    nbuf += cnt;
+    if (lane == 0) sm.full[it & 1][wave] = nbuf > kCap - kTile ? 1u : 0u;
   }
 
   if (!active) return;
