@@ -120,6 +120,9 @@ dsa_status dsa_topk_select(const float *scores, int64_t ld_scores, const int32_t
  * Limits: BF16 needs H a multiple of 16; F32 needs H <= 128; k <= 2048.
  * workspace (optional) lets the kernel split long selections across more
  * workgroups when T is small; size it with dsa_sparse_mla_workspace_bytes().
+ * Each split's output is then held in bf16, normalised by its own softmax
+ * sum, and merged by LSE weighting in fp32 (one extra bf16 rounding).  The
+ * workspace needs no initialisation; calls that share one must not overlap.
  */
 size_t dsa_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t k);
 dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const int32_t *idx,

@@ -199,7 +199,7 @@ __device__ __forceinline__ void wait_all_but_newest_tile(int wave) {
 template <int NW, bool fixed>
 __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18], float &m_ref, float scale_log2,
                                          int64_t t, int H, int hw0, __bf16 *__restrict__ out,
-                                         float *__restrict__ lse, int splits, int sp, float *__restrict__ part_o,
+                                         float *__restrict__ lse, int splits, int sp, __bf16 *__restrict__ part_o,
                                          float *__restrict__ part_ml) {
   constexpr int MT = 32 / NW;  // value-dim tiles of 16 per wave
   const int g = cx.g, c = cx.c, wave = cx.wave;
@@ -307,15 +307,13 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int dv = (wave * MT + i) * 16 + 4 * g;
-      if (splits == 1) {
-        const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-        bf16x4 v;
+      // the output, or this split's partial output, normalised by its own sum
+      __bf16 *dst = splits == 1 ? out + (t * H + head) * 512 : part_o + ((t * splits + sp) * H + head) * 512;
+      const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+      bf16x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[i][n][r] * inv);
-        *reinterpret_cast<bf16x4 *>(out + (t * H + head) * 512 + dv) = v;
-      } else {
-        *reinterpret_cast<f32x4 *>(part_o + ((t * splits + sp) * H + head) * 512 + dv) = o[i][n];
-      }
+      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[i][n][r] * inv);
+      *reinterpret_cast<bf16x4 *>(dst + dv) = v;
     }
   }
   return true;
@@ -375,11 +373,10 @@ __device__ __forceinline__ void load_qt(bf16x8 (&qr)[18], const __bf16 *__restri
 // The first output element of a work item doubles as its "redo" mark: an
 // all-ones (NaN) pattern written when the item's first pass was discarded.
 // Every completed item overwrites it with its result.
-__device__ __forceinline__ uint32_t *redo_mark_f32(float *part_o, int64_t t, int splits, int sp, int H, int hw0) {
-  return reinterpret_cast<uint32_t *>(part_o + ((t * splits + sp) * H + hw0) * 512);
-}
-__device__ __forceinline__ uint16_t *redo_mark_bf16(__bf16 *out, int64_t t, int H, int hw0) {
-  return reinterpret_cast<uint16_t *>(out + (t * H + hw0) * 512);
+__device__ __forceinline__ uint16_t *redo_mark(__bf16 *out, __bf16 *part_o, int64_t t, int splits, int sp, int H,
+                                               int hw0) {
+  return reinterpret_cast<uint16_t *>(splits == 1 ? out + (t * H + hw0) * 512
+                                                  : part_o + ((t * splits + sp) * H + hw0) * 512);
 }
 
 // NW waves: 16*NW heads per workgroup; for the logits wave w owns 16 heads,
@@ -396,8 +393,8 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ bt, int max_blocks, int64_t N, int T, int H, int k, float scale_log2,
-    __bf16 *__restrict__ out, float *__restrict__ lse, int splits, float *__restrict__ part_o,
-    float *__restrict__ part_ml) {
+    __bf16 *__restrict__ out, float *__restrict__ lse, int splits, __bf16 *__restrict__ part_o,
+    float *__restrict__ part_ml, int *__restrict__ redo_any) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   MlaCtx cx;
   cx.kv = kv;
@@ -408,10 +405,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
   if (mla_pass<NW, false>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o, part_ml))
     return;
   if (threadIdx.x == 0) {
-    if (splits == 1)
-      *redo_mark_bf16(out, it.t, H, it.hw0) = 0xFFFFu;
-    else
-      *redo_mark_f32(part_o, it.t, splits, it.sp, H, it.hw0) = 0xFFFFFFFFu;
+    *redo_mark(out, part_o, it.t, splits, it.sp, H, it.hw0) = 0xFFFFu;
+    if (redo_any) *redo_any = 1;  // the redo kernel has work
   }
 }
 
@@ -422,12 +417,15 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_redo_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ bt, int max_blocks, int64_t N, int T, int H, int k, float scale_log2,
-    __bf16 *__restrict__ out, float *__restrict__ lse, int splits, float *__restrict__ part_o,
-    float *__restrict__ part_ml, int64_t nitems) {
+    __bf16 *__restrict__ out, float *__restrict__ lse, int splits, __bf16 *__restrict__ part_o,
+    float *__restrict__ part_ml, const int *__restrict__ redo_any, int64_t nitems) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   __shared__ int64_t todo[NW * 64];
   __shared__ int ntodo;
   const int tid = threadIdx.x;
+  // with a split workspace, the main kernel raises redo_any with any mark
+  // (the combine clears it); a nonzero value only costs the scan
+  if (redo_any && *redo_any == 0) return;
   const int n_hg = H / (16 * NW);
   for (int64_t base = (int64_t)blockIdx.x * (NW * 64); base < nitems; base += (int64_t)gridDim.x * (NW * 64)) {
     if (tid == 0) ntodo = 0;
@@ -438,8 +436,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_redo_kernel(
       const int64_t rest = wid / splits;
       const int hw0 = (int)(rest % n_hg) * NW * 16;
       const int64_t t = rest / n_hg;
-      const bool marked = splits == 1 ? *redo_mark_bf16(out, t, H, hw0) == 0xFFFFu
-                                      : *redo_mark_f32(part_o, t, splits, sp, H, hw0) == 0xFFFFFFFFu;
+      const bool marked = *redo_mark(out, part_o, t, splits, sp, H, hw0) == 0xFFFFu;
       if (marked) todo[atomicAdd(&ntodo, 1)] = wid;
     }
     __syncthreads();
@@ -464,33 +461,49 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_redo_kernel(
 }
 
 // LSE-weighted combine of split partials.  grid (T*H/4), block 256: 4 heads,
-// 64 threads per head, 8 value dims per thread.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restrict__ part_o,
+// 64 threads per head, 8 value dims per thread.  Split s left its output
+// normalised by its own sum l_s, with reference m_s:
+//     out = sum_s w_s l_s P_s / sum_s w_s l_s,   w_s = 2^(m_s - max m).
+// Lane s < splits reads the (m_s, l_s) pair; the partials of up to eight
+// splits are requested together before any is used.  Block 0 clears the redo
+// flag for the next call (the redo kernel ran before this one).
+constexpr int kCombineBatch = 8;
+__global__ __launch_bounds__(256) void mla_combine_kernel(const __bf16 *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int T, int H,
                                                           int splits, __bf16 *__restrict__ out,
-                                                          float *__restrict__ lse) {
+                                                          float *__restrict__ lse, int *__restrict__ redo_any) {
+  if (blockIdx.x == 0 && threadIdx.x == 0 && redo_any) *redo_any = 0;
   const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (th >= (int64_t)T * H) return;
+  if (th >= (int64_t)T * H) return;  // uniform per wave
   const int lane = threadIdx.x & 63;
   const int64_t t = th / H;
   const int h = (int)(th % H);
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((t * splits + s) * H + h) * 2]);
-  float Lsum = 0.0f;
+  float ms = -INFINITY, ls = 0.0f;
+  if (lane < splits) {
+    const float *pm = part_ml + ((t * splits + lane) * H + h) * 2;
+    ms = pm[0];
+    ls = pm[1];
+  }
+  const float M = wave_max(ms);
+  // weight of split `lane` times its sum (0 for empty splits)
+  const float wl = ms == -INFINITY ? 0.0f : exp2f(ms - M) * ls;
+  const float Lsum = wave_sum(wl);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const float *pm = part_ml + ((t * splits + s) * H + h) * 2;
-    const float ms = pm[0], ls = pm[1];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
-    Lsum += wgt * ls;
-    const float *po = part_o + ((t * splits + s) * H + h) * 512 + lane * 8;
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(po);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(po + 4);
+  for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
+    bf16x8 pv[kCombineBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] += wgt * a[i];
-      acc[4 + i] += wgt * b[i];
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (s0 + u < splits)
+        pv[u] = *reinterpret_cast<const bf16x8 *>(part_o + ((t * splits + s0 + u) * H + h) * 512 + lane * 8);
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      if (s0 + u < splits) {
+        const float wgt = __shfl(wl, s0 + u);
+        if (wgt != 0.0f) {  // empty splits hold no partial
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, (float)pv[u][i], acc[i]);
+        }
+      }
     }
   }
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
@@ -566,7 +579,7 @@ __global__ __launch_bounds__(256) void sparse_mla_f32_kernel(const float *__rest
 template <int NW>
 hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, const int32_t *bt,
                           int max_blocks, int64_t N, int T, int H, int k, float scale_log2, void *out, float *lse,
-                          int splits, float *part_o, float *part_ml, hipStream_t s) {
+                          int splits, __bf16 *part_o, float *part_ml, int *redo_any, hipStream_t s) {
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void *)sparse_mla_bf16_kernel<NW>,
@@ -580,7 +593,7 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
   const int64_t items = (int64_t)T * (H / (16 * NW)) * splits;
   hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW>), dim3((uint32_t)items), dim3(NW * 64), kSmemMla, s,
                      (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
-                     (__bf16 *)out, lse, splits, part_o, part_ml);
+                     (__bf16 *)out, lse, splits, part_o, part_ml, redo_any);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
@@ -588,7 +601,7 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
   const int64_t grid = std::min<int64_t>(cus, (items + NW * 64 - 1) / (NW * 64));
   hipLaunchKernelGGL((sparse_mla_bf16_redo_kernel<NW>), dim3((uint32_t)grid), dim3(NW * 64), kSmemMla, s,
                      (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
-                     (__bf16 *)out, lse, splits, part_o, part_ml, items);
+                     (__bf16 *)out, lse, splits, part_o, part_ml, redo_any, items);
   return hipGetLastError();
 }
 
@@ -598,26 +611,27 @@ namespace dsa {
 hipError_t launch_sparse_mla_bf16(const void *q, const void *kv, const int32_t *idx,
                                   const int32_t *block_table, int32_t max_blocks, int64_t N, int32_t T,
                                   int32_t H, int32_t k, float sm_scale, void *out, float *lse,
-                                  int32_t splits, float *part_o, float *part_ml, hipStream_t s) {
+                                  int32_t splits, void *part_o_v, float *part_ml, int *redo_any, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  __bf16 *part_o = (__bf16 *)part_o_v;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   hipError_t e;
   if (H % 128 == 0)
     e = launch_bf16_nw<8>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, s);
+                          part_o, part_ml, redo_any, s);
   else if (H % 64 == 0)
     e = launch_bf16_nw<4>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, s);
+                          part_o, part_ml, redo_any, s);
   else if (H % 32 == 0)
     e = launch_bf16_nw<2>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, s);
+                          part_o, part_ml, redo_any, s);
   else
     e = launch_bf16_nw<1>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, s);
+                          part_o, part_ml, redo_any, s);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t th = (int64_t)T * H;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((uint32_t)((th + 3) / 4)), dim3(256), 0, s, part_o, part_ml, T,
-                     H, splits, (__bf16 *)out, lse);
+                     H, splits, (__bf16 *)out, lse, redo_any);
   return hipGetLastError();
 }
 
