@@ -39,21 +39,18 @@ static int mla_splits(int64_t T, int H, int k) {
   return s < 1 ? 1 : s;
 }
 // Split workspace: bf16 partial outputs [T][splits][H][512] (each normalised
-// by its own softmax sum), fp32 (reference, sum) pairs [T][splits][H][2], and
-// one int that tells the redo kernel whether any work item was marked.
+// by its own softmax sum), then fp32 (reference, sum) pairs [T][splits][H][2].
 static size_t mla_ws_bytes(int64_t T, int H, int k) {
   const int s = mla_splits(T, H, k);
   if (s <= 1) return 0;
-  return align_up((size_t)T * s * H * 512 * 2, 256) + align_up((size_t)T * s * H * 2 * 4, 256) + 256;
+  return align_up((size_t)T * s * H * 512 * 2, 256) + align_up((size_t)T * s * H * 2 * 4, 256);
 }
-static void mla_ws_split(void *ws, int64_t T, int H, int k, void **po, float **pml, int **redo_any) {
+static void mla_ws_split(void *ws, int64_t T, int H, int k, void **po, float **pml) {
   const int s = mla_splits(T, H, k);
   char *p = (char *)ws;
   *po = p;
   p += align_up((size_t)T * s * H * 512 * 2, 256);
   *pml = (float *)p;
-  p += align_up((size_t)T * s * H * 2 * 4, 256);
-  *redo_any = (int *)p;
 }
 }  // namespace dsa
 
@@ -144,15 +141,14 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
     int splits = 1;
     void *po = nullptr;
     float *pml = nullptr;
-    int *redo_any = nullptr;
     if (workspace && need > 0) {
       REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu", workspace_bytes,
               need);
       splits = mla_splits(T, H, k);
-      mla_ws_split(workspace, T, H, k, &po, &pml, &redo_any);
+      mla_ws_split(workspace, T, H, k, &po, &pml);
     }
     return hip_check(launch_sparse_mla_bf16(q, kv, idx, nullptr, 0, N, T, H, k, sm_scale, out, lse, splits,
-                                            po, pml, redo_any, stream),
+                                            po, pml, stream),
                      "sparse mla launch");
   }
   if (dt == DSA_F32) {
@@ -244,7 +240,7 @@ dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t worksp
   if (st != DSA_OK) return st;
   if (a->attn_dt == DSA_BF16)
     return hip_check(launch_sparse_mla_bf16(a->q, a->kv, a->idx, nullptr, 0, L, L, a->H, a->k, a->sm_scale,
-                                            a->out, a->lse, 1, nullptr, nullptr, nullptr, stream),
+                                            a->out, a->lse, 1, nullptr, nullptr, stream),
                      "sparse mla launch");
   return hip_check(launch_sparse_mla_f32((const float *)a->q, (const float *)a->kv, a->idx, L, L, a->H, a->k,
                                          a->sm_scale, (float *)a->out, a->lse, stream),
@@ -316,14 +312,13 @@ dsa_status dsa_sparse_mla_paged_fwd(const void *q, const void *kv_pool, int64_t 
   int splits = 1;
   void *po = nullptr;
     float *pml = nullptr;
-    int *redo_any = nullptr;
   if (workspace && need > 0) {
     REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu", workspace_bytes, need);
     splits = mla_splits(T, H, k);
-    mla_ws_split(workspace, T, H, k, &po, &pml, &redo_any);
+    mla_ws_split(workspace, T, H, k, &po, &pml);
   }
   return hip_check(launch_sparse_mla_bf16(q, kv_pool, idx, block_table, max_blocks, n_pool_rows, T, H, k,
-                                          sm_scale, out, lse, splits, po, pml, redo_any, stream),
+                                          sm_scale, out, lse, splits, po, pml, stream),
                    "sparse mla launch");
 }
 
@@ -346,9 +341,8 @@ dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspac
   }
   void *po = nullptr;
     float *pml = nullptr;
-    int *redo_any = nullptr;
   const int splits = mla_splits(a->B, a->H, a->k);
-  if (splits > 1) mla_ws_split(p, a->B, a->H, a->k, &po, &pml, &redo_any);
+  if (splits > 1) mla_ws_split(p, a->B, a->H, a->k, &po, &pml);
   st = hip_check(launch_decode_indexer(a->q8, a->q_scale, a->w, a->k8_pool, a->ks_pool, a->block_table,
                                        a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores, ld,
                                        stream),
@@ -357,8 +351,7 @@ dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspac
   st = hip_check(launch_topk(scores, ld, a->ctx_len, a->max_ctx, a->B, a->k, idx, stream), "topk launch");
   if (st != DSA_OK) return st;
   return hip_check(launch_sparse_mla_bf16(a->q, a->kv_pool, idx, a->block_table, a->max_blocks, a->n_pool_rows,
-                                          a->B, a->H, a->k, a->sm_scale, a->out, a->lse, splits, po, pml, redo_any,
-                                          stream),
+                                          a->B, a->H, a->k, a->sm_scale, a->out, a->lse, splits, po, pml, stream),
                    "sparse mla launch");
 }
 

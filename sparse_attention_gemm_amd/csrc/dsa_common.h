@@ -107,7 +107,7 @@ hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const
 hipError_t launch_sparse_mla_bf16(const void *q, const void *kv, const int32_t *idx,
                                   const int32_t *block_table, int32_t max_blocks, int64_t N, int32_t T,
                                   int32_t H, int32_t k, float sm_scale, void *out, float *lse,
-                                  int32_t splits, void *part_o, float *part_ml, int *redo_any, hipStream_t s);
+                                  int32_t splits, void *part_o, float *part_ml, hipStream_t s);
 hipError_t launch_sparse_mla_f32(const float *q, const float *kv, const int32_t *idx, int64_t N, int32_t T,
                                  int32_t H, int32_t k, float sm_scale, float *out, float *lse,
                                  hipStream_t s);

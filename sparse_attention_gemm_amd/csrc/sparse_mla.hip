@@ -329,7 +329,8 @@ struct MlaItem {
 };
 
 template <int NW>
-__device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, uint8_t *smem_raw, int64_t wid, const int32_t *__restrict__ idx,
+__device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, bf16x8 (&qr)[18], const __bf16 *__restrict__ q,
+                                             uint8_t *smem_raw, int64_t wid, const int32_t *__restrict__ idx,
                                              const int32_t *__restrict__ bt, int max_blocks, int64_t N, int H, int k,
                                              int splits) {
   cx.tiles = smem_raw;
@@ -354,6 +355,10 @@ __device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, uint8_t *smem_raw, int6
   const int per = (ntiles + splits - 1) / splits;
   cx.tb = it.sp * per;
   cx.te = min(ntiles, cx.tb + per);
+  // Q^T first: its loads are in flight while the rows are resolved
+  const __bf16 *qrow = q + (it.t * H + it.hw0 + 16 * cx.wave + cx.c) * 576 + cx.g * 8;
+#pragma unroll
+  for (int s = 0; s < 18; ++s) qr[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
   const int32_t *irow = idx + it.t * k;
   // physical rows of this workgroup's entries [tb*32, te*32)
   for (int e = tid; e < (cx.te - cx.tb) * kBN; e += NW * 64)
@@ -363,20 +368,28 @@ __device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, uint8_t *smem_raw, int6
   return it;
 }
 
-__device__ __forceinline__ void load_qt(bf16x8 (&qr)[18], const __bf16 *__restrict__ q, int64_t t, int H, int hw0,
-                                        const MlaCtx &cx) {
-  const __bf16 *qrow = q + (t * H + hw0 + 16 * cx.wave + cx.c) * 576 + cx.g * 8;
-#pragma unroll
-  for (int s = 0; s < 18; ++s) qr[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
-}
-
-// The first output element of a work item doubles as its "redo" mark: an
-// all-ones (NaN) pattern written when the item's first pass was discarded.
-// Every completed item overwrites it with its result.
-__device__ __forceinline__ uint16_t *redo_mark(__bf16 *out, __bf16 *part_o, int64_t t, int splits, int sp, int H,
-                                               int hw0) {
-  return reinterpret_cast<uint16_t *>(splits == 1 ? out + (t * H + hw0) * 512
-                                                  : part_o + ((t * splits + sp) * H + hw0) * 512);
+// Recomputes work item `wid` with exact per-head maxima: one logits-only
+// pass for the maxima, then the accumulation pass with those references.
+// Out of line: it only runs when the first pass was discarded (rare), and
+// keeps its registers out of the main pass.
+template <int NW>
+__device__ __noinline__ void mla_redo_item(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
+                                           const int32_t *__restrict__ idx, const int32_t *__restrict__ bt,
+                                           int max_blocks, int64_t N, int H, int k, float scale_log2,
+                                           __bf16 *__restrict__ out, float *__restrict__ lse, int splits,
+                                           __bf16 *__restrict__ part_o, float *__restrict__ part_ml, int64_t wid) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  MlaCtx cx;
+  cx.kv = kv;
+  bf16x8 qr[18];
+  const MlaItem it = mla_setup<NW>(cx, qr, q, smem_raw, wid, idx, bt, max_blocks, N, H, k, splits);
+  float m_ref = -INFINITY;
+  for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
+    float x[8];
+    tile_logits(ct, rv, qr, scale_log2, cx.g, cx.c, x);
+    m_ref = fmaxf(m_ref, tile_max(x, scale_log2));
+  });
+  mla_pass<NW, true>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o, part_ml);
 }
 
 // NW waves: 16*NW heads per workgroup; for the logits wave w owns 16 heads,
@@ -387,77 +400,23 @@ __device__ __forceinline__ uint16_t *redo_mark(__bf16 *out, __bf16 *part_o, int6
 // entry, and then stays fixed, so the accumulators are only ever written by
 // MFMAs.  Probabilities are exp2(x - m_ref); while x <= m_ref + 64 they stay
 // below 2^64, far inside the fp32/bf16 range, and the result is the same
-// softmax.  If any tile overshoots that, the workgroup writes its redo mark
-// instead and sparse_mla_bf16_redo_kernel recomputes it with exact maxima.
+// softmax.  If any tile overshoots that, the pass is discarded and the
+// workgroup recomputes the item with exact maxima (mla_redo_item).
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ bt, int max_blocks, int64_t N, int T, int H, int k, float scale_log2,
     __bf16 *__restrict__ out, float *__restrict__ lse, int splits, __bf16 *__restrict__ part_o,
-    float *__restrict__ part_ml, int *__restrict__ redo_any) {
+    float *__restrict__ part_ml) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   MlaCtx cx;
   cx.kv = kv;
-  const MlaItem it = mla_setup<NW>(cx, smem_raw, blockIdx.x, idx, bt, max_blocks, N, H, k, splits);
   bf16x8 qr[18];
-  load_qt(qr, q, it.t, H, it.hw0, cx);
+  const MlaItem it = mla_setup<NW>(cx, qr, q, smem_raw, blockIdx.x, idx, bt, max_blocks, N, H, k, splits);
   float m_ref = -INFINITY;
   if (mla_pass<NW, false>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o, part_ml))
     return;
-  if (threadIdx.x == 0) {
-    *redo_mark(out, part_o, it.t, splits, it.sp, H, it.hw0) = 0xFFFFu;
-    if (redo_any) *redo_any = 1;  // the redo kernel has work
-  }
-}
-
-// Recomputes, with exact per-head maxima, the work items whose redo mark is
-// set.  One workgroup per CU walks the items in strides; it reads one mark
-// per item and exits when none is set (the overshoot is rare).
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_redo_kernel(
-    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ bt, int max_blocks, int64_t N, int T, int H, int k, float scale_log2,
-    __bf16 *__restrict__ out, float *__restrict__ lse, int splits, __bf16 *__restrict__ part_o,
-    float *__restrict__ part_ml, const int *__restrict__ redo_any, int64_t nitems) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  __shared__ int64_t todo[NW * 64];
-  __shared__ int ntodo;
-  const int tid = threadIdx.x;
-  // with a split workspace, the main kernel raises redo_any with any mark
-  // (the combine clears it); a nonzero value only costs the scan
-  if (redo_any && *redo_any == 0) return;
-  const int n_hg = H / (16 * NW);
-  for (int64_t base = (int64_t)blockIdx.x * (NW * 64); base < nitems; base += (int64_t)gridDim.x * (NW * 64)) {
-    if (tid == 0) ntodo = 0;
-    __syncthreads();
-    const int64_t wid = base + tid;
-    if (wid < nitems) {
-      const int sp = (int)(wid % splits);
-      const int64_t rest = wid / splits;
-      const int hw0 = (int)(rest % n_hg) * NW * 16;
-      const int64_t t = rest / n_hg;
-      const bool marked = *redo_mark(out, part_o, t, splits, sp, H, hw0) == 0xFFFFu;
-      if (marked) todo[atomicAdd(&ntodo, 1)] = wid;
-    }
-    __syncthreads();
-    const int n = ntodo;
-    for (int i = 0; i < n; ++i) {
-      const int64_t w = todo[i];
-      MlaCtx cx;
-      cx.kv = kv;
-      const MlaItem it = mla_setup<NW>(cx, smem_raw, w, idx, bt, max_blocks, N, H, k, splits);
-      bf16x8 qr[18];
-      load_qt(qr, q, it.t, H, it.hw0, cx);
-      float m_ref = -INFINITY;
-      for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
-        float x[8];
-        tile_logits(ct, rv, qr, scale_log2, cx.g, cx.c, x);
-        m_ref = fmaxf(m_ref, tile_max(x, scale_log2));
-      });
-      mla_pass<NW, true>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o, part_ml);
-    }
-    __syncthreads();
-  }
+  mla_redo_item<NW>(q, kv, idx, bt, max_blocks, N, H, k, scale_log2, out, lse, splits, part_o, part_ml, blockIdx.x);
 }
 
 // LSE-weighted combine of split partials.  grid (T*H/4), block 256: 4 heads,
@@ -465,14 +424,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_redo_kernel(
 // normalised by its own sum l_s, with reference m_s:
 //     out = sum_s w_s l_s P_s / sum_s w_s l_s,   w_s = 2^(m_s - max m).
 // Lane s < splits reads the (m_s, l_s) pair; the partials of up to eight
-// splits are requested together before any is used.  Block 0 clears the redo
-// flag for the next call (the redo kernel ran before this one).
+// splits are requested together before any is used.
 constexpr int kCombineBatch = 8;
 __global__ __launch_bounds__(256) void mla_combine_kernel(const __bf16 *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int T, int H,
                                                           int splits, __bf16 *__restrict__ out,
-                                                          float *__restrict__ lse, int *__restrict__ redo_any) {
-  if (blockIdx.x == 0 && threadIdx.x == 0 && redo_any) *redo_any = 0;
+                                                          float *__restrict__ lse) {
   const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (th >= (int64_t)T * H) return;  // uniform per wave
   const int lane = threadIdx.x & 63;
@@ -579,29 +536,18 @@ __global__ __launch_bounds__(256) void sparse_mla_f32_kernel(const float *__rest
 template <int NW>
 hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, const int32_t *bt,
                           int max_blocks, int64_t N, int T, int H, int k, float scale_log2, void *out, float *lse,
-                          int splits, __bf16 *part_o, float *part_ml, int *redo_any, hipStream_t s) {
+                          int splits, __bf16 *part_o, float *part_ml, hipStream_t s) {
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void *)sparse_mla_bf16_kernel<NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemMla);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)sparse_mla_bf16_redo_kernel<NW>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kSmemMla);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   const int64_t items = (int64_t)T * (H / (16 * NW)) * splits;
   hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW>), dim3((uint32_t)items), dim3(NW * 64), kSmemMla, s,
                      (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
-                     (__bf16 *)out, lse, splits, part_o, part_ml, redo_any);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int64_t grid = std::min<int64_t>(cus, (items + NW * 64 - 1) / (NW * 64));
-  hipLaunchKernelGGL((sparse_mla_bf16_redo_kernel<NW>), dim3((uint32_t)grid), dim3(NW * 64), kSmemMla, s,
-                     (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
-                     (__bf16 *)out, lse, splits, part_o, part_ml, redo_any, items);
+                     (__bf16 *)out, lse, splits, part_o, part_ml);
   return hipGetLastError();
 }
 
@@ -611,27 +557,27 @@ namespace dsa {
 hipError_t launch_sparse_mla_bf16(const void *q, const void *kv, const int32_t *idx,
                                   const int32_t *block_table, int32_t max_blocks, int64_t N, int32_t T,
                                   int32_t H, int32_t k, float sm_scale, void *out, float *lse,
-                                  int32_t splits, void *part_o_v, float *part_ml, int *redo_any, hipStream_t s) {
+                                  int32_t splits, void *part_o_v, float *part_ml, hipStream_t s) {
   if (T == 0) return hipSuccess;
   __bf16 *part_o = (__bf16 *)part_o_v;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   hipError_t e;
   if (H % 128 == 0)
     e = launch_bf16_nw<8>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, redo_any, s);
+                          part_o, part_ml, s);
   else if (H % 64 == 0)
     e = launch_bf16_nw<4>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, redo_any, s);
+                          part_o, part_ml, s);
   else if (H % 32 == 0)
     e = launch_bf16_nw<2>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, redo_any, s);
+                          part_o, part_ml, s);
   else
     e = launch_bf16_nw<1>(q, kv, idx, block_table, max_blocks, N, T, H, k, scale_log2, out, lse, splits,
-                          part_o, part_ml, redo_any, s);
+                          part_o, part_ml, s);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t th = (int64_t)T * H;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((uint32_t)((th + 3) / 4)), dim3(256), 0, s, part_o, part_ml, T,
-                     H, splits, (__bf16 *)out, lse, redo_any);
+                     H, splits, (__bf16 *)out, lse);
   return hipGetLastError();
 }
 
