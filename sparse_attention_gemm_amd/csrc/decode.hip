@@ -36,40 +36,39 @@ __global__ __launch_bounds__(kWavesD * 64) void decode_indexer_kernel(
   const int np = min(kPagesPerWave, npages - p0);  // pages of this wave
   if (np <= 0) return;
   float *srow = scores + b * ld;
-  // physical first row of page p0 + j, or -1 when unmapped
+  // the wave's block-table entries, one per lane, requested before the query
+  // set-up so that their latency overlaps it
+  const int32_t blk_l = lane < np ? bt[b * max_blocks + p0 + lane] : -1;
+  IdxQuery<4> Q;
+  idx_load_query<4>(Q, q8 + b * 64 * 128, w + b * 64, qs[b], lane, qscratch[wave]);
+  // physical first row of page p0 + j (j uniform), or -1 when unmapped
   auto page_row = [&](int j) -> int64_t {
-    const int32_t blk = bt[b * max_blocks + p0 + j];
+    const int32_t blk = __builtin_amdgcn_readlane(blk_l, j);
     const int64_t prow = (int64_t)blk * 64;
     return (blk < 0 || prow + 64 > n_pool_rows) ? -1 : prow;
   };
-  IdxQuery<4> Q;
-  idx_load_query<4>(Q, q8 + b * 64 * 128, w + b * 64, qs[b], lane, qscratch[wave]);
+  // Page loads are unconditional (an unmapped or missing page reads row 0 of
+  // the pool and is discarded): with no branch around them the compiler can
+  // wait for exactly the loads a key block needs, leaving the next page's
+  // loads in flight.
   i32x8 kb[2][4];
   float kscale[2];
+  auto load_page = [&](int buf, int64_t prow) {
+    const int64_t r = prow < 0 ? 0 : prow;
+    idx_load_keys(kb[buf], k8_pool + r * 128, 128, lane);
+    kscale[buf] = ks_pool[r + lane];
+  };
   int64_t prow = page_row(0);
-  if (prow >= 0) {
-    idx_load_keys(kb[0], k8_pool + prow * 128, 128, lane);
-    kscale[0] = ks_pool[prow + lane];
-  }
+  load_page(0, prow);
 #pragma unroll
   for (int j = 0; j < kPagesPerWave; ++j) {
     if (j >= np) break;  // uniform
     const int cur = j & 1;
-    int64_t next = -1;
-    if (j + 1 < np) {
-      next = page_row(j + 1);
-      if (next >= 0) {
-        idx_load_keys(kb[cur ^ 1], k8_pool + next * 128, 128, lane);
-        kscale[cur ^ 1] = ks_pool[next + lane];
-      }
-    }
+    const int64_t next = j + 1 < np ? page_row(j + 1) : -1;
+    if (j + 1 < kPagesPerWave) load_page(cur ^ 1, next);
     const int s = (p0 + j) * 64 + lane;
-    if (prow >= 0) {
-      const float tot = idx_score64<4>(Q, kb[cur]);
-      if (s < ctx) srow[s] = canon_zero(tot * kscale[cur]);
-    } else if (s < ctx) {
-      srow[s] = -INFINITY;  // unmapped page: nothing to score
-    }
+    const float tot = idx_score64<4>(Q, kb[cur]);
+    if (s < ctx) srow[s] = prow >= 0 ? canon_zero(tot * kscale[cur]) : -INFINITY;  // unmapped page: nothing to score
     prow = next;
   }
 }
