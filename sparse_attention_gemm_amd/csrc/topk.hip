@@ -26,13 +26,14 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCand = 18432;  // candidates held in LDS
-constexpr int kU = 4;         // groups of 4 row elements per thread in flight
+constexpr int kU = 8;         // groups of 4 row elements per thread in flight (32768 elements)
 
 struct TopkShared {
   uint32_t hist[kBins];
   uint32_t ckey[kCand];
   int32_t cpos[kCand];
   uint32_t wred[2][kWaves];
+  uint32_t upre[kU][kWaves];  // pass 2: exclusive offsets of (group u, wave) in position order
   uint32_t bstar, above, bcnt;
 };
 constexpr size_t kTopkSmem = sizeof(TopkShared);
@@ -243,23 +244,55 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
       return;
     }
   }
-  // ---- pass 2: candidates (key >= edge) into LDS, in position order
+  // ---- pass 2: candidates (key >= edge) into LDS, in position order.  The
+  // element order within a batch is (group u, thread); the offsets of all kU
+  // groups come from one set of wave scans and one 128-entry scan.
   uint32_t m = 0;
-  for_row4(sc, aligned, n, [&](int i0, const uint32_t (&k4)[4]) {
-    uint32_t cnt = 0;
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int b0 = 0; b0 < n; b0 += 4 * kThreads * kU) {
+      uint32_t kk[kU][4], cnt[kU], incl[kU];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cnt += (i0 + j < n && k4[j] >= edge) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t off = m + block_excl_scan(cnt, sm.wred[0], tot);
+      for (int u = 0; u < kU; ++u) load4(sc, aligned, b0 + 4 * (u * kThreads + tid), n, kk[u]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i0 + j < n && k4[j] >= edge) {
-        sm.ckey[off] = k4[j];
-        sm.cpos[off] = i0 + j;
-        ++off;
+      for (int u = 0; u < kU; ++u) {
+        const int i0 = b0 + 4 * (u * kThreads + tid);
+        cnt[u] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt[u] += (i0 + j < n && kk[u][j] >= edge) ? 1u : 0u;
+        incl[u] = wave_incl_scan(cnt[u], lane);
+        if (lane == 63) sm.upre[u][wave] = incl[u];  // wave total
       }
-    m += tot;
-  });
+      __syncthreads();
+      if (wave == 0) {
+        // exclusive scan of the kU x kWaves totals in (u, wave) order; lane
+        // handles entries 2 lane and 2 lane + 1
+        uint32_t *flat = &sm.upre[0][0];
+        static_assert(kU * kWaves == 128, "two entries per lane");
+        const uint32_t a0 = flat[2 * lane], a1 = flat[2 * lane + 1];
+        const uint32_t pair = a0 + a1;
+        const uint32_t pin = wave_incl_scan(pair, lane);
+        flat[2 * lane] = pin - pair;
+        flat[2 * lane + 1] = pin - pair + a0;
+        if (lane == 63) sm.bcnt = pin;  // batch total
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i0 = b0 + 4 * (u * kThreads + tid);
+        uint32_t off = m + sm.upre[u][wave] + incl[u] - cnt[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (i0 + j < n && kk[u][j] >= edge) {
+            sm.ckey[off] = kk[u][j];
+            sm.cpos[off] = i0 + j;
+            ++off;
+          }
+      }
+      m += sm.bcnt;
+      __syncthreads();  // upre and bcnt are rewritten by the next batch
+    }
+  }
   __syncthreads();
   // ---- exact k-th key among the m candidates (all >= edge)
   Narrow nc;
