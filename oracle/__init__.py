@@ -9,6 +9,7 @@ Functions follow the plain definitions written out in dsa_oracle.c:
   * indexer scores  I[t,s] = sum_j w[t,j] ReLU((qs q[t,j]) . (ks k[s]))  for s <= pos(t),
   * top-k under (score desc, position desc),
   * sparse MLA-MQA attention over the selected latent rows,
+  * masked multi-head attention in MLA's multi-head form (short-prefill mode),
   * one paged decode query per sequence.
 """
 from __future__ import annotations
@@ -23,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
 
 
 def build(force: bool = False) -> str:
@@ -59,6 +60,8 @@ def lib():
         L.ora_topk_row.restype = i64
         L.ora_topk_rows.argtypes = [P, i64, P, i64, i32, P, P]
         L.ora_sparse_mla_rows.argtypes = [ctypes.c_int, P, P, P, i64, i32, i64, i32, i32, i32, dbl,
+                                          P, i64, P, P]
+        L.ora_masked_mha_rows.argtypes = [ctypes.c_int, P, P, P, P, P, i32, i32, i32, i32, i32, i32, dbl,
                                           P, i64, P, P]
         L.ora_decode.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                  dbl, P, i64, P, P, P, P]
@@ -96,6 +99,8 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
+    if a.dtype == np.float64:
+        return F64
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -176,7 +181,7 @@ def sparse_mla_rows(q, kv, idx, sm_scale, rows=None, Dv=512):
     """q [T, H, Dqk], kv [N, Dqk] (fp32 or bf16), idx [T, k] -> (o [n,H,Dv], lse [n,H]) fp64."""
     q, kv, idx = _np(q), _np(kv), _np(idx, np.int32)
     dt = _dtype_code(q)
-    assert _dtype_code(kv) == dt and dt in (F32, BF16)
+    assert _dtype_code(kv) == dt and dt in (F32, BF16, F64)
     T, H, Dqk = q.shape
     N = kv.shape[0]
     k = idx.shape[1]
@@ -185,6 +190,26 @@ def sparse_mla_rows(q, kv, idx, sm_scale, rows=None, Dv=512):
     lse = np.empty((len(rows), H), dtype=np.float64)
     lib().ora_sparse_mla_rows(dt, _p(q), _p(kv), _p(idx), T, H, N, k, Dqk, Dv, float(sm_scale),
                               _p(rows), len(rows), _p(o), _p(lse))
+    return o, lse
+
+
+def masked_mha_rows(q, kv, w_uk, w_uv, idx, sm_scale, rows=None, Dr=64):
+    """Masked MHA in MLA's multi-head form.  q [T, H, Dn+Dr], kv [N, Dc+Dr],
+    w_uk [H, Dn, Dc], w_uv [H, Dvh, Dc] (all fp32, bf16 or fp64, one dtype),
+    idx [T, k] -> (o [n, H, Dvh], lse [n, H]) fp64."""
+    q, kv, w_uk, w_uv, idx = _np(q), _np(kv), _np(w_uk), _np(w_uv), _np(idx, np.int32)
+    dt = _dtype_code(q)
+    assert all(_dtype_code(a) == dt for a in (kv, w_uk, w_uv)) and dt in (F32, BF16, F64)
+    T, H, Dq = q.shape
+    Hw, Dn, Dc = w_uk.shape
+    Dvh = w_uv.shape[1]
+    assert Hw == H and w_uv.shape == (H, Dvh, Dc) and Dn + Dr == Dq and kv.shape[1] == Dc + Dr
+    k = idx.shape[1]
+    rows = np.arange(T, dtype=np.int64) if rows is None else _np(rows, np.int64)
+    o = np.empty((len(rows), H, Dvh), dtype=np.float64)
+    lse = np.empty((len(rows), H), dtype=np.float64)
+    lib().ora_masked_mha_rows(dt, _p(q), _p(kv), _p(w_uk), _p(w_uv), _p(idx), H, k, Dc, Dr, Dn, Dvh,
+                              float(sm_scale), _p(rows), len(rows), _p(o), _p(lse))
     return o, lse
 
 

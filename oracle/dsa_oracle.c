@@ -34,6 +34,12 @@
  *    row is all zero); payload = RNE-to-E4M3, saturating at +-448, of the fp32
  *    quotient x/scale.
  *  - an empty selected set gives o = 0 and lse = -inf.
+ *  - the masked-MHA mode for short prefill (mizuki-eaf.pages.dev, "parity
+ *    evaluation"; m.digipub.cc, section 2) is read as MLA in its multi-head
+ *    form: every head gets its own key (the latent's 512 dims up-projected to
+ *    128, plus the shared 64 rope dims) and value (the latent up-projected to
+ *    128), and attends densely over its causal positions with every position
+ *    outside the query's top-k selection masked out.
  *
  * Every floating-point accumulation here is fp64, in the plain loop order of
  * the definition; nothing is blocked, fused or reordered.
@@ -127,7 +133,7 @@ void ora_quantize_rows(const float *x, int64_t rows, int32_t cols, uint8_t *x8, 
 
 /* ----------------------------------------------------------------- indexer */
 
-enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_E4M3 = 2 };
+enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_E4M3 = 2, ORA_F64 = 3 };
 
 static double elem(int dtype, const void *p, int64_t i)
 {
@@ -135,6 +141,8 @@ static double elem(int dtype, const void *p, int64_t i)
         return ora_e4m3_decode(((const uint8_t *)p)[i]);
     if (dtype == ORA_BF16)
         return ora_bf16_decode(((const uint16_t *)p)[i]);
+    if (dtype == ORA_F64)
+        return ((const double *)p)[i];
     return (double)((const float *)p)[i];
 }
 
@@ -383,5 +391,93 @@ void ora_decode(const uint8_t *q8, const float *qs, const float *w, const uint16
         }
         free(sc);
         free(phys);
+    }
+}
+
+/* ------------------------------------------------- masked MHA (short prefill) */
+
+/*
+ * Masked multi-head attention in MLA's multi-head form.  Latent rows kv
+ * [N, Dc + Dr] (Dc compressed dims, Dr rope dims); per head h the up-projections
+ * w_uk [H, Dn, Dc] and w_uv [H, Dvh, Dc]:
+ *   K_h[s] = ( sum_c w_uk[h,e,c] kv[s,c]  for e < Dn ,  kv[s, Dc + j]  for j < Dr )
+ *   V_h[s] =   sum_c w_uv[h,e,c] kv[s,c]  for e < Dvh
+ * Query q [T, H, Dn + Dr].  For t = rows[i], head h, over the positions allowed
+ * by the query's mask -- the valid entries r_1..r_m of idx[t] --
+ *   z_a = sm_scale * q[t,h,:] . K_h[r_a]
+ *   o[i,h,:] = sum_a softmax(z)_a V_h[r_a],  lse[i,h] = log sum_a exp(z_a)
+ * with m = 0 giving o = 0, lse = -inf.  K_h and V_h are formed from their
+ * definition for every row they are needed for.
+ */
+void ora_masked_mha_rows(int dtype, const void *q, const void *kv, const void *w_uk, const void *w_uv,
+                         const int32_t *idx, int32_t H, int32_t k, int32_t Dc, int32_t Dr, int32_t Dn,
+                         int32_t Dvh, double sm_scale, const int64_t *rows, int64_t nrows, double *o,
+                         double *lse)
+{
+    int64_t i;
+    const int32_t Dq = Dn + Dr, Dl = Dc + Dr;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        int64_t t = rows[i];
+        const int32_t *sel = idx + t * (int64_t)k;
+        double *z = (double *)malloc(sizeof(double) * (size_t)k);
+        double *key = (double *)malloc(sizeof(double) * (size_t)Dq);
+        double *val = (double *)malloc(sizeof(double) * (size_t)Dvh);
+        int32_t h;
+        for (h = 0; h < H; ++h) {
+            double *oh = o + (i * H + h) * (int64_t)Dvh;
+            double mx = -INFINITY, sum = 0.0;
+            int32_t a, c, e, m = 0;
+            for (e = 0; e < Dvh; ++e)
+                oh[e] = 0.0;
+            for (a = 0; a < k; ++a) {
+                double dot = 0.0;
+                int64_t r = sel[a];
+                if (r < 0) {
+                    z[a] = -INFINITY;
+                    continue;
+                }
+                for (e = 0; e < Dn; ++e) {
+                    double acc = 0.0;
+                    for (c = 0; c < Dc; ++c)
+                        acc += elem(dtype, w_uk, ((int64_t)h * Dn + e) * Dc + c) * elem(dtype, kv, r * Dl + c);
+                    key[e] = acc;
+                }
+                for (e = 0; e < Dr; ++e)
+                    key[Dn + e] = elem(dtype, kv, r * Dl + Dc + e);
+                for (e = 0; e < Dq; ++e)
+                    dot += elem(dtype, q, (t * H + h) * (int64_t)Dq + e) * key[e];
+                z[a] = sm_scale * dot;
+                if (z[a] > mx)
+                    mx = z[a];
+                ++m;
+            }
+            if (m == 0) {
+                lse[i * H + h] = -INFINITY;
+                continue;
+            }
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    sum += exp(z[a] - mx);
+            for (a = 0; a < k; ++a) {
+                double p;
+                int64_t r = sel[a];
+                if (r < 0)
+                    continue;
+                p = exp(z[a] - mx) / sum;
+                for (e = 0; e < Dvh; ++e) {
+                    double acc = 0.0;
+                    for (c = 0; c < Dc; ++c)
+                        acc += elem(dtype, w_uv, ((int64_t)h * Dvh + e) * Dc + c) * elem(dtype, kv, r * Dl + c);
+                    val[e] = acc;
+                }
+                for (e = 0; e < Dvh; ++e)
+                    oh[e] += p * val[e];
+            }
+            lse[i * H + h] = mx + log(sum);
+        }
+        free(z);
+        free(key);
+        free(val);
     }
 }

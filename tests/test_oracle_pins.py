@@ -347,6 +347,71 @@ def test_mla_order_and_padding_invariance(ora):
     assert np.all(e == 0) and np.all(np.isneginf(le))
 
 
+# ------------------------------------------------------ masked MHA (short prefill)
+def _mha_inputs(seed, T, N, H, Dc=32, Dr=8, Dn=16, Dvh=12, dtype=torch.float64):
+    q = synth.normal(seed, 1, (T, H, Dn + Dr)).to(dtype)
+    kv = synth.normal(seed, 2, (N, Dc + Dr), std=0.5).to(dtype)
+    w_uk = synth.normal(seed, 3, (H, Dn, Dc), std=1 / math.sqrt(Dc)).to(dtype)
+    w_uv = synth.normal(seed, 4, (H, Dvh, Dc), std=1 / math.sqrt(Dc)).to(dtype)
+    return q, kv, w_uk, w_uv
+
+
+def test_masked_mha_equals_absorbed_mqa(ora):
+    """MLA's two forms agree: scores q_h.(W_uk c, r) = (W_uk^T q_n, q_r).(c, r), and
+    the value W_uv c comes out of the softmax sum.  So masked MHA equals the MQA
+    oracle run on absorbed queries, followed by the value up-projection."""
+    T, N, H, k, Dc, Dr, Dn, Dvh = 9, 30, 3, 7, 32, 8, 16, 12
+    q, kv, w_uk, w_uv = _mha_inputs(11, T, N, H, Dc, Dr, Dn, Dvh)
+    idx = np.full((T, k), -1, np.int32)
+    perm = synth.permutation(11, 5, N).numpy()
+    for t in range(T):
+        m = (t % k) + 1 if t != 4 else 0   # one query with an empty selection
+        idx[t, :m] = perm[(3 * t + np.arange(m)) % N]
+    scale = 0.17
+    o, lse = ora.masked_mha_rows(q, kv, w_uk, w_uv, idx, scale, Dr=Dr)
+    qn, qr = q[..., :Dn].numpy(), q[..., Dn:].numpy()
+    q_abs = np.concatenate([np.einsum("hec,the->thc", w_uk.numpy(), qn), qr], axis=-1)
+    oa, la = ora.sparse_mla_rows(np.ascontiguousarray(q_abs), kv.numpy(), idx, scale, Dv=Dc)
+    ref = np.einsum("hec,thc->the", w_uv.numpy(), oa)
+    np.testing.assert_allclose(o, ref, rtol=1e-11, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(la))
+    fin = np.isfinite(la)
+    np.testing.assert_allclose(lse[fin], la[fin], rtol=1e-12, atol=1e-12)
+    assert np.all(o[4] == 0) and np.all(np.isneginf(lse[4]))
+
+
+def test_masked_mha_full_selection_equals_dense_causal_mha(ora):
+    """k >= L: the mask keeps every causal position, so the result is dense
+    causal multi-head attention with per-head keys and values."""
+    L, H, Dc, Dr, Dn, Dvh = 24, 2, 32, 8, 16, 12
+    q, kv, w_uk, w_uv = _mha_inputs(12, L, L, H, Dc, Dr, Dn, Dvh)
+    idx = np.full((L, 32), -1, np.int32)
+    for t in range(L):
+        idx[t, :t + 1] = np.arange(t + 1)
+    scale = 1 / math.sqrt(Dn + Dr)
+    o, lse = ora.masked_mha_rows(q, kv, w_uk, w_uv, idx, scale, Dr=Dr)
+    K = torch.cat([torch.einsum("hec,sc->hse", w_uk, kv[:, :Dc]), kv[None, :, Dc:].expand(H, -1, -1)], -1)
+    V = torch.einsum("hec,sc->hse", w_uv, kv[:, :Dc])
+    qt = q.permute(1, 0, 2)
+    mask = torch.tril(torch.ones(L, L, dtype=torch.bool))
+    ro = torch.nn.functional.scaled_dot_product_attention(qt, K, V, attn_mask=mask, scale=scale)
+    rl = torch.logsumexp(((qt @ K.transpose(1, 2)) * scale).masked_fill(~mask, -math.inf), -1)
+    np.testing.assert_allclose(o, ro.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, rl.T.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_masked_mha_mask_order_and_padding_invariance(ora):
+    T, N, H, k = 4, 40, 2, 16
+    q, kv, w_uk, w_uv = _mha_inputs(13, T, N, H, dtype=torch.bfloat16)
+    sel = synth.permutation(13, 6, N)[:T * 10].view(T, 10).to(torch.int32).numpy()
+    pad = np.full((T, k), -1, np.int32)
+    pad[:, 3:13] = sel
+    a, la = ora.masked_mha_rows(q, kv, w_uk, w_uv, pad, 0.2, Dr=8)
+    b, lb = ora.masked_mha_rows(q, kv, w_uk, w_uv, np.ascontiguousarray(sel[:, ::-1]), 0.2, Dr=8)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(la, lb, rtol=1e-14)
+
+
 # ------------------------------------------------------------------ decode
 def _small_decode(shuffled, seed=4, B=3, lo=70, hi=300, k=64):
     cfg = synth.DecodeConfig("t", B, lo, hi, 4, 32, 8, k, seed, shuffled)
