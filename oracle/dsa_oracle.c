@@ -406,45 +406,82 @@ void ora_decode(const uint8_t *q8, const float *qs, const float *w, const uint16
  * by the query's mask -- the valid entries r_1..r_m of idx[t] --
  *   z_a = sm_scale * q[t,h,:] . K_h[r_a]
  *   o[i,h,:] = sum_a softmax(z)_a V_h[r_a],  lse[i,h] = log sum_a exp(z_a)
- * with m = 0 giving o = 0, lse = -inf.  K_h and V_h are formed from their
- * definition for every row they are needed for.
+ * with m = 0 giving o = 0, lse = -inf.  Head by head, K_h and V_h are formed
+ * from their definition once for each position that a requested row selects
+ * and then read by every row that selects it.
  */
 void ora_masked_mha_rows(int dtype, const void *q, const void *kv, const void *w_uk, const void *w_uv,
                          const int32_t *idx, int32_t H, int32_t k, int32_t Dc, int32_t Dr, int32_t Dn,
                          int32_t Dvh, double sm_scale, const int64_t *rows, int64_t nrows, double *o,
                          double *lse)
 {
-    int64_t i;
     const int32_t Dq = Dn + Dr, Dl = Dc + Dr;
-#pragma omp parallel for schedule(dynamic, 1)
+    int64_t i, p, npos = 0, top = -1;
+    int64_t *slot, *pos;
+    double *K, *V;
+    int32_t h;
+    /* the positions the requested rows select, each given a table slot */
     for (i = 0; i < nrows; ++i) {
-        int64_t t = rows[i];
-        const int32_t *sel = idx + t * (int64_t)k;
-        double *z = (double *)malloc(sizeof(double) * (size_t)k);
-        double *key = (double *)malloc(sizeof(double) * (size_t)Dq);
-        double *val = (double *)malloc(sizeof(double) * (size_t)Dvh);
-        int32_t h;
-        for (h = 0; h < H; ++h) {
+        int32_t a;
+        for (a = 0; a < k; ++a)
+            if (idx[rows[i] * (int64_t)k + a] > top)
+                top = idx[rows[i] * (int64_t)k + a];
+    }
+    slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(top + 1 > 0 ? top + 1 : 1));
+    pos = (int64_t *)malloc(sizeof(int64_t) * (size_t)(top + 1 > 0 ? top + 1 : 1));
+    for (p = 0; p <= top; ++p)
+        slot[p] = -1;
+    for (i = 0; i < nrows; ++i) {
+        int32_t a;
+        for (a = 0; a < k; ++a) {
+            int64_t r = idx[rows[i] * (int64_t)k + a];
+            if (r >= 0 && slot[r] < 0) {
+                slot[r] = npos;
+                pos[npos++] = r;
+            }
+        }
+    }
+    K = (double *)malloc(sizeof(double) * (size_t)(npos > 0 ? npos : 1) * (size_t)Dq);
+    V = (double *)malloc(sizeof(double) * (size_t)(npos > 0 ? npos : 1) * (size_t)Dvh);
+    for (h = 0; h < H; ++h) {
+#pragma omp parallel for schedule(static)
+        for (p = 0; p < npos; ++p) {
+            const int64_t r = pos[p];
+            double *key = K + p * Dq, *val = V + p * Dvh;
+            int32_t c, e;
+            for (e = 0; e < Dn; ++e) {
+                double acc = 0.0;
+                for (c = 0; c < Dc; ++c)
+                    acc += elem(dtype, w_uk, ((int64_t)h * Dn + e) * Dc + c) * elem(dtype, kv, r * Dl + c);
+                key[e] = acc;
+            }
+            for (e = 0; e < Dr; ++e)
+                key[Dn + e] = elem(dtype, kv, r * Dl + Dc + e);
+            for (e = 0; e < Dvh; ++e) {
+                double acc = 0.0;
+                for (c = 0; c < Dc; ++c)
+                    acc += elem(dtype, w_uv, ((int64_t)h * Dvh + e) * Dc + c) * elem(dtype, kv, r * Dl + c);
+                val[e] = acc;
+            }
+        }
+#pragma omp parallel for schedule(dynamic, 1)
+        for (i = 0; i < nrows; ++i) {
+            const int64_t t = rows[i];
+            const int32_t *sel = idx + t * (int64_t)k;
             double *oh = o + (i * H + h) * (int64_t)Dvh;
+            double *z = (double *)malloc(sizeof(double) * (size_t)k);
             double mx = -INFINITY, sum = 0.0;
-            int32_t a, c, e, m = 0;
+            int32_t a, e, m = 0;
             for (e = 0; e < Dvh; ++e)
                 oh[e] = 0.0;
             for (a = 0; a < k; ++a) {
                 double dot = 0.0;
-                int64_t r = sel[a];
-                if (r < 0) {
+                const double *key;
+                if (sel[a] < 0) {
                     z[a] = -INFINITY;
                     continue;
                 }
-                for (e = 0; e < Dn; ++e) {
-                    double acc = 0.0;
-                    for (c = 0; c < Dc; ++c)
-                        acc += elem(dtype, w_uk, ((int64_t)h * Dn + e) * Dc + c) * elem(dtype, kv, r * Dl + c);
-                    key[e] = acc;
-                }
-                for (e = 0; e < Dr; ++e)
-                    key[Dn + e] = elem(dtype, kv, r * Dl + Dc + e);
+                key = K + slot[sel[a]] * Dq;
                 for (e = 0; e < Dq; ++e)
                     dot += elem(dtype, q, (t * H + h) * (int64_t)Dq + e) * key[e];
                 z[a] = sm_scale * dot;
@@ -454,30 +491,28 @@ void ora_masked_mha_rows(int dtype, const void *q, const void *kv, const void *w
             }
             if (m == 0) {
                 lse[i * H + h] = -INFINITY;
+                free(z);
                 continue;
             }
             for (a = 0; a < k; ++a)
                 if (sel[a] >= 0)
                     sum += exp(z[a] - mx);
             for (a = 0; a < k; ++a) {
-                double p;
-                int64_t r = sel[a];
-                if (r < 0)
+                double pr;
+                const double *val;
+                if (sel[a] < 0)
                     continue;
-                p = exp(z[a] - mx) / sum;
-                for (e = 0; e < Dvh; ++e) {
-                    double acc = 0.0;
-                    for (c = 0; c < Dc; ++c)
-                        acc += elem(dtype, w_uv, ((int64_t)h * Dvh + e) * Dc + c) * elem(dtype, kv, r * Dl + c);
-                    val[e] = acc;
-                }
+                pr = exp(z[a] - mx) / sum;
+                val = V + slot[sel[a]] * Dvh;
                 for (e = 0; e < Dvh; ++e)
-                    oh[e] += p * val[e];
+                    oh[e] += pr * val[e];
             }
             lse[i * H + h] = mx + log(sum);
+            free(z);
         }
-        free(z);
-        free(key);
-        free(val);
     }
+    free(slot);
+    free(pos);
+    free(K);
+    free(V);
 }
