@@ -54,7 +54,11 @@ enum {
     DSA_D_QK = 576,    /* latent width: 512 no-rope + 64 rope               */
     DSA_D_V = 512,     /* value width: the first 512 dims of the latent     */
     DSA_MAX_K = 2048,  /* largest supported top-k                           */
-    DSA_PAGE = 64      /* tokens per page of the paged decode cache         */
+    DSA_PAGE = 64,     /* tokens per page of the paged decode cache         */
+    DSA_MHA_DN = 128,  /* masked MHA: per-head no-rope key dims             */
+    DSA_MHA_DR = 64,   /* masked MHA: rope dims (shared by every head)      */
+    DSA_MHA_DV = 128,  /* masked MHA: per-head value dims                   */
+    DSA_MHA_MAX_L = 65536  /* masked MHA: longest sequence                  */
 };
 
 /* Message of the last failed call on this thread ("" if none). */
@@ -129,6 +133,36 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
                               int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale,
                               void *out, float *lse, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Masked multi-head attention for short prefill (the mode that stands in for
+ * DSA on short sequences: mizuki-eaf.pages.dev, "parity evaluation";
+ * m.digipub.cc, section 2).  MLA in its multi-head form over one causal
+ * sequence (query t sits at position t): per head h
+ *   K_h[s] = ( W_uk[h] kv[s, 0:512] ,  kv[s, 512:576] )       (128 + 64 dims)
+ *   V_h[s] =   W_uv[h] kv[s, 0:512]                           (128 dims)
+ *   o[t,h] = sum_s softmax_s(sm_scale * q[t,h].K_h[s]) V_h[s]
+ * over the positions s <= t that idx[t] selects (the top-k mask); entries
+ * outside [0, t] (-1 padding among them) are ignored and a position listed
+ * twice counts once.  It equals dsa_sparse_mla_fwd on the same selection with
+ * the up-projections absorbed into the query (out = W_uv[h] o_MQA, same lse).
+ *   q    [L, H, 192] BF16 (128 no-rope dims, then the 64 rope dims)
+ *   kv   [L, 576]    BF16 latent rows (512 compressed + 64 rope)
+ *   w_uk [H, 128, 512] BF16,  w_uv [H, 128, 512] BF16 (row e of head h maps
+ *        the 512 compressed dims to output dim e)
+ *   idx  [L, k] int32;  out [L, H, 128] BF16;  lse [L, H] fp32 (natural log,
+ *        may be NULL).  A query with nothing selected gets o = 0, lse = -inf.
+ * K_h and V_h are formed once per call in bf16 (fp32 accumulation, one bf16
+ * rounding); logits, softmax and the output accumulate in fp32.
+ * workspace: dsa_masked_mha_workspace_bytes(L, H) bytes (K, V and the L x L
+ * bit mask), required, no initialisation; calls sharing one must not overlap.
+ * Limits: L <= DSA_MHA_MAX_L.
+ */
+size_t dsa_masked_mha_workspace_bytes(int32_t L, int32_t H);
+dsa_status dsa_masked_mha_prefill(const void *q, const void *kv, const void *w_uk, const void *w_uv,
+                                  const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale,
+                                  void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Fused prefill of one causal sequence (query t sits at position t):

@@ -159,6 +159,29 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
   return fail(DSA_ERR_UNSUPPORTED, "sparse MLA dtype must be BF16 or F32");
 }
 
+size_t dsa_masked_mha_workspace_bytes(int32_t L, int32_t H) {
+  if (L <= 0 || H <= 0) return 0;
+  return masked_mha_workspace_bytes(L, H);
+}
+
+dsa_status dsa_masked_mha_prefill(const void *q, const void *kv, const void *w_uk, const void *w_uv,
+                                  const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale,
+                                  void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(L >= 0, DSA_ERR_INVALID_ARG, "L must be >= 0 (got %d)", L);
+  REQUIRE(H > 0, DSA_ERR_INVALID_ARG, "H must be > 0");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(L <= DSA_MHA_MAX_L, DSA_ERR_UNSUPPORTED, "masked MHA needs L <= %d (got %d)", DSA_MHA_MAX_L, L);
+  REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (L == 0) return DSA_OK;
+  REQUIRE(q && kv && w_uk && w_uv && idx && out && workspace, DSA_ERR_INVALID_ARG, "null pointer");
+  const size_t need = masked_mha_workspace_bytes(L, H);
+  REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu", workspace_bytes, need);
+  return hip_check(launch_masked_mha(q, kv, w_uk, w_uv, idx, L, H, k, sm_scale, out, lse, workspace, stream),
+                   "masked mha launch");
+}
+
 static dsa_status check_prefill(const dsa_prefill_args *a, bool attention) {
   REQUIRE(a, DSA_ERR_INVALID_ARG, "null args");
   REQUIRE(a->L >= 1, DSA_ERR_INVALID_ARG, "L must be >= 1");

@@ -116,6 +116,12 @@ hipError_t launch_decode_indexer(const uint8_t *q8, const float *qs, const float
                                  const int32_t *block_table, int32_t max_blocks,
                                  const int32_t *ctx_len, int32_t B, int32_t max_ctx, int64_t n_pool_rows,
                                  float *scores, int64_t ld, hipStream_t s);
+// Masked MHA in MLA's multi-head form (BF16; per head 128 + 64 logit dims,
+// 128 value dims, latent 512 + 64).  workspace: masked_mha_workspace_bytes(L, H).
+size_t masked_mha_workspace_bytes(int32_t L, int32_t H);
+hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, const void *w_uv,
+                             const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale, void *out,
+                             float *lse, void *workspace, hipStream_t s);
 hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStream_t s);
 hipError_t launch_cache_append(const void *latent, const uint8_t *k8, const float *ks,
                                const int32_t *pos, int32_t B, int32_t D_I,

@@ -24,7 +24,8 @@ EXPORTS = (
     "dsa_last_error", "dsa_version", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select",
     "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_fwd", "dsa_prefill_workspace_bytes", "dsa_prefill",
     "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
-    "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd",
+    "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd", "dsa_masked_mha_workspace_bytes",
+    "dsa_masked_mha_prefill",
 )
 
 
@@ -82,7 +83,10 @@ def load():
     L.dsa_prefill_select.argtypes = [ctypes.POINTER(PrefillArgs), _P, _SZ, _P]
     L.dsa_decode_indexer_scores.argtypes = [ctypes.POINTER(DecodeArgs), _P, _I64, _P]
     L.dsa_sparse_mla_paged_fwd.argtypes = [_P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]
-    for name in ("dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
+    L.dsa_masked_mha_workspace_bytes.argtypes = [_I32, _I32]
+    L.dsa_masked_mha_workspace_bytes.restype = _SZ
+    L.dsa_masked_mha_prefill.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]
+    for name in ("dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
                  "dsa_prefill", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
                  "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd"):
         getattr(L, name).restype = ctypes.c_int
@@ -158,6 +162,20 @@ def dsa_sparse_mla_fwd(q, kv, idx, sm_scale, out, lse=None, dt=None, workspace=N
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().dsa_sparse_mla_fwd(_ptr(q), _ptr(kv), dt, _ptr(idx), T, H, N, k, float(sm_scale), _ptr(out),
                                      _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_masked_mha_workspace_bytes(L: int, H: int) -> int:
+    return int(load().dsa_masked_mha_workspace_bytes(L, H))
+
+
+def dsa_masked_mha_prefill(q, kv, w_uk, w_uv, idx, sm_scale, out, workspace, lse=None, stream=None):
+    """q [L,H,192], kv [L,576], w_uk/w_uv [H,128,512] bf16, idx [L,k] -> out [L,H,128] bf16, lse [L,H]."""
+    L, H = q.shape[0], q.shape[1]
+    k = idx.shape[1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().dsa_masked_mha_prefill(_ptr(q), _ptr(kv), _ptr(w_uk), _ptr(w_uv), _ptr(idx), L, H, k,
+                                         float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                         _stream(stream)))
 
 
 def make_prefill_args(L, H_I, D_I, H, k, idx_dt, q_idx, q_scale, k_idx, k_scale, w, attn_dt, q, kv, sm_scale,

@@ -145,12 +145,15 @@ def to_e4m3_bits(x: torch.Tensor) -> torch.Tensor:
 # tensor ids (part of the counter; fixed forever so that drawn data is stable)
 T_QI, T_KI, T_W, T_Q, T_KV, T_QS, T_KS, T_CTX, T_PERM = range(1, 10)
 T_NEW_KV, T_NEW_K8, T_NEW_KS = 10, 11, 12
+T_MHA_Q, T_WUK, T_WUV = 13, 14, 15
 
 # Logical per-sequence row stride of decode tensors: every position of every
 # sequence has a fixed counter, independent of paging.
 DECODE_MAXCTX = 131072
 PAGE = 64
 D_QK, D_V = 576, 512
+# masked-MHA mode: per-head no-rope key, rope and value dims; compressed latent dims
+MHA_DN, MHA_DR, MHA_DV, MHA_DC = 128, 64, 128, 512
 
 
 @dataclass
@@ -193,6 +196,8 @@ CONFIGS = {
     "decode": DecodeConfig("decode_B64_ctx32768", 64, 32768, 32768, 64, 128, 128, 2048, 0, False),
     "prefill16k": PrefillConfig("prefill_L16384", 16384, 64, 128, 128, 2048, 1, "bf16", True),
     "prefill128k": PrefillConfig("prefill_L131072", 131072, 64, 128, 128, 2048, 1, "bf16", True),
+    # short prefill through the masked-MHA mode (dense multi-head attention under the top-k mask)
+    "mha4k": PrefillConfig("masked_mha_prefill_L4096", 4096, 64, 128, 128, 2048, 3, "bf16", True),
     "paged": DecodeConfig("paged_decode_B128_ctx4096-131072", 128, 4096, 131072, 64, 128, 128, 2048, 2,
                           True),
 }
@@ -240,6 +245,26 @@ def prefill_latent(cfg: PrefillConfig, device="cpu"):
     """Latent cache [L, 576] ~ N(0,1)/24 in the attention dtype."""
     kv = normal(cfg.seed, T_KV, (cfg.L, D_QK), device=device, std=1.0 / 24.0)
     return kv if cfg.attn_dtype == "f32" else kv.to(torch.bfloat16)
+
+
+def mha_query(cfg: PrefillConfig, rows=None, device="cpu"):
+    """Masked-MHA query [T, H, 192] bf16 (128 no-rope dims, then 64 rope dims),
+    N(0, q_std^2) before the RNE cast."""
+    r0, r1 = (0, cfg.L) if rows is None else rows
+    per = cfg.H * (MHA_DN + MHA_DR)
+    q = normal(cfg.seed, T_MHA_Q, (r1 - r0, cfg.H, MHA_DN + MHA_DR), start=r0 * per, device=device,
+               std=cfg.q_std)
+    return q.to(torch.bfloat16)
+
+
+def mha_up_weights(cfg: PrefillConfig, device="cpu"):
+    """Up-projections w_uk [H, 128, 512] and w_uv [H, 128, 512] bf16 with std
+    24/sqrt(512): applied to the latent (std 1/24) they give per-head keys and
+    values of about unit scale."""
+    std = 24.0 / math.sqrt(MHA_DC)
+    w_uk = normal(cfg.seed, T_WUK, (cfg.H, MHA_DN, MHA_DC), device=device, std=std)
+    w_uv = normal(cfg.seed, T_WUV, (cfg.H, MHA_DV, MHA_DC), device=device, std=std)
+    return w_uk.to(torch.bfloat16), w_uv.to(torch.bfloat16)
 
 
 # ------------------------------------------------------------------ decode draws

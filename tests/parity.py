@@ -17,6 +17,11 @@ Tolerances (stated once, used by every parity test):
     fp32 max|do| <= 1e-4 and <= 1e-5 * max|o_ora|, |dlse| <= 1e-5.
     Attention is always checked with the GPU's own selection fed to the
     oracle, since a legal tie swap changes the output.
+  * masked MHA (MLA's multi-head form): the attention bounds above, with
+    lse_slack added to the lse bound: each up-projected key is held in bf16
+    once (unit roundoff 2^-9), which moves a logit by at most
+    2^-9 sm_scale sum_e |q_e K_e|; the slack is twice that (fp32
+    accumulation order on top), maximised over the row's selected keys.
 """
 import numpy as np
 
@@ -79,7 +84,7 @@ def check_topk_row(gpu_idx, ora_scores_row, n, k, label=""):
     return int(diff.size)
 
 
-def check_attention(o_gpu, lse_gpu, o_ora, lse_ora, dtype, label=""):
+def check_attention(o_gpu, lse_gpu, o_ora, lse_ora, dtype, label="", lse_slack=0.0):
     o_gpu = np.asarray(o_gpu, np.float64)
     lse_gpu = np.asarray(lse_gpu, np.float64)
     d = np.abs(o_gpu - o_ora).max() if o_ora.size else 0.0
@@ -93,6 +98,9 @@ def check_attention(o_gpu, lse_gpu, o_ora, lse_ora, dtype, label=""):
     fin = np.isfinite(lse_ora)
     assert np.array_equal(np.isfinite(lse_gpu), fin), f"{label}: lse -inf pattern"
     if fin.any():
-        dl = np.abs(lse_gpu[fin] - lse_ora[fin]).max()
-        assert dl <= lse_tol, f"{label}: max|dlse| {dl:.3e} > {lse_tol}"
+        slack = np.broadcast_to(np.asarray(lse_slack, np.float64), lse_ora.shape)[fin]
+        dl = np.abs(lse_gpu[fin] - lse_ora[fin])
+        bad = dl > lse_tol + slack
+        assert not bad.any(), (f"{label}: {bad.sum()} lse out of tolerance; worst |dlse| {dl.max():.3e} "
+                               f"(bound {lse_tol} + slack up to {slack.max() if slack.size else 0:.3e})")
     return d, omax

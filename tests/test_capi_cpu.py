@@ -127,6 +127,43 @@ def test_sparse_mla_validation(dsa):
     assert L.dsa_sparse_mla_workspace_bytes(100000, 128, 2048) == 0  # enough queries: no split
 
 
+def test_masked_mha_validation(dsa):
+    L = dsa.load()
+    f = L.dsa_masked_mha_prefill
+    need = L.dsa_masked_mha_workspace_bytes(4096, 128)
+    # K and V [L, H, 128] bf16 plus the L x L bit mask
+    assert need >= 2 * 4096 * 128 * 128 * 2 + 4096 * 4096 // 8
+    assert L.dsa_masked_mha_workspace_bytes(0, 128) == 0
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 128, 2048, 0.07, FAKE, FAKE, FAKE, need, None]
+    b = list(base)
+    b[5] = -1
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[5] = 65537
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[6] = 0
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[7] = 0
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[8] = float("nan")
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[2] = None  # w_uk
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[11] = None  # the workspace is required
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[12] = need - 1
+    assert f(*b) == dsa.DSA_ERR_WORKSPACE
+    b = list(base)
+    b[5] = 0  # nothing to do
+    assert f(*b) == dsa.DSA_OK
+
+
 def test_prefill_validation(dsa):
     L = dsa.load()
     a = dsa.make_prefill_args(1000, 64, 128, 128, 2048, dsa.DSA_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE, dsa.DSA_BF16,
