@@ -152,8 +152,12 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
  *        the 512 compressed dims to output dim e)
  *   idx  [L, k] int32;  out [L, H, 128] BF16;  lse [L, H] fp32 (natural log,
  *        may be NULL).  A query with nothing selected gets o = 0, lse = -inf.
- * K_h and V_h are formed once per call in bf16 (fp32 accumulation, one bf16
- * rounding); logits, softmax and the output accumulate in fp32.
+ * K_h and V_h are formed once per call with fp32 accumulation and held in
+ * fp16 (one round-to-nearest-even, saturating at +-65504); the no-rope part
+ * of q enters the logits in fp16 and the rope part in bf16; logits, softmax
+ * and the output accumulate in fp32, probabilities enter the value sum in
+ * fp16.  Values of q, K_h or V_h beyond fp16's range (|x| > 65504) are
+ * outside what this mode supports.
  * workspace: dsa_masked_mha_workspace_bytes(L, H) bytes (K, V and the L x L
  * bit mask), required, no initialisation; calls sharing one must not overlap.
  * Limits: L <= DSA_MHA_MAX_L.

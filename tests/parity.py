@@ -18,9 +18,9 @@ Tolerances (stated once, used by every parity test):
     Attention is always checked with the GPU's own selection fed to the
     oracle, since a legal tie swap changes the output.
   * masked MHA (MLA's multi-head form): the attention bounds above, with
-    lse_slack added to the lse bound: each up-projected key is held in bf16
-    once (unit roundoff 2^-9), which moves a logit by at most
-    2^-9 sm_scale sum_e |q_e K_e|; the slack is twice that (fp32
+    lse_slack added to the lse bound: each up-projected key is held in fp16
+    once (unit roundoff 2^-11), which moves a logit by at most
+    2^-11 sm_scale sum_e |q_e K_e|; the slack is twice that (fp32
     accumulation order on top), maximised over the row's selected keys.
 """
 import numpy as np

@@ -31,11 +31,26 @@ def dsa():
     return d
 
 
-def _inputs(L, H, seed, q_std=1.0):
+def _selector_weights(H, seed):
+    """Up-projections with one weight of 32 per output dim (a seeded choice of
+    latent dim): every K_h and V_h element is 32 times a bf16 latent value,
+    exact in fp16, so the kernel's one rounding of K_h and V_h vanishes and
+    sharp softmaxes test the attention arithmetic alone."""
+    ws = []
+    for m in range(2):
+        w = torch.zeros((H, DN, synth.MHA_DC), dtype=torch.bfloat16)
+        for h in range(H):
+            pick = synth.permutation(seed, 40 + 2 * h + m, synth.MHA_DC)[:DN]
+            w[h, torch.arange(DN), pick] = 32.0
+        ws.append(w)
+    return ws
+
+
+def _inputs(L, H, seed, q_std=1.0, selector=False):
     cfg = synth.PrefillConfig(f"mha_L{L}", L, 64, 128, H, 2048, seed, "bf16", True, q_std=q_std)
     q = synth.mha_query(cfg)
     kv = synth.prefill_latent(cfg)
-    w_uk, w_uv = synth.mha_up_weights(cfg)
+    w_uk, w_uv = _selector_weights(H, seed) if selector else synth.mha_up_weights(cfg)
     return cfg, q, kv, w_uk, w_uv
 
 
@@ -50,7 +65,7 @@ def _run(dsa, q, kv, w_uk, w_uv, idx, scale):
 
 
 def _lse_slack(q, kv, w_uk, idx, rows, heads, scale):
-    """2 * 2^-9 * sm_scale * max over the row's selected keys of sum_e |q_e K_e|
+    """2 * 2^-11 * sm_scale * max over the row's selected keys of sum_e |q_e K_e|
     over the up-projected (no-rope) dims; see tests/parity.py."""
     c = kv[:, :synth.MHA_DC].double().numpy()
     out = np.zeros((len(rows), len(heads)))
@@ -61,7 +76,7 @@ def _lse_slack(q, kv, w_uk, idx, rows, heads, scale):
             sel = idx[r][idx[r] >= 0]
             if sel.size:
                 out[i, j] = (kabs[sel] @ qabs[i]).max()
-    return 2.0 * 2.0 ** -9 * scale * out
+    return 2.0 * 2.0 ** -11 * scale * out
 
 
 def _reference_idx(idx):
@@ -103,10 +118,14 @@ def _check(ora, q, kv, w_uk, w_uv, idx_np, g, gl, rows, scale, label, heads=None
     return check_attention(g[rows][:, heads], gl[rows][:, heads], o, l, "bf16", label, lse_slack=slack)
 
 
-@pytest.mark.parametrize("L,H,k,q_std", [(2000, 16, 256, 1.0), (2000, 16, 256, 4.0), (1100, 8, 2048, 2.0)])
-def test_masked_mha_random_selection(dsa, ora, L, H, k, q_std):
-    _say(f"masked mha random selection L={L} H={H} k={k} q_std={q_std}")
-    cfg, q, kv, w_uk, w_uv = _inputs(L, H, 31, q_std)
+# q_std 1, 2 and 4 give logits of about 0.8, 1.6 and 3.1 nats std with the
+# random up-projections; the selector cases reach about 4 and 9 nats.
+@pytest.mark.parametrize("L,H,k,q_std,selector", [(2000, 16, 256, 1.0, False), (2000, 16, 256, 4.0, False),
+                                                  (1100, 8, 2048, 2.0, False), (2000, 16, 256, 4.0, True),
+                                                  (1100, 8, 2048, 8.0, True)])
+def test_masked_mha_random_selection(dsa, ora, L, H, k, q_std, selector):
+    _say(f"masked mha random selection L={L} H={H} k={k} q_std={q_std} selector={selector}")
+    cfg, q, kv, w_uk, w_uv = _inputs(L, H, 31, q_std, selector)
     idx = _random_selection(L, k, 31)
     idx[5] = -1                                   # empty selection
     idx[300, k // 2:] = -1                        # ragged
