@@ -129,8 +129,7 @@ __global__ __launch_bounds__(256) void mha_upproj_kernel(const __bf16 *__restric
   // lane (g, c) of tile (m, n): output dims e0 + 16m + 4g .. +4 of token t0 + 16n + c
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
-    const int s = s0 + t0 + 16 * n + c;
-    if (s >= L) continue;
+    const int s = s0 + t0 + 16 * n + c;  // rows past L (up to the block's end) are written too
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       f16x4 v;
@@ -162,75 +161,97 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int32_t *__restrict
 }
 
 // ------------------------------------------------------------ attention
-constexpr int kQW = 32;                 // queries per wave (two groups of 16)
-constexpr int kQB = 4 * kQW;            // queries per workgroup
-constexpr int kKT = 32;                 // keys per tile
-constexpr int kKRowSlots = 25;          // K row: 24 x 16 B of data (192 dims) + 1 pad (100 dwords)
-constexpr int kVRowSlots = 18;          // V row: 16 x 16 B of data (128 dims) + 2 pad (72 dwords)
-constexpr int kKRow = kKRowSlots * 16;
-constexpr int kVRow = kVRowSlots * 16;
-constexpr int kKInsts = (kKT * kKRowSlots + 63) / 64;  // 13 wave-wide 1 KB loads (the last one partly padding)
-constexpr int kVInsts = kKT * kVRowSlots / 64;         // 9
-constexpr int kMInsts = kQB * 4 / 256;                 // 2 wave-wide 256 B loads: one mask word per query
-static_assert(kKT * kVRowSlots % 64 == 0, "whole V instructions");
-constexpr int kTileInsts = kKInsts + kVInsts + kMInsts;
-static_assert(kTileInsts % 4 == 0, "every wave issues the same number of loads per tile");
-constexpr int kInstsPerWave = kTileInsts / 4;
-constexpr int kVOff = kKInsts * 1024;            // V rows follow the K rows in a tile buffer
-constexpr int kMOff = kVOff + kVInsts * 1024;    // then the mask words of the workgroup's queries
+constexpr int kQW = 32;        // queries per wave (two groups of 16)
+constexpr int kQB = 4 * kQW;   // queries per workgroup
+constexpr int kKT = 32;        // keys per tile
+// A tile buffer holds four regions, each filled by whole direct-to-LDS
+// instructions (1 KB, or 256 B for the mask words); instruction i writes
+// 16 (or 4) bytes per lane in lane order.  Row strides are padded so that the
+// operand reads below hit distinct banks.
+constexpr int kKnSlots = 17;  // K no-rope row: 16 x 16 B (128 fp16 dims) + 1 pad (68 dwords)
+constexpr int kKrSlots = 9;   // K rope row: 8 x 16 B (64 bf16 dims) + 1 pad (36 dwords)
+constexpr int kVSlots = 18;   // V row: 16 x 16 B (128 fp16 dims) + 2 pad (72 dwords)
+constexpr int kKnRow = kKnSlots * 16, kKrRow = kKrSlots * 16, kVRow = kVSlots * 16;
+constexpr int kKnInsts = (kKT * kKnSlots + 63) / 64;  // 9
+constexpr int kKrInsts = (kKT * kKrSlots + 63) / 64;  // 5
+constexpr int kVInsts = (kKT * kVSlots + 63) / 64;    // 9
+constexpr int kMInsts = kQB * 4 / 256;                // 2: one mask word per query
+constexpr int kKrOff = kKnInsts * 1024;
+constexpr int kVOff = kKrOff + kKrInsts * 1024;
+constexpr int kMOff = kVOff + kVInsts * 1024;
 constexpr int kTileBytes = kMOff + kMInsts * 256;
-constexpr int kNBuf = 3;                         // tile j+2 loads while tile j is computed
-constexpr int kAttnSmem = kNBuf * kTileBytes;
-constexpr int kSteps = kDq / 32;  // 6 K steps of the logits MFMA
-constexpr int kNopeSteps = kDn / 32;  // the first 4 cover the up-projected (fp16) dims
-constexpr int kVT = kDvh / 16;    // 8 value tiles of the PV MFMA
-// A query's exponent reference moves only when its running max exceeds it by
-// more than this (base-2 units): probabilities stay below 2^8, and the output
-// is rescaled only on the rare tiles that raise the max that far.
-constexpr float kRefSlack = 8.0f;
+constexpr int kTileInsts = kKnInsts + kKrInsts + kVInsts + kMInsts;  // 25
+constexpr int kInstsW0 = (kTileInsts + 3) / 4;                       // wave 0 issues 7, the others 6
+static_assert(kTileInsts % 4 == 1, "wave 0 issues one load more than the others");
+constexpr int kNBuf = 3;                  // tile j+2 loads while tile j is computed
+constexpr int kLutOff = kNBuf * kTileBytes;
+constexpr int kAttnSmem = kLutOff + 256 * 16;  // + the mask table
+constexpr int kSteps = kDq / 32;       // 6 K steps of the logits MFMA
+constexpr int kNopeSteps = kDn / 32;   // the first 4 cover the up-projected (fp16) dims
+constexpr int kVT = kDvh / 16;         // 8 value tiles of the PV MFMA (a ninth sums the probabilities)
+constexpr float kUnset = -1e30f;       // no reference yet
+constexpr uint32_t kRaiseBits = 0x5C00u;  // fp16 bits of 2^8
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+
+// Per-half unsigned max of two packed 16-bit pairs.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 m = __builtin_elementwise_max(*reinterpret_cast<const u16x2 *>(&a), *reinterpret_cast<const u16x2 *>(&b));
+  return *reinterpret_cast<const uint32_t *>(&m);
+}
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding
 // (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// Direct-to-LDS loads of key tile `tile` of head h into buffer dst; each wave
-// issues kInstsPerWave of the tile's kTileInsts instructions.
-//  * K: slot q = 25 r + j holds, for key r, 16 bytes j of (K_h no-rope 256 B,
-//    then the 128 B rope part of the latent row) for j < 24 (j = 24 and the
-//    tail slots repeat data);
-//  * V: slot 18 r + j holds 16 bytes j of V_h (j >= 16 repeat chunk 15);
-//  * mask: word q of the workgroup's query q0 + q for this tile.
-// Keys past L - 1 read key L - 1, queries past L - 1 the row of query L - 1
-// (both are excluded by the mask or never stored).
-__device__ __forceinline__ void mha_load_tile(uint8_t *dst, const _Float16 *__restrict__ kbuf,
-                                              const _Float16 *__restrict__ vbuf, const __bf16 *__restrict__ kv,
-                                              const uint32_t *__restrict__ mask, int L, int H, int h, int q0,
-                                              int nw, int tile, int wave, int lane) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
+// Per-workgroup state shared by the walks.
+struct MhaCtx {
+  uint8_t *smem;
+  const char *kn, *kr, *vb, *mk;     // tile-0 bases: K_h no-rope, latent rope, V_h, mask column 0
+  int kr_len, mk_len;                // bytes readable from the rope and mask bases
+  int64_t kv_tile;                   // bytes between tiles in K_h / V_h (32 keys x H heads x 256 B)
+  uint32_t loff[kInstsW0];           // the lane's byte offset within its instructions' tiles
+  int wave, lane, g, c;
+  int L, H, h, q0, ntiles, wave_last;
+};
+
+// Raw buffer descriptor of [base + skip, base + len): loads past the end read
+// 0.  Uniform 32-bit arithmetic (scalar unit).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int len, int skip) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(base + skip), 0, max(len - skip, 0), (int)kRsrcWord3);
+}
+// Descriptor of base + skip with no bound (the K_h / V_h rows of every tile exist).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int64_t skip) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(base + skip), 0, 0x7fffffff, (int)kRsrcWord3);
+}
+
+// Issue this wave's direct-to-LDS loads of tile `tile` into buffer dst.
+// Instruction i = wave + 4n covers its region's slots in lane order; a slot
+// past a region's data loads a duplicate of valid data.  Each region is read
+// through a descriptor rebased on the tile and bounded by its buffer, so the
+// rope rows past L (the caller's latent has L rows) read 0; K_h and V_h rows
+// past L exist (padded to whole up-projection blocks).  All of them are
+// masked.
+__device__ __forceinline__ void mha_load_tile(const MhaCtx &cx, uint8_t *dst, int tile) {
+  const __amdgpu_buffer_rsrc_t rkn = tile_rsrc(cx.kn, tile * cx.kv_tile);
+  const __amdgpu_buffer_rsrc_t rkr = tile_rsrc(cx.kr, cx.kr_len, tile * kKT * kDl * 2);
+  const __amdgpu_buffer_rsrc_t rvb = tile_rsrc(cx.vb, tile * cx.kv_tile);
+  const __amdgpu_buffer_rsrc_t rmk = tile_rsrc(cx.mk, cx.mk_len, tile * 4);
 #pragma unroll
-  for (int n = 0; n < kInstsPerWave; ++n) {
-    const int i = wave + 4 * n;  // uniform
-    if (i < kKInsts) {
-      const int slot = i * 64 + l;
-      const int r = min(slot / kKRowSlots, kKT - 1);
-      const int j = min(slot - (slot / kKRowSlots) * kKRowSlots, 23);
-      const int64_t s = min(tile * kKT + r, L - 1);
-      const void *src = j < 16 ? (const void *)(kbuf + (s * H + h) * kDn + j * 8)
-                               : (const void *)(kv + s * kDl + kDc + (j - 16) * 8);
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + i * 1024), 16, 0, 0);
-    } else if (i < kKInsts + kVInsts) {
-      const int slot = (i - kKInsts) * 64 + l;
-      const int r = slot / kVRowSlots;
-      const int j = min(slot - r * kVRowSlots, 15);
-      const int64_t s = min(tile * kKT + r, L - 1);
-      __builtin_amdgcn_global_load_lds(vbuf + (s * H + h) * kDvh + j * 8, (lds_void *)(dst + i * 1024), 16, 0,
-                                       0);
-    } else {
-      const int m = i - kKInsts - kVInsts;
-      const int64_t t = min(q0 + m * 64 + l, L - 1);
-      __builtin_amdgcn_global_load_lds(mask + t * nw + tile, (lds_void *)(dst + kMOff + m * 256), 4, 0, 0);
-    }
+  for (int n = 0; n < kInstsW0; ++n) {
+    const int i = cx.wave + 4 * n;  // uniform
+    if (i >= kTileInsts) break;
+    if (i < kKnInsts)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkn, (lds_void *)(dst + i * 1024), 16, cx.loff[n], 0, 0, 0);
+    else if (i < kKnInsts + kKrInsts)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkr, (lds_void *)(dst + kKrOff + (i - kKnInsts) * 1024), 16,
+                                               cx.loff[n], 0, 0, 0);
+    else if (i < kKnInsts + kKrInsts + kVInsts)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rvb, (lds_void *)(dst + kVOff + (i - kKnInsts - kKrInsts) * 1024),
+                                               16, cx.loff[n], 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rmk, (lds_void *)(dst + kMOff + (i - kKnInsts - kKrInsts - kVInsts) * 256), 4, cx.loff[n], 0, 0, 0);
   }
 }
 
@@ -238,55 +259,24 @@ __device__ __forceinline__ void mha_load_tile(uint8_t *dst, const _Float16 *__re
 // c+32, c+48 hold the same query).  With both operands equal, a permlane swap
 // returns the row pair's two halves.
 __device__ __forceinline__ float query_max(const float (&x)[8]) {
-  float mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
   const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
   mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
   const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
-// One workgroup per (128 queries, head).  Wave w owns queries q0 + 32 w ..
-// +32 in two groups of 16; lane (g, c) holds query q0 + 32 w + 16 u + c of
-// group u for the softmax and the output (its four value dims per value
-// tile).  Each K and V fragment read from LDS feeds both groups' MFMAs.
-// Workgroups are numbered head-major with each head's longest query blocks
-// first, and consecutive numbers go to the same XCD (workgroup i runs on XCD
-// i mod 8), so that one head's keys and values stay in one L2.
-__global__ __launch_bounds__(256) void masked_mha_kernel(const __bf16 *__restrict__ q,
-                                                         const __bf16 *__restrict__ kv,
-                                                         const _Float16 *__restrict__ kbuf,
-                                                         const _Float16 *__restrict__ vbuf,
-                                                         const uint32_t *__restrict__ mask, int L, int H,
-                                                         float scale_log2, __bf16 *__restrict__ out,
-                                                         float *__restrict__ lse) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];  // kNBuf tile buffers of kTileBytes
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nqb = (L + kQB - 1) / kQB;
-  int lin;
-  {
-    const int n = gridDim.x, i = blockIdx.x, x = i & 7, per = n >> 3, rem = n & 7;
-    lin = x * per + min(x, rem) + (i >> 3);
-  }
-  const int h = lin / nqb;
-  const int q0 = (nqb - 1 - lin % nqb) * kQB;
-  const int nw = (L + 31) >> 5;
-  const int ntiles = (min(q0 + kQB, L) + kKT - 1) / kKT;  // causal bound of the workgroup
-  const int wave_last = min(q0 + kQW * wave + kQW - 1, L - 1);  // this wave's last query
-
-  // Q^T of the lane's two queries, dims 32 s + 8 g .. +8: the no-rope steps
-  // in fp16 (exact for |q| within fp16's normal range) against the fp16 K_h,
-  // the rope steps in bf16 against the latent's rope dims
-  f16x8 qn[2][kNopeSteps];
-  bf16x8 qr[2][kSteps - kNopeSteps];
+// Q^T of the lane's two queries, dims 32 s + 8 g .. +8: the no-rope steps in
+// fp16 (exact for |q| within fp16's normal range) against the fp16 K_h, the
+// rope steps in bf16 against the latent's rope dims.
+__device__ __forceinline__ void mha_load_q(const MhaCtx &cx, const __bf16 *__restrict__ q, f16x8 (&qn)[2][kNopeSteps],
+                                           bf16x8 (&qr)[2][kSteps - kNopeSteps]) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int64_t tq = min(q0 + kQW * wave + 16 * u + c, L - 1);
+    const int64_t tq = min(cx.q0 + kQW * cx.wave + 16 * u + cx.c, cx.L - 1);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(q + (tq * H + h) * kDq + 32 * s + 8 * g);
+      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(q + (tq * cx.H + cx.h) * kDq + 32 * s + 8 * cx.g);
       if (s < kNopeSteps) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) qn[u][s][i] = to_f16_sat((float)v[i]);
@@ -295,155 +285,270 @@ __global__ __launch_bounds__(256) void masked_mha_kernel(const __bf16 *__restric
       }
     }
   }
-  f32x4 o[2][kVT];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < kVT; ++v) o[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // exponent reference (base 2, scaled) and the lane's share of the softmax sum;
-  // the finite start keeps exp2 of masked (-inf) logits at 0 before any key
-  float m_ref[2] = {-1e30f, -1e30f}, l_run[2] = {0.0f, 0.0f};
-  // transposing-load lane roles: row 4g + (c>>2) of each 4-row group, value chunk (c&3)
-  const int tr_off = kVOff + (4 * g + (c >> 2)) * kVRow + (c & 3) * 8;
-  const uint32_t lane_bits = 0x000F000Fu << (4 * g);  // the lane's 8 keys of a tile
+}
 
-  auto buf = [&](int j) { return smem_raw + (j % kNBuf) * kTileBytes; };
-  mha_load_tile(buf(0), kbuf, vbuf, kv, mask, L, H, h, q0, nw, 0, wave, lane);
-  if (ntiles > 1) mha_load_tile(buf(1), kbuf, vbuf, kv, mask, L, H, h, q0, nw, 1, wave, lane);
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstsPerWave));  // tile it landed (tile it+1 may be in flight)
-    else
+// The walk over the workgroup's key tiles (loads pipelined kNBuf - 1 tiles
+// ahead, one barrier per tile).  Per group u: logits S^T[key, query] with
+// x[r] = key 4g + r, x[4 + r] = key 16 + 4g + r of the tile; probabilities
+// p = 2^(x * scale_log2 - m_ref) in fp16, the unselected ones zeroed by an
+// AND with the mask table's lane masks; the PV MFMA takes V^T through the
+// transposing LDS load, and a ninth tile of constant ones rows sums the
+// probabilities: o[u][kVT] row 0 is the query's softmax sum.
+// A query's reference m_ref only moves up: when some probability of the
+// wave reaches 2^8 (or the query has no reference yet, which makes its
+// selected probabilities infinite), the wave takes the re-reference branch:
+// the exact max of each query's selected logits in the tile becomes its
+// reference where it lies above the old one, the query's accumulators are
+// scaled down to it, and the probabilities are formed again.  So every
+// probability that reaches the sums is below 2^8.
+__device__ __forceinline__ void mha_walk(const MhaCtx &cx, const f16x8 (&qn)[2][kNopeSteps],
+                                         const bf16x8 (&qr)[2][kSteps - kNopeSteps], float scale_log2,
+                                         float (&m_ref)[2], f32x4 (&o)[2][kVT + 1]) {
+  const int g = cx.g, c = cx.c, wave = cx.wave;
+  const int tr_off = kVOff + (4 * g + (c >> 2)) * kVRow + (c & 3) * 8;
+  const uint4 *lut = reinterpret_cast<const uint4 *>(cx.smem + kLutOff);
+  f16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = c == 0 ? (_Float16)1.0f : (_Float16)0.0f;
+  // tile it sits in buffer it % kNBuf: cur is its byte offset, nxt2 that of tile it + 2
+  int cur = 0, nxt2 = 2 * kTileBytes;
+  auto step = [](int b) { return b == (kNBuf - 1) * kTileBytes ? 0 : b + kTileBytes; };
+  mha_load_tile(cx, cx.smem, 0);
+  if (cx.ntiles > 1) mha_load_tile(cx, cx.smem + kTileBytes, 1);
+  for (int it = 0; it < cx.ntiles; ++it, cur = step(cur), nxt2 = step(nxt2)) {
+    if (it + 1 < cx.ntiles) {  // tile it landed; tile it+1 may still be in flight
+      if (wave == 0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstsW0));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstsW0 - 1));
+    } else {
       __builtin_amdgcn_s_waitcnt(0);
+    }
     __syncthreads();  // every wave's loads of tile it landed; nobody reads tile it-1 any more
-    if (it + 2 < ntiles) mha_load_tile(buf(it + 2), kbuf, vbuf, kv, mask, L, H, h, q0, nw, it + 2, wave, lane);
-    if (it * kKT > wave_last) continue;  // past every query of this wave
-    const uint8_t *tb = buf(it);
-    const uint32_t mw0 = *reinterpret_cast<const uint32_t *>(tb + kMOff + (kQW * wave + c) * 4);
-    const uint32_t mw1 = *reinterpret_cast<const uint32_t *>(tb + kMOff + (kQW * wave + 16 + c) * 4);
-    if (__builtin_amdgcn_ballot_w64((mw0 | mw1) != 0u) == 0) continue;  // nothing selected in this tile
-    // logits S^T[key, query]: x[r] = key 4g + r, x[4 + r] = key 16 + 4g + r
+    if (it + 2 < cx.ntiles) mha_load_tile(cx, cx.smem + nxt2, it + 2);
+    if (it * kKT > cx.wave_last) continue;  // past every query of this wave
+    const uint8_t *tb = cx.smem + cur;
+    uint32_t mw[2];
+    mw[0] = *reinterpret_cast<const uint32_t *>(tb + kMOff + (kQW * wave + c) * 4);
+    mw[1] = *reinterpret_cast<const uint32_t *>(tb + kMOff + (kQW * wave + 16 + c) * 4);
+    if (__builtin_amdgcn_ballot_w64((mw[0] | mw[1]) != 0u) == 0) continue;  // nothing selected in this tile
     f32x4 s[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) s[u][0] = s[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      if (st < kNopeSteps) {
-        const f16x8 a0 = *reinterpret_cast<const f16x8 *>(tb + c * kKRow + st * 64 + g * 16);
-        const f16x8 a1 = *reinterpret_cast<const f16x8 *>(tb + (16 + c) * kKRow + st * 64 + g * 16);
+    for (int st = 0; st < kNopeSteps; ++st) {
+      const f16x8 a0 = *reinterpret_cast<const f16x8 *>(tb + c * kKnRow + st * 64 + g * 16);
+      const f16x8 a1 = *reinterpret_cast<const f16x8 *>(tb + (16 + c) * kKnRow + st * 64 + g * 16);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          s[u][0] = mfma_f16_16x16x32(a0, qn[u][st], s[u][0]);
-          s[u][1] = mfma_f16_16x16x32(a1, qn[u][st], s[u][1]);
-        }
-      } else {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tb + c * kKRow + st * 64 + g * 16);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tb + (16 + c) * kKRow + st * 64 + g * 16);
+      for (int u = 0; u < 2; ++u) {
+        s[u][0] = mfma_f16_16x16x32(a0, qn[u][st], s[u][0]);
+        s[u][1] = mfma_f16_16x16x32(a1, qn[u][st], s[u][1]);
+      }
+    }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          s[u][0] = mfma_bf16_16x16x32(a0, qr[u][st - kNopeSteps], s[u][0]);
-          s[u][1] = mfma_bf16_16x16x32(a1, qr[u][st - kNopeSteps], s[u][1]);
-        }
+    for (int st = 0; st < kSteps - kNopeSteps; ++st) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tb + kKrOff + c * kKrRow + st * 64 + g * 16);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tb + kKrOff + (16 + c) * kKrRow + st * 64 + g * 16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        s[u][0] = mfma_bf16_16x16x32(a0, qr[u][st], s[u][0]);
+        s[u][1] = mfma_bf16_16x16x32(a1, qr[u][st], s[u][1]);
       }
     }
     float x[2][8];
+    uint4 keep[2];  // fp16 lane masks of the selected keys, in x order
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         x[u][r] = s[u][0][r];
         x[u][4 + r] = s[u][1][r];
       }
-    // mask the unselected keys, unless every lane's keys are all selected
-    const bool partial = (mw0 & lane_bits) != lane_bits || (mw1 & lane_bits) != lane_bits;
-    if (__builtin_amdgcn_ballot_w64(partial) != 0) {
-      const uint32_t mw[2] = {mw0, mw1};
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int bit = (r < 4 ? 0 : 12) + 4 * g + r;
-          x[u][r] = (mw[u] >> bit) & 1u ? x[u][r] : -INFINITY;
-        }
+      keep[u] = lut[((mw[u] >> (4 * g)) & 0xFu) | ((mw[u] >> (12 + 4 * g)) & 0xF0u)];
     }
-    float mx[2];
-    bool raise = false;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      mx[u] = query_max(x[u]) * scale_log2;
-      raise |= mx[u] > m_ref[u] + kRefSlack;
-    }
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // rare: move the references, rescale what was summed
+    uint4 pbits[2];
+    auto probabilities = [&]() {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bool up = mx[u] > m_ref[u] + kRefSlack;
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_ref[u] - mx[u]) : 1.0f;
-        m_ref[u] = up ? mx[u] : m_ref[u];
-        l_run[u] *= alpha;
+        f16x8 p;
 #pragma unroll
-        for (int v = 0; v < kVT; ++v)
+        for (int i = 0; i < 8; ++i) p[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(x[u][i], scale_log2, -m_ref[u]));
+        const uint4 b = *reinterpret_cast<const uint4 *>(&p);
+        pbits[u] = uint4{b.x & keep[u].x, b.y & keep[u].y, b.z & keep[u].z, b.w & keep[u].w};
+      }
+    };
+    probabilities();
+    // largest kept probability of the lane (non-negative fp16 orders like its bits)
+    uint32_t top = pk_max_u16(pk_max_u16(pk_max_u16(pbits[0].x, pbits[0].y), pk_max_u16(pbits[0].z, pbits[0].w)),
+                              pk_max_u16(pk_max_u16(pbits[1].x, pbits[1].y), pk_max_u16(pbits[1].z, pbits[1].w)));
+    top = pk_max_u16(top, top >> 16) & 0xFFFFu;
+    if (__builtin_amdgcn_ballot_w64(top >= kRaiseBits) != 0) {  // rare: move references up
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t sel = ((mw[u] >> (4 * g)) & 0xFu) | ((mw[u] >> (12 + 4 * g)) & 0xF0u);
+        float xm[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) xm[r] = (sel >> r) & 1u ? x[u][r] : -INFINITY;
+        const float mx = query_max(xm) * scale_log2;
+        const float ref = mx > m_ref[u] ? mx : m_ref[u];
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[u] - ref);  // 0 from the unset reference
+        m_ref[u] = ref;
+#pragma unroll
+        for (int v = 0; v <= kVT; ++v)
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[u][v][r] *= alpha;
       }
+      probabilities();
     }
-    // probabilities in fp16 (at most 2^8 against the reference)
     f16x8 pb[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(x[u][i], scale_log2, -m_ref[u]));
-        psum += p;
-        pb[u][i] = (_Float16)p;
-      }
-      l_run[u] += psum;
-    }
+    for (int u = 0; u < 2; ++u) pb[u] = *reinterpret_cast<const f16x8 *>(&pbits[u]);
     // PV: O^T[dv, query] += V^T[dv, keys] P^T[keys, query]
+    lds_i16x4 *vrow = (lds_i16x4 *)(tb + tr_off);  // LDS-space pointer: the reads below take immediate offsets
 #pragma unroll
     for (int v = 0; v < kVT; ++v) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tb + tr_off + v * 32));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tb + tr_off + v * 32 + 16 * kVRow));
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vrow + v * 4);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vrow + v * 4 + 16 * kVRow / 8);
       const i16x4 lohi[2] = {lo, hi};
       const f16x8 va = *reinterpret_cast<const f16x8 *>(lohi);
 #pragma unroll
       for (int u = 0; u < 2; ++u) o[u][v] = mfma_f16_16x16x32(va, pb[u], o[u][v]);
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) o[u][kVT] = mfma_f16_16x16x32(ones, pb[u], o[u][kVT]);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // the tile buffers are free
+}
+
+// The query's softmax sum, from row 0 of the sums tile (lane (0, c)).
+__device__ __forceinline__ float query_sum(const f32x4 &sums, int c) { return __shfl(sums[0], c); }
+
+// Normalise and store the lane's outputs (value dims 16 v + 4 g .. +4) and lse.
+__device__ __forceinline__ void mha_epilogue(const MhaCtx &cx, const float (&m_ref)[2], const float (&l)[2],
+                                             const f32x4 (&o)[2][kVT + 1], __bf16 *__restrict__ out,
+                                             float *__restrict__ lse) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    // the four lane groups hold different keys of the same query
-    float l_tot = l_run[u] + __shfl_xor(l_run[u], 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const int t = q0 + kQW * wave + 16 * u + c;
-    if (t >= L) continue;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    // lane (g, c): value dims 16 v + 4 g .. +4 of query t
+    const int t = cx.q0 + kQW * cx.wave + 16 * u + cx.c;
+    if (t >= cx.L) continue;
+    const float inv = l[u] > 0.0f ? 1.0f / l[u] : 0.0f;
 #pragma unroll
     for (int v = 0; v < kVT; ++v) {
       bf16x4 o4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(o[u][v][r] * inv);
-      *reinterpret_cast<bf16x4 *>(out + ((int64_t)t * H + h) * kDvh + 16 * v + 4 * g) = o4;
+      *reinterpret_cast<bf16x4 *>(out + ((int64_t)t * cx.H + cx.h) * kDvh + 16 * v + 4 * cx.g) = o4;
     }
-    if (lse && g == 0)
-      lse[(int64_t)t * H + h] = l_tot > 0.0f ? (m_ref[u] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (lse && cx.g == 0)
+      lse[(int64_t)t * cx.H + cx.h] = l[u] > 0.0f ? (m_ref[u] + log2f(l[u])) * 0.69314718055994531f : -INFINITY;
   }
+}
+
+// One workgroup per (128 queries, head).  Wave w owns queries q0 + 32 w ..
+// +32 in two groups of 16; lane (g, c) holds query q0 + 32 w + 16 u + c of
+// group u for the softmax and the output.  Each K and V fragment read from
+// LDS feeds both groups' MFMAs.  Workgroups are numbered head-major with each
+// head's longest query blocks first, and consecutive numbers go to the same
+// XCD (workgroup i runs on XCD i mod 8), so that one head's keys and values
+// stay in one L2.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void masked_mha_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const _Float16 *__restrict__ kbuf,
+    const _Float16 *__restrict__ vbuf, const uint32_t *__restrict__ mask, int L, int H, float scale_log2,
+    __bf16 *__restrict__ out, float *__restrict__ lse) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];  // tile buffers, then the mask table
+  MhaCtx cx;
+  cx.smem = smem_raw;
+  const int tid = threadIdx.x;
+  cx.lane = tid & 63;
+  cx.g = cx.lane >> 4;
+  cx.c = cx.lane & 15;
+  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  cx.L = L;
+  cx.H = H;
+  const int nqb = (L + kQB - 1) / kQB;
+  int lin;
+  {
+    const int n = gridDim.x, i = blockIdx.x, x = i & 7, per = n >> 3, rem = n & 7;
+    lin = x * per + min(x, rem) + (i >> 3);
+  }
+  cx.h = lin / nqb;
+  cx.q0 = (nqb - 1 - lin % nqb) * kQB;
+  cx.ntiles = (min(cx.q0 + kQB, L) + kKT - 1) / kKT;           // causal bound of the workgroup
+  cx.wave_last = min(cx.q0 + kQW * cx.wave + kQW - 1, L - 1);  // this wave's last query
+  const int nw = (L + 31) >> 5;
+  cx.kn = (const char *)(kbuf + cx.h * kDn);
+  cx.vb = (const char *)(vbuf + cx.h * kDvh);
+  cx.kr = (const char *)(kv + kDc);
+  cx.mk = (const char *)mask;
+  cx.kr_len = L * kDl * 2 - kDc * 2;  // < 2^31 for L <= 65536
+  cx.mk_len = L * nw * 4;
+  cx.kv_tile = (int64_t)kKT * H * kDn * 2;
+  // lane offsets of this wave's instructions (fixed for every tile)
+#pragma unroll
+  for (int n = 0; n < kInstsW0; ++n) {
+    const int i = cx.wave + 4 * n;
+    uint32_t off = 0;
+    if (i < kKnInsts) {
+      const int slot = i * 64 + cx.lane, r = min(slot / kKnSlots, kKT - 1), j = min(slot % kKnSlots, 15);
+      off = (uint32_t)r * H * kDn * 2 + j * 16;
+    } else if (i < kKnInsts + kKrInsts) {
+      const int slot = (i - kKnInsts) * 64 + cx.lane, r = min(slot / kKrSlots, kKT - 1), j = min(slot % kKrSlots, 7);
+      off = (uint32_t)r * kDl * 2 + j * 16;
+    } else if (i < kKnInsts + kKrInsts + kVInsts) {
+      const int slot = (i - kKnInsts - kKrInsts) * 64 + cx.lane, r = min(slot / kVSlots, kKT - 1),
+                j = min(slot % kVSlots, 15);
+      off = (uint32_t)r * H * kDvh * 2 + j * 16;
+    } else if (i < kTileInsts) {
+      const int t = min(cx.q0 + (i - kKnInsts - kKrInsts - kVInsts) * 64 + cx.lane, L - 1);
+      off = (uint32_t)t * nw * 4;
+    }
+    cx.loff[n] = off;
+  }
+  // mask table: entry n keeps fp16 element e of a group's 8 probabilities iff bit e of n is set
+  {
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      w[d] = ((tid >> (2 * d)) & 1 ? 0x0000FFFFu : 0u) | ((tid >> (2 * d + 1)) & 1 ? 0xFFFF0000u : 0u);
+    *reinterpret_cast<uint4 *>(smem_raw + kLutOff + tid * 16) = uint4{w[0], w[1], w[2], w[3]};
+  }
+  // (the table is read only after the walk's first barrier)
+  f16x8 qn[2][kNopeSteps];
+  bf16x8 qr[2][kSteps - kNopeSteps];
+  mha_load_q(cx, q, qn, qr);
+  f32x4 o[2][kVT + 1];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v <= kVT; ++v) o[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {kUnset, kUnset}, l[2];
+  mha_walk(cx, qn, qr, scale_log2, m_ref, o);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) l[u] = query_sum(o[u][kVT], cx.c);
+  mha_epilogue(cx, m_ref, l, o, out, lse);
 }
 
 }  // namespace
 
 namespace dsa {
+// K_h and V_h [Lp, H, 128] fp16 with Lp = L rounded up to whole up-projection
+// blocks, then the bit mask [L, ceil(L/32)] u32.
+static size_t mha_kv_bytes(int32_t L, int32_t H) {
+  const size_t Lp = (size_t)(L + kUpT - 1) / kUpT * kUpT;
+  return align_up(Lp * H * kDn * 2, 256);
+}
+static size_t mha_mask_bytes(int32_t L) { return align_up((size_t)L * ((L + 31) / 32) * 4, 256); }
+static size_t mha_groups(int32_t L, int32_t H) { return (size_t)(L + kQB - 1) / kQB * H; }
 size_t masked_mha_workspace_bytes(int32_t L, int32_t H) {
-  const size_t kvb = (size_t)L * H * kDn * 2;
-  return 2 * align_up(kvb, 256) + align_up((size_t)L * ((L + 31) / 32) * 4, 256);
+  return 2 * mha_kv_bytes(L, H) + mha_mask_bytes(L);
 }
 
 hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, const void *w_uv,
                              const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale, void *out,
                              float *lse, void *workspace, hipStream_t s) {
   if (L == 0) return hipSuccess;
-  const size_t kvb = align_up((size_t)L * H * kDn * 2, 256);
+  const size_t kvb = mha_kv_bytes(L, H);
   _Float16 *kbuf = (_Float16 *)workspace;
   _Float16 *vbuf = (_Float16 *)((char *)workspace + kvb);
   uint32_t *mask = (uint32_t *)((char *)workspace + 2 * kvb);
@@ -452,8 +557,7 @@ hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, co
     hipError_t e = hipFuncSetAttribute((const void *)mha_upproj_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kUpBuf);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)masked_mha_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kAttnSmem);
+    e = hipFuncSetAttribute((const void *)masked_mha_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmem);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
@@ -464,10 +568,10 @@ hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, co
   hipLaunchKernelGGL(mha_mask_kernel, dim3(L), dim3(256), 0, s, idx, L, k, mask);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nqb = (L + kQB - 1) / kQB;
-  hipLaunchKernelGGL(masked_mha_kernel, dim3((uint32_t)nqb * H), dim3(256), kAttnSmem, s, (const __bf16 *)q,
-                     (const __bf16 *)kv, kbuf, vbuf, mask, L, H, sm_scale * 1.4426950408889634f, (__bf16 *)out,
-                     lse);
+  const dim3 grid((uint32_t)mha_groups(L, H));
+  const float sl2 = sm_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(masked_mha_kernel, grid, dim3(256), kAttnSmem, s, (const __bf16 *)q, (const __bf16 *)kv, kbuf,
+                     vbuf, mask, L, H, sl2, (__bf16 *)out, lse);
   return hipGetLastError();
 }
 }  // namespace dsa

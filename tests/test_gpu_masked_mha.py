@@ -153,6 +153,26 @@ def test_masked_mha_dense_small(dsa, ora, L, H):
     _check(ora, q, kv, w_uk, w_uv, idx.numpy(), g, gl, np.arange(L), cfg.sm_scale, f"masked mha dense L={L}")
 
 
+def test_masked_mha_reference_overshoot(dsa, ora):
+    """The first 64 latent rows scaled by 2^-6: a query's first tile of keys
+    sits tens of nats below its later keys, so probabilities against the
+    first tile's max leave fp16's range and the workgroups take the exact
+    two-walk path (maxima first, then the sums)."""
+    L, H = 700, 4
+    _say(f"masked mha reference overshoot L={L} H={H}")
+    cfg, q, kv, w_uk, w_uv = _inputs(L, H, 33, 8.0, selector=True)
+    kv = kv.clone()
+    kv[:64] = (kv[:64].float() * 2.0 ** -6).to(torch.bfloat16)
+    k = 1024
+    idx = torch.full((L, k), -1, dtype=torch.int32)
+    for t in range(L):
+        idx[t, :t + 1] = torch.arange(t + 1)
+    g, gl = _run(dsa, q, kv, w_uk, w_uv, idx, cfg.sm_scale)
+    assert np.isfinite(g).all() and np.isfinite(gl).all()
+    rows = np.unique(np.concatenate([np.arange(0, L, 23), [0, 31, 32, 63, 64, 127, 128, L - 1]]))
+    _check(ora, q, kv, w_uk, w_uv, idx.numpy(), g, gl, rows, cfg.sm_scale, "masked mha overshoot")
+
+
 def _prefill_selection(dsa, cfg):
     """The library's fused FP8 indexer + top-k selection of one sequence."""
     L = cfg.L
