@@ -13,7 +13,9 @@ prefill tokens/s = L * K / wall time of K steps (inputs resident in HBM).
 Also reported (one JSON line): per-kernel HIP-event times and their roofline
 fractions, decode tokens/s for B = 64 sequences at context 32768 and for the
 ragged paged batch (B = 128, context 4096..131072, shuffled 64-token pages),
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+short prefill (L = 4096) through the masked-MHA mode next to the same
+selection through sparse MLA, and the fp64 CPU oracle timed on a bounded
+sample of the headline workload.
 
 Inputs are synthetic (synth), drawn on the GPU with the same counter-based
 generator the oracle side uses.
@@ -44,6 +46,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=30)
     ap.add_argument("--no-decode", action="store_true", help="prefill only")
     ap.add_argument("--no-paged", action="store_true", help="skip the ragged paged decode batch")
+    ap.add_argument("--no-short", action="store_true", help="skip the short-prefill (masked MHA) section")
+    ap.add_argument("--short-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="query rows in the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -221,6 +225,87 @@ def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
     return res
 
 
+# --------------------------------------------------------------------------- short prefill
+def run_short_prefill(torch, dsa, synth, cfg, dev, steps, warmup):
+    """One causal sequence of cfg.L tokens: quantise + fused indexer/top-k, then
+    attention over the selection either through the masked-MHA mode (per-head
+    K/V up-projected from the latent, dense causal tiles under the top-k mask)
+    or through sparse MLA in MQA mode (absorbed queries over the 576-d latent)."""
+    L, H = cfg.L, cfg.H
+    q_i, k_i, w = synth.prefill_indexer_inputs(cfg, device=dev)
+    t = {"qi": q_i.view(L, -1), "ki": k_i, "w": w}
+    t["q8"] = torch.empty((L, cfg.H_I, cfg.D_I), dtype=torch.uint8, device=dev)
+    t["qs"] = torch.empty(L, dtype=torch.float32, device=dev)
+    t["k8"] = torch.empty((L, cfg.D_I), dtype=torch.uint8, device=dev)
+    t["ks"] = torch.empty(L, dtype=torch.float32, device=dev)
+    t["idx"] = torch.empty((L, cfg.k), dtype=torch.int32, device=dev)
+    args = dsa.make_prefill_args(L, cfg.H_I, cfg.D_I, H, cfg.k, dsa.DSA_E4M3, t["q8"], t["qs"], t["k8"], t["ks"],
+                                 t["w"], dsa.DSA_BF16, None, None, cfg.sm_scale, t["idx"], None, None)
+    t["sel_ws"] = torch.empty(dsa.dsa_prefill_workspace_bytes(args), dtype=torch.uint8, device=dev)
+    t["q"] = synth.mha_query(cfg, device=dev)
+    t["kv"] = synth.prefill_latent(cfg, device=dev)
+    t["w_uk"], t["w_uv"] = synth.mha_up_weights(cfg, device=dev)
+    t["out"] = torch.empty((L, H, synth.MHA_DV), dtype=torch.bfloat16, device=dev)
+    t["lse"] = torch.empty((L, H), dtype=torch.float32, device=dev)
+    t["mha_ws"] = torch.empty(dsa.dsa_masked_mha_workspace_bytes(L, H), dtype=torch.uint8, device=dev)
+    t["q_mqa"] = synth.prefill_attn_q(cfg, device=dev)
+    t["out_mqa"] = torch.empty((L, H, 512), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(evs, mode):
+        evs[0].record(stream)
+        dsa.dsa_quantize_e4m3_per_token(t["qi"], t["q8"], t["qs"], rows=L, cols=cfg.H_I * cfg.D_I, stream=stream)
+        dsa.dsa_quantize_e4m3_per_token(t["ki"], t["k8"], t["ks"], rows=L, cols=cfg.D_I, stream=stream)
+        evs[1].record(stream)
+        dsa.dsa_prefill_select(args, t["sel_ws"], stream=stream)
+        evs[2].record(stream)
+        if mode == "mha":
+            dsa.dsa_masked_mha_prefill(t["q"], t["kv"], t["w_uk"], t["w_uv"], t["idx"], cfg.sm_scale, t["out"],
+                                       t["mha_ws"], t["lse"], stream=stream)
+        else:
+            dsa.dsa_sparse_mla_fwd(t["q_mqa"], t["kv"], t["idx"], cfg.sm_scale, t["out_mqa"], t["lse"],
+                                   stream=stream)
+        evs[3].record(stream)
+
+    res = {}
+    for mode in ("mha", "mqa"):
+        st = Stages(torch, ["quantize", "indexer_topk", "attention"])
+        for _ in range(warmup):
+            step(st.new(), mode)
+        torch.cuda.synchronize()
+        all_evs = [st.new() for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(all_evs[i], mode)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for e in all_evs:
+            st.add(e)
+        ms = st.avg_ms()
+        res[mode] = {"tokens_per_s": round(L * steps / wall, 1), "ms_per_step": round(wall / steps * 1e3, 3),
+                     "stages_ms": {k: round(v, 4) for k, v in ms.items()}}
+    # algorithmic work of the masked-MHA mode: per-head K/V up-projection, then
+    # dense causal attention (logits over 192 dims, values over 128) under the mask
+    causal = L * (L + 1) // 2
+    up_flop = 2 * L * H * (synth.MHA_DN + synth.MHA_DV) * synth.MHA_DC
+    att_flop = 2 * causal * H * (synth.MHA_DN + synth.MHA_DR + synth.MHA_DV)
+    mha_ms = res["mha"]["stages_ms"]["attention"]
+    tf = (up_flop + att_flop) / (mha_ms / 1e3) / 1e12
+    res["mha"]["roofline"] = dict(_rl("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s"),
+                                  kernel="masked_mha (up-projection + mask + attention)")
+    sel = sum(min(i + 1, cfg.k) for i in range(L))
+    mqa_ms = res["mqa"]["stages_ms"]["attention"]
+    res["mqa"]["roofline"] = dict(_rl("mfma", 2 * sel * H * (576 + 512) / (mqa_ms / 1e3) / 1e12, PEAK_BF16_TFLOPS,
+                                      "TFLOP/s"), kernel="sparse_mla_bf16")
+    res.update({"workload": cfg.name, "L": L, "H": H, "k": cfg.k, "steps": steps,
+                "work": {"mha_upproj_flop": up_flop, "mha_attention_flop": att_flop,
+                         "mqa_flop": 2 * sel * H * (576 + 512)},
+                "attention_speedup_mha_vs_mqa": round(mqa_ms / mha_ms, 3)})
+    del t
+    torch.cuda.empty_cache()
+    return res
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "prefill_indexer_topk_L131072_traffic.json")
 
 
@@ -381,6 +466,9 @@ def main():
             line["paged_decode"] = run_decode(torch, dsa, synth, synth.CONFIGS["paged"], dev, args.decode_steps, 3,
                                               flush)
         del flush
+    if not args.no_short:
+        print("[bench] short prefill L=4096 (masked MHA and sparse MLA)", file=sys.stderr, flush=True)
+        line["short_prefill"] = run_short_prefill(torch, dsa, synth, synth.CONFIGS["mha4k"], dev, args.short_steps, 3)
     if not args.no_cpu_baseline:
         print(f"[bench] oracle on {args.cpu_rows} sampled rows", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(torch, synth, cfg, args.cpu_rows)
