@@ -10,6 +10,7 @@ Functions follow the plain definitions written out in dsa_oracle.c:
   * top-k under (score desc, position desc),
   * sparse MLA-MQA attention over the selected latent rows,
   * masked multi-head attention in MLA's multi-head form (short-prefill mode),
+  * the indexer's KL-alignment loss per query token,
   * one paged decode query per sequence.
 """
 from __future__ import annotations
@@ -63,6 +64,7 @@ def lib():
                                           P, i64, P, P]
         L.ora_masked_mha_rows.argtypes = [ctypes.c_int, P, P, P, P, P, i32, i32, i32, i32, i32, i32, dbl,
                                           P, i64, P, P]
+        L.ora_indexer_kl_rows.argtypes = [ctypes.c_int, P, P, P, P, i32, i32, i32, dbl, P, i64, P, P]
         L.ora_decode.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                  dbl, P, i64, P, P, P, P]
         _lib = L
@@ -211,6 +213,25 @@ def masked_mha_rows(q, kv, w_uk, w_uv, idx, sm_scale, rows=None, Dr=64):
     lib().ora_masked_mha_rows(dt, _p(q), _p(kv), _p(w_uk), _p(w_uv), _p(idx), H, k, Dc, Dr, Dn, Dvh,
                               float(sm_scale), _p(rows), len(rows), _p(o), _p(lse))
     return o, lse
+
+
+def indexer_kl_rows(q, kv, idx, scores, sm_scale, rows=None):
+    """Per-token KL(p || pi) of the indexer against the head-averaged main
+    attention over the valid entries of idx.  q [T, H, Dqk], kv [N, Dqk]
+    (fp32, bf16 or fp64, one dtype), idx [T, k], scores [T, k] (index scores
+    of the entries) -> (kl [n], mag [n]) fp64, mag = sum_a p_a |log p_a - log pi_a|."""
+    q, kv, idx, sc = _np(q), _np(kv), _np(idx, np.int32), _np(scores, np.float64)
+    dt = _dtype_code(q)
+    assert _dtype_code(kv) == dt and dt in (F32, BF16, F64)
+    T, H, Dqk = q.shape
+    k = idx.shape[1]
+    assert sc.shape == idx.shape and kv.shape[1] == Dqk
+    rows = np.arange(T, dtype=np.int64) if rows is None else _np(rows, np.int64)
+    kl = np.empty(len(rows), dtype=np.float64)
+    mag = np.empty(len(rows), dtype=np.float64)
+    lib().ora_indexer_kl_rows(dt, _p(q), _p(kv), _p(idx), _p(sc), H, k, Dqk, float(sm_scale), _p(rows), len(rows),
+                              _p(kl), _p(mag))
+    return kl, mag
 
 
 # ------------------------------------------------------------------ decode

@@ -40,6 +40,15 @@
  *    128, plus the shared 64 rope dims) and value (the latent up-projected to
  *    128), and attends densely over its causal positions with every position
  *    outside the query's top-k selection masked out.
+ *  - the indexer's KL-alignment loss (mizuki-eaf.pages.dev, two-stage
+ *    continued pre-training; m.36881.com.cn, dense warm-up and sparse
+ *    training; m.digipub.cc, section 2) is read per query token t as
+ *    KL(p_t || pi_t) over a set S_t of positions: p_t is the main attention
+ *    distribution of t over S_t aggregated over heads (the heads' softmaxes
+ *    summed and L1-normalised, i.e. averaged), pi_t the softmax of t's index
+ *    scores over S_t.  S_t is the top-k selection in sparse training and all
+ *    causal positions in the dense warm-up.  The loss value is per token; how
+ *    tokens are summed or averaged is left to the caller.
  *
  * Every floating-point accumulation here is fp64, in the plain loop order of
  * the definition; nothing is blocked, fused or reordered.
@@ -329,6 +338,89 @@ void ora_sparse_mla_rows(int dtype, const void *q, const void *kv, const int32_t
         }
         free(z);
         free(qh);
+    }
+}
+
+/* ------------------------------------------------ indexer KL-alignment loss */
+
+/*
+ * Per-token KL(p_t || pi_t) for selected query rows.
+ *   q [T, H, Dqk], kv [N, Dqk] (F32, BF16 or F64); idx [T, k] rows of kv
+ *   (-1 entries are skipped); scores [T, k] fp64: the index score of each
+ *   entry (ignored where idx is -1).
+ * For t = rows[i], over the valid entries r_1..r_m of idx[t]:
+ *   z_{h,a}  = sm_scale * q[t,h,:] . kv[r_a,:]
+ *   p_a      = (1/H) sum_h softmax_a(z_{h,.})        (main attention, heads averaged)
+ *   pi_a     = softmax_a(scores[t,a])                 (indexer distribution)
+ *   kl[i]    = sum_a p_a (log p_a - log pi_a)         (natural log; terms with p_a = 0 add 0)
+ *   mag[i]   = sum_a p_a |log p_a - log pi_a|         (the same sum of magnitudes)
+ * m = 0 gives kl = mag = 0.
+ */
+void ora_indexer_kl_rows(int dtype, const void *q, const void *kv, const int32_t *idx, const double *scores,
+                         int32_t H, int32_t k, int32_t Dqk, double sm_scale, const int64_t *rows, int64_t nrows,
+                         double *kl, double *mag)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        const int64_t t = rows[i];
+        const int32_t *sel = idx + t * (int64_t)k;
+        const double *sc = scores + t * (int64_t)k;
+        double *z = (double *)malloc(sizeof(double) * (size_t)k);
+        double *pa = (double *)calloc((size_t)k, sizeof(double));
+        double smax = -INFINITY, ssum = 0.0, lse_i, acc = 0.0, accm = 0.0;
+        int32_t a, h, d, m = 0;
+        for (a = 0; a < k; ++a)
+            if (sel[a] >= 0)
+                ++m;
+        if (m == 0) {
+            kl[i] = 0.0;
+            mag[i] = 0.0;
+            free(z);
+            free(pa);
+            continue;
+        }
+        /* main attention: each head's softmax over the valid entries, averaged */
+        for (h = 0; h < H; ++h) {
+            double mx = -INFINITY, sum = 0.0;
+            for (a = 0; a < k; ++a) {
+                double dot = 0.0;
+                const int64_t r = sel[a];
+                if (r < 0)
+                    continue;
+                for (d = 0; d < Dqk; ++d)
+                    dot += elem(dtype, q, (t * H + h) * (int64_t)Dqk + d) * elem(dtype, kv, r * Dqk + d);
+                z[a] = sm_scale * dot;
+                if (z[a] > mx)
+                    mx = z[a];
+            }
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    sum += exp(z[a] - mx);
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    pa[a] += exp(z[a] - mx) / sum / H;
+        }
+        /* indexer distribution: log-softmax of the scores over the valid entries */
+        for (a = 0; a < k; ++a)
+            if (sel[a] >= 0 && sc[a] > smax)
+                smax = sc[a];
+        for (a = 0; a < k; ++a)
+            if (sel[a] >= 0)
+                ssum += exp(sc[a] - smax);
+        lse_i = smax + log(ssum);
+        for (a = 0; a < k; ++a) {
+            double term;
+            if (sel[a] < 0 || pa[a] == 0.0)
+                continue;
+            term = pa[a] * (log(pa[a]) - (sc[a] - lse_i));
+            acc += term;
+            accm += fabs(term);
+        }
+        kl[i] = acc;
+        mag[i] = accm;
+        free(z);
+        free(pa);
     }
 }
 

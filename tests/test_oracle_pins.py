@@ -478,3 +478,99 @@ def test_page_constants_fix_k_and_context():
         assert synth.CONFIGS[name].k == g["top_k"]
     assert synth.CONFIGS["prefill128k"].L == ctx
     assert synth.CONFIGS["paged"].ctx_hi == ctx
+
+
+# ------------------------------------------------ indexer KL-alignment loss
+def _kl_inputs(seed, T, N, H, D, k, q_std=1.0):
+    q = synth.normal(seed, 1, (T, H, D), std=q_std).double()
+    kv = synth.normal(seed, 2, (N, D), std=0.5).double()
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        m = 2 + (3 * t) % (k - 1)
+        idx[t, :m] = synth.permutation(seed, 10 + t, N)[:m].numpy()
+    scores = synth.normal(seed, 3, (T, k), std=2.0).double().numpy()
+    return q, kv, idx, scores
+
+
+def _head_avg_attention(q, kv, sel, scale):
+    """p over the entries sel of one query: per-head softmax (torch), averaged over heads."""
+    z = scale * torch.einsum("hd,ad->ha", q, kv[torch.from_numpy(sel).long()])
+    return torch.softmax(z, dim=1).mean(dim=0).numpy()
+
+
+def test_indexer_kl_matches_scipy_relative_entropy(ora):
+    """KL(p || pi) against scipy's relative entropy, with p from torch's softmax
+    averaged over heads and pi from torch's softmax of the scores."""
+    import scipy.stats
+    T, N, H, D, k = 7, 40, 3, 12, 9
+    q, kv, idx, sc = _kl_inputs(21, T, N, H, D, k)
+    kl, mag = ora.indexer_kl_rows(q, kv, idx, sc, 0.3)
+    for t in range(T):
+        valid = idx[t] >= 0
+        p = _head_avg_attention(q[t], kv, idx[t][valid], 0.3)
+        pi = torch.softmax(torch.from_numpy(sc[t][valid]), dim=0).numpy()
+        ref = scipy.stats.entropy(p, pi)
+        assert abs(kl[t] - ref) <= 1e-12 * max(1.0, abs(ref))
+        assert kl[t] >= 0.0 and mag[t] >= kl[t] - 1e-15
+
+
+def test_indexer_kl_zero_when_scores_are_the_logits(ora):
+    """One head whose logits are the index scores: p = pi, so the loss is 0."""
+    T, N, D, k = 6, 30, 16, 8
+    q, kv, idx, _ = _kl_inputs(22, T, N, 1, D, k)
+    sc = np.zeros((T, k))
+    for t in range(T):
+        valid = idx[t] >= 0
+        sc[t, valid] = (0.4 * (kv[torch.from_numpy(idx[t][valid]).long()] @ q[t, 0])).numpy()
+        sc[t, ~valid] = np.nan  # ignored entries
+    kl, mag = ora.indexer_kl_rows(q, kv, idx, sc, 0.4)
+    assert np.all(np.abs(kl) < 1e-13) and np.all(mag < 1e-12)
+
+
+def test_indexer_kl_two_entries_is_bernoulli_kl(ora):
+    """Two entries and one head: KL of two Bernoulli distributions, closed form."""
+    q, kv, _, _ = _kl_inputs(23, 1, 5, 1, 10, 4, q_std=2.0)
+    idx = np.array([[3, -1, 1, -1]], np.int32)
+    sc = np.array([[0.7, 5.0, -1.3, 9.0]])
+    kl, _ = ora.indexer_kl_rows(q, kv, idx, sc, 0.5)
+    z3, z1 = (0.5 * (kv[3] @ q[0, 0])).item(), (0.5 * (kv[1] @ q[0, 0])).item()
+    p = 1.0 / (1.0 + math.exp(z1 - z3))
+    pi = 1.0 / (1.0 + math.exp(-1.3 - 0.7))
+    ref = p * math.log(p / pi) + (1 - p) * math.log((1 - p) / (1 - pi))
+    assert abs(kl[0] - ref) <= 1e-13
+
+
+def test_indexer_kl_uniform_indexer_is_log_m_minus_entropy(ora):
+    """Equal index scores: KL(p || uniform) = log m - entropy(p)."""
+    import scipy.stats
+    T, N, H, D, k = 5, 50, 4, 8, 12
+    q, kv, idx, _ = _kl_inputs(24, T, N, H, D, k, q_std=3.0)
+    sc = np.full((T, k), 1.25)
+    kl, _ = ora.indexer_kl_rows(q, kv, idx, sc, 0.2)
+    for t in range(T):
+        valid = idx[t] >= 0
+        p = _head_avg_attention(q[t], kv, idx[t][valid], 0.2)
+        ref = math.log(valid.sum()) - scipy.stats.entropy(p)
+        assert abs(kl[t] - ref) <= 1e-12
+
+
+def test_indexer_kl_invariances(ora):
+    """Shifting every score by a constant, permuting the entries together with
+    their scores, appending padding, and duplicating every head change nothing;
+    an empty selection gives 0."""
+    T, N, H, D, k = 6, 40, 2, 10, 7
+    q, kv, idx, sc = _kl_inputs(25, T, N, H, D, k)
+    kl, _ = ora.indexer_kl_rows(q, kv, idx, sc, 0.3)
+    kl_shift, _ = ora.indexer_kl_rows(q, kv, idx, sc + 17.5, 0.3)
+    np.testing.assert_allclose(kl_shift, kl, rtol=1e-11, atol=1e-13)
+    perm = synth.permutation(25, 99, k).numpy()
+    kl_perm, _ = ora.indexer_kl_rows(q, kv, idx[:, perm], sc[:, perm], 0.3)
+    np.testing.assert_allclose(kl_perm, kl, rtol=1e-11, atol=1e-13)
+    idx_pad = np.concatenate([idx, np.full((T, 5), -1, np.int32)], axis=1)
+    sc_pad = np.concatenate([sc, np.full((T, 5), 1e9)], axis=1)
+    kl_pad, _ = ora.indexer_kl_rows(q, kv, idx_pad, sc_pad, 0.3)
+    np.testing.assert_allclose(kl_pad, kl, rtol=1e-13, atol=0)
+    kl_dup, _ = ora.indexer_kl_rows(torch.cat([q, q], dim=1), kv, idx, sc, 0.3)
+    np.testing.assert_allclose(kl_dup, kl, rtol=1e-11, atol=1e-13)
+    kl_empty, mag_empty = ora.indexer_kl_rows(q[:1], kv, np.full((1, k), -1, np.int32), sc[:1], 0.3)
+    assert kl_empty[0] == 0.0 and mag_empty[0] == 0.0
