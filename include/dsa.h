@@ -135,6 +135,43 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Index scores at listed positions: the scores a selection ranked, as the
+ * indexer's KL loss needs them.  out[t, a] = I[t, idx[t, a]] with the E4M3
+ * arithmetic of dsa_indexer_scores (same expression, bit-identical values),
+ * and -inf where idx[t, a] is outside [0, S).  No causal check is made.
+ *   q8 [T, H_I, D_I] E4M3 + q_scale [T], k8 [S, D_I] E4M3 + k_scale [S],
+ *   w [T, H_I] fp32, idx [T, k] int32, out [T, k] fp32.
+ * Limits: D_I = 128, H_I 32 or 64, S >= 1.
+ */
+dsa_status dsa_indexer_scores_at(const uint8_t *q8, const float *q_scale, const uint8_t *k8, const float *k_scale,
+                                 const float *w, const int32_t *idx, int32_t T, int32_t S, int32_t H_I, int32_t D_I,
+                                 int32_t k, float *out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Indexer KL-alignment loss, forward.  In both continued-pre-training
+ * stages a KL loss aligns the indexer's output distribution with the main
+ * attention's (mizuki-eaf.pages.dev, two-stage continued pre-training;
+ * m.36881.com.cn, dense warm-up and sparse training).  Per query t, over the
+ * valid entries a of idx[t] (the top-k selection in sparse training; all
+ * causal positions in the dense warm-up):
+ *   p_a  = (1/H) sum_h softmax_a(sm_scale q[t,h] . kv[idx[t,a]])   heads averaged
+ *   pi_a = softmax_a(idx_scores[t, a])
+ *   kl[t] = sum_a p_a (log p_a - log pi_a)   (natural log; 0 with no valid entry)
+ *   q [T, H, 576] BF16, kv [N, 576] BF16, idx [T, k] rows of kv (entries
+ *   outside [0, N) are skipped), idx_scores [T, k] fp32 (dsa_indexer_scores_at),
+ *   lse [T, H] fp32: each head's natural-log log-sum-exp over the same
+ *   entries (the lse output of dsa_sparse_mla_fwd on this idx), kl [T] fp32.
+ * Each head's softmax is taken against lse; the head sum is then normalised
+ * by its own total, so p sums to one whatever small error lse carries.
+ * Logits are bf16 MFMA with fp32 sums; exponentials, logs and sums are fp32.
+ * How the per-token values are summed or averaged is left to the caller.
+ * Limits: H one of 16, 32, 64, 128; k <= 2048.
+ */
+dsa_status dsa_indexer_kl_fwd(const void *q, const void *kv, const int32_t *idx, const float *idx_scores,
+                              const float *lse, int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *kl,
+                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Masked multi-head attention for short prefill (the mode that stands in for
  * DSA on short sequences: mizuki-eaf.pages.dev, "parity evaluation";
  * m.digipub.cc, section 2).  MLA in its multi-head form over one causal

@@ -159,6 +159,33 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
   return fail(DSA_ERR_UNSUPPORTED, "sparse MLA dtype must be BF16 or F32");
 }
 
+dsa_status dsa_indexer_scores_at(const uint8_t *q8, const float *q_scale, const uint8_t *k8, const float *k_scale,
+                                 const float *w, const int32_t *idx, int32_t T, int32_t S, int32_t H_I, int32_t D_I,
+                                 int32_t k, float *out, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0 && S >= 1 && k >= 1, DSA_ERR_INVALID_ARG, "need T >= 0, S >= 1, k >= 1");
+  REQUIRE(D_I == 128 && (H_I == 32 || H_I == 64), DSA_ERR_UNSUPPORTED, "E4M3 index scores need D_I = 128 and H_I 32 or 64");
+  if (T == 0) return DSA_OK;
+  REQUIRE(q8 && q_scale && k8 && k_scale && w && idx && out, DSA_ERR_INVALID_ARG, "null pointer");
+  return hip_check(launch_indexer_scores_at(q8, q_scale, k8, k_scale, w, idx, T, S, H_I, k, out, stream),
+                   "indexer scores-at launch");
+}
+
+dsa_status dsa_indexer_kl_fwd(const void *q, const void *kv, const int32_t *idx, const float *idx_scores,
+                              const float *lse, int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *kl,
+                              hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0 && N >= 0, DSA_ERR_INVALID_ARG, "T and N must be >= 0");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(H == 16 || H == 32 || H == 64 || H == 128, DSA_ERR_UNSUPPORTED, "KL loss needs H in {16, 32, 64, 128} (got %d)", H);
+  REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (T == 0) return DSA_OK;
+  REQUIRE(q && kv && idx && idx_scores && lse && kl, DSA_ERR_INVALID_ARG, "null pointer");
+  return hip_check(launch_indexer_kl(q, kv, idx, idx_scores, lse, N, T, H, k, sm_scale, kl, stream),
+                   "indexer KL launch");
+}
+
 size_t dsa_masked_mha_workspace_bytes(int32_t L, int32_t H) {
   if (L <= 0 || H <= 0) return 0;
   return masked_mha_workspace_bytes(L, H);

@@ -122,6 +122,13 @@ size_t masked_mha_workspace_bytes(int32_t L, int32_t H);
 hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, const void *w_uv,
                              const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale, void *out,
                              float *lse, void *workspace, hipStream_t s);
+// Index scores at listed positions (E4M3, D_I = 128, H_I 32 or 64) and the
+// indexer KL-alignment loss (H / 16 in {1, 2, 4, 8}, k <= 2048).
+hipError_t launch_indexer_scores_at(const uint8_t *q8, const float *qs, const uint8_t *k8, const float *ks,
+                                    const float *w, const int32_t *idx, int32_t T, int32_t S, int32_t H_I, int32_t k,
+                                    float *out, hipStream_t s);
+hipError_t launch_indexer_kl(const void *q, const void *kv, const int32_t *idx, const float *scores, const float *lse,
+                             int64_t N, int32_t T, int32_t H, int32_t k, float sm_scale, float *kl, hipStream_t s);
 hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStream_t s);
 hipError_t launch_cache_append(const void *latent, const uint8_t *k8, const float *ks,
                                const int32_t *pos, int32_t B, int32_t D_I,

@@ -25,7 +25,7 @@ EXPORTS = (
     "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_fwd", "dsa_prefill_workspace_bytes", "dsa_prefill",
     "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
     "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd", "dsa_masked_mha_workspace_bytes",
-    "dsa_masked_mha_prefill",
+    "dsa_masked_mha_prefill", "dsa_indexer_scores_at", "dsa_indexer_kl_fwd",
 )
 
 
@@ -86,7 +86,9 @@ def load():
     L.dsa_masked_mha_workspace_bytes.argtypes = [_I32, _I32]
     L.dsa_masked_mha_workspace_bytes.restype = _SZ
     L.dsa_masked_mha_prefill.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]
-    for name in ("dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
+    L.dsa_indexer_scores_at.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]
+    L.dsa_indexer_kl_fwd.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P]
+    for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
                  "dsa_prefill", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
                  "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd"):
         getattr(L, name).restype = ctypes.c_int
@@ -176,6 +178,22 @@ def dsa_masked_mha_prefill(q, kv, w_uk, w_uv, idx, sm_scale, out, workspace, lse
     _check(load().dsa_masked_mha_prefill(_ptr(q), _ptr(kv), _ptr(w_uk), _ptr(w_uv), _ptr(idx), L, H, k,
                                          float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                          _stream(stream)))
+
+
+def dsa_indexer_scores_at(q8, q_scale, k8, k_scale, w, idx, out, S=None, stream=None):
+    """I[t, idx[t, a]] for E4M3 q8 [T, H_I, 128], k8 [S, 128] -> out [T, k] fp32."""
+    T, H_I, D_I = q8.shape
+    S = k8.shape[0] if S is None else S
+    _check(load().dsa_indexer_scores_at(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(w), _ptr(idx), T, S,
+                                        H_I, D_I, idx.shape[1], _ptr(out), _stream(stream)))
+
+
+def dsa_indexer_kl_fwd(q, kv, idx, idx_scores, lse, sm_scale, kl, N=None, stream=None):
+    """Per-token KL(p || pi): q [T, H, 576], kv [N, 576] bf16, idx/idx_scores [T, k], lse [T, H] -> kl [T]."""
+    T, H = q.shape[0], q.shape[1]
+    N = kv.shape[0] if N is None else N
+    _check(load().dsa_indexer_kl_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(idx_scores), _ptr(lse), T, H, N,
+                                     idx.shape[1], float(sm_scale), _ptr(kl), _stream(stream)))
 
 
 def make_prefill_args(L, H_I, D_I, H, k, idx_dt, q_idx, q_scale, k_idx, k_scale, w, attn_dt, q, kv, sm_scale,

@@ -164,6 +164,38 @@ def test_masked_mha_validation(dsa):
     assert f(*b) == dsa.DSA_OK
 
 
+def test_indexer_kl_validation(dsa):
+    L = dsa.load()
+    f = L.dsa_indexer_kl_fwd
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 5000, 2048, 0.07, FAKE, None]
+    b = list(base)
+    b[6] = 48  # H not in {16, 32, 64, 128}
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[8] = 2049
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[3] = None  # scores
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[9] = 0.0
+    assert f(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(base)
+    b[5] = 0
+    assert f(*b) == dsa.DSA_OK
+    g = L.dsa_indexer_scores_at
+    gb = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 5000, 64, 128, 2048, FAKE, None]
+    b = list(gb)
+    b[8] = 16
+    assert g(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(gb)
+    b[7] = 0
+    assert g(*b) == dsa.DSA_ERR_INVALID_ARG
+    b = list(gb)
+    b[11] = None
+    assert g(*b) == dsa.DSA_ERR_INVALID_ARG
+
+
 def test_prefill_validation(dsa):
     L = dsa.load()
     a = dsa.make_prefill_args(1000, 64, 128, 128, 2048, dsa.DSA_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE, dsa.DSA_BF16,
