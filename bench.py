@@ -14,8 +14,9 @@ Also reported (one JSON line): per-kernel HIP-event times and their roofline
 fractions, decode tokens/s for B = 64 sequences at context 32768 and for the
 ragged paged batch (B = 128, context 4096..131072, shuffled 64-token pages),
 short prefill (L = 4096) through the masked-MHA mode next to the same
-selection through sparse MLA, and the fp64 CPU oracle timed on a bounded
-sample of the headline workload.
+selection through sparse MLA, the indexer's KL-alignment loss forward on the
+headline selection (the step beside the path in sparse training), and the
+fp64 CPU oracle timed on a bounded sample of the headline workload.
 
 Inputs are synthetic (synth), drawn on the GPU with the same counter-based
 generator the oracle side uses.
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="prefill only")
     ap.add_argument("--no-paged", action="store_true", help="skip the ragged paged decode batch")
     ap.add_argument("--no-short", action="store_true", help="skip the short-prefill (masked MHA) section")
+    ap.add_argument("--no-kl", action="store_true", help="skip the indexer KL-loss section")
+    ap.add_argument("--kl-steps", type=int, default=3)
     ap.add_argument("--short-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="query rows in the oracle sample")
@@ -222,6 +225,45 @@ def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
     }
     del t
     torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------- KL loss
+def run_kl(torch, dsa, cfg, t, dev, steps):
+    """The indexer KL-alignment loss forward on the headline step's own outputs:
+    index scores at the selected positions, then the per-token loss against
+    the head-averaged attention (each head against the sparse-MLA lse)."""
+    L, k = cfg.L, cfg.k
+    sc = torch.empty((L, k), dtype=torch.float32, device=dev)
+    kl = torch.empty(L, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    st = Stages(torch, ["scores_at", "kl"])
+    for i in range(steps + 1):
+        evs = st.new()
+        evs[0].record(stream)
+        dsa.dsa_indexer_scores_at(t["q8"], t["qs"], t["k8"], t["ks"], t["w"], t["idx"], sc, stream=stream)
+        evs[1].record(stream)
+        dsa.dsa_indexer_kl_fwd(t["q"], t["kv"], t["idx"], sc, t["lse"], cfg.sm_scale, kl, stream=stream)
+        evs[2].record(stream)
+        torch.cuda.synchronize()
+        if i > 0:
+            st.add(evs)
+    ms = st.avg_ms()
+    selected = prefill_work(cfg)["selected_pairs"]
+    sa_flop = 2 * cfg.H_I * cfg.D_I * selected
+    kl_flop = 2 * cfg.H * 576 * selected
+    res = {
+        "workload": cfg.name, "L": L, "H": cfg.H, "k": k, "steps": steps,
+        "stages_ms": {n: round(v, 3) for n, v in ms.items()},
+        "tokens_per_s": round(L / ((ms["scores_at"] + ms["kl"]) / 1e3), 1),
+        "mean_kl": float(kl.double().mean()),
+        "roofline": {
+            "scores_at": _rl("mfma", sa_flop / (ms["scores_at"] / 1e3) / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"),
+            "kl": _rl("mfma", kl_flop / (ms["kl"] / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
+        },
+        "work": {"scores_at_flop": sa_flop, "kl_flop": kl_flop, "selected_pairs": selected},
+    }
+    del sc, kl
     return res
 
 
@@ -440,6 +482,9 @@ def main():
         },
         "work": work,
     }
+    if not args.no_kl:
+        print("[bench] indexer KL loss on the headline selection", file=sys.stderr, flush=True)
+        line["kl_loss"] = run_kl(torch, dsa, cfg, t, dev, args.kl_steps)
     if args.calibrate_copy:
         # plain copies of known size for scaling HBM counters: the runtime's
         # device copy, then an elementwise kernel (vector loads and stores)
