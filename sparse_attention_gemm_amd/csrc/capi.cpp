@@ -5,7 +5,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "dsa_common.h"
+#include "dsa_launch.h"
 
 namespace dsa {
 static thread_local char g_err[512];

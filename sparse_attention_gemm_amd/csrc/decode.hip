@@ -12,6 +12,7 @@
 // registers and scores kPagesPerWave pages (64 keys, 8 KB contiguous in the
 // pool, each read exactly once), loading the next page's keys while it
 // computes the current one.
+#include "dsa_launch.h"
 #include "indexer_core.h"
 
 namespace {

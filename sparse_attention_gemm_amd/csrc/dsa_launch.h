@@ -1,0 +1,64 @@
+// dsa_launch.h -- host-side launchers of the library's kernels and the
+// C ABI layer's helpers (status, messages).  Each launcher enqueues its
+// kernels on the given stream and validates nothing: the C ABI layer does.
+#pragma once
+#include "dsa_common.h"
+
+namespace dsa {
+dsa_status fail(dsa_status st, const char *fmt, ...);
+dsa_status hip_check(hipError_t e, const char *what);
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Launchers (each validates nothing: the C ABI layer does).
+hipError_t launch_quantize(const float *x, int64_t rows, int32_t cols, uint8_t *x8, float *scale,
+                           hipStream_t s);
+hipError_t launch_indexer_scores_fp8(const uint8_t *q, const float *qs, const uint8_t *k,
+                                     const float *ks, const float *w, const int32_t *q_pos,
+                                     int32_t T, int32_t S, int32_t H_I, float *scores, int64_t ld,
+                                     hipStream_t s);
+hipError_t launch_indexer_scores_f32(const float *q, const float *k, const float *w,
+                                     const int32_t *q_pos, int32_t T, int32_t S, int32_t H_I,
+                                     int32_t D_I, float *scores, int64_t ld, hipStream_t s);
+// Rows take min(n_valid[t], n_cap) candidates (n_cap guards the row length).
+hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
+                       int32_t k, int32_t *idx, hipStream_t s);
+// Fused prefill selection; cand: prefill_candidate_bytes(L) of scratch.
+size_t prefill_candidate_bytes(int32_t L);
+hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const uint8_t *k8,
+                                       const float *ks, const float *w, int32_t L, int32_t k,
+                                       int32_t *idx, uint32_t *cand, hipStream_t s);
+// Sparse MLA.  block_table != NULL: idx holds logical positions of sequence
+// t (page size 64); otherwise idx holds rows of kv.  Entries that do not map
+// to a row in [0, N) are skipped like -1.  splits > 1 needs the
+// partial buffers (part_o [T,splits,H,512] f32, part_ml [T,splits,H,2] f32).
+hipError_t launch_sparse_mla_bf16(const void *q, const void *kv, const int32_t *idx,
+                                  const int32_t *block_table, int32_t max_blocks, int64_t N, int32_t T,
+                                  int32_t H, int32_t k, float sm_scale, void *out, float *lse,
+                                  int32_t splits, void *part_o, float *part_ml, hipStream_t s);
+hipError_t launch_sparse_mla_f32(const float *q, const float *kv, const int32_t *idx, int64_t N, int32_t T,
+                                 int32_t H, int32_t k, float sm_scale, float *out, float *lse,
+                                 hipStream_t s);
+hipError_t launch_decode_indexer(const uint8_t *q8, const float *qs, const float *w,
+                                 const uint8_t *k8_pool, const float *ks_pool,
+                                 const int32_t *block_table, int32_t max_blocks,
+                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, int64_t n_pool_rows,
+                                 float *scores, int64_t ld, hipStream_t s);
+// Masked MHA in MLA's multi-head form (BF16; per head 128 + 64 logit dims,
+// 128 value dims, latent 512 + 64).  workspace: masked_mha_workspace_bytes(L, H).
+size_t masked_mha_workspace_bytes(int32_t L, int32_t H);
+hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, const void *w_uv,
+                             const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale, void *out,
+                             float *lse, void *workspace, hipStream_t s);
+// Index scores at listed positions (E4M3, D_I = 128, H_I 32 or 64) and the
+// indexer KL-alignment loss (H / 16 in {1, 2, 4, 8}, k <= 2048).
+hipError_t launch_indexer_scores_at(const uint8_t *q8, const float *qs, const uint8_t *k8, const float *ks,
+                                    const float *w, const int32_t *idx, int32_t T, int32_t S, int32_t H_I, int32_t k,
+                                    float *out, hipStream_t s);
+hipError_t launch_indexer_kl(const void *q, const void *kv, const int32_t *idx, const float *scores, const float *lse,
+                             int64_t N, int32_t T, int32_t H, int32_t k, float sm_scale, float *kl, hipStream_t s);
+hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStream_t s);
+hipError_t launch_cache_append(const void *latent, const uint8_t *k8, const float *ks,
+                               const int32_t *pos, int32_t B, int32_t D_I,
+                               const int32_t *block_table, int32_t max_blocks, int64_t n_pool_rows,
+                               void *kv_pool, uint8_t *k8_pool, float *ks_pool, hipStream_t s);
+}  // namespace dsa

@@ -22,7 +22,7 @@
 //    Latent rows are gathered 32 per tile into LDS with direct-to-LDS loads
 //    (double-buffered); the logits S = Q C^T (bf16 MFMA, fp32 sums) put the
 //    heads along rows, so the head sum is in-lane adds plus permlane swaps.
-#include "dsa_common.h"
+#include "dsa_launch.h"
 #include "indexer_core.h"
 
 namespace {

@@ -26,7 +26,7 @@
 //    and values in fp16.
 #include <algorithm>
 
-#include "dsa_common.h"
+#include "dsa_launch.h"
 
 namespace {
 
@@ -51,91 +51,106 @@ __device__ __forceinline__ f32x4 mfma_f16_16x16x32(const f16x8 &a, const f16x8 &
 __device__ __forceinline__ _Float16 to_f16_sat(float x) { return (_Float16)fminf(fmaxf(x, -65504.0f), 65504.0f); }
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// ------------------------------------------------------------- up-projection
-constexpr int kUpE = 128;    // output dims per workgroup (one head)
-constexpr int kUpT = 128;    // tokens per workgroup
-constexpr int kUpK = 64;     // latent dims per LDS chunk
-constexpr int kUpRow = 144;  // LDS bytes per row of a chunk: 128 + 16 pad (36 dwords: conflict-free reads)
-constexpr int kUpBuf = (kUpE + kUpT) * kUpRow;
-constexpr int kUpLoads = (kUpE + kUpT) * (kUpK * 2 / 16) / 256;  // 16-byte loads per thread per chunk
-static_assert(kUpLoads == 8, "chunk loads per thread");
+// s_waitcnt immediate: at most n vector-memory operations outstanding
+// (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// out[s, h, e] = fp16(sum_c w[h, e, c] kv[s, c]) for one head h (blockIdx.y) and
-// 128 tokens (blockIdx.x); blockIdx.z picks W_uk -> K or W_uv -> V.  The MFMA
-// computes the transpose, D[e][s] = W[e][:] . kv[s][:], so that a lane ends
-// with four consecutive output dims of one token (one 8-byte store).  Wave w
-// owns output dims 64 (w & 1) .. +64 and tokens 64 (w >> 1) .. +64.
-__global__ __launch_bounds__(256) void mha_upproj_kernel(const __bf16 *__restrict__ kv,
+// ------------------------------------------------------------- up-projection
+constexpr int kUpE = 2 * kDn;  // output rows per workgroup: K_h (W_uk[h] rows), then V_h (W_uv[h] rows)
+constexpr int kUpT = 256;      // tokens per workgroup (K_h and V_h rows are padded to a multiple of this)
+constexpr int kUpK = 32;       // latent dims per LDS chunk
+constexpr int kUpSlots = 5;    // LDS row: 4 x 16 B of data + 1 pad (20 dwords: conflict-free 16-B reads)
+constexpr int kUpRow = kUpSlots * 16;
+constexpr int kUpRows = kUpE + kUpT;                       // W rows, then token rows
+constexpr int kUpInsts = kUpRows * kUpSlots / 64;          // 40 wave-wide 1 KB loads per chunk
+static_assert(kUpRows * kUpSlots % 64 == 0 && kUpInsts % 8 == 0, "whole loads, the same count per wave");
+constexpr int kUpStage = kUpInsts * 1024;                  // 40 KB
+constexpr int kUpNBuf = 3;                                 // chunk kc+2 loads while chunk kc is computed
+constexpr int kUpSmem = kUpNBuf * kUpStage;
+constexpr int kUpChunks = kDc / kUpK;                      // 16
+
+// K_h[s, e] = fp16(sum_c w_uk[h, e, c] kv[s, c]) and V_h[s, e] likewise, for
+// one head h (blockIdx.y) and 256 tokens (blockIdx.x): a 256 x 256 x 512 GEMM
+// per workgroup, which reads 512 KB for 67 MFLOP.  The MFMA computes the
+// transpose D[e][s] = W[e][:] . kv[s][:], so a lane ends with four
+// consecutive output dims of one token (one 8-byte store).  Eight waves: wave
+// w owns rows 64 (w & 3) .. +64 (K_h for w & 3 < 2, V_h otherwise) and tokens
+// 128 (w >> 2) .. +128.  Operands reach LDS by direct-to-LDS loads in chunks of
+// 32 latent dims, three chunks deep; token rows past L read row L - 1 and
+// their outputs land in the padding rows.
+__global__ __launch_bounds__(512) void mha_upproj_kernel(const __bf16 *__restrict__ kv,
                                                          const __bf16 *__restrict__ w_uk,
                                                          const __bf16 *__restrict__ w_uv, int L, int H,
                                                          _Float16 *__restrict__ kout, _Float16 *__restrict__ vout) {
-  extern __shared__ __align__(16) uint8_t up_smem[];  // two chunk buffers of kUpBuf bytes
+  extern __shared__ __align__(16) uint8_t up_smem[];  // kUpNBuf chunk buffers of kUpStage bytes
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y;
   const int s0 = blockIdx.x * kUpT;
-  const __bf16 *w = (blockIdx.z == 0 ? w_uk : w_uv) + (int64_t)h * kUpE * kDc;
-  _Float16 *out = blockIdx.z == 0 ? kout : vout;
-  // thread loads: rows 0..127 are W rows (e), 128..255 are token rows; 8
-  // chunks of 16 bytes per row and chunk
-  auto load_chunk = [&](int kc, i32x4 (&r)[kUpLoads]) {
+  // this wave's loads: instruction i = wave + 8 n, slot i*64 + lane -> row slot/5, chunk slot%5
+  const char *src[kUpInsts / 8];
+  {
+    int l = lane;
+    asm volatile("" : "+v"(l));
 #pragma unroll
-    for (int i = 0; i < kUpLoads; ++i) {
-      const int slot = i * 256 + tid;
-      const int row = slot >> 3, part = slot & 7;
-      const __bf16 *src = row < kUpE ? w + (int64_t)row * kDc + kc * kUpK + part * 8
-                                     : kv + (int64_t)min(s0 + row - kUpE, L - 1) * kDl + kc * kUpK + part * 8;
-      r[i] = *reinterpret_cast<const i32x4 *>(src);
+    for (int n = 0; n < kUpInsts / 8; ++n) {
+      const int slot = (wave + 8 * n) * 64 + l;
+      const int row = slot / kUpSlots, j = min(slot % kUpSlots, 3);
+      const __bf16 *p;
+      if (row < kDn)
+        p = w_uk + ((int64_t)h * kDn + row) * kDc;
+      else if (row < kUpE)
+        p = w_uv + ((int64_t)h * kDvh + row - kDn) * kDc;
+      else
+        p = kv + (int64_t)min(s0 + row - kUpE, L - 1) * kDl;
+      src[n] = (const char *)p + j * 16;
     }
-  };
-  auto store_chunk = [&](uint8_t *dst, const i32x4 (&r)[kUpLoads]) {
+  }
+  auto load_chunk = [&](int kc, uint8_t *dst) {
 #pragma unroll
-    for (int i = 0; i < kUpLoads; ++i) {
-      const int slot = i * 256 + tid;
-      *reinterpret_cast<i32x4 *>(dst + (slot >> 3) * kUpRow + (slot & 7) * 16) = r[i];
-    }
+    for (int n = 0; n < kUpInsts / 8; ++n)
+      __builtin_amdgcn_global_load_lds(src[n] + kc * kUpK * 2, (lds_void *)(dst + (wave + 8 * n) * 1024), 16, 0, 0);
   };
-  f32x4 acc[4][4];
+  f32x4 acc[4][8];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int e0 = 64 * (wave & 1), t0 = 64 * (wave >> 1);
-  i32x4 r[kUpLoads];
-  load_chunk(0, r);
-  store_chunk(up_smem, r);
-  __syncthreads();
-  constexpr int nchunks = kDc / kUpK;
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const uint8_t *cur = up_smem + (kc & 1) * kUpBuf;
-    if (kc + 1 < nchunks) load_chunk(kc + 1, r);  // in flight during this chunk's MFMAs
+    for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int e0 = 64 * (wave & 3), t0 = kUpE + 128 * (wave >> 2);  // LDS row of the wave's first W / token row
+  load_chunk(0, up_smem);
+  load_chunk(1, up_smem + kUpStage);
+  int cur = 0, nxt2 = 2 * kUpStage;
+  auto step = [](int b) { return b == (kUpNBuf - 1) * kUpStage ? 0 : b + kUpStage; };
+  for (int kc = 0; kc < kUpChunks; ++kc, cur = step(cur), nxt2 = step(nxt2)) {
+    if (kc + 1 < kUpChunks)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kUpInsts / 8));  // chunk kc landed; chunk kc+1 may be in flight
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave's loads of chunk kc landed; chunk kc-1's buffer is free
+    if (kc + 2 < kUpChunks) load_chunk(kc + 2, up_smem + nxt2);
+    const uint8_t *b = up_smem + cur;
+    bf16x8 a[4];
 #pragma unroll
-    for (int ks = 0; ks < kUpK / 32; ++ks) {
-      bf16x8 a[4], b[4];
+    for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const bf16x8 *>(b + (e0 + 16 * m + c) * kUpRow + g * 16);
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        a[m] = *reinterpret_cast<const bf16x8 *>(cur + (e0 + 16 * m + c) * kUpRow + ks * 64 + g * 16);
+    for (int n = 0; n < 8; ++n) {
+      const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(b + (t0 + 16 * n + c) * kUpRow + g * 16);
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        b[n] = *reinterpret_cast<const bf16x8 *>(cur + (kUpE + t0 + 16 * n + c) * kUpRow + ks * 64 + g * 16);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = mfma_bf16_16x16x32(a[m], b[n], acc[m][n]);
+      for (int m = 0; m < 4; ++m) acc[m][n] = mfma_bf16_16x16x32(a[m], bb, acc[m][n]);
     }
-    if (kc + 1 < nchunks) store_chunk(up_smem + ((kc + 1) & 1) * kUpBuf, r);
-    __syncthreads();
   }
-  // lane (g, c) of tile (m, n): output dims e0 + 16m + 4g .. +4 of token t0 + 16n + c
+  // lane (g, c) of tile (m, n): output dims e0 + 16m + 4g .. +4 of token s0 + 128 (w >> 2) + 16n + c
+  _Float16 *out = (wave & 3) < 2 ? kout : vout;
+  const int eo = 64 * (wave & 1);  // first dim of the wave within K_h or V_h
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int s = s0 + t0 + 16 * n + c;  // rows past L (up to the block's end) are written too
+  for (int n = 0; n < 8; ++n) {
+    const int64_t s = s0 + 128 * (wave >> 2) + 16 * n + c;  // rows past L (up to the block's end) are written too
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       f16x4 v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = to_f16_sat(acc[m][n][i]);
-      *reinterpret_cast<f16x4 *>(out + ((int64_t)s * H + h) * kDn + e0 + 16 * m + 4 * g) = v;
+      *reinterpret_cast<f16x4 *>(out + (s * H + h) * kDn + eo + 16 * m + 4 * g) = v;
     }
   }
 }
@@ -200,9 +215,6 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return *reinterpret_cast<const uint32_t *>(&m);
 }
 
-// s_waitcnt immediate: at most n vector-memory operations outstanding
-// (expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Per-workgroup state shared by the walks.
 struct MhaCtx {
@@ -555,13 +567,13 @@ hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, co
   static bool attr_done = false;  // per process: the attribute holds for every device
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void *)mha_upproj_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kUpBuf);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kUpSmem);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void *)masked_mha_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmem);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(mha_upproj_kernel, dim3((L + kUpT - 1) / kUpT, H, 2), dim3(256), 2 * kUpBuf, s, (const __bf16 *)kv,
+  hipLaunchKernelGGL(mha_upproj_kernel, dim3((L + kUpT - 1) / kUpT, H), dim3(512), kUpSmem, s, (const __bf16 *)kv,
                      (const __bf16 *)w_uk, (const __bf16 *)w_uv, L, H, kbuf, vbuf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

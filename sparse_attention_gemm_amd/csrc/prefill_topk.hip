@@ -36,6 +36,7 @@
 //
 // Workgroups are issued longest-first (the last query block first) so that
 // the causal triangle drains evenly.
+#include "dsa_launch.h"
 #include "indexer_core.h"
 
 namespace {

@@ -7,7 +7,7 @@
 //
 // One wavefront per row; the row is read twice (the second read hits L2/L1),
 // so HBM traffic is 4 B in + 1 B out per element plus 4 B per row.
-#include "dsa_common.h"
+#include "dsa_launch.h"
 
 namespace {
 

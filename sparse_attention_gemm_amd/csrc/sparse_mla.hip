@@ -30,7 +30,7 @@
 //    combine (used when there are too few queries to fill the GPU).
 #include <algorithm>
 
-#include "dsa_common.h"
+#include "dsa_launch.h"
 
 namespace {
 

@@ -18,7 +18,7 @@
 // through ordered block scans, so results are deterministic.  If a single
 // key value is too frequent to fit (massive ties), the output pass runs over
 // the row in global memory instead.
-#include "dsa_common.h"
+#include "dsa_launch.h"
 
 namespace {
 
