@@ -59,12 +59,16 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 constexpr int kUpE = 2 * kDn;  // output rows per workgroup: K_h (W_uk[h] rows), then V_h (W_uv[h] rows)
 constexpr int kUpT = 256;      // tokens per workgroup (K_h and V_h rows are padded to a multiple of this)
 constexpr int kUpK = 32;       // latent dims per LDS chunk
-constexpr int kUpSlots = 5;    // LDS row: 4 x 16 B of data + 1 pad (20 dwords: conflict-free 16-B reads)
+constexpr int kUpSlots = 4;    // LDS row: 4 x 16 B, unpadded; chunk j of row r sits at chunk up_chunk(r, j)
 constexpr int kUpRow = kUpSlots * 16;
+// Swizzle of the 16-byte chunks of a 64-byte row: with the operand reads
+// (lane 16g + c: row c, chunk g) it spreads a read over distinct banks
+// (measured on gfx950: half the LDS cycles of a 16-byte row padding).
+__host__ __device__ constexpr int up_chunk(int r, int j) { return j ^ ((r >> 1) & 3); }
 constexpr int kUpRows = kUpE + kUpT;                       // W rows, then token rows
-constexpr int kUpInsts = kUpRows * kUpSlots / 64;          // 40 wave-wide 1 KB loads per chunk
+constexpr int kUpInsts = kUpRows * kUpSlots / 64;          // 32 wave-wide 1 KB loads per chunk
 static_assert(kUpRows * kUpSlots % 64 == 0 && kUpInsts % 8 == 0, "whole loads, the same count per wave");
-constexpr int kUpStage = kUpInsts * 1024;                  // 40 KB
+constexpr int kUpStage = kUpInsts * 1024;                  // 32 KB
 constexpr int kUpNBuf = 3;                                 // chunk kc+2 loads while chunk kc is computed
 constexpr int kUpSmem = kUpNBuf * kUpStage;
 constexpr int kUpChunks = kDc / kUpK;                      // 16
@@ -76,8 +80,8 @@ constexpr int kUpChunks = kDc / kUpK;                      // 16
 // consecutive output dims of one token (one 8-byte store).  Eight waves: wave
 // w owns rows 64 (w & 3) .. +64 (K_h for w & 3 < 2, V_h otherwise) and tokens
 // 128 (w >> 2) .. +128.  Operands reach LDS by direct-to-LDS loads in chunks of
-// 32 latent dims, three chunks deep; token rows past L read row L - 1 and
-// their outputs land in the padding rows.
+// 32 latent dims (64-byte rows, chunk-swizzled), three chunks deep; token rows
+// past L read row L - 1 and their outputs land in the padding rows.
 __global__ __launch_bounds__(512) void mha_upproj_kernel(const __bf16 *__restrict__ kv,
                                                          const __bf16 *__restrict__ w_uk,
                                                          const __bf16 *__restrict__ w_uv, int L, int H,
@@ -87,7 +91,8 @@ __global__ __launch_bounds__(512) void mha_upproj_kernel(const __bf16 *__restric
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y;
   const int s0 = blockIdx.x * kUpT;
-  // this wave's loads: instruction i = wave + 8 n, slot i*64 + lane -> row slot/5, chunk slot%5
+  // this wave's loads: instruction i = wave + 8 n, slot i*64 + lane -> LDS row slot/4, chunk slot%4,
+  // which holds the source row's chunk up_chunk(row, slot%4)
   const char *src[kUpInsts / 8];
   {
     int l = lane;
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(512) void mha_upproj_kernel(const __bf16 *__restric
 #pragma unroll
     for (int n = 0; n < kUpInsts / 8; ++n) {
       const int slot = (wave + 8 * n) * 64 + l;
-      const int row = slot / kUpSlots, j = min(slot % kUpSlots, 3);
+      const int row = slot / kUpSlots, j = up_chunk(row, slot % kUpSlots);
       const __bf16 *p;
       if (row < kDn)
         p = w_uk + ((int64_t)h * kDn + row) * kDc;
@@ -128,13 +133,13 @@ __global__ __launch_bounds__(512) void mha_upproj_kernel(const __bf16 *__restric
       __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // every wave's loads of chunk kc landed; chunk kc-1's buffer is free
     if (kc + 2 < kUpChunks) load_chunk(kc + 2, up_smem + nxt2);
-    const uint8_t *b = up_smem + cur;
+    const uint8_t *b = up_smem + cur + c * kUpRow + up_chunk(c, g) * 16;  // rows 16i + c share the swizzle of c
     bf16x8 a[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const bf16x8 *>(b + (e0 + 16 * m + c) * kUpRow + g * 16);
+    for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const bf16x8 *>(b + (e0 + 16 * m) * kUpRow);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(b + (t0 + 16 * n + c) * kUpRow + g * 16);
+      const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(b + (t0 + 16 * n) * kUpRow);
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[m][n] = mfma_bf16_16x16x32(a[m], bb, acc[m][n]);
     }
@@ -183,21 +188,25 @@ constexpr int kKT = 32;        // keys per tile
 // instructions (1 KB, or 256 B for the mask words); instruction i writes
 // 16 (or 4) bytes per lane in lane order.  Row strides are padded so that the
 // operand reads below hit distinct banks.
-constexpr int kKnSlots = 17;  // K no-rope row: 16 x 16 B (128 fp16 dims) + 1 pad (68 dwords)
-constexpr int kKrSlots = 9;   // K rope row: 8 x 16 B (64 bf16 dims) + 1 pad (36 dwords)
+constexpr int kKnSlots = 18;  // K no-rope row: 16 x 16 B (128 fp16 dims) + 2 pad (72 dwords)
+constexpr int kKrSlots = 8;   // K rope row: 8 x 16 B (64 bf16 dims), unpadded; chunk j of row r at kr_chunk(r, j)
 constexpr int kVSlots = 18;   // V row: 16 x 16 B (128 fp16 dims) + 2 pad (72 dwords)
 constexpr int kKnRow = kKnSlots * 16, kKrRow = kKrSlots * 16, kVRow = kVSlots * 16;
+// Row strides (72-dword rows) and the rope swizzle keep the operand reads
+// (lane 16g + c: row c, 16-byte chunk g of a K step) on distinct banks
+// (measured on gfx950: half the LDS cycles of 68- or 36-dword rows).
+__host__ __device__ constexpr int kr_chunk(int r, int j) { return j ^ (r & 7); }
 constexpr int kKnInsts = (kKT * kKnSlots + 63) / 64;  // 9
-constexpr int kKrInsts = (kKT * kKrSlots + 63) / 64;  // 5
+constexpr int kKrInsts = (kKT * kKrSlots + 63) / 64;  // 4
 constexpr int kVInsts = (kKT * kVSlots + 63) / 64;    // 9
 constexpr int kMInsts = kQB * 4 / 256;                // 2: one mask word per query
 constexpr int kKrOff = kKnInsts * 1024;
 constexpr int kVOff = kKrOff + kKrInsts * 1024;
 constexpr int kMOff = kVOff + kVInsts * 1024;
 constexpr int kTileBytes = kMOff + kMInsts * 256;
-constexpr int kTileInsts = kKnInsts + kKrInsts + kVInsts + kMInsts;  // 25
-constexpr int kInstsW0 = (kTileInsts + 3) / 4;                       // wave 0 issues 7, the others 6
-static_assert(kTileInsts % 4 == 1, "wave 0 issues one load more than the others");
+constexpr int kTileInsts = kKnInsts + kKrInsts + kVInsts + kMInsts;  // 24
+constexpr int kInstsW = kTileInsts / 4;                              // 6 per wave
+static_assert(kTileInsts % 4 == 0, "every wave issues the same number of loads per tile");
 constexpr int kNBuf = 3;                  // tile j+2 loads while tile j is computed
 constexpr int kLutOff = kNBuf * kTileBytes;
 constexpr int kAttnSmem = kLutOff + 256 * 16;  // + the mask table
@@ -222,7 +231,7 @@ struct MhaCtx {
   const char *kn, *kr, *vb, *mk;     // tile-0 bases: K_h no-rope, latent rope, V_h, mask column 0
   int kr_len, mk_len;                // bytes readable from the rope and mask bases
   int64_t kv_tile;                   // bytes between tiles in K_h / V_h (32 keys x H heads x 256 B)
-  uint32_t loff[kInstsW0];           // the lane's byte offset within its instructions' tiles
+  uint32_t loff[kInstsW];           // the lane's byte offset within its instructions' tiles
   int wave, lane, g, c;
   int L, H, h, q0, ntiles, wave_last;
 };
@@ -250,7 +259,7 @@ __device__ __forceinline__ void mha_load_tile(const MhaCtx &cx, uint8_t *dst, in
   const __amdgpu_buffer_rsrc_t rvb = tile_rsrc(cx.vb, tile * cx.kv_tile);
   const __amdgpu_buffer_rsrc_t rmk = tile_rsrc(cx.mk, cx.mk_len, tile * 4);
 #pragma unroll
-  for (int n = 0; n < kInstsW0; ++n) {
+  for (int n = 0; n < kInstsW; ++n) {
     const int i = cx.wave + 4 * n;  // uniform
     if (i >= kTileInsts) break;
     if (i < kKnInsts)
@@ -329,10 +338,7 @@ __device__ __forceinline__ void mha_walk(const MhaCtx &cx, const f16x8 (&qn)[2][
   if (cx.ntiles > 1) mha_load_tile(cx, cx.smem + kTileBytes, 1);
   for (int it = 0; it < cx.ntiles; ++it, cur = step(cur), nxt2 = step(nxt2)) {
     if (it + 1 < cx.ntiles) {  // tile it landed; tile it+1 may still be in flight
-      if (wave == 0)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstsW0));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstsW0 - 1));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstsW));
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
@@ -359,8 +365,10 @@ __device__ __forceinline__ void mha_walk(const MhaCtx &cx, const f16x8 (&qn)[2][
     }
 #pragma unroll
     for (int st = 0; st < kSteps - kNopeSteps; ++st) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tb + kKrOff + c * kKrRow + st * 64 + g * 16);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tb + kKrOff + (16 + c) * kKrRow + st * 64 + g * 16);
+      // rows c and 16 + c share the swizzle of c
+      const int kro = kKrOff + c * kKrRow + kr_chunk(c, 4 * st + g) * 16;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tb + kro);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tb + kro + 16 * kKrRow);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         s[u][0] = mfma_bf16_16x16x32(a0, qr[u][st], s[u][0]);
@@ -498,14 +506,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   cx.kv_tile = (int64_t)kKT * H * kDn * 2;
   // lane offsets of this wave's instructions (fixed for every tile)
 #pragma unroll
-  for (int n = 0; n < kInstsW0; ++n) {
+  for (int n = 0; n < kInstsW; ++n) {
     const int i = cx.wave + 4 * n;
     uint32_t off = 0;
     if (i < kKnInsts) {
       const int slot = i * 64 + cx.lane, r = min(slot / kKnSlots, kKT - 1), j = min(slot % kKnSlots, 15);
       off = (uint32_t)r * H * kDn * 2 + j * 16;
     } else if (i < kKnInsts + kKrInsts) {
-      const int slot = (i - kKnInsts) * 64 + cx.lane, r = min(slot / kKrSlots, kKT - 1), j = min(slot % kKrSlots, 7);
+      const int slot = (i - kKnInsts) * 64 + cx.lane, r = slot / kKrSlots, j = kr_chunk(r, slot % kKrSlots);
       off = (uint32_t)r * kDl * 2 + j * 16;
     } else if (i < kKnInsts + kKrInsts + kVInsts) {
       const int slot = (i - kKnInsts - kKrInsts) * 64 + cx.lane, r = min(slot / kVSlots, kKT - 1),
