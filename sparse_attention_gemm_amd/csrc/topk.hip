@@ -12,10 +12,12 @@
 //      usually after the first histogram);
 //   2. one ordered pass that copies those candidates (key, position) into
 //      LDS in position order.
-// The exact k-th key tau is then found by narrowing over the candidates in
-// LDS, and the output pass keeps key > tau plus the most recent
-// (largest-position) ties at tau, writing positions in ascending order
-// through ordered block scans, so results are deterministic.  If a single
+// The exact k-th key tau lies in the last bin of pass 1; narrowing over the
+// candidates of that bin in LDS finds it (two more levels).  The output pass
+// keeps key > tau plus the most recent (largest-position) ties at tau and
+// writes positions in ascending order: each thread owns a contiguous run of
+// the position-ordered candidates and one block scan places the runs, so
+// results are deterministic.  If a single
 // key value is too frequent to fit (massive ties), the output pass runs over
 // the row in global memory instead.
 #include "dsa_launch.h"
@@ -154,12 +156,12 @@ struct Narrow {
     nbins = kBins;
     remaining = k;
   }
-  __device__ __forceinline__ void init(uint32_t lo, uint32_t hi, uint32_t k) {
+  // the window [lo, lo + 2^w) (one bin of an earlier level), rank r inside it
+  __device__ __forceinline__ void init_bin(uint32_t lo, int w, uint32_t r) {
     base = lo;
-    const uint32_t span = hi - lo;
-    shift = span == 0 ? 0 : max(0, 32 - __clz(span) - 11);
-    nbins = kBins;
-    remaining = k;
+    shift = max(0, w - 11);
+    nbins = 1u << (w - shift);
+    remaining = r;
   }
   __device__ __forceinline__ void add(TopkShared &sm, uint32_t key) const {
     if (key >= base) {
@@ -201,6 +203,10 @@ __device__ __forceinline__ void emit_block(TopkShared &sm, bool in, uint32_t key
   tie_seen += n_tie;
 }
 
+// kResident: every row has at most one batch (32768 scores), read once and
+// kept in registers for every later pass; otherwise rows are streamed again
+// per pass.
+template <bool kResident>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ n_valid, int32_t n_cap,
                                                              int32_t k, int32_t *__restrict__ idx) {
@@ -216,13 +222,31 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
     return;
   }
   const bool aligned = (reinterpret_cast<uintptr_t>(sc) & 15) == 0;
+  constexpr int kBatch = 4 * kThreads * kU;
+  constexpr bool resident = kResident;
+  uint32_t rk[kU][4];
+  if (resident) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) load4(sc, aligned, 4 * (u * kThreads + tid), n, rk[u]);
+  }
+  auto for_keys = [&](auto &&f) {
+    if (resident) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (4 * u * kThreads >= n) break;  // uniform
+        f(4 * (u * kThreads + tid), rk[u]);
+      }
+    } else {
+      for_row4(sc, aligned, n, f);
+    }
+  };
   // ---- pass 1: narrow over the row until the candidates fit in LDS
   Narrow nw;
   nw.init_full((uint32_t)k);
-  uint32_t above_total = 0, edge = 0;
+  uint32_t above_total = 0, edge = 0, rank_in_bin = 0;
   while (true) {
     clear_hist(sm);
-    for_row4(sc, aligned, n, [&](int i0, const uint32_t (&k4)[4]) {
+    for_keys([&](int i0, const uint32_t (&k4)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (i0 + j < n) nw.add(sm, k4[j]);
@@ -231,6 +255,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
     uint32_t bstar, above, bcnt;
     select_bin(sm, nw.remaining, bstar, above, bcnt);
     edge = nw.base + (bstar << nw.shift);
+    rank_in_bin = nw.remaining - above;
     if (above_total + above + bcnt <= (uint32_t)kCand) break;
     above_total += above;
     if (!nw.descend(bstar, above)) {
@@ -250,10 +275,17 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
   uint32_t m = 0;
   {
     const int lane = tid & 63, wave = tid >> 6;
-    for (int b0 = 0; b0 < n; b0 += 4 * kThreads * kU) {
+    for (int b0 = 0; b0 < n; b0 += kBatch) {
       uint32_t kk[kU][4], cnt[kU], incl[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) load4(sc, aligned, b0 + 4 * (u * kThreads + tid), n, kk[u]);
+      for (int u = 0; u < kU; ++u) {
+        if (resident) {  // b0 = 0
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kk[u][j] = rk[u][j];
+        } else {
+          load4(sc, aligned, b0 + 4 * (u * kThreads + tid), n, kk[u]);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i0 = b0 + 4 * (u * kThreads + tid);
@@ -294,11 +326,12 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
     }
   }
   __syncthreads();
-  // ---- exact k-th key among the m candidates (all >= edge)
+  // ---- exact k-th key: it lies in the last bin of pass 1, [edge, edge + 2^shift),
+  // at rank rank_in_bin; the candidates above that bin are all kept
   Narrow nc;
-  nc.init(edge, 0xFFFFFFFFu, (uint32_t)k);
-  uint32_t tau, ties;
-  while (true) {
+  nc.init_bin(edge, nw.shift, rank_in_bin);
+  uint32_t tau = edge, ties = 0;
+  while (nw.shift > 0) {
     clear_hist(sm);
     for (int i = tid; i < (int)m; i += kThreads) nc.add(sm, sm.ckey[i]);
     __syncthreads();
@@ -310,13 +343,38 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
       break;
     }
   }
-  // ---- ordered output from LDS
+  if (nw.shift == 0) {  // pass 1 ended on a single key value
+    ties = 0;
+    for (int i = tid; i < (int)m; i += kThreads) ties += sm.ckey[i] == tau ? 1u : 0u;
+    uint32_t tot;
+    block_excl_scan(ties, sm.wred[0], tot);
+    ties = tot;
+    nc.remaining = rank_in_bin;
+  }
+  // ---- ordered output from LDS: thread t owns the candidates [t R, t R + R),
+  // which are in position order.  One scan of packed (greater, tie) counts
+  // gives each thread its output offset: the greater keys before its run plus
+  // the ties before its run that rank at or after tie_cut.
   const uint32_t tie_cut = ties - nc.remaining;
-  uint32_t dst = 0, tie_seen = 0;
-  for (int b0 = 0; b0 < (int)m; b0 += kThreads) {
-    const int i = b0 + tid;
-    const bool in = i < (int)m;
-    emit_block(sm, in, in ? sm.ckey[i] : 0u, in ? sm.cpos[i] : 0, tau, tie_cut, dst, tie_seen, out);
+  const int R = ((int)m + kThreads - 1) / kThreads;
+  const int i0 = min(tid * R, (int)m), i1 = min(i0 + R, (int)m);
+  uint32_t n_gt = 0, n_tie = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = sm.ckey[i];
+    n_gt += key > tau ? 1u : 0u;
+    n_tie += key == tau ? 1u : 0u;
+  }
+  static_assert(kCand < 65536, "counts pack into 16 bits");
+  uint32_t packed_tot;
+  const uint32_t pre = block_excl_scan((n_gt << 16) | n_tie, sm.wred[0], packed_tot);
+  const uint32_t gt_before = pre >> 16, tie_before = pre & 0xFFFFu;
+  uint32_t dst = gt_before + (tie_before > tie_cut ? tie_before - tie_cut : 0u);
+  uint32_t tie_rank = tie_before;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = sm.ckey[i];
+    const bool tie = key == tau;
+    if (key > tau || (tie && tie_rank >= tie_cut)) out[dst++] = sm.cpos[i];
+    tie_rank += tie ? 1u : 0u;
   }
 }
 
@@ -341,15 +399,21 @@ hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStre
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
                        int32_t k, int32_t *idx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  static bool attr_done = false;
+  static bool attr_done = false;  // per process: the attribute holds for every device
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)topk_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kTopkSmem);
-    if (e != hipSuccess) return e;
+    for (const void *f : {(const void *)topk_rows_kernel<true>, (const void *)topk_rows_kernel<false>}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTopkSmem);
+      if (e != hipSuccess) return e;
+    }
     attr_done = true;
   }
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
-                     idx);
+  // rows are at most n_cap long: one batch fits in registers
+  if (n_cap <= 4 * kThreads * kU)
+    hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
+                       idx);
+  else
+    hipLaunchKernelGGL(topk_rows_kernel<false>, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
+                       idx);
   return hipGetLastError();
 }
 }  // namespace dsa
