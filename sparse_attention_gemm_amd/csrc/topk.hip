@@ -203,10 +203,6 @@ __device__ __forceinline__ void emit_block(TopkShared &sm, bool in, uint32_t key
   tie_seen += n_tie;
 }
 
-// kResident: every row has at most one batch (32768 scores), read once and
-// kept in registers for every later pass; otherwise rows are streamed again
-// per pass.
-template <bool kResident>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ n_valid, int32_t n_cap,
                                                              int32_t k, int32_t *__restrict__ idx) {
@@ -222,31 +218,13 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
     return;
   }
   const bool aligned = (reinterpret_cast<uintptr_t>(sc) & 15) == 0;
-  constexpr int kBatch = 4 * kThreads * kU;
-  constexpr bool resident = kResident;
-  uint32_t rk[kU][4];
-  if (resident) {
-#pragma unroll
-    for (int u = 0; u < kU; ++u) load4(sc, aligned, 4 * (u * kThreads + tid), n, rk[u]);
-  }
-  auto for_keys = [&](auto &&f) {
-    if (resident) {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (4 * u * kThreads >= n) break;  // uniform
-        f(4 * (u * kThreads + tid), rk[u]);
-      }
-    } else {
-      for_row4(sc, aligned, n, f);
-    }
-  };
   // ---- pass 1: narrow over the row until the candidates fit in LDS
   Narrow nw;
   nw.init_full((uint32_t)k);
   uint32_t above_total = 0, edge = 0, rank_in_bin = 0;
   while (true) {
     clear_hist(sm);
-    for_keys([&](int i0, const uint32_t (&k4)[4]) {
+    for_row4(sc, aligned, n, [&](int i0, const uint32_t (&k4)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (i0 + j < n) nw.add(sm, k4[j]);
@@ -275,17 +253,10 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
   uint32_t m = 0;
   {
     const int lane = tid & 63, wave = tid >> 6;
-    for (int b0 = 0; b0 < n; b0 += kBatch) {
+    for (int b0 = 0; b0 < n; b0 += 4 * kThreads * kU) {
       uint32_t kk[kU][4], cnt[kU], incl[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (resident) {  // b0 = 0
-#pragma unroll
-          for (int j = 0; j < 4; ++j) kk[u][j] = rk[u][j];
-        } else {
-          load4(sc, aligned, b0 + 4 * (u * kThreads + tid), n, kk[u]);
-        }
-      }
+      for (int u = 0; u < kU; ++u) load4(sc, aligned, b0 + 4 * (u * kThreads + tid), n, kk[u]);
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i0 = b0 + 4 * (u * kThreads + tid);
@@ -399,21 +370,15 @@ hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStre
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
                        int32_t k, int32_t *idx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  static bool attr_done = false;  // per process: the attribute holds for every device
+  static bool attr_done = false;
   if (!attr_done) {
-    for (const void *f : {(const void *)topk_rows_kernel<true>, (const void *)topk_rows_kernel<false>}) {
-      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTopkSmem);
-      if (e != hipSuccess) return e;
-    }
+    hipError_t e = hipFuncSetAttribute((const void *)topk_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kTopkSmem);
+    if (e != hipSuccess) return e;
     attr_done = true;
   }
-  // rows are at most n_cap long: one batch fits in registers
-  if (n_cap <= 4 * kThreads * kU)
-    hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
-                       idx);
-  else
-    hipLaunchKernelGGL(topk_rows_kernel<false>, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
-                       idx);
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
+                     idx);
   return hipGetLastError();
 }
 }  // namespace dsa
