@@ -74,7 +74,8 @@ const char *dsa_version(void);
  *   x8     [rows, cols] E4M3 out;  scale [rows] fp32 out
  * scale[r] = amax_c |x[r,c]| / 448 (fp32 division; 1 if the row is all zero);
  * x8[r,c] = E4M3 of the fp32 quotient x[r,c]/scale[r], round-to-nearest-even,
- * saturating at +-448.  cols must be a multiple of 4 and at most 16384.
+ * saturating at +-448.  cols must be a multiple of 4 and at most 16384;
+ * rows at most 2^31 - 1.  x must be 16-byte aligned, x8 4-byte aligned.
  */
 dsa_status dsa_quantize_e4m3_per_token(const float *x, int64_t rows, int32_t cols, uint8_t *x8,
                                        float *scale, hipStream_t stream);

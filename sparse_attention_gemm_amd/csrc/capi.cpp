@@ -74,6 +74,7 @@ dsa_status dsa_quantize_e4m3_per_token(const float *x, int64_t rows, int32_t col
   REQUIRE(cols > 0, DSA_ERR_INVALID_ARG, "cols must be > 0 (got %d)", cols);
   REQUIRE(rows == 0 || (x && x8 && scale), DSA_ERR_INVALID_ARG, "null pointer");
   REQUIRE(cols % 4 == 0 && cols <= 16384, DSA_ERR_UNSUPPORTED, "cols must be a multiple of 4, <= 16384");
+  REQUIRE(rows <= 0x7FFFFFFF, DSA_ERR_UNSUPPORTED, "rows must be < 2^31");
   return hip_check(launch_quantize(x, rows, cols, x8, scale, stream), "quantize launch");
 }
 

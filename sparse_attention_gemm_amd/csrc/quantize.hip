@@ -7,7 +7,8 @@
 //
 // General rows: one wavefront per row; the row is read twice (the second read
 // hits L2/L1), so HBM traffic is 4 B in + 1 B out per element plus 4 B per
-// row.  Rows of 128 have a kernel of their own (below).
+// row.  Rows of 128 and of 1024, 2048, 4096 or 8192 have kernels of their own
+// (below).
 #include "dsa_launch.h"
 
 namespace {
@@ -93,12 +94,54 @@ __global__ __launch_bounds__(256) void quantize_e4m3_128_kernel(const float *__r
   }
 }
 
+// Rows of 1024 NV (per-token scales over all indexer heads: 64 x 128 =
+// 8192): one workgroup per row, each thread holding NV float4 of it in
+// registers (the row is read once, NV loads in flight per thread), the row
+// max through LDS.  Same arithmetic as the general kernel.
+template <int NV>
+__global__ __launch_bounds__(256) void quantize_e4m3_wide_kernel(const float *__restrict__ x, uint8_t *__restrict__ x8,
+                                                                 float *__restrict__ scale) {
+  __shared__ float wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float4 *xr = reinterpret_cast<const float4 *>(x + r * (NV * 1024));
+  float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = xr[i * 256 + tid];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  amax = wave_max(amax);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  float s = __fdiv_rn(amax, 448.0f);
+  if (!(s > 0.0f)) s = 1.0f;
+  if (tid == 0) scale[r] = s;
+  uint32_t *out = reinterpret_cast<uint32_t *>(x8 + r * (NV * 1024));
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(v[i].x, s), e4m3_input(v[i].y, s), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_input(v[i].z, s), e4m3_input(v[i].w, s), w, true);
+    out[i * 256 + tid] = (uint32_t)w;
+  }
+}
+
 }  // namespace
 
 namespace dsa {
 hipError_t launch_quantize(const float *x, int64_t rows, int32_t cols, uint8_t *x8, float *scale,
                            hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (cols == 1024 || cols == 2048 || cols == 4096 || cols == 8192) {
+    const dim3 grid((uint32_t)rows);
+    if (cols == 1024) hipLaunchKernelGGL(quantize_e4m3_wide_kernel<1>, grid, dim3(256), 0, s, x, x8, scale);
+    if (cols == 2048) hipLaunchKernelGGL(quantize_e4m3_wide_kernel<2>, grid, dim3(256), 0, s, x, x8, scale);
+    if (cols == 4096) hipLaunchKernelGGL(quantize_e4m3_wide_kernel<4>, grid, dim3(256), 0, s, x, x8, scale);
+    if (cols == 8192) hipLaunchKernelGGL(quantize_e4m3_wide_kernel<8>, grid, dim3(256), 0, s, x, x8, scale);
+    return hipGetLastError();
+  }
   if (cols == 128) {
     const int64_t rows_per_block = 4 * kQ128RowsPerWave;
     hipLaunchKernelGGL(quantize_e4m3_128_kernel, dim3((uint32_t)((rows + rows_per_block - 1) / rows_per_block)),
