@@ -17,9 +17,8 @@
 // keeps key > tau plus the most recent (largest-position) ties at tau and
 // writes positions in ascending order: each thread owns a contiguous run of
 // the position-ordered candidates and one block scan places the runs, so
-// results are deterministic.  If a single
-// key value is too frequent to fit (massive ties), the output pass runs over
-// the row in global memory instead.
+// results are deterministic.  If a single key value is too frequent to fit
+// (massive ties), the output pass runs over the row in global memory instead.
 #include "dsa_launch.h"
 
 namespace {
