@@ -144,6 +144,9 @@ def setup_decode(torch, dsa, synth, cfg, dev):
     t["lse"] = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=dev)
     nws = dsa.dsa_sparse_mla_workspace_bytes(cfg.B, cfg.H, cfg.k)
     t["ws"] = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    # rows are at most ld long: a short batch may split its top-k rows over more CUs
+    ntw = dsa.dsa_topk_workspace_bytes(cfg.B, t["ld"], cfg.k)
+    t["topk_ws"] = torch.empty(ntw, dtype=torch.uint8, device=dev) if ntw > 0 else None
     t["args"] = dsa.make_decode_args(cfg.B, cfg.H_I, cfg.D_I, cfg.H, cfg.k, t["q8"], t["qs"], t["w"], t["q"],
                                      t["k8p"], t["ksp"], t["kvp"], nb * 64, t["bt"], bt.shape[1], t["ctx"],
                                      max_ctx, cfg.sm_scale, t["out"], t["lse"], t["idx"])
@@ -165,7 +168,7 @@ def decode_step(dsa, cfg, t, evs, stream):
     evs[1].record(stream)
     dsa.dsa_decode_indexer_scores(t["args"], t["scores"], stream=stream)
     evs[2].record(stream)
-    dsa.dsa_topk_select(t["scores"], t["ctx"], cfg.k, t["idx"], stream=stream)
+    dsa.dsa_topk_select(t["scores"], t["ctx"], cfg.k, t["idx"], workspace=t["topk_ws"], stream=stream)
     evs[3].record(stream)
     dsa.dsa_sparse_mla_paged_fwd(t["q"], t["kvp"], t["bt"], t["idx"], cfg.sm_scale, t["out"], t["lse"],
                                  workspace=t["ws"], n_pool_rows=t["nb"] * 64, stream=stream)

@@ -105,12 +105,21 @@ dsa_status dsa_indexer_scores(const void *q, const float *q_scale, const void *k
  *   n_valid [T] int32 (device)
  *   idx     [T, k] int32 out: the min(k, n_valid[t]) selected positions in
  *           ascending order, then -1.
- * Order: score descending, then position descending.  k <= 2048; rows of any
- * length up to 2^31-1.  No workspace is needed (pass NULL, 0).
+ * Order: score descending, then position descending.  k <= 2048.
+ * Without a workspace (NULL, 0) rows may be of any length up to 2^31-1 and
+ * each row is one workgroup.  With a workspace of at least
+ * dsa_topk_workspace_bytes(T, ld_scores, k) bytes (ld_scores > 0), rows are
+ * taken to be at most ld_scores long, and a batch too short to fill the GPU
+ * is split: each row's column chunks are selected separately, then merged
+ * (same result).  The workspace is scratch, overwritten by the call.
  */
 dsa_status dsa_topk_select(const float *scores, int64_t ld_scores, const int32_t *n_valid,
                            int32_t T, int32_t k, int32_t *idx, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes for a split dsa_topk_select of T rows of at most
+ * ld_scores scores (0: the batch is never split). */
+size_t dsa_topk_workspace_bytes(int32_t T, int64_t ld_scores, int32_t k);
 
 /* ---------------------------------------------------------------------------
  * Sparse MLA forward in MQA mode (mizuki-eaf.pages.dev, "built on MLA";

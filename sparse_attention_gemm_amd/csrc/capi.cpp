@@ -1,6 +1,7 @@
 // capi.cpp -- the C ABI of libdsa: argument validation, workspace layout and
 // dispatch to the gfx950 kernels.  Validation happens before any HIP call;
 // nothing is enqueued on failure.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -109,15 +110,23 @@ dsa_status dsa_topk_select(const float *scores, int64_t ld_scores, const int32_t
                            int32_t k, int32_t *idx, void *workspace, size_t workspace_bytes,
                            hipStream_t stream) {
   CLEAR_ERR();
-  (void)workspace;
-  (void)workspace_bytes;
   REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "T must be >= 0");
   REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
   REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d (got %d)", DSA_MAX_K, k);
   REQUIRE(ld_scores >= 0, DSA_ERR_INVALID_ARG, "ld_scores must be >= 0");
   if (T == 0) return DSA_OK;
   REQUIRE(scores && n_valid && idx, DSA_ERR_INVALID_ARG, "null pointer");
-  return hip_check(launch_topk(scores, ld_scores, n_valid, 0x7FFFFFFF, T, k, idx, stream), "topk launch");
+  // with a workspace, rows are at most ld_scores long and short batches split
+  const bool split = workspace && ld_scores > 0;
+  const int32_t n_cap = split ? (int32_t)std::min<int64_t>(ld_scores, 0x7FFFFFFF) : 0x7FFFFFFF;
+  return hip_check(launch_topk(scores, ld_scores, n_valid, n_cap, T, k, idx, stream, split ? workspace : nullptr,
+                               split ? workspace_bytes : 0),
+                   "topk launch");
+}
+
+size_t dsa_topk_workspace_bytes(int32_t T, int64_t ld_scores, int32_t k) {
+  if (T <= 0 || ld_scores <= 0 || k <= 0) return 0;
+  return topk_workspace_bytes(T, (int32_t)std::min<int64_t>(ld_scores, 0x7FFFFFFF), std::min<int32_t>(k, DSA_MAX_K));
 }
 
 size_t dsa_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t k) {
@@ -326,7 +335,9 @@ size_t dsa_decode_workspace_bytes(const dsa_decode_args *a) {
   if (!a || a->B <= 0 || a->max_ctx <= 0 || a->k <= 0) return 0;
   size_t n = align_up((size_t)a->B * decode_ld(a) * 4, 256);
   if (!a->idx_out) n += align_up((size_t)a->B * a->k * 4, 256);
-  if (a->H > 0 && a->H % 16 == 0) n += mla_ws_bytes(a->B, a->H, a->k);
+  // one region, used first by a split top-k and then by the split attention
+  const size_t mla = (a->H > 0 && a->H % 16 == 0) ? mla_ws_bytes(a->B, a->H, a->k) : 0;
+  n += std::max(mla, topk_workspace_bytes(a->B, a->max_ctx, a->k));
   return n;
 }
 
@@ -391,15 +402,18 @@ dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspac
     p += align_up((size_t)a->B * a->k * 4, 256);
   }
   void *po = nullptr;
-    float *pml = nullptr;
+  float *pml = nullptr;
   const int splits = mla_splits(a->B, a->H, a->k);
   if (splits > 1) mla_ws_split(p, a->B, a->H, a->k, &po, &pml);
+  const size_t topk_ws = topk_workspace_bytes(a->B, a->max_ctx, a->k);  // the same region, before the attention
   st = hip_check(launch_decode_indexer(a->q8, a->q_scale, a->w, a->k8_pool, a->ks_pool, a->block_table,
                                        a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores, ld,
                                        stream),
                  "decode indexer launch");
   if (st != DSA_OK) return st;
-  st = hip_check(launch_topk(scores, ld, a->ctx_len, a->max_ctx, a->B, a->k, idx, stream), "topk launch");
+  st = hip_check(launch_topk(scores, ld, a->ctx_len, a->max_ctx, a->B, a->k, idx, stream, topk_ws ? p : nullptr,
+                             topk_ws),
+                 "topk launch");
   if (st != DSA_OK) return st;
   return hip_check(launch_sparse_mla_bf16(a->q, a->kv_pool, idx, a->block_table, a->max_blocks, a->n_pool_rows,
                                           a->B, a->H, a->k, a->sm_scale, a->out, a->lse, splits, po, pml, stream),

@@ -20,8 +20,13 @@ hipError_t launch_indexer_scores_f32(const float *q, const float *k, const float
                                      const int32_t *q_pos, int32_t T, int32_t S, int32_t H_I,
                                      int32_t D_I, float *scores, int64_t ld, hipStream_t s);
 // Rows take min(n_valid[t], n_cap) candidates (n_cap guards the row length).
+// Row top-k over rows of at most n_cap scores.  With a workspace of at least
+// topk_workspace_bytes(T, n_cap, k) bytes a short batch is split into column
+// chunks (one selection per chunk, then a merge per row).
+int topk_split_chunks(int64_t T, int32_t n_cap, int32_t k);
+size_t topk_workspace_bytes(int64_t T, int32_t n_cap, int32_t k);
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
-                       int32_t k, int32_t *idx, hipStream_t s);
+                       int32_t k, int32_t *idx, hipStream_t s, void *ws = nullptr, size_t ws_bytes = 0);
 // Fused prefill selection; cand: prefill_candidate_bytes(L) of scratch.
 size_t prefill_candidate_bytes(int32_t L);
 hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const uint8_t *k8,

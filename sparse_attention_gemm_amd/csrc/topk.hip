@@ -19,6 +19,8 @@
 // the position-ordered candidates and one block scan places the runs, so
 // results are deterministic.  If a single key value is too frequent to fit
 // (massive ties), the output pass runs over the row in global memory instead.
+#include <algorithm>
+
 #include "dsa_launch.h"
 
 namespace {
@@ -28,6 +30,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCand = 18432;  // candidates held in LDS
 constexpr int kU = 8;         // groups of 4 row elements per thread in flight (32768 elements)
+constexpr int kMaxChunks = 8;  // chunks per row of a split selection
+static_assert(kMaxChunks * 2048 <= 18432, "a merge's candidates fit in LDS");
 
 struct TopkShared {
   uint32_t hist[kBins];
@@ -202,16 +206,81 @@ __device__ __forceinline__ void emit_block(TopkShared &sm, bool in, uint32_t key
   tie_seen += n_tie;
 }
 
+// Exact k-th key and ordered output of the m candidates (key, position) in
+// sm.ckey / sm.cpos, which are in position order and hold every key above
+// `edge` plus all keys of the window [edge, edge + 2^width) (width 32: the
+// whole key space); the k-th key has rank rank_in_bin inside that window.
+__device__ void cut_and_output(TopkShared &sm, uint32_t m, uint32_t edge, int width, uint32_t rank_in_bin,
+                               int32_t *__restrict__ out) {
+  const int tid = threadIdx.x;
+  // ---- exact k-th key: narrow over the window's candidates in LDS
+  Narrow nc;
+  nc.init_bin(edge, width, rank_in_bin);
+  uint32_t tau = edge, ties = 0;
+  while (width > 0) {
+    clear_hist(sm);
+    for (int i = tid; i < (int)m; i += kThreads) nc.add(sm, sm.ckey[i]);
+    __syncthreads();
+    uint32_t bstar, above, bcnt;
+    select_bin(sm, nc.remaining, bstar, above, bcnt);
+    if (!nc.descend(bstar, above)) {
+      tau = nc.base;
+      ties = bcnt;
+      break;
+    }
+  }
+  if (width == 0) {  // the window is a single key value
+    ties = 0;
+    for (int i = tid; i < (int)m; i += kThreads) ties += sm.ckey[i] == tau ? 1u : 0u;
+    uint32_t tot;
+    block_excl_scan(ties, sm.wred[0], tot);
+    ties = tot;
+    nc.remaining = rank_in_bin;
+  }
+  // ---- ordered output from LDS: thread t owns the candidates [t R, t R + R),
+  // which are in position order.  One scan of packed (greater, tie) counts
+  // gives each thread its output offset: the greater keys before its run plus
+  // the ties before its run that rank at or after tie_cut.
+  const uint32_t tie_cut = ties - nc.remaining;
+  const int R = ((int)m + kThreads - 1) / kThreads;
+  const int i0 = min(tid * R, (int)m), i1 = min(i0 + R, (int)m);
+  uint32_t n_gt = 0, n_tie = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = sm.ckey[i];
+    n_gt += key > tau ? 1u : 0u;
+    n_tie += key == tau ? 1u : 0u;
+  }
+  static_assert(kCand < 65536, "counts pack into 16 bits");
+  uint32_t packed_tot;
+  const uint32_t pre = block_excl_scan((n_gt << 16) | n_tie, sm.wred[0], packed_tot);
+  const uint32_t gt_before = pre >> 16, tie_before = pre & 0xFFFFu;
+  uint32_t dst = gt_before + (tie_before > tie_cut ? tie_before - tie_cut : 0u);
+  uint32_t tie_rank = tie_before;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = sm.ckey[i];
+    const bool tie = key == tau;
+    if (key > tau || (tie && tie_rank >= tie_cut)) out[dst++] = sm.cpos[i];
+    tie_rank += tie ? 1u : 0u;
+  }
+}
+
+// One workgroup per (row, chunk): workgroup b takes columns [c chunk,
+// (c + 1) chunk) of row b / nch, c = b % nch (nch = 1: the whole row), and
+// writes its selection (positions within the chunk) to idx + b k, and, when
+// cnt is given, its size to cnt[b].
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ n_valid, int32_t n_cap,
-                                                             int32_t k, int32_t *__restrict__ idx) {
+                                                             int32_t nch, int32_t chunk, int32_t k,
+                                                             int32_t *__restrict__ idx, int32_t *__restrict__ cnt) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   TopkShared &sm = *reinterpret_cast<TopkShared *>(smem_raw);
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int n = max(0, min(n_valid[row], n_cap));
-  const float *sc = scores + row * ld;
-  int32_t *out = idx + row * (int64_t)k;
+  const int64_t row = blockIdx.x / nch;
+  const int c0 = (int)(blockIdx.x % nch) * chunk;
+  const int n = max(0, min(min(n_valid[row], n_cap) - c0, chunk));
+  const float *sc = scores + row * ld + c0;
+  int32_t *out = idx + (int64_t)blockIdx.x * k;
+  if (cnt && tid == 0) cnt[blockIdx.x] = min(n, k);
   if (n <= k) {
     for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
     return;
@@ -296,56 +365,44 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(const float *__rest
     }
   }
   __syncthreads();
-  // ---- exact k-th key: it lies in the last bin of pass 1, [edge, edge + 2^shift),
+  // the exact k-th key lies in the last bin of pass 1, [edge, edge + 2^shift),
   // at rank rank_in_bin; the candidates above that bin are all kept
-  Narrow nc;
-  nc.init_bin(edge, nw.shift, rank_in_bin);
-  uint32_t tau = edge, ties = 0;
-  while (nw.shift > 0) {
-    clear_hist(sm);
-    for (int i = tid; i < (int)m; i += kThreads) nc.add(sm, sm.ckey[i]);
-    __syncthreads();
-    uint32_t bstar, above, bcnt;
-    select_bin(sm, nc.remaining, bstar, above, bcnt);
-    if (!nc.descend(bstar, above)) {
-      tau = nc.base;
-      ties = bcnt;
-      break;
-    }
+  cut_and_output(sm, m, edge, nw.shift, rank_in_bin, out);
+}
+
+// Second pass of a chunked selection: row b's candidates are the nch chunk
+// selections of the first pass (positions within their chunk, cnt[b nch + c]
+// of them), in position order.  At most nch k <= kCand of them, so they all
+// go to LDS and only the exact cut remains.
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const float *__restrict__ scores, int64_t ld,
+                                                              const int32_t *__restrict__ cpos,
+                                                              const int32_t *__restrict__ cnt, int32_t nch,
+                                                              int32_t chunk, int32_t k, int32_t *__restrict__ idx) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  TopkShared &sm = *reinterpret_cast<TopkShared *>(smem_raw);
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const float *sc = scores + row * ld;
+  int32_t *out = idx + row * (int64_t)k;
+  int off[kMaxChunks + 1];
+  off[0] = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) off[c + 1] = off[c] + (c < nch ? cnt[row * nch + c] : 0);
+  const int m = off[kMaxChunks];
+  for (int i = tid; i < m; i += kThreads) {
+    int c = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxChunks; ++j) c += i >= off[j] ? 1 : 0;
+    const int p = c * chunk + cpos[(row * nch + c) * (int64_t)k + (i - off[c])];
+    sm.cpos[i] = p;
+    sm.ckey[i] = row_key(sc, p);
   }
-  if (nw.shift == 0) {  // pass 1 ended on a single key value
-    ties = 0;
-    for (int i = tid; i < (int)m; i += kThreads) ties += sm.ckey[i] == tau ? 1u : 0u;
-    uint32_t tot;
-    block_excl_scan(ties, sm.wred[0], tot);
-    ties = tot;
-    nc.remaining = rank_in_bin;
+  __syncthreads();
+  if (m <= k) {
+    for (int i = tid; i < k; i += kThreads) out[i] = i < m ? sm.cpos[i] : -1;
+    return;
   }
-  // ---- ordered output from LDS: thread t owns the candidates [t R, t R + R),
-  // which are in position order.  One scan of packed (greater, tie) counts
-  // gives each thread its output offset: the greater keys before its run plus
-  // the ties before its run that rank at or after tie_cut.
-  const uint32_t tie_cut = ties - nc.remaining;
-  const int R = ((int)m + kThreads - 1) / kThreads;
-  const int i0 = min(tid * R, (int)m), i1 = min(i0 + R, (int)m);
-  uint32_t n_gt = 0, n_tie = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = sm.ckey[i];
-    n_gt += key > tau ? 1u : 0u;
-    n_tie += key == tau ? 1u : 0u;
-  }
-  static_assert(kCand < 65536, "counts pack into 16 bits");
-  uint32_t packed_tot;
-  const uint32_t pre = block_excl_scan((n_gt << 16) | n_tie, sm.wred[0], packed_tot);
-  const uint32_t gt_before = pre >> 16, tie_before = pre & 0xFFFFu;
-  uint32_t dst = gt_before + (tie_before > tie_cut ? tie_before - tie_cut : 0u);
-  uint32_t tie_rank = tie_before;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = sm.ckey[i];
-    const bool tie = key == tau;
-    if (key > tau || (tie && tie_rank >= tie_cut)) out[dst++] = sm.cpos[i];
-    tie_rank += tie ? 1u : 0u;
-  }
+  cut_and_output(sm, (uint32_t)m, 0u, 32, (uint32_t)k, out);
 }
 
 __global__ void positions_kernel(int32_t *__restrict__ q_pos, int32_t *__restrict__ n_valid, int32_t L) {
@@ -366,18 +423,58 @@ hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStre
   return hipGetLastError();
 }
 
+// Chunks per row for T rows of at most n_cap scores: enough workgroups for
+// about one per CU, each chunk at least 16 k long (1: no split).  Measured on
+// rows of 32768 (B = 64, k = 2048): chunks of 8192 or 16384 make the two
+// launches slower than one workgroup per row (41 and 38 us against 28); on
+// rows up to 131072 (B = 128), two chunks per row gain about 10%.
+int topk_split_chunks(int64_t T, int32_t n_cap, int32_t k) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                 hipSuccess && v > 0)
+      n_cu = v;
+    else
+      return 1;
+  }
+  if (T <= 0 || n_cap <= 0 || k <= 0) return 1;
+  int nch = (int)std::min<int64_t>(kMaxChunks, n_cu / T);
+  while (nch > 1 && (n_cap + nch - 1) / nch < 16 * k) --nch;
+  return std::max(nch, 1);
+}
+
+size_t topk_workspace_bytes(int64_t T, int32_t n_cap, int32_t k) {
+  const int nch = topk_split_chunks(T, n_cap, k);
+  if (nch <= 1) return 0;
+  return align_up((size_t)T * nch * k * 4, 256) + align_up((size_t)T * nch * 4, 256);
+}
+
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
-                       int32_t k, int32_t *idx, hipStream_t s) {
+                       int32_t k, int32_t *idx, hipStream_t s, void *ws, size_t ws_bytes) {
   if (T == 0) return hipSuccess;
-  static bool attr_done = false;
+  static bool attr_done = false;  // per process: the attribute holds for every device
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)topk_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kTopkSmem);
-    if (e != hipSuccess) return e;
+    for (const void *f : {(const void *)topk_rows_kernel, (const void *)topk_merge_kernel}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTopkSmem);
+      if (e != hipSuccess) return e;
+    }
     attr_done = true;
   }
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, k,
-                     idx);
+  const int nch = ws ? topk_split_chunks(T, n_cap, k) : 1;
+  if (nch > 1 && ws_bytes >= topk_workspace_bytes(T, n_cap, k)) {
+    // chunk-wise selections, then one merge per row over their union
+    const int chunk = (int)align_up((size_t)((n_cap + nch - 1) / nch), 4);
+    int32_t *cpos = (int32_t *)ws;
+    int32_t *ccnt = (int32_t *)((char *)ws + align_up((size_t)T * nch * k * 4, 256));
+    hipLaunchKernelGGL(topk_rows_kernel, dim3((uint32_t)(T * nch)), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid,
+                       n_cap, nch, chunk, k, cpos, ccnt);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, cpos, ccnt, nch, chunk,
+                       k, idx);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(T), dim3(kThreads), kTopkSmem, s, scores, ld, n_valid, n_cap, 1, n_cap,
+                     k, idx, (int32_t *)nullptr);
   return hipGetLastError();
 }
 }  // namespace dsa

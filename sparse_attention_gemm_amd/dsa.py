@@ -21,7 +21,7 @@ DSA_F32, DSA_BF16, DSA_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
                 4: "DSA_ERR_HIP"}
 EXPORTS = (
-    "dsa_last_error", "dsa_version", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select",
+    "dsa_last_error", "dsa_version", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_topk_workspace_bytes",
     "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_fwd", "dsa_prefill_workspace_bytes", "dsa_prefill",
     "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
     "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd", "dsa_masked_mha_workspace_bytes",
@@ -70,6 +70,8 @@ def load():
     L.dsa_quantize_e4m3_per_token.argtypes = [_P, _I64, _I32, _P, _P, _P]
     L.dsa_indexer_scores.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I64, _P]
     L.dsa_topk_select.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
+    L.dsa_topk_workspace_bytes.argtypes = [_I32, _I64, _I32]
+    L.dsa_topk_workspace_bytes.restype = _SZ
     L.dsa_sparse_mla_workspace_bytes.argtypes = [_I32, _I32, _I32]
     L.dsa_sparse_mla_workspace_bytes.restype = _SZ
     L.dsa_sparse_mla_fwd.argtypes = [_P, _P, ctypes.c_int, _P, _I32, _I32, _I64, _I32, _F32, _P, _P, _P, _SZ, _P]
@@ -149,6 +151,10 @@ def dsa_topk_select(scores, n_valid, k, idx, T=None, ld_scores=None, workspace=N
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().dsa_topk_select(_ptr(scores), ld, _ptr(n_valid), T, k, _ptr(idx), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
+
+
+def dsa_topk_workspace_bytes(T: int, ld_scores: int, k: int) -> int:
+    return int(load().dsa_topk_workspace_bytes(T, ld_scores, k))
 
 
 def dsa_sparse_mla_workspace_bytes(T: int, H: int, k: int) -> int:

@@ -155,6 +155,28 @@ def test_topk_matches_oracle_on_same_scores(dsa, ora, n, k):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("n,k", [(70000, 2048), (131072, 2048), (33000, 256), (20000, 1)])
+def test_topk_split_rows_match_oracle(dsa, ora, n, k):
+    """With a workspace, a short batch splits each row into column chunks and
+    merges their selections: the result must still be the oracle's exactly
+    (ties across chunk boundaries, -inf scores, a row shorter than k)."""
+    T = 4
+    _say(f"topk split n={n} k={k}")
+    sc = synth.normal(9, 1, (T, n))
+    sc[0, :100] = -float("inf")
+    sc[1] = torch.round(sc[1] * 4) / 4  # heavy ties, across every chunk
+    sc[2] = 0.25                         # one tie class
+    nv = torch.tensor([n, n - 17, max(1, n // 3), max(1, k - 5)], dtype=torch.int32)
+    nbytes = dsa.dsa_topk_workspace_bytes(T, n, k)
+    assert nbytes > 0, "this batch should be split"
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk_select(sc.to(DEV), nv.to(DEV), k, idx, workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = ora.topk_rows(sc.double().numpy(), nv.numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 def test_topk_negative_zero_and_all_equal(dsa, ora):
     _say("topk -0 / all equal")
     n, k = 5000, 300
