@@ -64,7 +64,8 @@ enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char *dsa_last_error(void);
 
-/* Library version string. */
+/* Library version string: "libdsa <version> gfx950 src=<hash>", where <hash>
+ * identifies the sources the library was built from. */
 const char *dsa_version(void);
 
 /* ---------------------------------------------------------------------------
@@ -325,8 +326,12 @@ dsa_status dsa_sparse_mla_paged_fwd(const void *q, const void *kv_pool, int64_t 
  * Paged cache append (MLA's latent cache: jienda.com, section 2.1): write one
  * token per sequence into the pools at logical position pos[b].
  *   latent [B,576] BF16, k8 [B,D_I] E4M3, ks [B] fp32, pos [B] int32 (device)
- *   pools and block_table as for dsa_decode.  Positions must be mapped by the
- *   block table (the page must exist); rows of different b must differ.
+ *   pools and block_table as for dsa_decode; D_I must be 128 (the row stride
+ *   of the key pool that dsa_decode reads).  A position that the block table
+ *   does not map (negative, past max_blocks, an unmapped page, a row past the
+ *   pool) writes nothing; rows of different b must differ.
+ * dsa_decode does not append: a serving step calls this, then dsa_decode
+ * with ctx_len grown by one, so the new token is its own query's candidate.
  */
 dsa_status dsa_paged_cache_append(const void *latent, const uint8_t *k8, const float *ks,
                                   const int32_t *pos, int32_t B, int32_t D_I,

@@ -11,7 +11,8 @@ Functions follow the plain definitions written out in dsa_oracle.c:
   * sparse MLA-MQA attention over the selected latent rows,
   * masked multi-head attention in MLA's multi-head form (short-prefill mode),
   * the indexer's KL-alignment loss per query token,
-  * one paged decode query per sequence.
+  * one paged decode query per sequence,
+  * the paged cache append of one new token per sequence.
 """
 from __future__ import annotations
 
@@ -67,6 +68,7 @@ def lib():
         L.ora_indexer_kl_rows.argtypes = [ctypes.c_int, P, P, P, P, i32, i32, i32, dbl, P, i64, P, P]
         L.ora_decode.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                  dbl, P, i64, P, P, P, P]
+        L.ora_paged_cache_append.argtypes = [P, P, P, P, i32, i32, i32, P, i32, i64, P, P, P]
         _lib = L
     return _lib
 
@@ -254,3 +256,23 @@ def decode(q8, qs, w, q, k8_pool, ks_pool, kv_pool, block_table, ctx, k, sm_scal
                      _p(ctx), B, H_I, D_I, H, k, Dqk, Dv, float(sm_scale), _p(seqs), n, _p(idx),
                      _p(tau), _p(o), _p(lse))
     return idx, tau, o, lse
+
+
+def paged_cache_append(latent, k8, ks, pos, block_table, kv_pool, k8_pool, ks_pool):
+    """Write token b (latent [B, Dqk] bf16, k8 [B, D_I] E4M3, ks [B] fp32) at
+    logical position pos[b] of sequence b into copies of the pools (kv
+    [n, Dqk] bf16 bits, k8 [n, D_I] u8, ks [n] f32; any leading shape that
+    flattens to rows) -> the three updated pools (numpy)."""
+    lat, k8, ks = _np(latent), _np(k8, np.uint8), _np(ks, np.float32)
+    assert lat.dtype == np.uint16
+    pos, bt = _np(pos, np.int32), _np(block_table, np.int32)
+    kvp = np.array(_np(kv_pool), copy=True)
+    k8p = np.array(_np(k8_pool, np.uint8), copy=True)
+    ksp = np.array(_np(ks_pool, np.float32), copy=True)
+    B, Dqk = lat.shape
+    D_I = k8.shape[1]
+    n_rows = ksp.size
+    assert kvp.size == n_rows * Dqk and k8p.size == n_rows * D_I and bt.shape[0] == B
+    lib().ora_paged_cache_append(_p(lat), _p(k8), _p(ks), _p(pos), B, D_I, Dqk, _p(bt), bt.shape[1], n_rows,
+                                 _p(kvp), _p(k8p), _p(ksp))
+    return kvp, k8p, ksp

@@ -486,6 +486,43 @@ void ora_decode(const uint8_t *q8, const float *qs, const float *w, const uint16
     }
 }
 
+/*
+ * Paged cache append: the latent KV cache of MLA holds one compressed latent
+ * row per token (jienda.com, section 2.1), and the indexer keeps one FP8 key
+ * with its scale per token; decode adds the new token of each sequence to
+ * both.  Token b goes to logical position pos[b] of sequence b, i.e. physical
+ * row  block_table[b*max_blocks + pos[b]/64]*64 + pos[b]%64  of each pool:
+ *   kv pool [n_pool_rows, Dqk] BF16 <- latent [B, Dqk]
+ *   k8 pool [n_pool_rows, D_I] E4M3 <- k8 [B, D_I]
+ *   ks pool [n_pool_rows] fp32      <- ks [B]
+ * A position outside the table (negative, page past max_blocks), an unmapped
+ * page (-1) or a row past the pool writes nothing.  Every other pool row is
+ * left as it was.
+ */
+void ora_paged_cache_append(const uint16_t *latent, const uint8_t *k8, const float *ks, const int32_t *pos,
+                            int32_t B, int32_t D_I, int32_t Dqk, const int32_t *block_table, int32_t max_blocks,
+                            int64_t n_pool_rows, uint16_t *kv_pool, uint8_t *k8_pool, float *ks_pool)
+{
+    int32_t b, d;
+    for (b = 0; b < B; ++b) {
+        int32_t p = pos[b], blk;
+        int64_t row;
+        if (p < 0 || p / 64 >= max_blocks)
+            continue;
+        blk = block_table[(int64_t)b * max_blocks + p / 64];
+        if (blk < 0)
+            continue;
+        row = (int64_t)blk * 64 + p % 64;
+        if (row >= n_pool_rows)
+            continue;
+        for (d = 0; d < Dqk; ++d)
+            kv_pool[row * Dqk + d] = latent[(int64_t)b * Dqk + d];
+        for (d = 0; d < D_I; ++d)
+            k8_pool[row * D_I + d] = k8[(int64_t)b * D_I + d];
+        ks_pool[row] = ks[b];
+    }
+}
+
 /* ------------------------------------------------- masked MHA (short prefill) */
 
 /*

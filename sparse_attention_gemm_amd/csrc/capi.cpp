@@ -66,7 +66,12 @@ using namespace dsa;
 extern "C" {
 
 const char *dsa_last_error(void) { return g_err; }
-const char *dsa_version(void) { return "libdsa 0.1 gfx950"; }
+#ifndef DSA_SOURCE_HASH
+#define DSA_SOURCE_HASH "unstamped"
+#endif
+// the build stamps the hash of the sources it compiled, so a binding can tell
+// a library built from other sources
+const char *dsa_version(void) { return "libdsa 0.2 gfx950 src=" DSA_SOURCE_HASH; }
 
 dsa_status dsa_quantize_e4m3_per_token(const float *x, int64_t rows, int32_t cols, uint8_t *x8,
                                        float *scale, hipStream_t stream) {
@@ -384,16 +389,13 @@ dsa_status dsa_sparse_mla_paged_fwd(const void *q, const void *kv_pool, int64_t 
                    "sparse mla launch");
 }
 
-dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  CLEAR_ERR();
-  dsa_status st = check_decode(a, true);
-  if (st != DSA_OK) return st;
-  if (a->B == 0) return DSA_OK;
-  const size_t need = dsa_decode_workspace_bytes(a);
-  REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
-          workspace ? workspace_bytes : (size_t)0, need);
+// The decode steps on a validated request, with scratch carved from `ws`
+// (at least dsa_decode_workspace_bytes(a) bytes): fp32 score rows [B, ld],
+// then the selection [B, k] unless the caller takes it in idx_out, then one
+// region used first by a split top-k and then by the split attention.
+static dsa_status decode_run(const dsa_decode_args *a, void *ws, hipStream_t stream) {
   const int64_t ld = decode_ld(a);
-  char *p = (char *)workspace;
+  char *p = (char *)ws;
   float *scores = (float *)p;
   p += align_up((size_t)a->B * ld * 4, 256);
   int32_t *idx = a->idx_out;
@@ -406,10 +408,10 @@ dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspac
   const int splits = mla_splits(a->B, a->H, a->k);
   if (splits > 1) mla_ws_split(p, a->B, a->H, a->k, &po, &pml);
   const size_t topk_ws = topk_workspace_bytes(a->B, a->max_ctx, a->k);  // the same region, before the attention
-  st = hip_check(launch_decode_indexer(a->q8, a->q_scale, a->w, a->k8_pool, a->ks_pool, a->block_table,
-                                       a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores, ld,
-                                       stream),
-                 "decode indexer launch");
+  dsa_status st = hip_check(launch_decode_indexer(a->q8, a->q_scale, a->w, a->k8_pool, a->ks_pool, a->block_table,
+                                                  a->max_blocks, a->ctx_len, a->B, a->max_ctx, a->n_pool_rows, scores,
+                                                  ld, stream),
+                            "decode indexer launch");
   if (st != DSA_OK) return st;
   st = hip_check(launch_topk(scores, ld, a->ctx_len, a->max_ctx, a->B, a->k, idx, stream, topk_ws ? p : nullptr,
                              topk_ws),
@@ -418,6 +420,17 @@ dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspac
   return hip_check(launch_sparse_mla_bf16(a->q, a->kv_pool, idx, a->block_table, a->max_blocks, a->n_pool_rows,
                                           a->B, a->H, a->k, a->sm_scale, a->out, a->lse, splits, po, pml, stream),
                    "sparse mla launch");
+}
+
+dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  dsa_status st = check_decode(a, true);
+  if (st != DSA_OK) return st;
+  if (a->B == 0) return DSA_OK;
+  const size_t need = dsa_decode_workspace_bytes(a);
+  REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
+          workspace ? workspace_bytes : (size_t)0, need);
+  return decode_run(a, workspace, stream);
 }
 
 dsa_status dsa_paged_cache_append(const void *latent, const uint8_t *k8, const float *ks, const int32_t *pos,
@@ -429,7 +442,8 @@ dsa_status dsa_paged_cache_append(const void *latent, const uint8_t *k8, const f
   REQUIRE(max_blocks >= 1, DSA_ERR_INVALID_ARG, "max_blocks must be >= 1");
   REQUIRE(n_pool_rows > 0 && n_pool_rows % DSA_PAGE == 0, DSA_ERR_INVALID_ARG,
           "n_pool_rows must be a positive multiple of 64");
-  REQUIRE(D_I > 0 && D_I % 16 == 0 && D_I <= 128, DSA_ERR_UNSUPPORTED, "D_I must be a multiple of 16, <= 128");
+  // the decode indexer reads the key pool with a 128-byte row stride
+  REQUIRE(D_I == 128, DSA_ERR_UNSUPPORTED, "the paged key pool needs D_I = 128 (got %d)", D_I);
   if (B == 0) return DSA_OK;
   REQUIRE(latent && k8 && ks && pos && block_table && kv_pool && k8_pool && ks_pool, DSA_ERR_INVALID_ARG,
           "null pointer");

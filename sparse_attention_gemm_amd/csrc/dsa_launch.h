@@ -1,8 +1,14 @@
 // dsa_launch.h -- host-side launchers of the library's kernels and the
 // C ABI layer's helpers (status, messages).  Each launcher enqueues its
 // kernels on the given stream and validates nothing: the C ABI layer does.
+// Host-only: it needs the HIP runtime API, not the device headers, so the
+// C ABI layer also compiles as plain C++ (the host sanitizer build).
 #pragma once
-#include "dsa_common.h"
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "dsa.h"
 
 namespace dsa {
 dsa_status fail(dsa_status st, const char *fmt, ...);
@@ -51,6 +57,7 @@ hipError_t launch_decode_indexer(const uint8_t *q8, const float *qs, const float
 // Masked MHA in MLA's multi-head form (BF16; per head 128 + 64 logit dims,
 // 128 value dims, latent 512 + 64).  workspace: masked_mha_workspace_bytes(L, H).
 size_t masked_mha_workspace_bytes(int32_t L, int32_t H);
+size_t masked_mha_kv_bytes(int32_t L, int32_t H);  // bytes of K_h (and of V_h) at the workspace's start
 hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, const void *w_uv,
                              const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale, void *out,
                              float *lse, void *workspace, hipStream_t s);

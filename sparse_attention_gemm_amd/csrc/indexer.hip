@@ -3,6 +3,7 @@
 // Used for decode-sized problems, for the tiny fp32 workload and to check the
 // fused prefill kernel stage by stage.  Scores of keys the query may not see
 // (s > q_pos[t]) are written as -inf.
+#include "dsa_common.h"
 #include "dsa_launch.h"
 #include "indexer_core.h"
 

@@ -26,13 +26,15 @@
 //    and values in fp16.
 #include <algorithm>
 
+#include "dsa_common.h"
 #include "dsa_launch.h"
+#include "dsa_sizes.h"
 
 namespace {
 
 constexpr int kDc = 512;   // compressed latent dims
 constexpr int kDr = 64;    // rope dims (shared by every head)
-constexpr int kDn = 128;   // per-head key dims from the up-projection
+constexpr int kDn = dsa::kMhaDn;  // per-head key dims from the up-projection
 constexpr int kDvh = 128;  // per-head value dims
 constexpr int kDq = kDn + kDr;
 constexpr int kDl = kDc + kDr;
@@ -57,7 +59,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 
 // ------------------------------------------------------------- up-projection
 constexpr int kUpE = 2 * kDn;  // output rows per workgroup: K_h (W_uk[h] rows), then V_h (W_uv[h] rows)
-constexpr int kUpT = 256;      // tokens per workgroup (K_h and V_h rows are padded to a multiple of this)
+constexpr int kUpT = dsa::kMhaUpT;  // tokens per workgroup (K_h and V_h rows are padded to a multiple of this)
 constexpr int kUpK = 32;       // latent dims per LDS chunk
 constexpr int kUpSlots = 4;    // LDS row: 4 x 16 B, unpadded; chunk j of row r sits at chunk up_chunk(r, j)
 constexpr int kUpRow = kUpSlots * 16;
@@ -183,6 +185,7 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int32_t *__restrict
 // ------------------------------------------------------------ attention
 constexpr int kQW = 32;        // queries per wave (two groups of 16)
 constexpr int kQB = 4 * kQW;   // queries per workgroup
+static_assert(kQB == dsa::kMhaQB, "queries per workgroup");
 constexpr int kKT = 32;        // keys per tile
 // A tile buffer holds four regions, each filled by whole direct-to-LDS
 // instructions (1 KB, or 256 B for the mask words); instruction i writes
@@ -552,23 +555,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }  // namespace
 
 namespace dsa {
-// K_h and V_h [Lp, H, 128] fp16 with Lp = L rounded up to whole up-projection
-// blocks, then the bit mask [L, ceil(L/32)] u32.
-static size_t mha_kv_bytes(int32_t L, int32_t H) {
-  const size_t Lp = (size_t)(L + kUpT - 1) / kUpT * kUpT;
-  return align_up(Lp * H * kDn * 2, 256);
-}
-static size_t mha_mask_bytes(int32_t L) { return align_up((size_t)L * ((L + 31) / 32) * 4, 256); }
 static size_t mha_groups(int32_t L, int32_t H) { return (size_t)(L + kQB - 1) / kQB * H; }
-size_t masked_mha_workspace_bytes(int32_t L, int32_t H) {
-  return 2 * mha_kv_bytes(L, H) + mha_mask_bytes(L);
-}
 
 hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, const void *w_uv,
                              const int32_t *idx, int32_t L, int32_t H, int32_t k, float sm_scale, void *out,
                              float *lse, void *workspace, hipStream_t s) {
   if (L == 0) return hipSuccess;
-  const size_t kvb = mha_kv_bytes(L, H);
+  const size_t kvb = masked_mha_kv_bytes(L, H);
   _Float16 *kbuf = (_Float16 *)workspace;
   _Float16 *vbuf = (_Float16 *)((char *)workspace + kvb);
   uint32_t *mask = (uint32_t *)((char *)workspace + 2 * kvb);

@@ -36,14 +36,16 @@
 //
 // Workgroups are issued longest-first (the last query block first) so that
 // the causal triangle drains evenly.
+#include "dsa_common.h"
 #include "dsa_launch.h"
+#include "dsa_sizes.h"
 #include "indexer_core.h"
 
 namespace {
 
 constexpr int kTok = 4;         // query tokens per workgroup
 constexpr int kWaves = kTok;    // one per token
-constexpr int kCap = 4096;      // candidate buffer entries per query
+constexpr int kCap = dsa::kPrefillCap;  // candidate buffer entries per query
 constexpr int kTile = 64;       // keys per tile
 constexpr int kKRow = 160;      // LDS bytes per key row: 128 + 32 pad (40 dwords mod 64: conflict-free reads)
 constexpr int kKSlots = kKRow / 16;
@@ -356,7 +358,6 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
 }  // namespace
 
 namespace dsa {
-size_t prefill_candidate_bytes(int32_t L) { return (size_t)L * 2 * kCap * sizeof(uint32_t); }
 
 hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const uint8_t *k8,
                                        const float *ks, const float *w, int32_t L, int32_t k,

@@ -9,6 +9,7 @@
 // hits L2/L1), so HBM traffic is 4 B in + 1 B out per element plus 4 B per
 // row.  Rows of 128 and of 1024, 2048, 4096 or 8192 have kernels of their own
 // (below).
+#include "dsa_common.h"
 #include "dsa_launch.h"
 
 namespace {

@@ -30,6 +30,7 @@
 //    combine (used when there are too few queries to fill the GPU).
 #include <algorithm>
 
+#include "dsa_common.h"
 #include "dsa_launch.h"
 
 namespace {
@@ -284,7 +285,17 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (!fixed && *cx.flag) return false;  // uniform: read after the final barrier
+  if (!fixed) {
+    // Uniform: every wave reads the flag after the final barrier, and nothing
+    // writes it again until the redo's set-up clears it.  The barrier below
+    // keeps that clear behind every wave's read, so no wave can miss the
+    // overshoot and take the accept path alone.
+    const int over = *cx.flag;
+    if (over) {
+      __syncthreads();
+      return false;
+    }
+  }
   // softmax sums of the wave's head tile -> LDS, for the waves that own other value dims
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);

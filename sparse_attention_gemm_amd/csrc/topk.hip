@@ -21,7 +21,9 @@
 // (massive ties), the output pass runs over the row in global memory instead.
 #include <algorithm>
 
+#include "dsa_common.h"
 #include "dsa_launch.h"
+#include "dsa_sizes.h"
 
 namespace {
 
@@ -30,7 +32,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCand = 18432;  // candidates held in LDS
 constexpr int kU = 8;         // groups of 4 row elements per thread in flight (32768 elements)
-constexpr int kMaxChunks = 8;  // chunks per row of a split selection
+constexpr int kMaxChunks = dsa::kTopkMaxChunks;  // chunks per row of a split selection
 static_assert(kMaxChunks * 2048 <= 18432, "a merge's candidates fit in LDS");
 
 struct TopkShared {
@@ -428,28 +430,6 @@ hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStre
 // rows of 32768 (B = 64, k = 2048): chunks of 8192 or 16384 make the two
 // launches slower than one workgroup per row (41 and 38 us against 28); on
 // rows up to 131072 (B = 128), two chunks per row gain about 10%.
-int topk_split_chunks(int64_t T, int32_t n_cap, int32_t k) {
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
-                                                 hipSuccess && v > 0)
-      n_cu = v;
-    else
-      return 1;
-  }
-  if (T <= 0 || n_cap <= 0 || k <= 0) return 1;
-  int nch = (int)std::min<int64_t>(kMaxChunks, n_cu / T);
-  while (nch > 1 && (n_cap + nch - 1) / nch < 16 * k) --nch;
-  return std::max(nch, 1);
-}
-
-size_t topk_workspace_bytes(int64_t T, int32_t n_cap, int32_t k) {
-  const int nch = topk_split_chunks(T, n_cap, k);
-  if (nch <= 1) return 0;
-  return align_up((size_t)T * nch * k * 4, 256) + align_up((size_t)T * nch * 4, 256);
-}
-
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t n_cap, int32_t T,
                        int32_t k, int32_t *idx, hipStream_t s, void *ws, size_t ws_bytes) {
   if (T == 0) return hipSuccess;

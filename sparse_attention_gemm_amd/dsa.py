@@ -55,6 +55,21 @@ class DecodeArgs(ctypes.Structure):
 
 
 _lib = None
+F32_T, U8_T, I32_T = torch.float32, torch.uint8, torch.int32
+
+
+def _check_fresh(L):
+    """Refuse a library built from other sources than the ones beside it (a
+    stale build would silently test old kernels).  Skipped when the sources
+    are not present."""
+    from . import build
+    if not os.path.isdir(build.CSRC):
+        return
+    got = L.dsa_version().decode()
+    want = build.source_hash()
+    if not got.endswith("src=" + want):
+        raise ImportError(f"libdsa.so is stale ({got}; sources are {want}); "
+                          "rebuild with python -m sparse_attention_gemm_amd.build")
 
 
 def load():
@@ -67,6 +82,7 @@ def load():
     L = ctypes.CDLL(LIB_PATH)
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_version.restype = ctypes.c_char_p
+    _check_fresh(L)
     L.dsa_quantize_e4m3_per_token.argtypes = [_P, _I64, _I32, _P, _P, _P]
     L.dsa_indexer_scores.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I64, _P]
     L.dsa_topk_select.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
@@ -98,11 +114,20 @@ def load():
     return L
 
 
-def _ptr(t):
+def _ptr(t, dtype=None, name="tensor"):
+    """Device address of a torch tensor (ints pass through as raw addresses).
+    The library reads tensors as dense, row-major device arrays: anything
+    else is refused here, before its address reaches a kernel."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     return t.data_ptr()
 
 
@@ -131,7 +156,8 @@ def dsa_quantize_e4m3_per_token(x, x8, scale, rows=None, cols=None, stream=None)
     """x [rows, cols] fp32 -> x8 [rows, cols] uint8 (E4M3), scale [rows] fp32."""
     rows = x.numel() // x.shape[-1] if rows is None else rows
     cols = x.shape[-1] if cols is None else cols
-    _check(load().dsa_quantize_e4m3_per_token(_ptr(x), rows, cols, _ptr(x8), _ptr(scale), _stream(stream)))
+    _check(load().dsa_quantize_e4m3_per_token(_ptr(x, F32_T, "x"), rows, cols, _ptr(x8, U8_T, "x8"),
+                                              _ptr(scale, F32_T, "scale"), _stream(stream)))
 
 
 def dsa_indexer_scores(q, q_scale, k, k_scale, w, q_pos, scores, dt, T=None, S=None, H_I=None, D_I=None,
@@ -141,15 +167,18 @@ def dsa_indexer_scores(q, q_scale, k, k_scale, w, q_pos, scores, dt, T=None, S=N
     H_I = q.shape[1] if H_I is None else H_I
     D_I = q.shape[2] if D_I is None else D_I
     ld = scores.stride(0) if ld_scores is None else ld_scores
-    _check(load().dsa_indexer_scores(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(q_pos),
-                                     T, S, H_I, D_I, dt, _ptr(scores), ld, _stream(stream)))
+    qk_t = U8_T if dt == DSA_E4M3 else F32_T
+    _check(load().dsa_indexer_scores(_ptr(q, qk_t, "q"), _ptr(q_scale, F32_T, "q_scale"), _ptr(k, qk_t, "k"),
+                                     _ptr(k_scale, F32_T, "k_scale"), _ptr(w, F32_T, "w"), _ptr(q_pos, I32_T, "q_pos"),
+                                     T, S, H_I, D_I, dt, _ptr(scores, F32_T, "scores"), ld, _stream(stream)))
 
 
 def dsa_topk_select(scores, n_valid, k, idx, T=None, ld_scores=None, workspace=None, stream=None):
     T = scores.shape[0] if T is None else T
     ld = scores.stride(0) if ld_scores is None else ld_scores
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().dsa_topk_select(_ptr(scores), ld, _ptr(n_valid), T, k, _ptr(idx), _ptr(workspace), ws_bytes,
+    _check(load().dsa_topk_select(_ptr(scores, F32_T, "scores"), ld, _ptr(n_valid, I32_T, "n_valid"), T, k,
+                                  _ptr(idx, I32_T, "idx"), _ptr(workspace, name="workspace"), ws_bytes,
                                   _stream(stream)))
 
 
@@ -168,8 +197,10 @@ def dsa_sparse_mla_fwd(q, kv, idx, sm_scale, out, lse=None, dt=None, workspace=N
     if dt is None:
         dt = DSA_BF16 if q.dtype == torch.bfloat16 else DSA_F32
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().dsa_sparse_mla_fwd(_ptr(q), _ptr(kv), dt, _ptr(idx), T, H, N, k, float(sm_scale), _ptr(out),
-                                     _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    at = torch.bfloat16 if dt == DSA_BF16 else torch.float32
+    _check(load().dsa_sparse_mla_fwd(_ptr(q, at, "q"), _ptr(kv, at, "kv"), dt, _ptr(idx, I32_T, "idx"), T, H, N, k,
+                                     float(sm_scale), _ptr(out, at, "out"), _ptr(lse, F32_T, "lse"),
+                                     _ptr(workspace, name="workspace"), ws_bytes, _stream(stream)))
 
 
 def dsa_masked_mha_workspace_bytes(L: int, H: int) -> int:
@@ -181,31 +212,40 @@ def dsa_masked_mha_prefill(q, kv, w_uk, w_uv, idx, sm_scale, out, workspace, lse
     L, H = q.shape[0], q.shape[1]
     k = idx.shape[1]
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(load().dsa_masked_mha_prefill(_ptr(q), _ptr(kv), _ptr(w_uk), _ptr(w_uv), _ptr(idx), L, H, k,
-                                         float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                                         _stream(stream)))
+    bf = torch.bfloat16
+    _check(load().dsa_masked_mha_prefill(_ptr(q, bf, "q"), _ptr(kv, bf, "kv"), _ptr(w_uk, bf, "w_uk"),
+                                         _ptr(w_uv, bf, "w_uv"), _ptr(idx, I32_T, "idx"), L, H, k, float(sm_scale),
+                                         _ptr(out, bf, "out"), _ptr(lse, F32_T, "lse"),
+                                         _ptr(workspace, name="workspace"), ws_bytes, _stream(stream)))
 
 
 def dsa_indexer_scores_at(q8, q_scale, k8, k_scale, w, idx, out, S=None, stream=None):
     """I[t, idx[t, a]] for E4M3 q8 [T, H_I, 128], k8 [S, 128] -> out [T, k] fp32."""
     T, H_I, D_I = q8.shape
     S = k8.shape[0] if S is None else S
-    _check(load().dsa_indexer_scores_at(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(w), _ptr(idx), T, S,
-                                        H_I, D_I, idx.shape[1], _ptr(out), _stream(stream)))
+    _check(load().dsa_indexer_scores_at(_ptr(q8, U8_T, "q8"), _ptr(q_scale, F32_T, "q_scale"), _ptr(k8, U8_T, "k8"),
+                                        _ptr(k_scale, F32_T, "k_scale"), _ptr(w, F32_T, "w"), _ptr(idx, I32_T, "idx"),
+                                        T, S, H_I, D_I, idx.shape[1], _ptr(out, F32_T, "out"), _stream(stream)))
 
 
 def dsa_indexer_kl_fwd(q, kv, idx, idx_scores, lse, sm_scale, kl, N=None, stream=None):
     """Per-token KL(p || pi): q [T, H, 576], kv [N, 576] bf16, idx/idx_scores [T, k], lse [T, H] -> kl [T]."""
     T, H = q.shape[0], q.shape[1]
     N = kv.shape[0] if N is None else N
-    _check(load().dsa_indexer_kl_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(idx_scores), _ptr(lse), T, H, N,
-                                     idx.shape[1], float(sm_scale), _ptr(kl), _stream(stream)))
+    bf = torch.bfloat16
+    _check(load().dsa_indexer_kl_fwd(_ptr(q, bf, "q"), _ptr(kv, bf, "kv"), _ptr(idx, I32_T, "idx"),
+                                     _ptr(idx_scores, F32_T, "idx_scores"), _ptr(lse, F32_T, "lse"), T, H, N,
+                                     idx.shape[1], float(sm_scale), _ptr(kl, F32_T, "kl"), _stream(stream)))
 
 
 def make_prefill_args(L, H_I, D_I, H, k, idx_dt, q_idx, q_scale, k_idx, k_scale, w, attn_dt, q, kv, sm_scale,
                       idx, out, lse=None) -> PrefillArgs:
-    return PrefillArgs(L, H_I, D_I, H, k, idx_dt, _ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w),
-                       attn_dt, _ptr(q), _ptr(kv), float(sm_scale), _ptr(idx), _ptr(out), _ptr(lse))
+    it = U8_T if idx_dt == DSA_E4M3 else F32_T
+    at = torch.bfloat16 if attn_dt == DSA_BF16 else F32_T
+    return PrefillArgs(L, H_I, D_I, H, k, idx_dt, _ptr(q_idx, it, "q_idx"), _ptr(q_scale, F32_T, "q_scale"),
+                       _ptr(k_idx, it, "k_idx"), _ptr(k_scale, F32_T, "k_scale"), _ptr(w, F32_T, "w"), attn_dt,
+                       _ptr(q, at, "q"), _ptr(kv, at, "kv"), float(sm_scale), _ptr(idx, I32_T, "idx"),
+                       _ptr(out, at, "out"), _ptr(lse, F32_T, "lse"))
 
 
 def dsa_prefill_workspace_bytes(args: PrefillArgs) -> int:
@@ -224,9 +264,12 @@ def dsa_prefill_select(args: PrefillArgs, workspace=None, stream=None):
 
 def make_decode_args(B, H_I, D_I, H, k, q8, q_scale, w, q, k8_pool, ks_pool, kv_pool, n_pool_rows, block_table,
                      max_blocks, ctx_len, max_ctx, sm_scale, out, lse=None, idx_out=None) -> DecodeArgs:
-    return DecodeArgs(B, H_I, D_I, H, k, _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(q), _ptr(k8_pool), _ptr(ks_pool),
-                      _ptr(kv_pool), n_pool_rows, _ptr(block_table), max_blocks, _ptr(ctx_len), max_ctx,
-                      float(sm_scale), _ptr(idx_out), _ptr(out), _ptr(lse))
+    bf = torch.bfloat16
+    return DecodeArgs(B, H_I, D_I, H, k, _ptr(q8, U8_T, "q8"), _ptr(q_scale, F32_T, "q_scale"), _ptr(w, F32_T, "w"),
+                      _ptr(q, bf, "q"), _ptr(k8_pool, U8_T, "k8_pool"), _ptr(ks_pool, F32_T, "ks_pool"),
+                      _ptr(kv_pool, bf, "kv_pool"), n_pool_rows, _ptr(block_table, I32_T, "block_table"), max_blocks,
+                      _ptr(ctx_len, I32_T, "ctx_len"), max_ctx, float(sm_scale), _ptr(idx_out, I32_T, "idx_out"),
+                      _ptr(out, bf, "out"), _ptr(lse, F32_T, "lse"))
 
 
 def dsa_decode_workspace_bytes(args: DecodeArgs) -> int:
@@ -249,9 +292,12 @@ def dsa_sparse_mla_paged_fwd(q, kv_pool, block_table, idx, sm_scale, out, lse=No
     k = idx.shape[1]
     n_pool_rows = kv_pool.numel() // 576 if n_pool_rows is None else n_pool_rows
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().dsa_sparse_mla_paged_fwd(_ptr(q), _ptr(kv_pool), n_pool_rows, _ptr(block_table),
-                                           block_table.shape[1], _ptr(idx), T, H, k, float(sm_scale), _ptr(out),
-                                           _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    bf = torch.bfloat16
+    _check(load().dsa_sparse_mla_paged_fwd(_ptr(q, bf, "q"), _ptr(kv_pool, bf, "kv_pool"), n_pool_rows,
+                                           _ptr(block_table, I32_T, "block_table"), block_table.shape[1],
+                                           _ptr(idx, I32_T, "idx"), T, H, k, float(sm_scale), _ptr(out, bf, "out"),
+                                           _ptr(lse, F32_T, "lse"), _ptr(workspace, name="workspace"), ws_bytes,
+                                           _stream(stream)))
 
 
 def dsa_paged_cache_append(latent, k8, ks, pos, block_table, kv_pool, k8_pool, ks_pool, B=None, D_I=None,
@@ -260,6 +306,8 @@ def dsa_paged_cache_append(latent, k8, ks, pos, block_table, kv_pool, k8_pool, k
     D_I = k8.shape[-1] if D_I is None else D_I
     max_blocks = block_table.shape[1] if max_blocks is None else max_blocks
     n_pool_rows = kv_pool.numel() // 576 if n_pool_rows is None else n_pool_rows
-    _check(load().dsa_paged_cache_append(_ptr(latent), _ptr(k8), _ptr(ks), _ptr(pos), B, D_I, _ptr(block_table),
-                                         max_blocks, _ptr(kv_pool), _ptr(k8_pool), _ptr(ks_pool), n_pool_rows,
-                                         _stream(stream)))
+    bf = torch.bfloat16
+    _check(load().dsa_paged_cache_append(_ptr(latent, bf, "latent"), _ptr(k8, U8_T, "k8"), _ptr(ks, F32_T, "ks"),
+                                         _ptr(pos, I32_T, "pos"), B, D_I, _ptr(block_table, I32_T, "block_table"),
+                                         max_blocks, _ptr(kv_pool, bf, "kv_pool"), _ptr(k8_pool, U8_T, "k8_pool"),
+                                         _ptr(ks_pool, F32_T, "ks_pool"), n_pool_rows, _stream(stream)))

@@ -247,6 +247,9 @@ def test_cache_append_validation(dsa):
     f = dsa.load().dsa_paged_cache_append
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, FAKE, 10, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 120, FAKE, 10, FAKE, FAKE, FAKE, 640, None) == dsa.DSA_ERR_UNSUPPORTED
+    # the decode reads the key pool at a 128-byte stride: other key widths are refused
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 64, FAKE, 10, FAKE, FAKE, FAKE, 640, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert "D_I = 128" in dsa.dsa_last_error()
     assert f(FAKE, None, FAKE, FAKE, 4, 128, FAKE, 10, FAKE, FAKE, FAKE, 640, None) == dsa.DSA_ERR_INVALID_ARG
     assert f(None, None, None, None, 0, 128, None, 10, None, None, None, 640, None) == dsa.DSA_OK
 
@@ -259,3 +262,44 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     with pytest.raises(ImportError):
         d.load()
     importlib.reload(d)
+
+
+def test_binding_refuses_host_strided_and_mistyped_tensors(dsa):
+    """The binding passes raw addresses to the library, so it checks each
+    tensor first: host memory, a strided view or the wrong dtype raises before
+    the library is called."""
+    import torch
+    host = torch.zeros((4, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensor"):
+        dsa.dsa_topk_select(host, host[:, 0].to(torch.int32), 4, torch.zeros((4, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="device tensor"):
+        dsa.make_decode_args(1, 64, 128, 16, 4, host.to(torch.uint8), None, None, None, None, None, None, 64, None,
+                             1, None, 1, 0.1, None)
+    # the dtype and layout checks, exercised on the checker itself (no device here)
+    class Fake:
+        is_cuda = True
+
+        def __init__(self, dtype, contiguous=True):
+            self.dtype, self._c = dtype, contiguous
+
+        def is_contiguous(self):
+            return self._c
+
+        def data_ptr(self):
+            return 0x1000
+    assert dsa._ptr(Fake(torch.float32), torch.float32) == 0x1000
+    with pytest.raises(TypeError, match="must be"):
+        dsa._ptr(Fake(torch.float16), torch.bfloat16, "q")
+    with pytest.raises(ValueError, match="contiguous"):
+        dsa._ptr(Fake(torch.float32, contiguous=False), torch.float32)
+
+
+def test_binding_refuses_a_stale_library(dsa, monkeypatch):
+    """A library stamped with other sources' hash is refused on load."""
+    from sparse_attention_gemm_amd import build
+    L = dsa.load()
+    dsa._check_fresh(L)  # the built library matches its sources
+    monkeypatch.setattr(build, "source_hash", lambda: "0123456789abcdef")
+    with pytest.raises(ImportError, match="stale"):
+        dsa._check_fresh(L)
+

@@ -1,8 +1,8 @@
 """GPU parity of every hot-path step against the fp64 oracle, through the C ABI.
 
 Sizes here finish in seconds on the oracle yet span several tiles and ragged
-tails; the full-size workloads are in test_gpu_fullsize.py.  Each test prints
-its case before touching the GPU.
+tails; the full-size workloads (marked slow) are at the end of this file,
+checked on sampled rows.  Each test prints its case before touching the GPU.
 """
 import math
 
@@ -94,8 +94,8 @@ def test_indexer_fp8_scores(dsa, ora, H_I):
     q8 = torch.from_numpy(q8).view(T, H_I, 128)
     g = _gpu_scores(dsa, q8, torch.from_numpy(qs), torch.from_numpy(k8), torch.from_numpy(ks), w, pos, S,
                     dsa.DSA_E4M3)
-    o, a, m = oracle_score_bounds(ora, q8.numpy(), k8, w.numpy(), pos, q_scale=qs, k_scale=ks)
-    check_scores(g, o, a, m, 128 + H_I, "fp8 scores")
+    o, m = oracle_score_bounds(ora, q8.numpy(), k8, w.numpy(), pos, q_scale=qs, k_scale=ks)
+    check_scores(g, o, m, 128 + H_I, "fp8 scores")
 
 
 def test_indexer_fp8_exact_arithmetic(dsa, ora):
@@ -132,8 +132,8 @@ def test_indexer_f32_tiny_config(dsa, ora):
     pos = torch.arange(cfg.L, dtype=torch.int32)
     g = _gpu_scores(dsa, q, None, k, None, w, pos, cfg.L, dsa.DSA_F32)
     rows = np.arange(0, cfg.L, 7)
-    o, a, m = oracle_score_bounds(ora, q.numpy(), k.numpy(), w.numpy(), pos, rows=rows)
-    check_scores(g[rows], o, a, m, cfg.D_I + cfg.H_I, "f32 scores")
+    o, m = oracle_score_bounds(ora, q.numpy(), k.numpy(), w.numpy(), pos, rows=rows)
+    check_scores(g[rows], o, m, cfg.D_I + cfg.H_I, "f32 scores")
 
 
 # ------------------------------------------------------------------ A2
@@ -391,7 +391,7 @@ def test_prefill_select_fused_long(dsa, ora):
     assert not bad, f"fused and unfused selections differ in {len(bad)} rows, first {bad[:5]}"
     # sampled rows against the oracle's scores and selection
     rows = np.array([0, k - 1, k, 4095, 4096, 4097, 9000, L - 2, L - 1])
-    o, _, _ = oracle_score_bounds(ora, q8.cpu().numpy(), k8.cpu().numpy(), w.numpy(),
+    o, _ = oracle_score_bounds(ora, q8.cpu().numpy(), k8.cpu().numpy(), w.numpy(),
                                   torch.arange(L, dtype=torch.int32), q_scale=qs.cpu().numpy(),
                                   k_scale=ks.cpu().numpy(), rows=rows)
     for j, r in enumerate(rows):
@@ -477,27 +477,72 @@ def test_decode_block_shuffle_invariance(dsa):
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
 
 
-def test_paged_cache_append(dsa):
-    _say("paged cache append")
+def test_paged_cache_append(dsa, ora):
+    """The pools after a GPU append equal the oracle's append, byte for byte,
+    including tokens aimed at positions the block table does not map."""
+    _say("paged cache append vs oracle")
     cfg = synth.DecodeConfig("t", 6, 100, 1000, 64, 128, 128, 64, 12, True)
     ctx = synth.decode_ctx(cfg)
-    bt, nb = synth.decode_block_table(cfg, ctx)
+    bt, nb = synth.decode_block_table(cfg, ctx + 1)
     k8p, ksp, kvp = synth.build_decode_pools(cfg, ctx, bt, nb)
     lat, k8, ks = synth.new_token_rows(cfg, 0)
-    pos = (ctx - 1).to(torch.int32)
+    pos = ctx.to(torch.int32).clone()
+    pos[1] = -1                       # nothing written
+    pos[4] = bt.shape[1] * 64 + 3     # past the table: nothing written
     dk8, dks, dkv = k8p.to(DEV), ksp.to(DEV), kvp.to(DEV)
     dl, d8, ds, dp, dbt = lat.to(DEV), k8.to(DEV), ks.to(DEV), pos.to(DEV), bt.to(DEV)
     dsa.dsa_paged_cache_append(dl, d8, ds, dp, dbt, dkv, dk8, dks, n_pool_rows=nb * 64)
     torch.cuda.synchronize()
-    ek8, eks, ekv = k8p.clone(), ksp.clone(), kvp.clone()
+    ekv, ek8, eks = ora.paged_cache_append(lat, k8, ks, pos, bt, kvp.view(-1, 576), k8p.view(-1, 128), ksp.view(-1))
+    assert np.array_equal(dk8.cpu().view(-1, 128).numpy(), ek8)
+    assert np.array_equal(dks.cpu().view(-1).numpy(), eks)
+    assert np.array_equal(dkv.cpu().view(-1, 576).view(torch.int16).numpy().view(np.uint16), ekv)
+    assert not np.array_equal(ekv, kvp.view(-1, 576).view(torch.int16).numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("shuffled", [True, False])
+def test_append_then_decode(dsa, ora, shuffled):
+    """A serving step: append each sequence's new token at position ctx, then
+    decode with ctx + 1 (the new token is its own query's candidate).  The
+    pools match the oracle's append byte for byte, and the decode matches the
+    oracle's decode of the appended pools (contexts ending on a page boundary
+    open a new page)."""
+    _say(f"append then decode shuffled={shuffled}")
+    cfg = synth.DecodeConfig("t", 5, 60, 3000, 64, 128, 128, 2048, 14, shuffled)
+    ctx = synth.decode_ctx(cfg)
+    ctx[0], ctx[1] = 64, 2048         # page boundary; the new token is the 2049th
+    bt, nb = synth.decode_block_table(cfg, ctx + 1)
+    pools = synth.build_decode_pools(cfg, ctx, bt, nb)
+    qside = synth.decode_queries(cfg)
+    lat, k8, ks = synth.new_token_rows(cfg, 3)
+    pos = ctx.to(torch.int32)
+    dk8, dks, dkv = [p.to(DEV) for p in pools]
+    dsa.dsa_paged_cache_append(lat.to(DEV), k8.to(DEV), ks.to(DEV), pos.to(DEV), bt.to(DEV), dkv, dk8, dks,
+                               n_pool_rows=nb * 64)
+    torch.cuda.synchronize()
+    ekv, ek8, eks = ora.paged_cache_append(lat, k8, ks, pos, bt, pools[2].view(-1, 576), pools[0].view(-1, 128),
+                                           pools[1].view(-1))
+    assert np.array_equal(dk8.cpu().view(-1, 128).numpy(), ek8)
+    assert np.array_equal(dks.cpu().view(-1).numpy(), eks)
+    assert np.array_equal(dkv.cpu().view(-1, 576).view(torch.int16).numpy().view(np.uint16), ekv)
+    ctx1 = ctx + 1
+    out, lse, idx = _run_decode(dsa, cfg, ctx1, bt, nb, (dk8, dks, dkv), qside)
+    gidx = idx.cpu().numpy()
+    q8, qs, w, q = qside
+    ridx, rtau, _, _ = ora.decode(q8, qs, w, q, ek8, eks, ekv, bt, ctx1, cfg.k, cfg.sm_scale)
     for b in range(cfg.B):
-        p = int(pos[b])
-        blk = int(bt[b, p // 64])
-        ek8[blk, p % 64] = k8[b]
-        eks[blk, p % 64] = ks[b]
-        ekv[blk, p % 64] = lat[b]
-    assert torch.equal(dk8.cpu(), ek8) and torch.equal(dks.cpu(), eks)
-    assert torch.equal(dkv.cpu().view(torch.int16), ekv.view(torch.int16))
+        c = int(ctx1[b])
+        kb, sb = synth.decode_seq_keys(cfg, b, c - 1)
+        kb = torch.cat([kb, k8[b:b + 1]])
+        sb = torch.cat([sb, ks[b:b + 1]])
+        sc = ora.indexer_rows(q8[b:b + 1], kb, w[b:b + 1], np.array([c - 1], np.int32), q_scale=qs[b:b + 1],
+                              k_scale=sb)
+        check_topk_row(gidx[b], sc[0], c, cfg.k, f"append+decode b={b}")
+        check_topk_row(ridx[b], sc[0], c, cfg.k, f"oracle append+decode b={b}")
+        lat_b = torch.cat([synth.decode_seq_latent(cfg, b, c - 1), lat[b:b + 1]])
+        o, l = ora.sparse_mla_rows(q[b:b + 1], lat_b, gidx[b:b + 1], cfg.sm_scale)
+        check_attention(out[b:b + 1].float().cpu().double().numpy(), lse[b:b + 1].cpu().double().numpy(), o, l,
+                        "bf16", f"append+decode b={b}")
 
 
 def test_decode_equals_its_stages(dsa):
@@ -544,25 +589,53 @@ def test_prefill_select_equals_prefill_selection(dsa):
     assert torch.equal(idx2, t["idx"])
 
 
-@pytest.mark.parametrize("H", [128, 16])
-def test_sparse_mla_bf16_late_large_logits(dsa, ora, H):
+@pytest.mark.parametrize("H,use_ws", [(128, True), (16, True), (128, False), (16, False)])
+def test_sparse_mla_bf16_late_large_logits(dsa, ora, H, use_ws):
     """Logits in a late tile far above the first tile's (over 2^64 in base 2)
-    for some heads: the result must still be the exact softmax."""
-    _say(f"sparse mla bf16 late large logits H={H}")
+    for some heads: the result must still be the exact softmax.  With a
+    workspace the short batch is split across workgroups; without one every
+    query is a single workgroup (the path every prefill takes).  The large
+    component sits in a rope dim, which enters the logits but not the value,
+    so the outputs keep the workload's magnitude."""
+    _say(f"sparse mla bf16 late large logits H={H} ws={use_ws}")
     N, T, k = 3000, 3, 2048
     q = synth.normal(13, 1, (T, H, 576)) * 0.5
     kv = synth.normal(13, 2, (N, 576), std=1 / 24)
-    q[:, ::3, 0] = 30.0            # every third head looks along dim 0
-    kv[:, 0] = 0.01
+    q[:, ::3, 512] = 30.0          # every third head looks along rope dim 0
+    kv[:, 512] = 0.01
     late = torch.arange(2500, 2520)
-    kv[late, 0] = 100.0            # logit 3000 * sm_scale for those heads, only in late rows
+    kv[late, 512] = 100.0          # logit 3000 * sm_scale for those heads, only in late rows
     q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
-    idx = torch.stack([torch.arange(k) + t * 100 for t in range(T)]).to(torch.int32)
-    idx[idx >= N] = -1
-    g, gl = _mla_gpu(dsa, q, kv, idx, 1 / math.sqrt(192), "bf16", use_ws=True)
+    # ascending selections whose last tile holds the late rows
+    idx = torch.stack([torch.cat([torch.arange(k - 20) + t * 100, late]) for t in range(T)]).to(torch.int32)
+    g, gl = _mla_gpu(dsa, q, kv, idx, 1 / math.sqrt(192), "bf16", use_ws=use_ws)
     o, l = ora.sparse_mla_rows(q, kv, idx.numpy(), 1 / math.sqrt(192))
     assert np.isfinite(g).all() and np.isfinite(gl).all()
+    assert l[:, ::3].min() > 150.0 and np.abs(l[:, 1::3]).max() < 20.0   # the spike decides those heads only
     check_attention(g, gl, o, l, "bf16", "mla late large logits")
+
+
+def test_prefill_late_large_logits(dsa, ora):
+    """The fused prefill with a few late latent rows that give some heads
+    logits far above anything in their first tile (through a rope dim, so
+    the values keep the workload's scale): those queries take the recompute
+    path of the unsplit kernel."""
+    L, k, H = 3000, 2048, 16
+    _say(f"prefill late large logits L={L} H={H}")
+    cfg = synth.scaled_down(synth.CONFIGS["prefill16k"], L=L, k=k, H=H, seed=17)
+    q_i, k_i, w, q, kv = _prefill_inputs(cfg)
+    q, kv = q.float(), kv.float()
+    q[:, ::3, 512] = 30.0
+    kv[:, 512] = 0.01
+    kv[2500:2520, 512] = 100.0
+    q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
+    t = _run_prefill(dsa, cfg, q_i, k_i, w, q, kv)
+    rows = np.array([0, 100, 2047, 2499, 2519, 2520, 2600, 2800, 2999])
+    _check_prefill_rows(ora, cfg, q_i, k_i, w, q, kv, t, rows, "prefill late large logits")
+    # the later queries select some of the late rows, past their first tile
+    gidx = t["idx"].cpu().numpy()
+    assert np.isin(np.arange(2500, 2520), gidx[2999]).any()
+    assert (t["lse"].cpu()[2999, ::3] > 150.0).all()
 
 
 # ------------------------------------------------------------------ full-size workloads
@@ -573,10 +646,14 @@ def _sample_rows(L, extra, seed):
 
 
 @pytest.mark.slow
-def test_prefill_full_size_sampled_rows(dsa, ora):
-    """The benchmarked L = 131072 pipeline (quantise -> fused indexer + top-k ->
-    sparse MLA), checked against the oracle on sampled query rows."""
-    cfg = synth.CONFIGS["prefill128k"]
+@pytest.mark.parametrize("name", ["prefill128k", "prefill16k"])
+def test_prefill_full_size_sampled_rows(dsa, ora, name):
+    """The full-size prefill workloads (L = 131072, the benchmarked one, and
+    L = 16384), each through the pipeline the benchmark times (quantise ->
+    fused indexer + top-k -> sparse MLA), checked against the oracle on 64
+    sampled query rows: nine fixed rows at the selection's edges plus 55
+    drawn ones."""
+    cfg = synth.CONFIGS[name]
     L, k = cfg.L, cfg.k
     _say(f"prefill full size L={L}")
     q_i, k_i, w = synth.prefill_indexer_inputs(cfg, device=DEV)
@@ -598,7 +675,8 @@ def test_prefill_full_size_sampled_rows(dsa, ora):
     dsa.dsa_sparse_mla_fwd(q, kv, idx, cfg.sm_scale, out, lse)
     torch.cuda.synchronize()
     del ws
-    rows = _sample_rows(L, 3, 21)
+    rows = _sample_rows(L, 55, 21)
+    assert len(rows) >= 60
     rt = torch.from_numpy(rows).to(DEV)
     # quantiser: bit-exact on the sampled query rows and on every key
     o8, os_ = ora.quantize_rows(q_i[rt].view(len(rows), -1).cpu().numpy())

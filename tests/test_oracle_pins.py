@@ -468,6 +468,72 @@ def test_decode_never_reads_page_tails(ora):
         assert np.array_equal(x, y)
 
 
+# ------------------------------------------------------------ cache append
+def _append_case(shuffled):
+    """Sequences of lengths ctx (one ends on a page boundary, so its next token
+    opens a new page), a block table sized for one more token each, pools
+    holding the first ctx tokens, and the logical token at position ctx."""
+    cfg = synth.DecodeConfig("t", 4, 1, 1, 4, 32, 8, 64, 6, shuffled)
+    ctx = torch.tensor([64, 130, 1, 255], dtype=torch.int64)
+    bt, nb = synth.decode_block_table(cfg, ctx + 1)
+    pools = synth.build_decode_pools(cfg, ctx, bt, nb)
+    lat, k8, ks = [], [], []
+    for b in range(cfg.B):
+        c = int(ctx[b])
+        kb, sb = synth.decode_seq_keys(cfg, b, c + 1)
+        lat.append(synth.decode_seq_latent(cfg, b, c + 1)[c])
+        k8.append(kb[c])
+        ks.append(sb[c])
+    return cfg, ctx, bt, nb, pools, (torch.stack(lat), torch.stack(k8), torch.stack(ks))
+
+
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_cache_append_grows_the_logical_sequence(ora, shuffled):
+    """Appending each sequence's token at position ctx to pools that hold ctx
+    tokens gives, byte for byte, the pools that hold ctx + 1 tokens (the
+    generator writes logical rows independently of the append)."""
+    cfg, ctx, bt, nb, (k8, ks, kv), (lat, tk8, tks) = _append_case(shuffled)
+    kvp, k8p, ksp = ora.paged_cache_append(lat, tk8, tks, ctx.to(torch.int32), bt, kv.view(-1, 576),
+                                           k8.view(-1, cfg.D_I), ks.view(-1))
+    ek8, eks, ekv = synth.build_decode_pools(cfg, ctx + 1, bt, nb)
+    assert np.array_equal(k8p, ek8.view(-1, cfg.D_I).numpy())
+    assert np.array_equal(ksp, eks.view(-1).numpy())
+    assert np.array_equal(kvp, ekv.view(-1, 576).view(torch.int16).numpy().view(np.uint16))
+    # and exactly one row per sequence changed
+    changed = (kvp != kv.view(-1, 576).view(torch.int16).numpy().view(np.uint16)).any(axis=1)
+    assert changed.sum() == cfg.B
+
+
+def test_cache_append_skips_positions_outside_the_table(ora):
+    cfg, ctx, bt, nb, (k8, ks, kv), (lat, tk8, tks) = _append_case(True)
+    bt2 = bt.clone()
+    bt2[3, :] = -1                                     # sequence 3: its page is unmapped
+    pos = torch.tensor([-1, bt.shape[1] * 64, 5, 200], dtype=torch.int32)  # before, past the table, ok, unmapped
+    kvp, k8p, ksp = ora.paged_cache_append(lat, tk8, tks, pos, bt2, kv.view(-1, 576), k8.view(-1, cfg.D_I),
+                                           ks.view(-1))
+    row = int(bt[2, 0]) * 64 + 5
+    kv0 = kv.view(-1, 576).view(torch.int16).numpy().view(np.uint16)
+    changed = np.nonzero((kvp != kv0).any(axis=1))[0]
+    assert changed.tolist() == [row]
+    assert np.array_equal(np.delete(k8p, row, 0), np.delete(k8.view(-1, cfg.D_I).numpy(), row, 0))
+    assert ksp[row] == tks[2].item() and np.array_equal(np.delete(ksp, row), np.delete(ks.view(-1).numpy(), row))
+
+
+def test_append_then_decode_equals_decode_of_longer_sequence(ora):
+    cfg, ctx, bt, nb, (k8, ks, kv), (lat, tk8, tks) = _append_case(True)
+    kvp, k8p, ksp = ora.paged_cache_append(lat, tk8, tks, ctx.to(torch.int32), bt, kv.view(-1, 576),
+                                           k8.view(-1, cfg.D_I), ks.view(-1))
+    q8, qs, w, q = synth.decode_queries(cfg)
+    a = ora.decode(q8, qs, w, q, k8p, ksp, kvp, bt, ctx + 1, cfg.k, cfg.sm_scale)
+    ek8, eks, ekv = synth.build_decode_pools(cfg, ctx + 1, bt, nb)
+    b_ = ora.decode(q8, qs, w, q, ek8.view(-1, cfg.D_I), eks.view(-1), ekv.view(-1, 576), bt, ctx + 1, cfg.k,
+                    cfg.sm_scale)
+    for x, y in zip(a, b_):
+        assert np.array_equal(x, y)
+    # the appended token is a candidate of its own query (position ctx), selected when k covers it
+    assert all(int(ctx[b]) in a[0][b] for b in range(cfg.B) if int(ctx[b]) + 1 <= cfg.k)
+
+
 # ------------------------------------------------------------ page constants
 def test_page_constants_fix_k_and_context():
     g = json.load(open(os.path.join(HERE, "golden", "pages_constants.json")))
