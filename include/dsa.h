@@ -299,6 +299,23 @@ size_t dsa_decode_workspace_bytes(const dsa_decode_args *a);
 dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* Allocation-free dsa_decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same steps and kernels as dsa_decode, bit-identical
+ * results, with the workspace carved from a static device array inside the
+ * library instead of a caller buffer.  No allocation of any kind is made.
+ *   - The array holds dsa_decode_static_scratch_bytes() bytes (128 MiB) on
+ *     every GPU the library runs on, from its first use until the process
+ *     ends.  A request whose dsa_decode_workspace_bytes() exceeds it fails
+ *     with DSA_ERR_UNSUPPORTED before anything is enqueued.
+ *   - `stream` must belong to the current device (the array's address is
+ *     looked up once per device, on the current device).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; nothing in it needs to start at zero.  Calls that
+ *     overlap in time on one GPU (other streams, other threads) race. */
+size_t dsa_decode_static_scratch_bytes(void);
+dsa_status dsa_decode_noalloc(const dsa_decode_args *a, hipStream_t stream);
+
 /* The stages of dsa_decode, callable one by one.  dsa_decode is exactly
  *   dsa_decode_indexer_scores -> dsa_topk_select (n_valid = ctx_len) ->
  *   dsa_sparse_mla_paged_fwd

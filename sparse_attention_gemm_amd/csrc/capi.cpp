@@ -433,6 +433,24 @@ dsa_status dsa_decode(const dsa_decode_args *a, void *workspace, size_t workspac
   return decode_run(a, workspace, stream);
 }
 
+size_t dsa_decode_static_scratch_bytes(void) { return static_scratch_bytes(); }
+
+dsa_status dsa_decode_noalloc(const dsa_decode_args *a, hipStream_t stream) {
+  CLEAR_ERR();
+  dsa_status st = check_decode(a, true);
+  if (st != DSA_OK) return st;
+  if (a->B == 0) return DSA_OK;
+  const size_t need = dsa_decode_workspace_bytes(a);
+  REQUIRE(need <= static_scratch_bytes(), DSA_ERR_UNSUPPORTED,
+          "this decode needs %zu bytes of scratch; the library's static scratch holds %zu (use dsa_decode with a "
+          "workspace)",
+          need, static_scratch_bytes());
+  void *scratch = nullptr;
+  st = hip_check(static_scratch(stream, &scratch), "static scratch");
+  if (st != DSA_OK) return st;
+  return decode_run(a, scratch, stream);
+}
+
 dsa_status dsa_paged_cache_append(const void *latent, const uint8_t *k8, const float *ks, const int32_t *pos,
                                   int32_t B, int32_t D_I, const int32_t *block_table, int32_t max_blocks,
                                   void *kv_pool, uint8_t *k8_pool, float *ks_pool, int64_t n_pool_rows,

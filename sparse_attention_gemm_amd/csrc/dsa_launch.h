@@ -69,6 +69,11 @@ hipError_t launch_indexer_scores_at(const uint8_t *q8, const float *qs, const ui
 hipError_t launch_indexer_kl(const void *q, const void *kv, const int32_t *idx, const float *scores, const float *lse,
                              int64_t N, int32_t T, int32_t H, int32_t k, float sm_scale, float *kl, hipStream_t s);
 hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStream_t s);
+// The library's static device scratch (scratch.hip): its size, and its
+// address on the device that owns `stream` (which must be the current device),
+// looked up once per device.
+size_t static_scratch_bytes();
+hipError_t static_scratch(hipStream_t stream, void **ptr);
 hipError_t launch_cache_append(const void *latent, const uint8_t *k8, const float *ks,
                                const int32_t *pos, int32_t B, int32_t D_I,
                                const int32_t *block_table, int32_t max_blocks, int64_t n_pool_rows,

@@ -25,7 +25,8 @@ EXPORTS = (
     "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_fwd", "dsa_prefill_workspace_bytes", "dsa_prefill",
     "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
     "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd", "dsa_masked_mha_workspace_bytes",
-    "dsa_masked_mha_prefill", "dsa_indexer_scores_at", "dsa_indexer_kl_fwd",
+    "dsa_masked_mha_prefill", "dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_decode_static_scratch_bytes",
+    "dsa_decode_noalloc",
 )
 
 
@@ -97,6 +98,9 @@ def load():
     L.dsa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
     L.dsa_decode_workspace_bytes.restype = _SZ
     L.dsa_decode.argtypes = [ctypes.POINTER(DecodeArgs), _P, _SZ, _P]
+    L.dsa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _P]
+    L.dsa_decode_static_scratch_bytes.argtypes = []
+    L.dsa_decode_static_scratch_bytes.restype = _SZ
     L.dsa_paged_cache_append.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _P, _I64, _P]
     L.dsa_prefill_select.argtypes = [ctypes.POINTER(PrefillArgs), _P, _SZ, _P]
     L.dsa_decode_indexer_scores.argtypes = [ctypes.POINTER(DecodeArgs), _P, _I64, _P]
@@ -107,7 +111,7 @@ def load():
     L.dsa_indexer_scores_at.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]
     L.dsa_indexer_kl_fwd.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P]
     for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
-                 "dsa_prefill", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
+                 "dsa_prefill", "dsa_decode", "dsa_decode_noalloc", "dsa_paged_cache_append", "dsa_prefill_select",
                  "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -279,6 +283,15 @@ def dsa_decode_workspace_bytes(args: DecodeArgs) -> int:
 def dsa_decode(args: DecodeArgs, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().dsa_decode(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_decode_static_scratch_bytes() -> int:
+    return int(load().dsa_decode_static_scratch_bytes())
+
+
+def dsa_decode_noalloc(args: DecodeArgs, stream=None):
+    """dsa_decode with its workspace in the library's static device scratch."""
+    _check(load().dsa_decode_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def dsa_decode_indexer_scores(args: DecodeArgs, scores, ld_scores=None, stream=None):

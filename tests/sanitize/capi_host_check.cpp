@@ -217,6 +217,13 @@ hipError_t launch_cache_append(const void *latent, const uint8_t *k8, const floa
   read_all(ks_pool, (size_t)n_pool_rows * 4);
   return hipSuccess;
 }
+// the static scratch: a host buffer of the same size, so a request carved past it overflows
+static std::vector<unsigned char> g_scratch(size_t(128) << 20);
+size_t static_scratch_bytes() { return g_scratch.size(); }
+hipError_t static_scratch(hipStream_t, void **ptr) {
+  *ptr = g_scratch.data();
+  return hipSuccess;
+}
 }  // namespace dsa
 
 // ------------------------------------------------------------ driver
@@ -362,6 +369,7 @@ static void check_decode() {
     Buf ws(wsb);
     EXPECT(dsa_decode(&a, ws.p(), wsb, 0) == DSA_OK);
     EXPECT(dsa_decode(&a, ws.p(), wsb - 1, 0) == DSA_ERR_WORKSPACE);
+    EXPECT(dsa_decode_noalloc(&a, 0) == (wsb <= dsa_decode_static_scratch_bytes() ? DSA_OK : DSA_ERR_UNSUPPORTED));
     Buf sc((size_t)c.B * c.max_ctx * 4);
     EXPECT(dsa_decode_indexer_scores(&a, (float *)sc.p(), c.max_ctx, 0) == DSA_OK);
     const size_t mwsb = dsa_sparse_mla_workspace_bytes(c.B, c.H, c.k);
@@ -400,6 +408,28 @@ int main() {
   check_prefill();
   check_decode();
   check_training_side();
+  {  // a decode too large for the static scratch is refused before any launch
+    dsa_decode_args a;
+    std::memset(&a, 0, sizeof a);
+    a.B = 1024;
+    a.H_I = 64;
+    a.D_I = 128;
+    a.H = 128;
+    a.k = 2048;
+    a.max_ctx = 131072;
+    a.max_blocks = 2048;
+    a.n_pool_rows = 64;
+    a.sm_scale = 0.07f;
+    Buf fake(64);
+    a.q8 = (uint8_t *)fake.p(), a.q_scale = (float *)fake.p(), a.w = (float *)fake.p(), a.q = fake.p();
+    a.k8_pool = (uint8_t *)fake.p(), a.ks_pool = (float *)fake.p(), a.kv_pool = fake.p();
+    a.block_table = (int32_t *)fake.p(), a.ctx_len = (int32_t *)fake.p(), a.out = fake.p();
+    const int before = g_launches;
+    EXPECT(dsa_decode_workspace_bytes(&a) > dsa_decode_static_scratch_bytes());
+    EXPECT(dsa_decode_noalloc(&a, 0) == DSA_ERR_UNSUPPORTED);
+    EXPECT(std::strstr(dsa_last_error(), "static scratch") != nullptr);
+    EXPECT(g_launches == before);
+  }
   EXPECT(g_launches > 50);
   std::printf("capi host check ok: %d stubbed launches\n", g_launches);
   return 0;

@@ -303,3 +303,19 @@ def test_binding_refuses_a_stale_library(dsa, monkeypatch):
     with pytest.raises(ImportError, match="stale"):
         dsa._check_fresh(L)
 
+
+def test_noalloc_decode_refuses_oversized_request(dsa):
+    """dsa_decode_noalloc checks the request's workspace against its static
+    scratch before touching the device: B = 1024 sequences at context 131072
+    is refused with DSA_ERR_UNSUPPORTED (nothing here reaches HIP)."""
+    L = dsa.load()
+    a = L.dsa_decode_noalloc.argtypes[0]._type_()  # the struct class this library object was bound with
+    a.B, a.H_I, a.D_I, a.H, a.k = 1024, 64, 128, 128, 2048
+    for f in ("q8", "q_scale", "w", "q", "k8_pool", "ks_pool", "kv_pool", "block_table", "ctx_len", "out"):
+        setattr(a, f, FAKE)
+    a.n_pool_rows, a.max_blocks, a.max_ctx, a.sm_scale = 64, 2048, 131072, 0.07
+    assert L.dsa_decode_workspace_bytes(ctypes.byref(a)) > L.dsa_decode_static_scratch_bytes() == 128 << 20
+    assert L.dsa_decode_noalloc(ctypes.byref(a), None) == dsa.DSA_ERR_UNSUPPORTED
+    assert "static scratch" in dsa.dsa_last_error()
+    a.B = -1
+    assert L.dsa_decode_noalloc(ctypes.byref(a), None) == dsa.DSA_ERR_INVALID_ARG
