@@ -12,7 +12,9 @@ Functions follow the plain definitions written out in dsa_oracle.c:
   * masked multi-head attention in MLA's multi-head form (short-prefill mode),
   * the indexer's KL-alignment loss per query token,
   * one paged decode query per sequence,
-  * the paged cache append of one new token per sequence.
+  * the paged cache append of one new token per sequence,
+  * the backward of sparse MLA (dq, dkv) and of the indexer's KL loss
+    (the score gradient, then dw, dq_I, dk_I).
 """
 from __future__ import annotations
 
@@ -69,6 +71,10 @@ def lib():
         L.ora_decode.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                  dbl, P, i64, P, P, P, P]
         L.ora_paged_cache_append.argtypes = [P, P, P, P, i32, i32, i32, P, i32, i64, P, P, P]
+        L.ora_sparse_mla_bwd.argtypes = [ctypes.c_int, P, P, P, P, i64, i32, i64, i32, i32, i32, dbl,
+                                         P, P, P, P]
+        L.ora_indexer_kl_bwd.argtypes = [ctypes.c_int, P, P, ctypes.c_int, P, P, P, P, P, P, P, i64, i64, i32,
+                                         i32, i32, i32, i32, dbl, P, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -276,3 +282,53 @@ def paged_cache_append(latent, k8, ks, pos, block_table, kv_pool, k8_pool, ks_po
     lib().ora_paged_cache_append(_p(lat), _p(k8), _p(ks), _p(pos), B, D_I, Dqk, _p(bt), bt.shape[1], n_rows,
                                  _p(kvp), _p(k8p), _p(ksp))
     return kvp, k8p, ksp
+
+
+# ------------------------------------------------------------------ backward
+def sparse_mla_bwd(q, kv, idx, dout, sm_scale, Dv=512):
+    """q [T,H,Dqk], kv [N,Dqk], dout [T,H,Dv] (one dtype: f32, bf16 or f64),
+    idx [T,k] -> dict of fp64 arrays: dq [T,H,Dqk], dkv [N,Dqk], and the
+    rounding magnitudes mag_dq, mag_dkv of the same shapes."""
+    q, kv, idx, dout = _np(q), _np(kv), _np(idx, np.int32), _np(dout)
+    dt = _dtype_code(q)
+    assert _dtype_code(kv) == dt and _dtype_code(dout) == dt and dt in (F32, BF16, F64)
+    T, H, Dqk = q.shape
+    N = kv.shape[0]
+    k = idx.shape[1]
+    assert dout.shape == (T, H, Dv)
+    dq = np.empty((T, H, Dqk)); mdq = np.empty((T, H, Dqk))
+    dkv = np.empty((N, Dqk)); mdkv = np.empty((N, Dqk))
+    lib().ora_sparse_mla_bwd(dt, _p(q), _p(kv), _p(idx), _p(dout), T, H, N, k, Dqk, Dv, float(sm_scale),
+                             _p(dq), _p(dkv), _p(mdq), _p(mdkv))
+    return {"dq": dq, "dkv": dkv, "mag_dq": mdq, "mag_dkv": mdkv}
+
+
+def indexer_kl_bwd(q_att, kv, q_idx, k_idx, w, idx, dkl, sm_scale, q_scale=None, k_scale=None):
+    """Gradient of the per-token KL(p || pi) (weighted by dkl [T]) into the
+    indexer.  q_att [T,H,Dqk], kv [N,Dqk] (f32, bf16 or f64); q_idx [T,H_I,D_I],
+    k_idx [N,D_I] (E4M3 payloads with q_scale [T], k_scale [N], or f32/f64);
+    w [T,H_I]; idx [T,k] rows of kv and k_idx.  -> dict of fp64 arrays
+    g [T,k], dw [T,H_I], dq [T,H_I,D_I], dk [N,D_I], and mag_dw, mag_dq,
+    mag_dk, amb_dq, amb_dk (see dsa_oracle.c)."""
+    q_att, kv = _np(q_att), _np(kv)
+    at = _dtype_code(q_att)
+    assert _dtype_code(kv) == at and at in (F32, BF16, F64)
+    q_idx, k_idx = _np(q_idx), _np(k_idx)
+    it = _dtype_code(q_idx)
+    assert _dtype_code(k_idx) == it
+    w, dkl, idx = _np(w, np.float64), _np(dkl, np.float64), _np(idx, np.int32)
+    T, H, Dqk = q_att.shape
+    N = kv.shape[0]
+    _, H_I, D_I = q_idx.shape
+    k = idx.shape[1]
+    assert k_idx.shape == (N, D_I) and w.shape == (T, H_I) and dkl.shape == (T,)
+    qs = _np(q_scale, np.float32) if q_scale is not None else np.ones(T, np.float32)
+    ks = _np(k_scale, np.float32) if k_scale is not None else np.ones(N, np.float32)
+    out = {"g": np.empty((T, k)), "dw": np.empty((T, H_I)), "dq": np.empty((T, H_I, D_I)),
+           "dk": np.empty((N, D_I)), "mag_dw": np.empty((T, H_I)), "mag_dq": np.empty((T, H_I, D_I)),
+           "mag_dk": np.empty((N, D_I)), "amb_dq": np.empty((T, H_I, D_I)), "amb_dk": np.empty((N, D_I))}
+    lib().ora_indexer_kl_bwd(at, _p(q_att), _p(kv), it, _p(q_idx), _p(qs), _p(k_idx), _p(ks), _p(w), _p(idx),
+                             _p(dkl), T, N, H, H_I, D_I, k, Dqk, float(sm_scale), _p(out["g"]), _p(out["dw"]),
+                             _p(out["dq"]), _p(out["dk"]), _p(out["mag_dw"]), _p(out["mag_dq"]), _p(out["mag_dk"]),
+                             _p(out["amb_dq"]), _p(out["amb_dk"]))
+    return out

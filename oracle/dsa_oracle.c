@@ -341,6 +341,128 @@ void ora_sparse_mla_rows(int dtype, const void *q, const void *kv, const int32_t
     }
 }
 
+/* --------------------------------------------------- sparse MLA backward */
+
+/*
+ * Gradient of sparse MLA in MQA mode.  In sparse training the main model is
+ * trained on the language-modelling loss through the attention over the
+ * selected entries (mizuki-eaf.pages.dev, two-stage continued pre-training /
+ * sparse training; m.36881.com.cn, sparse training); the selection itself
+ * carries no gradient.  With the forward of ora_sparse_mla_rows, for every
+ * query t and head h, over the valid entries r_a of idx[t]:
+ *   z_a = s q.c_a,  P_a = softmax(z)_a,  o = sum_a P_a v_a     (c_a = kv[r_a], v_a = c_a[0..Dv))
+ * and an upstream gradient dout[t,h] = dL/do, the chain rule gives
+ *   dP_a   = dout . v_a
+ *   D      = sum_a P_a dP_a  (= dout . o)
+ *   dz_a   = P_a (dP_a - D)
+ *   dq     = s sum_a dz_a c_a
+ *   dkv[r_a] += s dz_a q  +  P_a dout   (the second term on the value dims 0..Dv only)
+ * where dkv sums over every query and head that selected the row (an entry
+ * listed twice counts twice, as in the forward).  All T queries are taken;
+ * dq [T,H,Dqk], dkv [N,Dqk] (zeroed here), fp64.  Inputs q, kv, dout share
+ * one dtype (F32, BF16 or F64).
+ * The magnitudes that bound rounding in an evaluation whose dz and P are held
+ * in a short format, and whose D comes from a rounded o, are returned too:
+ *   mD          = sum_d |dout_d| |o_d|
+ *   mag_dq      = s sum_a (|dz_a| + P_a mD) |c_a|
+ *   mag_dkv[r]  = sum over the same terms of s (|dz_a| + P_a mD) |q| + P_a |dout|
+ */
+void ora_sparse_mla_bwd(int dtype, const void *q, const void *kv, const int32_t *idx, const void *dout, int64_t T,
+                        int32_t H, int64_t N, int32_t k, int32_t Dqk, int32_t Dv, double sm_scale, double *dq,
+                        double *dkv, double *mag_dq, double *mag_dkv)
+{
+    int64_t t, i;
+    double *z = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double *pr = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double *dpa = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double *qh = (double *)malloc(sizeof(double) * (size_t)Dqk);
+    double *gh = (double *)malloc(sizeof(double) * (size_t)Dv);
+    double *oh = (double *)malloc(sizeof(double) * (size_t)Dv);
+    for (i = 0; i < N * Dqk; ++i) {
+        dkv[i] = 0.0;
+        mag_dkv[i] = 0.0;
+    }
+    for (t = 0; t < T; ++t) {
+        const int32_t *sel = idx + t * (int64_t)k;
+        int32_t h;
+        for (h = 0; h < H; ++h) {
+            double *dqh = dq + (t * H + h) * (int64_t)Dqk, *mqh = mag_dq + (t * H + h) * (int64_t)Dqk;
+            double mx = -INFINITY, sum = 0.0, D = 0.0, mD = 0.0;
+            int32_t a, d, m = 0;
+            for (d = 0; d < Dqk; ++d) {
+                qh[d] = elem(dtype, q, (t * H + h) * (int64_t)Dqk + d);
+                dqh[d] = 0.0;
+                mqh[d] = 0.0;
+            }
+            for (d = 0; d < Dv; ++d) {
+                gh[d] = elem(dtype, dout, (t * H + h) * (int64_t)Dv + d);
+                oh[d] = 0.0;
+            }
+            for (a = 0; a < k; ++a) {
+                double dot = 0.0;
+                const int64_t r = sel[a];
+                if (r < 0)
+                    continue;
+                for (d = 0; d < Dqk; ++d)
+                    dot += qh[d] * elem(dtype, kv, r * Dqk + d);
+                z[a] = sm_scale * dot;
+                if (z[a] > mx)
+                    mx = z[a];
+                ++m;
+            }
+            if (m == 0)
+                continue;
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    sum += exp(z[a] - mx);
+            /* probabilities, the output, and dP */
+            for (a = 0; a < k; ++a) {
+                const int64_t r = sel[a];
+                double dp = 0.0;
+                if (r < 0)
+                    continue;
+                pr[a] = exp(z[a] - mx) / sum;
+                for (d = 0; d < Dv; ++d) {
+                    const double v = elem(dtype, kv, r * Dqk + d);
+                    oh[d] += pr[a] * v;
+                    dp += gh[d] * v;
+                }
+                dpa[a] = dp;
+            }
+            for (d = 0; d < Dv; ++d) {
+                D += gh[d] * oh[d];
+                mD += fabs(gh[d]) * fabs(oh[d]);
+            }
+            for (a = 0; a < k; ++a) {
+                const int64_t r = sel[a];
+                double dz, adz;
+                if (r < 0)
+                    continue;
+                dz = pr[a] * (dpa[a] - D);
+                adz = fabs(dz) + pr[a] * mD;
+                for (d = 0; d < Dqk; ++d) {
+                    const double c = elem(dtype, kv, r * Dqk + d);
+                    dqh[d] += sm_scale * dz * c;
+                    mqh[d] += sm_scale * adz * fabs(c);
+                    dkv[r * Dqk + d] += sm_scale * dz * qh[d];
+                    mag_dkv[r * Dqk + d] += sm_scale * adz * fabs(qh[d]);
+                }
+                for (d = 0; d < Dv; ++d) {
+                    dkv[r * Dqk + d] += pr[a] * gh[d];
+                    mag_dkv[r * Dqk + d] += pr[a] * fabs(gh[d]);
+                }
+            }
+        }
+    }
+    (void)N;
+    free(z);
+    free(pr);
+    free(dpa);
+    free(qh);
+    free(gh);
+    free(oh);
+}
+
 /* ------------------------------------------------ indexer KL-alignment loss */
 
 /*
@@ -422,6 +544,161 @@ void ora_indexer_kl_rows(int dtype, const void *q, const void *kv, const int32_t
         free(z);
         free(pa);
     }
+}
+
+/*
+ * Gradient of the indexer's KL-alignment loss.  In sparse training the
+ * indexer's input is detached from the main model and the indexer is trained
+ * by the KL loss alone (mizuki-eaf.pages.dev, two-stage continued
+ * pre-training; m.36881.com.cn, sparse training): the target p (the main
+ * attention, heads averaged) carries no gradient, and the loss reaches only
+ * the indexer's queries, keys and head weights.  For every query t, over the
+ * valid entries r_a of idx[t] (rows of both kv and the indexer keys):
+ *   x_ja   = qh_j . kh_a          qh_j = qs[t] q[t,j,:], kh_a = ks[r_a] k[r_a,:]  (dequantised)
+ *   I_a    = sum_j w_j max(0, x_ja)
+ *   pi_a   = softmax_a(I),   p_a = (1/H) sum_h softmax_a(sm_scale q_att[t,h] . kv[r_a])
+ *   g_a    = dkl[t] (pi_a - p_a)                       (d KL(p || pi) / d I_a, times dkl)
+ *   dw[t,j]    = sum_a g_a max(0, x_ja)
+ *   dq[t,j,:]  = sum_a g_a w_j [x_ja > 0] kh_a
+ *   dk[r_a,:] += g_a sum_j w_j [x_ja > 0] qh_j        (summed over every query selecting the row)
+ * ([x > 0] is 0 at the kink.)  The indexer inputs are E4M3 payloads with
+ * per-token scales, or F32 / F64 values (scales ignored); w, dkl are fp64.
+ * Outputs (fp64): g [T,k] (0 at invalid entries), dw [T,H_I], dq [T,H_I,D_I],
+ * dk [N,D_I] (zeroed here).  For tolerances: mag_* are the same sums over
+ * |terms| with |g_a| + dkl (pi_a + p_a) in place of g_a (the scale of an error
+ * in pi or p), and amb_* collect the terms whose dot product lies within the
+ * fp32 rounding bound (D_I + 2) 2^-24 sum_d |qh_jd kh_ad| of the ReLU kink,
+ * where an fp32 evaluation may take either side.
+ */
+void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int idx_dtype, const void *q_idx,
+                        const float *q_scale, const void *k_idx, const float *k_scale, const double *w,
+                        const int32_t *idx, const double *dkl, int64_t T, int64_t N, int32_t H, int32_t H_I,
+                        int32_t D_I, int32_t k, int32_t Dqk, double sm_scale, double *g, double *dw, double *dq,
+                        double *dk, double *mag_dw, double *mag_dq, double *mag_dk, double *amb_dq, double *amb_dk)
+{
+    const double u = ldexp(1.0, -24);
+    int64_t t, i;
+    double *z = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double *pa = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double *Ia = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double *qh = (double *)malloc(sizeof(double) * (size_t)H_I * (size_t)D_I);
+    double *kh = (double *)malloc(sizeof(double) * (size_t)D_I);
+    for (i = 0; i < N * D_I; ++i) {
+        dk[i] = 0.0;
+        mag_dk[i] = 0.0;
+        amb_dk[i] = 0.0;
+    }
+    for (t = 0; t < T; ++t) {
+        const int32_t *sel = idx + t * (int64_t)k;
+        const double qs = idx_dtype == ORA_E4M3 ? (double)q_scale[t] : 1.0;
+        double smax = -INFINITY, ssum = 0.0;
+        int32_t a, h, j, d, m = 0;
+        for (j = 0; j < H_I; ++j) {
+            dw[t * H_I + j] = 0.0;
+            mag_dw[t * H_I + j] = 0.0;
+            for (d = 0; d < D_I; ++d) {
+                qh[j * D_I + d] = qs * elem(idx_dtype, q_idx, (t * H_I + j) * (int64_t)D_I + d);
+                dq[(t * H_I + j) * (int64_t)D_I + d] = 0.0;
+                mag_dq[(t * H_I + j) * (int64_t)D_I + d] = 0.0;
+                amb_dq[(t * H_I + j) * (int64_t)D_I + d] = 0.0;
+            }
+        }
+        for (a = 0; a < k; ++a) {
+            g[t * (int64_t)k + a] = 0.0;
+            pa[a] = 0.0;
+            if (sel[a] >= 0)
+                ++m;
+        }
+        if (m == 0)
+            continue;
+        /* target: each head's softmax over the valid entries, averaged */
+        for (h = 0; h < H; ++h) {
+            double mx = -INFINITY, sum = 0.0;
+            for (a = 0; a < k; ++a) {
+                double dot = 0.0;
+                const int64_t r = sel[a];
+                if (r < 0)
+                    continue;
+                for (d = 0; d < Dqk; ++d)
+                    dot += elem(att_dtype, q_att, (t * H + h) * (int64_t)Dqk + d) * elem(att_dtype, kv, r * Dqk + d);
+                z[a] = sm_scale * dot;
+                if (z[a] > mx)
+                    mx = z[a];
+            }
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    sum += exp(z[a] - mx);
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    pa[a] += exp(z[a] - mx) / sum / H;
+        }
+        /* index scores and their softmax */
+        for (a = 0; a < k; ++a) {
+            const int64_t r = sel[a];
+            double acc = 0.0;
+            if (r < 0)
+                continue;
+            for (d = 0; d < D_I; ++d)
+                kh[d] = (idx_dtype == ORA_E4M3 ? (double)k_scale[r] : 1.0) * elem(idx_dtype, k_idx, r * D_I + d);
+            for (j = 0; j < H_I; ++j) {
+                double x = 0.0;
+                for (d = 0; d < D_I; ++d)
+                    x += qh[j * D_I + d] * kh[d];
+                acc += w[t * H_I + j] * (x > 0.0 ? x : 0.0);
+            }
+            Ia[a] = acc;
+            if (acc > smax)
+                smax = acc;
+        }
+        for (a = 0; a < k; ++a)
+            if (sel[a] >= 0)
+                ssum += exp(Ia[a] - smax);
+        /* the gradient, pair by pair */
+        for (a = 0; a < k; ++a) {
+            const int64_t r = sel[a];
+            double pi, ga, gm;
+            if (r < 0)
+                continue;
+            pi = exp(Ia[a] - smax) / ssum;
+            ga = dkl[t] * (pi - pa[a]);
+            gm = fabs(ga) + fabs(dkl[t]) * (pi + pa[a]);
+            g[t * (int64_t)k + a] = ga;
+            for (d = 0; d < D_I; ++d)
+                kh[d] = (idx_dtype == ORA_E4M3 ? (double)k_scale[r] : 1.0) * elem(idx_dtype, k_idx, r * D_I + d);
+            for (j = 0; j < H_I; ++j) {
+                const double wj = w[t * H_I + j];
+                double x = 0.0, xm = 0.0;
+                int amb;
+                for (d = 0; d < D_I; ++d) {
+                    x += qh[j * D_I + d] * kh[d];
+                    xm += fabs(qh[j * D_I + d] * kh[d]);
+                }
+                amb = fabs(x) <= (D_I + 2) * u * xm;
+                if (x > 0.0) {
+                    dw[t * H_I + j] += ga * x;
+                    mag_dw[t * H_I + j] += gm * x;
+                }
+                for (d = 0; d < D_I; ++d) {
+                    const int64_t qi = (t * H_I + j) * (int64_t)D_I + d;
+                    if (x > 0.0) {
+                        dq[qi] += ga * wj * kh[d];
+                        mag_dq[qi] += gm * fabs(wj * kh[d]);
+                        dk[r * D_I + d] += ga * wj * qh[j * D_I + d];
+                        mag_dk[r * D_I + d] += gm * fabs(wj * qh[j * D_I + d]);
+                    }
+                    if (amb) {
+                        amb_dq[qi] += fabs(ga * wj * kh[d]);
+                        amb_dk[r * D_I + d] += fabs(ga * wj * qh[j * D_I + d]);
+                    }
+                }
+            }
+        }
+    }
+    free(z);
+    free(pa);
+    free(Ia);
+    free(qh);
+    free(kh);
 }
 
 /* ------------------------------------------------------------ paged decode */
