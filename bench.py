@@ -44,7 +44,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--decode-steps", type=int, default=30)
+    ap.add_argument("--decode-steps", type=int, default=100, help="decode steps timed (median reported)")
+    ap.add_argument("--decode-warmup", type=int, default=5)
+    ap.add_argument("--no-prefill16k", action="store_true", help="skip the L=16384 prefill entry")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
+    ap.add_argument("--cpu-rows-1t", type=int, default=16, help="query rows in the single-thread oracle sample")
     ap.add_argument("--no-decode", action="store_true", help="prefill only")
     ap.add_argument("--no-paged", action="store_true", help="skip the ragged paged decode batch")
     ap.add_argument("--no-short", action="store_true", help="skip the short-prefill (masked MHA) section")
@@ -78,6 +82,25 @@ class Stages:
 
     def avg_ms(self):
         return {n: self.acc[n] / max(self.count, 1) for n in self.names}
+
+
+class StageSamples(Stages):
+    """Per-step stage times kept whole, for medians."""
+
+    def __init__(self, torch, names):
+        super().__init__(torch, names)
+        self.samples = {n: [] for n in names}
+
+    def add(self, evs):
+        super().add(evs)
+        for i, n in enumerate(self.names):
+            self.samples[n].append(evs[i].elapsed_time(evs[i + 1]))
+        tot = evs[0].elapsed_time(evs[-1])
+        self.samples.setdefault("_step", []).append(tot)
+
+    def median_ms(self):
+        import statistics
+        return {n: statistics.median(v) for n, v in self.samples.items() if v}
 
 
 # --------------------------------------------------------------------------- prefill
@@ -194,7 +217,7 @@ def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
     t = setup_decode(torch, dsa, synth, cfg, dev)
     stream = torch.cuda.current_stream()
     names = ["cache_append", "decode_indexer", "topk", "sparse_mla"]
-    st = Stages(torch, names)
+    st = StageSamples(torch, names)
     for i in range(warmup + steps):
         # evict the 256 MB MALL and the L2s by reading 512 MB (a read leaves no dirty
         # lines behind to be written back during the step): each step reads its inputs from HBM
@@ -204,13 +227,15 @@ def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
         torch.cuda.synchronize()
         if i >= warmup:
             st.add(evs)
-    ms = st.avg_ms()
+    med = st.median_ms()
+    ms = {n: med[n] for n in names}
     work = decode_work(cfg, t["ctx_cpu"])
-    step_ms = sum(ms.values())
+    step_ms = med["_step"]
     res = {
         "workload": cfg.name, "B": cfg.B, "ctx_min": int(t["ctx_cpu"].min()), "ctx_max": int(t["ctx_cpu"].max()),
         "ctx_mean": float(t["ctx_cpu"].float().mean()), "k": cfg.k, "H": cfg.H,
-        "paged_shuffled": cfg.shuffled, "steps": steps,
+        "paged_shuffled": cfg.shuffled, "steps": steps, "warmup": warmup,
+        "timing": f"median over {steps} steps after {warmup} warm-up steps, each step after a 512 MB cache-evicting read",
         "ms_per_step": step_ms,
         "tokens_per_s": cfg.B / (step_ms / 1e3),
         "unit": "tokens/s",
@@ -351,7 +376,8 @@ def run_short_prefill(torch, dsa, synth, cfg, dev, steps, warmup):
     return res
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "prefill_indexer_topk_L131072_traffic.json")
+INDEXER_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_indexer_topk_L131072_traffic.json")
+MLA_TRAFFIC = os.path.join(ROOT, "profiles", "sparse_mla_bf16_L131072_traffic.json")
 
 
 def kernel_source_hash(files):
@@ -363,12 +389,12 @@ def kernel_source_hash(files):
     return h.hexdigest()
 
 
-def recorded_traffic(L):
-    """HBM bytes per launch of the fused indexer from the committed rocprofv3
+def recorded_traffic(record, L):
+    """HBM bytes per launch of a kernel from its committed rocprofv3
     FETCH_SIZE/WRITE_SIZE record, if it was taken on these kernel sources at
     this L; otherwise None."""
     try:
-        with open(TRAFFIC_RECORD) as fh:
+        with open(record) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -382,15 +408,141 @@ def _rl(bound, achieved, peak, unit, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
+# --------------------------------------------------------------------------- measured peaks
+def measure_peaks(torch, dev, reps=5):
+    """The chip's rates measured by plain microbenchmarks (libdsa_peaks.so):
+    dense FP8 and bf16 MFMA loops, and a streaming HBM read of 8 GiB.  Best of
+    `reps` runs each."""
+    import ctypes
+    from sparse_attention_gemm_amd import build
+    lib = ctypes.CDLL(build.PEAKS_LIB)
+    lib.dsa_peak_fp8_flop_per_wave_iter.restype = ctypes.c_int64
+    lib.dsa_peak_bf16_flop_per_wave_iter.restype = ctypes.c_int64
+    lib.dsa_peak_fp8_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dsa_peak_bf16_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dsa_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = n_cu * 8
+    sink = torch.zeros(blocks, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def best(launch):
+        ts = []
+        for _ in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            assert launch() == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts[1:])
+
+    iters = 4000
+    waves = blocks * 4
+    fp8_ms = best(lambda: lib.dsa_peak_fp8_mfma(blocks, iters, sink.data_ptr(), stream.cuda_stream))
+    bf16_ms = best(lambda: lib.dsa_peak_bf16_mfma(blocks, iters, sink.data_ptr(), stream.cuda_stream))
+    fp8 = waves * iters * lib.dsa_peak_fp8_flop_per_wave_iter() / (fp8_ms / 1e3) / 1e12
+    bf16 = waves * iters * lib.dsa_peak_bf16_flop_per_wave_iter() / (bf16_ms / 1e3) / 1e12
+    buf = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
+    hbm_ms = best(lambda: lib.dsa_peak_hbm_read(buf.data_ptr(), buf.numel(), n_cu * 16, sink.data_ptr(),
+                                                 stream.cuda_stream))
+    hbm = buf.numel() / (hbm_ms / 1e3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"fp8_mfma_tflops": round(fp8, 1), "bf16_mfma_tflops": round(bf16, 1), "hbm_read_gbs": round(hbm, 1),
+            "method": f"best of {reps}: {blocks} workgroups x 4 waves x {iters} iterations of 4 independent "
+                      "32x32x64 E4M3 / 32x32x16 bf16 MFMAs; an 8 GiB streaming read with 16-byte loads",
+            "datasheet": {"fp8_mfma_tflops": PEAK_FP8_TFLOPS, "bf16_mfma_tflops": PEAK_BF16_TFLOPS,
+                          "hbm_gbs": PEAK_HBM_GBS}}
+
+
+def _with_measured(rl, measured):
+    """Add the fraction of the measured peak to a roofline entry."""
+    if measured:
+        rl = dict(rl)
+        rl["measured_peak"] = measured
+        rl["frac_of_measured"] = round(rl["achieved"] / measured, 4)
+    return rl
+
+
+# --------------------------------------------------------------------------- prefill runs
+def run_prefill(torch, dsa, synth, cfg, dev, steps, warmup, log):
+    """Time `steps` whole prefill steps (after `warmup`) on resident inputs.
+    Returns (wall seconds, per-stage median ms, inputs)."""
+    log(f"drawing prefill inputs L={cfg.L}")
+    t = setup_prefill(torch, dsa, synth, cfg, dev)
+    stream = torch.cuda.current_stream()
+    st = StageSamples(torch, ["quantize", "indexer_topk", "sparse_mla"])
+    for i in range(warmup):
+        prefill_step(dsa, cfg, t, st.new(), stream)
+        torch.cuda.synchronize()
+        log(f"warmup step {i} done")
+    all_evs = [st.new() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        prefill_step(dsa, cfg, t, all_evs[i], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e in all_evs:
+        st.add(e)
+    log(f"{steps} prefill steps at L={cfg.L} in {wall:.3f} s")
+    return wall, st.median_ms(), t
+
+
+def prefill_rooflines(cfg, ms, peaks, traffic=True):
+    work = prefill_work(cfg)
+    idx_tflops = work["indexer_flop"] / (ms["indexer_topk"] / 1e3) / 1e12
+    mla_tflops = work["mla_flop"] / (ms["sparse_mla"] / 1e3) / 1e12
+    q_gbs = work["quantize_bytes"] / (ms["quantize"] / 1e3) / 1e9
+    mp = peaks or {}
+    kernels = {
+        "prefill_indexer_topk": _with_measured(
+            dict(_rl("mfma", idx_tflops, PEAK_FP8_TFLOPS, "TFLOP/s",
+                     recorded_traffic(INDEXER_TRAFFIC, cfg.L) if traffic else None),
+                 kernel="prefill_indexer_topk", ms=round(ms["indexer_topk"], 3)), mp.get("fp8_mfma_tflops")),
+        "sparse_mla_bf16": _with_measured(
+            dict(_rl("mfma", mla_tflops, PEAK_BF16_TFLOPS, "TFLOP/s",
+                     recorded_traffic(MLA_TRAFFIC, cfg.L) if traffic else None),
+                 kernel="sparse_mla_bf16", ms=round(ms["sparse_mla"], 3)), mp.get("bf16_mfma_tflops")),
+    }
+    stages = {
+        "quantize": _with_measured(dict(ms=round(ms["quantize"], 3), **_rl("hbm", q_gbs, PEAK_HBM_GBS, "GB/s")),
+                                   mp.get("hbm_read_gbs")),
+        "indexer_topk": kernels["prefill_indexer_topk"],
+        "sparse_mla": kernels["sparse_mla_bf16"],
+    }
+    # the headline roofline is the kernel that takes longest in the step
+    dominant = max(kernels.values(), key=lambda r: r["ms"])
+    return dominant, kernels, stages, work
+
+
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(torch, synth, cfg, nrows):
-    """The fp64 oracle on `nrows` query rows evenly spaced over the sequence
-    (an unbiased sample of the per-row cost), with the same inputs."""
-    import numpy as np
-    import oracle
-    oracle.build()
-    L = cfg.L
-    rows = np.unique(((np.arange(nrows) + 0.5) * L / nrows).astype(np.int64))
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp():
+    """The OpenMP runtime the oracle runs on (libgomp, loaded with it)."""
+    import ctypes
+    try:
+        g = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    g.omp_get_max_threads.restype = ctypes.c_int
+    g.omp_set_num_threads.argtypes = [ctypes.c_int]
+    return g
+
+
+def _oracle_sample(torch, synth, cfg, rows):
+    """Inputs of the given query rows (drawn with the same generator as the GPU's)."""
     k_i = synth.prefill_indexer_keys(cfg)
     kv = synth.prefill_latent(cfg)
     q_rows, w_rows, qa_rows = [], [], []
@@ -399,11 +551,14 @@ def cpu_baseline(torch, synth, cfg, nrows):
         q_rows.append(qi)
         w_rows.append(w)
         qa_rows.append(synth.prefill_attn_q(cfg, rows=(int(r), int(r) + 1)))
-    qi = torch.cat(q_rows)
-    w = torch.cat(w_rows)
-    qa = torch.cat(qa_rows)
+    return torch.cat(q_rows), k_i, torch.cat(w_rows), torch.cat(qa_rows), kv
+
+
+def _oracle_path(oracle, cfg, rows, qi, k_i, w, qa, kv):
+    """The whole path for the sampled rows: quantise, indexer over s <= t,
+    top-k, sparse MLA.  Returns seconds."""
+    import numpy as np
     n = len(rows)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
     q8, qsc = oracle.quantize_rows(qi.view(n, -1).numpy())
     k8, ksc = oracle.quantize_rows(k_i.numpy())
@@ -411,10 +566,43 @@ def cpu_baseline(torch, synth, cfg, nrows):
     sc = oracle.indexer_rows(q8.reshape(n, cfg.H_I, cfg.D_I), k8, w.numpy(), pos, q_scale=qsc, k_scale=ksc)
     idx, _ = oracle.topk_rows(sc, pos.astype(np.int64) + 1, cfg.k)
     oracle.sparse_mla_rows(qa, kv, idx, cfg.sm_scale)
-    dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} query rows evenly spaced over L={L} (quantise, fp64 indexer over all s<=t, "
-                      f"top-{cfg.k}, fp64 sparse MLA over 128 heads); {dt:.1f} s wall"}
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(torch, synth, cfg, nrows, nrows_1t):
+    """The fp64 oracle on `nrows` query rows evenly spaced over the sequence
+    (an unbiased sample of the per-row cost, since the rows cover every
+    context length in proportion), on every host thread; then on `nrows_1t`
+    rows on one thread.  Rates are tokens/s of the whole path; the full-length
+    run time is extrapolated from them (the whole oracle run is not made)."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    L = cfg.L
+    rows = np.unique(((np.arange(nrows) + 0.5) * L / nrows).astype(np.int64))
+    ins = _oracle_sample(torch, synth, cfg, rows)
+    omp = _omp()
+    threads = omp.omp_get_max_threads() if omp else int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    dt = _oracle_path(oracle, cfg, rows, *ins)
+    value = len(rows) / dt
+    res = {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": _cpu_model(), "host_threads": os.cpu_count(),
+           "sample": f"{len(rows)} query rows evenly spaced over L={L} (quantise, fp64 indexer over all s<=t, "
+                     f"top-{cfg.k}, fp64 sparse MLA over {cfg.H} heads); {dt:.1f} s wall on {threads} threads",
+           "extrapolated_full_run_hours": round(L / value / 3600, 2),
+           "extrapolation": f"the full L={L} oracle run is not made; its time is L / value, from the sampled "
+                            "rows' rate (evenly spaced rows cover every context length in proportion)"}
+    if omp and nrows_1t > 0:
+        rows1 = np.unique(((np.arange(nrows_1t) + 0.5) * L / nrows_1t).astype(np.int64))
+        ins1 = _oracle_sample(torch, synth, cfg, rows1)
+        omp.omp_set_num_threads(1)
+        try:
+            dt1 = _oracle_path(oracle, cfg, rows1, *ins1)
+        finally:
+            omp.omp_set_num_threads(threads)
+        res["single_thread"] = {"value": round(len(rows1) / dt1, 3), "unit": "tokens/s", "cores": 1,
+                                "sample": f"{len(rows1)} evenly spaced rows, {dt1:.1f} s wall"}
+    return res
 
 
 # --------------------------------------------------------------------------- main
@@ -431,34 +619,19 @@ def main():
     dsa.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    peaks = None
+    if not args.no_peaks:
+        log("measured peaks (FP8 / bf16 MFMA loops, HBM read stream)")
+        peaks = measure_peaks(torch, dev)
     cfg = synth.CONFIGS["prefill128k"]
     if args.L:
         cfg = synth.scaled_down(cfg, L=args.L)
-    print(f"[bench] drawing prefill inputs L={cfg.L}", file=sys.stderr, flush=True)
-    t = setup_prefill(torch, dsa, synth, cfg, dev)
-    stream = torch.cuda.current_stream()
-    names = ["quantize", "indexer_topk", "sparse_mla"]
-    st = Stages(torch, names)
-    for i in range(args.warmup):
-        evs = st.new()
-        prefill_step(dsa, cfg, t, evs, stream)
-        torch.cuda.synchronize()
-        print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
-    all_evs = [st.new() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        prefill_step(dsa, cfg, t, all_evs[i], stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for e in all_evs:
-        st.add(e)
-    print(f"[bench] {args.steps} prefill steps in {wall:.3f} s", file=sys.stderr, flush=True)
-    ms = st.avg_ms()
-    work = prefill_work(cfg)
-    idx_tflops = work["indexer_flop"] / (ms["indexer_topk"] / 1e3) / 1e12
-    mla_tflops = work["mla_flop"] / (ms["sparse_mla"] / 1e3) / 1e12
-    q_gbs = work["quantize_bytes"] / (ms["quantize"] / 1e3) / 1e9
+    wall, ms, t = run_prefill(torch, dsa, synth, cfg, dev, args.steps, args.warmup, log)
+    dominant, kernels, stages, work = prefill_rooflines(cfg, ms, peaks)
     value = cfg.L * args.steps / wall
     line = {
         "metric": METRIC,
@@ -475,18 +648,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "L": cfg.L, "H_I": cfg.H_I, "D_I": cfg.D_I, "H": cfg.H, "k": cfg.k,
                    "seed": cfg.seed, "parallelism": "single GPU"},
-        "roofline": dict(_rl("mfma", idx_tflops, PEAK_FP8_TFLOPS, "TFLOP/s", recorded_traffic(cfg.L)),
-                         kernel="prefill_indexer_topk"),
-        "stages": {
-            "quantize": dict(ms=round(ms["quantize"], 3), **_rl("hbm", q_gbs, PEAK_HBM_GBS, "GB/s")),
-            "indexer_topk": dict(ms=round(ms["indexer_topk"], 3),
-                                 **_rl("mfma", idx_tflops, PEAK_FP8_TFLOPS, "TFLOP/s")),
-            "sparse_mla": dict(ms=round(ms["sparse_mla"], 3), **_rl("mfma", mla_tflops, PEAK_BF16_TFLOPS, "TFLOP/s")),
-        },
+        "roofline": dominant,
+        "rooflines": kernels,
+        "stages": stages,
+        "stage_timing": f"median over the {args.steps} timed steps (HIP events on the launching stream)",
+        "measured_peaks": peaks,
         "work": work,
     }
     if not args.no_kl:
-        print("[bench] indexer KL loss on the headline selection", file=sys.stderr, flush=True)
+        log("indexer KL loss on the headline selection")
         line["kl_loss"] = run_kl(torch, dsa, cfg, t, dev, args.kl_steps)
     if args.calibrate_copy:
         # plain copies of known size for scaling HBM counters: the runtime's
@@ -504,22 +674,36 @@ def main():
         del a, b
     del t
     torch.cuda.empty_cache()
+    if not args.no_prefill16k and not args.L:
+        c16 = synth.CONFIGS["prefill16k"]
+        w16, ms16, t16 = run_prefill(torch, dsa, synth, c16, dev, max(args.steps, 5), 1, log)
+        d16, k16, s16, work16 = prefill_rooflines(c16, ms16, peaks, traffic=False)
+        line["prefill16k"] = {"workload": c16.name, "L": c16.L, "tokens_per_s": round(c16.L * max(args.steps, 5) / w16, 1),
+                              "ms_per_step": round(w16 / max(args.steps, 5) * 1e3, 3), "stages": s16, "work": work16}
+        del t16
+        torch.cuda.empty_cache()
     if not args.no_decode:
         flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
         dcfg = synth.CONFIGS["decode"]
-        print("[bench] decode B=64 ctx=32768", file=sys.stderr, flush=True)
-        line["decode"] = run_decode(torch, dsa, synth, dcfg, dev, args.decode_steps, 3, flush)
+        log("decode B=64 ctx=32768")
+        line["decode"] = run_decode(torch, dsa, synth, dcfg, dev, args.decode_steps, args.decode_warmup, flush)
         if not args.no_paged:
-            print("[bench] paged decode B=128", file=sys.stderr, flush=True)
-            line["paged_decode"] = run_decode(torch, dsa, synth, synth.CONFIGS["paged"], dev, args.decode_steps, 3,
-                                              flush)
+            log("paged decode B=128")
+            line["paged_decode"] = run_decode(torch, dsa, synth, synth.CONFIGS["paged"], dev, args.decode_steps,
+                                              args.decode_warmup, flush)
+        for key in ("decode", "paged_decode"):
+            if key in line and peaks:
+                rl = line[key]["roofline"]
+                for name in ("decode_indexer", "topk", "sparse_mla"):
+                    rl[name] = _with_measured(rl[name], peaks["hbm_read_gbs"])
+                rl["sparse_mla_mfma"] = _with_measured(rl["sparse_mla_mfma"], peaks["bf16_mfma_tflops"])
         del flush
     if not args.no_short:
-        print("[bench] short prefill L=4096 (masked MHA and sparse MLA)", file=sys.stderr, flush=True)
+        log("short prefill L=4096 (masked MHA and sparse MLA)")
         line["short_prefill"] = run_short_prefill(torch, dsa, synth, synth.CONFIGS["mha4k"], dev, args.short_steps, 3)
     if not args.no_cpu_baseline:
-        print(f"[bench] oracle on {args.cpu_rows} sampled rows", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(torch, synth, cfg, args.cpu_rows)
+        log(f"oracle on {args.cpu_rows} sampled rows, then {args.cpu_rows_1t} on one thread")
+        line["cpu_baseline"] = cpu_baseline(torch, synth, cfg, args.cpu_rows, args.cpu_rows_1t)
     print(json.dumps(line), flush=True)
 
 

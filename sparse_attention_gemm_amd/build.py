@@ -3,7 +3,8 @@
     python -m sparse_attention_gemm_amd.build
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-selection disabled.
+selection disabled.  Also builds libdsa_peaks.so, the measured-peak
+microbenchmarks the benchmark reports next to the datasheet peaks.
 """
 from __future__ import annotations
 
@@ -65,7 +66,27 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    build_peaks(verbose)
     return LIB
+
+
+PEAKS_SRC = os.path.join(HERE, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(HERE, "libdsa_peaks.so")
+
+
+def build_peaks(verbose: bool = False) -> str:
+    """The measured-peak microbenchmarks the benchmark prices kernels against
+    (a library of their own: they are not part of the path)."""
+    tmp = PEAKS_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-shared", "-o", tmp, PEAKS_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if p.returncode != 0:
+        sys.stderr.write(p.stdout.decode(errors="replace"))
+        raise RuntimeError(f"hipcc failed for {PEAKS_SRC}")
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
 
 
 def _wait(item, verbose):
