@@ -183,6 +183,45 @@ dsa_status dsa_indexer_kl_fwd(const void *q, const void *kv, const int32_t *idx,
                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Backward of the indexer's KL-alignment loss.  In sparse training the
+ * indexer's input is detached and the indexer is trained by the KL loss
+ * alone (mizuki-eaf.pages.dev, two-stage continued pre-training / sparse
+ * training; m.36881.com.cn, sparse training): the target p (the main
+ * attention) carries no gradient.
+ *
+ * dsa_indexer_kl_bwd: the gradient of sum_t dkl[t] KL_t with respect to the
+ * index scores of the entries, with the inputs of dsa_indexer_kl_fwd and
+ *   dkl [T] fp32 (upstream gradient of each token's loss), grad_scores [T, k]
+ *   fp32 out: grad[t, a] = dkl[t] (pi_a - p_a), 0 where the entry has no row.
+ * Limits as dsa_indexer_kl_fwd.
+ */
+dsa_status dsa_indexer_kl_bwd(const void *q, const void *kv, const int32_t *idx, const float *idx_scores,
+                              const float *lse, const float *dkl, int32_t T, int32_t H, int64_t N, int32_t k,
+                              float sm_scale, float *grad_scores, hipStream_t stream);
+
+/* dsa_indexer_bwd: the indexer's own gradients from the score gradient.
+ * With I[t,a] = sum_j w[t,j] ReLU(x_ja), x_ja = (qs[t] q8[t,j]) . (ks[r] k8[r]),
+ * r = idx[t,a] (the FP8 encoding passed straight through):
+ *   dw [T, H_I]         dw[t,j]  = sum_a g[t,a] ReLU(x_ja)
+ *   dq [T, H_I, D_I]    dq[t,j]  = sum_a g[t,a] w[t,j] [x_ja > 0] ks[r] k8[r]
+ *   dk [S, D_I]         dk[r]    = sum over the (t, a) with idx[t,a] = r of
+ *                                  g[t,a] qs[t] sum_j w[t,j] [x_ja > 0] q8[t,j]
+ * (gradients with respect to the dequantised q and k; [x > 0] is 0 at the
+ * kink).  q8 [T,H_I,D_I] E4M3 + q_scale [T], k8 [S,D_I] E4M3 + k_scale [S],
+ * w [T,H_I], idx [T,k] (entries outside [0,S) skipped), grad_scores [T,k]; all
+ * outputs fp32, fully overwritten.  Products come from the FP8 MFMA as in the
+ * forward; sums are fp32.  dk is summed per key over its pairs in increasing
+ * (t, a) order (an inverted selection, no atomics), so it is deterministic
+ * as long as no idx row lists one key more than 4096 times.
+ * workspace: dsa_indexer_bwd_workspace_bytes(T, S, k) bytes, required.
+ * Limits: H_I = 64, D_I = 128, k <= 2048. */
+size_t dsa_indexer_bwd_workspace_bytes(int32_t T, int32_t S, int32_t k);
+dsa_status dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const uint8_t *k8, const float *k_scale,
+                           const float *w, const int32_t *idx, const float *grad_scores, int32_t T, int32_t S,
+                           int32_t H_I, int32_t D_I, int32_t k, float *dw, float *dq, float *dk, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Masked multi-head attention for short prefill (the mode that stands in for
  * DSA on short sequences: mizuki-eaf.pages.dev, "parity evaluation";
  * m.digipub.cc, section 2).  MLA in its multi-head form over one causal

@@ -75,6 +75,9 @@ def lib():
                                          P, P, P, P]
         L.ora_indexer_kl_bwd.argtypes = [ctypes.c_int, P, P, ctypes.c_int, P, P, P, P, P, P, P, i64, i64, i32,
                                          i32, i32, i32, i32, dbl, P, P, P, P, P, P, P, P, P]
+        L.ora_indexer_kl_grad.argtypes = [ctypes.c_int, P, P, P, P, P, i64, i32, i32, i32, dbl, P]
+        L.ora_indexer_bwd.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, i64, i64, i32, i32, i32, P, P, P, P, P, P,
+                                      P, P]
         _lib = L
     return _lib
 
@@ -301,6 +304,41 @@ def sparse_mla_bwd(q, kv, idx, dout, sm_scale, Dv=512):
     lib().ora_sparse_mla_bwd(dt, _p(q), _p(kv), _p(idx), _p(dout), T, H, N, k, Dqk, Dv, float(sm_scale),
                              _p(dq), _p(dkv), _p(mdq), _p(mdkv))
     return {"dq": dq, "dkv": dkv, "mag_dq": mdq, "mag_dkv": mdkv}
+
+
+def indexer_kl_grad(q_att, kv, idx, scores, dkl, sm_scale):
+    """Gradient of sum_t dkl[t] KL_t with respect to the given index scores
+    [T, k]: g = dkl (softmax(scores) - p) at the valid entries, 0 elsewhere."""
+    q_att, kv = _np(q_att), _np(kv)
+    at = _dtype_code(q_att)
+    assert _dtype_code(kv) == at and at in (F32, BF16, F64)
+    idx, sc, dkl = _np(idx, np.int32), _np(scores, np.float64), _np(dkl, np.float64)
+    T, H, Dqk = q_att.shape
+    k = idx.shape[1]
+    g = np.empty((T, k))
+    lib().ora_indexer_kl_grad(at, _p(q_att), _p(kv), _p(idx), _p(sc), _p(dkl), T, H, k, Dqk, float(sm_scale), _p(g))
+    return g
+
+
+def indexer_bwd(q_idx, k_idx, w, idx, g, q_scale=None, k_scale=None):
+    """The indexer's gradients from a score gradient g [T, k] -> dict of fp64
+    dw, dq, dk and mag_dw, mag_dq, mag_dk, amb_dq, amb_dk."""
+    q_idx, k_idx = _np(q_idx), _np(k_idx)
+    it = _dtype_code(q_idx)
+    assert _dtype_code(k_idx) == it
+    w, g, idx = _np(w, np.float64), _np(g, np.float64), _np(idx, np.int32)
+    T, H_I, D_I = q_idx.shape
+    N = k_idx.shape[0]
+    k = idx.shape[1]
+    qs = _np(q_scale, np.float32) if q_scale is not None else np.ones(T, np.float32)
+    ks = _np(k_scale, np.float32) if k_scale is not None else np.ones(N, np.float32)
+    out = {"dw": np.empty((T, H_I)), "dq": np.empty((T, H_I, D_I)), "dk": np.empty((N, D_I)),
+           "mag_dw": np.empty((T, H_I)), "mag_dq": np.empty((T, H_I, D_I)), "mag_dk": np.empty((N, D_I)),
+           "amb_dq": np.empty((T, H_I, D_I)), "amb_dk": np.empty((N, D_I))}
+    lib().ora_indexer_bwd(it, _p(q_idx), _p(qs), _p(k_idx), _p(ks), _p(w), _p(idx), _p(g), T, N, H_I, D_I, k,
+                          _p(out["dw"]), _p(out["dq"]), _p(out["dk"]), _p(out["mag_dw"]), _p(out["mag_dq"]),
+                          _p(out["mag_dk"]), _p(out["amb_dq"]), _p(out["amb_dk"]))
+    return out
 
 
 def indexer_kl_bwd(q_att, kv, q_idx, k_idx, w, idx, dkl, sm_scale, q_scale=None, k_scale=None):

@@ -552,35 +552,93 @@ void ora_indexer_kl_rows(int dtype, const void *q, const void *kv, const int32_t
  * by the KL loss alone (mizuki-eaf.pages.dev, two-stage continued
  * pre-training; m.36881.com.cn, sparse training): the target p (the main
  * attention, heads averaged) carries no gradient, and the loss reaches only
- * the indexer's queries, keys and head weights.  For every query t, over the
- * valid entries r_a of idx[t] (rows of both kv and the indexer keys):
+ * the indexer's queries, keys and head weights.  Two steps, then their
+ * composition:
+ *
+ * ora_indexer_kl_grad -- the gradient of sum_t dkl[t] KL_t with respect to
+ * the index scores of the entries.  For query t, over the valid entries r_a
+ * of idx[t] (rows of kv):
+ *   pi_a = softmax_a(scores[t, a]),   p_a = (1/H) sum_h softmax_a(sm_scale q[t,h] . kv[r_a])
+ *   g[t, a] = dkl[t] (pi_a - p_a)          (d KL(p || pi) / d I_a, since p sums to one)
+ * and 0 at invalid entries.  q, kv: F32, BF16 or F64; scores, dkl, g fp64.
+ */
+void ora_indexer_kl_grad(int att_dtype, const void *q_att, const void *kv, const int32_t *idx, const double *scores,
+                         const double *dkl, int64_t T, int32_t H, int32_t k, int32_t Dqk, double sm_scale, double *g)
+{
+    int64_t t;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (t = 0; t < T; ++t) {
+        const int32_t *sel = idx + t * (int64_t)k;
+        const double *sc = scores + t * (int64_t)k;
+        double *z = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        double *pa = (double *)calloc((size_t)(k > 0 ? k : 1), sizeof(double));
+        double smax = -INFINITY, ssum = 0.0;
+        int32_t a, h, d, m = 0;
+        for (a = 0; a < k; ++a) {
+            g[t * (int64_t)k + a] = 0.0;
+            if (sel[a] >= 0)
+                ++m;
+        }
+        if (m > 0) {
+            for (h = 0; h < H; ++h) {
+                double mx = -INFINITY, sum = 0.0;
+                for (a = 0; a < k; ++a) {
+                    double dot = 0.0;
+                    const int64_t r = sel[a];
+                    if (r < 0)
+                        continue;
+                    for (d = 0; d < Dqk; ++d)
+                        dot += elem(att_dtype, q_att, (t * H + h) * (int64_t)Dqk + d) * elem(att_dtype, kv, r * Dqk + d);
+                    z[a] = sm_scale * dot;
+                    if (z[a] > mx)
+                        mx = z[a];
+                }
+                for (a = 0; a < k; ++a)
+                    if (sel[a] >= 0)
+                        sum += exp(z[a] - mx);
+                for (a = 0; a < k; ++a)
+                    if (sel[a] >= 0)
+                        pa[a] += exp(z[a] - mx) / sum / H;
+            }
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0 && sc[a] > smax)
+                    smax = sc[a];
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    ssum += exp(sc[a] - smax);
+            for (a = 0; a < k; ++a)
+                if (sel[a] >= 0)
+                    g[t * (int64_t)k + a] = dkl[t] * (exp(sc[a] - smax) / ssum - pa[a]);
+        }
+        free(z);
+        free(pa);
+    }
+}
+
+/*
+ * ora_indexer_bwd -- the indexer's gradients from the score gradient g [T,k].
+ * For query t and valid entry r_a (a row of the indexer keys):
  *   x_ja   = qh_j . kh_a          qh_j = qs[t] q[t,j,:], kh_a = ks[r_a] k[r_a,:]  (dequantised)
- *   I_a    = sum_j w_j max(0, x_ja)
- *   pi_a   = softmax_a(I),   p_a = (1/H) sum_h softmax_a(sm_scale q_att[t,h] . kv[r_a])
- *   g_a    = dkl[t] (pi_a - p_a)                       (d KL(p || pi) / d I_a, times dkl)
+ *   (I_a   = sum_j w_j max(0, x_ja))
  *   dw[t,j]    = sum_a g_a max(0, x_ja)
  *   dq[t,j,:]  = sum_a g_a w_j [x_ja > 0] kh_a
  *   dk[r_a,:] += g_a sum_j w_j [x_ja > 0] qh_j        (summed over every query selecting the row)
- * ([x > 0] is 0 at the kink.)  The indexer inputs are E4M3 payloads with
- * per-token scales, or F32 / F64 values (scales ignored); w, dkl are fp64.
- * Outputs (fp64): g [T,k] (0 at invalid entries), dw [T,H_I], dq [T,H_I,D_I],
- * dk [N,D_I] (zeroed here).  For tolerances: mag_* are the same sums over
- * |terms| with |g_a| + dkl (pi_a + p_a) in place of g_a (the scale of an error
- * in pi or p), and amb_* collect the terms whose dot product lies within the
- * fp32 rounding bound (D_I + 2) 2^-24 sum_d |qh_jd kh_ad| of the ReLU kink,
- * where an fp32 evaluation may take either side.
+ * ([x > 0] is 0 at the kink.)  q, k: E4M3 payloads with per-token scales, or
+ * F32 / F64 values (scales ignored); w, g fp64.  Outputs fp64: dw [T,H_I],
+ * dq [T,H_I,D_I], dk [N,D_I] (zeroed here).  For tolerances: mag_dq, mag_dk
+ * are the same sums over |terms|, mag_dw sums |g_a| sum_d |qh_jd kh_ad| (which
+ * bounds |g_a x_ja| and the rounding of x_ja), and amb_* collect the terms
+ * whose dot product lies
+ * within the fp32 rounding bound (D_I + 2) 2^-24 sum_d |qh_jd kh_ad| of the
+ * kink, where an fp32 evaluation may take either side.
  */
-void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int idx_dtype, const void *q_idx,
-                        const float *q_scale, const void *k_idx, const float *k_scale, const double *w,
-                        const int32_t *idx, const double *dkl, int64_t T, int64_t N, int32_t H, int32_t H_I,
-                        int32_t D_I, int32_t k, int32_t Dqk, double sm_scale, double *g, double *dw, double *dq,
-                        double *dk, double *mag_dw, double *mag_dq, double *mag_dk, double *amb_dq, double *amb_dk)
+void ora_indexer_bwd(int idx_dtype, const void *q_idx, const float *q_scale, const void *k_idx, const float *k_scale,
+                     const double *w, const int32_t *idx, const double *g, int64_t T, int64_t N, int32_t H_I,
+                     int32_t D_I, int32_t k, double *dw, double *dq, double *dk, double *mag_dw, double *mag_dq,
+                     double *mag_dk, double *amb_dq, double *amb_dk)
 {
     const double u = ldexp(1.0, -24);
     int64_t t, i;
-    double *z = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
-    double *pa = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
-    double *Ia = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
     double *qh = (double *)malloc(sizeof(double) * (size_t)H_I * (size_t)D_I);
     double *kh = (double *)malloc(sizeof(double) * (size_t)D_I);
     for (i = 0; i < N * D_I; ++i) {
@@ -591,8 +649,7 @@ void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int id
     for (t = 0; t < T; ++t) {
         const int32_t *sel = idx + t * (int64_t)k;
         const double qs = idx_dtype == ORA_E4M3 ? (double)q_scale[t] : 1.0;
-        double smax = -INFINITY, ssum = 0.0;
-        int32_t a, h, j, d, m = 0;
+        int32_t a, j, d;
         for (j = 0; j < H_I; ++j) {
             dw[t * H_I + j] = 0.0;
             mag_dw[t * H_I + j] = 0.0;
@@ -604,65 +661,10 @@ void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int id
             }
         }
         for (a = 0; a < k; ++a) {
-            g[t * (int64_t)k + a] = 0.0;
-            pa[a] = 0.0;
-            if (sel[a] >= 0)
-                ++m;
-        }
-        if (m == 0)
-            continue;
-        /* target: each head's softmax over the valid entries, averaged */
-        for (h = 0; h < H; ++h) {
-            double mx = -INFINITY, sum = 0.0;
-            for (a = 0; a < k; ++a) {
-                double dot = 0.0;
-                const int64_t r = sel[a];
-                if (r < 0)
-                    continue;
-                for (d = 0; d < Dqk; ++d)
-                    dot += elem(att_dtype, q_att, (t * H + h) * (int64_t)Dqk + d) * elem(att_dtype, kv, r * Dqk + d);
-                z[a] = sm_scale * dot;
-                if (z[a] > mx)
-                    mx = z[a];
-            }
-            for (a = 0; a < k; ++a)
-                if (sel[a] >= 0)
-                    sum += exp(z[a] - mx);
-            for (a = 0; a < k; ++a)
-                if (sel[a] >= 0)
-                    pa[a] += exp(z[a] - mx) / sum / H;
-        }
-        /* index scores and their softmax */
-        for (a = 0; a < k; ++a) {
             const int64_t r = sel[a];
-            double acc = 0.0;
-            if (r < 0)
+            const double ga = g[t * (int64_t)k + a], gm = fabs(ga);
+            if (r < 0 || r >= N)
                 continue;
-            for (d = 0; d < D_I; ++d)
-                kh[d] = (idx_dtype == ORA_E4M3 ? (double)k_scale[r] : 1.0) * elem(idx_dtype, k_idx, r * D_I + d);
-            for (j = 0; j < H_I; ++j) {
-                double x = 0.0;
-                for (d = 0; d < D_I; ++d)
-                    x += qh[j * D_I + d] * kh[d];
-                acc += w[t * H_I + j] * (x > 0.0 ? x : 0.0);
-            }
-            Ia[a] = acc;
-            if (acc > smax)
-                smax = acc;
-        }
-        for (a = 0; a < k; ++a)
-            if (sel[a] >= 0)
-                ssum += exp(Ia[a] - smax);
-        /* the gradient, pair by pair */
-        for (a = 0; a < k; ++a) {
-            const int64_t r = sel[a];
-            double pi, ga, gm;
-            if (r < 0)
-                continue;
-            pi = exp(Ia[a] - smax) / ssum;
-            ga = dkl[t] * (pi - pa[a]);
-            gm = fabs(ga) + fabs(dkl[t]) * (pi + pa[a]);
-            g[t * (int64_t)k + a] = ga;
             for (d = 0; d < D_I; ++d)
                 kh[d] = (idx_dtype == ORA_E4M3 ? (double)k_scale[r] : 1.0) * elem(idx_dtype, k_idx, r * D_I + d);
             for (j = 0; j < H_I; ++j) {
@@ -674,10 +676,9 @@ void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int id
                     xm += fabs(qh[j * D_I + d] * kh[d]);
                 }
                 amb = fabs(x) <= (D_I + 2) * u * xm;
-                if (x > 0.0) {
+                if (x > 0.0)
                     dw[t * H_I + j] += ga * x;
-                    mag_dw[t * H_I + j] += gm * x;
-                }
+                mag_dw[t * H_I + j] += gm * xm;   /* bounds |g x| and the rounding of x itself */
                 for (d = 0; d < D_I; ++d) {
                     const int64_t qi = (t * H_I + j) * (int64_t)D_I + d;
                     if (x > 0.0) {
@@ -687,17 +688,55 @@ void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int id
                         mag_dk[r * D_I + d] += gm * fabs(wj * qh[j * D_I + d]);
                     }
                     if (amb) {
-                        amb_dq[qi] += fabs(ga * wj * kh[d]);
-                        amb_dk[r * D_I + d] += fabs(ga * wj * qh[j * D_I + d]);
+                        amb_dq[qi] += gm * fabs(wj * kh[d]);
+                        amb_dk[r * D_I + d] += gm * fabs(wj * qh[j * D_I + d]);
                     }
                 }
             }
         }
     }
-    free(z);
-    free(pa);
-    free(Ia);
     free(qh);
+    free(kh);
+}
+
+/*
+ * ora_indexer_kl_bwd -- the two steps composed: the index scores of the
+ * entries from the indexer's inputs (I_a = sum_j w_j max(0, x_ja)), their
+ * gradient g, then dw, dq, dk.  Entries of idx index both kv and the keys.
+ */
+void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int idx_dtype, const void *q_idx,
+                        const float *q_scale, const void *k_idx, const float *k_scale, const double *w,
+                        const int32_t *idx, const double *dkl, int64_t T, int64_t N, int32_t H, int32_t H_I,
+                        int32_t D_I, int32_t k, int32_t Dqk, double sm_scale, double *g, double *dw, double *dq,
+                        double *dk, double *mag_dw, double *mag_dq, double *mag_dk, double *amb_dq, double *amb_dk)
+{
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(T * k > 0 ? T * k : 1));
+    double *kh = (double *)malloc(sizeof(double) * (size_t)D_I);
+    int64_t t;
+    for (t = 0; t < T; ++t) {
+        const double qs = idx_dtype == ORA_E4M3 ? (double)q_scale[t] : 1.0;
+        int32_t a, j, d;
+        for (a = 0; a < k; ++a) {
+            const int64_t r = idx[t * (int64_t)k + a];
+            double acc = 0.0;
+            sc[t * (int64_t)k + a] = 0.0;
+            if (r < 0 || r >= N)
+                continue;
+            for (d = 0; d < D_I; ++d)
+                kh[d] = (idx_dtype == ORA_E4M3 ? (double)k_scale[r] : 1.0) * elem(idx_dtype, k_idx, r * D_I + d);
+            for (j = 0; j < H_I; ++j) {
+                double x = 0.0;
+                for (d = 0; d < D_I; ++d)
+                    x += qs * elem(idx_dtype, q_idx, (t * H_I + j) * (int64_t)D_I + d) * kh[d];
+                acc += w[t * H_I + j] * (x > 0.0 ? x : 0.0);
+            }
+            sc[t * (int64_t)k + a] = acc;
+        }
+    }
+    ora_indexer_kl_grad(att_dtype, q_att, kv, idx, sc, dkl, T, H, k, Dqk, sm_scale, g);
+    ora_indexer_bwd(idx_dtype, q_idx, q_scale, k_idx, k_scale, w, idx, g, T, N, H_I, D_I, k, dw, dq, dk, mag_dw,
+                    mag_dq, mag_dk, amb_dq, amb_dk);
+    free(sc);
     free(kh);
 }
 

@@ -201,6 +201,74 @@ dsa_status dsa_indexer_kl_fwd(const void *q, const void *kv, const int32_t *idx,
                    "indexer KL launch");
 }
 
+dsa_status dsa_indexer_kl_bwd(const void *q, const void *kv, const int32_t *idx, const float *idx_scores,
+                              const float *lse, const float *dkl, int32_t T, int32_t H, int64_t N, int32_t k,
+                              float sm_scale, float *grad_scores, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0 && N >= 0, DSA_ERR_INVALID_ARG, "T and N must be >= 0");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(H == 16 || H == 32 || H == 64 || H == 128, DSA_ERR_UNSUPPORTED,
+          "KL gradient needs H in {16, 32, 64, 128} (got %d)", H);
+  REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (T == 0) return DSA_OK;
+  REQUIRE(q && kv && idx && idx_scores && lse && dkl && grad_scores, DSA_ERR_INVALID_ARG, "null pointer");
+  return hip_check(launch_indexer_kl_grad(q, kv, idx, idx_scores, lse, dkl, N, T, H, k, sm_scale, grad_scores, stream),
+                   "indexer KL gradient launch");
+}
+
+// Indexer backward workspace for one chunk of up to kIdxBwdChunk queries:
+// u [Tc, k, 128] fp32, then the inverted selection (cnt, start [S + 1], list [Tc k]).
+static constexpr int32_t kIdxBwdChunk = 1024;
+static int32_t idx_bwd_chunk(int32_t T) { return T < kIdxBwdChunk ? T : kIdxBwdChunk; }
+static size_t idx_bwd_ws(int32_t T, int32_t S, int32_t k) {
+  const size_t tc = (size_t)idx_bwd_chunk(T);
+  return align_up(tc * k * 128 * 4, 256) + 2 * align_up(((size_t)S + 1) * 4, 256) + align_up(tc * k * 4, 256);
+}
+
+size_t dsa_indexer_bwd_workspace_bytes(int32_t T, int32_t S, int32_t k) {
+  if (T <= 0 || S <= 0 || k <= 0) return 0;
+  return idx_bwd_ws(T, S, std::min<int32_t>(k, DSA_MAX_K));
+}
+
+dsa_status dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const uint8_t *k8, const float *k_scale,
+                           const float *w, const int32_t *idx, const float *grad_scores, int32_t T, int32_t S,
+                           int32_t H_I, int32_t D_I, int32_t k, float *dw, float *dq, float *dk, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0 && S >= 1 && k >= 1, DSA_ERR_INVALID_ARG, "need T >= 0, S >= 1, k >= 1");
+  REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(H_I == 64 && D_I == 128, DSA_ERR_UNSUPPORTED, "indexer backward needs H_I = 64, D_I = 128 (got %d, %d)",
+          H_I, D_I);
+  if (T == 0) return DSA_OK;
+  REQUIRE(q8 && q_scale && k8 && k_scale && w && idx && grad_scores && dw && dq && dk, DSA_ERR_INVALID_ARG,
+          "null pointer");
+  const size_t need = idx_bwd_ws(T, S, k);
+  REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
+          workspace ? workspace_bytes : (size_t)0, need);
+  const int32_t tc_max = idx_bwd_chunk(T);
+  char *p = (char *)workspace;
+  float *u = (float *)p;
+  p += align_up((size_t)tc_max * k * 128 * 4, 256);
+  int32_t *cnt = (int32_t *)p;
+  p += align_up(((size_t)S + 1) * 4, 256);
+  int32_t *start = (int32_t *)p;
+  p += align_up(((size_t)S + 1) * 4, 256);
+  int32_t *list = (int32_t *)p;
+  dsa_status st = hip_check(launch_fill_zero_f32(dk, (int64_t)S * 128, stream), "fill launch");
+  for (int32_t t0 = 0; t0 < T && st == DSA_OK; t0 += tc_max) {
+    const int32_t tc = std::min(tc_max, T - t0);
+    const int32_t *idx_c = idx + (int64_t)t0 * k;
+    st = hip_check(launch_indexer_bwd_chunk(q8, q_scale, k8, k_scale, w, idx, grad_scores, t0, tc, S, k, dw, dq, u,
+                                            stream),
+                   "indexer backward launch");
+    if (st == DSA_OK)
+      st = hip_check(launch_scatter_build(idx_c, (int64_t)tc * k, S, cnt, start, list, stream), "scatter launch");
+    if (st == DSA_OK) st = hip_check(launch_scatter_add(start, list, S, u, 128, dk, stream), "scatter launch");
+  }
+  return st;
+}
+
 size_t dsa_masked_mha_workspace_bytes(int32_t L, int32_t H) {
   if (L <= 0 || H <= 0) return 0;
   return masked_mha_workspace_bytes(L, H);

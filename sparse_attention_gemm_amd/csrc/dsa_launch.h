@@ -69,6 +69,23 @@ hipError_t launch_indexer_scores_at(const uint8_t *q8, const float *qs, const ui
 hipError_t launch_indexer_kl(const void *q, const void *kv, const int32_t *idx, const float *scores, const float *lse,
                              int64_t N, int32_t T, int32_t H, int32_t k, float sm_scale, float *kl, hipStream_t s);
 hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStream_t s);
+// Backward.  The KL loss's gradient with respect to the index scores
+// (grad [T, k]); the indexer's backward for queries [t0, t0 + Tc) (dw, dq of
+// those queries, and each pair's share u [Tc, k, 128] of dk).
+hipError_t launch_indexer_kl_grad(const void *q, const void *kv, const int32_t *idx, const float *scores,
+                                  const float *lse, const float *dkl, int64_t N, int32_t T, int32_t H, int32_t k,
+                                  float sm_scale, float *grad, hipStream_t s);
+hipError_t launch_indexer_bwd_chunk(const uint8_t *q8, const float *qs, const uint8_t *k8, const float *ks,
+                                    const float *w, const int32_t *idx, const float *grad, int64_t t0, int32_t Tc,
+                                    int32_t S, int32_t k, float *dw, float *dq, float *u, hipStream_t s);
+// The selection of npairs pairs (idx entries in [0, N) are rows) inverted:
+// cnt, start [N + 1] and list [npairs] of workspace; then
+// Y[r, :] += sum over r's pairs, in increasing pair index, of X[pair, :] (W <= 768).
+hipError_t launch_scatter_build(const int32_t *idx, int64_t npairs, int64_t N, int32_t *cnt, int32_t *start,
+                                int32_t *list, hipStream_t s);
+hipError_t launch_scatter_add(const int32_t *start, const int32_t *list, int64_t N, const float *X, int32_t W, float *Y,
+                              hipStream_t s);
+hipError_t launch_fill_zero_f32(float *p, int64_t n, hipStream_t s);
 // The library's static device scratch (scratch.hip): its size, and its
 // address on the device that owns `stream` (which must be the current device),
 // looked up once per device.

@@ -13,7 +13,8 @@
 //  * indexer_scores_at_kernel: I[t, s] for the listed positions, through the
 //    same FP8 core (and the same expression) as the fused selection, so the
 //    values are bit-identical to the scores the selection ranked;
-//  * indexer_kl_kernel: one workgroup per query token.  Each head's softmax
+//  * indexer_kl_kernel: one workgroup per query token (the loss, or its
+//    gradient with respect to the index scores).  Each head's softmax
 //    is taken against the head's log-sum-exp from the sparse-MLA forward
 //    (the same set of entries), the heads are summed, and the aggregate is
 //    normalised by its own sum, so p sums to one exactly:
@@ -77,9 +78,10 @@ static_assert(kBN * kRowSlots % 64 == 0, "whole gather instructions");
 constexpr int kSteps = 576 / 32;                      // 18 K steps of the logits MFMA
 
 // LDS of one workgroup: two tile buffers, the resolved rows and scores of the
-// query's entries (kpad = k rounded up to the tile), per-wave key partials.
-__host__ __device__ constexpr int kl_smem_bytes(int kpad, int nw) {
-  return 2 * kTileBytes + kpad * 4 * 2 + 2 * nw * kBN * 4;
+// query's entries (kpad = k rounded up to the tile), per-wave key partials,
+// and (gradient only) each entry's head sum P.
+__host__ __device__ constexpr int kl_smem_bytes(int kpad, int nw, bool grad) {
+  return 2 * kTileBytes + kpad * 4 * 2 + 2 * nw * kBN * 4 + (grad ? kpad * 4 : 0);
 }
 
 // x of this lane plus x of lane l ^ 32 (resp. l ^ 16).
@@ -114,13 +116,19 @@ __device__ __forceinline__ void kl_gather(uint8_t *__restrict__ dst, const int *
 }
 
 // One workgroup of NW waves per query token; wave w owns heads 16 w .. +16.
-template <int NW>
+// GRAD = false: the loss kl[t].  GRAD = true: the gradient of dkl[t] * KL_t
+// with respect to the index scores of the entries (the target p carries no
+// gradient): since pi = softmax(I) and p sums to one,
+//   d KL_t / d I_a = pi_a - p_a,   out[t, a] = dkl[t] (pi_a - P_a / Z)
+// (0 where the entry has no row); P_a is kept in LDS until Z is known.
+template <int NW, bool GRAD>
 __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__restrict__ q,
                                                              const __bf16 *__restrict__ kv,
                                                              const int32_t *__restrict__ idx,
                                                              const float *__restrict__ scores,
-                                                             const float *__restrict__ lse, int64_t N, int H, int k,
-                                                             float scale_log2, float *__restrict__ kl) {
+                                                             const float *__restrict__ lse, const float *__restrict__ dkl,
+                                                             int64_t N, int H, int k, float scale_log2,
+                                                             float *__restrict__ out) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -130,6 +138,7 @@ __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__res
   int *rows = reinterpret_cast<int *>(smem + 2 * kTileBytes);
   float *sc = reinterpret_cast<float *>(rows + kpad);
   float *part = sc + kpad;  // [2][NW][32]
+  float *pP = part + 2 * NW * kBN;  // GRAD: each entry's head sum
 
   // entries: rows of kv (or -1) and their index scores (-inf where no row)
   for (int a = tid; a < kpad; a += NW * 64) {
@@ -159,9 +168,10 @@ __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__res
       for (int w2 = 0; w2 < NW; ++w2) P += part[((j & 1) * NW + w2) * kBN + lane];
       const int a = j * kBN + lane;
       if (rows[a] >= 0 && P > 0.0f) {
-        accA += P * (logf(P) - sc[a]);
+        if (!GRAD) accA += P * (logf(P) - sc[a]);
         accZ += P;
       }
+      if (GRAD) pP[a] = rows[a] >= 0 ? P : 0.0f;
     }
   };
   kl_gather<NW>(tiles, rows, 0, kv, wave, lane);
@@ -209,7 +219,14 @@ __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__res
   if (smax != -INFINITY)
     for (int a = lane; a < kpad; a += 64) ssum += rows[a] >= 0 ? expf(sc[a] - smax) : 0.0f;
   ssum = wave_sum(ssum);
-  if (lane == 0) kl[t] = accZ > 0.0f ? accA / accZ - logf(accZ) + (smax + logf(ssum)) : 0.0f;
+  if (!GRAD) {
+    if (lane == 0) out[t] = accZ > 0.0f ? accA / accZ - logf(accZ) + (smax + logf(ssum)) : 0.0f;
+    return;
+  }
+  // pi_a - P_a / Z, scaled by the token's upstream gradient; wave 0 wrote pP
+  const float lse_i = smax + logf(ssum), invZ = accZ > 0.0f ? 1.0f / accZ : 0.0f, dk = dkl[t];
+  for (int a = lane; a < k; a += 64)
+    out[t * k + a] = (rows[a] >= 0 && accZ > 0.0f) ? dk * (expf(sc[a] - lse_i) - pP[a] * invZ) : 0.0f;
 }
 
 }  // namespace
@@ -227,23 +244,26 @@ hipError_t launch_indexer_scores_at(const uint8_t *q8, const float *qs, const ui
   return hipGetLastError();
 }
 
-hipError_t launch_indexer_kl(const void *q, const void *kv, const int32_t *idx, const float *scores, const float *lse,
-                             int64_t N, int32_t T, int32_t H, int32_t k, float sm_scale, float *kl, hipStream_t s) {
+template <bool GRAD>
+static hipError_t launch_kl(const void *q, const void *kv, const int32_t *idx, const float *scores, const float *lse,
+                            const float *dkl, int64_t N, int32_t T, int32_t H, int32_t k, float sm_scale, float *out,
+                            hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int kpad = (k + kBN - 1) / kBN * kBN;
   const float sl2 = sm_scale * 1.4426950408889634f;
 #define DSA_KL_CASE(NW)                                                                                          \
   case NW: {                                                                                                     \
-    const int bytes = kl_smem_bytes(kpad, NW);                                                                   \
+    const int bytes = kl_smem_bytes(kpad, NW, GRAD);                                                             \
     static bool attr_done = false; /* per process: the attribute holds for every device */                       \
     if (!attr_done) {                                                                                            \
-      hipError_t e = hipFuncSetAttribute((const void *)indexer_kl_kernel<NW>,                                    \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kl_smem_bytes(2048, NW));   \
+      hipError_t e = hipFuncSetAttribute((const void *)indexer_kl_kernel<NW, GRAD>,                              \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,                             \
+                                         kl_smem_bytes(2048, NW, GRAD));                                         \
       if (e != hipSuccess) return e;                                                                             \
       attr_done = true;                                                                                          \
     }                                                                                                            \
-    hipLaunchKernelGGL(indexer_kl_kernel<NW>, dim3(T), dim3(NW * 64), bytes, s, (const __bf16 *)q,               \
-                       (const __bf16 *)kv, idx, scores, lse, N, H, k, sl2, kl);                                  \
+    hipLaunchKernelGGL((indexer_kl_kernel<NW, GRAD>), dim3(T), dim3(NW * 64), bytes, s, (const __bf16 *)q,       \
+                       (const __bf16 *)kv, idx, scores, lse, dkl, N, H, k, sl2, out);                            \
     break;                                                                                                       \
   }
   switch (H / 16) {
@@ -256,5 +276,16 @@ hipError_t launch_indexer_kl(const void *q, const void *kv, const int32_t *idx, 
   }
 #undef DSA_KL_CASE
   return hipGetLastError();
+}
+
+hipError_t launch_indexer_kl(const void *q, const void *kv, const int32_t *idx, const float *scores, const float *lse,
+                             int64_t N, int32_t T, int32_t H, int32_t k, float sm_scale, float *kl, hipStream_t s) {
+  return launch_kl<false>(q, kv, idx, scores, lse, nullptr, N, T, H, k, sm_scale, kl, s);
+}
+
+hipError_t launch_indexer_kl_grad(const void *q, const void *kv, const int32_t *idx, const float *scores,
+                                  const float *lse, const float *dkl, int64_t N, int32_t T, int32_t H, int32_t k,
+                                  float sm_scale, float *grad, hipStream_t s) {
+  return launch_kl<true>(q, kv, idx, scores, lse, dkl, N, T, H, k, sm_scale, grad, s);
 }
 }  // namespace dsa

@@ -1,0 +1,172 @@
+// scatter.hip -- the selection inverted: per latent row (or indexer key), the
+// (query, entry) pairs that selected it, and a deterministic sum of per-pair
+// vectors into each row.
+//
+// The backward passes produce one gradient vector per selected pair (query t,
+// entry a of idx[t]) and need, for every row r, the sum over the pairs whose
+// entry is r -- a scatter-add over the top-k output.  Instead of
+// floating-point atomics (whose summation order, and so whose rounding,
+// changes from run to run), the selection of a chunk of Tc queries is
+// inverted with a counting sort:
+//   1. cnt[r]  = number of pairs with entry r          (integer atomics: exact)
+//   2. start   = exclusive prefix sum of cnt           (one workgroup)
+//   3. list[start[r] + i] = pair index of r's i-th pair (in arrival order)
+// and the reduce sorts each row's list by pair index before it sums, so every
+// row is summed in increasing (query, entry) order, whatever the arrival
+// order was.  Rows with more pairs than the sort holds in LDS are summed in
+// arrival order (only possible when a query lists one row several times).
+#include "dsa_common.h"
+#include "dsa_launch.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float *__restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
+// pairs of a chunk: pair p = t * k + a for t < Tc; its entry idx[p], valid in [0, N)
+__global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t *__restrict__ idx, int64_t npairs,
+                                                            int64_t N, int32_t *__restrict__ cnt) {
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < npairs; p += (int64_t)gridDim.x * 256) {
+    const int32_t r = idx[p];
+    if (r >= 0 && r < N) atomicAdd(cnt + r, 1);
+  }
+}
+
+// start[0..N] = exclusive prefix sum of cnt[0..N); one workgroup of 1024
+// threads, each summing a contiguous run of the array.
+__global__ __launch_bounds__(1024) void scatter_scan_kernel(const int32_t *__restrict__ cnt, int64_t N,
+                                                            int32_t *__restrict__ start) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (N + 1023) / 1024;
+  const int64_t b = tid * per, e = min(N, b + per);
+  int32_t s = 0;
+  for (int64_t i = b; i < e; ++i) s += cnt[i];
+  part[tid] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the 1024 run sums
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - s;  // exclusive prefix of this run
+  for (int64_t i = b; i < e; ++i) {
+    start[i] = run;
+    run += cnt[i];
+  }
+  if (tid == 1023) start[N] = part[1023];
+}
+
+__global__ __launch_bounds__(256) void scatter_fill_kernel(const int32_t *__restrict__ idx, int64_t npairs, int64_t N,
+                                                           const int32_t *__restrict__ start,
+                                                           int32_t *__restrict__ cursor, int32_t *__restrict__ list) {
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < npairs; p += (int64_t)gridDim.x * 256) {
+    const int32_t r = idx[p];
+    if (r >= 0 && r < N) list[start[r] + atomicAdd(cursor + r, 1)] = (int32_t)p;
+  }
+}
+
+constexpr int kSortCap = 4096;  // pairs of one row sorted in LDS
+
+// Y[r, :] += sum over r's pairs p, in increasing p, of X[p, :].  One
+// workgroup per row; W <= 768 (up to three values per thread).
+__global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t *__restrict__ start,
+                                                          const int32_t *__restrict__ list, const float *__restrict__ X,
+                                                          int W, float *__restrict__ Y) {
+  __shared__ int32_t keys[kSortCap];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t b = start[r], n = start[r + 1] - b;
+  if (n == 0) return;  // uniform
+  const bool sorted = n <= kSortCap;
+  if (sorted) {
+    int m = 1;
+    while (m < n) m <<= 1;
+    for (int i = tid; i < m; i += 256) keys[i] = i < n ? list[b + i] : 0x7FFFFFFF;
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int size = 2; size <= m; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < (m >> 1); i += 256) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const int32_t x = keys[lo], y = keys[hi];
+          if ((x > y) == up) {
+            keys[lo] = y;
+            keys[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  float acc[3] = {0.f, 0.f, 0.f};
+  constexpr int kAhead = 8;  // pairs whose loads are in flight together; the adds stay in order
+  for (int i0 = 0; i0 < n; i0 += kAhead) {
+    float v[kAhead][3];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int i = i0 + u;
+      const int32_t p = i < n ? (sorted ? keys[i] : list[b + i]) : -1;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int d = tid + 256 * j;
+        v[u][j] = (p >= 0 && d < W) ? X[(int64_t)p * W + d] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) acc[j] += v[u][j];
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int d = tid + 256 * j;
+    if (d < W) Y[r * W + d] += acc[j];
+  }
+}
+
+int grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
+}  // namespace
+
+namespace dsa {
+
+hipError_t launch_fill_zero_f32(float *p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_build(const int32_t *idx, int64_t npairs, int64_t N, int32_t *cnt, int32_t *start,
+                                int32_t *list, hipStream_t s) {
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(N)), dim3(256), 0, s, cnt, N, 0);
+  if (npairs > 0)
+    hipLaunchKernelGGL(scatter_count_kernel, dim3(grid_for(npairs)), dim3(256), 0, s, idx, npairs, N, cnt);
+  hipLaunchKernelGGL(scatter_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, N, start);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(N)), dim3(256), 0, s, cnt, N, 0);
+  if (npairs > 0)
+    hipLaunchKernelGGL(scatter_fill_kernel, dim3(grid_for(npairs)), dim3(256), 0, s, idx, npairs, N, start, cnt,
+                       list);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_add(const int32_t *start, const int32_t *list, int64_t N, const float *X, int32_t W, float *Y,
+                              hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_add_kernel, dim3((uint32_t)N), dim3(256), 0, s, start, list, X, W, Y);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -26,7 +26,7 @@ EXPORTS = (
     "dsa_decode_workspace_bytes", "dsa_decode", "dsa_paged_cache_append", "dsa_prefill_select",
     "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd", "dsa_masked_mha_workspace_bytes",
     "dsa_masked_mha_prefill", "dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_decode_static_scratch_bytes",
-    "dsa_decode_noalloc",
+    "dsa_decode_noalloc", "dsa_indexer_kl_bwd", "dsa_indexer_bwd_workspace_bytes", "dsa_indexer_bwd",
 )
 
 
@@ -110,7 +110,11 @@ def load():
     L.dsa_masked_mha_prefill.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]
     L.dsa_indexer_scores_at.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]
     L.dsa_indexer_kl_fwd.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P]
-    for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
+    L.dsa_indexer_kl_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P]
+    L.dsa_indexer_bwd_workspace_bytes.argtypes = [_I32, _I32, _I32]
+    L.dsa_indexer_bwd_workspace_bytes.restype = _SZ
+    L.dsa_indexer_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
+    for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_indexer_kl_bwd", "dsa_indexer_bwd", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
                  "dsa_prefill", "dsa_decode", "dsa_decode_noalloc", "dsa_paged_cache_append", "dsa_prefill_select",
                  "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd"):
         getattr(L, name).restype = ctypes.c_int
@@ -240,6 +244,33 @@ def dsa_indexer_kl_fwd(q, kv, idx, idx_scores, lse, sm_scale, kl, N=None, stream
     _check(load().dsa_indexer_kl_fwd(_ptr(q, bf, "q"), _ptr(kv, bf, "kv"), _ptr(idx, I32_T, "idx"),
                                      _ptr(idx_scores, F32_T, "idx_scores"), _ptr(lse, F32_T, "lse"), T, H, N,
                                      idx.shape[1], float(sm_scale), _ptr(kl, F32_T, "kl"), _stream(stream)))
+
+
+def dsa_indexer_kl_bwd(q, kv, idx, idx_scores, lse, dkl, sm_scale, grad, N=None, stream=None):
+    """Score gradient of sum_t dkl[t] KL_t: grad [T, k] = dkl (pi - p) at the valid entries."""
+    T, H = q.shape[0], q.shape[1]
+    N = kv.shape[0] if N is None else N
+    bf = torch.bfloat16
+    _check(load().dsa_indexer_kl_bwd(_ptr(q, bf, "q"), _ptr(kv, bf, "kv"), _ptr(idx, I32_T, "idx"),
+                                     _ptr(idx_scores, F32_T, "idx_scores"), _ptr(lse, F32_T, "lse"),
+                                     _ptr(dkl, F32_T, "dkl"), T, H, N, idx.shape[1], float(sm_scale),
+                                     _ptr(grad, F32_T, "grad"), _stream(stream)))
+
+
+def dsa_indexer_bwd_workspace_bytes(T: int, S: int, k: int) -> int:
+    return int(load().dsa_indexer_bwd_workspace_bytes(T, S, k))
+
+
+def dsa_indexer_bwd(q8, q_scale, k8, k_scale, w, idx, grad, dw, dq, dk, workspace, S=None, stream=None):
+    """dw [T, H_I], dq [T, H_I, D_I], dk [S, D_I] from the score gradient grad [T, k]."""
+    T, H_I, D_I = q8.shape
+    S = k8.shape[0] if S is None else S
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().dsa_indexer_bwd(_ptr(q8, U8_T, "q8"), _ptr(q_scale, F32_T, "q_scale"), _ptr(k8, U8_T, "k8"),
+                                  _ptr(k_scale, F32_T, "k_scale"), _ptr(w, F32_T, "w"), _ptr(idx, I32_T, "idx"),
+                                  _ptr(grad, F32_T, "grad"), T, S, H_I, D_I, idx.shape[1], _ptr(dw, F32_T, "dw"),
+                                  _ptr(dq, F32_T, "dq"), _ptr(dk, F32_T, "dk"), _ptr(workspace, name="workspace"),
+                                  ws_bytes, _stream(stream)))
 
 
 def make_prefill_args(L, H_I, D_I, H, k, idx_dt, q_idx, q_scale, k_idx, k_scale, w, attn_dt, q, kv, sm_scale,

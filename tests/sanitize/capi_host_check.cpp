@@ -217,6 +217,58 @@ hipError_t launch_cache_append(const void *latent, const uint8_t *k8, const floa
   read_all(ks_pool, (size_t)n_pool_rows * 4);
   return hipSuccess;
 }
+hipError_t launch_indexer_kl_grad(const void *q, const void *kv, const int32_t *idx, const float *scores,
+                                  const float *lse, const float *dkl, int64_t N, int32_t T, int32_t H, int32_t k, float,
+                                  float *grad, hipStream_t) {
+  ++g_launches;
+  read_all(q, (size_t)T * H * 576 * 2);
+  read_all(kv, (size_t)N * 576 * 2);
+  read_all(idx, (size_t)T * k * 4);
+  read_all(scores, (size_t)T * k * 4);
+  read_all(lse, (size_t)T * H * 4);
+  read_all(dkl, (size_t)T * 4);
+  touch(grad, (size_t)T * k * 4);
+  return hipSuccess;
+}
+hipError_t launch_indexer_bwd_chunk(const uint8_t *q8, const float *qs, const uint8_t *k8, const float *ks,
+                                    const float *w, const int32_t *idx, const float *grad, int64_t t0, int32_t Tc,
+                                    int32_t S, int32_t k, float *dw, float *dq, float *u, hipStream_t) {
+  ++g_launches;
+  read_all(q8 + t0 * 64 * 128, (size_t)Tc * 64 * 128);
+  read_all(qs + t0, (size_t)Tc * 4);
+  read_all(k8, (size_t)S * 128);
+  read_all(ks, (size_t)S * 4);
+  read_all(w + t0 * 64, (size_t)Tc * 64 * 4);
+  read_all(idx + t0 * k, (size_t)Tc * k * 4);
+  read_all(grad + t0 * k, (size_t)Tc * k * 4);
+  touch(dw + t0 * 64, (size_t)Tc * 64 * 4);
+  touch(dq + t0 * 64 * 128, (size_t)Tc * 64 * 128 * 4);
+  touch(u, (size_t)Tc * k * 128 * 4);
+  return hipSuccess;
+}
+hipError_t launch_scatter_build(const int32_t *idx, int64_t npairs, int64_t N, int32_t *cnt, int32_t *start,
+                                int32_t *list, hipStream_t) {
+  ++g_launches;
+  read_all(idx, (size_t)npairs * 4);
+  touch(cnt, (size_t)N * 4);
+  touch(start, (size_t)(N + 1) * 4);
+  touch(list, (size_t)npairs * 4);
+  return hipSuccess;
+}
+hipError_t launch_scatter_add(const int32_t *start, const int32_t *list, int64_t N, const float *X, int32_t W, float *Y,
+                              hipStream_t) {
+  ++g_launches;
+  read_all(start, (size_t)(N + 1) * 4);
+  (void)list;
+  (void)X;
+  touch(Y, (size_t)N * W * 4);
+  return hipSuccess;
+}
+hipError_t launch_fill_zero_f32(float *p, int64_t n, hipStream_t) {
+  ++g_launches;
+  touch(p, (size_t)n * 4);
+  return hipSuccess;
+}
 // the static scratch: a host buffer of the same size, so a request carved past it overflows
 static std::vector<unsigned char> g_scratch(size_t(128) << 20);
 size_t static_scratch_bytes() { return g_scratch.size(); }
@@ -384,6 +436,26 @@ static void check_decode() {
   }
 }
 
+static void check_indexer_backward() {
+  for (int T : {1, 37, 1500}) {
+    const int S = 3000, k = 2048;
+    Buf q_att((size_t)T * 128 * 576 * 2), kv((size_t)S * 576 * 2), idx((size_t)T * k * 4), sc((size_t)T * k * 4),
+        lse((size_t)T * 128 * 4), dkl(T * 4), grad((size_t)T * k * 4), q8((size_t)T * 64 * 128), qs(T * 4),
+        k8((size_t)S * 128), ks(S * 4), w((size_t)T * 64 * 4), dw((size_t)T * 64 * 4), dq((size_t)T * 64 * 128 * 4),
+        dk((size_t)S * 128 * 4);
+    EXPECT(dsa_indexer_kl_bwd(q_att.p(), kv.p(), (int32_t *)idx.p(), (float *)sc.p(), (float *)lse.p(),
+                              (float *)dkl.p(), T, 128, S, k, 0.07f, (float *)grad.p(), 0) == DSA_OK);
+    const size_t wsb = dsa_indexer_bwd_workspace_bytes(T, S, k);
+    Buf ws(wsb);
+    EXPECT(dsa_indexer_bwd((uint8_t *)q8.p(), (float *)qs.p(), (uint8_t *)k8.p(), (float *)ks.p(), (float *)w.p(),
+                           (int32_t *)idx.p(), (float *)grad.p(), T, S, 64, 128, k, (float *)dw.p(), (float *)dq.p(),
+                           (float *)dk.p(), ws.p(), wsb, 0) == DSA_OK);
+    EXPECT(dsa_indexer_bwd((uint8_t *)q8.p(), (float *)qs.p(), (uint8_t *)k8.p(), (float *)ks.p(), (float *)w.p(),
+                           (int32_t *)idx.p(), (float *)grad.p(), T, S, 64, 128, k, (float *)dw.p(), (float *)dq.p(),
+                           (float *)dk.p(), ws.p(), wsb - 1, 0) == DSA_ERR_WORKSPACE);
+  }
+}
+
 static void check_training_side() {
   const int T = 50, H = 128, k = 2048, S = 3000, L = 700;
   Buf q8((size_t)T * 64 * 128), qs(T * 4), k8((size_t)S * 128), ks(S * 4), w((size_t)T * 64 * 4),
@@ -408,6 +480,7 @@ int main() {
   check_prefill();
   check_decode();
   check_training_side();
+  check_indexer_backward();
   {  // a decode too large for the static scratch is refused before any launch
     dsa_decode_args a;
     std::memset(&a, 0, sizeof a);

@@ -1,0 +1,217 @@
+"""GPU parity of the backward entries against the fp64 oracle, through the C ABI.
+
+Tolerances (each derived from the arithmetic of the kernel it checks):
+  * score gradient of the KL loss, g = dkl (pi - p): pi is an fp32 softmax of
+    the given scores and p sums each head's exp(z - lse) with z from bf16 MFMA
+    logits (fp32 sums) and lse from the sparse-MLA forward; both carry relative
+    errors far below 1e-4, so |dg| <= 1e-4 dkl (pi + p) + 1e-9.
+  * indexer gradients from a given score gradient: the products are exact
+    (E4M3 x E4M3) and every sum is fp32, over at most k keys (dw, dq), H_I heads
+    and T pairs (dk); the a-priori bound (k + H_I + T + 8) 2^-24 mag covers the
+    rounding, with mag the oracle's sum of |terms| (for dw, |g| times the
+    magnitude of each dot product, which also bounds its own rounding), plus
+    amb: the terms whose dot product lies within fp32 rounding of the ReLU
+    kink, where the GPU may take the other side.
+Each test prints its case before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U = 2.0 ** -24
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_gemm_amd import dsa as d
+    d.load()
+    return d
+
+
+def _selection(seed, T, N, k, causal=False):
+    """Sorted selections with padding, an empty row and out-of-range entries."""
+    rows = []
+    for t in range(T):
+        n = min(k, (t + 1) if causal else N)
+        pool = (t + 1) if causal else N
+        sel = torch.sort(synth.permutation(seed, 100 + t, pool)[:n]).values
+        rows.append(torch.cat([sel, torch.full((k - n,), -1, dtype=torch.int64)]))
+    idx = torch.stack(rows).to(torch.int32)
+    if T > 3:
+        idx[1, k // 3:] = -1          # ragged
+        idx[2, :] = -1                # empty
+    return idx
+
+
+def _pi_p(scores, idx, g_ref, dkl):
+    """pi = softmax of the scores over the valid entries, and p = pi - g / dkl
+    (the oracle's target), the scales of the score gradient's tolerance."""
+    sc = np.where(idx >= 0, scores, -np.inf)
+    mx = np.max(np.where(np.isfinite(sc), sc, -1e300), axis=1, keepdims=True)
+    e = np.where(np.isfinite(sc), np.exp(np.minimum(sc - mx, 0.0)), 0.0)
+    tot = e.sum(axis=1, keepdims=True)
+    pi = np.divide(e, tot, out=np.zeros_like(e), where=tot > 0)
+    return pi, pi - g_ref / np.asarray(dkl)[:, None]
+
+
+def _check(name, gpu, ref, tol):
+    gpu = np.asarray(gpu, np.float64)
+    err = np.abs(gpu - ref)
+    bad = err > tol
+    worst = float((err / np.maximum(tol, 1e-300)).max()) if err.size else 0.0
+    print(f"[grad] {name}: worst err/bound {worst:.3g}, max|ref| {np.abs(ref).max():.3g}", flush=True)
+    assert not bad.any(), f"{name}: {bad.sum()} of {bad.size} out of tolerance; worst err/bound {worst:.3g}"
+
+
+@pytest.mark.parametrize("H,k,sstd", [(128, 2048, 1.0), (16, 256, 4.0), (64, 100, 0.3)])
+def test_indexer_kl_grad(dsa, ora, H, k, sstd):
+    T, N = 12, 3000
+    _say(f"indexer KL score gradient H={H} k={k} sstd={sstd}")
+    q = synth.normal(41, 1, (T, H, 576)).to(torch.bfloat16)
+    kv = synth.normal(41, 2, (N, 576), std=1 / 24).to(torch.bfloat16)
+    idx = _selection(41, T, N, k)
+    idx[3, 7] = N + 5                 # out of range: no row
+    scores = synth.normal(41, 3, (T, k), std=sstd)
+    dkl = synth.uniform(41, 4, (T,), lo=0.5, hi=1.5)
+    d = {n: x.to(DEV) for n, x in dict(q=q, kv=kv, idx=idx, sc=scores, dkl=dkl).items()}
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_mla_fwd(d["q"], d["kv"], d["idx"], 1 / math.sqrt(192), out, lse)
+    grad = torch.full((T, k), 7.0, dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_kl_bwd(d["q"], d["kv"], d["idx"], d["sc"], lse, d["dkl"], 1 / math.sqrt(192), grad)
+    torch.cuda.synchronize()
+    ref_idx = idx.clone()
+    ref_idx[3, 7] = -1
+    g_ref = ora.indexer_kl_grad(q, kv, ref_idx.numpy(), scores.double().numpy(), dkl.double().numpy(),
+                                1 / math.sqrt(192))
+    pi, p = _pi_p(scores.double().numpy(), ref_idx.numpy(), g_ref, dkl.double().numpy())
+    tol = 1e-4 * dkl.double().numpy()[:, None] * (pi + np.abs(p)) + 1e-9
+    _check("score gradient", grad.cpu().numpy(), g_ref, tol)
+    assert torch.all(grad.cpu()[2] == 0) and grad.cpu()[3, 7] == 0
+    np.testing.assert_allclose(grad.cpu().double().sum(dim=1).numpy(), 0, atol=1e-5)
+
+
+def _indexer_inputs(seed, T, S):
+    q = synth.normal(seed, synth.T_QI, (T, 64, 128))
+    kk = synth.normal(seed, synth.T_KI, (S, 128))
+    w = synth.normal(seed, synth.T_W, (T, 64), std=0.5)
+    return q, kk, w
+
+
+@pytest.mark.parametrize("T,S,k,causal", [(40, 3000, 2048, False), (300, 300, 256, True), (1100, 2500, 64, False)])
+def test_indexer_bwd_from_score_gradient(dsa, ora, T, S, k, causal):
+    """dw, dq, dk from a given score gradient; T = 1100 spans two query chunks
+    of the inverted-selection reduce."""
+    _say(f"indexer backward T={T} S={S} k={k} causal={causal}")
+    q, kk, w = _indexer_inputs(43, T, S)
+    q8, qs = ora.quantize_rows(q.view(T, -1).numpy())
+    k8, ks = ora.quantize_rows(kk.numpy())
+    q8 = q8.reshape(T, 64, 128)
+    idx = _selection(43, T, S, k, causal=causal)
+    idx[0, 1] = S + 7                 # out of range: skipped
+    g = synth.normal(43, 5, (T, k), std=1e-2)
+    d = {n: torch.from_numpy(np.ascontiguousarray(x)).to(DEV) if isinstance(x, np.ndarray) else x.to(DEV)
+         for n, x in dict(q8=q8, qs=qs, k8=k8, ks=ks, w=w, idx=idx, g=g).items()}
+    dw = torch.full((T, 64), 7.0, device=DEV)
+    dq = torch.full((T, 64, 128), 7.0, device=DEV)
+    dk = torch.full((S, 128), 7.0, device=DEV)
+    ws = torch.empty(dsa.dsa_indexer_bwd_workspace_bytes(T, S, k), dtype=torch.uint8, device=DEV)
+    dsa.dsa_indexer_bwd(d["q8"], d["qs"], d["k8"], d["ks"], d["w"], d["idx"], d["g"], dw, dq, dk, ws)
+    torch.cuda.synchronize()
+    ref_idx = idx.clone()
+    ref_idx[0, 1] = -1
+    r = ora.indexer_bwd(q8, k8, w.double().numpy(), ref_idx.numpy(), g.double().numpy(), q_scale=qs, k_scale=ks)
+    f = (k + 64 + T + 8) * U
+    _check("dw", dw.cpu().numpy(), r["dw"], f * r["mag_dw"] + 1e-30)
+    _check("dq", dq.cpu().numpy(), r["dq"], f * r["mag_dq"] + r["amb_dq"] + 1e-30)
+    _check("dk", dk.cpu().numpy(), r["dk"], f * r["mag_dk"] + r["amb_dk"] + 1e-30)
+    # keys nobody selected get exactly zero
+    chosen = np.zeros(S, bool)
+    chosen[ref_idx.numpy()[ref_idx.numpy() >= 0]] = True
+    assert torch.all(dk.cpu()[torch.from_numpy(~chosen)] == 0)
+
+
+def test_indexer_bwd_is_deterministic(dsa):
+    """The dk reduce sums each key's pairs in a fixed order: two runs agree bit for bit."""
+    T, S, k = 700, 2000, 512
+    _say("indexer backward determinism")
+    q, kk, w = _indexer_inputs(44, T, S)
+    q8 = synth.to_e4m3_bits(q).to(DEV)
+    k8 = synth.to_e4m3_bits(kk).to(DEV)
+    qs, ks = torch.ones(T, device=DEV), torch.ones(S, device=DEV)
+    idx = _selection(44, T, S, k).to(DEV)
+    g = synth.normal(44, 5, (T, k), std=1e-2).to(DEV)
+    ws = torch.empty(dsa.dsa_indexer_bwd_workspace_bytes(T, S, k), dtype=torch.uint8, device=DEV)
+    res = []
+    for _ in range(2):
+        dw, dq, dk = torch.empty((T, 64), device=DEV), torch.empty((T, 64, 128), device=DEV), torch.empty((S, 128),
+                                                                                                            device=DEV)
+        dsa.dsa_indexer_bwd(q8, qs, k8, ks, w.to(DEV), idx, g, dw, dq, dk, ws)
+        torch.cuda.synchronize()
+        res.append((dw.cpu(), dq.cpu(), dk.cpu()))
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_indexer_kl_backward_after_prefill_selection(dsa, ora):
+    """The sparse-training indexer step end to end on the library's own fused
+    selection: quantise -> fused indexer + top-k -> sparse MLA (lse) ->
+    scores at the selection -> KL score gradient -> indexer backward, against
+    the oracle's composed KL backward on the same selection."""
+    L, k, H = 700, 128, 16
+    _say(f"KL backward after the fused selection L={L} k={k} H={H}")
+    cfg = synth.scaled_down(synth.CONFIGS["prefill16k"], L=L, k=k, H=H, seed=45)
+    q_i, k_i, w = synth.prefill_indexer_inputs(cfg)
+    q, kv = synth.prefill_attn_q(cfg), synth.prefill_latent(cfg)
+    q8, qs = ora.quantize_rows(q_i.view(L, -1).numpy())
+    k8, ks = ora.quantize_rows(k_i.numpy())
+    q8 = q8.reshape(L, 64, 128)
+    d = {n: torch.from_numpy(np.ascontiguousarray(x)).to(DEV) if isinstance(x, np.ndarray) else x.to(DEV)
+         for n, x in dict(q8=q8, qs=qs, k8=k8, ks=ks, w=w, q=q, kv=kv).items()}
+    idx = torch.empty((L, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((L, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((L, H), dtype=torch.float32, device=DEV)
+    args = dsa.make_prefill_args(L, 64, 128, H, k, dsa.DSA_E4M3, d["q8"], d["qs"], d["k8"], d["ks"], d["w"],
+                                 dsa.DSA_BF16, d["q"], d["kv"], cfg.sm_scale, idx, out, lse)
+    pws = torch.empty(dsa.dsa_prefill_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    dsa.dsa_prefill(args, pws)
+    sc = torch.empty((L, k), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_scores_at(d["q8"], d["qs"], d["k8"], d["ks"], d["w"], idx, sc)
+    dkl = torch.full((L,), 1.0 / L, dtype=torch.float32, device=DEV)   # the mean over tokens
+    grad = torch.empty((L, k), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_kl_bwd(d["q"], d["kv"], idx, sc, lse, dkl, cfg.sm_scale, grad)
+    dw, dq, dk = (torch.empty((L, 64), device=DEV), torch.empty((L, 64, 128), device=DEV),
+                  torch.empty((L, 128), device=DEV))
+    ws = torch.empty(dsa.dsa_indexer_bwd_workspace_bytes(L, L, k), dtype=torch.uint8, device=DEV)
+    dsa.dsa_indexer_bwd(d["q8"], d["qs"], d["k8"], d["ks"], d["w"], idx, grad, dw, dq, dk, ws)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    # step 1, the score gradient, against the oracle on the GPU's own scores
+    dklv = np.full(L, 1.0 / L)
+    g_ref = ora.indexer_kl_grad(q, kv, gidx, sc.cpu().double().numpy(), dklv, cfg.sm_scale)
+    pi, p = _pi_p(sc.cpu().double().numpy(), gidx, g_ref, dklv)
+    _check("score gradient (pipeline)", grad.cpu().numpy(), g_ref, 1e-4 * dklv[:, None] * (pi + np.abs(p)) + 1e-12)
+    # step 2, the indexer gradients, on the GPU's own score gradient
+    r = ora.indexer_bwd(q8, k8, w.double().numpy(), gidx, grad.cpu().double().numpy(), q_scale=qs, k_scale=ks)
+    f = (k + 64 + L + 8) * U
+    _check("dw (pipeline)", dw.cpu().numpy(), r["dw"], f * r["mag_dw"] + 1e-30)
+    _check("dq (pipeline)", dq.cpu().numpy(), r["dq"], f * r["mag_dq"] + r["amb_dq"] + 1e-30)
+    _check("dk (pipeline)", dk.cpu().numpy(), r["dk"], f * r["mag_dk"] + r["amb_dk"] + 1e-30)
+    # and the composition: the GPU's steps reproduce the oracle's KL backward of the indexer's own
+    # scores, up to those scores' fp32 rounding (pi moves by at most 2 pi |dI|)
+    full = ora.indexer_kl_bwd(q, kv, q8, k8, w.double().numpy(), gidx, dklv, cfg.sm_scale, q_scale=qs, k_scale=ks)
+    sco = np.take_along_axis(ora.indexer_rows(q8, k8, w, np.arange(L, dtype=np.int32), q_scale=qs, k_scale=ks),
+                             np.maximum(gidx, 0).astype(np.int64), axis=1)
+    dI = float(np.abs(sc.cpu().double().numpy() - sco)[gidx >= 0].max())
+    _check("score gradient vs the oracle's own scores", grad.cpu().numpy(), full["g"],
+           (1e-4 + 2 * dI) * dklv[:, None] * (pi + np.abs(p)) + 1e-12)

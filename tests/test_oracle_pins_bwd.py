@@ -221,3 +221,16 @@ def test_kl_bwd_e4m3_equals_dequantised_f64(ora):
     b = ora.indexer_kl_bwd(q_att, kv, qd, kd, w.numpy().astype(np.float64), idx, dkl, 0.2)
     for key in ("g", "dw", "dq", "dk"):
         np.testing.assert_allclose(a[key], b[key], rtol=1e-12, atol=1e-15)
+
+
+def test_kl_bwd_is_the_composition_of_its_two_steps(ora):
+    """ora_indexer_kl_bwd = index scores -> ora_indexer_kl_grad -> ora_indexer_bwd."""
+    q_att, kv, q_idx, k_idx, w, idx, dkl, sm = _kl_case(seed=8)
+    a = ora.indexer_kl_bwd(q_att, kv, q_idx, k_idx, w, idx, dkl, sm)
+    pos = np.full(q_idx.shape[0], k_idx.shape[0] - 1, np.int32)
+    sc = np.take_along_axis(ora.indexer_rows(q_idx, k_idx, w, pos), np.maximum(idx, 0).astype(np.int64), axis=1)
+    g = ora.indexer_kl_grad(q_att, kv, idx, sc, dkl, sm)
+    np.testing.assert_allclose(g, a["g"], rtol=1e-12, atol=1e-15)
+    b = ora.indexer_bwd(q_idx, k_idx, w, idx, g)
+    for key in ("dw", "dq", "dk"):
+        np.testing.assert_allclose(b[key], a[key], rtol=1e-12, atol=1e-15)
