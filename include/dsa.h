@@ -146,6 +146,34 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Sparse MLA backward.  In sparse training the main model is trained by the
+ * language-modelling loss through the attention over the selected entries
+ * (mizuki-eaf.pages.dev, two-stage continued pre-training / sparse training;
+ * m.36881.com.cn, sparse training); the selection carries no gradient.  With
+ * the forward of dsa_sparse_mla_fwd (its out and lse) and the upstream
+ * gradient dout, for every query t, head h and valid entry a (row r = idx[t,a],
+ * c = kv[r], v = c[0:512], P_a the forward's probability):
+ *   dS_a = P_a (dout . v_a - dout . o)
+ *   dq[t,h]  = sm_scale sum_a dS_a c_a
+ *   dkv[r]  += sm_scale dS_a q[t,h] + P_a dout[t,h]   (the second term on dims 0..511)
+ * summed over every query and head that selected the row (an entry listed
+ * twice counts twice).
+ *   q [T,H,576], kv [N,576], out [T,H,512], dout [T,H,512] BF16; idx [T,k];
+ *   lse [T,H] fp32 (the forward's); dq [T,H,576], dkv [N,576] fp32 out, fully
+ *   overwritten.
+ * bf16 MFMA with fp32 sums; dS and P enter the products rounded to bf16, and
+ * dout . o uses the forward's bf16 output.  dkv is summed per row over its
+ * pairs in increasing (t, a) order (an inverted selection, no atomics), so
+ * it is deterministic as long as no idx row lists one row more than 4096
+ * times.
+ * workspace: dsa_sparse_mla_bwd_workspace_bytes(T, H, N, k), required.
+ * Limits: H a multiple of 32, at most 128; k <= 2048. */
+size_t dsa_sparse_mla_bwd_workspace_bytes(int32_t T, int32_t H, int64_t N, int32_t k);
+dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx, const void *out, const float *lse,
+                              const void *dout, int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *dq,
+                              float *dkv, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Index scores at listed positions: the scores a selection ranked, as the
  * indexer's KL loss needs them.  out[t, a] = I[t, idx[t, a]] with the E4M3
  * arithmetic of dsa_indexer_scores (same expression, bit-identical values),

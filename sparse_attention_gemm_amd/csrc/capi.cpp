@@ -269,6 +269,67 @@ dsa_status dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const uint8_
   return st;
 }
 
+// Sparse MLA backward workspace: D [T, H] fp32, then for one chunk of up to
+// kMlaBwdChunk queries s dS and P [Tc, k, H] bf16, the pair gradients
+// G [Tc, k, 576] fp32 and the inverted selection (cnt, start [N + 1], list [Tc k]).
+static constexpr int32_t kMlaBwdChunk = 512;
+static int32_t mla_bwd_chunk(int32_t T) { return T < kMlaBwdChunk ? T : kMlaBwdChunk; }
+static size_t mla_bwd_ws(int32_t T, int32_t H, int64_t N, int32_t k) {
+  const size_t tc = (size_t)mla_bwd_chunk(T);
+  return align_up((size_t)T * H * 4, 256) + 2 * align_up(tc * k * H * 2, 256) + align_up(tc * k * 576 * 4, 256) +
+         2 * align_up(((size_t)N + 1) * 4, 256) + align_up(tc * k * 4, 256);
+}
+
+size_t dsa_sparse_mla_bwd_workspace_bytes(int32_t T, int32_t H, int64_t N, int32_t k) {
+  if (T <= 0 || H <= 0 || N <= 0 || k <= 0) return 0;
+  return mla_bwd_ws(T, H, N, std::min<int32_t>(k, DSA_MAX_K));
+}
+
+dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx, const void *out, const float *lse,
+                              const void *dout, int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *dq,
+                              float *dkv, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "need T >= 0 and N >= 1");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
+  REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
+  REQUIRE(H > 0 && H % 32 == 0 && H <= 128, DSA_ERR_UNSUPPORTED,
+          "sparse MLA backward needs H a multiple of 32, at most 128 (got %d)", H);
+  REQUIRE(N <= 0x7FFFFFFF, DSA_ERR_UNSUPPORTED, "N must be < 2^31");
+  REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (T == 0) return DSA_OK;
+  REQUIRE(q && kv && idx && out && lse && dout && dq && dkv, DSA_ERR_INVALID_ARG, "null pointer");
+  const size_t need = mla_bwd_ws(T, H, N, k);
+  REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
+          workspace ? workspace_bytes : (size_t)0, need);
+  const int32_t tc_max = mla_bwd_chunk(T);
+  char *p = (char *)workspace;
+  float *D = (float *)p;
+  p += align_up((size_t)T * H * 4, 256);
+  void *dsT = p;
+  p += align_up((size_t)tc_max * k * H * 2, 256);
+  void *pT = p;
+  p += align_up((size_t)tc_max * k * H * 2, 256);
+  float *G = (float *)p;
+  p += align_up((size_t)tc_max * k * 576 * 4, 256);
+  int32_t *cnt = (int32_t *)p;
+  p += align_up(((size_t)N + 1) * 4, 256);
+  int32_t *start = (int32_t *)p;
+  p += align_up(((size_t)N + 1) * 4, 256);
+  int32_t *list = (int32_t *)p;
+  dsa_status st = hip_check(launch_mla_bwd_delta(out, dout, (int64_t)T * H, D, stream), "delta launch");
+  if (st == DSA_OK) st = hip_check(launch_fill_zero_f32(dkv, N * 576, stream), "fill launch");
+  for (int32_t t0 = 0; t0 < T && st == DSA_OK; t0 += tc_max) {
+    const int32_t tc = std::min(tc_max, T - t0);
+    st = hip_check(launch_mla_bwd_chunk(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, tc, dq, dsT, pT, G, stream),
+                   "sparse mla backward launch");
+    if (st == DSA_OK)
+      st = hip_check(launch_scatter_build(idx + (int64_t)t0 * k, (int64_t)tc * k, N, cnt, start, list, stream),
+                     "scatter launch");
+    if (st == DSA_OK) st = hip_check(launch_scatter_add(start, list, N, G, 576, dkv, stream), "scatter launch");
+  }
+  return st;
+}
+
 size_t dsa_masked_mha_workspace_bytes(int32_t L, int32_t H) {
   if (L <= 0 || H <= 0) return 0;
   return masked_mha_workspace_bytes(L, H);

@@ -583,6 +583,226 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
                                         part_ml, s);
 }
 
+// ------------------------------------------------------------------ backward
+//
+// In sparse training the main model is trained by the language-modelling
+// loss through the attention over the selected entries (mizuki-eaf.pages.dev,
+// two-stage continued pre-training / sparse training; m.36881.com.cn, sparse
+// training).  For query t, head h, entry a (latent row c_a, value v_a =
+// c_a[0..512)), with P from the forward's own log-sum-exp and the upstream
+// gradient dO:
+//   dP_a = dO . v_a,   D = dO . o,   dS_a = P_a (dP_a - D)
+//   dq   = s sum_a dS_a c_a
+//   dkv[r_a] += s dS_a q + P_a dO        (value dims get the second term)
+// Three kernels per chunk of queries, then the inverted-selection reduce:
+//  * mla_bwd_delta_kernel: D[t,h] = dO . o (o: the forward's output);
+//  * mla_bwd_ds_kernel: per (query, 16*NW heads), the forward's gather and
+//    logits, dP with dO^T resident, then dq^T += C^T dS^T (the transposing
+//    LDS read of the forward's PV, over all 576 dims, with the wave's own dS
+//    as the B operand); s dS and P go to the workspace key-major [pair][head]
+//    in bf16;
+//  * mla_bwd_g_kernel: per query, the pair gradients G[pair, :] =
+//    (s dS)^T q + P^T dO, a GEMM over the heads (K = heads, bf16 MFMA, fp32
+//    sums) with q and dO resident per wave for its 48 dims;
+//  * dkv[r] = sum of G over r's pairs in increasing pair order (scatter.hip).
+
+// D[t, h] = sum_d dO[t,h,d] o[t,h,d]: one wave per (t, h), 8 dims per lane.
+__global__ __launch_bounds__(256) void mla_bwd_delta_kernel(const __bf16 *__restrict__ out,
+                                                            const __bf16 *__restrict__ dout, int64_t TH,
+                                                            float *__restrict__ D) {
+  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (th >= TH) return;  // uniform per wave
+  const int lane = threadIdx.x & 63;
+  const bf16x8 o = *reinterpret_cast<const bf16x8 *>(out + th * 512 + lane * 8);
+  const bf16x8 g = *reinterpret_cast<const bf16x8 *>(dout + th * 512 + lane * 8);
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = fmaf((float)o[i], (float)g[i], acc);
+  acc = wave_sum(acc);
+  if (lane == 0) D[th] = acc;
+}
+
+// S^T-layout dot products of a gathered tile with NS resident 32-dim B
+// operands (dims 0 .. 32 NS): lane (g, c) gets x[r] = key 4g+r and x[4+r] =
+// key 16+4g+r of head c (no masking).
+template <int NS>
+__device__ __forceinline__ void tile_dot(const uint8_t *__restrict__ ct, const bf16x8 (&b)[NS], int g, int c,
+                                         float (&x)[8]) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t *arow0 = ct + c * kCRow + g * 16;
+  const uint8_t *arow1 = arow0 + 16 * kCRow;
+  bf16x8 op[2][2];
+  op[0][0] = *reinterpret_cast<const bf16x8 *>(arow0);
+  op[0][1] = *reinterpret_cast<const bf16x8 *>(arow1);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int cs = s & 1;
+    if (s + 1 < NS) {
+      op[cs ^ 1][0] = *reinterpret_cast<const bf16x8 *>(arow0 + (s + 1) * 64);
+      op[cs ^ 1][1] = *reinterpret_cast<const bf16x8 *>(arow1 + (s + 1) * 64);
+    }
+    s0 = mfma_bf16_16x16x32(op[cs][0], b[s], s0);
+    s1 = mfma_bf16_16x16x32(op[cs][1], b[s], s1);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = s0[r];
+    x[4 + r] = s1[r];
+  }
+}
+
+constexpr int kBwdNBuf = 2;
+// LDS of the dS kernel: two gathered tiles and the resolved rows of the query's entries
+constexpr int kSmemBwd = kBwdNBuf * kTileBytes + 2048 * 4;
+
+// One workgroup of NW waves per (query t0 + blockIdx.x, head group blockIdx.y
+// of 16 NW heads); wave w owns heads 16 w .. +16 of the group.
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
+    const float *__restrict__ lse, const __bf16 *__restrict__ dout, const float *__restrict__ Dd, int64_t N, int H,
+    int k, float sm_scale, int64_t t0, float *__restrict__ dq, __bf16 *__restrict__ dsT, __bf16 *__restrict__ pT) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  uint8_t *tiles = smem_raw;
+  int *rows = reinterpret_cast<int *>(smem_raw + kBwdNBuf * kTileBytes);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tc = blockIdx.x, t = t0 + tc;
+  const int head = blockIdx.y * 16 * NW + 16 * wave + c;  // this lane's head
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  const int ntiles = (k + kBN - 1) / kBN;
+  // Q^T and dO^T of the wave's heads (B operands: lane (g, c) holds head c, dims 32 s + 8 g .. +8)
+  bf16x8 qr[18], gr[16];
+  const __bf16 *qrow = q + (t * H + head) * 576 + g * 8;
+  const __bf16 *grow = dout + (t * H + head) * 512 + g * 8;
+#pragma unroll
+  for (int s = 0; s < 18; ++s) qr[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
+#pragma unroll
+  for (int s = 0; s < 16; ++s) gr[s] = *reinterpret_cast<const bf16x8 *>(grow + s * 32);
+  const float lse2 = lse[t * H + head] * 1.4426950408889634f;  // base-2 log-sum-exp of head c
+  const float Dh = Dd[t * H + head];
+  const int32_t *irow = idx + t * k;
+  for (int e = tid; e < ntiles * kBN; e += NW * 64) rows[e] = (int)phys_row(irow, nullptr, 0, N, t, e, k);
+  // dq^T accumulators: dims 16 i + 4 g + r of head c
+  f32x4 acc[36];
+#pragma unroll
+  for (int i = 0; i < 36; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tr_base = (4 * g + (c >> 2)) * kCRow + (c & 3) * 8;
+  __syncthreads();
+  if (ntiles > 0) gather_tile_async<NW>(tiles, rows, 0, kv, wave, lane);
+  for (int j = 0; j < ntiles; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's gathers of tile j have landed
+    __syncthreads();                // ... and every wave's; tile j-1 is free
+    if (j + 1 < ntiles) gather_tile_async<NW>(tiles + ((j + 1) & 1) * kTileBytes, rows, (j + 1) * kBN, kv, wave, lane);
+    const uint8_t *ct = tiles + (j & 1) * kTileBytes;
+    const int *rv = rows + j * kBN;
+    float x[8], dp[8];
+    tile_dot<18>(ct, qr, g, c, x);
+    tile_dot<16>(ct, gr, g, c, dp);
+    bf16x8 dsb;
+    float pv[8], dsv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
+      const float p = rv[key] >= 0 ? __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -lse2)) : 0.0f;
+      pv[i] = p;
+      dsv[i] = p * (dp[i] - Dh);
+      dsb[i] = (__bf16)dsv[i];
+    }
+    // dq^T[dims, head] += C^T[dims, keys] dS^T[keys, head]
+#pragma unroll
+    for (int i = 0; i < 36; ++i) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(ct + tr_base + i * 32));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(ct + tr_base + i * 32 + 16 * kCRow));
+      const i16x4 lohi[2] = {lo, hi};
+      acc[i] = mfma_bf16_16x16x32(*reinterpret_cast<const bf16x8 *>(lohi), dsb, acc[i]);
+    }
+    // s dS and P of the tile's entries, key-major
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = j * kBN + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
+      if (key < k) {
+        const int64_t o = (tc * k + key) * H + head;
+        dsT[o] = (__bf16)(sm_scale * dsv[i]);
+        pT[o] = (__bf16)pv[i];
+      }
+    }
+  }
+  float *dqrow = dq + (t * H + head) * 576 + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 36; ++i)
+    *reinterpret_cast<f32x4 *>(dqrow + 16 * i) =
+        f32x4{sm_scale * acc[i][0], sm_scale * acc[i][1], sm_scale * acc[i][2], sm_scale * acc[i][3]};
+}
+
+// Pair gradients of one query: G[pair, d] = sum_h (s dS)[pair, h] q[h, d] +
+// P[pair, h] dO[h, d] (the dO term for d < 512).  Workgroup (query,
+// blockIdx.y) of four waves covers dim tiles 12 y .. 12 y + 11 (16 dims
+// each); wave w owns three of them and holds their B operands (q and dO with
+// the heads along K) for the whole key loop.  KS = H / 32 K steps.
+constexpr int kGTilesPerWave = 3;
+constexpr int kGTilesPerGroup = 4 * kGTilesPerWave;  // 36 tiles of 16 dims: 3 groups
+template <int KS>
+__global__ __launch_bounds__(256) void mla_bwd_g_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ dout,
+                                                        const __bf16 *__restrict__ dsT, const __bf16 *__restrict__ pT,
+                                                        int k, int64_t t0, float *__restrict__ G) {
+  constexpr int H = 32 * KS;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tc = blockIdx.x, t = t0 + tc;
+  const int ti0 = blockIdx.y * kGTilesPerGroup + kGTilesPerWave * wave;  // uniform
+  // B operands: lane (g, c) holds heads 32 s + 8 g .. +8 of dim 16 (ti0 + j) + c
+  bf16x8 bq[kGTilesPerWave][KS], bo[kGTilesPerWave][KS];
+#pragma unroll
+  for (int jt = 0; jt < kGTilesPerWave; ++jt) {
+    const int d = 16 * (ti0 + jt) + c;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t h = 32 * s + 8 * g + e;
+        bq[jt][s][e] = q[(t * H + h) * 576 + d];
+        bo[jt][s][e] = d < 512 ? dout[(t * H + h) * 512 + d] : (__bf16)0.0f;
+      }
+    }
+  }
+  const __bf16 *dsq = dsT + tc * k * H;
+  const __bf16 *pq = pT + tc * k * H;
+  float *Gq = G + tc * k * 576;
+  for (int kb = 0; kb < k; kb += 16) {
+    // A operands: lane (g, c) holds key kb + c, heads 32 s + 8 g .. +8
+    const int key = kb + c;
+    bf16x8 ads[KS], ap[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (key < k) {
+        ads[s] = *reinterpret_cast<const bf16x8 *>(dsq + (int64_t)key * H + 32 * s + 8 * g);
+        ap[s] = *reinterpret_cast<const bf16x8 *>(pq + (int64_t)key * H + 32 * s + 8 * g);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ads[s][e] = ap[s][e] = (__bf16)0.0f;
+      }
+    }
+#pragma unroll
+    for (int jt = 0; jt < kGTilesPerWave; ++jt) {
+      const int ti = ti0 + jt;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) o = mfma_bf16_16x16x32(ads[s], bq[jt][s], o);
+      if (ti < 32) {  // value dims: uniform per wave and tile
+#pragma unroll
+        for (int s = 0; s < KS; ++s) o = mfma_bf16_16x16x32(ap[s], bo[jt][s], o);
+      }
+      // rows 4 g + r (keys), column c (dim)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = kb + 4 * g + r;
+        if (kr < k) Gq[(int64_t)kr * 576 + 16 * ti + c] = o[r];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 namespace dsa {
@@ -610,6 +830,62 @@ hipError_t launch_sparse_mla_bf16(const void *q, const void *kv, const int32_t *
   const int64_t th = (int64_t)T * H;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((uint32_t)((th + 3) / 4)), dim3(256), 0, s, part_o, part_ml, T,
                      H, splits, (__bf16 *)out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, float *D, hipStream_t s) {
+  if (TH == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_bwd_delta_kernel, dim3((uint32_t)((TH + 3) / 4)), dim3(256), 0, s, (const __bf16 *)out,
+                     (const __bf16 *)dout, TH, D);
+  return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_ds_nw(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
+                               const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0, int32_t Tc,
+                               float *dq, void *dsT, void *pT, hipStream_t s) {
+  static bool attr_done = false;  // per process: the attribute holds for every device
+  if (!attr_done) {
+    hipError_t e =
+        hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBwd);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(mla_bwd_ds_kernel<NW>, dim3((uint32_t)Tc, H / (16 * NW)), dim3(NW * 64), kSmemBwd, s,
+                     (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D, N, H, k, sm_scale, t0,
+                     dq, (__bf16 *)dsT, (__bf16 *)pT);
+  return hipGetLastError();
+}
+
+// Queries [t0, t0 + Tc): dq of those queries; s dS and P [Tc, k, H] bf16; then
+// the pair gradients G [Tc, k, 576] fp32.  H a multiple of 32, at most 128.
+hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
+                                const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0,
+                                int32_t Tc, float *dq, void *dsT, void *pT, float *G, hipStream_t s) {
+  if (Tc <= 0) return hipSuccess;
+  hipError_t e = H % 64 == 0 ? launch_ds_nw<4>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s)
+                             : launch_ds_nw<2>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s);
+  if (e != hipSuccess) return e;
+  switch (H / 32) {
+    case 1:
+      hipLaunchKernelGGL(mla_bwd_g_kernel<1>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
+                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
+      break;
+    case 2:
+      hipLaunchKernelGGL(mla_bwd_g_kernel<2>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
+                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
+      break;
+    case 3:
+      hipLaunchKernelGGL(mla_bwd_g_kernel<3>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
+                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
+      break;
+    case 4:
+      hipLaunchKernelGGL(mla_bwd_g_kernel<4>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
+                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

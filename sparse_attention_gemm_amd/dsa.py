@@ -27,6 +27,7 @@ EXPORTS = (
     "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd", "dsa_masked_mha_workspace_bytes",
     "dsa_masked_mha_prefill", "dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_decode_static_scratch_bytes",
     "dsa_decode_noalloc", "dsa_indexer_kl_bwd", "dsa_indexer_bwd_workspace_bytes", "dsa_indexer_bwd",
+    "dsa_sparse_mla_bwd_workspace_bytes", "dsa_sparse_mla_bwd",
 )
 
 
@@ -111,10 +112,13 @@ def load():
     L.dsa_indexer_scores_at.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]
     L.dsa_indexer_kl_fwd.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P]
     L.dsa_indexer_kl_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P]
+    L.dsa_sparse_mla_bwd_workspace_bytes.argtypes = [_I32, _I32, _I64, _I32]
+    L.dsa_sparse_mla_bwd_workspace_bytes.restype = _SZ
+    L.dsa_sparse_mla_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P, _P, _SZ, _P]
     L.dsa_indexer_bwd_workspace_bytes.argtypes = [_I32, _I32, _I32]
     L.dsa_indexer_bwd_workspace_bytes.restype = _SZ
     L.dsa_indexer_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
-    for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_indexer_kl_bwd", "dsa_indexer_bwd", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
+    for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_indexer_kl_bwd", "dsa_indexer_bwd", "dsa_sparse_mla_bwd", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
                  "dsa_prefill", "dsa_decode", "dsa_decode_noalloc", "dsa_paged_cache_append", "dsa_prefill_select",
                  "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd"):
         getattr(L, name).restype = ctypes.c_int
@@ -244,6 +248,22 @@ def dsa_indexer_kl_fwd(q, kv, idx, idx_scores, lse, sm_scale, kl, N=None, stream
     _check(load().dsa_indexer_kl_fwd(_ptr(q, bf, "q"), _ptr(kv, bf, "kv"), _ptr(idx, I32_T, "idx"),
                                      _ptr(idx_scores, F32_T, "idx_scores"), _ptr(lse, F32_T, "lse"), T, H, N,
                                      idx.shape[1], float(sm_scale), _ptr(kl, F32_T, "kl"), _stream(stream)))
+
+
+def dsa_sparse_mla_bwd_workspace_bytes(T: int, H: int, N: int, k: int) -> int:
+    return int(load().dsa_sparse_mla_bwd_workspace_bytes(T, H, N, k))
+
+
+def dsa_sparse_mla_bwd(q, kv, idx, out, lse, dout, sm_scale, dq, dkv, workspace, N=None, stream=None):
+    """dq [T, H, 576], dkv [N, 576] fp32 from the forward's out, lse and the upstream dout."""
+    T, H = q.shape[0], q.shape[1]
+    N = kv.shape[0] if N is None else N
+    bf = torch.bfloat16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().dsa_sparse_mla_bwd(_ptr(q, bf, "q"), _ptr(kv, bf, "kv"), _ptr(idx, I32_T, "idx"),
+                                     _ptr(out, bf, "out"), _ptr(lse, F32_T, "lse"), _ptr(dout, bf, "dout"), T, H, N,
+                                     idx.shape[1], float(sm_scale), _ptr(dq, F32_T, "dq"), _ptr(dkv, F32_T, "dkv"),
+                                     _ptr(workspace, name="workspace"), ws_bytes, _stream(stream)))
 
 
 def dsa_indexer_kl_bwd(q, kv, idx, idx_scores, lse, dkl, sm_scale, grad, N=None, stream=None):

@@ -269,6 +269,30 @@ hipError_t launch_fill_zero_f32(float *p, int64_t n, hipStream_t) {
   touch(p, (size_t)n * 4);
   return hipSuccess;
 }
+hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, float *D, hipStream_t) {
+  ++g_launches;
+  read_all(out, (size_t)TH * 512 * 2);
+  read_all(dout, (size_t)TH * 512 * 2);
+  touch(D, (size_t)TH * 4);
+  return hipSuccess;
+}
+hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
+                                const float *D, int64_t N, int32_t H, int32_t k, float, int64_t t0, int32_t Tc,
+                                float *dq, void *dsT, void *pT, float *G, hipStream_t) {
+  ++g_launches;
+  EXPECT(H % 32 == 0 && H <= 128);
+  read_all((const char *)q + t0 * H * 576 * 2, (size_t)Tc * H * 576 * 2);
+  read_all(kv, (size_t)N * 576 * 2);
+  read_all(idx + t0 * k, (size_t)Tc * k * 4);
+  read_all(lse + t0 * H, (size_t)Tc * H * 4);
+  read_all((const char *)dout + t0 * H * 512 * 2, (size_t)Tc * H * 512 * 2);
+  read_all(D + t0 * H, (size_t)Tc * H * 4);
+  touch(dq + t0 * H * 576, (size_t)Tc * H * 576 * 4);
+  touch(dsT, (size_t)Tc * k * H * 2);
+  touch(pT, (size_t)Tc * k * H * 2);
+  touch(G, (size_t)Tc * k * 576 * 4);
+  return hipSuccess;
+}
 // the static scratch: a host buffer of the same size, so a request carved past it overflows
 static std::vector<unsigned char> g_scratch(size_t(128) << 20);
 size_t static_scratch_bytes() { return g_scratch.size(); }
@@ -456,6 +480,25 @@ static void check_indexer_backward() {
   }
 }
 
+static void check_mla_backward() {
+  for (int T : {1, 6, 700}) {
+    for (int H : {32, 96, 128}) {
+      const int N = 2500, k = 2048;
+      Buf q((size_t)T * H * 576 * 2), kv((size_t)N * 576 * 2), idx((size_t)T * k * 4), out((size_t)T * H * 512 * 2),
+          lse((size_t)T * H * 4), dout((size_t)T * H * 512 * 2), dq((size_t)T * H * 576 * 4), dkv((size_t)N * 576 * 4);
+      const size_t wsb = dsa_sparse_mla_bwd_workspace_bytes(T, H, N, k);
+      Buf ws(wsb);
+      EXPECT(dsa_sparse_mla_bwd(q.p(), kv.p(), (int32_t *)idx.p(), out.p(), (float *)lse.p(), dout.p(), T, H, N, k,
+                                0.07f, (float *)dq.p(), (float *)dkv.p(), ws.p(), wsb, 0) == DSA_OK);
+      EXPECT(dsa_sparse_mla_bwd(q.p(), kv.p(), (int32_t *)idx.p(), out.p(), (float *)lse.p(), dout.p(), T, H, N, k,
+                                0.07f, (float *)dq.p(), (float *)dkv.p(), ws.p(), wsb - 1, 0) == DSA_ERR_WORKSPACE);
+    }
+  }
+  Buf one(64);
+  EXPECT(dsa_sparse_mla_bwd(one.p(), one.p(), (int32_t *)one.p(), one.p(), (float *)one.p(), one.p(), 1, 16, 1, 1,
+                            0.07f, (float *)one.p(), (float *)one.p(), one.p(), 64, 0) == DSA_ERR_UNSUPPORTED);
+}
+
 static void check_training_side() {
   const int T = 50, H = 128, k = 2048, S = 3000, L = 700;
   Buf q8((size_t)T * 64 * 128), qs(T * 4), k8((size_t)S * 128), ks(S * 4), w((size_t)T * 64 * 4),
@@ -481,6 +524,7 @@ int main() {
   check_decode();
   check_training_side();
   check_indexer_backward();
+  check_mla_backward();
   {  // a decode too large for the static scratch is refused before any launch
     dsa_decode_args a;
     std::memset(&a, 0, sizeof a);

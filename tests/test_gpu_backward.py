@@ -215,3 +215,89 @@ def test_indexer_kl_backward_after_prefill_selection(dsa, ora):
     dI = float(np.abs(sc.cpu().double().numpy() - sco)[gidx >= 0].max())
     _check("score gradient vs the oracle's own scores", grad.cpu().numpy(), full["g"],
            (1e-4 + 2 * dI) * dklv[:, None] * (pi + np.abs(p)) + 1e-12)
+
+
+# ------------------------------------------------------------------ sparse MLA backward
+# dS and P enter the products rounded to bf16 (unit roundoff 2^-8 each), and
+# D = dout . o uses the forward's bf16 output; the oracle's magnitudes carry
+# the matching terms (|dS| + P sum|dout||o|, and P |dout|), so the error is
+# within 2^-8 of them per rounding: 3 * 2^-8 mag covers the two roundings a
+# term meets plus the fp32 sums.
+MLA_BWD_RTOL = 3 * 2.0 ** -8
+
+
+def _mla_bwd_gpu(dsa, q, kv, idx, dout, sm):
+    T, H = q.shape[0], q.shape[1]
+    N, k = kv.shape[0], idx.shape[1]
+    d = {n: x.to(DEV) for n, x in dict(q=q, kv=kv, idx=idx, dout=dout).items()}
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_mla_fwd(d["q"], d["kv"], d["idx"], sm, out, lse)
+    dq = torch.full((T, H, 576), 7.0, device=DEV)
+    dkv = torch.full((N, 576), 7.0, device=DEV)
+    ws = torch.empty(dsa.dsa_sparse_mla_bwd_workspace_bytes(T, H, N, k), dtype=torch.uint8, device=DEV)
+    dsa.dsa_sparse_mla_bwd(d["q"], d["kv"], d["idx"], out, lse, d["dout"], sm, dq, dkv, ws)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dkv.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,N,k,qstd", [(6, 128, 5000, 2048, 1.0), (600, 64, 3000, 256, 1.0),
+                                          (9, 32, 2000, 100, 40.0), (5, 96, 1500, 512, 3.0)])
+def test_sparse_mla_bwd(dsa, ora, T, H, N, k, qstd):
+    """dq and dkv against the oracle; T = 600 spans two query chunks; a sharp
+    softmax (q x 40); a ragged, an empty and a duplicated entry, and an entry
+    outside the latent rows."""
+    _say(f"sparse mla backward T={T} H={H} N={N} k={k} qstd={qstd}")
+    sm = 1 / math.sqrt(192)
+    q = synth.normal(51, 1, (T, H, 576), std=qstd).to(torch.bfloat16)
+    kv = synth.normal(51, 2, (N, 576), std=1 / 24).to(torch.bfloat16)
+    dout = synth.normal(51, 3, (T, H, 512)).to(torch.bfloat16)
+    idx = _selection(51, T, N - 1, k)          # row N-1 is never selected
+    idx[0, 5] = N + 3                          # outside the rows: skipped
+    idx[4, 1] = idx[4, 0]                      # one row listed twice
+    dq, dkv = _mla_bwd_gpu(dsa, q, kv, idx, dout, sm)
+    ref_idx = idx.clone()
+    ref_idx[0, 5] = -1
+    r = ora.sparse_mla_bwd(q, kv, ref_idx.numpy(), dout, sm)
+    _check("dq", dq, r["dq"], MLA_BWD_RTOL * r["mag_dq"] + 1e-30)
+    _check("dkv", dkv, r["dkv"], MLA_BWD_RTOL * r["mag_dkv"] + 1e-30)
+    assert np.all(dkv[N - 1] == 0) and np.all(dq[2] == 0)
+
+
+def test_sparse_mla_bwd_is_deterministic(dsa):
+    T, H, N, k = 700, 128, 4000, 512
+    _say("sparse mla backward determinism")
+    q = synth.normal(52, 1, (T, H, 576)).to(torch.bfloat16)
+    kv = synth.normal(52, 2, (N, 576), std=1 / 24).to(torch.bfloat16)
+    dout = synth.normal(52, 3, (T, H, 512)).to(torch.bfloat16)
+    idx = _selection(52, T, N, k)
+    a = _mla_bwd_gpu(dsa, q, kv, idx, dout, 0.07)
+    b = _mla_bwd_gpu(dsa, q, kv, idx, dout, 0.07)
+    assert np.array_equal(a[0].view(np.int32), b[0].view(np.int32))
+    assert np.array_equal(a[1].view(np.int32), b[1].view(np.int32))
+
+
+def test_sparse_mla_bwd_after_prefill_selection(dsa, ora):
+    """The sparse-training attention step on the library's own fused causal
+    selection: fused prefill -> backward, against the oracle on that selection."""
+    L, k, H = 1200, 256, 64
+    _say(f"sparse mla backward after the fused selection L={L} k={k} H={H}")
+    cfg = synth.scaled_down(synth.CONFIGS["prefill16k"], L=L, k=k, H=H, seed=53)
+    q_i, k_i, w = synth.prefill_indexer_inputs(cfg)
+    q, kv = synth.prefill_attn_q(cfg), synth.prefill_latent(cfg)
+    q8, qs = ora.quantize_rows(q_i.view(L, -1).numpy())
+    k8, ks = ora.quantize_rows(k_i.numpy())
+    d = {n: torch.from_numpy(np.ascontiguousarray(x)).to(DEV) if isinstance(x, np.ndarray) else x.to(DEV)
+         for n, x in dict(q8=q8.reshape(L, 64, 128), qs=qs, k8=k8, ks=ks, w=w, q=q, kv=kv).items()}
+    idx = torch.empty((L, k), dtype=torch.int32, device=DEV)
+    args = dsa.make_prefill_args(L, 64, 128, H, k, dsa.DSA_E4M3, d["q8"], d["qs"], d["k8"], d["ks"], d["w"],
+                                 dsa.DSA_BF16, None, None, cfg.sm_scale, idx, None, None)
+    ws = torch.empty(dsa.dsa_prefill_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    dsa.dsa_prefill_select(args, ws)
+    torch.cuda.synchronize()
+    dout = synth.normal(53, 9, (L, H, 512), std=0.01).to(torch.bfloat16)
+    gidx = idx.cpu()
+    dq, dkv = _mla_bwd_gpu(dsa, q, kv, gidx, dout, cfg.sm_scale)
+    r = ora.sparse_mla_bwd(q, kv, gidx.numpy(), dout, cfg.sm_scale)
+    _check("dq (pipeline)", dq, r["dq"], MLA_BWD_RTOL * r["mag_dq"] + 1e-30)
+    _check("dkv (pipeline)", dkv, r["dkv"], MLA_BWD_RTOL * r["mag_dkv"] + 1e-30)
