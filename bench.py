@@ -15,8 +15,10 @@ fractions, decode tokens/s for B = 64 sequences at context 32768 and for the
 ragged paged batch (B = 128, context 4096..131072, shuffled 64-token pages),
 short prefill (L = 4096) through the masked-MHA mode next to the same
 selection through sparse MLA, the indexer's KL-alignment loss forward on the
-headline selection (the step beside the path in sparse training), and the
-fp64 CPU oracle timed on a bounded sample of the headline workload.
+headline selection (the step beside the path in sparse training), the
+L = 16384 prefill and the backward of its sparse-training step, the measured
+MFMA/HBM peaks, and the fp64 CPU oracle timed on a bounded sample of the
+headline workload.
 
 Inputs are synthetic (synth), drawn on the GPU with the same counter-based
 generator the oracle side uses.
@@ -36,6 +38,7 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "DSA prefill tokens/s at L=128K + decode tokens/s; % FP8 MFMA / HBM peak"
 
 
@@ -48,6 +51,8 @@ def parse():
     ap.add_argument("--decode-warmup", type=int, default=5)
     ap.add_argument("--no-prefill16k", action="store_true", help="skip the L=16384 prefill entry")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward section")
+    ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--cpu-rows-1t", type=int, default=16, help="query rows in the single-thread oracle sample")
     ap.add_argument("--no-decode", action="store_true", help="prefill only")
     ap.add_argument("--no-paged", action="store_true", help="skip the ragged paged decode batch")
@@ -295,6 +300,66 @@ def run_kl(torch, dsa, cfg, t, dev, steps):
     return res
 
 
+# --------------------------------------------------------------------------- backward
+def run_backward(torch, dsa, cfg, t, dev, steps):
+    """One sparse-training step's backward on a prefill's own outputs (its
+    selection, attention output and lse): the sparse-MLA backward with a
+    synthetic upstream gradient, and the indexer's KL backward (scores at the
+    selection, the score gradient of the mean per-token KL, then dw, dq, dk)."""
+    import synth
+    L, H, k = cfg.L, cfg.H, cfg.k
+    dout = synth.normal(cfg.seed, 91, (L, H, 512), device=dev, std=0.01).to(torch.bfloat16)
+    dq = torch.empty((L, H, 576), dtype=torch.float32, device=dev)
+    dkv = torch.empty((L, 576), dtype=torch.float32, device=dev)
+    mws = torch.empty(dsa.dsa_sparse_mla_bwd_workspace_bytes(L, H, L, k), dtype=torch.uint8, device=dev)
+    sc = torch.empty((L, k), dtype=torch.float32, device=dev)
+    dkl = torch.full((L,), 1.0 / L, dtype=torch.float32, device=dev)
+    grad = torch.empty((L, k), dtype=torch.float32, device=dev)
+    dw = torch.empty((L, cfg.H_I), dtype=torch.float32, device=dev)
+    dqi = torch.empty((L, cfg.H_I, cfg.D_I), dtype=torch.float32, device=dev)
+    dki = torch.empty((L, cfg.D_I), dtype=torch.float32, device=dev)
+    iws = torch.empty(dsa.dsa_indexer_bwd_workspace_bytes(L, L, k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    st = StageSamples(torch, ["sparse_mla_bwd", "scores_at", "kl_grad", "indexer_bwd"])
+    for i in range(steps + 1):
+        evs = st.new()
+        evs[0].record(stream)
+        dsa.dsa_sparse_mla_bwd(t["q"], t["kv"], t["idx"], t["out"], t["lse"], dout, cfg.sm_scale, dq, dkv, mws,
+                               stream=stream)
+        evs[1].record(stream)
+        dsa.dsa_indexer_scores_at(t["q8"], t["qs"], t["k8"], t["ks"], t["w"], t["idx"], sc, stream=stream)
+        evs[2].record(stream)
+        dsa.dsa_indexer_kl_bwd(t["q"], t["kv"], t["idx"], sc, t["lse"], dkl, cfg.sm_scale, grad, stream=stream)
+        evs[3].record(stream)
+        dsa.dsa_indexer_bwd(t["q8"], t["qs"], t["k8"], t["ks"], t["w"], t["idx"], grad, dw, dqi, dki, iws,
+                            stream=stream)
+        evs[4].record(stream)
+        torch.cuda.synchronize()
+        if i > 0:
+            st.add(evs)
+    ms = {n: v for n, v in st.median_ms().items() if n != "_step"}
+    pairs = prefill_work(cfg)["selected_pairs"]
+    # the four products of the attention backward (dP, dq, dkv's logit and value parts):
+    # 2 H (512 + 576 + 576 + 512) FLOP per selected pair; the logits' recompute is not counted
+    mla_flop = 2 * H * (512 + 576 + 576 + 512) * pairs
+    # the indexer backward: the dot products again (FP8 MFMA), then dq and each pair's dk share (fp32)
+    idx_flop = 3 * 2 * cfg.H_I * cfg.D_I * pairs
+    res = {
+        "workload": cfg.name, "L": L, "H": H, "k": k, "steps": steps,
+        "stages_ms": {n: round(v, 3) for n, v in ms.items()},
+        "tokens_per_s": round(L / (sum(ms.values()) / 1e3), 1),
+        "roofline": {
+            "sparse_mla_bwd": _rl("mfma", mla_flop / (ms["sparse_mla_bwd"] / 1e3) / 1e12, PEAK_BF16_TFLOPS,
+                                  "TFLOP/s"),
+            "indexer_bwd": _rl("alu", idx_flop / (ms["indexer_bwd"] / 1e3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+        },
+        "work": {"selected_pairs": pairs, "sparse_mla_bwd_flop": mla_flop, "indexer_bwd_flop": idx_flop},
+        "data": "synthetic upstream gradient dout ~ N(0, 0.01^2) bf16; dkl = 1/L (mean of the per-token loss)",
+    }
+    del dout, dq, dkv, mws, sc, grad, dw, dqi, dki, iws
+    return res
+
+
 # --------------------------------------------------------------------------- short prefill
 def run_short_prefill(torch, dsa, synth, cfg, dev, steps, warmup):
     """One causal sequence of cfg.L tokens: quantise + fused indexer/top-k, then
@@ -411,8 +476,8 @@ def _rl(bound, achieved, peak, unit, traffic=None):
 # --------------------------------------------------------------------------- measured peaks
 def measure_peaks(torch, dev, reps=5):
     """The chip's rates measured by plain microbenchmarks (libdsa_peaks.so):
-    dense FP8 and bf16 MFMA loops, and a streaming HBM read of 8 GiB.  Best of
-    `reps` runs each."""
+    dense FP8 and bf16 MFMA loops, and a streaming HBM read and write of 8 GiB.
+    Best of `reps` runs each."""
     import ctypes
     from sparse_attention_gemm_amd import build
     lib = ctypes.CDLL(build.PEAKS_LIB)
@@ -421,6 +486,7 @@ def measure_peaks(torch, dev, reps=5):
     lib.dsa_peak_fp8_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dsa_peak_bf16_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dsa_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dsa_peak_hbm_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     blocks = n_cu * 8
     sink = torch.zeros(blocks, dtype=torch.float32, device=dev)
@@ -447,11 +513,18 @@ def measure_peaks(torch, dev, reps=5):
     hbm_ms = best(lambda: lib.dsa_peak_hbm_read(buf.data_ptr(), buf.numel(), n_cu * 16, sink.data_ptr(),
                                                  stream.cuda_stream))
     hbm = buf.numel() / (hbm_ms / 1e3) / 1e9
+    wr = {}
+    for nt in (0, 1):
+        ms = best(lambda: lib.dsa_peak_hbm_write(buf.data_ptr(), buf.numel(), n_cu * 16, nt, stream.cuda_stream))
+        wr[nt] = buf.numel() / (ms / 1e3) / 1e9
     del buf
     torch.cuda.empty_cache()
     return {"fp8_mfma_tflops": round(fp8, 1), "bf16_mfma_tflops": round(bf16, 1), "hbm_read_gbs": round(hbm, 1),
+            "hbm_write_gbs": round(max(wr.values()), 1),
+            "hbm_write_gbs_by_policy": {"default": round(wr[0], 1), "streaming": round(wr[1], 1)},
             "method": f"best of {reps}: {blocks} workgroups x 4 waves x {iters} iterations of 4 independent "
-                      "32x32x64 E4M3 / 32x32x16 bf16 MFMAs; an 8 GiB streaming read with 16-byte loads",
+                      "32x32x64 E4M3 / 32x32x16 bf16 MFMAs; an 8 GiB streaming read with 16-byte loads; the "
+                      "same 8 GiB written with 16-byte stores",
             "datasheet": {"fp8_mfma_tflops": PEAK_FP8_TFLOPS, "bf16_mfma_tflops": PEAK_BF16_TFLOPS,
                           "hbm_gbs": PEAK_HBM_GBS}}
 
@@ -680,6 +753,9 @@ def main():
         d16, k16, s16, work16 = prefill_rooflines(c16, ms16, peaks, traffic=False)
         line["prefill16k"] = {"workload": c16.name, "L": c16.L, "tokens_per_s": round(c16.L * max(args.steps, 5) / w16, 1),
                               "ms_per_step": round(w16 / max(args.steps, 5) * 1e3, 3), "stages": s16, "work": work16}
+        if not args.no_backward:
+            log("backward of the L=16384 step (sparse MLA, indexer KL)")
+            line["backward"] = run_backward(torch, dsa, c16, t16, dev, args.backward_steps)
         del t16
         torch.cuda.empty_cache()
     if not args.no_decode:

@@ -597,13 +597,14 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
 // Three kernels per chunk of queries, then the inverted-selection reduce:
 //  * mla_bwd_delta_kernel: D[t,h] = dO . o (o: the forward's output);
 //  * mla_bwd_ds_kernel: per (query, 16*NW heads), the forward's gather and
-//    logits, dP with dO^T resident, then dq^T += C^T dS^T (the transposing
+//    logits, and dP with dO^T resident (one LDS read of each tile fragment
+//    feeds both), then dq^T += C^T dS^T (the transposing
 //    LDS read of the forward's PV, over all 576 dims, with the wave's own dS
 //    as the B operand); s dS and P go to the workspace key-major [pair][head]
 //    in bf16;
 //  * mla_bwd_g_kernel: per query, the pair gradients G[pair, :] =
 //    (s dS)^T q + P^T dO, a GEMM over the heads (K = heads, bf16 MFMA, fp32
-//    sums) with q and dO resident per wave for its 48 dims;
+//    sums) with q^T and dO^T resident in registers and s dS, P streamed;
 //  * dkv[r] = sum of G over r's pairs in increasing pair order (scatter.hip).
 
 // D[t, h] = sum_d dO[t,h,d] o[t,h,d]: one wave per (t, h), 8 dims per lane.
@@ -622,53 +623,141 @@ __global__ __launch_bounds__(256) void mla_bwd_delta_kernel(const __bf16 *__rest
   if (lane == 0) D[th] = acc;
 }
 
-// S^T-layout dot products of a gathered tile with NS resident 32-dim B
-// operands (dims 0 .. 32 NS): lane (g, c) gets x[r] = key 4g+r and x[4+r] =
-// key 16+4g+r of head c (no masking).
-template <int NS>
-__device__ __forceinline__ void tile_dot(const uint8_t *__restrict__ ct, const bf16x8 (&b)[NS], int g, int c,
-                                         float (&x)[8]) {
+// S^T-layout dot products of a gathered tile with the resident Q^T (all 576
+// dims) and dO^T (the 512 value dims) of a head: lane (g, c) gets x[r] /
+// dp[r] = key 4g+r and x[4+r] / dp[4+r] = key 16+4g+r of head c (no
+// masking).  Each tile fragment is read from LDS once for both products.
+__device__ __forceinline__ void tile_dot_pair(const uint8_t *__restrict__ ct, const bf16x8 (&bq)[18],
+                                              const bf16x8 (&bo)[16], int g, int c, float (&x)[8], float (&dp)[8]) {
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
   const uint8_t *arow0 = ct + c * kCRow + g * 16;
   const uint8_t *arow1 = arow0 + 16 * kCRow;
-  bf16x8 op[2][2];
-  op[0][0] = *reinterpret_cast<const bf16x8 *>(arow0);
-  op[0][1] = *reinterpret_cast<const bf16x8 *>(arow1);
+  bf16x8 op[3][2];  // operands of steps s, s+1 and s+2 in flight
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int cs = s & 1;
-    if (s + 1 < NS) {
-      op[cs ^ 1][0] = *reinterpret_cast<const bf16x8 *>(arow0 + (s + 1) * 64);
-      op[cs ^ 1][1] = *reinterpret_cast<const bf16x8 *>(arow1 + (s + 1) * 64);
+  for (int s = 0; s < 2; ++s) {
+    op[s][0] = *reinterpret_cast<const bf16x8 *>(arow0 + s * 64);
+    op[s][1] = *reinterpret_cast<const bf16x8 *>(arow1 + s * 64);
+  }
+#pragma unroll
+  for (int s = 0; s < 18; ++s) {
+    const int cs = s % 3;
+    if (s + 2 < 18) {
+      op[(s + 2) % 3][0] = *reinterpret_cast<const bf16x8 *>(arow0 + (s + 2) * 64);
+      op[(s + 2) % 3][1] = *reinterpret_cast<const bf16x8 *>(arow1 + (s + 2) * 64);
     }
-    s0 = mfma_bf16_16x16x32(op[cs][0], b[s], s0);
-    s1 = mfma_bf16_16x16x32(op[cs][1], b[s], s1);
+    s0 = mfma_bf16_16x16x32(op[cs][0], bq[s], s0);
+    s1 = mfma_bf16_16x16x32(op[cs][1], bq[s], s1);
+    if (s < 16) {
+      d0 = mfma_bf16_16x16x32(op[cs][0], bo[s], d0);
+      d1 = mfma_bf16_16x16x32(op[cs][1], bo[s], d1);
+    }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     x[r] = s0[r];
     x[4 + r] = s1[r];
+    dp[r] = d0[r];
+    dp[4 + r] = d1[r];
   }
 }
 
-constexpr int kBwdNBuf = 2;
-// LDS of the dS kernel: two gathered tiles and the resolved rows of the query's entries
-constexpr int kSmemBwd = kBwdNBuf * kTileBytes + 2048 * 4;
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete,
+// then the hardware barrier (a compiler barrier for memory too).  Unlike
+// __syncthreads() it carries no release fence on global memory, which would
+// also wait for every gather and store in flight; gathers are waited for
+// explicitly before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Transposing LDS reads issued as one block that also waits for them.  LLVM
+// cannot tell these reads from the direct-to-LDS gathers in flight, and would
+// otherwise wait for every outstanding gather (the next tiles') before each
+// of them; the buffers they read were completed by an explicit wait and a
+// barrier.  Reads a[n] at base + OFF[n].
+#define DSA_TR_READ4(a, base, o0, o1, o2, o3)                                                     \
+  asm volatile(                                                                                   \
+      "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"                                                   \
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"                                                   \
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"                                                   \
+      "ds_read_b64_tr_b16 %3, %4 offset:%8\n\t"                                                   \
+      "s_waitcnt lgkmcnt(0)"                                                                      \
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])                                        \
+      : "v"(base), "i"(o0), "i"(o1), "i"(o2), "i"(o3)                                             \
+      : "memory")
+
+#define DSA_TR_READ12(a, base, o0, o1, o2, o3, o4, o5, o6, o7, o8, o9, o10, o11)                       \
+  asm volatile(                                                                                    \
+      "ds_read_b64_tr_b16 %0, %12 offset:%13\n\t"                                                  \
+      "ds_read_b64_tr_b16 %1, %12 offset:%14\n\t"                                                  \
+      "ds_read_b64_tr_b16 %2, %12 offset:%15\n\t"                                                  \
+      "ds_read_b64_tr_b16 %3, %12 offset:%16\n\t"                                                  \
+      "ds_read_b64_tr_b16 %4, %12 offset:%17\n\t"                                                  \
+      "ds_read_b64_tr_b16 %5, %12 offset:%18\n\t"                                                  \
+      "ds_read_b64_tr_b16 %6, %12 offset:%19\n\t"                                                  \
+      "ds_read_b64_tr_b16 %7, %12 offset:%20\n\t"                                                  \
+      "ds_read_b64_tr_b16 %8, %12 offset:%21\n\t"                                                  \
+      "ds_read_b64_tr_b16 %9, %12 offset:%22\n\t"                                                  \
+      "ds_read_b64_tr_b16 %10, %12 offset:%23\n\t"                                                 \
+      "ds_read_b64_tr_b16 %11, %12 offset:%24\n\t"                                                 \
+      "s_waitcnt lgkmcnt(0)"                                                                       \
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), \
+        "=&v"(a[7]), "=&v"(a[8]), "=&v"(a[9]), "=&v"(a[10]), "=&v"(a[11])                           \
+      : "v"(base), "i"(o0), "i"(o1), "i"(o2), "i"(o3), "i"(o4), "i"(o5), "i"(o6), "i"(o7), "i"(o8), \
+        "i"(o9), "i"(o10), "i"(o11)                                                                \
+      : "memory")
+
+// The A operands of dq^T tiles I .. I+5 (dims 16 i .. +16, the tile's 32 keys)
+// through the transposing read: rows 4 g + (c >> 2) (+16), columns 16 i + 4 (c & 3).
+template <int I>
+__device__ __forceinline__ void dq_operands6(uint32_t base, bf16x8 (&op)[6]) {
+  constexpr int h = 16 * kCRow;
+  i16x4 r[12];
+  DSA_TR_READ12(r, base, I * 32, I * 32 + h, (I + 1) * 32, (I + 1) * 32 + h, (I + 2) * 32, (I + 2) * 32 + h,
+                (I + 3) * 32, (I + 3) * 32 + h, (I + 4) * 32, (I + 4) * 32 + h, (I + 5) * 32, (I + 5) * 32 + h);
+#pragma unroll
+  for (int n = 0; n < 6; ++n) {
+    const i16x4 a[2] = {r[2 * n], r[2 * n + 1]};
+    op[n] = *reinterpret_cast<const bf16x8 *>(a);
+  }
+}
+
+constexpr int kBwdNBuf = 3;  // gathered tiles: computed, landed, in flight
+constexpr int kStageRow = 2 * kBN + 8;  // LDS bytes per head row of staged s dS or P (32 keys + pad):
+                                        // 18 dwords keeps both the 8-byte writes and the
+                                        // transposing reads conflict-free
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+// LDS of the dS kernel: two gathered tiles, the resolved rows of the query's
+// entries, and two buffers of staged s dS and P (16 NW heads x 32 keys each)
+template <int NW>
+constexpr int smem_bwd_bytes() {
+  return kBwdNBuf * kTileBytes + 2048 * 4 + 2 * 2 * 16 * NW * kStageRow;
+}
 
 // One workgroup of NW waves per (query t0 + blockIdx.x, head group blockIdx.y
-// of 16 NW heads); wave w owns heads 16 w .. +16 of the group.
+// of 16 NW heads); wave w owns heads 16 w .. +16 of the group.  The tile's
+// s dS and P go to LDS head-major and leave one tile later as 16-byte runs of
+// the key-major workspace rows, so the only vector-memory operations a tile
+// waits for are its own gathers (loads and stores complete in issue order).
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const float *__restrict__ Dd, int64_t N, int H,
     int k, float sm_scale, int64_t t0, float *__restrict__ dq, __bf16 *__restrict__ dsT, __bf16 *__restrict__ pT) {
+  constexpr int kHeads = 16 * NW;
+  constexpr int kStageBuf = 2 * kHeads * kStageRow;  // s dS rows, then P rows
   extern __shared__ __align__(16) uint8_t smem_raw[];
   uint8_t *tiles = smem_raw;
   int *rows = reinterpret_cast<int *>(smem_raw + kBwdNBuf * kTileBytes);
+  uint8_t *stage = smem_raw + kBwdNBuf * kTileBytes + 2048 * 4;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tc = blockIdx.x, t = t0 + tc;
-  const int head = blockIdx.y * 16 * NW + 16 * wave + c;  // this lane's head
+  const int head = blockIdx.y * kHeads + 16 * wave + c;  // this lane's head
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const int ntiles = (k + kBN - 1) / kBN;
   // Q^T and dO^T of the wave's heads (B operands: lane (g, c) holds head c, dims 32 s + 8 g .. +8)
@@ -688,45 +777,98 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
 #pragma unroll
   for (int i = 0; i < 36; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int tr_base = (4 * g + (c >> 2)) * kCRow + (c & 3) * 8;
+  // The query's s dS and P rows as bounded buffers: stores of entries >= k are dropped.
+  const __amdgpu_buffer_rsrc_t rds =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(dsT + tc * k * H), 0, k * H * 2, (int)kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rp =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(pT + tc * k * H), 0, k * H * 2, (int)kRsrcWord3);
+  // Write-out roles: lane group tid / 16 takes key 16 (group & 1) + c and the
+  // group's 8 heads 8 (group >> 1) .. +8, read from the head-major staging
+  // with the transposing load (lane c of a group gets column c of a 4 x 16 block).
+  const int grp = tid >> 4, okey = 16 * (grp & 1) + c, oh = 8 * (grp >> 1);
+  const int tr_stage = (oh + (c >> 2)) * kStageRow + (16 * (grp & 1) + 4 * (c & 3)) * 2;
+  const int ooff = (okey * H + blockIdx.y * kHeads + oh) * 2;  // bytes, within a tile's rows
+  auto write_out = [&](int jt) {  // tile jt's staged values to the workspace
+    const uint8_t *sb = stage + (jt & 1) * kStageBuf;
+    i16x4 r[4];
+    DSA_TR_READ4(r, lds_addr(sb + tr_stage), 0, 4 * kStageRow, kHeads * kStageRow, kHeads * kStageRow + 4 * kStageRow);
+    const i16x4 dd[2] = {r[0], r[1]}, pp[2] = {r[2], r[3]};
+    const int off = jt * kBN * H * 2 + ooff;
+    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4 *>(dd), rds, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4 *>(pp), rp, off, 0, 0);
+  };
+  // gather instructions a wave issues per tile (the fewest, over the waves)
+  constexpr int kGatherMin = kGatherInsts / NW;
   __syncthreads();
   if (ntiles > 0) gather_tile_async<NW>(tiles, rows, 0, kv, wave, lane);
+  if (ntiles > 1) gather_tile_async<NW>(tiles + kTileBytes, rows, kBN, kv, wave, lane);
   for (int j = 0; j < ntiles; ++j) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's gathers of tile j have landed
-    __syncthreads();                // ... and every wave's; tile j-1 is free
-    if (j + 1 < ntiles) gather_tile_async<NW>(tiles + ((j + 1) & 1) * kTileBytes, rows, (j + 1) * kBN, kv, wave, lane);
-    const uint8_t *ct = tiles + (j & 1) * kTileBytes;
+    // This wave's gathers of tile j have landed.  Issued after them, in order:
+    // the stores of tile j-3 (j >= 3), the gathers of tile j+1 (j+1 < ntiles)
+    // and the stores of tile j-2 (j >= 2); waiting until at most that many are
+    // outstanding (counting the fewest gathers any wave issues) leaves them in
+    // flight.
+    {
+      const int ns = (j >= 3 ? 2 : 0) + (j >= 2 ? 2 : 0);  // uniform
+      if (j + 1 < ntiles) {
+        if (ns == 4)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + kGatherMin));
+        else if (ns == 2)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 + kGatherMin));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGatherMin));
+      } else {
+        if (ns == 4)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        else if (ns == 2)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+        else
+          __builtin_amdgcn_s_waitcnt(0);
+      }
+    }
+    lds_barrier();  // every wave's; tile j-1's buffer and staging buffer (j-1) & 1 are complete
+    if (j + 2 < ntiles)
+      gather_tile_async<NW>(tiles + ((j + 2) % kBwdNBuf) * kTileBytes, rows, (j + 2) * kBN, kv, wave, lane);
+    if (j >= 1) write_out(j - 1);
+    const uint8_t *ct = tiles + (j % kBwdNBuf) * kTileBytes;
     const int *rv = rows + j * kBN;
     float x[8], dp[8];
-    tile_dot<18>(ct, qr, g, c, x);
-    tile_dot<16>(ct, gr, g, c, dp);
-    bf16x8 dsb;
-    float pv[8], dsv[8];
+    tile_dot_pair(ct, qr, gr, g, c, x, dp);
+    bf16x8 dsb, sdb, pb;
+    float dsv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
       const float p = rv[key] >= 0 ? __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -lse2)) : 0.0f;
-      pv[i] = p;
       dsv[i] = p * (dp[i] - Dh);
       dsb[i] = (__bf16)dsv[i];
+      sdb[i] = (__bf16)(sm_scale * dsv[i]);
+      pb[i] = (__bf16)p;
+    }
+    // s dS and P of the tile, head-major: row 16 wave + c, keys 4 g .. +4 and 16 + 4 g .. +4
+    {
+      uint8_t *sb = stage + (j & 1) * kStageBuf + (16 * wave + c) * kStageRow + 8 * g;
+      const bf16x4 *sd4 = reinterpret_cast<const bf16x4 *>(&sdb);
+      const bf16x4 *p4 = reinterpret_cast<const bf16x4 *>(&pb);
+      *reinterpret_cast<bf16x4 *>(sb) = sd4[0];
+      *reinterpret_cast<bf16x4 *>(sb + 32) = sd4[1];
+      *reinterpret_cast<bf16x4 *>(sb + kHeads * kStageRow) = p4[0];
+      *reinterpret_cast<bf16x4 *>(sb + kHeads * kStageRow + 32) = p4[1];
     }
     // dq^T[dims, head] += C^T[dims, keys] dS^T[keys, head]
-#pragma unroll
-    for (int i = 0; i < 36; ++i) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(ct + tr_base + i * 32));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(ct + tr_base + i * 32 + 16 * kCRow));
-      const i16x4 lohi[2] = {lo, hi};
-      acc[i] = mfma_bf16_16x16x32(*reinterpret_cast<const bf16x8 *>(lohi), dsb, acc[i]);
-    }
-    // s dS and P of the tile's entries, key-major
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = j * kBN + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
-      if (key < k) {
-        const int64_t o = (tc * k + key) * H + head;
-        dsT[o] = (__bf16)(sm_scale * dsv[i]);
-        pT[o] = (__bf16)pv[i];
-      }
-    }
+    const uint32_t trb = lds_addr(ct + tr_base);
+#define DSA_DQ_SIX(I)                                                                 \
+  {                                                                                   \
+    bf16x8 op[6];                                                                     \
+    dq_operands6<I>(trb, op);                                                         \
+    _Pragma("unroll") for (int n = 0; n < 6; ++n) acc[I + n] = mfma_bf16_16x16x32(op[n], dsb, acc[I + n]); \
+  }
+    DSA_DQ_SIX(0) DSA_DQ_SIX(6) DSA_DQ_SIX(12) DSA_DQ_SIX(18) DSA_DQ_SIX(24) DSA_DQ_SIX(30)
+#undef DSA_DQ_SIX
+  }
+  if (ntiles > 0) {
+    __syncthreads();  // the last tile's staging is complete
+    write_out(ntiles - 1);
   }
   float *dqrow = dq + (t * H + head) * 576 + 4 * g;
 #pragma unroll
@@ -736,70 +878,175 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
 }
 
 // Pair gradients of one query: G[pair, d] = sum_h (s dS)[pair, h] q[h, d] +
-// P[pair, h] dO[h, d] (the dO term for d < 512).  Workgroup (query,
-// blockIdx.y) of four waves covers dim tiles 12 y .. 12 y + 11 (16 dims
-// each); wave w owns three of them and holds their B operands (q and dO with
-// the heads along K) for the whole key loop.  KS = H / 32 K steps.
-constexpr int kGTilesPerWave = 3;
-constexpr int kGTilesPerGroup = 4 * kGTilesPerWave;  // 36 tiles of 16 dims: 3 groups
+// P[pair, h] dO[h, d] (the dO term for d < 512), computed transposed,
+// G^T[dims, keys] = q^T (s dS)^T + dO^T P^T: a GEMM over the heads whose
+// A operands (q^T and dO^T, 16 dims x 32 heads per step) are constant for the
+// query and whose B operands (the key-major s dS and P rows) stream through
+// LDS.  One workgroup per query: twelve compute waves, wave w owning the
+// 16-dim tiles 3w .. 3w+2 (tiles 32..35 are the rope dims, which have no dO
+// term), and four loader waves.
+//  * set-up: q[t] and then dO[t] are staged row-major in LDS and read back
+//    with the transposing LDS load, so each compute lane holds its A operands
+//    (dims 16 i + c, heads 32 s + 8 g .. +8) in registers;
+//  * key loop, blocks of 32 keys in three LDS buffers: while the compute
+//    waves work on block j, the loader waves fetch block j + 2 straight into
+//    LDS and wait only until block j + 1 has landed; one barrier a block.  The
+//    compute waves issue only stores, so nothing ever makes them wait for
+//    memory (loads and stores share one completion counter, and a wait for a
+//    load would also wait for every store issued before it);
+//  * each lane ends a 16 x 16 tile with dims 4 g .. 4 g + 3 of one key, a
+//    16-byte run of that key's G row, stored through a buffer bounded to the
+//    query's rows, which drops the stores of keys >= k.  (A streaming cache
+//    hint on these stores measured slower: plain 16-byte stores stream at
+//    4.6 TB/s on MI355X, streaming-hinted ones at 4.4.)
+constexpr int kGWaves = 12;                   // compute waves
+constexpr int kGLoaders = 4;                  // loader waves
+constexpr int kGThreads = (kGWaves + kGLoaders) * 64;
+constexpr int kGNBuf = 3;                     // key blocks in LDS: computed, landed, in flight
+constexpr int kGKeys = 32;                    // keys per LDS block
+constexpr int kGStageRow = kCRow;             // LDS bytes per staged row of q or dO
+
+template <int H>
+struct GShape {
+  static constexpr int kRowSlots = H / 4 + 1;  // 16-byte LDS slots per key: s dS | P | pad
+  static constexpr int kRow = 16 * kRowSlots;  // stride 4 (mod 64) dwords at H = 32 .. 128: conflict-free reads
+  static constexpr int kInsts = (kGKeys * kRowSlots + 63) / 64;  // loader instructions (1 KB each) per block
+  static constexpr int kBuf = kInsts * 1024;
+  static constexpr int kSmem = H * kGStageRow > kGNBuf * kBuf ? H * kGStageRow : kGNBuf * kBuf;
+};
+
+// A operand of a 16x16x32 MFMA from a row-major [K rows][M cols] bf16 matrix
+// in LDS: lane (g, c) gets column m0 + c, rows k0 + 8 g .. + 8.
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t *base, int row_bytes, int k0, int m0, int g, int c) {
+  const uint8_t *p = base + (k0 + 8 * g + (c >> 2)) * row_bytes + (m0 + 4 * (c & 3)) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * row_bytes));
+  const i16x4 lohi[2] = {lo, hi};
+  return *reinterpret_cast<const bf16x8 *>(lohi);
+}
+
+// rows [0, H) of `width` bf16 each, from global (contiguous) into LDS rows of kGStageRow bytes
+template <int H>
+__device__ __forceinline__ void g_stage_rows(uint8_t *lds, const __bf16 *src, int width, int tid) {
+  const int chunks = width / 8;  // 16-byte pieces per row
+  for (int e = tid; e < H * chunks; e += kGThreads) {
+    const int h = e / chunks, ch = e - h * chunks;
+    *reinterpret_cast<i32x4 *>(lds + h * kGStageRow + ch * 16) =
+        *reinterpret_cast<const i32x4 *>(src + (int64_t)h * width + ch * 8);
+  }
+}
+
 template <int KS>
-__global__ __launch_bounds__(256) void mla_bwd_g_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ dout,
-                                                        const __bf16 *__restrict__ dsT, const __bf16 *__restrict__ pT,
-                                                        int k, int64_t t0, float *__restrict__ G) {
+__global__ __launch_bounds__(kGThreads, 1) void mla_bwd_g_kernel(const __bf16 *__restrict__ q,
+                                                                 const __bf16 *__restrict__ dout,
+                                                                 const __bf16 *__restrict__ dsT,
+                                                                 const __bf16 *__restrict__ pT, int k, int64_t t0,
+                                                                 float *__restrict__ G) {
   constexpr int H = 32 * KS;
+  using S = GShape<H>;
+  extern __shared__ __align__(16) uint8_t smem_raw[];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool loader = wave >= kGWaves;  // uniform
+  const int li = wave - kGWaves;        // loader index (uniform)
   const int64_t tc = blockIdx.x, t = t0 + tc;
-  const int ti0 = blockIdx.y * kGTilesPerGroup + kGTilesPerWave * wave;  // uniform
-  // B operands: lane (g, c) holds heads 32 s + 8 g .. +8 of dim 16 (ti0 + j) + c
-  bf16x8 bq[kGTilesPerWave][KS], bo[kGTilesPerWave][KS];
+  const int ti0 = 3 * (loader ? 0 : wave);  // uniform
+  bf16x8 aq[3][KS], ao[3][KS];
+  g_stage_rows<H>(smem_raw, q + t * H * 576, 576, tid);
+  __syncthreads();
 #pragma unroll
-  for (int jt = 0; jt < kGTilesPerWave; ++jt) {
-    const int d = 16 * (ti0 + jt) + c;
+  for (int jt = 0; jt < 3; ++jt)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KS; ++s) aq[jt][s] = tr_operand(smem_raw, kGStageRow, 32 * s, 16 * (ti0 + jt), g, c);
+  __syncthreads();
+  g_stage_rows<H>(smem_raw, dout + t * H * 512, 512, tid);
+  __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t h = 32 * s + 8 * g + e;
-        bq[jt][s][e] = q[(t * H + h) * 576 + d];
-        bo[jt][s][e] = d < 512 ? dout[(t * H + h) * 512 + d] : (__bf16)0.0f;
-      }
-    }
-  }
+  for (int jt = 0; jt < 3; ++jt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      ao[jt][s] = ti0 + jt < 32 ? tr_operand(smem_raw, kGStageRow, 32 * s, 16 * (ti0 + jt), g, c)
+                                : bf16x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // the staging area is free for the key blocks
   const __bf16 *dsq = dsT + tc * k * H;
   const __bf16 *pq = pT + tc * k * H;
-  float *Gq = G + tc * k * 576;
-  for (int kb = 0; kb < k; kb += 16) {
-    // A operands: lane (g, c) holds key kb + c, heads 32 s + 8 g .. +8
-    const int key = kb + c;
-    bf16x8 ads[KS], ap[KS];
+  const int nblk = (k + kGKeys - 1) / kGKeys;
+  // Loader li: instructions li, li + 4, ... of block b into dst.  Instruction
+  // i writes slots [64 i, 64 i + 64); slot s holds key s / kRowSlots, piece
+  // s % kRowSlots (the pad piece and the slots past the block's keys re-read a
+  // valid piece); entries past k re-read entry k - 1, whose results are never
+  // stored.
+  auto issue_block = [&](int b, uint8_t *dst) {
+    int l = lane;
+    asm volatile("" : "+v"(l));  // recompute the lane roles per block instead of holding addresses
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (key < k) {
-        ads[s] = *reinterpret_cast<const bf16x8 *>(dsq + (int64_t)key * H + 32 * s + 8 * g);
-        ap[s] = *reinterpret_cast<const bf16x8 *>(pq + (int64_t)key * H + 32 * s + 8 * g);
+    for (int n = 0; n < (S::kInsts + kGLoaders - 1) / kGLoaders; ++n) {
+      const int i = li + kGLoaders * n;  // uniform
+      if (i >= S::kInsts) break;
+      const int slot = i * 64 + l;
+      const int kk = slot / S::kRowSlots;
+      const int part = min(slot - kk * S::kRowSlots, H / 4 - 1);
+      const int key = min(b * kGKeys + min(kk, kGKeys - 1), k - 1);
+      const __bf16 *src = part < H / 8 ? dsq + (int64_t)key * H + part * 8 : pq + (int64_t)key * H + (part - H / 8) * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(dst + i * 1024), 16, 0, 0);
+    }
+  };
+  // wait until only this loader's newest block may still be in flight
+  auto wait_all_but_newest = [&]() {
+    constexpr int base = S::kInsts / kGLoaders, rem = S::kInsts % kGLoaders;
+    if (rem != 0 && li < rem)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(base + 1));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(base));
+  };
+  if (loader) {
+    if (nblk > 0) issue_block(0, smem_raw);
+    if (nblk > 1) {
+      issue_block(1, smem_raw + S::kBuf);
+      wait_all_but_newest();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
+  __syncthreads();
+  // G rows of this query as a bounded buffer: stores of keys >= k are dropped
+  const __amdgpu_buffer_rsrc_t gr =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(G + tc * k * 576), 0, k * 576 * 4, (int)kRsrcWord3);
+  const int goff = c * 576 * 4 + (16 * ti0 + 4 * g) * 4;  // bytes: key c of a tile, this lane's dims
+  for (int j = 0; j < nblk; ++j) {
+    if (loader) {
+      // block j + 2 goes to the buffer last read before the previous barrier
+      if (j + 2 < nblk) {
+        issue_block(j + 2, smem_raw + ((j + 2) % kGNBuf) * S::kBuf);
+        wait_all_but_newest();
       } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    } else {
+#pragma unroll 1
+      for (int kt = 0; kt < kGKeys / 16; ++kt) {
+        const uint8_t *brow = smem_raw + (j % kGNBuf) * S::kBuf + (16 * kt + c) * S::kRow + 16 * g;
+        f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ads[s][e] = ap[s][e] = (__bf16)0.0f;
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 64 * s);
+#pragma unroll
+          for (int jt = 0; jt < 3; ++jt) acc[jt] = mfma_bf16_16x16x32(aq[jt][s], b, acc[jt]);
+        }
+        // the dO term (zero operands on the rope tiles)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 2 * H + 64 * s);
+#pragma unroll
+          for (int jt = 0; jt < 3; ++jt) acc[jt] = mfma_bf16_16x16x32(ao[jt][s], b, acc[jt]);
+        }
+        const int off = (j * kGKeys + 16 * kt) * 576 * 4 + goff;
+#pragma unroll
+        for (int jt = 0; jt < 3; ++jt)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[jt]), gr, off + 64 * jt, 0, 0);
       }
     }
-#pragma unroll
-    for (int jt = 0; jt < kGTilesPerWave; ++jt) {
-      const int ti = ti0 + jt;
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) o = mfma_bf16_16x16x32(ads[s], bq[jt][s], o);
-      if (ti < 32) {  // value dims: uniform per wave and tile
-#pragma unroll
-        for (int s = 0; s < KS; ++s) o = mfma_bf16_16x16x32(ap[s], bo[jt][s], o);
-      }
-      // rows 4 g + r (keys), column c (dim)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = kb + 4 * g + r;
-        if (kr < k) Gq[(int64_t)kr * 576 + 16 * ti + c] = o[r];
-      }
-    }
+    __syncthreads();
   }
 }
 
@@ -846,14 +1093,30 @@ static hipError_t launch_ds_nw(const void *q, const void *kv, const int32_t *idx
                                float *dq, void *dsT, void *pT, hipStream_t s) {
   static bool attr_done = false;  // per process: the attribute holds for every device
   if (!attr_done) {
-    hipError_t e =
-        hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBwd);
+    hipError_t e = hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       smem_bwd_bytes<NW>());
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(mla_bwd_ds_kernel<NW>, dim3((uint32_t)Tc, H / (16 * NW)), dim3(NW * 64), kSmemBwd, s,
+  hipLaunchKernelGGL(mla_bwd_ds_kernel<NW>, dim3((uint32_t)Tc, H / (16 * NW)), dim3(NW * 64), smem_bwd_bytes<NW>(), s,
                      (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D, N, H, k, sm_scale, t0,
                      dq, (__bf16 *)dsT, (__bf16 *)pT);
+  return hipGetLastError();
+}
+
+template <int KS>
+static hipError_t launch_g_ks(const void *q, const void *dout, const void *dsT, const void *pT, int32_t k, int64_t t0,
+                              int32_t Tc, float *G, hipStream_t s) {
+  constexpr int bytes = GShape<32 * KS>::kSmem;
+  static bool attr_done = false;  // per process: the attribute holds for every device
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void *)mla_bwd_g_kernel<KS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       bytes);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(mla_bwd_g_kernel<KS>, dim3((uint32_t)Tc), dim3(kGThreads), bytes, s, (const __bf16 *)q,
+                     (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
   return hipGetLastError();
 }
 
@@ -868,25 +1131,16 @@ hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *id
   if (e != hipSuccess) return e;
   switch (H / 32) {
     case 1:
-      hipLaunchKernelGGL(mla_bwd_g_kernel<1>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
-                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
-      break;
+      return launch_g_ks<1>(q, dout, dsT, pT, k, t0, Tc, G, s);
     case 2:
-      hipLaunchKernelGGL(mla_bwd_g_kernel<2>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
-                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
-      break;
+      return launch_g_ks<2>(q, dout, dsT, pT, k, t0, Tc, G, s);
     case 3:
-      hipLaunchKernelGGL(mla_bwd_g_kernel<3>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
-                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
-      break;
+      return launch_g_ks<3>(q, dout, dsT, pT, k, t0, Tc, G, s);
     case 4:
-      hipLaunchKernelGGL(mla_bwd_g_kernel<4>, dim3((uint32_t)Tc, 36 / kGTilesPerGroup), dim3(256), 0, s, (const __bf16 *)q,
-                         (const __bf16 *)dout, (const __bf16 *)dsT, (const __bf16 *)pT, k, t0, G);
-      break;
+      return launch_g_ks<4>(q, dout, dsT, pT, k, t0, Tc, G, s);
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_sparse_mla_f32(const float *q, const float *kv, const int32_t *idx, int64_t N, int32_t T,

@@ -91,6 +91,20 @@ __global__ __launch_bounds__(256) void hbm_read_stream(const f32x4 *__restrict__
   if (s == 1234.5f) sink[blockIdx.x] = s;
 }
 
+// Streaming write of n16 16-byte vectors (grid-stride, one store per
+// iteration per lane); `nt` sets the streaming cache policy on the stores.
+template <bool NT>
+__global__ __launch_bounds__(256) void hbm_write_stream(f32x4 *__restrict__ x, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const f32x4 v = {1.f, 2.f, 3.f, 4.f};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+    if (NT)
+      __builtin_nontemporal_store(v, x + i);
+    else
+      x[i] = v;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,6 +126,15 @@ int dsa_peak_bf16_mfma(int blocks, int iters, float *sink, hipStream_t s) {
 // Read `bytes` (a multiple of 16, 16-byte aligned) of device memory at x.
 int dsa_peak_hbm_read(const void *x, int64_t bytes, int blocks, float *sink, hipStream_t s) {
   hipLaunchKernelGGL(hbm_read_stream, dim3(blocks), dim3(256), 0, s, (const f32x4 *)x, bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// Write `bytes` (a multiple of 16) to x with 16-byte stores; nt != 0 marks them streaming.
+int dsa_peak_hbm_write(void *x, int64_t bytes, int blocks, int nt, hipStream_t s) {
+  if (nt)
+    hipLaunchKernelGGL(hbm_write_stream<true>, dim3(blocks), dim3(256), 0, s, (f32x4 *)x, bytes / 16);
+  else
+    hipLaunchKernelGGL(hbm_write_stream<false>, dim3(blocks), dim3(256), 0, s, (f32x4 *)x, bytes / 16);
   return (int)hipGetLastError();
 }
 }
