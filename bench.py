@@ -38,7 +38,6 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "DSA prefill tokens/s at L=128K + decode tokens/s; % FP8 MFMA / HBM peak"
 
 
@@ -342,7 +341,8 @@ def run_backward(torch, dsa, cfg, t, dev, steps):
     # the four products of the attention backward (dP, dq, dkv's logit and value parts):
     # 2 H (512 + 576 + 576 + 512) FLOP per selected pair; the logits' recompute is not counted
     mla_flop = 2 * H * (512 + 576 + 576 + 512) * pairs
-    # the indexer backward: the dot products again (FP8 MFMA), then dq and each pair's dk share (fp32)
+    # the indexer backward: the dot products again (FP8 MFMA), then dq and each pair's dk share (bf16 MFMA,
+    # the fp32 coefficient as two bf16 terms: the hardware does twice this count for those two products)
     idx_flop = 3 * 2 * cfg.H_I * cfg.D_I * pairs
     res = {
         "workload": cfg.name, "L": L, "H": H, "k": k, "steps": steps,
@@ -351,7 +351,7 @@ def run_backward(torch, dsa, cfg, t, dev, steps):
         "roofline": {
             "sparse_mla_bwd": _rl("mfma", mla_flop / (ms["sparse_mla_bwd"] / 1e3) / 1e12, PEAK_BF16_TFLOPS,
                                   "TFLOP/s"),
-            "indexer_bwd": _rl("alu", idx_flop / (ms["indexer_bwd"] / 1e3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "indexer_bwd": _rl("mfma", idx_flop / (ms["indexer_bwd"] / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
         },
         "work": {"selected_pairs": pairs, "sparse_mla_bwd_flop": mla_flop, "indexer_bwd_flop": idx_flop},
         "data": "synthetic upstream gradient dout ~ N(0, 0.01^2) bf16; dkl = 1/L (mean of the per-token loss)",

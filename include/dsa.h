@@ -132,7 +132,9 @@ size_t dsa_topk_workspace_bytes(int32_t T, int64_t ld_scores, int32_t k);
  *   o[t,h] = sum_i softmax_i(sm_scale * q[t,h].kv[idx[t,i]]) kv[idx[t,i], :512]
  * A query with no valid entry gets o = 0 and lse = -inf.
  * BF16: bf16 MFMA, fp32 softmax and accumulation, output rounded (RNE) to bf16.
- * Limits: BF16 needs H a multiple of 16; F32 needs H <= 128; k <= 2048.
+ * Limits: BF16 needs H a multiple of 8 (the kernel works in tiles of 16
+ * heads; a last, partial tile is padded with zero queries whose outputs are
+ * never written); F32 needs H <= 128; k <= 2048.
  * workspace (optional) lets the kernel split long selections across more
  * workgroups when T is small; size it with dsa_sparse_mla_workspace_bytes().
  * Each split's output is then held in bf16, normalised by its own softmax
@@ -340,7 +342,7 @@ dsa_status dsa_prefill_select(const dsa_prefill_args *a, void *workspace, size_t
  *   max_ctx: host-side upper bound of ctx_len (sizes grids and workspace)
  *   idx_out [B,k] int32 (optional, logical positions ascending, -1 padded)
  *   out [B,H,512] BF16, lse [B,H] fp32 (may be NULL)
- * Limits: D_I = 128, H_I = 64, H a multiple of 16, 1 <= ctx_len <= max_ctx.
+ * Limits: D_I = 128, H_I = 64, H a multiple of 8, 1 <= ctx_len <= max_ctx.
  */
 typedef struct {
     int32_t B, H_I, D_I, H, k;

@@ -31,7 +31,8 @@ hipError_t launch_positions(int32_t *q_pos, int32_t *n_valid, int32_t L, hipStre
 // heads per workgroup of the bf16 kernel (16 per wave)
 static int mla_heads_per_wg(int H) { return H % 128 == 0 ? 128 : H % 64 == 0 ? 64 : H % 32 == 0 ? 32 : 16; }
 static int mla_splits(int64_t T, int H, int k) {
-  const int64_t base = T * (H / mla_heads_per_wg(H));
+  const int hpw = mla_heads_per_wg(H);
+  const int64_t base = T * ((H + hpw - 1) / hpw);
   const int ntiles = (k + 31) / 32;
   if (base <= 0 || base >= 256) return 1;
   int s = (int)((256 + base - 1) / base);
@@ -135,7 +136,7 @@ size_t dsa_topk_workspace_bytes(int32_t T, int64_t ld_scores, int32_t k) {
 }
 
 size_t dsa_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t k) {
-  if (T <= 0 || H <= 0 || k <= 0 || H % 16) return 0;
+  if (T <= 0 || H <= 0 || k <= 0 || H % 8) return 0;
   return mla_ws_bytes(T, H, k);
 }
 
@@ -151,7 +152,7 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
   if (T == 0) return DSA_OK;
   REQUIRE(q && kv && idx && out, DSA_ERR_INVALID_ARG, "null pointer");
   if (dt == DSA_BF16) {
-    REQUIRE(H % 16 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 16 (got %d)", H);
+    REQUIRE(H % 8 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 8 (got %d)", H);
     const size_t need = mla_ws_bytes(T, H, k);
     int splits = 1;
     void *po = nullptr;
@@ -376,7 +377,7 @@ static dsa_status check_prefill(const dsa_prefill_args *a, bool attention) {
   }
   if (!attention) return DSA_OK;
   if (a->attn_dt == DSA_BF16)
-    REQUIRE(a->H % 16 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 16");
+    REQUIRE(a->H % 8 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 8");
   else
     REQUIRE(a->attn_dt == DSA_F32, DSA_ERR_UNSUPPORTED, "attention dtype must be BF16 or F32");
   return DSA_OK;
@@ -453,7 +454,7 @@ static dsa_status check_decode(const dsa_decode_args *a, bool attention) {
           "n_pool_rows must be a positive multiple of 64");
   REQUIRE(a->H_I == 64 && a->D_I == 128, DSA_ERR_UNSUPPORTED, "decode indexer needs H_I = 64, D_I = 128");
   if (attention) {
-    REQUIRE(a->H > 0 && a->H % 16 == 0, DSA_ERR_UNSUPPORTED, "decode attention needs H a multiple of 16");
+    REQUIRE(a->H > 0 && a->H % 8 == 0, DSA_ERR_UNSUPPORTED, "decode attention needs H a multiple of 8");
     REQUIRE(a->sm_scale == a->sm_scale && a->sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
   }
   if (a->B == 0) return DSA_OK;
@@ -470,7 +471,7 @@ size_t dsa_decode_workspace_bytes(const dsa_decode_args *a) {
   size_t n = align_up((size_t)a->B * decode_ld(a) * 4, 256);
   if (!a->idx_out) n += align_up((size_t)a->B * a->k * 4, 256);
   // one region, used first by a split top-k and then by the split attention
-  const size_t mla = (a->H > 0 && a->H % 16 == 0) ? mla_ws_bytes(a->B, a->H, a->k) : 0;
+  const size_t mla = (a->H > 0 && a->H % 8 == 0) ? mla_ws_bytes(a->B, a->H, a->k) : 0;
   n += std::max(mla, topk_workspace_bytes(a->B, a->max_ctx, a->k));
   return n;
 }
@@ -500,7 +501,7 @@ dsa_status dsa_sparse_mla_paged_fwd(const void *q, const void *kv_pool, int64_t 
   REQUIRE(max_blocks >= 1, DSA_ERR_INVALID_ARG, "max_blocks must be >= 1");
   REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
   REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
-  REQUIRE(H > 0 && H % 16 == 0, DSA_ERR_UNSUPPORTED, "paged sparse MLA needs H a multiple of 16");
+  REQUIRE(H > 0 && H % 8 == 0, DSA_ERR_UNSUPPORTED, "paged sparse MLA needs H a multiple of 8");
   REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
   if (T == 0) return DSA_OK;
   REQUIRE(q && kv_pool && block_table && idx && out, DSA_ERR_INVALID_ARG, "null pointer");

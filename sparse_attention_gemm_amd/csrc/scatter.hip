@@ -76,10 +76,11 @@ __global__ __launch_bounds__(256) void scatter_fill_kernel(const int32_t *__rest
 constexpr int kSortCap = 4096;  // pairs of one row sorted in LDS
 
 // Y[r, :] += sum over r's pairs p, in increasing p, of X[p, :].  One
-// workgroup per row; W <= 768 (up to three values per thread).
-__global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t *__restrict__ start,
-                                                          const int32_t *__restrict__ list, const float *__restrict__ X,
-                                                          int W, float *__restrict__ Y) {
+// workgroup of BS threads per row, NCOL columns per thread (W <= BS NCOL).
+template <int BS, int NCOL>
+__global__ __launch_bounds__(BS) void scatter_add_kernel(const int32_t *__restrict__ start,
+                                                         const int32_t *__restrict__ list, const float *__restrict__ X,
+                                                         int W, float *__restrict__ Y) {
   __shared__ int32_t keys[kSortCap];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -89,12 +90,12 @@ __global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t *__restr
   if (sorted) {
     int m = 1;
     while (m < n) m <<= 1;
-    for (int i = tid; i < m; i += 256) keys[i] = i < n ? list[b + i] : 0x7FFFFFFF;
+    for (int i = tid; i < m; i += BS) keys[i] = i < n ? list[b + i] : 0x7FFFFFFF;
     __syncthreads();
     // bitonic sort, ascending
     for (int size = 2; size <= m; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < (m >> 1); i += 256) {
+        for (int i = tid; i < (m >> 1); i += BS) {
           const int lo = 2 * i - (i & (stride - 1));
           const int hi = lo + stride;
           const bool up = (lo & size) == 0;
@@ -108,28 +109,30 @@ __global__ __launch_bounds__(256) void scatter_add_kernel(const int32_t *__restr
       }
     }
   }
-  float acc[3] = {0.f, 0.f, 0.f};
+  float acc[NCOL];
+#pragma unroll
+  for (int j = 0; j < NCOL; ++j) acc[j] = 0.0f;
   constexpr int kAhead = 8;  // pairs whose loads are in flight together; the adds stay in order
   for (int i0 = 0; i0 < n; i0 += kAhead) {
-    float v[kAhead][3];
+    float v[kAhead][NCOL];
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
       const int i = i0 + u;
       const int32_t p = i < n ? (sorted ? keys[i] : list[b + i]) : -1;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int d = tid + 256 * j;
+      for (int j = 0; j < NCOL; ++j) {
+        const int d = tid + BS * j;
         v[u][j] = (p >= 0 && d < W) ? X[(int64_t)p * W + d] : 0.0f;
       }
     }
 #pragma unroll
     for (int u = 0; u < kAhead; ++u)
 #pragma unroll
-      for (int j = 0; j < 3; ++j) acc[j] += v[u][j];
+      for (int j = 0; j < NCOL; ++j) acc[j] += v[u][j];
   }
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int d = tid + 256 * j;
+  for (int j = 0; j < NCOL; ++j) {
+    const int d = tid + BS * j;
     if (d < W) Y[r * W + d] += acc[j];
   }
 }
@@ -165,7 +168,12 @@ hipError_t launch_scatter_build(const int32_t *idx, int64_t npairs, int64_t N, i
 hipError_t launch_scatter_add(const int32_t *start, const int32_t *list, int64_t N, const float *X, int32_t W, float *Y,
                               hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_add_kernel, dim3((uint32_t)N), dim3(256), 0, s, start, list, X, W, Y);
+  if (W <= 128)  // one wave per row, two columns per lane
+    hipLaunchKernelGGL((scatter_add_kernel<64, 2>), dim3((uint32_t)N), dim3(64), 0, s, start, list, X, W, Y);
+  else if (W <= 768)
+    hipLaunchKernelGGL((scatter_add_kernel<256, 3>), dim3((uint32_t)N), dim3(256), 0, s, start, list, X, W, Y);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -302,7 +302,7 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
   if (g == 0) cx.lbuf[wave * 16 + c] = l_tot;
   const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
   const int head_own = hw0 + wave * 16 + c;
-  if (g == 0) {
+  if (g == 0 && head_own < H) {  // heads past H pad the last head tile
     if (splits == 1) {
       if (lse) lse[t * H + head_own] = l_tot > 0.0f ? (mr + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     } else {
@@ -316,6 +316,7 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
   for (int n = 0; n < NW; ++n) {
     const int head = hw0 + n * 16 + c;
     const float lh = cx.lbuf[n * 16 + c];
+    if (head >= H) continue;  // padding of the last head tile
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int dv = (wave * MT + i) * 16 + 4 * g;
@@ -351,7 +352,7 @@ __device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, bf16x8 (&qr)[18], const
   int *rows = reinterpret_cast<int *>(cx.lbuf + 128);   // <= 2048 physical rows
   cx.rows = rows;
   cx.flag = rows + 2048;
-  const int n_hg = H / (16 * NW);
+  const int n_hg = (H + 16 * NW - 1) / (16 * NW);  // the last group is padded when 16 NW does not divide H
   MlaItem it;
   it.sp = (int)(wid % splits);
   const int64_t rest = wid / splits;
@@ -367,10 +368,17 @@ __device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, bf16x8 (&qr)[18], const
   const int per = (ntiles + splits - 1) / splits;
   cx.tb = it.sp * per;
   cx.te = min(ntiles, cx.tb + per);
-  // Q^T first: its loads are in flight while the rows are resolved
-  const __bf16 *qrow = q + (it.t * H + it.hw0 + 16 * cx.wave + cx.c) * 576 + cx.g * 8;
+  // Q^T first: its loads are in flight while the rows are resolved.  Heads
+  // past H (padding of the last head tile) get a zero query: finite logits,
+  // and their outputs are never written.
+  const int qh = it.hw0 + 16 * cx.wave + cx.c;
+  const bool qvalid = qh < H;
+  const __bf16 *qrow = q + (it.t * H + (qvalid ? qh : 0)) * 576 + cx.g * 8;
 #pragma unroll
-  for (int s = 0; s < 18; ++s) qr[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
+  for (int s = 0; s < 18; ++s) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(qrow + s * 32);
+    qr[s] = qvalid ? v : bf16x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  }
   const int32_t *irow = idx + it.t * k;
   // physical rows of this workgroup's entries [tb*32, te*32)
   for (int e = tid; e < (cx.te - cx.tb) * kBN; e += NW * 64)
@@ -557,7 +565,7 @@ hipError_t launch_bf16_variant(const void *q, const void *kv, const int32_t *idx
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  const int64_t items = (int64_t)T * (H / (16 * NW)) * splits;
+  const int64_t items = (int64_t)T * ((H + 16 * NW - 1) / (16 * NW)) * splits;
   hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW, late>), dim3((uint32_t)items), dim3(NW * 64), kSmemMla, s,
                      (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
                      (__bf16 *)out, lse, splits, part_o, part_ml);

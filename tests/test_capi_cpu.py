@@ -105,7 +105,7 @@ def test_sparse_mla_validation(dsa):
     f = L.dsa_sparse_mla_fwd
     base = [FAKE, FAKE, dsa.DSA_BF16, FAKE, 64, 128, 1000, 2048, 0.07, FAKE, FAKE, None, 0, None]
     b = list(base)
-    b[5] = 24  # H not a multiple of 16 for bf16
+    b[5] = 20  # H not a multiple of 8 for bf16
     assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
     b = list(base)
     b[7] = 4096
@@ -210,7 +210,7 @@ def test_prefill_validation(dsa):
     a.q_scale = None
     assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     a.q_scale = FAKE
-    a.H = 8
+    a.H = 12  # not a multiple of 8
     assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
     a.H = 128
     a.idx_dt = dsa.DSA_F32
@@ -236,7 +236,7 @@ def test_decode_validation(dsa):
     a.n_pool_rows = 6401
     assert L.dsa_decode(ctypes.byref(a), FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG
     a.n_pool_rows = 6400
-    a.H = 120
+    a.H = 124  # not a multiple of 8
     assert L.dsa_decode(ctypes.byref(a), FAKE, need, None) == dsa.DSA_ERR_UNSUPPORTED
     a.H = 128
     a.ctx_len = None

@@ -229,7 +229,9 @@ def _mla_gpu(dsa, q, kv, idx, scale, dtype, use_ws=False):
 
 
 @pytest.mark.parametrize("H,k,use_ws,qstd", [(128, 2048, False, 1.0), (128, 2048, True, 40.0), (16, 256, False, 1.0),
-                                             (64, 100, True, 40.0), (32, 48, False, 1.0)])
+                                             (64, 100, True, 40.0), (32, 48, False, 1.0),
+                                             # H a multiple of 8 but not of 16: a padded last head tile
+                                             (8, 256, False, 1.0), (24, 2048, True, 40.0), (40, 100, False, 1.0)])
 def test_sparse_mla_bf16(dsa, ora, H, k, use_ws, qstd):
     N, T = 5000, 6
     _say(f"sparse mla bf16 H={H} k={k} ws={use_ws} qstd={qstd}")
@@ -444,11 +446,12 @@ def _run_decode(dsa, cfg, ctx, bt, nb, pools, qside, with_idx=True):
     return out, lse, idx
 
 
-@pytest.mark.parametrize("B,lo,hi,k,shuffled", [(5, 100, 3000, 256, True), (4, 2000, 2100, 2048, False),
-                                                (3, 1, 70, 64, True), (6, 4096, 9000, 2048, True)])
-def test_decode_paged(dsa, ora, B, lo, hi, k, shuffled):
-    cfg = synth.DecodeConfig("t", B, lo, hi, 64, 128, 128, k, 9, shuffled)
-    _say(f"decode B={B} ctx=[{lo},{hi}] k={k} shuffled={shuffled}")
+@pytest.mark.parametrize("B,lo,hi,k,shuffled,H", [(5, 100, 3000, 256, True, 128), (4, 2000, 2100, 2048, False, 128),
+                                                  (3, 1, 70, 64, True, 128), (6, 4096, 9000, 2048, True, 128),
+                                                  (4, 3000, 5000, 2048, True, 24)])
+def test_decode_paged(dsa, ora, B, lo, hi, k, shuffled, H):
+    cfg = synth.DecodeConfig("t", B, lo, hi, 64, 128, H, k, 9, shuffled)
+    _say(f"decode B={B} ctx=[{lo},{hi}] k={k} shuffled={shuffled} H={H}")
     ctx, bt, nb, pools, qside = _decode_case(cfg)
     out, lse, idx = _run_decode(dsa, cfg, ctx, bt, nb, pools, qside)
     gidx = idx.cpu().numpy()
