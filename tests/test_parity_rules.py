@@ -1,6 +1,6 @@
 """The comparison rules of tests/parity.py, checked on the CPU.
 
-Each rule is exercised on values whose verdict is known: a result inside the
+Each rule is exercised on values whose outcome is known: a result inside the
 stated bound passes, a planted error just outside it fails.  The planted
 errors sit in the values handed to the checker, never in the GPU path.
 """
