@@ -70,6 +70,17 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 
+// s_waitcnt immediate: at most n vector-memory operations outstanding
+// (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete,
+// then the hardware barrier (a compiler barrier for memory too).  Unlike
+// __syncthreads() it carries no release fence on global memory, which would
+// also wait for every load and store in flight; a kernel that shares
+// direct-to-LDS loads across waves waits for its own explicitly before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Lane index within the wave and the number of lanes below it in `mask`.
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ int lanes_below(uint64_t mask) {

@@ -314,10 +314,17 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
   uint32_t klo = 0xFFFFFFFFu, khi = 0u;  // bounds of the keys this lane appended since the last cut
 
   load_tile_async(sm.keys[0], sm.ksc[0], k8, ks, L, 0, wave, lane);
+  bool appended = false;  // the previous tile's two append stores follow its prefetch
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed in LDS
-    __syncthreads();                // ... and every wave's; tile it-1's buffer is free
+    // this wave's loads of tile `it` have landed in LDS; the previous tile's
+    // appends, issued after them, may still be in flight (loads and stores
+    // complete in issue order)
+    if (appended)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();  // ... and every wave's; tile it-1's buffer is free
     if (it > 0) {
       const int par = (it - 1) & 1;
       const uint32_t any = __builtin_amdgcn_readfirstlane(sm.full[par][0] | sm.full[par][1] | sm.full[par][2] |
@@ -328,6 +335,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
       }
     }
     const bool need = active && it * kTile <= t;
+    appended = false;
     const float v = score_and_prefetch(sm.keys[buf ^ 1], sm.ksc[buf ^ 1], sm.keys[buf], sm.ksc[buf], it + 1 < ntiles,
                                        need, Q, k8, ks, L, it + 1, wave, lane);
     if (need) {
@@ -344,6 +352,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void prefill_indexer_topk_kernel(
         bp[dst] = (uint32_t)s;
       }
       nbuf += __popcll(mask);
+      appended = mask != 0;  // uniform
     }
     if (lane == 0) sm.full[it & 1][wave] = nbuf > kCap - kTile ? 1u : 0u;
   }

@@ -165,10 +165,6 @@ __device__ __forceinline__ void for_each_tile(const MlaCtx &cx, Body &&body) {
   __syncthreads();
 }
 
-// s_waitcnt immediate: at most n vector-memory operations outstanding
-// (expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 // Wait until only the newest tile's gathers may still be in flight (every
 // tile costs a wave the same number of gather instructions).
 template <int NW>
@@ -669,13 +665,6 @@ __device__ __forceinline__ void tile_dot_pair(const uint8_t *__restrict__ ct, co
     dp[4 + r] = d1[r];
   }
 }
-
-// Workgroup barrier for LDS traffic only: this wave's LDS operations complete,
-// then the hardware barrier (a compiler barrier for memory too).  Unlike
-// __syncthreads() it carries no release fence on global memory, which would
-// also wait for every gather and store in flight; gathers are waited for
-// explicitly before it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // LDS byte address of a shared-memory pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
