@@ -885,7 +885,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
 //  * set-up: q[t] and then dO[t] are staged row-major in LDS and read back
 //    with the transposing LDS load, so each compute lane holds its A operands
 //    (dims 16 i + c, heads 32 s + 8 g .. +8) in registers;
-//  * key loop, blocks of 32 keys in three LDS buffers: while the compute
+//  * key loop, blocks of 64 keys in three LDS buffers: while the compute
 //    waves work on block j, the loader waves fetch block j + 2 straight into
 //    LDS and wait only until block j + 1 has landed; one barrier a block.  The
 //    compute waves issue only stores, so nothing ever makes them wait for
@@ -900,7 +900,7 @@ constexpr int kGWaves = 12;                   // compute waves
 constexpr int kGLoaders = 4;                  // loader waves
 constexpr int kGThreads = (kGWaves + kGLoaders) * 64;
 constexpr int kGNBuf = 3;                     // key blocks in LDS: computed, landed, in flight
-constexpr int kGKeys = 32;                    // keys per LDS block
+constexpr int kGKeys = 64;                    // keys per LDS block (64 measured 5% faster than 32)
 constexpr int kGStageRow = kCRow;             // LDS bytes per staged row of q or dO
 
 template <int H>
