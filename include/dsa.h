@@ -90,8 +90,12 @@ dsa_status dsa_quantize_e4m3_per_token(const float *x, int64_t rows, int32_t col
  *   w       [T, H_I] fp32 head weights
  *   q_pos   [T] int32: query t may see keys s in [0, q_pos[t]]
  *   scores  [T, ld_scores] fp32 out; s > q_pos[t] (s < S) is written -inf.
- * E4M3: products are exact, sums are fp32 (FP8 MFMA); scales must be > 0.
- * Limits: E4M3 needs D_I = 128 and H_I a multiple of 32 (<= 64);
+ * E4M3: products are exact; scales must be > 0.  H_I 32 or 64 with
+ *   D_I = 128 runs on the FP8 MFMA, whose fp32 result comes from a coarser
+ *   internal sum of the 128 products (measured on gfx950: within 2^-12 of the
+ *   sum of their magnitudes); every other E4M3 shape sums the exact products
+ *   with IEEE fp32 fused multiply-adds.
+ * Limits: E4M3 needs D_I in {64, 128} and H_I <= 64;
  *         F32 needs D_I <= 128 and H_I <= 64.
  */
 dsa_status dsa_indexer_scores(const void *q, const float *q_scale, const void *k,
@@ -291,9 +295,11 @@ dsa_status dsa_masked_mha_prefill(const void *q, const void *kv, const void *w_u
  * streaming top-k held on chip, so the L x L score matrix is never written;
  * then sparse MLA over the selected rows.
  *   idx_dt E4M3: q_idx [L,H_I,D_I] + q_scale [L], k_idx [L,D_I] + k_scale [L]
- *          (D_I = 128, H_I = 64);
+ *          (D_I in {64, 128}, H_I <= 64).  H_I = 64 with D_I = 128 is the
+ *          fused streaming path; any other E4M3 shape runs like F32;
  *   idx_dt F32 : same shapes in fp32, scales NULL; runs the three unfused
- *          calls with the L x L scores in the workspace (small L only).
+ *          calls with the L x L scores in the workspace (small L only:
+ *          L <= 16384).
  *   w [L,H_I] fp32;  q [L,H,576], kv [L,576] in attn_dt (BF16 or F32);
  *   idx [L,k] int32 out (selected positions, ascending, -1 padded);
  *   out [L,H,512] in attn_dt;  lse [L,H] fp32 (may be NULL).
@@ -324,7 +330,8 @@ dsa_status dsa_prefill(const dsa_prefill_args *a, void *workspace, size_t worksp
  * this call followed by dsa_sparse_mla_fwd on a->idx with no workspace.
  * Both need dsa_prefill_workspace_bytes(a) of workspace: for E4M3 the
  * streaming top-k keeps a 4096-entry candidate buffer per query there
- * (32 KiB per query: 4 GiB at L = 131072); for F32, the L x L scores. */
+ * (32 KiB per query: 4 GiB at L = 131072); for F32 and the other E4M3
+ * shapes, the L x L scores. */
 dsa_status dsa_prefill_select(const dsa_prefill_args *a, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
 

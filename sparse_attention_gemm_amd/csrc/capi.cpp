@@ -97,10 +97,10 @@ dsa_status dsa_indexer_scores(const void *q, const float *q_scale, const void *k
   REQUIRE(q && k && w && q_pos && scores, DSA_ERR_INVALID_ARG, "null pointer");
   if (dt == DSA_E4M3) {
     REQUIRE(q_scale && k_scale, DSA_ERR_INVALID_ARG, "E4M3 needs q_scale and k_scale");
-    REQUIRE(D_I == 128 && (H_I == 32 || H_I == 64), DSA_ERR_UNSUPPORTED,
-            "E4M3 indexer needs D_I = 128 and H_I in {32, 64} (got %d, %d)", D_I, H_I);
+    REQUIRE((D_I == 64 || D_I == 128) && H_I <= 64, DSA_ERR_UNSUPPORTED,
+            "E4M3 indexer needs D_I in {64, 128} and H_I <= 64 (got %d, %d)", D_I, H_I);
     return hip_check(launch_indexer_scores_fp8((const uint8_t *)q, q_scale, (const uint8_t *)k, k_scale, w,
-                                               q_pos, T, S, H_I, scores, ld_scores, stream),
+                                               q_pos, T, S, H_I, D_I, scores, ld_scores, stream),
                      "indexer launch");
   }
   if (dt == DSA_F32) {
@@ -354,6 +354,13 @@ dsa_status dsa_masked_mha_prefill(const void *q, const void *kv, const void *w_u
                    "masked mha launch");
 }
 
+// The fused indexer + streaming top-k covers the full-size E4M3 indexer (64
+// heads of 128 dims); every other indexer shape scores the L x L matrix into
+// the workspace and selects rows from it.
+static bool prefill_fused(const dsa_prefill_args *a) {
+  return a->idx_dt == DSA_E4M3 && a->H_I == 64 && a->D_I == 128;
+}
+
 static dsa_status check_prefill(const dsa_prefill_args *a, bool attention) {
   REQUIRE(a, DSA_ERR_INVALID_ARG, "null args");
   REQUIRE(a->L >= 1, DSA_ERR_INVALID_ARG, "L must be >= 1");
@@ -367,14 +374,17 @@ static dsa_status check_prefill(const dsa_prefill_args *a, bool attention) {
   }
   if (a->idx_dt == DSA_E4M3) {
     REQUIRE(a->q_scale && a->k_scale, DSA_ERR_INVALID_ARG, "E4M3 needs q_scale and k_scale");
-    REQUIRE(a->H_I == 64 && a->D_I == 128, DSA_ERR_UNSUPPORTED, "fused E4M3 prefill needs H_I = 64, D_I = 128");
+    REQUIRE((a->D_I == 64 || a->D_I == 128) && a->H_I <= 64, DSA_ERR_UNSUPPORTED,
+            "E4M3 prefill needs D_I in {64, 128} and H_I <= 64 (got %d, %d)", a->D_I, a->H_I);
   } else if (a->idx_dt == DSA_F32) {
     REQUIRE(a->D_I <= 128 && a->H_I <= 64, DSA_ERR_UNSUPPORTED, "F32 indexer needs D_I <= 128, H_I <= 64");
-    REQUIRE((int64_t)a->L * a->L <= (int64_t)1 << 28, DSA_ERR_UNSUPPORTED,
-            "the F32 prefill keeps the L x L scores in the workspace; L must be <= 16384");
   } else {
     return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be E4M3 or F32");
   }
+  if (!prefill_fused(a))
+    REQUIRE((int64_t)a->L * a->L <= (int64_t)1 << 28, DSA_ERR_UNSUPPORTED,
+            "this indexer shape keeps the L x L scores in the workspace; L must be <= 16384 (only E4M3 with "
+            "H_I = 64, D_I = 128 streams them)");
   if (!attention) return DSA_OK;
   if (a->attn_dt == DSA_BF16)
     REQUIRE(a->H % 8 == 0, DSA_ERR_UNSUPPORTED, "BF16 sparse MLA needs H a multiple of 8");
@@ -385,7 +395,7 @@ static dsa_status check_prefill(const dsa_prefill_args *a, bool attention) {
 
 size_t dsa_prefill_workspace_bytes(const dsa_prefill_args *a) {
   if (!a || a->L < 1) return 0;
-  if (a->idx_dt == DSA_F32) {
+  if (!prefill_fused(a)) {
     const size_t L = (size_t)a->L;
     return align_up(L * L * 4, 256) + 2 * align_up(L * 4, 256);
   }
@@ -395,7 +405,7 @@ size_t dsa_prefill_workspace_bytes(const dsa_prefill_args *a) {
 // indexer + top-k of one prefill sequence into a->idx
 static dsa_status prefill_select(const dsa_prefill_args *a, void *workspace, hipStream_t stream) {
   const int L = a->L;
-  if (a->idx_dt == DSA_E4M3)
+  if (prefill_fused(a))
     return hip_check(launch_prefill_indexer_topk((const uint8_t *)a->q_idx, a->q_scale, (const uint8_t *)a->k_idx,
                                                  a->k_scale, a->w, L, a->k, a->idx, (uint32_t *)workspace, stream),
                      "prefill indexer/top-k launch");
@@ -403,7 +413,11 @@ static dsa_status prefill_select(const dsa_prefill_args *a, void *workspace, hip
   int32_t *qpos = (int32_t *)((char *)workspace + align_up((size_t)L * L * 4, 256));
   int32_t *nval = (int32_t *)((char *)qpos + align_up((size_t)L * 4, 256));
   dsa_status st = hip_check(launch_positions(qpos, nval, L, stream), "positions launch");
-  if (st == DSA_OK)
+  if (st == DSA_OK && a->idx_dt == DSA_E4M3)
+    st = hip_check(launch_indexer_scores_fp8((const uint8_t *)a->q_idx, a->q_scale, (const uint8_t *)a->k_idx,
+                                             a->k_scale, a->w, qpos, L, L, a->H_I, a->D_I, sc, L, stream),
+                   "indexer launch");
+  else if (st == DSA_OK)
     st = hip_check(launch_indexer_scores_f32((const float *)a->q_idx, (const float *)a->k_idx, a->w, qpos, L, L,
                                              a->H_I, a->D_I, sc, L, stream),
                    "indexer launch");

@@ -20,7 +20,7 @@ hipError_t launch_quantize(const float *x, int64_t rows, int32_t cols, uint8_t *
                            hipStream_t s);
 hipError_t launch_indexer_scores_fp8(const uint8_t *q, const float *qs, const uint8_t *k,
                                      const float *ks, const float *w, const int32_t *q_pos,
-                                     int32_t T, int32_t S, int32_t H_I, float *scores, int64_t ld,
+                                     int32_t T, int32_t S, int32_t H_I, int32_t D_I, float *scores, int64_t ld,
                                      hipStream_t s);
 hipError_t launch_indexer_scores_f32(const float *q, const float *k, const float *w,
                                      const int32_t *q_pos, int32_t T, int32_t S, int32_t H_I,

@@ -13,6 +13,10 @@
 //    flight.
 // Each kernel folds its results into a value that is stored only if it hits an
 // impossible constant, so no work can be removed.
+//
+// Also here: one E4M3 16x16x128 MFMA per wave on given operands, to measure
+// how the matrix core sums the 128 products of each dot product (the caller
+// compares with exact sums).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -105,6 +109,20 @@ __global__ __launch_bounds__(256) void hbm_write_stream(f32x4 *__restrict__ x, i
   }
 }
 
+// Trial t: D[t] = A[t] B[t]^T, A[t] and B[t] [16][128] E4M3 bytes (row j of
+// B[t] is column j of the MFMA's B operand), D[t] [16][16] fp32, zero
+// accumulator input.  One wave per trial.
+__global__ __launch_bounds__(64) void fp8_mfma_dot(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
+                                                  float *__restrict__ D) {
+  const int l = threadIdx.x, g = l >> 4, c = l & 15;
+  const size_t t = blockIdx.x;
+  const i32x8 a = *reinterpret_cast<const i32x8 *>(A + (t * 16 + c) * 128 + 32 * g);
+  const i32x8 b = *reinterpret_cast<const i32x8 *>(B + (t * 16 + c) * 128 + 32 * g);
+  const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) D[(t * 16 + 4 * g + r) * 16 + c] = d[r];
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,6 +144,14 @@ int dsa_peak_bf16_mfma(int blocks, int iters, float *sink, hipStream_t s) {
 // Read `bytes` (a multiple of 16, 16-byte aligned) of device memory at x.
 int dsa_peak_hbm_read(const void *x, int64_t bytes, int blocks, float *sink, hipStream_t s) {
   hipLaunchKernelGGL(hbm_read_stream, dim3(blocks), dim3(256), 0, s, (const f32x4 *)x, bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// `trials` E4M3 16x16x128 MFMAs on device operands A, B ([trials][16][128]
+// bytes each) into D ([trials][16][16] fp32).
+int dsa_peak_fp8_mfma_dot(const void *A, const void *B, float *D, int trials, hipStream_t s) {
+  if (trials <= 0) return 0;
+  hipLaunchKernelGGL(fp8_mfma_dot, dim3(trials), dim3(64), 0, s, (const uint8_t *)A, (const uint8_t *)B, D);
   return (int)hipGetLastError();
 }
 

@@ -193,6 +193,8 @@ class DecodeConfig:
 CONFIGS = {
     # tiny fp32 prefill: parity only
     "tiny": PrefillConfig("tiny_fp32_L2048", 2048, 4, 64, 8, 256, 0, "f32", False),
+    # the same with the indexer operands quantised per token to e4m3 (4 heads of 64 dims)
+    "tiny_fp8": PrefillConfig("tiny_fp8_L2048", 2048, 4, 64, 8, 256, 0, "f32", True),
     "decode": DecodeConfig("decode_B64_ctx32768", 64, 32768, 32768, 64, 128, 128, 2048, 0, False),
     "prefill16k": PrefillConfig("prefill_L16384", 16384, 64, 128, 128, 2048, 1, "bf16", True),
     "prefill128k": PrefillConfig("prefill_L131072", 131072, 64, 128, 128, 2048, 1, "bf16", True),

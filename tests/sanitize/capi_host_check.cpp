@@ -64,10 +64,10 @@ hipError_t launch_quantize(const float *x, int64_t rows, int32_t cols, uint8_t *
 }
 hipError_t launch_indexer_scores_fp8(const uint8_t *q, const float *qs, const uint8_t *k, const float *ks,
                                      const float *w, const int32_t *q_pos, int32_t T, int32_t S, int32_t H_I,
-                                     float *scores, int64_t ld, hipStream_t) {
+                                     int32_t D_I, float *scores, int64_t ld, hipStream_t) {
   ++g_launches;
-  read_all(q, (size_t)T * H_I * 128);
-  read_all(k, (size_t)S * 128);
+  read_all(q, (size_t)T * H_I * D_I);
+  read_all(k, (size_t)S * D_I);
   read_all(qs, (size_t)T * 4);
   read_all(ks, (size_t)S * 4);
   read_all(w, (size_t)T * H_I * 4);
@@ -322,6 +322,9 @@ static void check_quantize_and_indexer() {
                             HI, 128, DSA_E4M3, (float *)out.p(), 1005, 0) == DSA_OK);
   EXPECT(dsa_indexer_scores(q.p(), (float *)qs.p(), k.p(), (float *)ks.p(), (float *)w.p(), (int32_t *)pos.p(), T, S,
                             HI, 128, DSA_E4M3, (float *)out.p(), 999, 0) == DSA_ERR_INVALID_ARG);
+  Buf q4(T * 4 * 64), k4(S * 64), w4(T * 4 * 4);  // the tiny workload's E4M3 indexer: 4 heads of 64 dims
+  EXPECT(dsa_indexer_scores(q4.p(), (float *)qs.p(), k4.p(), (float *)ks.p(), (float *)w4.p(), (int32_t *)pos.p(), T,
+                            S, 4, 64, DSA_E4M3, (float *)out.p(), 1005, 0) == DSA_OK);
   Buf qf(T * 4 * 64 * 4), kf(S * 64 * 4);
   EXPECT(dsa_indexer_scores(qf.p(), nullptr, kf.p(), nullptr, (float *)w.p(), (int32_t *)pos.p(), T, S, 4, 64,
                             DSA_F32, (float *)out.p(), 1005, 0) == DSA_OK);
@@ -390,13 +393,18 @@ static dsa_prefill_args prefill_args(int L, dsa_dtype idt, Buf &qi, Buf &qs, Buf
 
 static void check_prefill() {
   for (int L : {130, 2500}) {
-    for (dsa_dtype idt : {DSA_E4M3, DSA_F32}) {
-      const int H = 16, k = 256, e = idt == DSA_E4M3 ? 1 : 4, HI = idt == DSA_E4M3 ? 64 : 4,
-                DI = idt == DSA_E4M3 ? 128 : 64;
+    // E4M3 64 x 128 (fused), F32 4 x 64, and E4M3 4 x 64 (the unfused path with fp32 attention)
+    for (int mode = 0; mode < 3; ++mode) {
+      const dsa_dtype idt = mode == 1 ? DSA_F32 : DSA_E4M3;
+      const bool bf = mode == 0;
+      const int H = 16, k = 256, e = idt == DSA_E4M3 ? 1 : 4, HI = mode == 0 ? 64 : 4, DI = mode == 0 ? 128 : 64;
       Buf qi((size_t)L * HI * DI * e), qs(L * 4), ki((size_t)L * DI * e), ks(L * 4), w((size_t)L * HI * 4),
-          q((size_t)L * H * 576 * (idt == DSA_E4M3 ? 2 : 4)), kv((size_t)L * 576 * (idt == DSA_E4M3 ? 2 : 4)),
-          idx((size_t)L * k * 4), out((size_t)L * H * 512 * (idt == DSA_E4M3 ? 2 : 4)), lse((size_t)L * H * 4);
+          q((size_t)L * H * 576 * (bf ? 2 : 4)), kv((size_t)L * 576 * (bf ? 2 : 4)), idx((size_t)L * k * 4),
+          out((size_t)L * H * 512 * (bf ? 2 : 4)), lse((size_t)L * H * 4);
       dsa_prefill_args a = prefill_args(L, idt, qi, qs, ki, ks, w, q, kv, idx, out, lse, H, k);
+      a.H_I = HI;
+      a.D_I = DI;
+      a.attn_dt = bf ? DSA_BF16 : DSA_F32;
       const size_t wsb = dsa_prefill_workspace_bytes(&a);
       Buf ws(wsb);
       EXPECT(dsa_prefill(&a, ws.p(), wsb, 0) == DSA_OK);

@@ -72,10 +72,10 @@ def test_indexer_validation(dsa):
     bad[1] = None  # E4M3 without q scale
     assert f(*bad) == dsa.DSA_ERR_INVALID_ARG
     bad = list(ok_args)
-    bad[9] = 64  # D_I 64 with E4M3
+    bad[9] = 96  # E4M3 widths are 64 or 128
     assert f(*bad) == dsa.DSA_ERR_UNSUPPORTED
     bad = list(ok_args)
-    bad[8] = 48
+    bad[8] = 65  # more than 64 E4M3 heads
     assert f(*bad) == dsa.DSA_ERR_UNSUPPORTED
     bad = list(ok_args)
     bad[10] = dsa.DSA_BF16
@@ -201,9 +201,15 @@ def test_prefill_validation(dsa):
     a = dsa.make_prefill_args(1000, 64, 128, 128, 2048, dsa.DSA_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE, dsa.DSA_BF16,
                               FAKE, FAKE, 0.07, FAKE, FAKE, FAKE)
     assert L.dsa_prefill(None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
-    a.H_I = 32
+    a.H_I = 80
     assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
-    a.H_I = 64
+    # other E4M3 shapes are accepted (unfused, L x L scores in the workspace): the missing workspace is the error
+    a.H_I, a.D_I = 4, 64
+    assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_prefill_workspace_bytes(ctypes.byref(a)) >= 1000 * 1000 * 4
+    a.L = 20000  # ... but only while L x L fits
+    assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    a.L, a.H_I, a.D_I = 1000, 64, 128
     a.k = 0
     assert L.dsa_prefill(ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     a.k = 2048

@@ -65,9 +65,9 @@ def test_quantize_bit_exact(dsa, ora):
 
 
 # ------------------------------------------------------------------ A1
-def _indexer_case(seed, T, S, H_I, fp8=True, pos_offset=0):
-    q = synth.normal(seed, synth.T_QI, (T, H_I, 128))
-    k = synth.normal(seed, synth.T_KI, (S, 128))
+def _indexer_case(seed, T, S, H_I, fp8=True, pos_offset=0, D_I=128):
+    q = synth.normal(seed, synth.T_QI, (T, H_I, D_I))
+    k = synth.normal(seed, synth.T_KI, (S, D_I))
     w = synth.normal(seed, synth.T_W, (T, H_I), std=0.5)
     pos = (torch.arange(T, dtype=torch.int32) * max(1, S // max(T, 1)) + pos_offset).clamp(max=S - 1)
     return q, k, w, pos
@@ -84,29 +84,37 @@ def _gpu_scores(dsa, q8, qs, k8, ks, w, pos, S, dt):
     return out[:, :S].double().numpy()
 
 
-@pytest.mark.parametrize("H_I", [64, 32])
-def test_indexer_fp8_scores(dsa, ora, H_I):
+# (64, 128) and (32, 128) are the full-size FP8 MFMA kernel; the rest sum the
+# exact E4M3 products in fp32 ((4, 64) is the tiny workload's indexer)
+FP8_SHAPES = [(64, 128), (32, 128), (4, 64), (20, 64), (48, 128), (1, 128), (64, 64)]
+
+
+@pytest.mark.parametrize("H_I,D_I", FP8_SHAPES)
+def test_indexer_fp8_scores(dsa, ora, H_I, D_I):
     T, S = 37, 1000  # ragged: S not a multiple of 64 or 512
-    _say(f"indexer fp8 T={T} S={S} H_I={H_I}")
-    q, k, w, pos = _indexer_case(3, T, S, H_I)
+    _say(f"indexer fp8 T={T} S={S} H_I={H_I} D_I={D_I}")
+    q, k, w, pos = _indexer_case(3, T, S, H_I, D_I=D_I)
     q8, qs = ora.quantize_rows(q.view(T, -1).numpy())
     k8, ks = ora.quantize_rows(k.numpy())
-    q8 = torch.from_numpy(q8).view(T, H_I, 128)
+    q8 = torch.from_numpy(q8).view(T, H_I, D_I)
     g = _gpu_scores(dsa, q8, torch.from_numpy(qs), torch.from_numpy(k8), torch.from_numpy(ks), w, pos, S,
                     dsa.DSA_E4M3)
     o, m = oracle_score_bounds(ora, q8.numpy(), k8, w.numpy(), pos, q_scale=qs, k_scale=ks)
-    check_scores(g, o, m, 128 + H_I, "fp8 scores")
+    check_scores(g, o, m, D_I + H_I, "fp8 scores")
 
 
-def test_indexer_fp8_exact_arithmetic(dsa, ora):
+@pytest.mark.parametrize("H_I,D_I", [(64, 128), (4, 64), (20, 64), (36, 128)])
+def test_indexer_fp8_exact_arithmetic(dsa, ora, H_I, D_I):
     """E4M3 payloads in {0,+-1,+-2}, scales 1, w in {+-1,+-0.5}: every partial
     sum is exact in fp32, so scores must be bit-identical and the top-k
-    (full of exact ties) identical under the position tie rule."""
-    T, S, H_I = 70, 700, 64
-    _say("indexer exact arithmetic")
+    (full of exact ties) identical under the position tie rule.  For the
+    other shapes this also pins the head and dim bounds: a stray head or dim
+    would change some sum."""
+    T, S = 70, 700
+    _say(f"indexer exact arithmetic H_I={H_I} D_I={D_I}")
     lut = torch.tensor([0xC0, 0xB8, 0x00, 0x38, 0x40], dtype=torch.uint8)  # -2,-1,0,1,2
-    qi = synth.randint(4, 1, (T, H_I, 128), 0, 4)
-    ki = synth.randint(4, 2, (S, 128), 0, 4)
+    qi = synth.randint(4, 1, (T, H_I, D_I), 0, 4)
+    ki = synth.randint(4, 2, (S, D_I), 0, 4)
     q8, k8 = lut[qi], lut[ki]
     w = torch.tensor([-1.0, -0.5, 0.5, 1.0])[synth.randint(4, 3, (T, H_I), 0, 3)]
     ones_t, ones_s = torch.ones(T), torch.ones(S)
@@ -334,6 +342,18 @@ def test_prefill_tiny_fp32_config(dsa, ora):
     t = _run_prefill(dsa, cfg, *ins)
     rows = np.unique(np.concatenate([np.arange(0, cfg.L, 37), [0, 1, 255, 256, 257, 2047]]))
     _check_prefill_rows(ora, cfg, *ins, t, rows, "tiny fp32")
+
+
+@pytest.mark.parametrize("attn", ["f32", "bf16"])
+def test_prefill_tiny_fp8_config(dsa, ora, attn):
+    """The tiny workload with its 4 x 64 indexer in E4M3 (zero-padded FP8
+    scores, row top-k) and the attention in fp32 or bf16."""
+    cfg = synth.scaled_down(synth.CONFIGS["tiny_fp8"], attn_dtype=attn)
+    _say(f"prefill tiny fp8 indexer L=2048 attention {attn}")
+    ins = _prefill_inputs(cfg)
+    t = _run_prefill(dsa, cfg, *ins)
+    rows = np.unique(np.concatenate([np.arange(0, cfg.L, 37), [0, 1, 255, 256, 257, 2047]]))
+    _check_prefill_rows(ora, cfg, *ins, t, rows, f"tiny fp8/{attn}")
 
 
 @pytest.mark.parametrize("L,k,H", [(1000, 256, 16), (777, 64, 32), (4500, 2048, 128), (130, 2048, 16)])
