@@ -74,10 +74,10 @@ def lib():
         L.ora_sparse_mla_bwd.argtypes = [ctypes.c_int, P, P, P, P, i64, i32, i64, i32, i32, i32, dbl,
                                          P, P, P, P]
         L.ora_indexer_kl_bwd.argtypes = [ctypes.c_int, P, P, ctypes.c_int, P, P, P, P, P, P, P, i64, i64, i32,
-                                         i32, i32, i32, i32, dbl, P, P, P, P, P, P, P, P, P]
+                                         i32, i32, i32, i32, dbl, P, P, P, P, P, P, P, P, P, dbl]
         L.ora_indexer_kl_grad.argtypes = [ctypes.c_int, P, P, P, P, P, i64, i32, i32, i32, dbl, P]
         L.ora_indexer_bwd.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, i64, i64, i32, i32, i32, P, P, P, P, P, P,
-                                      P, P]
+                                      P, P, dbl]
         _lib = L
     return _lib
 
@@ -320,9 +320,12 @@ def indexer_kl_grad(q_att, kv, idx, scores, dkl, sm_scale):
     return g
 
 
-def indexer_bwd(q_idx, k_idx, w, idx, g, q_scale=None, k_scale=None):
+def indexer_bwd(q_idx, k_idx, w, idx, g, q_scale=None, k_scale=None, kink_rel=None):
     """The indexer's gradients from a score gradient g [T, k] -> dict of fp64
-    dw, dq, dk and mag_dw, mag_dq, mag_dk, amb_dq, amb_dk."""
+    dw, dq, dk and mag_dw, mag_dq, mag_dk, amb_dq, amb_dk.  kink_rel: the
+    relative accuracy of the evaluation being checked, which sets the width of
+    the ambiguous band around the ReLU kink (default: an IEEE fp32 sum of D_I
+    products, (D_I + 2) 2^-24)."""
     q_idx, k_idx = _np(q_idx), _np(k_idx)
     it = _dtype_code(q_idx)
     assert _dtype_code(k_idx) == it
@@ -337,17 +340,17 @@ def indexer_bwd(q_idx, k_idx, w, idx, g, q_scale=None, k_scale=None):
            "amb_dq": np.empty((T, H_I, D_I)), "amb_dk": np.empty((N, D_I))}
     lib().ora_indexer_bwd(it, _p(q_idx), _p(qs), _p(k_idx), _p(ks), _p(w), _p(idx), _p(g), T, N, H_I, D_I, k,
                           _p(out["dw"]), _p(out["dq"]), _p(out["dk"]), _p(out["mag_dw"]), _p(out["mag_dq"]),
-                          _p(out["mag_dk"]), _p(out["amb_dq"]), _p(out["amb_dk"]))
+                          _p(out["mag_dk"]), _p(out["amb_dq"]), _p(out["amb_dk"]), float(kink_rel or 0.0))
     return out
 
 
-def indexer_kl_bwd(q_att, kv, q_idx, k_idx, w, idx, dkl, sm_scale, q_scale=None, k_scale=None):
+def indexer_kl_bwd(q_att, kv, q_idx, k_idx, w, idx, dkl, sm_scale, q_scale=None, k_scale=None, kink_rel=None):
     """Gradient of the per-token KL(p || pi) (weighted by dkl [T]) into the
     indexer.  q_att [T,H,Dqk], kv [N,Dqk] (f32, bf16 or f64); q_idx [T,H_I,D_I],
     k_idx [N,D_I] (E4M3 payloads with q_scale [T], k_scale [N], or f32/f64);
     w [T,H_I]; idx [T,k] rows of kv and k_idx.  -> dict of fp64 arrays
     g [T,k], dw [T,H_I], dq [T,H_I,D_I], dk [N,D_I], and mag_dw, mag_dq,
-    mag_dk, amb_dq, amb_dk (see dsa_oracle.c)."""
+    mag_dk, amb_dq, amb_dk (see dsa_oracle.c); kink_rel as for indexer_bwd."""
     q_att, kv = _np(q_att), _np(kv)
     at = _dtype_code(q_att)
     assert _dtype_code(kv) == at and at in (F32, BF16, F64)
@@ -368,5 +371,5 @@ def indexer_kl_bwd(q_att, kv, q_idx, k_idx, w, idx, dkl, sm_scale, q_scale=None,
     lib().ora_indexer_kl_bwd(at, _p(q_att), _p(kv), it, _p(q_idx), _p(qs), _p(k_idx), _p(ks), _p(w), _p(idx),
                              _p(dkl), T, N, H, H_I, D_I, k, Dqk, float(sm_scale), _p(out["g"]), _p(out["dw"]),
                              _p(out["dq"]), _p(out["dk"]), _p(out["mag_dw"]), _p(out["mag_dq"]), _p(out["mag_dk"]),
-                             _p(out["amb_dq"]), _p(out["amb_dk"]))
+                             _p(out["amb_dq"]), _p(out["amb_dk"]), float(kink_rel or 0.0))
     return out

@@ -628,16 +628,16 @@ void ora_indexer_kl_grad(int att_dtype, const void *q_att, const void *kv, const
  * dq [T,H_I,D_I], dk [N,D_I] (zeroed here).  For tolerances: mag_dq, mag_dk
  * are the same sums over |terms|, mag_dw sums |g_a| sum_d |qh_jd kh_ad| (which
  * bounds |g_a x_ja| and the rounding of x_ja), and amb_* collect the terms
- * whose dot product lies
- * within the fp32 rounding bound (D_I + 2) 2^-24 sum_d |qh_jd kh_ad| of the
- * kink, where an fp32 evaluation may take either side.
+ * whose dot product lies within kink_rel sum_d |qh_jd kh_ad| of the kink,
+ * where an evaluation of that accuracy may take either side (an IEEE fp32
+ * sum: kink_rel = (D_I + 2) 2^-24; kink_rel <= 0 selects that value).
  */
 void ora_indexer_bwd(int idx_dtype, const void *q_idx, const float *q_scale, const void *k_idx, const float *k_scale,
                      const double *w, const int32_t *idx, const double *g, int64_t T, int64_t N, int32_t H_I,
                      int32_t D_I, int32_t k, double *dw, double *dq, double *dk, double *mag_dw, double *mag_dq,
-                     double *mag_dk, double *amb_dq, double *amb_dk)
+                     double *mag_dk, double *amb_dq, double *amb_dk, double kink_rel)
 {
-    const double u = ldexp(1.0, -24);
+    const double win = kink_rel > 0.0 ? kink_rel : (D_I + 2) * ldexp(1.0, -24);
     int64_t t, i;
     double *qh = (double *)malloc(sizeof(double) * (size_t)H_I * (size_t)D_I);
     double *kh = (double *)malloc(sizeof(double) * (size_t)D_I);
@@ -675,7 +675,7 @@ void ora_indexer_bwd(int idx_dtype, const void *q_idx, const float *q_scale, con
                     x += qh[j * D_I + d] * kh[d];
                     xm += fabs(qh[j * D_I + d] * kh[d]);
                 }
-                amb = fabs(x) <= (D_I + 2) * u * xm;
+                amb = fabs(x) <= win * xm;
                 if (x > 0.0)
                     dw[t * H_I + j] += ga * x;
                 mag_dw[t * H_I + j] += gm * xm;   /* bounds |g x| and the rounding of x itself */
@@ -703,12 +703,14 @@ void ora_indexer_bwd(int idx_dtype, const void *q_idx, const float *q_scale, con
  * ora_indexer_kl_bwd -- the two steps composed: the index scores of the
  * entries from the indexer's inputs (I_a = sum_j w_j max(0, x_ja)), their
  * gradient g, then dw, dq, dk.  Entries of idx index both kv and the keys.
+ * kink_rel: as for ora_indexer_bwd.
  */
 void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int idx_dtype, const void *q_idx,
                         const float *q_scale, const void *k_idx, const float *k_scale, const double *w,
                         const int32_t *idx, const double *dkl, int64_t T, int64_t N, int32_t H, int32_t H_I,
                         int32_t D_I, int32_t k, int32_t Dqk, double sm_scale, double *g, double *dw, double *dq,
-                        double *dk, double *mag_dw, double *mag_dq, double *mag_dk, double *amb_dq, double *amb_dk)
+                        double *dk, double *mag_dw, double *mag_dq, double *mag_dk, double *amb_dq, double *amb_dk,
+                        double kink_rel)
 {
     double *sc = (double *)malloc(sizeof(double) * (size_t)(T * k > 0 ? T * k : 1));
     double *kh = (double *)malloc(sizeof(double) * (size_t)D_I);
@@ -735,7 +737,7 @@ void ora_indexer_kl_bwd(int att_dtype, const void *q_att, const void *kv, int id
     }
     ora_indexer_kl_grad(att_dtype, q_att, kv, idx, sc, dkl, T, H, k, Dqk, sm_scale, g);
     ora_indexer_bwd(idx_dtype, q_idx, q_scale, k_idx, k_scale, w, idx, g, T, N, H_I, D_I, k, dw, dq, dk, mag_dw,
-                    mag_dq, mag_dk, amb_dq, amb_dk);
+                    mag_dq, mag_dk, amb_dq, amb_dk, kink_rel);
     free(sc);
     free(kh);
 }

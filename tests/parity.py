@@ -28,6 +28,10 @@ import numpy as np
 
 SCORE_RTOL = 1e-3
 TIE_RTOL = 1e-4
+# Accuracy of one E4M3 16x16x128 MFMA dot product: its fp32 result lies within
+# this fraction of the sum of the 128 products' magnitudes of the exact sum
+# (twice the largest error measured; test_gpu_fp8_mfma_sums.py pins it).
+FP8_MFMA_SUM_REL = 2.0 ** -11
 
 
 def abs_payload(x):

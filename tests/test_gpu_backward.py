@@ -14,8 +14,9 @@ Tolerances (each derived from the arithmetic of the kernel it checks):
     ((k + H_I + T + 8) 2^-24 + 2^-18) mag covers this, with mag the oracle's
     sum of |terms| (for dw, |g| times the magnitude of each dot product, which
     also bounds its own rounding), plus amb: the terms whose dot product lies
-    within fp32 rounding of the ReLU kink, where the GPU may take the other
-    side.
+    within the FP8 MFMA's accuracy (FP8_MFMA_SUM_REL of the sum of the
+    products' magnitudes; the kernel forms x with that MFMA) of the ReLU kink,
+    where the GPU may take the other side.
 Each test prints its case before touching the GPU.
 """
 import math
@@ -25,6 +26,7 @@ import pytest
 import torch
 
 import synth
+from tests.parity import FP8_MFMA_SUM_REL
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -135,7 +137,8 @@ def test_indexer_bwd_from_score_gradient(dsa, ora, T, S, k, causal):
     torch.cuda.synchronize()
     ref_idx = idx.clone()
     ref_idx[0, 1] = -1
-    r = ora.indexer_bwd(q8, k8, w.double().numpy(), ref_idx.numpy(), g.double().numpy(), q_scale=qs, k_scale=ks)
+    r = ora.indexer_bwd(q8, k8, w.double().numpy(), ref_idx.numpy(), g.double().numpy(), q_scale=qs, k_scale=ks,
+                        kink_rel=FP8_MFMA_SUM_REL)
     f = (k + 64 + T + 8) * U
     fs = f + SPLIT  # dq, dk: the coefficient enters as two bf16 terms
     _check("dw", dw.cpu().numpy(), r["dw"], f * r["mag_dw"] + 1e-30)
@@ -208,7 +211,8 @@ def test_indexer_kl_backward_after_prefill_selection(dsa, ora):
     pi, p = _pi_p(sc.cpu().double().numpy(), gidx, g_ref, dklv)
     _check("score gradient (pipeline)", grad.cpu().numpy(), g_ref, 1e-4 * dklv[:, None] * (pi + np.abs(p)) + 1e-12)
     # step 2, the indexer gradients, on the GPU's own score gradient
-    r = ora.indexer_bwd(q8, k8, w.double().numpy(), gidx, grad.cpu().double().numpy(), q_scale=qs, k_scale=ks)
+    r = ora.indexer_bwd(q8, k8, w.double().numpy(), gidx, grad.cpu().double().numpy(), q_scale=qs, k_scale=ks,
+                        kink_rel=FP8_MFMA_SUM_REL)
     f = (k + 64 + L + 8) * U
     fs = f + SPLIT  # dq, dk: the coefficient enters as two bf16 terms
     _check("dw (pipeline)", dw.cpu().numpy(), r["dw"], f * r["mag_dw"] + 1e-30)
@@ -216,7 +220,8 @@ def test_indexer_kl_backward_after_prefill_selection(dsa, ora):
     _check("dk (pipeline)", dk.cpu().numpy(), r["dk"], fs * r["mag_dk"] + r["amb_dk"] + 1e-30)
     # and the composition: the GPU's steps reproduce the oracle's KL backward of the indexer's own
     # scores, up to those scores' fp32 rounding (pi moves by at most 2 pi |dI|)
-    full = ora.indexer_kl_bwd(q, kv, q8, k8, w.double().numpy(), gidx, dklv, cfg.sm_scale, q_scale=qs, k_scale=ks)
+    full = ora.indexer_kl_bwd(q, kv, q8, k8, w.double().numpy(), gidx, dklv, cfg.sm_scale, q_scale=qs, k_scale=ks,
+                              kink_rel=FP8_MFMA_SUM_REL)
     sco = np.take_along_axis(ora.indexer_rows(q8, k8, w, np.arange(L, dtype=np.int32), q_scale=qs, k_scale=ks),
                              np.maximum(gidx, 0).astype(np.int64), axis=1)
     dI = float(np.abs(sc.cpu().double().numpy() - sco)[gidx >= 0].max())
