@@ -168,8 +168,10 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
  *   lse [T,H] fp32 (the forward's); dq [T,H,576], dkv [N,576] fp32 out, fully
  *   overwritten.
  * bf16 MFMA with fp32 sums; dS and P enter the products rounded to bf16, and
- * dout . o uses the forward's bf16 output.  dkv is summed per row over its
- * pairs in increasing (t, a) order (an inverted selection, no atomics), so
+ * dout . o uses the forward's bf16 output.  Each pair's contribution to dkv
+ * (its sum over the heads) is rounded to bf16 once; dkv is summed in fp32 per
+ * row over its pairs in increasing (t, a) order (an inverted selection, no
+ * atomics), so
  * it is deterministic as long as no idx row lists one row more than 4096
  * times.
  * workspace: dsa_sparse_mla_bwd_workspace_bytes(T, H, N, k), required.

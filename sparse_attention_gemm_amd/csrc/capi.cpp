@@ -272,12 +272,12 @@ dsa_status dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const uint8_
 
 // Sparse MLA backward workspace: D [T, H] fp32, then for one chunk of up to
 // kMlaBwdChunk queries s dS and P [Tc, k, H] bf16, the pair gradients
-// G [Tc, k, 576] fp32 and the inverted selection (cnt, start [N + 1], list [Tc k]).
+// G [Tc, k, 576] bf16 and the inverted selection (cnt, start [N + 1], list [Tc k]).
 static constexpr int32_t kMlaBwdChunk = 512;
 static int32_t mla_bwd_chunk(int32_t T) { return T < kMlaBwdChunk ? T : kMlaBwdChunk; }
 static size_t mla_bwd_ws(int32_t T, int32_t H, int64_t N, int32_t k) {
   const size_t tc = (size_t)mla_bwd_chunk(T);
-  return align_up((size_t)T * H * 4, 256) + 2 * align_up(tc * k * H * 2, 256) + align_up(tc * k * 576 * 4, 256) +
+  return align_up((size_t)T * H * 4, 256) + 2 * align_up(tc * k * H * 2, 256) + align_up(tc * k * 576 * 2, 256) +
          2 * align_up(((size_t)N + 1) * 4, 256) + align_up(tc * k * 4, 256);
 }
 
@@ -310,8 +310,8 @@ dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx,
   p += align_up((size_t)tc_max * k * H * 2, 256);
   void *pT = p;
   p += align_up((size_t)tc_max * k * H * 2, 256);
-  float *G = (float *)p;
-  p += align_up((size_t)tc_max * k * 576 * 4, 256);
+  void *G = p;
+  p += align_up((size_t)tc_max * k * 576 * 2, 256);
   int32_t *cnt = (int32_t *)p;
   p += align_up(((size_t)N + 1) * 4, 256);
   int32_t *start = (int32_t *)p;
@@ -326,7 +326,7 @@ dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx,
     if (st == DSA_OK)
       st = hip_check(launch_scatter_build(idx + (int64_t)t0 * k, (int64_t)tc * k, N, cnt, start, list, stream),
                      "scatter launch");
-    if (st == DSA_OK) st = hip_check(launch_scatter_add(start, list, N, G, 576, dkv, stream), "scatter launch");
+    if (st == DSA_OK) st = hip_check(launch_scatter_add_bf16(start, list, N, G, 576, dkv, stream), "scatter launch");
   }
   return st;
 }

@@ -85,14 +85,17 @@ hipError_t launch_scatter_build(const int32_t *idx, int64_t npairs, int64_t N, i
                                 int32_t *list, hipStream_t s);
 hipError_t launch_scatter_add(const int32_t *start, const int32_t *list, int64_t N, const float *X, int32_t W, float *Y,
                               hipStream_t s);
+// The same with bf16 X [npairs, W] (W even, at most 768), summed in fp32.
+hipError_t launch_scatter_add_bf16(const int32_t *start, const int32_t *list, int64_t N, const void *X, int32_t W,
+                                   float *Y, hipStream_t s);
 hipError_t launch_fill_zero_f32(float *p, int64_t n, hipStream_t s);
 // Sparse MLA backward: D = dO . o per (token, head); then for queries
 // [t0, t0 + Tc): dq, s dS and P [Tc, k, H] bf16, and the pair gradients
-// G [Tc, k, 576] fp32 (H a multiple of 32, at most 128).
+// G [Tc, k, 576] bf16 (H a multiple of 32, at most 128).
 hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, float *D, hipStream_t s);
 hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                 const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0,
-                                int32_t Tc, float *dq, void *dsT, void *pT, float *G, hipStream_t s);
+                                int32_t Tc, float *dq, void *dsT, void *pT, void *G, hipStream_t s);
 // The library's static device scratch (scratch.hip): its size, and its
 // address on the device that owns `stream` (which must be the current device),
 // looked up once per device.

@@ -137,6 +137,76 @@ __global__ __launch_bounds__(BS) void scatter_add_kernel(const int32_t *__restri
   }
 }
 
+// The same for bf16 X (W even): thread u of a row owns the column pairs
+// 2 (u + BS j), 2 (u + BS j) + 1 and adds them in fp32, in the same order.
+template <int BS, int NPAIR>
+__global__ __launch_bounds__(BS) void scatter_add_bf16_kernel(const int32_t *__restrict__ start,
+                                                              const int32_t *__restrict__ list,
+                                                              const __bf16 *__restrict__ X, int W,
+                                                              float *__restrict__ Y) {
+  __shared__ int32_t keys[kSortCap];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t b = start[r], n = start[r + 1] - b;
+  if (n == 0) return;  // uniform
+  const bool sorted = n <= kSortCap;
+  if (sorted) {
+    int m = 1;
+    while (m < n) m <<= 1;
+    for (int i = tid; i < m; i += BS) keys[i] = i < n ? list[b + i] : 0x7FFFFFFF;
+    __syncthreads();
+    for (int size = 2; size <= m; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < (m >> 1); i += BS) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const int32_t x = keys[lo], y = keys[hi];
+          if ((x > y) == up) {
+            keys[lo] = y;
+            keys[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  const int W2 = W / 2;
+  float acc[NPAIR][2];
+#pragma unroll
+  for (int j = 0; j < NPAIR; ++j) acc[j][0] = acc[j][1] = 0.0f;
+  constexpr int kAhead = 8;
+  for (int i0 = 0; i0 < n; i0 += kAhead) {
+    bf16x2 v[kAhead][NPAIR];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int i = i0 + u;
+      const int32_t p = i < n ? (sorted ? keys[i] : list[b + i]) : -1;
+#pragma unroll
+      for (int j = 0; j < NPAIR; ++j) {
+        const int d2 = tid + BS * j;
+        v[u][j] = (p >= 0 && d2 < W2) ? *reinterpret_cast<const bf16x2 *>(X + (int64_t)p * W + 2 * d2)
+                                      : bf16x2{0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u)
+#pragma unroll
+      for (int j = 0; j < NPAIR; ++j) {
+        acc[j][0] += (float)v[u][j][0];
+        acc[j][1] += (float)v[u][j][1];
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < NPAIR; ++j) {
+    const int d2 = tid + BS * j;
+    if (d2 < W2) {
+      Y[r * W + 2 * d2] += acc[j][0];
+      Y[r * W + 2 * d2 + 1] += acc[j][1];
+    }
+  }
+}
+
 int grid_for(int64_t n) {
   const int64_t b = (n + 255) / 256;
   return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
@@ -174,6 +244,15 @@ hipError_t launch_scatter_add(const int32_t *start, const int32_t *list, int64_t
     hipLaunchKernelGGL((scatter_add_kernel<256, 3>), dim3((uint32_t)N), dim3(256), 0, s, start, list, X, W, Y);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_add_bf16(const int32_t *start, const int32_t *list, int64_t N, const void *X, int32_t W,
+                                   float *Y, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (W % 2 != 0 || W > 768) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((scatter_add_bf16_kernel<128, 3>), dim3((uint32_t)N), dim3(128), 0, s, start, list,
+                     (const __bf16 *)X, W, Y);
   return hipGetLastError();
 }
 

@@ -608,7 +608,8 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
 //    in bf16;
 //  * mla_bwd_g_kernel: per query, the pair gradients G[pair, :] =
 //    (s dS)^T q + P^T dO, a GEMM over the heads (K = heads, bf16 MFMA, fp32
-//    sums) with q^T and dO^T resident in registers and s dS, P streamed;
+//    sums, stored rounded to bf16) with q^T and dO^T resident in registers and
+//    s dS, P streamed;
 //  * dkv[r] = sum of G over r's pairs in increasing pair order (scatter.hip).
 
 // D[t, h] = sum_d dO[t,h,d] o[t,h,d]: one wave per (t, h), 8 dims per lane.
@@ -938,7 +939,7 @@ __global__ __launch_bounds__(kGThreads, 1) void mla_bwd_g_kernel(const __bf16 *_
                                                                  const __bf16 *__restrict__ dout,
                                                                  const __bf16 *__restrict__ dsT,
                                                                  const __bf16 *__restrict__ pT, int k, int64_t t0,
-                                                                 float *__restrict__ G) {
+                                                                 __bf16 *__restrict__ G) {
   constexpr int H = 32 * KS;
   using S = GShape<H>;
   extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -1006,10 +1007,10 @@ __global__ __launch_bounds__(kGThreads, 1) void mla_bwd_g_kernel(const __bf16 *_
     }
   }
   __syncthreads();
-  // G rows of this query as a bounded buffer: stores of keys >= k are dropped
+  // G rows of this query (bf16) as a bounded buffer: stores of keys >= k are dropped
   const __amdgpu_buffer_rsrc_t gr =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(G + tc * k * 576), 0, k * 576 * 4, (int)kRsrcWord3);
-  const int goff = c * 576 * 4 + (16 * ti0 + 4 * g) * 4;  // bytes: key c of a tile, this lane's dims
+      __builtin_amdgcn_make_buffer_rsrc((void *)(G + tc * k * 576), 0, k * 576 * 2, (int)kRsrcWord3);
+  const int goff = c * 576 * 2 + (16 * ti0 + 4 * g) * 2;  // bytes: key c of a tile, this lane's dims
   for (int j = 0; j < nblk; ++j) {
     if (loader) {
       // block j + 2 goes to the buffer last read before the previous barrier
@@ -1037,10 +1038,14 @@ __global__ __launch_bounds__(kGThreads, 1) void mla_bwd_g_kernel(const __bf16 *_
 #pragma unroll
           for (int jt = 0; jt < 3; ++jt) acc[jt] = mfma_bf16_16x16x32(ao[jt][s], b, acc[jt]);
         }
-        const int off = (j * kGKeys + 16 * kt) * 576 * 4 + goff;
+        const int off = (j * kGKeys + 16 * kt) * 576 * 2 + goff;
 #pragma unroll
-        for (int jt = 0; jt < 3; ++jt)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[jt]), gr, off + 64 * jt, 0, 0);
+        for (int jt = 0; jt < 3; ++jt) {
+          bf16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[jt][r];  // RNE
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), gr, off + 32 * jt, 0, 0);
+        }
       }
     }
     __syncthreads();
@@ -1103,7 +1108,7 @@ static hipError_t launch_ds_nw(const void *q, const void *kv, const int32_t *idx
 
 template <int KS>
 static hipError_t launch_g_ks(const void *q, const void *dout, const void *dsT, const void *pT, int32_t k, int64_t t0,
-                              int32_t Tc, float *G, hipStream_t s) {
+                              int32_t Tc, __bf16 *G, hipStream_t s) {
   constexpr int bytes = GShape<32 * KS>::kSmem;
   static bool attr_done = false;  // per process: the attribute holds for every device
   if (!attr_done) {
@@ -1118,11 +1123,13 @@ static hipError_t launch_g_ks(const void *q, const void *dout, const void *dsT, 
 }
 
 // Queries [t0, t0 + Tc): dq of those queries; s dS and P [Tc, k, H] bf16; then
-// the pair gradients G [Tc, k, 576] fp32.  H a multiple of 32, at most 128.
+// the pair gradients G [Tc, k, 576] (fp32 sums rounded to bf16).  H a multiple
+// of 32, at most 128.
 hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                 const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0,
-                                int32_t Tc, float *dq, void *dsT, void *pT, float *G, hipStream_t s) {
+                                int32_t Tc, float *dq, void *dsT, void *pT, void *Gv, hipStream_t s) {
   if (Tc <= 0) return hipSuccess;
+  __bf16 *G = (__bf16 *)Gv;
   hipError_t e = H % 64 == 0 ? launch_ds_nw<4>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s)
                              : launch_ds_nw<2>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s);
   if (e != hipSuccess) return e;

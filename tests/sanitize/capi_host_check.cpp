@@ -255,6 +255,16 @@ hipError_t launch_scatter_build(const int32_t *idx, int64_t npairs, int64_t N, i
   touch(list, (size_t)npairs * 4);
   return hipSuccess;
 }
+hipError_t launch_scatter_add_bf16(const int32_t *start, const int32_t *list, int64_t N, const void *X, int32_t W,
+                                   float *Y, hipStream_t) {
+  ++g_launches;
+  EXPECT(W % 2 == 0 && W <= 768);
+  read_all(start, (size_t)(N + 1) * 4);
+  (void)list;
+  (void)X;
+  touch(Y, (size_t)N * W * 4);
+  return hipSuccess;
+}
 hipError_t launch_scatter_add(const int32_t *start, const int32_t *list, int64_t N, const float *X, int32_t W, float *Y,
                               hipStream_t) {
   ++g_launches;
@@ -278,7 +288,7 @@ hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, f
 }
 hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                 const float *D, int64_t N, int32_t H, int32_t k, float, int64_t t0, int32_t Tc,
-                                float *dq, void *dsT, void *pT, float *G, hipStream_t) {
+                                float *dq, void *dsT, void *pT, void *G, hipStream_t) {
   ++g_launches;
   EXPECT(H % 32 == 0 && H <= 128);
   read_all((const char *)q + t0 * H * 576 * 2, (size_t)Tc * H * 576 * 2);
@@ -290,7 +300,7 @@ hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *id
   touch(dq + t0 * H * 576, (size_t)Tc * H * 576 * 4);
   touch(dsT, (size_t)Tc * k * H * 2);
   touch(pT, (size_t)Tc * k * H * 2);
-  touch(G, (size_t)Tc * k * 576 * 4);
+  touch(G, (size_t)Tc * k * 576 * 2);
   return hipSuccess;
 }
 // the static scratch: a host buffer of the same size, so a request carved past it overflows

@@ -233,8 +233,9 @@ def test_indexer_kl_backward_after_prefill_selection(dsa, ora):
 # dS and P enter the products rounded to bf16 (unit roundoff 2^-8 each), and
 # D = dout . o uses the forward's bf16 output; the oracle's magnitudes carry
 # the matching terms (|dS| + P sum|dout||o|, and P |dout|), so the error is
-# within 2^-8 of them per rounding: 3 * 2^-8 mag covers the two roundings a
-# term meets plus the fp32 sums.
+# within 2^-8 of them per rounding.  A dkv term also meets the bf16 rounding
+# of its pair's sum over the heads (at most 2^-9 of that sum's magnitude), so
+# 3 * 2^-8 mag covers the roundings a term meets plus the fp32 sums.
 MLA_BWD_RTOL = 3 * 2.0 ** -8
 
 
