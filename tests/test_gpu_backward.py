@@ -150,6 +150,35 @@ def test_indexer_bwd_from_score_gradient(dsa, ora, T, S, k, causal):
     assert torch.all(dk.cpu()[torch.from_numpy(~chosen)] == 0)
 
 
+def test_indexer_bwd_row_past_the_sort(dsa, ora):
+    """Every query lists key 7 eight times: 8192 pairs of one key in the first
+    chunk of 1024 queries, more than the reduce sorts in LDS (4096), so that
+    key is summed in arrival order; the rest as usual."""
+    T, S, k = 1100, 500, 64
+    _say(f"indexer backward, a key listed past the sort capacity T={T} S={S} k={k}")
+    q, kk, w = _indexer_inputs(45, T, S)
+    q8, qs = ora.quantize_rows(q.view(T, -1).numpy())
+    k8, ks = ora.quantize_rows(kk.numpy())
+    q8 = q8.reshape(T, 64, 128)
+    idx = _selection(45, T, S, k)
+    idx[:, :8] = 7
+    g = synth.normal(45, 5, (T, k), std=1e-2)
+    d = {n: torch.from_numpy(np.ascontiguousarray(x)).to(DEV) if isinstance(x, np.ndarray) else x.to(DEV)
+         for n, x in dict(q8=q8, qs=qs, k8=k8, ks=ks, w=w, idx=idx, g=g).items()}
+    dw, dq, dk = (torch.empty((T, 64), device=DEV), torch.empty((T, 64, 128), device=DEV),
+                  torch.empty((S, 128), device=DEV))
+    ws = torch.empty(dsa.dsa_indexer_bwd_workspace_bytes(T, S, k), dtype=torch.uint8, device=DEV)
+    dsa.dsa_indexer_bwd(d["q8"], d["qs"], d["k8"], d["ks"], d["w"], d["idx"], d["g"], dw, dq, dk, ws)
+    torch.cuda.synchronize()
+    r = ora.indexer_bwd(q8, k8, w.double().numpy(), idx.numpy(), g.double().numpy(), q_scale=qs, k_scale=ks,
+                        kink_rel=FP8_MFMA_SUM_REL)
+    # key 7's dk sums up to 8 T pairs, so the fp32 term count grows accordingly
+    f = (k + 64 + 8 * T + 8) * U
+    _check("dw", dw.cpu().numpy(), r["dw"], f * r["mag_dw"] + 1e-30)
+    _check("dq", dq.cpu().numpy(), r["dq"], (f + SPLIT) * r["mag_dq"] + r["amb_dq"] + 1e-30)
+    _check("dk", dk.cpu().numpy(), r["dk"], (f + SPLIT) * r["mag_dk"] + r["amb_dk"] + 1e-30)
+
+
 def test_indexer_bwd_is_deterministic(dsa):
     """The dk reduce sums each key's pairs in a fixed order: two runs agree bit for bit."""
     T, S, k = 700, 2000, 512
@@ -275,6 +304,25 @@ def test_sparse_mla_bwd(dsa, ora, T, H, N, k, qstd):
     _check("dq", dq, r["dq"], MLA_BWD_RTOL * r["mag_dq"] + 1e-30)
     _check("dkv", dkv, r["dkv"], MLA_BWD_RTOL * r["mag_dkv"] + 1e-30)
     assert np.all(dkv[N - 1] == 0) and np.all(dq[2] == 0)
+
+
+def test_sparse_mla_bwd_row_past_the_sort(dsa, ora):
+    """Every query lists latent row 7 ten times: 5120 pairs of one row in the
+    first chunk of 512 queries, more than the reduce sorts in LDS (4096), so
+    that row is summed in arrival order (and the forward weighs the row ten
+    times); the rest as usual."""
+    T, H, N, k = 600, 32, 500, 64
+    _say(f"sparse mla backward, a row listed past the sort capacity T={T} H={H} N={N} k={k}")
+    sm = 1 / math.sqrt(192)
+    q = synth.normal(54, 1, (T, H, 576)).to(torch.bfloat16)
+    kv = synth.normal(54, 2, (N, 576), std=1 / 24).to(torch.bfloat16)
+    dout = synth.normal(54, 3, (T, H, 512)).to(torch.bfloat16)
+    idx = _selection(54, T, N, k)
+    idx[:, :10] = 7
+    dq, dkv = _mla_bwd_gpu(dsa, q, kv, idx, dout, sm)
+    r = ora.sparse_mla_bwd(q, kv, idx.numpy(), dout, sm)
+    _check("dq", dq, r["dq"], MLA_BWD_RTOL * r["mag_dq"] + 1e-30)
+    _check("dkv", dkv, r["dkv"], MLA_BWD_RTOL * r["mag_dkv"] + 1e-30)
 
 
 def test_sparse_mla_bwd_is_deterministic(dsa):
