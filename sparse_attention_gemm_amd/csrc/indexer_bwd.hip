@@ -175,8 +175,6 @@ __global__ __launch_bounds__(256, 2) void indexer_bwd_kernel(const uint8_t *__re
 
   const int ntile = (k + kTile - 1) / kTile;
   // u rows of this query as a bounded buffer: stores of entries >= k are dropped
-  const __amdgpu_buffer_rsrc_t ur =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(u + tc * k * kDI), 0, k * kDI * 4, (int)kRsrcWord3);
   f32x4 dqa[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) dqa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -222,7 +220,10 @@ __global__ __launch_bounds__(256, 2) void indexer_bwd_kernel(const uint8_t *__re
         dqa[i] = mfma_bf16_16x16x32(ml[s], b, dqa[i]);
       }
     const float usc = sm.ga[16 * wave + c] * qsv;  // scale of this lane's u column (key 16 wave + c)
-    __syncthreads();  // nc is complete; the tile's key rows and coefficients are no longer read
+    // nc is complete; the tile's key rows and coefficients are no longer read.
+    // LDS only: the previous tile's u stores and the prefetched rows stay in
+    // flight (put() waits for its own registers).
+    lds_barrier();
     if (j + 1 < ntile) {
       put(a0 + kTile);
       if (j + 2 < ntile) fetch(a0 + 2 * kTile);
@@ -244,10 +245,14 @@ __global__ __launch_bounds__(256, 2) void indexer_bwd_kernel(const uint8_t *__re
       }
     }
     const int off = ((a0 + 16 * wave + c) * kDI + 4 * g) * 4;
+    // built here from scalar values, so the descriptor stays in SGPRs (one
+    // held across the loop was kept in VGPRs and each store became a loop)
+    const __amdgpu_buffer_rsrc_t ur =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(u + tc * k * kDI), 0, k * kDI * 4, (int)kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, ua[i] * usc), ur, off + 64 * i, 0, kCpolNT);
-    __syncthreads();  // nc is no longer read; the next tile's rows are in LDS
+    lds_barrier();  // nc is no longer read; the next tile's rows are in LDS (the u stores stay in flight)
   }
   // dq of heads 16 wave + 4 g + r
   float *dqrow = dq + (t * kHI + 16 * wave + 4 * g) * kDI + c;

@@ -1048,7 +1048,10 @@ __global__ __launch_bounds__(kGThreads, 1) void mla_bwd_g_kernel(const __bf16 *_
         }
       }
     }
-    __syncthreads();
+    // Only the key blocks in LDS need ordering: the loaders waited for their
+    // own block above, and nothing here reads G, so the G stores stay in
+    // flight across the barrier (a full __syncthreads would wait for them).
+    lds_barrier();
   }
 }
 
