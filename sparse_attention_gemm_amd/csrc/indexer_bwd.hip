@@ -17,7 +17,7 @@
 // indexer_bwd_kernel: one workgroup of four waves per query, 64 entries per
 // tile; wave w owns heads 16 w .. 16 w + 15.  Per tile:
 //  * x^T (keys x the wave's heads) = K8 Q8^T on the FP8 MFMA, exactly as in
-//    the forward (E4M3 x E4M3 products, fp32 sums); the lane holding x for
+//    the forward (E4M3 x E4M3 products, the matrix core's fp32 sum); the lane holding x for
 //    head c and keys 4 g + r (+16 n) forms the coefficients
 //    mc = g ks w [x > 0] and nc = w [x > 0] and its dw partial;
 //  * dq (the wave's heads x 128 dims) += MC KF on the bf16 MFMA: the E4M3

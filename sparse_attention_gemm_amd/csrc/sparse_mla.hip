@@ -888,15 +888,16 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
 //    (dims 16 i + c, heads 32 s + 8 g .. +8) in registers;
 //  * key loop, blocks of 64 keys in three LDS buffers: while the compute
 //    waves work on block j, the loader waves fetch block j + 2 straight into
-//    LDS and wait only until block j + 1 has landed; one barrier a block.  The
-//    compute waves issue only stores, so nothing ever makes them wait for
-//    memory (loads and stores share one completion counter, and a wait for a
-//    load would also wait for every store issued before it);
-//  * each lane ends a 16 x 16 tile with dims 4 g .. 4 g + 3 of one key, a
-//    16-byte run of that key's G row, stored through a buffer bounded to the
-//    query's rows, which drops the stores of keys >= k.  (A streaming cache
-//    hint on these stores measured slower: plain 16-byte stores stream at
-//    4.6 TB/s on MI355X, streaming-hinted ones at 4.4.)
+//    LDS and wait only until block j + 1 has landed; one LDS-only barrier a
+//    block.  The compute waves issue only stores, so nothing ever makes them
+//    wait for memory (loads and stores share one completion counter, and a
+//    wait for a load would also wait for every store issued before it; a full
+//    __syncthreads would too);
+//  * each lane ends a 16 x 16 tile with dims 4 g .. 4 g + 3 of one key, rounds
+//    them to bf16 and stores that 8-byte run of the key's G row through a
+//    buffer bounded to the query's rows, which drops the stores of keys >= k.
+//    (A streaming cache hint on fp32 G stores measured slower: plain 16-byte
+//    stores stream at 4.6 TB/s on MI355X, streaming-hinted ones at 4.4.)
 constexpr int kGWaves = 12;                   // compute waves
 constexpr int kGLoaders = 4;                  // loader waves
 constexpr int kGThreads = (kGWaves + kGLoaders) * 64;
