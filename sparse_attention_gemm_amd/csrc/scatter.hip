@@ -38,30 +38,71 @@ __global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t *__res
 }
 
 // start[0..N] = exclusive prefix sum of cnt[0..N); one workgroup of 1024
-// threads, each summing a contiguous run of the array.
+// threads over pages of 16384 entries.  Thread t owns the 16 consecutive
+// entries 16 t .. 16 t + 15 of a page: it loads them as four 16-byte vectors
+// (scalar loads only in a ragged last page), scans them in registers, and a
+// wave scan plus one cross-wave step give every run its offset.  (Scalar
+// accesses throughout if cnt or start is not 16-byte aligned.)
 __global__ __launch_bounds__(1024) void scatter_scan_kernel(const int32_t *__restrict__ cnt, int64_t N,
                                                             int32_t *__restrict__ start) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (N + 1023) / 1024;
-  const int64_t b = tid * per, e = min(N, b + per);
-  int32_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += cnt[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the 1024 run sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = tid >= off ? part[tid - off] : 0;
+  constexpr int kRun = 16;
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool vec = ((reinterpret_cast<uintptr_t>(cnt) | reinterpret_cast<uintptr_t>(start)) & 15) == 0;
+  int32_t carry = 0;  // total of the pages before this one
+  for (int64_t p0 = 0; p0 < N; p0 += (int64_t)kRun * 1024) {
+    const int64_t b = p0 + (int64_t)kRun * tid;
+    const bool whole = vec && b + kRun <= N;
+    int32_t v[kRun];
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < kRun / 4; ++q) {
+        const i32x4 x = *reinterpret_cast<const i32x4 *>(cnt + b + 4 * q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * q + j] = x[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRun; ++j) v[j] = b + j < N ? cnt[b + j] : 0;
+    }
+    int32_t inc[kRun];  // inclusive prefix within the run
+    inc[0] = v[0];
+#pragma unroll
+    for (int j = 1; j < kRun; ++j) inc[j] = inc[j - 1] + v[j];
+    const int32_t s = inc[kRun - 1];
+    int32_t ws = s;  // inclusive scan of the run totals within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t x = __shfl_up(ws, o);
+      if (lane >= o) ws += x;
+    }
+    if (lane == 63) wsum[wave] = ws;
     __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+    int32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int32_t x = wsum[w];
+      before += w < wave ? x : 0;
+      total += x;
+    }
+    __syncthreads();  // wsum is rewritten for the next page
+    const int32_t excl = carry + before + ws - s;  // entries before this run
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < kRun / 4; ++q) {
+        i32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = excl + inc[4 * q + j] - v[4 * q + j];
+        *reinterpret_cast<i32x4 *>(start + b + 4 * q) = o;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRun; ++j)
+        if (b + j < N) start[b + j] = excl + inc[j] - v[j];
+    }
+    carry += total;
   }
-  int32_t run = part[tid] - s;  // exclusive prefix of this run
-  for (int64_t i = b; i < e; ++i) {
-    start[i] = run;
-    run += cnt[i];
-  }
-  if (tid == 1023) start[N] = part[1023];
+  if (tid == 0) start[N] = carry;
 }
 
 __global__ __launch_bounds__(256) void scatter_fill_kernel(const int32_t *__restrict__ idx, int64_t npairs, int64_t N,

@@ -115,10 +115,12 @@ def _indexer_inputs(seed, T, S):
     return q, kk, w
 
 
-@pytest.mark.parametrize("T,S,k,causal", [(40, 3000, 2048, False), (300, 300, 256, True), (1100, 2500, 64, False)])
+@pytest.mark.parametrize("T,S,k,causal", [(40, 3000, 2048, False), (300, 300, 256, True), (1100, 2500, 64, False),
+                                          (24, 40000, 2048, False)])
 def test_indexer_bwd_from_score_gradient(dsa, ora, T, S, k, causal):
     """dw, dq, dk from a given score gradient; T = 1100 spans two query chunks
-    of the inverted-selection reduce."""
+    of the inverted-selection reduce; S = 40000 keys take three pages of its
+    prefix scan."""
     _say(f"indexer backward T={T} S={S} k={k} causal={causal}")
     q, kk, w = _indexer_inputs(43, T, S)
     q8, qs = ora.quantize_rows(q.view(T, -1).numpy())
@@ -284,11 +286,13 @@ def _mla_bwd_gpu(dsa, q, kv, idx, dout, sm):
 
 
 @pytest.mark.parametrize("T,H,N,k,qstd", [(6, 128, 5000, 2048, 1.0), (600, 64, 3000, 256, 1.0),
-                                          (9, 32, 2000, 100, 40.0), (5, 96, 1500, 512, 3.0)])
+                                          (9, 32, 2000, 100, 40.0), (5, 96, 1500, 512, 3.0),
+                                          (6, 32, 40000, 2048, 1.0)])
 def test_sparse_mla_bwd(dsa, ora, T, H, N, k, qstd):
     """dq and dkv against the oracle; T = 600 spans two query chunks; a sharp
-    softmax (q x 40); a ragged, an empty and a duplicated entry, and an entry
-    outside the latent rows."""
+    softmax (q x 40); N = 40000 rows take three pages of the reduce's prefix
+    scan; a ragged, an empty and a duplicated entry, and an entry outside the
+    latent rows."""
     _say(f"sparse mla backward T={T} H={H} N={N} k={k} qstd={qstd}")
     sm = 1 / math.sqrt(192)
     q = synth.normal(51, 1, (T, H, 576), std=qstd).to(torch.bfloat16)
