@@ -167,7 +167,7 @@ dsa_status dsa_sparse_mla_fwd(const void *q, const void *kv, dsa_dtype dt, const
  *   q [T,H,576], kv [N,576], out [T,H,512], dout [T,H,512] BF16; idx [T,k];
  *   lse [T,H] fp32 (the forward's); dq [T,H,576], dkv [N,576] fp32 out, fully
  *   overwritten.
- * bf16 MFMA with fp32 sums; dS and P enter the products rounded to bf16, and
+ * bf16 MFMA with fp32 sums; sm_scale dS and P enter the products rounded to bf16, and
  * dout . o uses the forward's bf16 output.  Each pair's contribution to dkv
  * (its sum over the heads) is rounded to bf16 once; dkv is summed in fp32 per
  * row over its pairs in increasing (t, a) order (an inverted selection, no

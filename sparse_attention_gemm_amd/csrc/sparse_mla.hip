@@ -600,12 +600,12 @@ hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, con
 //   dkv[r_a] += s dS_a q + P_a dO        (value dims get the second term)
 // Three kernels per chunk of queries, then the inverted-selection reduce:
 //  * mla_bwd_delta_kernel: D[t,h] = dO . o (o: the forward's output);
-//  * mla_bwd_ds_kernel: per (query, 16*NW heads), the forward's gather and
+//  * mla_bwd_ds_kernel: per (query, 16*HT heads), the forward's gather and
 //    logits, and dP with dO^T resident (one LDS read of each tile fragment
-//    feeds both), then dq^T += C^T dS^T (the transposing
-//    LDS read of the forward's PV, over all 576 dims, with the wave's own dS
-//    as the B operand); s dS and P go to the workspace key-major [pair][head]
-//    in bf16;
+//    feeds both), each wave on one head tile and half of each tile's keys;
+//    s dS and P are staged in LDS, and dq^T += C^T (s dS)^T (the transposing
+//    LDS read of the forward's PV) is split over the waves by latent dims;
+//    s dS and P go to the workspace key-major [pair][head] in bf16;
 //  * mla_bwd_g_kernel: per query, the pair gradients G[pair, :] =
 //    (s dS)^T q + P^T dO, a GEMM over the heads (K = heads, bf16 MFMA, fp32
 //    sums, stored rounded to bf16) with q^T and dO^T resident in registers and
@@ -628,43 +628,27 @@ __global__ __launch_bounds__(256) void mla_bwd_delta_kernel(const __bf16 *__rest
   if (lane == 0) D[th] = acc;
 }
 
-// S^T-layout dot products of a gathered tile with the resident Q^T (all 576
-// dims) and dO^T (the 512 value dims) of a head: lane (g, c) gets x[r] /
-// dp[r] = key 4g+r and x[4+r] / dp[4+r] = key 16+4g+r of head c (no
-// masking).  Each tile fragment is read from LDS once for both products.
-__device__ __forceinline__ void tile_dot_pair(const uint8_t *__restrict__ ct, const bf16x8 (&bq)[18],
-                                              const bf16x8 (&bo)[16], int g, int c, float (&x)[8], float (&dp)[8]) {
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-  const uint8_t *arow0 = ct + c * kCRow + g * 16;
-  const uint8_t *arow1 = arow0 + 16 * kCRow;
-  bf16x8 op[3][2];  // operands of steps s, s+1 and s+2 in flight
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    op[s][0] = *reinterpret_cast<const bf16x8 *>(arow0 + s * 64);
-    op[s][1] = *reinterpret_cast<const bf16x8 *>(arow1 + s * 64);
-  }
+// S^T-layout dot products of one 16-key half (keys 16 kb .. +16) of a
+// gathered tile with the resident Q^T (all 576 dims) and dO^T (the 512 value
+// dims) of a head tile: lane (g, c) gets x[r] / dp[r] = key 16 kb + 4 g + r of
+// head c (no masking).  Each tile fragment is read from LDS once for both
+// products; the operands of the next step are in flight.
+__device__ __forceinline__ void half_tile_dot_pair(const uint8_t *__restrict__ ct, const bf16x8 (&bq)[18],
+                                                   const bf16x8 (&bo)[16], int kb, int g, int c, f32x4 &x,
+                                                   f32x4 &dp) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, d0 = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t *arow = ct + (16 * kb + c) * kCRow + g * 16;
+  bf16x8 op[3];
+  op[0] = *reinterpret_cast<const bf16x8 *>(arow);
+  op[1] = *reinterpret_cast<const bf16x8 *>(arow + 64);
 #pragma unroll
   for (int s = 0; s < 18; ++s) {
-    const int cs = s % 3;
-    if (s + 2 < 18) {
-      op[(s + 2) % 3][0] = *reinterpret_cast<const bf16x8 *>(arow0 + (s + 2) * 64);
-      op[(s + 2) % 3][1] = *reinterpret_cast<const bf16x8 *>(arow1 + (s + 2) * 64);
-    }
-    s0 = mfma_bf16_16x16x32(op[cs][0], bq[s], s0);
-    s1 = mfma_bf16_16x16x32(op[cs][1], bq[s], s1);
-    if (s < 16) {
-      d0 = mfma_bf16_16x16x32(op[cs][0], bo[s], d0);
-      d1 = mfma_bf16_16x16x32(op[cs][1], bo[s], d1);
-    }
+    if (s + 2 < 18) op[(s + 2) % 3] = *reinterpret_cast<const bf16x8 *>(arow + (s + 2) * 64);
+    s0 = mfma_bf16_16x16x32(op[s % 3], bq[s], s0);
+    if (s < 16) d0 = mfma_bf16_16x16x32(op[s % 3], bo[s], d0);
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    x[r] = s0[r];
-    x[4 + r] = s1[r];
-    dp[r] = d0[r];
-    dp[4 + r] = d1[r];
-  }
+  x = s0;
+  dp = d0;
 }
 
 // LDS byte address of a shared-memory pointer.
@@ -677,6 +661,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // otherwise wait for every outstanding gather (the next tiles') before each
 // of them; the buffers they read were completed by an explicit wait and a
 // barrier.  Reads a[n] at base + OFF[n].
+#define DSA_TR_READ2(a, base, o0, o1)                                                             \
+  asm volatile(                                                                                   \
+      "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"                                                   \
+      "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"                                                   \
+      "s_waitcnt lgkmcnt(0)"                                                                      \
+      : "=&v"(a[0]), "=&v"(a[1])                                                                  \
+      : "v"(base), "i"(o0), "i"(o1)                                                               \
+      : "memory")
+
 #define DSA_TR_READ4(a, base, o0, o1, o2, o3)                                                     \
   asm volatile(                                                                                   \
       "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"                                                   \
@@ -688,77 +681,56 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       : "v"(base), "i"(o0), "i"(o1), "i"(o2), "i"(o3)                                             \
       : "memory")
 
-#define DSA_TR_READ12(a, base, o0, o1, o2, o3, o4, o5, o6, o7, o8, o9, o10, o11)                       \
-  asm volatile(                                                                                    \
-      "ds_read_b64_tr_b16 %0, %12 offset:%13\n\t"                                                  \
-      "ds_read_b64_tr_b16 %1, %12 offset:%14\n\t"                                                  \
-      "ds_read_b64_tr_b16 %2, %12 offset:%15\n\t"                                                  \
-      "ds_read_b64_tr_b16 %3, %12 offset:%16\n\t"                                                  \
-      "ds_read_b64_tr_b16 %4, %12 offset:%17\n\t"                                                  \
-      "ds_read_b64_tr_b16 %5, %12 offset:%18\n\t"                                                  \
-      "ds_read_b64_tr_b16 %6, %12 offset:%19\n\t"                                                  \
-      "ds_read_b64_tr_b16 %7, %12 offset:%20\n\t"                                                  \
-      "ds_read_b64_tr_b16 %8, %12 offset:%21\n\t"                                                  \
-      "ds_read_b64_tr_b16 %9, %12 offset:%22\n\t"                                                  \
-      "ds_read_b64_tr_b16 %10, %12 offset:%23\n\t"                                                 \
-      "ds_read_b64_tr_b16 %11, %12 offset:%24\n\t"                                                 \
-      "s_waitcnt lgkmcnt(0)"                                                                       \
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), \
-        "=&v"(a[7]), "=&v"(a[8]), "=&v"(a[9]), "=&v"(a[10]), "=&v"(a[11])                           \
-      : "v"(base), "i"(o0), "i"(o1), "i"(o2), "i"(o3), "i"(o4), "i"(o5), "i"(o6), "i"(o7), "i"(o8), \
-        "i"(o9), "i"(o10), "i"(o11)                                                                \
-      : "memory")
-
-// The A operands of dq^T tiles I .. I+5 (dims 16 i .. +16, the tile's 32 keys)
-// through the transposing read: rows 4 g + (c >> 2) (+16), columns 16 i + 4 (c & 3).
-template <int I>
-__device__ __forceinline__ void dq_operands6(uint32_t base, bf16x8 (&op)[6]) {
-  constexpr int h = 16 * kCRow;
-  i16x4 r[12];
-  DSA_TR_READ12(r, base, I * 32, I * 32 + h, (I + 1) * 32, (I + 1) * 32 + h, (I + 2) * 32, (I + 2) * 32 + h,
-                (I + 3) * 32, (I + 3) * 32 + h, (I + 4) * 32, (I + 4) * 32 + h, (I + 5) * 32, (I + 5) * 32 + h);
-#pragma unroll
-  for (int n = 0; n < 6; ++n) {
-    const i16x4 a[2] = {r[2 * n], r[2 * n + 1]};
-    op[n] = *reinterpret_cast<const bf16x8 *>(a);
-  }
-}
-
-constexpr int kBwdNBuf = 3;  // gathered tiles: computed, landed, in flight
+constexpr int kBwdNBuf = 3;  // gathered tiles: dq, logits, in flight
 constexpr int kStageRow = 2 * kBN + 8;  // LDS bytes per head row of staged s dS or P (32 keys + pad):
                                         // 18 dwords keeps both the 8-byte writes and the
                                         // transposing reads conflict-free
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
-// LDS of the dS kernel: two gathered tiles, the resolved rows of the query's
-// entries, and two buffers of staged s dS and P (16 NW heads x 32 keys each)
-template <int NW>
+// LDS of the dS kernel: three gathered tiles, the resolved rows of the query's
+// entries, and two buffers of staged s dS and P (16 HT heads x 32 keys each)
+template <int HT>
 constexpr int smem_bwd_bytes() {
-  return kBwdNBuf * kTileBytes + 2048 * 4 + 2 * 2 * 16 * NW * kStageRow;
+  return kBwdNBuf * kTileBytes + 2048 * 4 + 2 * 2 * 16 * HT * kStageRow;
 }
 
-// One workgroup of NW waves per (query t0 + blockIdx.x, head group blockIdx.y
-// of 16 NW heads); wave w owns heads 16 w .. +16 of the group.  The tile's
-// s dS and P go to LDS head-major and leave one tile later as 16-byte runs of
-// the key-major workspace rows, so the only vector-memory operations a tile
-// waits for are its own gathers (loads and stores complete in issue order).
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
+// One workgroup of 2 HT waves per (query t0 + blockIdx.x, head group
+// blockIdx.y of 16 HT heads).  Two roles per wave, pipelined across tiles
+// with one barrier per tile:
+//  * logits and dP: wave w owns head tile w % HT and keys 16 (w / HT) .. +16
+//    of each tile, with that head tile's Q^T and dO^T resident; it forms P and
+//    dS and stages s dS and P head-major in LDS (bf16);
+//  * dq^T[dims, heads] += C^T[dims, keys] (s dS)^T[keys, heads] over the
+//    staged s dS of every head tile: wave w owns the value-dim tiles
+//    w + 2 HT m (all HT head tiles) and two (rope-dim tile, head tile) pairs,
+//    18 accumulator tiles for every HT, so each dim of the gathered tile is
+//    read once per workgroup for dq.
+// Iteration j: barrier; gather tile j+2; tile j's staged values leave for the
+// key-major workspace rows as 16-byte runs; logits and dP of tile j+1; dq of
+// tile j.  The only vector-memory operations a tile waits for are its own
+// gathers (loads and stores complete in issue order).
+template <int HT>
+__global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const float *__restrict__ Dd, int64_t N, int H,
     int k, float sm_scale, int64_t t0, float *__restrict__ dq, __bf16 *__restrict__ dsT, __bf16 *__restrict__ pT) {
-  constexpr int kHeads = 16 * NW;
+  constexpr int NW = 2 * HT;
+  constexpr int kHeads = 16 * HT;
   constexpr int kStageBuf = 2 * kHeads * kStageRow;  // s dS rows, then P rows
+  constexpr int DT = 32 / NW;                         // value-dim tiles per wave
+  static_assert(DT <= 8 && DT * HT == 16, "16 value-dim accumulator tiles per wave");
   extern __shared__ __align__(16) uint8_t smem_raw[];
   uint8_t *tiles = smem_raw;
   int *rows = reinterpret_cast<int *>(smem_raw + kBwdNBuf * kTileBytes);
   uint8_t *stage = smem_raw + kBwdNBuf * kTileBytes + 2048 * 4;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ht = wave % HT, kb = wave / HT;  // uniform
   const int64_t tc = blockIdx.x, t = t0 + tc;
-  const int head = blockIdx.y * kHeads + 16 * wave + c;  // this lane's head
+  const int hbase = blockIdx.y * kHeads;
+  const int head = hbase + 16 * ht + c;  // this lane's head for the logits
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const int ntiles = (k + kBN - 1) / kBN;
-  // Q^T and dO^T of the wave's heads (B operands: lane (g, c) holds head c, dims 32 s + 8 g .. +8)
+  // Q^T and dO^T of the wave's head tile (B operands: lane (g, c) holds head c, dims 32 s + 8 g .. +8)
   bf16x8 qr[18], gr[16];
   const __bf16 *qrow = q + (t * H + head) * 576 + g * 8;
   const __bf16 *grow = dout + (t * H + head) * 512 + g * 8;
@@ -770,23 +742,36 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
   const float Dh = Dd[t * H + head];
   const int32_t *irow = idx + t * k;
   for (int e = tid; e < ntiles * kBN; e += NW * 64) rows[e] = (int)phys_row(irow, nullptr, 0, N, t, e, k);
-  // dq^T accumulators: dims 16 i + 4 g + r of head c
-  f32x4 acc[36];
+  // dq^T accumulators: acc[m HT + n] = value-dim tile wave + NW m, head tile n;
+  // acc[16], acc[17] = rope-dim tile 32 + 2 wave / HT, head tiles n0, n0 + 1.
+  // Lane (g, c) holds dims 16 i + 4 g .. +4 of head 16 n + c.
+  const int n0 = (2 * wave) % HT;                  // uniform
+  const int irope = 32 + (2 * wave) / HT;          // uniform
+  f32x4 acc[18];
 #pragma unroll
-  for (int i = 0; i < 36; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int tr_base = (4 * g + (c >> 2)) * kCRow + (c & 3) * 8;
+  for (int i = 0; i < 18; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Lane roles are recomputed in each phase from a laundered lane id:
+  // hoisted out of the tile loop, the per-step LDS addresses they feed would
+  // hold a dozen registers for the whole kernel.
+  auto laundered = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
   // The query's s dS and P rows as bounded buffers: stores of entries >= k are dropped.
   const __amdgpu_buffer_rsrc_t rds =
       __builtin_amdgcn_make_buffer_rsrc((void *)(dsT + tc * k * H), 0, k * H * 2, (int)kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rp =
       __builtin_amdgcn_make_buffer_rsrc((void *)(pT + tc * k * H), 0, k * H * 2, (int)kRsrcWord3);
-  // Write-out roles: lane group tid / 16 takes key 16 (group & 1) + c and the
-  // group's 8 heads 8 (group >> 1) .. +8, read from the head-major staging
-  // with the transposing load (lane c of a group gets column c of a 4 x 16 block).
-  const int grp = tid >> 4, okey = 16 * (grp & 1) + c, oh = 8 * (grp >> 1);
-  const int tr_stage = (oh + (c >> 2)) * kStageRow + (16 * (grp & 1) + 4 * (c & 3)) * 2;
-  const int ooff = (okey * H + blockIdx.y * kHeads + oh) * 2;  // bytes, within a tile's rows
+  // Write-out roles (waves 0 .. HT-1): lane group tid / 16 takes key
+  // 16 (group & 1) + c and the group's 8 heads 8 (group >> 1) .. +8, read from
+  // the head-major staging with the transposing load (lane c of a group gets
+  // column c of a 4 x 16 block).
   auto write_out = [&](int jt) {  // tile jt's staged values to the workspace
+    const int l = laundered(), lc = l & 15;
+    const int grp = 4 * wave + (l >> 4), okey = 16 * (grp & 1) + lc, oh = 8 * (grp >> 1);
+    const int tr_stage = (oh + (lc >> 2)) * kStageRow + (16 * (grp & 1) + 4 * (lc & 3)) * 2;
+    const int ooff = (okey * H + hbase + oh) * 2;  // bytes, within a tile's rows
     const uint8_t *sb = stage + (jt & 1) * kStageBuf;
     i16x4 r[4];
     DSA_TR_READ4(r, lds_addr(sb + tr_stage), 0, 4 * kStageRow, kHeads * kStageRow, kHeads * kStageRow + 4 * kStageRow);
@@ -795,84 +780,107 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(
     __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4 *>(dd), rds, off, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4 *>(pp), rp, off, 0, 0);
   };
+  // logits, P, dS of tile jt for the wave's (head tile, key half); s dS and P to staging buffer jt & 1
+  auto logits_ds = [&](int jt) {
+    const int l = laundered(), lg = l >> 4, lc = l & 15;
+    const uint8_t *ct = tiles + (jt % kBwdNBuf) * kTileBytes;
+    const int *rv = rows + jt * kBN + 16 * kb + 4 * lg;
+    f32x4 x, dp;
+    half_tile_dot_pair(ct, qr, gr, kb, lg, lc, x, dp);
+    bf16x4 sdb, pb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = rv[r] >= 0 ? __builtin_amdgcn_exp2f(fmaf(x[r], scale_log2, -lse2)) : 0.0f;
+      sdb[r] = (__bf16)(sm_scale * (p * (dp[r] - Dh)));
+      pb[r] = (__bf16)p;
+    }
+    // head-major: row 16 ht + c, keys 16 kb + 4 g .. +4
+    uint8_t *sb = stage + (jt & 1) * kStageBuf + (16 * ht + lc) * kStageRow + 32 * kb + 8 * lg;
+    *reinterpret_cast<bf16x4 *>(sb) = sdb;
+    *reinterpret_cast<bf16x4 *>(sb + kHeads * kStageRow) = pb;
+  };
+  // dq^T += C^T (s dS)^T for tile jt, s dS from staging buffer jt & 1
+  auto dq_tile = [&](int jt) {
+    const int l = laundered(), lg = l >> 4, lc = l & 15;
+    const int tr_base = (4 * lg + (lc >> 2)) * kCRow + (lc & 3) * 8;
+    const uint8_t *ct = tiles + (jt % kBwdNBuf) * kTileBytes;
+    const uint8_t *sb = stage + (jt & 1) * kStageBuf;
+    // B operand of head tile n: lane (g, c) holds head 16 n + c, keys
+    // 4 g .. +4 and 16 + 4 g .. +4, the key order of the transposing A reads
+    auto b_operand = [&](int n) {
+      const uint8_t *row = sb + (16 * n + lc) * kStageRow + 8 * lg;
+      const bf16x4 lohi[2] = {*reinterpret_cast<const bf16x4 *>(row), *reinterpret_cast<const bf16x4 *>(row + 32)};
+      return *reinterpret_cast<const bf16x8 *>(lohi);
+    };
+    {  // the rope-dim pairs first, with their own B operands (n0 is uniform, not a constant)
+      const bf16x8 rb0 = b_operand(n0), rb1 = b_operand(n0 + 1);
+      i16x4 r[2];
+      DSA_TR_READ2(r, lds_addr(ct + tr_base + irope * 32), 0, 16 * kCRow);
+      const bf16x8 ar = *reinterpret_cast<const bf16x8 *>(r);
+      acc[16] = mfma_bf16_16x16x32(ar, rb0, acc[16]);
+      acc[17] = mfma_bf16_16x16x32(ar, rb1, acc[17]);
+    }
+    bf16x8 bs[HT];
+#pragma unroll
+    for (int n = 0; n < HT; ++n) bs[n] = b_operand(n);
+    const uint32_t trw = lds_addr(ct + tr_base + wave * 32);  // value-dim tile `wave`
+#pragma unroll
+    for (int m = 0; m < DT; ++m) {
+      // A operand of value-dim tile wave + NW m
+      i16x4 r[2];
+      switch (m) {
+        case 0: DSA_TR_READ2(r, trw, 0, 16 * kCRow); break;
+        case 1: DSA_TR_READ2(r, trw, NW * 32, NW * 32 + 16 * kCRow); break;
+        case 2: DSA_TR_READ2(r, trw, 2 * NW * 32, 2 * NW * 32 + 16 * kCRow); break;
+        case 3: DSA_TR_READ2(r, trw, 3 * NW * 32, 3 * NW * 32 + 16 * kCRow); break;
+        case 4: DSA_TR_READ2(r, trw, 4 * NW * 32, 4 * NW * 32 + 16 * kCRow); break;
+        case 5: DSA_TR_READ2(r, trw, 5 * NW * 32, 5 * NW * 32 + 16 * kCRow); break;
+        case 6: DSA_TR_READ2(r, trw, 6 * NW * 32, 6 * NW * 32 + 16 * kCRow); break;
+        default: DSA_TR_READ2(r, trw, 7 * NW * 32, 7 * NW * 32 + 16 * kCRow); break;
+      }
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(r);
+#pragma unroll
+      for (int n = 0; n < HT; ++n) acc[m * HT + n] = mfma_bf16_16x16x32(a, bs[n], acc[m * HT + n]);
+    }
+  };
   // gather instructions a wave issues per tile (the fewest, over the waves)
   constexpr int kGatherMin = kGatherInsts / NW;
   __syncthreads();
   if (ntiles > 0) gather_tile_async<NW>(tiles, rows, 0, kv, wave, lane);
   if (ntiles > 1) gather_tile_async<NW>(tiles + kTileBytes, rows, kBN, kv, wave, lane);
+  if (ntiles > 0) {
+    if (ntiles > 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGatherMin));  // tile 0 landed (tile 1 may be in flight)
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();  // every wave's gathers of tile 0
+    logits_ds(0);
+  }
   for (int j = 0; j < ntiles; ++j) {
-    // This wave's gathers of tile j have landed.  Issued after them, in order:
-    // the stores of tile j-3 (j >= 3), the gathers of tile j+1 (j+1 < ntiles)
-    // and the stores of tile j-2 (j >= 2); waiting until at most that many are
-    // outstanding (counting the fewest gathers any wave issues) leaves them in
-    // flight.
-    {
-      const int ns = (j >= 3 ? 2 : 0) + (j >= 2 ? 2 : 0);  // uniform
-      if (j + 1 < ntiles) {
-        if (ns == 4)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + kGatherMin));
-        else if (ns == 2)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 + kGatherMin));
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGatherMin));
-      } else {
-        if (ns == 4)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-        else if (ns == 2)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
-        else
-          __builtin_amdgcn_s_waitcnt(0);
-      }
+    // This wave's gathers of tile j+1 have landed.  Issued after them: the
+    // stores of tile j-1 (write-out waves, j >= 1).
+    if (j + 1 < ntiles) {
+      if (wave < HT && j >= 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    lds_barrier();  // every wave's; tile j-1's buffer and staging buffer (j-1) & 1 are complete
+    lds_barrier();  // staging j & 1 and tile j+1 complete; tile j-1 and staging (j+1) & 1 no longer read
     if (j + 2 < ntiles)
       gather_tile_async<NW>(tiles + ((j + 2) % kBwdNBuf) * kTileBytes, rows, (j + 2) * kBN, kv, wave, lane);
-    if (j >= 1) write_out(j - 1);
-    const uint8_t *ct = tiles + (j % kBwdNBuf) * kTileBytes;
-    const int *rv = rows + j * kBN;
-    float x[8], dp[8];
-    tile_dot_pair(ct, qr, gr, g, c, x, dp);
-    bf16x8 dsb, sdb, pb;
-    float dsv[8];
+    if (wave < HT) write_out(j);
+    if (j + 1 < ntiles) logits_ds(j + 1);
+    dq_tile(j);
+  }
+  // dq of the wave's accumulator tiles
+  float *dqq = dq + (t * H + hbase + c) * 576 + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);
-      const float p = rv[key] >= 0 ? __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -lse2)) : 0.0f;
-      dsv[i] = p * (dp[i] - Dh);
-      dsb[i] = (__bf16)dsv[i];
-      sdb[i] = (__bf16)(sm_scale * dsv[i]);
-      pb[i] = (__bf16)p;
-    }
-    // s dS and P of the tile, head-major: row 16 wave + c, keys 4 g .. +4 and 16 + 4 g .. +4
-    {
-      uint8_t *sb = stage + (j & 1) * kStageBuf + (16 * wave + c) * kStageRow + 8 * g;
-      const bf16x4 *sd4 = reinterpret_cast<const bf16x4 *>(&sdb);
-      const bf16x4 *p4 = reinterpret_cast<const bf16x4 *>(&pb);
-      *reinterpret_cast<bf16x4 *>(sb) = sd4[0];
-      *reinterpret_cast<bf16x4 *>(sb + 32) = sd4[1];
-      *reinterpret_cast<bf16x4 *>(sb + kHeads * kStageRow) = p4[0];
-      *reinterpret_cast<bf16x4 *>(sb + kHeads * kStageRow + 32) = p4[1];
-    }
-    // dq^T[dims, head] += C^T[dims, keys] dS^T[keys, head]
-    const uint32_t trb = lds_addr(ct + tr_base);
-#define DSA_DQ_SIX(I)                                                                 \
-  {                                                                                   \
-    bf16x8 op[6];                                                                     \
-    dq_operands6<I>(trb, op);                                                         \
-    _Pragma("unroll") for (int n = 0; n < 6; ++n) acc[I + n] = mfma_bf16_16x16x32(op[n], dsb, acc[I + n]); \
-  }
-    DSA_DQ_SIX(0) DSA_DQ_SIX(6) DSA_DQ_SIX(12) DSA_DQ_SIX(18) DSA_DQ_SIX(24) DSA_DQ_SIX(30)
-#undef DSA_DQ_SIX
-  }
-  if (ntiles > 0) {
-    __syncthreads();  // the last tile's staging is complete
-    write_out(ntiles - 1);
-  }
-  float *dqrow = dq + (t * H + head) * 576 + 4 * g;
+  for (int m = 0; m < DT; ++m)
 #pragma unroll
-  for (int i = 0; i < 36; ++i)
-    *reinterpret_cast<f32x4 *>(dqrow + 16 * i) =
-        f32x4{sm_scale * acc[i][0], sm_scale * acc[i][1], sm_scale * acc[i][2], sm_scale * acc[i][3]};
+    for (int n = 0; n < HT; ++n)
+      *reinterpret_cast<f32x4 *>(dqq + (int64_t)16 * n * 576 + 16 * (wave + NW * m)) = acc[m * HT + n];
+  *reinterpret_cast<f32x4 *>(dqq + (int64_t)16 * n0 * 576 + 16 * irope) = acc[16];
+  *reinterpret_cast<f32x4 *>(dqq + (int64_t)16 * (n0 + 1) * 576 + 16 * irope) = acc[17];
 }
 
 // Pair gradients of one query: G[pair, d] = sum_h (s dS)[pair, h] q[h, d] +
@@ -1093,20 +1101,20 @@ hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, f
   return hipGetLastError();
 }
 
-template <int NW>
-static hipError_t launch_ds_nw(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
+template <int HT>
+static hipError_t launch_ds_ht(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0, int32_t Tc,
                                float *dq, void *dsT, void *pT, hipStream_t s) {
   static bool attr_done = false;  // per process: the attribute holds for every device
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       smem_bwd_bytes<NW>());
+    hipError_t e = hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<HT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       smem_bwd_bytes<HT>());
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(mla_bwd_ds_kernel<NW>, dim3((uint32_t)Tc, H / (16 * NW)), dim3(NW * 64), smem_bwd_bytes<NW>(), s,
-                     (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D, N, H, k, sm_scale, t0,
-                     dq, (__bf16 *)dsT, (__bf16 *)pT);
+  hipLaunchKernelGGL(mla_bwd_ds_kernel<HT>, dim3((uint32_t)Tc, H / (16 * HT)), dim3(HT * 128), smem_bwd_bytes<HT>(),
+                     s, (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D, N, H, k, sm_scale,
+                     t0, dq, (__bf16 *)dsT, (__bf16 *)pT);
   return hipGetLastError();
 }
 
@@ -1134,8 +1142,8 @@ hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *id
                                 int32_t Tc, float *dq, void *dsT, void *pT, void *Gv, hipStream_t s) {
   if (Tc <= 0) return hipSuccess;
   __bf16 *G = (__bf16 *)Gv;
-  hipError_t e = H % 64 == 0 ? launch_ds_nw<4>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s)
-                             : launch_ds_nw<2>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s);
+  hipError_t e = H % 64 == 0 ? launch_ds_ht<4>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s)
+                             : launch_ds_ht<2>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s);
   if (e != hipSuccess) return e;
   switch (H / 32) {
     case 1:
