@@ -302,9 +302,11 @@ def run_kl(torch, dsa, cfg, t, dev, steps):
 # --------------------------------------------------------------------------- backward
 def run_backward(torch, dsa, cfg, t, dev, steps):
     """One sparse-training step's backward on a prefill's own outputs (its
-    selection, attention output and lse): the sparse-MLA backward with a
-    synthetic upstream gradient, and the indexer's KL backward (scores at the
-    selection, the score gradient of the mean per-token KL, then dw, dq, dk)."""
+    selection, attention output and lse): the index scores at the selection,
+    then the sparse-MLA backward with a synthetic upstream gradient, which
+    also returns the score gradient of the mean per-token KL from the same
+    attention probabilities (one pass over the logits for both losses), then
+    the indexer's dw, dq, dk."""
     import synth
     L, H, k = cfg.L, cfg.H, cfg.k
     dout = synth.normal(cfg.seed, 91, (L, H, 512), device=dev, std=0.01).to(torch.bfloat16)
@@ -319,20 +321,18 @@ def run_backward(torch, dsa, cfg, t, dev, steps):
     dki = torch.empty((L, cfg.D_I), dtype=torch.float32, device=dev)
     iws = torch.empty(dsa.dsa_indexer_bwd_workspace_bytes(L, L, k), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    st = StageSamples(torch, ["sparse_mla_bwd", "scores_at", "kl_grad", "indexer_bwd"])
+    st = StageSamples(torch, ["scores_at", "sparse_mla_bwd_kl", "indexer_bwd"])
     for i in range(steps + 1):
         evs = st.new()
         evs[0].record(stream)
-        dsa.dsa_sparse_mla_bwd(t["q"], t["kv"], t["idx"], t["out"], t["lse"], dout, cfg.sm_scale, dq, dkv, mws,
-                               stream=stream)
-        evs[1].record(stream)
         dsa.dsa_indexer_scores_at(t["q8"], t["qs"], t["k8"], t["ks"], t["w"], t["idx"], sc, stream=stream)
+        evs[1].record(stream)
+        dsa.dsa_sparse_mla_bwd_kl(t["q"], t["kv"], t["idx"], t["out"], t["lse"], dout, sc, dkl, cfg.sm_scale, dq, dkv,
+                                  grad, mws, stream=stream)
         evs[2].record(stream)
-        dsa.dsa_indexer_kl_bwd(t["q"], t["kv"], t["idx"], sc, t["lse"], dkl, cfg.sm_scale, grad, stream=stream)
-        evs[3].record(stream)
         dsa.dsa_indexer_bwd(t["q8"], t["qs"], t["k8"], t["ks"], t["w"], t["idx"], grad, dw, dqi, dki, iws,
                             stream=stream)
-        evs[4].record(stream)
+        evs[3].record(stream)
         torch.cuda.synchronize()
         if i > 0:
             st.add(evs)
@@ -349,7 +349,8 @@ def run_backward(torch, dsa, cfg, t, dev, steps):
         "stages_ms": {n: round(v, 3) for n, v in ms.items()},
         "tokens_per_s": round(L / (sum(ms.values()) / 1e3), 1),
         "roofline": {
-            "sparse_mla_bwd": _rl("mfma", mla_flop / (ms["sparse_mla_bwd"] / 1e3) / 1e12, PEAK_BF16_TFLOPS,
+            # the attention backward's stage also forms the KL score gradient (a per-token pass over [T, k])
+            "sparse_mla_bwd": _rl("mfma", mla_flop / (ms["sparse_mla_bwd_kl"] / 1e3) / 1e12, PEAK_BF16_TFLOPS,
                                   "TFLOP/s"),
             "indexer_bwd": _rl("mfma", idx_flop / (ms["indexer_bwd"] / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
         },

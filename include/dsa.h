@@ -181,6 +181,28 @@ dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx,
                               const void *dout, int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *dq,
                               float *dkv, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* dsa_sparse_mla_bwd_kl: one sparse-training backward for both losses.  In
+ * sparse training the main model is trained by the language-modelling loss
+ * and the indexer, on the same selection, by the KL loss against the main
+ * attention (the pages cited at dsa_sparse_mla_bwd and dsa_indexer_kl_bwd).
+ * The attention's backward already forms every probability P of the
+ * selection with the forward's lse, and the KL target is their head average,
+ * so this call returns dsa_sparse_mla_bwd's dq and dkv and, from the same P,
+ * dsa_indexer_kl_bwd's score gradient, without a second pass over the
+ * logits:
+ *   grad_scores[t, a] = dkl[t] (pi_a - p_a),  pi = softmax(idx_scores[t]),
+ *   p_a = P_a / sum_a P_a,  P_a = sum over the heads of P[t, a, h]
+ * (0 where the entry has no row).  P_a is summed in fp32 per group of 64
+ * heads (32 when 64 does not divide H), the groups then added in order.
+ *   idx_scores [T, k] fp32 (dsa_indexer_scores_at on this idx), dkl [T] fp32,
+ *   grad_scores [T, k] fp32 out; every other argument, the workspace size and
+ *   the limits as dsa_sparse_mla_bwd (dq and dkv are bit-identical to its).
+ */
+dsa_status dsa_sparse_mla_bwd_kl(const void *q, const void *kv, const int32_t *idx, const void *out,
+                                 const float *lse, const void *dout, const float *idx_scores, const float *dkl,
+                                 int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *dq, float *dkv,
+                                 float *grad_scores, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Index scores at listed positions: the scores a selection ranked, as the
  * indexer's KL loss needs them.  out[t, a] = I[t, idx[t, a]] with the E4M3

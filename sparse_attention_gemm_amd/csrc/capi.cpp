@@ -275,10 +275,13 @@ dsa_status dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const uint8_
 // G [Tc, k, 576] bf16 and the inverted selection (cnt, start [N + 1], list [Tc k]).
 static constexpr int32_t kMlaBwdChunk = 512;
 static int32_t mla_bwd_chunk(int32_t T) { return T < kMlaBwdChunk ? T : kMlaBwdChunk; }
+// Head groups of the dS kernel: 64 heads when 64 divides H, else 32.
+static int32_t mla_bwd_head_groups(int32_t H) { return H % 64 == 0 ? H / 64 : H / 32; }
 static size_t mla_bwd_ws(int32_t T, int32_t H, int64_t N, int32_t k) {
   const size_t tc = (size_t)mla_bwd_chunk(T);
   return align_up((size_t)T * H * 4, 256) + 2 * align_up(tc * k * H * 2, 256) + align_up(tc * k * 576 * 2, 256) +
-         2 * align_up(((size_t)N + 1) * 4, 256) + align_up(tc * k * 4, 256);
+         2 * align_up(((size_t)N + 1) * 4, 256) + align_up(tc * k * 4, 256) +
+         align_up(tc * mla_bwd_head_groups(H) * k * 4, 256);
 }
 
 size_t dsa_sparse_mla_bwd_workspace_bytes(int32_t T, int32_t H, int64_t N, int32_t k) {
@@ -286,10 +289,12 @@ size_t dsa_sparse_mla_bwd_workspace_bytes(int32_t T, int32_t H, int64_t N, int32
   return mla_bwd_ws(T, H, N, std::min<int32_t>(k, DSA_MAX_K));
 }
 
-dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx, const void *out, const float *lse,
-                              const void *dout, int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *dq,
-                              float *dkv, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  CLEAR_ERR();
+// The sparse-MLA backward; with grad_scores, also the indexer KL score
+// gradient from the same P (idx_scores and dkl then required).
+static dsa_status mla_bwd_run(const void *q, const void *kv, const int32_t *idx, const void *out, const float *lse,
+                              const void *dout, const float *idx_scores, const float *dkl, int32_t T, int32_t H,
+                              int64_t N, int32_t k, float sm_scale, float *dq, float *dkv, float *grad_scores,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
   REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "need T >= 0 and N >= 1");
   REQUIRE(k >= 1, DSA_ERR_INVALID_ARG, "k must be >= 1");
   REQUIRE(k <= DSA_MAX_K, DSA_ERR_UNSUPPORTED, "k must be <= %d", DSA_MAX_K);
@@ -299,10 +304,12 @@ dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx,
   REQUIRE(sm_scale == sm_scale && sm_scale > 0.0f, DSA_ERR_INVALID_ARG, "sm_scale must be > 0");
   if (T == 0) return DSA_OK;
   REQUIRE(q && kv && idx && out && lse && dout && dq && dkv, DSA_ERR_INVALID_ARG, "null pointer");
+  REQUIRE(!grad_scores || (idx_scores && dkl), DSA_ERR_INVALID_ARG, "null pointer");
   const size_t need = mla_bwd_ws(T, H, N, k);
   REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu < required %zu",
           workspace ? workspace_bytes : (size_t)0, need);
   const int32_t tc_max = mla_bwd_chunk(T);
+  const int32_t nhg = mla_bwd_head_groups(H);
   char *p = (char *)workspace;
   float *D = (float *)p;
   p += align_up((size_t)T * H * 4, 256);
@@ -317,18 +324,43 @@ dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx,
   int32_t *start = (int32_t *)p;
   p += align_up(((size_t)N + 1) * 4, 256);
   int32_t *list = (int32_t *)p;
+  p += align_up((size_t)tc_max * k * 4, 256);
+  float *psum = grad_scores ? (float *)p : nullptr;
   dsa_status st = hip_check(launch_mla_bwd_delta(out, dout, (int64_t)T * H, D, stream), "delta launch");
   if (st == DSA_OK) st = hip_check(launch_fill_zero_f32(dkv, N * 576, stream), "fill launch");
   for (int32_t t0 = 0; t0 < T && st == DSA_OK; t0 += tc_max) {
     const int32_t tc = std::min(tc_max, T - t0);
-    st = hip_check(launch_mla_bwd_chunk(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, tc, dq, dsT, pT, G, stream),
-                   "sparse mla backward launch");
+    st = hip_check(
+        launch_mla_bwd_chunk(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, tc, dq, dsT, pT, G, psum, stream),
+        "sparse mla backward launch");
+    if (st == DSA_OK && psum)
+      st = hip_check(launch_kl_grad_from_head_sums(idx, idx_scores, dkl, psum, N, k, nhg, t0, tc, grad_scores,
+                                                   stream),
+                     "kl gradient launch");
     if (st == DSA_OK)
       st = hip_check(launch_scatter_build(idx + (int64_t)t0 * k, (int64_t)tc * k, N, cnt, start, list, stream),
                      "scatter launch");
     if (st == DSA_OK) st = hip_check(launch_scatter_add_bf16(start, list, N, G, 576, dkv, stream), "scatter launch");
   }
   return st;
+}
+
+dsa_status dsa_sparse_mla_bwd(const void *q, const void *kv, const int32_t *idx, const void *out, const float *lse,
+                              const void *dout, int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *dq,
+                              float *dkv, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  return mla_bwd_run(q, kv, idx, out, lse, dout, nullptr, nullptr, T, H, N, k, sm_scale, dq, dkv, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+dsa_status dsa_sparse_mla_bwd_kl(const void *q, const void *kv, const int32_t *idx, const void *out,
+                                 const float *lse, const void *dout, const float *idx_scores, const float *dkl,
+                                 int32_t T, int32_t H, int64_t N, int32_t k, float sm_scale, float *dq, float *dkv,
+                                 float *grad_scores, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  CLEAR_ERR();
+  REQUIRE(T == 0 || grad_scores, DSA_ERR_INVALID_ARG, "null pointer");
+  return mla_bwd_run(q, kv, idx, out, lse, dout, idx_scores, dkl, T, H, N, k, sm_scale, dq, dkv, grad_scores,
+                     workspace, workspace_bytes, stream);
 }
 
 size_t dsa_masked_mha_workspace_bytes(int32_t L, int32_t H) {

@@ -95,7 +95,13 @@ hipError_t launch_fill_zero_f32(float *p, int64_t n, hipStream_t s);
 hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, float *D, hipStream_t s);
 hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                 const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0,
-                                int32_t Tc, float *dq, void *dsT, void *pT, void *G, hipStream_t s);
+                                int32_t Tc, float *dq, void *dsT, void *pT, void *G, float *psum, hipStream_t s);
+// The KL score gradient of queries [t0, t0 + Tc) from psum (launch_mla_bwd_chunk's
+// head-group sums of P, nhg groups): grad[t, a] = dkl[t] (softmax(scores[t])_a
+// - P_a / Z), P_a the sum over the groups, Z its sum over the valid entries.
+hipError_t launch_kl_grad_from_head_sums(const int32_t *idx, const float *scores, const float *dkl, const float *psum,
+                                         int64_t N, int32_t k, int32_t nhg, int64_t t0, int32_t Tc, float *grad,
+                                         hipStream_t s);
 // The library's static device scratch (scratch.hip): its size, and its
 // address on the device that owns `stream` (which must be the current device),
 // looked up once per device.

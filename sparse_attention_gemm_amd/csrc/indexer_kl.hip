@@ -229,6 +229,78 @@ __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__res
     out[t * k + a] = (rows[a] >= 0 && accZ > 0.0f) ? dk * (expf(sc[a] - lse_i) - pP[a] * invZ) : 0.0f;
 }
 
+// The KL score gradient from head sums of P formed elsewhere (the sparse-MLA
+// backward forms every P of the selection with the forward's lse, and sums
+// them over each group of heads): one workgroup per query token, each thread
+// holding 8 entries (a = tid + 256 i) with all their loads in flight,
+//   P_a = sum over the groups of psum[tc, group, a],  Z = sum of P_a over the
+//   valid entries with P_a > 0,  out[t, a] = dkl[t] (pi_a - P_a / Z)
+// with pi = softmax of the index scores over the valid entries, and 0 where
+// the entry has no row (or no valid entry has P > 0), as in indexer_kl_kernel.
+constexpr int kKlThreads = 256;
+constexpr int kKlPer = 2048 / kKlThreads;  // entries per thread (k <= 2048)
+static_assert(kKlPer * kKlThreads >= DSA_MAX_K, "every entry of a row has a thread");
+
+// Sum (or max) over the workgroup in a fixed order: waves, then the 4 wave results.
+template <bool MAX>
+__device__ __forceinline__ float kl_block_reduce(float v, float *red) {
+  v = MAX ? wave_max(v) : wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // earlier readers of red are done
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kKlThreads / 64; ++w) r = MAX ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+
+__global__ __launch_bounds__(kKlThreads) void kl_grad_from_head_sums_kernel(const int32_t *__restrict__ idx,
+                                                                            const float *__restrict__ scores,
+                                                                            const float *__restrict__ dkl,
+                                                                            const float *__restrict__ psum,
+                                                                            int64_t N, int k, int nhg, int64_t t0,
+                                                                            float *__restrict__ out) {
+  __shared__ float red[kKlThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t tc = blockIdx.x, t = t0 + tc;
+  const int32_t *irow = idx + t * k;
+  const float *srow = scores + t * k;
+  const float *ps = psum + tc * nhg * k;
+  float P[kKlPer], sc[kKlPer];
+  bool v[kKlPer];
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i) {
+    const int a = tid + kKlThreads * i;
+    const bool in = a < k;
+    const int32_t r = in ? irow[a] : -1;
+    v[i] = r >= 0 && r < N;
+    sc[i] = in ? srow[a] : -INFINITY;
+    float s = 0.0f;
+    for (int n = 0; n < nhg; ++n) s += in ? ps[n * k + a] : 0.0f;
+    P[i] = s;
+  }
+  float z = 0.0f, m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i) {
+    if (v[i] && P[i] > 0.0f) z += P[i];
+    if (v[i]) m = fmaxf(m, sc[i]);
+  }
+  const float accZ = kl_block_reduce<false>(z, red);
+  const float smax = kl_block_reduce<true>(m, red);
+  float e = 0.0f;
+  if (smax != -INFINITY)
+#pragma unroll
+    for (int i = 0; i < kKlPer; ++i) e += v[i] ? expf(sc[i] - smax) : 0.0f;
+  const float ssum = kl_block_reduce<false>(e, red);
+  const float lse_i = smax + logf(ssum), invZ = accZ > 0.0f ? 1.0f / accZ : 0.0f, dk = dkl[t];
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i) {
+    const int a = tid + kKlThreads * i;
+    if (a < k) out[t * k + a] = (v[i] && accZ > 0.0f) ? dk * (expf(sc[i] - lse_i) - P[i] * invZ) : 0.0f;
+  }
+}
+
 }  // namespace
 
 namespace dsa {
@@ -287,5 +359,14 @@ hipError_t launch_indexer_kl_grad(const void *q, const void *kv, const int32_t *
                                   const float *lse, const float *dkl, int64_t N, int32_t T, int32_t H, int32_t k,
                                   float sm_scale, float *grad, hipStream_t s) {
   return launch_kl<true>(q, kv, idx, scores, lse, dkl, N, T, H, k, sm_scale, grad, s);
+}
+
+hipError_t launch_kl_grad_from_head_sums(const int32_t *idx, const float *scores, const float *dkl, const float *psum,
+                                         int64_t N, int32_t k, int32_t nhg, int64_t t0, int32_t Tc, float *grad,
+                                         hipStream_t s) {
+  if (Tc <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kl_grad_from_head_sums_kernel, dim3((uint32_t)Tc), dim3(kKlThreads), 0, s, idx, scores, dkl,
+                     psum, N, k, nhg, t0, grad);
+  return hipGetLastError();
 }
 }  // namespace dsa

@@ -687,10 +687,21 @@ constexpr int kStageRow = 2 * kBN + 8;  // LDS bytes per head row of staged s dS
                                         // transposing reads conflict-free
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 // LDS of the dS kernel: three gathered tiles, the resolved rows of the query's
-// entries, and two buffers of staged s dS and P (16 HT heads x 32 keys each)
+// entries, two buffers of staged s dS and P (16 HT heads x 32 keys each), and
+// two buffers of per-head-tile sums of P (HT x 32 fp32)
 template <int HT>
 constexpr int smem_bwd_bytes() {
-  return kBwdNBuf * kTileBytes + 2048 * 4 + 2 * 2 * 16 * HT * kStageRow;
+  return kBwdNBuf * kTileBytes + 2048 * 4 + 2 * 2 * 16 * HT * kStageRow + 2 * HT * kBN * 4;
+}
+
+// Sum of v over the 16 lanes of each DPP row (every lane gets its row's sum).
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
 }
 
 // One workgroup of 2 HT waves per (query t0 + blockIdx.x, head group
@@ -708,11 +719,16 @@ constexpr int smem_bwd_bytes() {
 // key-major workspace rows as 16-byte runs; logits and dP of tile j+1; dq of
 // tile j.  The only vector-memory operations a tile waits for are its own
 // gathers (loads and stores complete in issue order).
-template <int HT>
+// KL: also the sum over the group's heads of each entry's P, the indexer KL
+// loss's target before normalisation: each wave sums its 16 heads across
+// the lanes of a DPP row, the head tiles meet in LDS, and wave HT adds them
+// in head-tile order and stores psum[tc, head group, entry] (fp32).
+template <int HT, bool KL>
 __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const float *__restrict__ Dd, int64_t N, int H,
-    int k, float sm_scale, int64_t t0, float *__restrict__ dq, __bf16 *__restrict__ dsT, __bf16 *__restrict__ pT) {
+    int k, float sm_scale, int64_t t0, float *__restrict__ dq, __bf16 *__restrict__ dsT, __bf16 *__restrict__ pT,
+    float *__restrict__ psum) {
   constexpr int NW = 2 * HT;
   constexpr int kHeads = 16 * HT;
   constexpr int kStageBuf = 2 * kHeads * kStageRow;  // s dS rows, then P rows
@@ -722,6 +738,7 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
   uint8_t *tiles = smem_raw;
   int *rows = reinterpret_cast<int *>(smem_raw + kBwdNBuf * kTileBytes);
   uint8_t *stage = smem_raw + kBwdNBuf * kTileBytes + 2048 * 4;
+  float *hsum = reinterpret_cast<float *>(stage + 2 * kStageBuf);  // [2][HT][32]
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ht = wave % HT, kb = wave / HT;  // uniform
@@ -788,16 +805,37 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
     f32x4 x, dp;
     half_tile_dot_pair(ct, qr, gr, kb, lg, lc, x, dp);
     bf16x4 sdb, pb;
+    float p4[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = rv[r] >= 0 ? __builtin_amdgcn_exp2f(fmaf(x[r], scale_log2, -lse2)) : 0.0f;
       sdb[r] = (__bf16)(sm_scale * (p * (dp[r] - Dh)));
       pb[r] = (__bf16)p;
+      p4[r] = p;
     }
     // head-major: row 16 ht + c, keys 16 kb + 4 g .. +4
     uint8_t *sb = stage + (jt & 1) * kStageBuf + (16 * ht + lc) * kStageRow + 32 * kb + 8 * lg;
     *reinterpret_cast<bf16x4 *>(sb) = sdb;
     *reinterpret_cast<bf16x4 *>(sb + kHeads * kStageRow) = pb;
+    if (KL) {  // the head tile's sum of P for keys 16 kb + 4 g + r
+      f32x4 hs;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hs[r] = row16_sum(p4[r]);
+      if (lc == 0) *reinterpret_cast<f32x4 *>(hsum + ((jt & 1) * HT + ht) * kBN + 16 * kb + 4 * lg) = hs;
+    }
+  };
+  // KL, wave HT: tile jt's head sums over the group, stored through a buffer
+  // bounded to the query's k entries
+  auto store_hsum = [&](int jt) {
+    const __amdgpu_buffer_rsrc_t rps =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(psum + (tc * (H / kHeads) + blockIdx.y) * k), 0, k * 4,
+                                          (int)kRsrcWord3);
+    if (lane < kBN) {
+      float v = 0.0f;
+#pragma unroll
+      for (int n = 0; n < HT; ++n) v += hsum[((jt & 1) * HT + n) * kBN + lane];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), rps, (jt * kBN + lane) * 4, 0, 0);
+    }
   };
   // dq^T += C^T (s dS)^T for tile jt, s dS from staging buffer jt & 1
   auto dq_tile = [&](int jt) {
@@ -858,10 +896,13 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
   }
   for (int j = 0; j < ntiles; ++j) {
     // This wave's gathers of tile j+1 have landed.  Issued after them: the
-    // stores of tile j-1 (write-out waves, j >= 1).
+    // stores of tile j-1 (j >= 1): two per write-out wave, one for wave HT
+    // with KL (its lanes 0..31 always store).
     if (j + 1 < ntiles) {
       if (wave < HT && j >= 1)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+      else if (KL && wave == HT && j >= 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(1));
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
@@ -869,6 +910,7 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
     if (j + 2 < ntiles)
       gather_tile_async<NW>(tiles + ((j + 2) % kBwdNBuf) * kTileBytes, rows, (j + 2) * kBN, kv, wave, lane);
     if (wave < HT) write_out(j);
+    if (KL && wave == HT) store_hsum(j);
     if (j + 1 < ntiles) logits_ds(j + 1);
     dq_tile(j);
   }
@@ -1101,20 +1143,20 @@ hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, f
   return hipGetLastError();
 }
 
-template <int HT>
+template <int HT, bool KL>
 static hipError_t launch_ds_ht(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0, int32_t Tc,
-                               float *dq, void *dsT, void *pT, hipStream_t s) {
+                               float *dq, void *dsT, void *pT, float *psum, hipStream_t s) {
   static bool attr_done = false;  // per process: the attribute holds for every device
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<HT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       smem_bwd_bytes<HT>());
+    hipError_t e = hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<HT, KL>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem_bwd_bytes<HT>());
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(mla_bwd_ds_kernel<HT>, dim3((uint32_t)Tc, H / (16 * HT)), dim3(HT * 128), smem_bwd_bytes<HT>(),
-                     s, (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D, N, H, k, sm_scale,
-                     t0, dq, (__bf16 *)dsT, (__bf16 *)pT);
+  hipLaunchKernelGGL((mla_bwd_ds_kernel<HT, KL>), dim3((uint32_t)Tc, H / (16 * HT)), dim3(HT * 128),
+                     smem_bwd_bytes<HT>(), s, (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D,
+                     N, H, k, sm_scale, t0, dq, (__bf16 *)dsT, (__bf16 *)pT, psum);
   return hipGetLastError();
 }
 
@@ -1135,15 +1177,22 @@ static hipError_t launch_g_ks(const void *q, const void *dout, const void *dsT, 
 }
 
 // Queries [t0, t0 + Tc): dq of those queries; s dS and P [Tc, k, H] bf16; then
-// the pair gradients G [Tc, k, 576] (fp32 sums rounded to bf16).  H a multiple
-// of 32, at most 128.
+// the pair gradients G [Tc, k, 576] (fp32 sums rounded to bf16); with psum,
+// also each entry's sum of P over each head group, psum [Tc, H / 64 or H / 32,
+// k] fp32 (the groups of the dS kernel: 64 heads when 64 divides H, else 32).
+// H a multiple of 32, at most 128.
 hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                 const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0,
-                                int32_t Tc, float *dq, void *dsT, void *pT, void *Gv, hipStream_t s) {
+                                int32_t Tc, float *dq, void *dsT, void *pT, void *Gv, float *psum, hipStream_t s) {
   if (Tc <= 0) return hipSuccess;
   __bf16 *G = (__bf16 *)Gv;
-  hipError_t e = H % 64 == 0 ? launch_ds_ht<4>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s)
-                             : launch_ds_ht<2>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, s);
+  hipError_t e;
+  if (H % 64 == 0)
+    e = psum ? launch_ds_ht<4, true>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, psum, s)
+             : launch_ds_ht<4, false>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, psum, s);
+  else
+    e = psum ? launch_ds_ht<2, true>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, psum, s)
+             : launch_ds_ht<2, false>(q, kv, idx, lse, dout, D, N, H, k, sm_scale, t0, Tc, dq, dsT, pT, psum, s);
   if (e != hipSuccess) return e;
   switch (H / 32) {
     case 1:

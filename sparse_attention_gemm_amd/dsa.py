@@ -27,7 +27,7 @@ EXPORTS = (
     "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd", "dsa_masked_mha_workspace_bytes",
     "dsa_masked_mha_prefill", "dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_decode_static_scratch_bytes",
     "dsa_decode_noalloc", "dsa_indexer_kl_bwd", "dsa_indexer_bwd_workspace_bytes", "dsa_indexer_bwd",
-    "dsa_sparse_mla_bwd_workspace_bytes", "dsa_sparse_mla_bwd",
+    "dsa_sparse_mla_bwd_workspace_bytes", "dsa_sparse_mla_bwd", "dsa_sparse_mla_bwd_kl",
 )
 
 
@@ -115,10 +115,12 @@ def load():
     L.dsa_sparse_mla_bwd_workspace_bytes.argtypes = [_I32, _I32, _I64, _I32]
     L.dsa_sparse_mla_bwd_workspace_bytes.restype = _SZ
     L.dsa_sparse_mla_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P, _P, _SZ, _P]
+    L.dsa_sparse_mla_bwd_kl.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _F32, _P, _P, _P, _P,
+                                        _SZ, _P]
     L.dsa_indexer_bwd_workspace_bytes.argtypes = [_I32, _I32, _I32]
     L.dsa_indexer_bwd_workspace_bytes.restype = _SZ
     L.dsa_indexer_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
-    for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_indexer_kl_bwd", "dsa_indexer_bwd", "dsa_sparse_mla_bwd", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
+    for name in ("dsa_indexer_scores_at", "dsa_indexer_kl_fwd", "dsa_indexer_kl_bwd", "dsa_indexer_bwd", "dsa_sparse_mla_bwd", "dsa_sparse_mla_bwd_kl", "dsa_masked_mha_prefill", "dsa_quantize_e4m3_per_token", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_fwd",
                  "dsa_prefill", "dsa_decode", "dsa_decode_noalloc", "dsa_paged_cache_append", "dsa_prefill_select",
                  "dsa_decode_indexer_scores", "dsa_sparse_mla_paged_fwd"):
         getattr(L, name).restype = ctypes.c_int
@@ -264,6 +266,21 @@ def dsa_sparse_mla_bwd(q, kv, idx, out, lse, dout, sm_scale, dq, dkv, workspace,
                                      _ptr(out, bf, "out"), _ptr(lse, F32_T, "lse"), _ptr(dout, bf, "dout"), T, H, N,
                                      idx.shape[1], float(sm_scale), _ptr(dq, F32_T, "dq"), _ptr(dkv, F32_T, "dkv"),
                                      _ptr(workspace, name="workspace"), ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_mla_bwd_kl(q, kv, idx, out, lse, dout, idx_scores, dkl, sm_scale, dq, dkv, grad, workspace, N=None,
+                          stream=None):
+    """dsa_sparse_mla_bwd's dq and dkv, and dsa_indexer_kl_bwd's score gradient grad [T, k] from the same P."""
+    T, H = q.shape[0], q.shape[1]
+    N = kv.shape[0] if N is None else N
+    bf = torch.bfloat16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().dsa_sparse_mla_bwd_kl(_ptr(q, bf, "q"), _ptr(kv, bf, "kv"), _ptr(idx, I32_T, "idx"),
+                                        _ptr(out, bf, "out"), _ptr(lse, F32_T, "lse"), _ptr(dout, bf, "dout"),
+                                        _ptr(idx_scores, F32_T, "idx_scores"), _ptr(dkl, F32_T, "dkl"), T, H, N,
+                                        idx.shape[1], float(sm_scale), _ptr(dq, F32_T, "dq"), _ptr(dkv, F32_T, "dkv"),
+                                        _ptr(grad, F32_T, "grad"), _ptr(workspace, name="workspace"), ws_bytes,
+                                        _stream(stream)))
 
 
 def dsa_indexer_kl_bwd(q, kv, idx, idx_scores, lse, dkl, sm_scale, grad, N=None, stream=None):

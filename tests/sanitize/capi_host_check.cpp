@@ -288,9 +288,10 @@ hipError_t launch_mla_bwd_delta(const void *out, const void *dout, int64_t TH, f
 }
 hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                 const float *D, int64_t N, int32_t H, int32_t k, float, int64_t t0, int32_t Tc,
-                                float *dq, void *dsT, void *pT, void *G, hipStream_t) {
+                                float *dq, void *dsT, void *pT, void *G, float *psum, hipStream_t) {
   ++g_launches;
   EXPECT(H % 32 == 0 && H <= 128);
+  if (psum) touch(psum, (size_t)Tc * (H % 64 == 0 ? H / 64 : H / 32) * k * 4);
   read_all((const char *)q + t0 * H * 576 * 2, (size_t)Tc * H * 576 * 2);
   read_all(kv, (size_t)N * 576 * 2);
   read_all(idx + t0 * k, (size_t)Tc * k * 4);
@@ -301,6 +302,18 @@ hipError_t launch_mla_bwd_chunk(const void *q, const void *kv, const int32_t *id
   touch(dsT, (size_t)Tc * k * H * 2);
   touch(pT, (size_t)Tc * k * H * 2);
   touch(G, (size_t)Tc * k * 576 * 2);
+  return hipSuccess;
+}
+hipError_t launch_kl_grad_from_head_sums(const int32_t *idx, const float *scores, const float *dkl, const float *psum,
+                                         int64_t N, int32_t k, int32_t nhg, int64_t t0, int32_t Tc, float *grad,
+                                         hipStream_t) {
+  ++g_launches;
+  EXPECT(N >= 1 && nhg >= 1);
+  read_all(idx + t0 * k, (size_t)Tc * k * 4);
+  read_all(scores + t0 * k, (size_t)Tc * k * 4);
+  read_all(dkl + t0, (size_t)Tc * 4);
+  read_all(psum, (size_t)Tc * nhg * k * 4);
+  touch(grad + t0 * k, (size_t)Tc * k * 4);
   return hipSuccess;
 }
 // the static scratch: a host buffer of the same size, so a request carved past it overflows
@@ -510,6 +523,17 @@ static void check_mla_backward() {
                                 0.07f, (float *)dq.p(), (float *)dkv.p(), ws.p(), wsb, 0) == DSA_OK);
       EXPECT(dsa_sparse_mla_bwd(q.p(), kv.p(), (int32_t *)idx.p(), out.p(), (float *)lse.p(), dout.p(), T, H, N, k,
                                 0.07f, (float *)dq.p(), (float *)dkv.p(), ws.p(), wsb - 1, 0) == DSA_ERR_WORKSPACE);
+      // the same with the KL score gradient from the same P
+      Buf sc((size_t)T * k * 4), dkl((size_t)T * 4), grad((size_t)T * k * 4);
+      EXPECT(dsa_sparse_mla_bwd_kl(q.p(), kv.p(), (int32_t *)idx.p(), out.p(), (float *)lse.p(), dout.p(),
+                                   (float *)sc.p(), (float *)dkl.p(), T, H, N, k, 0.07f, (float *)dq.p(),
+                                   (float *)dkv.p(), (float *)grad.p(), ws.p(), wsb, 0) == DSA_OK);
+      EXPECT(dsa_sparse_mla_bwd_kl(q.p(), kv.p(), (int32_t *)idx.p(), out.p(), (float *)lse.p(), dout.p(),
+                                   (float *)sc.p(), (float *)dkl.p(), T, H, N, k, 0.07f, (float *)dq.p(),
+                                   (float *)dkv.p(), (float *)grad.p(), ws.p(), wsb - 1, 0) == DSA_ERR_WORKSPACE);
+      EXPECT(dsa_sparse_mla_bwd_kl(q.p(), kv.p(), (int32_t *)idx.p(), out.p(), (float *)lse.p(), dout.p(), nullptr,
+                                   (float *)dkl.p(), T, H, N, k, 0.07f, (float *)dq.p(), (float *)dkv.p(),
+                                   (float *)grad.p(), ws.p(), wsb, 0) == DSA_ERR_INVALID_ARG);
     }
   }
   Buf one(64);

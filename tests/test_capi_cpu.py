@@ -196,6 +196,32 @@ def test_indexer_kl_validation(dsa):
     assert g(*b) == dsa.DSA_ERR_INVALID_ARG
 
 
+def test_sparse_mla_bwd_kl_validation(dsa):
+    """The fused backward refuses what dsa_sparse_mla_bwd refuses, and a missing
+    score or gradient pointer, before any device work."""
+    L = dsa.load()
+    f = L.dsa_sparse_mla_bwd_kl
+    T, H, N, k = 6, 128, 5000, 2048
+    need = dsa.dsa_sparse_mla_bwd_workspace_bytes(T, H, N, k)
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, H, N, k, 0.07, FAKE, FAKE, FAKE, FAKE, need, None]
+    for i in (6, 7, 15):  # idx_scores, dkl, grad_scores
+        b = list(base)
+        b[i] = None
+        assert f(*b) == dsa.DSA_ERR_INVALID_ARG, i
+    b = list(base)
+    b[9] = 48  # H not a multiple of 32
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[11] = 2049
+    assert f(*b) == dsa.DSA_ERR_UNSUPPORTED
+    b = list(base)
+    b[17] = need - 1
+    assert f(*b) == dsa.DSA_ERR_WORKSPACE
+    b = list(base)
+    b[8] = 0
+    assert f(*b) == dsa.DSA_OK
+
+
 def test_prefill_validation(dsa):
     L = dsa.load()
     a = dsa.make_prefill_args(1000, 64, 128, 128, 2048, dsa.DSA_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE, dsa.DSA_BF16,

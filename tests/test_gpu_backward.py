@@ -342,6 +342,55 @@ def test_sparse_mla_bwd_is_deterministic(dsa):
     assert np.array_equal(a[1].view(np.int32), b[1].view(np.int32))
 
 
+@pytest.mark.parametrize("T,H,N,k,sstd", [(600, 128, 3000, 256, 1.0), (9, 32, 2000, 100, 4.0),
+                                          (5, 96, 1500, 512, 0.3), (6, 128, 5000, 2048, 1.0)])
+def test_sparse_mla_bwd_kl(dsa, ora, T, H, N, k, sstd):
+    """The backward of both losses from one pass: dq and dkv bit-identical to
+    dsa_sparse_mla_bwd's, and the KL score gradient from the same P against the
+    oracle, with the tolerance of the standalone KL gradient (and against
+    dsa_indexer_kl_bwd where it takes H).  T = 600 spans two query chunks and
+    two head groups of 64; H = 32 and 96 take groups of 32; a ragged row, an
+    empty row and an entry outside the latent rows."""
+    _say(f"sparse mla backward with the KL score gradient T={T} H={H} N={N} k={k} sstd={sstd}")
+    sm = 1 / math.sqrt(192)
+    q = synth.normal(55, 1, (T, H, 576)).to(torch.bfloat16)
+    kv = synth.normal(55, 2, (N, 576), std=1 / 24).to(torch.bfloat16)
+    dout = synth.normal(55, 3, (T, H, 512)).to(torch.bfloat16)
+    idx = _selection(55, T, N, k)
+    idx[0, 5] = N + 3                          # outside the rows: no row
+    scores = synth.normal(55, 4, (T, k), std=sstd)
+    dkl = synth.uniform(55, 5, (T,), lo=0.5, hi=1.5)
+    d = {n: x.to(DEV) for n, x in dict(q=q, kv=kv, idx=idx, dout=dout, sc=scores, dkl=dkl).items()}
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_mla_fwd(d["q"], d["kv"], d["idx"], sm, out, lse)
+    ws = torch.empty(dsa.dsa_sparse_mla_bwd_workspace_bytes(T, H, N, k), dtype=torch.uint8, device=DEV)
+    dq1, dkv1 = torch.full((T, H, 576), 7.0, device=DEV), torch.full((N, 576), 7.0, device=DEV)
+    dsa.dsa_sparse_mla_bwd(d["q"], d["kv"], d["idx"], out, lse, d["dout"], sm, dq1, dkv1, ws)
+    dq2, dkv2 = torch.full((T, H, 576), 7.0, device=DEV), torch.full((N, 576), 7.0, device=DEV)
+    grad = torch.full((T, k), 7.0, device=DEV)
+    dsa.dsa_sparse_mla_bwd_kl(d["q"], d["kv"], d["idx"], out, lse, d["dout"], d["sc"], d["dkl"], sm, dq2, dkv2, grad,
+                              ws)
+    standalone = None
+    if H in (16, 32, 64, 128):
+        standalone = torch.full((T, k), 7.0, device=DEV)
+        dsa.dsa_indexer_kl_bwd(d["q"], d["kv"], d["idx"], d["sc"], lse, d["dkl"], sm, standalone)
+    torch.cuda.synchronize()
+    assert torch.equal(dq1.view(torch.int32), dq2.view(torch.int32))
+    assert torch.equal(dkv1.view(torch.int32), dkv2.view(torch.int32))
+    ref_idx = idx.clone()
+    ref_idx[0, 5] = -1
+    g_ref = ora.indexer_kl_grad(q, kv, ref_idx.numpy(), scores.double().numpy(), dkl.double().numpy(), sm)
+    pi, p = _pi_p(scores.double().numpy(), ref_idx.numpy(), g_ref, dkl.double().numpy())
+    tol = 1e-4 * dkl.double().numpy()[:, None] * (pi + np.abs(p)) + 1e-9
+    g = grad.cpu()
+    _check("score gradient (fused)", g.numpy(), g_ref, tol)
+    if standalone is not None:
+        _check("score gradient (fused) vs dsa_indexer_kl_bwd", g.numpy(), standalone.cpu().double().numpy(), 2 * tol)
+    assert torch.all(g[2] == 0) and g[0, 5] == 0
+    np.testing.assert_allclose(g.double().sum(dim=1).numpy(), 0, atol=1e-5)
+
+
 def test_sparse_mla_bwd_after_prefill_selection(dsa, ora):
     """The sparse-training attention step on the library's own fused causal
     selection: fused prefill -> backward, against the oracle on that selection."""
