@@ -12,7 +12,9 @@
 //    then block table when paged) into LDS;
 //  * the selected latent rows are gathered 32 at a time straight from global
 //    memory into LDS (direct-to-LDS loads, no register staging), row-major,
-//    into three buffers; each row is fetched once for all heads;
+//    into three buffers; each row is fetched once for all heads; the buffers
+//    are separate static arrays and the loop is unrolled by three, so the
+//    compiler can tell a gather from the LDS reads of the other buffers;
 //  * logits are computed transposed, S^T = C Q^T (keys x heads), with bf16
 //    MFMA 16x16x32 and Q^T resident in registers; in that layout each lane
 //    holds 8 keys of one head, which is exactly the B operand layout the PV
@@ -29,6 +31,7 @@
 //  * optional split of the selection across workgroups with an LSE-weighted
 //    combine (used when there are too few queries to fill the GPU).
 #include <algorithm>
+#include <type_traits>
 
 #include "dsa_common.h"
 #include "dsa_launch.h"
@@ -44,7 +47,6 @@ constexpr int kTileSlots = kBN * kRowSlots;
 constexpr int kGatherInsts = (kTileSlots + 63) / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
 constexpr int kPBytes = 8 * 64 * 16;    // P^T of up to 8 head tiles, in B-operand lane order
 constexpr int kNBuf = 3;                 // gathered tiles: PV of tile j, logits of tile j+1, gather of j+2
-constexpr int kSmemMla = kNBuf * kTileBytes + 2 * kPBytes + 128 * 4 + 2048 * 4 + 16;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -61,6 +63,46 @@ __device__ __forceinline__ int64_t phys_row(const int32_t *__restrict__ irow, co
   const int32_t blk = bt[t * max_blocks + (sel >> 6)];
   const int64_t row = (int64_t)blk * 64 + (sel & 63);
   return (blk >= 0 && row < N) ? row : -1;
+}
+
+// LDS of the forward kernel, as separate static arrays: the three gathered
+// tiles are distinct objects, so the compiler can tell an LDS read of one tile
+// from the direct-to-LDS gather into another and waits for neither.
+__shared__ __align__(16) uint8_t g_mla_t0[kTileBytes];
+__shared__ __align__(16) uint8_t g_mla_t1[kTileBytes];
+__shared__ __align__(16) uint8_t g_mla_t2[kTileBytes];
+__shared__ __align__(16) uint8_t g_mla_p[2 * kPBytes];
+__shared__ __align__(16) float g_mla_l[128];
+__shared__ __align__(16) int g_mla_rows[2048];
+__shared__ int g_mla_flag;
+template <int B>
+__device__ __forceinline__ uint8_t *mla_tile() {
+  return B == 0 ? g_mla_t0 : (B == 1 ? g_mla_t1 : g_mla_t2);
+}
+
+// The gather of the forward kernel: the same LDS image as gather_tile_async,
+// through buffer loads indexed by row (a 1152-byte record per latent row, so
+// any row below 2^32 is reachable).  Unlike the flat form, the compiler counts
+// these loads in the vector-memory counter only and keeps exact counts of the
+// LDS reads issued after them.
+template <int NW>
+__device__ __forceinline__ void gather_tile_rec(uint8_t *__restrict__ dst, const int *__restrict__ rows, int r0,
+                                                const __bf16 *__restrict__ kv, int64_t N, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)kv, (short)(576 * 2), (int)(N < 0xFFFFFFFFll ? N : 0xFFFFFFFFll), (int)0x00020000u);
+  int l = lane;
+  asm volatile("" : "+v"(l));
+#pragma unroll
+  for (int n = 0; n < (kGatherInsts + NW - 1) / NW; ++n) {
+    const int i = wave + n * NW;  // uniform
+    if (i >= kGatherInsts) break;
+    const int slot = i * 64 + l;
+    const int r = slot / kRowSlots;
+    const int j = min(slot - r * kRowSlots, 71);
+    const int pr = rows[r0 + r];
+    __builtin_amdgcn_struct_ptr_buffer_load_lds(rs, (lds_void *)(dst + i * 1024), 16, pr >= 0 ? pr : 0, j * 16, 0, 0,
+                                                0);
+  }
 }
 
 // Issue the direct-to-LDS loads of tile rows [r0, r0+32) of this workgroup's
@@ -89,6 +131,18 @@ __device__ __forceinline__ void gather_tile_async(uint8_t *__restrict__ dst, con
   }
 }
 
+// The forward kernel's gather: record-indexed buffer loads when every byte
+// of kv lies within 4 GiB of its start (32-bit buffer offsets), else the flat
+// form, into the same LDS image.
+template <int NW, bool rec>
+__device__ __forceinline__ void gather_tile_fwd(uint8_t *__restrict__ dst, const int *__restrict__ rows, int r0,
+                                                const __bf16 *__restrict__ kv, int64_t N, int wave, int lane) {
+  if constexpr (rec)
+    gather_tile_rec<NW>(dst, rows, r0, kv, N, wave, lane);
+  else
+    gather_tile_async<NW>(dst, rows, r0, kv, wave, lane);
+}
+
 // Shared state of one sparse-MLA workgroup.
 struct MlaCtx {
   const __bf16 *kv;
@@ -97,6 +151,7 @@ struct MlaCtx {
   float *lbuf;          // softmax sums of the workgroup's heads
   const int *rows;      // physical rows of the workgroup's entries (LDS)
   int *flag;            // LDS: set when a tile overshoots the softmax reference
+  int64_t N;            // latent rows
   int tb, te;           // tile range of this workgroup
   int wave, lane, g, c;
 };
@@ -149,17 +204,17 @@ __device__ __forceinline__ float tile_max(const float (&x)[8], float scale_log2)
 
 // Walk the workgroup's tiles: wait for tile i, barrier, prefetch tile i+1,
 // then body(ct, rv) on tile i.  The gather of tile i+1 overlaps the body.
-template <int NW, typename Body>
+template <int NW, bool rec, typename Body>
 __device__ __forceinline__ void for_each_tile(const MlaCtx &cx, Body &&body) {
-  if (cx.tb < cx.te) gather_tile_async<NW>(cx.tiles, cx.rows, 0, cx.kv, cx.wave, cx.lane);
+  if (cx.tb < cx.te) gather_tile_fwd<NW, rec>(g_mla_t0, cx.rows, 0, cx.kv, cx.N, cx.wave, cx.lane);
   int cur = 0;
   for (int tile = cx.tb; tile < cx.te; ++tile, cur ^= 1) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of `tile` have landed in LDS
     __syncthreads();                // ... and every wave's; the other buffer is no longer read
     if (tile + 1 < cx.te)
-      gather_tile_async<NW>(cx.tiles + (cur ^ 1) * kTileBytes, cx.rows, (tile + 1 - cx.tb) * kBN, cx.kv, cx.wave,
-                            cx.lane);
-    body(cx.tiles + cur * kTileBytes, cx.rows + (tile - cx.tb) * kBN);
+      gather_tile_fwd<NW, rec>(cur ? g_mla_t0 : g_mla_t1, cx.rows, (tile + 1 - cx.tb) * kBN, cx.kv, cx.N, cx.wave,
+                               cx.lane);
+    body(cur ? g_mla_t1 : g_mla_t0, cx.rows + (tile - cx.tb) * kBN);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -193,7 +248,7 @@ __device__ __forceinline__ void wait_all_but_newest_tile(int wave) {
 // with a valid entry; a later tile more than 64 above it sets cx.flag and the
 // pass is discarded (returns false, nothing written).  fixed = true: the
 // references are given (exact maxima).
-template <int NW, bool fixed, bool late>
+template <int NW, bool fixed, bool late, bool rec>
 __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18], float &m_ref, float scale_log2,
                                          int64_t t, int H, int hw0, __bf16 *__restrict__ out,
                                          float *__restrict__ lse, int splits, int sp, __bf16 *__restrict__ part_o,
@@ -210,12 +265,13 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
   // starting at this wave's first value tile
   const int tr_off = (4 * g + (c >> 2)) * kCRow + (c & 3) * 8 + wave * MT * 32;
   const int n = cx.te - cx.tb;
-  auto tile_of = [&](int j) { return cx.tiles + (j % kNBuf) * kTileBytes; };
-  auto gather = [&](int j) { gather_tile_async<NW>(tile_of(j), cx.rows, j * kBN, cx.kv, cx.wave, cx.lane); };
-  // logits and probabilities of tile j, published in P buffer j&1
-  auto score_tile = [&](int j) {
+  auto gather = [&](uint8_t *dst, int j) {
+    gather_tile_fwd<NW, rec>(dst, cx.rows, j * kBN, cx.kv, cx.N, cx.wave, cx.lane);
+  };
+  // logits and probabilities of tile j (in ct), published in P buffer j&1
+  auto score_tile = [&](const uint8_t *ct, int j) {
     float x[8];
-    tile_logits(tile_of(j), cx.rows + j * kBN, qr, scale_log2, g, c, x);
+    tile_logits(ct, cx.rows + j * kBN, qr, scale_log2, g, c, x);
     bool over = false;
     if (!fixed) {
       const float mx = tile_max(x, scale_log2);
@@ -237,9 +293,8 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
     if (!fixed && __ballot(over) && cx.lane == 0) *cx.flag = 1;
     *reinterpret_cast<bf16x8 *>(cx.pbuf + (j & 1) * kPBytes + (wave * 64 + cx.lane) * 16) = pb;
   };
-  // PV of tile j with the probabilities in P buffer j&1
-  auto pv_tile = [&](int j) {
-    const uint8_t *ct = tile_of(j);
+  // PV of tile j (in ct) with the probabilities in P buffer j&1
+  auto pv_tile = [&](const uint8_t *ct, int j) {
     const uint8_t *pj = cx.pbuf + (j & 1) * kPBytes;
     // value operands of this wave's MT tiles (keys 4g..4g+3 | 16+4g..16+4g+3)
     bf16x8 va[MT];
@@ -260,23 +315,31 @@ __device__ __forceinline__ bool mla_pass(const MlaCtx &cx, const bf16x8 (&qr)[18
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Iteration j with tile j in buffer B = j % 3 (tile j+1 in B+1, j+2 in B+2):
+  // the loop is unrolled by three so that every buffer is a fixed object.
+  auto step = [&](auto bc, int j) {
+    constexpr int B = decltype(bc)::value;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's gathers of tile j+1 have landed
+    __syncthreads();  // P(j) from every wave; tile j+1 from every wave; nobody reads tile j-1 any more
+    if (!late && j + 2 < n) gather(mla_tile<(B + 2) % 3>(), j + 2);
+    if (j + 1 < n) score_tile(mla_tile<(B + 1) % 3>(), j + 1);
+    if (late && j + 2 < n) gather(mla_tile<(B + 2) % 3>(), j + 2);
+    pv_tile(mla_tile<B>(), j);
+  };
   if (n > 0) {
-    gather(0);
+    gather(g_mla_t0, 0);
     if (n > 1) {
-      gather(1);
+      gather(g_mla_t1, 1);
       wait_all_but_newest_tile<NW>(wave);  // tile 0 landed (tile 1 may be in flight)
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
-    score_tile(0);
-    for (int j = 0; j < n; ++j) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's gathers of tile j+1 have landed
-      __syncthreads();  // P(j) from every wave; tile j+1 from every wave; nobody reads tile j-1 any more
-      if (!late && j + 2 < n) gather(j + 2);
-      if (j + 1 < n) score_tile(j + 1);
-      if (late && j + 2 < n) gather(j + 2);
-      pv_tile(j);
+    score_tile(g_mla_t0, 0);
+    for (int j = 0; j < n; j += 3) {
+      step(std::integral_constant<int, 0>(), j);
+      if (j + 1 < n) step(std::integral_constant<int, 1>(), j + 1);
+      if (j + 2 < n) step(std::integral_constant<int, 2>(), j + 2);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -339,15 +402,16 @@ struct MlaItem {
 
 template <int NW>
 __device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, bf16x8 (&qr)[18], const __bf16 *__restrict__ q,
-                                             uint8_t *smem_raw, int64_t wid, const int32_t *__restrict__ idx,
+                                             int64_t wid, const int32_t *__restrict__ idx,
                                              const int32_t *__restrict__ bt, int max_blocks, int64_t N, int H, int k,
                                              int splits) {
-  cx.tiles = smem_raw;
-  cx.pbuf = smem_raw + kNBuf * kTileBytes;
-  cx.lbuf = reinterpret_cast<float *>(cx.pbuf + 2 * kPBytes);
-  int *rows = reinterpret_cast<int *>(cx.lbuf + 128);   // <= 2048 physical rows
+  cx.tiles = g_mla_t0;
+  cx.pbuf = g_mla_p;
+  cx.lbuf = g_mla_l;
+  int *rows = g_mla_rows;  // <= 2048 physical rows
   cx.rows = rows;
-  cx.flag = rows + 2048;
+  cx.flag = &g_mla_flag;
+  cx.N = N;
   const int n_hg = (H + 16 * NW - 1) / (16 * NW);  // the last group is padded when 16 NW does not divide H
   MlaItem it;
   it.sp = (int)(wid % splits);
@@ -388,24 +452,24 @@ __device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, bf16x8 (&qr)[18], const
 // pass for the maxima, then the accumulation pass with those references.
 // Out of line: it only runs when the first pass was discarded (rare), and
 // keeps its registers out of the main pass.
-template <int NW, bool late>
+template <int NW, bool late, bool rec>
 __device__ __noinline__ void mla_redo_item(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
                                            const int32_t *__restrict__ idx, const int32_t *__restrict__ bt,
                                            int max_blocks, int64_t N, int H, int k, float scale_log2,
                                            __bf16 *__restrict__ out, float *__restrict__ lse, int splits,
                                            __bf16 *__restrict__ part_o, float *__restrict__ part_ml, int64_t wid) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
   MlaCtx cx;
   cx.kv = kv;
   bf16x8 qr[18];
-  const MlaItem it = mla_setup<NW>(cx, qr, q, smem_raw, wid, idx, bt, max_blocks, N, H, k, splits);
+  const MlaItem it = mla_setup<NW>(cx, qr, q, wid, idx, bt, max_blocks, N, H, k, splits);
   float m_ref = -INFINITY;
-  for_each_tile<NW>(cx, [&](const uint8_t *ct, const int *rv) {
+  for_each_tile<NW, rec>(cx, [&](const uint8_t *ct, const int *rv) {
     float x[8];
     tile_logits(ct, rv, qr, scale_log2, cx.g, cx.c, x);
     m_ref = fmaxf(m_ref, tile_max(x, scale_log2));
   });
-  mla_pass<NW, true, late>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o, part_ml);
+  mla_pass<NW, true, late, rec>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o,
+                                part_ml);
 }
 
 // NW waves: 16*NW heads per workgroup; for the logits wave w owns 16 heads,
@@ -418,22 +482,22 @@ __device__ __noinline__ void mla_redo_item(const __bf16 *__restrict__ q, const _
 // below 2^64, far inside the fp32/bf16 range, and the result is the same
 // softmax.  If any tile overshoots that, the pass is discarded and the
 // workgroup recomputes the item with exact maxima (mla_redo_item).
-template <int NW, bool late>
+template <int NW, bool late, bool rec>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ bt, int max_blocks, int64_t N, int T, int H, int k, float scale_log2,
     __bf16 *__restrict__ out, float *__restrict__ lse, int splits, __bf16 *__restrict__ part_o,
     float *__restrict__ part_ml) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
   MlaCtx cx;
   cx.kv = kv;
   bf16x8 qr[18];
-  const MlaItem it = mla_setup<NW>(cx, qr, q, smem_raw, blockIdx.x, idx, bt, max_blocks, N, H, k, splits);
+  const MlaItem it = mla_setup<NW>(cx, qr, q, blockIdx.x, idx, bt, max_blocks, N, H, k, splits);
   float m_ref = -INFINITY;
-  if (mla_pass<NW, false, late>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o,
-                                part_ml))
+  if (mla_pass<NW, false, late, rec>(cx, qr, m_ref, scale_log2, it.t, H, it.hw0, out, lse, splits, it.sp, part_o,
+                                     part_ml))
     return;
-  mla_redo_item<NW, late>(q, kv, idx, bt, max_blocks, N, H, k, scale_log2, out, lse, splits, part_o, part_ml, blockIdx.x);
+  mla_redo_item<NW, late, rec>(q, kv, idx, bt, max_blocks, N, H, k, scale_log2, out, lse, splits, part_o, part_ml,
+                               blockIdx.x);
 }
 
 // LSE-weighted combine of split partials.  grid (T*H/4), block 256: 4 heads,
@@ -554,28 +618,26 @@ template <int NW, bool late>
 hipError_t launch_bf16_variant(const void *q, const void *kv, const int32_t *idx, const int32_t *bt,
                                int max_blocks, int64_t N, int T, int H, int k, float scale_log2, void *out, float *lse,
                                int splits, __bf16 *part_o, float *part_ml, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)sparse_mla_bf16_kernel<NW, late>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmemMla);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // LDS: the static arrays of the kernel (g_mla_*), no dynamic part
   const int64_t items = (int64_t)T * ((H + 16 * NW - 1) / (16 * NW)) * splits;
-  hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW, late>), dim3((uint32_t)items), dim3(NW * 64), kSmemMla, s,
-                     (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
-                     (__bf16 *)out, lse, splits, part_o, part_ml);
+  if (N * (576 * 2) <= (int64_t(1) << 32))  // every row within 4 GiB: record-indexed gathers
+    hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW, late, true>), dim3((uint32_t)items), dim3(NW * 64), 0, s,
+                       (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
+                       (__bf16 *)out, lse, splits, part_o, part_ml);
+  else
+    hipLaunchKernelGGL((sparse_mla_bf16_kernel<NW, late, false>), dim3((uint32_t)items), dim3(NW * 64), 0, s,
+                       (const __bf16 *)q, (const __bf16 *)kv, idx, bt, max_blocks, N, T, H, k, scale_log2,
+                       (__bf16 *)out, lse, splits, part_o, part_ml);
   return hipGetLastError();
 }
 
 // Order of a tile's gather within an iteration.  Issued before the logits
-// (early), it has a whole iteration to land, but while it is in flight the
-// compiler cannot count the logits' LDS reads (the direct-to-LDS load is a
-// flat instruction) and waits for all of them at every step.  Issued after
-// the logits (late), those reads overlap the MFMAs and the gather has about
-// half an iteration.  Measured: late is 3-4% faster over a long prefill
-// selection (whose rows come largely from L2/MALL); early is faster for split
-// decode items, whose rows come from HBM.
+// (early), it has a whole iteration to land; issued after them (late), about
+// half an iteration.  With record-indexed gathers the compiler counts the
+// logits' LDS reads exactly either way (with the flat form it waits for all
+// of them at every step while a gather is in flight).  Measured at L = 131072:
+// late 69.4-70.0 ms against early 70.8-71.4; early is faster for split decode
+// items, whose rows come from HBM.
 template <int NW>
 hipError_t launch_bf16_nw(const void *q, const void *kv, const int32_t *idx, const int32_t *bt,
                           int max_blocks, int64_t N, int T, int H, int k, float scale_log2, void *out, float *lse,
