@@ -23,6 +23,8 @@
 //    Latent rows are gathered 32 per tile into LDS with direct-to-LDS loads
 //    (double-buffered); the logits S = Q C^T (bf16 MFMA, fp32 sums) put the
 //    heads along rows, so the head sum is in-lane adds plus permlane swaps.
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_launch.h"
 #include "indexer_core.h"
@@ -77,11 +79,18 @@ constexpr int kGatherInsts = kBN * kRowSlots / 64;    // 37 wave-wide 1 KB loads
 static_assert(kBN * kRowSlots % 64 == 0, "whole gather instructions");
 constexpr int kSteps = 576 / 32;                      // 18 K steps of the logits MFMA
 
-// LDS of one workgroup: two tile buffers, the resolved rows and scores of the
-// query's entries (kpad = k rounded up to the tile), per-wave key partials,
-// and (gradient only) each entry's head sum P.
+// LDS of one workgroup: two tile buffers (static arrays, so that the compiler
+// can tell a gather into one from the LDS reads of the other), then, dynamic,
+// the resolved rows and scores of the query's entries (kpad = k rounded up to
+// the tile), per-wave key partials, and (gradient only) each entry's head sum P.
+__shared__ __align__(16) uint8_t g_kl_t0[kTileBytes];
+__shared__ __align__(16) uint8_t g_kl_t1[kTileBytes];
+template <int B>
+__device__ __forceinline__ uint8_t *kl_tile() {
+  return B == 0 ? g_kl_t0 : g_kl_t1;
+}
 __host__ __device__ constexpr int kl_smem_bytes(int kpad, int nw, bool grad) {
-  return 2 * kTileBytes + kpad * 4 * 2 + 2 * nw * kBN * 4 + (grad ? kpad * 4 : 0);
+  return kpad * 4 * 2 + 2 * nw * kBN * 4 + (grad ? kpad * 4 : 0);
 }
 
 // x of this lane plus x of lane l ^ 32 (resp. l ^ 16).
@@ -96,10 +105,14 @@ __device__ __forceinline__ float pair_sum16(float x) {
 
 // Direct-to-LDS gather of tile rows [r0, r0+32): slot q of the tile holds row
 // q / 74, 16-byte chunk q % 74 (chunks 72, 73 repeat chunk 71); entries with
-// no row load row 0 (they are masked).
-template <int NW>
+// no row load row 0 (they are masked).  rec: buffer loads indexed by row (a
+// 1152-byte record each), which the compiler counts in the vector-memory
+// counter only, so it keeps exact counts of the LDS reads issued after them;
+// usable while every row lies within 4 GiB of kv (32-bit offsets).  Else the
+// flat form.
+template <int NW, bool rec>
 __device__ __forceinline__ void kl_gather(uint8_t *__restrict__ dst, const int *__restrict__ rows, int r0,
-                                          const __bf16 *__restrict__ kv, int wave, int lane) {
+                                          const __bf16 *__restrict__ kv, int64_t N, int wave, int lane) {
   int l = lane;
   asm volatile("" : "+v"(l));
 #pragma unroll
@@ -110,8 +123,15 @@ __device__ __forceinline__ void kl_gather(uint8_t *__restrict__ dst, const int *
     const int r = slot / kRowSlots;
     const int j = min(slot - r * kRowSlots, 71);
     const int pr = rows[r0 + r];
-    __builtin_amdgcn_global_load_lds(kv + ((int64_t)(pr >= 0 ? pr : 0) * 576 + j * 8), (lds_void *)(dst + i * 1024),
-                                     16, 0, 0);
+    if constexpr (rec) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)kv, (short)(576 * 2), (int)(N < 0xFFFFFFFFll ? N : 0xFFFFFFFFll), (int)0x00020000u);
+      __builtin_amdgcn_struct_ptr_buffer_load_lds(rs, (lds_void *)(dst + i * 1024), 16, pr >= 0 ? pr : 0, j * 16,
+                                                  0, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(kv + ((int64_t)(pr >= 0 ? pr : 0) * 576 + j * 8),
+                                       (lds_void *)(dst + i * 1024), 16, 0, 0);
+    }
   }
 }
 
@@ -121,7 +141,7 @@ __device__ __forceinline__ void kl_gather(uint8_t *__restrict__ dst, const int *
 // gradient): since pi = softmax(I) and p sums to one,
 //   d KL_t / d I_a = pi_a - p_a,   out[t, a] = dkl[t] (pi_a - P_a / Z)
 // (0 where the entry has no row); P_a is kept in LDS until Z is known.
-template <int NW, bool GRAD>
+template <int NW, bool GRAD, bool rec>
 __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__restrict__ q,
                                                              const __bf16 *__restrict__ kv,
                                                              const int32_t *__restrict__ idx,
@@ -134,8 +154,7 @@ __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__res
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t t = blockIdx.x;
   const int ntiles = (k + kBN - 1) / kBN, kpad = ntiles * kBN;
-  uint8_t *tiles = smem;
-  int *rows = reinterpret_cast<int *>(smem + 2 * kTileBytes);
+  int *rows = reinterpret_cast<int *>(smem);
   float *sc = reinterpret_cast<float *>(rows + kpad);
   float *part = sc + kpad;  // [2][NW][32]
   float *pP = part + 2 * NW * kBN;  // GRAD: each entry's head sum
@@ -174,13 +193,15 @@ __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__res
       if (GRAD) pP[a] = rows[a] >= 0 ? P : 0.0f;
     }
   };
-  kl_gather<NW>(tiles, rows, 0, kv, wave, lane);
-  for (int it = 0; it < ntiles; ++it) {
+  kl_gather<NW, rec>(g_kl_t0, rows, 0, kv, N, wave, lane);
+  // tile it in buffer it & 1; unrolled by two so that each buffer is a fixed object
+  auto step = [&](auto bc, int it) {
+    constexpr int B = decltype(bc)::value;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's gathers of tile it have landed
     __syncthreads();                // every wave's; part[(it-1)&1] is complete; tile it-1 is free
-    if (it + 1 < ntiles) kl_gather<NW>(tiles + ((it + 1) & 1) * kTileBytes, rows, (it + 1) * kBN, kv, wave, lane);
+    if (it + 1 < ntiles) kl_gather<NW, rec>(kl_tile<B ^ 1>(), rows, (it + 1) * kBN, kv, N, wave, lane);
     if (wave == 0 && it > 0) consume(it - 1);
-    const uint8_t *tb = tiles + (it & 1) * kTileBytes;
+    const uint8_t *tb = kl_tile<B>();
     // S[head 4g + r][key c] (keys 0..15) and [key 16 + c] (keys 16..31)
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -202,9 +223,13 @@ __global__ __launch_bounds__(NW * 64) void indexer_kl_kernel(const __bf16 *__res
     // lane's and its partner's values
     const float y0 = pair_sum16(pair_sum32(e0)), y1 = pair_sum16(pair_sum32(e1));
     if (g == 0) {
-      part[((it & 1) * NW + wave) * kBN + c] = y0;
-      part[((it & 1) * NW + wave) * kBN + 16 + c] = y1;
+      part[(B * NW + wave) * kBN + c] = y0;
+      part[(B * NW + wave) * kBN + 16 + c] = y1;
     }
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(std::integral_constant<int, 0>(), it);
+    if (it + 1 < ntiles) step(std::integral_constant<int, 1>(), it + 1);
   }
   __syncthreads();  // the last tile's partials
   if (wave != 0) return;
@@ -323,19 +348,26 @@ static hipError_t launch_kl(const void *q, const void *kv, const int32_t *idx, c
   if (T == 0) return hipSuccess;
   const int kpad = (k + kBN - 1) / kBN * kBN;
   const float sl2 = sm_scale * 1.4426950408889634f;
+  const bool rec = N * (576 * 2) <= (int64_t(1) << 32);  // every row within 4 GiB: record-indexed gathers
 #define DSA_KL_CASE(NW)                                                                                          \
   case NW: {                                                                                                     \
     const int bytes = kl_smem_bytes(kpad, NW, GRAD);                                                             \
     static bool attr_done = false; /* per process: the attribute holds for every device */                       \
     if (!attr_done) {                                                                                            \
-      hipError_t e = hipFuncSetAttribute((const void *)indexer_kl_kernel<NW, GRAD>,                              \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,                             \
-                                         kl_smem_bytes(2048, NW, GRAD));                                         \
-      if (e != hipSuccess) return e;                                                                             \
+      for (const void *f : {(const void *)indexer_kl_kernel<NW, GRAD, true>,                                      \
+                            (const void *)indexer_kl_kernel<NW, GRAD, false>}) {                                  \
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,                         \
+                                           kl_smem_bytes(2048, NW, GRAD));                                        \
+        if (e != hipSuccess) return e;                                                                           \
+      }                                                                                                          \
       attr_done = true;                                                                                          \
     }                                                                                                            \
-    hipLaunchKernelGGL((indexer_kl_kernel<NW, GRAD>), dim3(T), dim3(NW * 64), bytes, s, (const __bf16 *)q,       \
-                       (const __bf16 *)kv, idx, scores, lse, dkl, N, H, k, sl2, out);                            \
+    if (rec)                                                                                                     \
+      hipLaunchKernelGGL((indexer_kl_kernel<NW, GRAD, true>), dim3(T), dim3(NW * 64), bytes, s,                  \
+                         (const __bf16 *)q, (const __bf16 *)kv, idx, scores, lse, dkl, N, H, k, sl2, out);       \
+    else                                                                                                         \
+      hipLaunchKernelGGL((indexer_kl_kernel<NW, GRAD, false>), dim3(T), dim3(NW * 64), bytes, s,                 \
+                         (const __bf16 *)q, (const __bf16 *)kv, idx, scores, lse, dkl, N, H, k, sl2, out);       \
     break;                                                                                                       \
   }
   switch (H / 16) {
