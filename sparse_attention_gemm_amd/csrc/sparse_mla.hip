@@ -753,7 +753,7 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 // two buffers of per-head-tile sums of P (HT x 32 fp32)
 template <int HT>
 constexpr int smem_bwd_bytes() {
-  return kBwdNBuf * kTileBytes + 2048 * 4 + 2 * 2 * 16 * HT * kStageRow + 2 * HT * kBN * 4;
+  return 2048 * 4 + 2 * 2 * 16 * HT * kStageRow + 2 * HT * kBN * 4;
 }
 
 // Sum of v over the 16 lanes of each DPP row (every lane gets its row's sum).
@@ -785,7 +785,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 // loss's target before normalisation: each wave sums its 16 heads across
 // the lanes of a DPP row, the head tiles meet in LDS, and wave HT adds them
 // in head-tile order and stores psum[tc, head group, entry] (fp32).
-template <int HT, bool KL>
+template <int HT, bool KL, bool rec>
 __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const int32_t *__restrict__ idx,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const float *__restrict__ Dd, int64_t N, int H,
@@ -797,9 +797,8 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
   constexpr int DT = 32 / NW;                         // value-dim tiles per wave
   static_assert(DT <= 8 && DT * HT == 16, "16 value-dim accumulator tiles per wave");
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  uint8_t *tiles = smem_raw;
-  int *rows = reinterpret_cast<int *>(smem_raw + kBwdNBuf * kTileBytes);
-  uint8_t *stage = smem_raw + kBwdNBuf * kTileBytes + 2048 * 4;
+  int *rows = reinterpret_cast<int *>(smem_raw);  // the gathered tiles are the static g_mla_t*
+  uint8_t *stage = smem_raw + 2048 * 4;
   float *hsum = reinterpret_cast<float *>(stage + 2 * kStageBuf);  // [2][HT][32]
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -860,9 +859,8 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
     __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4 *>(pp), rp, off, 0, 0);
   };
   // logits, P, dS of tile jt for the wave's (head tile, key half); s dS and P to staging buffer jt & 1
-  auto logits_ds = [&](int jt) {
+  auto logits_ds = [&](const uint8_t *ct, int jt) {
     const int l = laundered(), lg = l >> 4, lc = l & 15;
-    const uint8_t *ct = tiles + (jt % kBwdNBuf) * kTileBytes;
     const int *rv = rows + jt * kBN + 16 * kb + 4 * lg;
     f32x4 x, dp;
     half_tile_dot_pair(ct, qr, gr, kb, lg, lc, x, dp);
@@ -900,10 +898,9 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
     }
   };
   // dq^T += C^T (s dS)^T for tile jt, s dS from staging buffer jt & 1
-  auto dq_tile = [&](int jt) {
+  auto dq_tile = [&](const uint8_t *ct, int jt) {
     const int l = laundered(), lg = l >> 4, lc = l & 15;
     const int tr_base = (4 * lg + (lc >> 2)) * kCRow + (lc & 3) * 8;
-    const uint8_t *ct = tiles + (jt % kBwdNBuf) * kTileBytes;
     const uint8_t *sb = stage + (jt & 1) * kStageBuf;
     // B operand of head tile n: lane (g, c) holds head 16 n + c, keys
     // 4 g .. +4 and 16 + 4 g .. +4, the key order of the transposing A reads
@@ -946,17 +943,20 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
   // gather instructions a wave issues per tile (the fewest, over the waves)
   constexpr int kGatherMin = kGatherInsts / NW;
   __syncthreads();
-  if (ntiles > 0) gather_tile_async<NW>(tiles, rows, 0, kv, wave, lane);
-  if (ntiles > 1) gather_tile_async<NW>(tiles + kTileBytes, rows, kBN, kv, wave, lane);
+  if (ntiles > 0) gather_tile_fwd<NW, rec>(mla_tile<0>(), rows, 0, kv, N, wave, lane);
+  if (ntiles > 1) gather_tile_fwd<NW, rec>(mla_tile<1>(), rows, kBN, kv, N, wave, lane);
   if (ntiles > 0) {
     if (ntiles > 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGatherMin));  // tile 0 landed (tile 1 may be in flight)
     else
       __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();  // every wave's gathers of tile 0
-    logits_ds(0);
+    logits_ds(mla_tile<0>(), 0);
   }
-  for (int j = 0; j < ntiles; ++j) {
+  // Iteration j with tile j in static buffer B = j % 3 (j+1 in B+1, j+2 in
+  // B+2), unrolled by three so that every buffer is a fixed object.
+  auto step = [&](auto bc, int j) {
+    constexpr int B = decltype(bc)::value;
     // This wave's gathers of tile j+1 have landed.  Issued after them: the
     // stores of tile j-1 (j >= 1): two per write-out wave, one for wave HT
     // with KL (its lanes 0..31 always store).
@@ -969,12 +969,16 @@ __global__ __launch_bounds__(HT * 128, 1) void mla_bwd_ds_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     lds_barrier();  // staging j & 1 and tile j+1 complete; tile j-1 and staging (j+1) & 1 no longer read
-    if (j + 2 < ntiles)
-      gather_tile_async<NW>(tiles + ((j + 2) % kBwdNBuf) * kTileBytes, rows, (j + 2) * kBN, kv, wave, lane);
+    if (j + 2 < ntiles) gather_tile_fwd<NW, rec>(mla_tile<(B + 2) % 3>(), rows, (j + 2) * kBN, kv, N, wave, lane);
     if (wave < HT) write_out(j);
     if (KL && wave == HT) store_hsum(j);
-    if (j + 1 < ntiles) logits_ds(j + 1);
-    dq_tile(j);
+    if (j + 1 < ntiles) logits_ds(mla_tile<(B + 1) % 3>(), j + 1);
+    dq_tile(mla_tile<B>(), j);
+  };
+  for (int j = 0; j < ntiles; j += 3) {
+    step(std::integral_constant<int, 0>(), j);
+    if (j + 1 < ntiles) step(std::integral_constant<int, 1>(), j + 1);
+    if (j + 2 < ntiles) step(std::integral_constant<int, 2>(), j + 2);
   }
   // dq of the wave's accumulator tiles
   float *dqq = dq + (t * H + hbase + c) * 576 + 4 * g;
@@ -1209,16 +1213,16 @@ template <int HT, bool KL>
 static hipError_t launch_ds_ht(const void *q, const void *kv, const int32_t *idx, const float *lse, const void *dout,
                                const float *D, int64_t N, int32_t H, int32_t k, float sm_scale, int64_t t0, int32_t Tc,
                                float *dq, void *dsT, void *pT, float *psum, hipStream_t s) {
-  static bool attr_done = false;  // per process: the attribute holds for every device
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void *)mla_bwd_ds_kernel<HT, KL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem_bwd_bytes<HT>());
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  hipLaunchKernelGGL((mla_bwd_ds_kernel<HT, KL>), dim3((uint32_t)Tc, H / (16 * HT)), dim3(HT * 128),
-                     smem_bwd_bytes<HT>(), s, (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D,
-                     N, H, k, sm_scale, t0, dq, (__bf16 *)dsT, (__bf16 *)pT, psum);
+  // LDS: the static tile buffers (g_mla_t*) plus smem_bwd_bytes of dynamic LDS
+  const dim3 grid((uint32_t)Tc, H / (16 * HT));
+  if (N * (576 * 2) <= (int64_t(1) << 32))  // every row within 4 GiB: record-indexed gathers
+    hipLaunchKernelGGL((mla_bwd_ds_kernel<HT, KL, true>), grid, dim3(HT * 128), smem_bwd_bytes<HT>(), s,
+                       (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D, N, H, k, sm_scale, t0,
+                       dq, (__bf16 *)dsT, (__bf16 *)pT, psum);
+  else
+    hipLaunchKernelGGL((mla_bwd_ds_kernel<HT, KL, false>), grid, dim3(HT * 128), smem_bwd_bytes<HT>(), s,
+                       (const __bf16 *)q, (const __bf16 *)kv, idx, lse, (const __bf16 *)dout, D, N, H, k, sm_scale, t0,
+                       dq, (__bf16 *)dsT, (__bf16 *)pT, psum);
   return hipGetLastError();
 }
 
