@@ -26,6 +26,8 @@
 //    and values in fp16.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_launch.h"
 #include "dsa_sizes.h"
@@ -211,8 +213,21 @@ constexpr int kTileInsts = kKnInsts + kKrInsts + kVInsts + kMInsts;  // 24
 constexpr int kInstsW = kTileInsts / 4;                              // 6 per wave
 static_assert(kTileInsts % 4 == 0, "every wave issues the same number of loads per tile");
 constexpr int kNBuf = 3;                  // tile j+2 loads while tile j is computed
-constexpr int kLutOff = kNBuf * kTileBytes;
-constexpr int kAttnSmem = kLutOff + 256 * 16;  // + the mask table
+// LDS of the attention kernel, as separate static arrays: the kNBuf tile
+// buffers and the mask table (entry n keeps fp16 element e of a group's 8
+// probabilities iff bit e of n is set).  Distinct objects let the compiler
+// tell an LDS read of one buffer from the loads in flight into another; in
+// one block it waited for the next tile's loads before reading the current
+// tile.
+__shared__ __align__(16) uint8_t g_mha_r0[kTileBytes];
+__shared__ __align__(16) uint8_t g_mha_r1[kTileBytes];
+__shared__ __align__(16) uint8_t g_mha_r2[kTileBytes];
+__shared__ __align__(16) uint4 g_mha_lut[256];
+static_assert(kNBuf == 3, "three ring buffers");
+template <int B>
+__device__ __forceinline__ uint8_t *mha_ring() {
+  return B == 0 ? g_mha_r0 : (B == 1 ? g_mha_r1 : g_mha_r2);
+}
 constexpr int kSteps = kDq / 32;       // 6 K steps of the logits MFMA
 constexpr int kNopeSteps = kDn / 32;   // the first 4 cover the up-projected (fp16) dims
 constexpr int kVT = kDvh / 16;         // 8 value tiles of the PV MFMA (a ninth sums the probabilities)
@@ -230,7 +245,6 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 
 // Per-workgroup state shared by the walks.
 struct MhaCtx {
-  uint8_t *smem;
   const char *kn, *kr, *vb, *mk;     // tile-0 bases: K_h no-rope, latent rope, V_h, mask column 0
   int kr_len, mk_len;                // bytes readable from the rope and mask bases
   int64_t kv_tile;                   // bytes between tiles in K_h / V_h (32 keys x H heads x 256 B)
@@ -330,29 +344,29 @@ __device__ __forceinline__ void mha_walk(const MhaCtx &cx, const f16x8 (&qn)[2][
                                          float (&m_ref)[2], f32x4 (&o)[2][kVT + 1]) {
   const int g = cx.g, c = cx.c, wave = cx.wave;
   const int tr_off = kVOff + (4 * g + (c >> 2)) * kVRow + (c & 3) * 8;
-  const uint4 *lut = reinterpret_cast<const uint4 *>(cx.smem + kLutOff);
+  const uint4 *lut = g_mha_lut;
   f16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = c == 0 ? (_Float16)1.0f : (_Float16)0.0f;
-  // tile it sits in buffer it % kNBuf: cur is its byte offset, nxt2 that of tile it + 2
-  int cur = 0, nxt2 = 2 * kTileBytes;
-  auto step = [](int b) { return b == (kNBuf - 1) * kTileBytes ? 0 : b + kTileBytes; };
-  mha_load_tile(cx, cx.smem, 0);
-  if (cx.ntiles > 1) mha_load_tile(cx, cx.smem + kTileBytes, 1);
-  for (int it = 0; it < cx.ntiles; ++it, cur = step(cur), nxt2 = step(nxt2)) {
+  // tile it sits in ring buffer it % 3; the walk is unrolled by three so that
+  // every buffer is a fixed object
+  mha_load_tile(cx, mha_ring<0>(), 0);
+  if (cx.ntiles > 1) mha_load_tile(cx, mha_ring<1>(), 1);
+  auto tile_step = [&](auto bc, int it) {
+    constexpr int B = decltype(bc)::value;
     if (it + 1 < cx.ntiles) {  // tile it landed; tile it+1 may still be in flight
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstsW));
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();  // every wave's loads of tile it landed; nobody reads tile it-1 any more
-    if (it + 2 < cx.ntiles) mha_load_tile(cx, cx.smem + nxt2, it + 2);
-    if (it * kKT > cx.wave_last) continue;  // past every query of this wave
-    const uint8_t *tb = cx.smem + cur;
+    if (it + 2 < cx.ntiles) mha_load_tile(cx, mha_ring<(B + 2) % 3>(), it + 2);
+    if (it * kKT > cx.wave_last) return;  // past every query of this wave
+    const uint8_t *tb = mha_ring<B>();
     uint32_t mw[2];
     mw[0] = *reinterpret_cast<const uint32_t *>(tb + kMOff + (kQW * wave + c) * 4);
     mw[1] = *reinterpret_cast<const uint32_t *>(tb + kMOff + (kQW * wave + 16 + c) * 4);
-    if (__builtin_amdgcn_ballot_w64((mw[0] | mw[1]) != 0u) == 0) continue;  // nothing selected in this tile
+    if (__builtin_amdgcn_ballot_w64((mw[0] | mw[1]) != 0u) == 0) return;  // nothing selected in this tile
     f32x4 s[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) s[u][0] = s[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -439,6 +453,11 @@ __device__ __forceinline__ void mha_walk(const MhaCtx &cx, const f16x8 (&qn)[2][
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) o[u][kVT] = mfma_f16_16x16x32(ones, pb[u], o[u][kVT]);
+  };
+  for (int it = 0; it < cx.ntiles; it += 3) {
+    tile_step(std::integral_constant<int, 0>(), it);
+    if (it + 1 < cx.ntiles) tile_step(std::integral_constant<int, 1>(), it + 1);
+    if (it + 2 < cx.ntiles) tile_step(std::integral_constant<int, 2>(), it + 2);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // the tile buffers are free
@@ -479,9 +498,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv, const _Float16 *__restrict__ kbuf,
     const _Float16 *__restrict__ vbuf, const uint32_t *__restrict__ mask, int L, int H, float scale_log2,
     __bf16 *__restrict__ out, float *__restrict__ lse) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];  // tile buffers, then the mask table
   MhaCtx cx;
-  cx.smem = smem_raw;
   const int tid = threadIdx.x;
   cx.lane = tid & 63;
   cx.g = cx.lane >> 4;
@@ -534,7 +551,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int d = 0; d < 4; ++d)
       w[d] = ((tid >> (2 * d)) & 1 ? 0x0000FFFFu : 0u) | ((tid >> (2 * d + 1)) & 1 ? 0xFFFF0000u : 0u);
-    *reinterpret_cast<uint4 *>(smem_raw + kLutOff + tid * 16) = uint4{w[0], w[1], w[2], w[3]};
+    g_mha_lut[tid] = uint4{w[0], w[1], w[2], w[3]};
   }
   // (the table is read only after the walk's first barrier)
   f16x8 qn[2][kNopeSteps];
@@ -570,8 +587,6 @@ hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, co
     hipError_t e = hipFuncSetAttribute((const void *)mha_upproj_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kUpSmem);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)masked_mha_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmem);
-    if (e != hipSuccess) return e;
     attr_done = true;
   }
   hipLaunchKernelGGL(mha_upproj_kernel, dim3((L + kUpT - 1) / kUpT, H), dim3(512), kUpSmem, s, (const __bf16 *)kv,
@@ -583,7 +598,8 @@ hipError_t launch_masked_mha(const void *q, const void *kv, const void *w_uk, co
   if (e != hipSuccess) return e;
   const dim3 grid((uint32_t)mha_groups(L, H));
   const float sl2 = sm_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(masked_mha_kernel, grid, dim3(256), kAttnSmem, s, (const __bf16 *)q, (const __bf16 *)kv, kbuf,
+  // the attention kernel's LDS is static (g_mha_*)
+  hipLaunchKernelGGL(masked_mha_kernel, grid, dim3(256), 0, s, (const __bf16 *)q, (const __bf16 *)kv, kbuf,
                      vbuf, mask, L, H, sl2, (__bf16 *)out, lse);
   return hipGetLastError();
 }

@@ -46,7 +46,6 @@ constexpr int kTileBytes = kBN * kCRow;  // 37376
 constexpr int kTileSlots = kBN * kRowSlots;
 constexpr int kGatherInsts = (kTileSlots + 63) / 64;  // wave-wide 1 KB direct-to-LDS loads per tile
 constexpr int kPBytes = 8 * 64 * 16;    // P^T of up to 8 head tiles, in B-operand lane order
-constexpr int kNBuf = 3;                 // gathered tiles: PV of tile j, logits of tile j+1, gather of j+2
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -146,7 +145,6 @@ __device__ __forceinline__ void gather_tile_fwd(uint8_t *__restrict__ dst, const
 // Shared state of one sparse-MLA workgroup.
 struct MlaCtx {
   const __bf16 *kv;
-  uint8_t *tiles;       // kNBuf x kTileBytes of LDS
   uint8_t *pbuf;        // P^T exchange, two buffers of [head tile][lane] x 16 bytes
   float *lbuf;          // softmax sums of the workgroup's heads
   const int *rows;      // physical rows of the workgroup's entries (LDS)
@@ -405,7 +403,6 @@ __device__ __forceinline__ MlaItem mla_setup(MlaCtx &cx, bf16x8 (&qr)[18], const
                                              int64_t wid, const int32_t *__restrict__ idx,
                                              const int32_t *__restrict__ bt, int max_blocks, int64_t N, int H, int k,
                                              int splits) {
-  cx.tiles = g_mla_t0;
   cx.pbuf = g_mla_p;
   cx.lbuf = g_mla_l;
   int *rows = g_mla_rows;  // <= 2048 physical rows
@@ -743,7 +740,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       : "v"(base), "i"(o0), "i"(o1), "i"(o2), "i"(o3)                                             \
       : "memory")
 
-constexpr int kBwdNBuf = 3;  // gathered tiles: dq, logits, in flight
 constexpr int kStageRow = 2 * kBN + 8;  // LDS bytes per head row of staged s dS or P (32 keys + pad):
                                         // 18 dwords keeps both the 8-byte writes and the
                                         // transposing reads conflict-free
