@@ -1124,8 +1124,12 @@ __global__ __launch_bounds__(kGThreads, 1) void mla_bwd_g_kernel(const __bf16 *_
   const __amdgpu_buffer_rsrc_t gr =
       __builtin_amdgcn_make_buffer_rsrc((void *)(G + tc * k * 576), 0, k * 576 * 2, (int)kRsrcWord3);
   const int goff = c * 576 * 2 + (16 * ti0 + 4 * g) * 2;  // bytes: key c of a tile, this lane's dims
-  for (int j = 0; j < nblk; ++j) {
-    if (loader) {
+  // The two roles run loops of their own with the same barriers, so the
+  // compute waves' code holds no direct-to-LDS load: the compiler then counts
+  // their LDS reads exactly (a flat direct-to-LDS load anywhere on a path
+  // makes it wait for every LDS read at each step).
+  if (loader) {
+    for (int j = 0; j < nblk; ++j) {
       // block j + 2 goes to the buffer last read before the previous barrier
       if (j + 2 < nblk) {
         issue_block(j + 2, smem_raw + ((j + 2) % kGNBuf) * S::kBuf);
@@ -1133,32 +1137,35 @@ __global__ __launch_bounds__(kGThreads, 1) void mla_bwd_g_kernel(const __bf16 *_
       } else {
         __builtin_amdgcn_s_waitcnt(0);
       }
-    } else {
+      lds_barrier();
+    }
+    return;
+  }
+  for (int j = 0; j < nblk; ++j) {
 #pragma unroll 1
-      for (int kt = 0; kt < kGKeys / 16; ++kt) {
-        const uint8_t *brow = smem_raw + (j % kGNBuf) * S::kBuf + (16 * kt + c) * S::kRow + 16 * g;
-        f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int kt = 0; kt < kGKeys / 16; ++kt) {
+      const uint8_t *brow = smem_raw + (j % kGNBuf) * S::kBuf + (16 * kt + c) * S::kRow + 16 * g;
+      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 64 * s);
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 64 * s);
 #pragma unroll
-          for (int jt = 0; jt < 3; ++jt) acc[jt] = mfma_bf16_16x16x32(aq[jt][s], b, acc[jt]);
-        }
-        // the dO term (zero operands on the rope tiles)
+        for (int jt = 0; jt < 3; ++jt) acc[jt] = mfma_bf16_16x16x32(aq[jt][s], b, acc[jt]);
+      }
+      // the dO term (zero operands on the rope tiles)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 2 * H + 64 * s);
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(brow + 2 * H + 64 * s);
 #pragma unroll
-          for (int jt = 0; jt < 3; ++jt) acc[jt] = mfma_bf16_16x16x32(ao[jt][s], b, acc[jt]);
-        }
-        const int off = (j * kGKeys + 16 * kt) * 576 * 2 + goff;
+        for (int jt = 0; jt < 3; ++jt) acc[jt] = mfma_bf16_16x16x32(ao[jt][s], b, acc[jt]);
+      }
+      const int off = (j * kGKeys + 16 * kt) * 576 * 2 + goff;
 #pragma unroll
-        for (int jt = 0; jt < 3; ++jt) {
-          bf16x4 v;
+      for (int jt = 0; jt < 3; ++jt) {
+        bf16x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[jt][r];  // RNE
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), gr, off + 32 * jt, 0, 0);
-        }
+        for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[jt][r];  // RNE
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), gr, off + 32 * jt, 0, 0);
       }
     }
     // Only the key blocks in LDS need ordering: the loaders waited for their
