@@ -41,7 +41,7 @@ hipError_t launch_prefill_indexer_topk(const uint8_t *q8, const float *qs, const
 // Sparse MLA.  block_table != NULL: idx holds logical positions of sequence
 // t (page size 64); otherwise idx holds rows of kv.  Entries that do not map
 // to a row in [0, N) are skipped like -1.  splits > 1 needs the
-// partial buffers (part_o [T,splits,H,512] f32, part_ml [T,splits,H,2] f32).
+// partial buffers (part_o [T,splits,H,512] bf16, part_ml [T,splits,H,2] f32).
 hipError_t launch_sparse_mla_bf16(const void *q, const void *kv, const int32_t *idx,
                                   const int32_t *block_table, int32_t max_blocks, int64_t N, int32_t T,
                                   int32_t H, int32_t k, float sm_scale, void *out, float *lse,
