@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import json
 import math
+import statistics
 import os
 import sys
 import time
@@ -233,14 +234,32 @@ def run_decode(torch, dsa, synth, cfg, dev, steps, warmup, flush):
             st.add(evs)
     med = st.median_ms()
     ms = {n: med[n] for n in names}
+    # the step as a caller runs it: the append, then the fused entry (indexer, top-k and attention in one call)
+    ws = torch.empty(max(dsa.dsa_decode_workspace_bytes(t["args"]), 256), dtype=torch.uint8, device=dev)
+    fused = []
+    for i in range(warmup + steps):
+        flush.view(torch.int64).sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dsa.dsa_paged_cache_append(t["app_lat"], t["app_k8"], t["app_ks"], t["app_pos"], t["bt"], t["kvp"], t["k8p"],
+                                   t["ksp"], n_pool_rows=t["nb"] * 64, stream=stream)
+        dsa.dsa_decode(t["args"], ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            fused.append(e0.elapsed_time(e1))
+    del ws
     work = decode_work(cfg, t["ctx_cpu"])
-    step_ms = med["_step"]
+    step_ms = statistics.median(fused)
     res = {
         "workload": cfg.name, "B": cfg.B, "ctx_min": int(t["ctx_cpu"].min()), "ctx_max": int(t["ctx_cpu"].max()),
         "ctx_mean": float(t["ctx_cpu"].float().mean()), "k": cfg.k, "H": cfg.H,
         "paged_shuffled": cfg.shuffled, "steps": steps, "warmup": warmup,
         "timing": f"median over {steps} steps after {warmup} warm-up steps, each step after a 512 MB cache-evicting read",
         "ms_per_step": step_ms,
+        "step": "dsa_paged_cache_append + dsa_decode (the fused entry); stages_ms time the per-stage entries in a "
+                "separate loop of the same length",
+        "ms_per_step_staged": med["_step"],
         "tokens_per_s": cfg.B / (step_ms / 1e3),
         "unit": "tokens/s",
         "cold_cache": True,
